@@ -1,0 +1,245 @@
+"""CPU oracle of the IQ1_S / IQ2_XS codebook-search encode and choice search.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+bench's ``cpu_baseline`` leg may import this package.  The product path
+(``ggml_iq_codebook_amd``) never imports it, and the two share no code: the
+arithmetic lives in ``iq_oracle.c`` (plain C, float64, OpenMP over blocks),
+which this module loads with ctypes.  Every function below cites, in
+``iq_oracle.c``, the passage of the NVIDIA Model-Optimizer pages it follows.
+
+Layouts match the C-ABI of the product so results can be compared directly:
+weights ``[batch, rows, cols]`` float32, importance ``[batch, cols]`` or None,
+packed ``[batch, rows, cols/256, block_bytes]`` uint8.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "iq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BLOCK_BYTES = {"iq1_s": 50, "iq2_xs": 74}
+NUM_CHOICE_GROUPS = {"iq1_s": 8, "iq2_xs": 16}
+
+ERRORS = {1: "non-finite weight", 2: "negative or non-finite importance",
+          3: "scale out of fp16 range", 4: "bad argument", 5: "grid index beyond the grid"}
+
+
+class OracleError(ValueError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile iq_oracle.c into liboracle.so (gcc, -O2, OpenMP, no contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.orc_f16_to_f64.restype = ctypes.c_double
+        L.orc_predict_scale.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float]
+        L.orc_predict_scale.restype = ctypes.c_uint16
+        for name in ("orc_iq1s_encode", "orc_iq2xs_encode"):
+            f = getattr(L, name)
+            f.argtypes = [P, P, i64, P, i32, P, P, P]
+            f.restype = ctypes.c_int
+        for name in ("orc_iq1s_decode", "orc_iq2xs_decode"):
+            f = getattr(L, name)
+            f.argtypes = [P, i64, P, i32, P]
+            f.restype = ctypes.c_int
+        L.orc_iq2xs_candidates.argtypes = [P, P, i64, P, i32, i32, P, P, P]
+        L.orc_iq2xs_candidates.restype = ctypes.c_int
+        L.orc_choice_search.argtypes = [P, P, i64, i32, i32, i32, P, P]
+        L.orc_choice_search.restype = ctypes.c_int
+        L.orc_choice_objective.argtypes = [P, P, i32, i32, P]
+        L.orc_choice_objective.restype = ctypes.c_double
+        L.orc_choice_replay.argtypes = [P, P, i32, i32, i32, P, ctypes.c_double,
+                                        ctypes.POINTER(ctypes.c_double)]
+        L.orc_choice_replay.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _blocks(w: np.ndarray, importance):
+    """[B,R,C] weight -> [nblk,256] blocks, plus the per-block importance."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim == 2:
+        w = w[None]
+    B, R, C = w.shape
+    if C % 256 or w.size == 0:
+        raise OracleError("cols must be a positive multiple of 256")
+    x = w.reshape(-1, 256)
+    imp = None
+    if importance is not None:
+        imp = np.ascontiguousarray(importance, dtype=np.float32).reshape(B, C)
+        imp = np.ascontiguousarray(np.broadcast_to(imp[:, None, :], (B, R, C))).reshape(-1, 256)
+    return w.shape, x, imp
+
+
+# --------------------------------------------------------------------------
+# scale
+# --------------------------------------------------------------------------
+
+def f32_to_f16_bits(v: float) -> int:
+    return int(lib().orc_f32_to_f16(float(v)))
+
+
+def f16_bits_to_float(h: int) -> float:
+    return float(lib().orc_f16_to_f64(int(h)))
+
+
+def predict_scale_bits(amax: float, fmt: str = "iq1_s") -> int:
+    """fp16 bits of (amax / divisor) * 0.61, computed in fp32."""
+    divisor = 16.875 if fmt == "iq1_s" else 155.0
+    return int(lib().orc_predict_scale(float(amax), divisor, 0.61))
+
+
+# --------------------------------------------------------------------------
+# encode / decode
+# --------------------------------------------------------------------------
+
+def encode(fmt: str, w, grid, importance=None, scales=None, choices=None) -> np.ndarray:
+    """Exhaustive importance-weighted encode.  Returns [B,R,C/256,bytes] uint8.
+
+    scales: None or fp16 bits [B,R,C/256] (pinned super-block scales).
+    choices: None or [B,R,C/256,G] forced per-choice-group picks.
+    """
+    shape, x, imp = _blocks(w, importance)
+    B, R, C = shape
+    nblk = x.shape[0]
+    grid = np.ascontiguousarray(grid, dtype=np.float32)
+    nb = BLOCK_BYTES[fmt]
+    out = np.zeros((nblk, nb), dtype=np.uint8)
+    sc = None if scales is None else np.ascontiguousarray(scales, dtype=np.uint16).reshape(nblk)
+    ch = None
+    if choices is not None:
+        G = NUM_CHOICE_GROUPS[fmt]
+        ch = np.ascontiguousarray(choices, dtype=np.int32).reshape(nblk, G)
+        if ch.min() < 0 or ch.max() >= 16:
+            raise OracleError("choice out of range")
+    f = lib().orc_iq1s_encode if fmt == "iq1_s" else lib().orc_iq2xs_encode
+    st = f(_ptr(x), _ptr(imp), nblk, _ptr(grid), grid.shape[0], _ptr(sc), _ptr(ch), _ptr(out))
+    if st:
+        raise OracleError(ERRORS.get(st, "error %d" % st))
+    return out.reshape(B, R, C // 256, nb)
+
+
+def decode(fmt: str, packed, grid, strict: bool = True) -> np.ndarray:
+    """Decode to float64, shape [..., cols].  An index beyond the grid raises
+    (strict) or decodes its group to zero."""
+    nb = BLOCK_BYTES[fmt]
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    lead = p.shape[:-2]
+    nblk = p.size // nb
+    grid = np.ascontiguousarray(grid, dtype=np.float32)
+    out = np.zeros((nblk, 256), dtype=np.float64)
+    f = lib().orc_iq1s_decode if fmt == "iq1_s" else lib().orc_iq2xs_decode
+    st = f(_ptr(p), nblk, _ptr(grid), grid.shape[0], _ptr(out))
+    if st and strict:
+        raise OracleError(ERRORS.get(st, "error %d" % st))
+    return out.reshape(*lead, p.shape[-2] * 256)
+
+
+def iq2xs_candidates(w, grid, importance=None, top_c: int = 8):
+    """Top-C local scales per 16-column scale group with their error vectors.
+
+    Returns cand_err [B*R*C/256, 16, top_c, 16] float32 (xhat - x),
+    cand_choice [.., 16, top_c] int32 and cand_codes [.., 16, top_c, 2] uint16.
+    """
+    shape, x, imp = _blocks(w, importance)
+    nblk = x.shape[0]
+    grid = np.ascontiguousarray(grid, dtype=np.float32)
+    err = np.zeros((nblk, 16, top_c, 16), dtype=np.float32)
+    ch = np.zeros((nblk, 16, top_c), dtype=np.int32)
+    codes = np.zeros((nblk, 16, top_c, 2), dtype=np.uint16)
+    st = lib().orc_iq2xs_candidates(_ptr(x), _ptr(imp), nblk, _ptr(grid), grid.shape[0], top_c,
+                                    _ptr(err), _ptr(ch), _ptr(codes))
+    if st:
+        raise OracleError(ERRORS.get(st, "error %d" % st))
+    return err, ch, codes
+
+
+# --------------------------------------------------------------------------
+# choice search
+# --------------------------------------------------------------------------
+
+def choice_search(H, cand_err, sweeps: int = 2):
+    """cand_err [rows, G, C, 256/G]; returns (picks [rows,G], trace [sweeps+1,rows,G])."""
+    H = np.ascontiguousarray(H, dtype=np.float32)
+    cand = np.ascontiguousarray(cand_err, dtype=np.float32)
+    rows, G, C, L = cand.shape
+    picks = np.zeros((rows, G), dtype=np.int32)
+    trace = np.zeros((sweeps + 1, rows, G), dtype=np.int32)
+    st = lib().orc_choice_search(_ptr(H), _ptr(cand), rows, G, C, sweeps, _ptr(picks), _ptr(trace))
+    if st:
+        raise OracleError(ERRORS.get(st, "error %d" % st))
+    return picks, trace
+
+
+def choice_objective(H, cand_err, picks) -> np.ndarray:
+    """J = e^T H e per row for the given picks (float64)."""
+    H = np.ascontiguousarray(H, dtype=np.float32)
+    cand = np.ascontiguousarray(cand_err, dtype=np.float32)
+    picks = np.ascontiguousarray(picks, dtype=np.int32)
+    rows, G, C, L = cand.shape
+    out = np.empty(rows)
+    for r in range(rows):
+        out[r] = lib().orc_choice_objective(_ptr(H), _ptr(cand[r]), G, C, _ptr(picks[r]))
+    return out
+
+
+def choice_replay(H, cand_row, trace_row, tol: float):
+    """Check another implementation's decisions on one row; (fail_index, worst)."""
+    H = np.ascontiguousarray(H, dtype=np.float32)
+    cand = np.ascontiguousarray(cand_row, dtype=np.float32)
+    tr = np.ascontiguousarray(trace_row, dtype=np.int32)
+    G, C, L = cand.shape
+    worst = ctypes.c_double(0.0)
+    fail = lib().orc_choice_replay(_ptr(H), _ptr(cand), G, C, tr.shape[0] - 1, _ptr(tr), tol,
+                                   ctypes.byref(worst))
+    return int(fail), float(worst.value)
+
+
+# --------------------------------------------------------------------------
+# float64 error of a payload against the weight (used to judge ties)
+# --------------------------------------------------------------------------
+
+def unit_errors(fmt: str, packed, w, grid, importance=None) -> np.ndarray:
+    """Weighted squared error per choice group (IQ1_S: 32 values, IQ2_XS: 16).
+
+    Returns [nblk, G] float64: sum over the unit of w * (x - xhat)^2.
+    """
+    shape, x, imp = _blocks(w, importance)
+    xhat = decode(fmt, packed, grid).reshape(-1, 256)
+    wt = np.ones_like(x, dtype=np.float64) if imp is None else imp.astype(np.float64)
+    e = wt * (x.astype(np.float64) - xhat) ** 2
+    G = NUM_CHOICE_GROUPS[fmt]
+    return e.reshape(-1, G, 256 // G).sum(axis=2)
