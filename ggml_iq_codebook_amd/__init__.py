@@ -1,0 +1,261 @@
+"""Python binding of libiqcodec.so: MI355X-native importance-weighted IQ1_S /
+IQ2_XS codebook-search encode, decode, candidate emission and local-Hessian
+choice search.
+
+This module only marshals arguments: it checks tensors, takes their device
+pointers and the current HIP stream from PyTorch, and calls the C-ABI declared
+in ``include/iq_codec.h``.  Every step of the computation runs in the HIP
+kernels of the library.  There is no CPU path: if the library is not built, or
+the device is not a gfx950 GPU, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (device memory and streams; loads the HIP runtime first)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libiqcodec.so")
+
+FORMATS = {"iq1_s": 0, "iq2_xs": 1}
+BLOCK_BYTES = {"iq1_s": 50, "iq2_xs": 74}
+CHOICE_GROUPS = {"iq1_s": 8, "iq2_xs": 16}
+
+STATUS = {
+    0: "IQ_OK", 1: "IQ_ERR_NULL", 2: "IQ_ERR_FORMAT", 3: "IQ_ERR_SHAPE", 4: "IQ_ERR_GRID",
+    5: "IQ_ERR_NONFINITE", 6: "IQ_ERR_IMPORTANCE", 7: "IQ_ERR_SCALE_RANGE", 8: "IQ_ERR_ARG",
+    9: "IQ_ERR_CODE", 10: "IQ_ERR_HIP", 11: "IQ_ERR_DEVICE",
+}
+
+
+class IQError(RuntimeError):
+    """A non-zero iq_status_t from the library."""
+
+    def __init__(self, code: int, where: str):
+        self.code = int(code)
+        self.name = STATUS.get(self.code, "unknown")
+        super().__init__("%s: %s (%d): %s" % (where, self.name, self.code, _status_str(self.code)))
+
+
+class _FormatInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("block_elems", "block_bytes", "group", "index_bits",
+                                               "grid_max", "choice_groups", "num_choices")]
+
+
+_lib = None
+
+
+def load(build_if_missing: bool = True):
+    """Load libiqcodec.so (building it first only if it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise ImportError("libiqcodec.so is not built (run ggml_iq_codebook_amd.build.build())")
+        from . import build as _build
+        _build.build()
+    L = ctypes.CDLL(LIB_PATH)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.iq_format_info.argtypes = [ctypes.c_int, ctypes.POINTER(_FormatInfo)]
+    L.iq_format_info.restype = ctypes.c_int
+    L.iq_status_str.argtypes = [ctypes.c_int]
+    L.iq_status_str.restype = ctypes.c_char_p
+    L.iq_encode.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, i32, P, P, P, P, P]
+    L.iq_encode.restype = ctypes.c_int
+    L.iq_dequant.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i32, P, P, P]
+    L.iq_dequant.restype = ctypes.c_int
+    L.iq_encode_candidates.argtypes = [ctypes.c_int, P, i64, i64, P, P, i32, i32, P, P, P, P, P]
+    L.iq_encode_candidates.restype = ctypes.c_int
+    L.iq_choice_search.argtypes = [P, P, i64, i32, i32, i32, P, P, P]
+    L.iq_choice_search.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _status_str(code: int) -> str:
+    try:
+        return load().iq_status_str(int(code)).decode()
+    except Exception:  # pragma: no cover - only for messages
+        return ""
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise IQError(code, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev_tensor(t, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be on the GPU" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _fmt(fmt):
+    if fmt not in FORMATS:
+        raise ValueError("unknown format %r" % (fmt,))
+    return FORMATS[fmt]
+
+
+def format_info(fmt: str) -> dict:
+    info = _FormatInfo()
+    _check(load().iq_format_info(_fmt(fmt), ctypes.byref(info)), "iq_format_info")
+    return {n: getattr(info, n) for n, _ in _FormatInfo._fields_}
+
+
+def _status_tensor(status, device):
+    if status is None:
+        return torch.zeros(1, dtype=torch.int32, device=device), True
+    _dev_tensor(status, torch.int32, "status")
+    return status, False
+
+
+def _raise_on_status(status, where):
+    code = int(status.item())
+    if code:
+        raise IQError(code, where)
+
+
+def encode(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, out=None,
+           status=None, check=True):
+    """Encode a [batch, rows, cols] (or [rows, cols]) fp32 weight.
+
+    Returns the packed payload [batch, rows, cols/256, block_bytes] uint8 (the
+    batch dimension is dropped again for a 2-D weight).  ``importance`` is
+    [batch, cols] / [cols]; ``scales`` pinned fp16 bits [batch, rows, cols/256]
+    (int16/uint16 tensor); ``choices`` forced picks [batch, rows, cols/256, G].
+    With ``check`` the call synchronizes and raises IQError on a data error.
+    """
+    f = _fmt(fmt)
+    _dev_tensor(w, torch.float32, "w")
+    squeeze = w.dim() == 2
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [rows, cols] or [batch, rows, cols]")
+    B, R, C = (1, *w.shape) if squeeze else w.shape
+    _dev_tensor(grid, torch.float32, "grid")
+    if grid.dim() != 2 or grid.shape[1] != 8:
+        raise ValueError("grid must be [n, 8]")
+    if importance is not None:
+        _dev_tensor(importance, torch.float32, "importance")
+        if importance.numel() != B * C:
+            raise ValueError("importance must have batch*cols = %d values" % (B * C))
+    if scales is not None:
+        if scales.dtype == torch.int16:
+            scales = scales.view(torch.uint16) if hasattr(torch, "uint16") else scales
+        if not scales.is_cuda or not scales.is_contiguous() or scales.element_size() != 2:
+            raise ValueError("scales must be a contiguous 16-bit GPU tensor of fp16 bits")
+        if scales.numel() != B * R * (C // 256):
+            raise ValueError("scales must have one value per block")
+    if choices is not None:
+        _dev_tensor(choices, torch.int32, "choices")
+        if choices.numel() != B * R * (C // 256) * CHOICE_GROUPS[fmt]:
+            raise ValueError("choices must have %d values per block" % CHOICE_GROUPS[fmt])
+    nb = BLOCK_BYTES[fmt]
+    shape = (B, R, C // 256, nb) if C % 256 == 0 else (B, R, 0, nb)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.uint8, device=w.device)
+    else:
+        _dev_tensor(out, torch.uint8, "out")
+        if out.numel() != B * R * (C // 256) * nb:
+            raise ValueError("out has the wrong size")
+    status, own = _status_tensor(status, w.device)
+    code = load().iq_encode(f, _ptr(w), B, R, C, _ptr(importance), _ptr(grid), grid.shape[0],
+                            _ptr(scales), _ptr(choices), _ptr(out), _ptr(status), _stream())
+    _check(code, "iq_encode")
+    if check:
+        _raise_on_status(status, "iq_encode")
+    return out[0] if squeeze else out
+
+
+def dequant(packed, grid, *, fmt="iq1_s", out=None, status=None, check=True):
+    """Decode [batch, rows, cols/256, block_bytes] (or without batch) to fp32."""
+    f = _fmt(fmt)
+    _dev_tensor(packed, torch.uint8, "packed")
+    _dev_tensor(grid, torch.float32, "grid")
+    squeeze = packed.dim() == 3
+    if packed.dim() not in (3, 4) or packed.shape[-1] != BLOCK_BYTES[fmt]:
+        raise ValueError("packed must be [(batch,) rows, cols/256, %d]" % BLOCK_BYTES[fmt])
+    B, R, NB, _ = (1, *packed.shape) if squeeze else packed.shape
+    C = NB * 256
+    if out is None:
+        out = torch.empty((B, R, C), dtype=torch.float32, device=packed.device)
+    else:
+        _dev_tensor(out, torch.float32, "out")
+        if out.numel() != B * R * C:
+            raise ValueError("out has the wrong size")
+    status, own = _status_tensor(status, packed.device)
+    code = load().iq_dequant(f, _ptr(packed), B, R, C, _ptr(grid), grid.shape[0], _ptr(out),
+                             _ptr(status), _stream())
+    _check(code, "iq_dequant")
+    if check:
+        _raise_on_status(status, "iq_dequant")
+    return out[0] if squeeze else out
+
+
+def encode_candidates(w, grid, importance=None, *, fmt="iq2_xs", top_c=8, codes=False,
+                      status=None, check=True):
+    """Top-C choices per scale group of every 256-column block of [rows, cols].
+
+    Returns (cand_err [rows, cols/256, 16, top_c, 16] fp32, cand_choice
+    [rows, cols/256, 16, top_c] int32, cand_codes [..., 2] uint16 view as int16
+    or None).
+    """
+    f = _fmt(fmt)
+    _dev_tensor(w, torch.float32, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [rows, cols]")
+    R, C = w.shape
+    _dev_tensor(grid, torch.float32, "grid")
+    if importance is not None:
+        _dev_tensor(importance, torch.float32, "importance")
+        if importance.numel() != C:
+            raise ValueError("importance must have cols values")
+    NB = C // 256
+    err = torch.empty((R, NB, 16, top_c, 16), dtype=torch.float32, device=w.device)
+    ch = torch.empty((R, NB, 16, top_c), dtype=torch.int32, device=w.device)
+    cc = torch.empty((R, NB, 16, top_c, 2), dtype=torch.int16, device=w.device) if codes else None
+    status, own = _status_tensor(status, w.device)
+    code = load().iq_encode_candidates(f, _ptr(w), R, C, _ptr(importance), _ptr(grid),
+                                       grid.shape[0], int(top_c), _ptr(err), _ptr(ch), _ptr(cc),
+                                       _ptr(status), _stream())
+    _check(code, "iq_encode_candidates")
+    if check:
+        _raise_on_status(status, "iq_encode_candidates")
+    return err, ch, cc
+
+
+def choice_search(H, cand_err, *, sweeps=2, trace=False):
+    """Local-Hessian choice search of one 256-column block.
+
+    H [256, 256] fp32 symmetric; cand_err [rows, G, C, 256/G] fp32.
+    Returns picks [rows, G] int32 (and the trace [sweeps+1, rows, G] if asked).
+    """
+    _dev_tensor(H, torch.float32, "H")
+    _dev_tensor(cand_err, torch.float32, "cand_err")
+    if H.shape != (256, 256):
+        raise ValueError("H must be [256, 256]")
+    if cand_err.dim() != 4 or cand_err.shape[1] * cand_err.shape[3] != 256:
+        raise ValueError("cand_err must be [rows, G, C, 256/G]")
+    R, G, C, _ = cand_err.shape
+    picks = torch.empty((R, G), dtype=torch.int32, device=H.device)
+    tr = torch.empty((sweeps + 1, R, G), dtype=torch.int32, device=H.device) if trace else None
+    code = load().iq_choice_search(_ptr(H), _ptr(cand_err), R, G, C, int(sweeps), _ptr(picks),
+                                   _ptr(tr), _stream())
+    _check(code, "iq_choice_search")
+    return (picks, tr) if trace else picks

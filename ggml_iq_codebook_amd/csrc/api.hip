@@ -1,0 +1,169 @@
+// api.hip -- the extern "C" entry points of libiqcodec.so declared in
+// include/iq_codec.h: argument validation, the gfx950 device check, and the
+// stream-ordered launches.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "iq_codec.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per device: 0 = not checked, 1 = gfx950, 2 = other.
+std::atomic<int> g_device_kind[kMaxDevices];
+
+iq_status_t check_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return IQ_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return IQ_ERR_DEVICE;
+    int kind = g_device_kind[dev].load(std::memory_order_acquire);
+    if (kind == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return IQ_ERR_HIP;
+        kind = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_kind[dev].store(kind, std::memory_order_release);
+    }
+    return kind == 1 ? IQ_OK : IQ_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Geometry of [batch][rows][cols] with every size positive and cols % 256 == 0.
+iq_status_t geometry(int64_t batch, int64_t rows, int64_t cols, iqk::BlockGeom* g)
+{
+    if (batch <= 0 || rows <= 0 || cols <= 0 || (cols % 256) != 0) return IQ_ERR_SHAPE;
+    const int64_t bpr = cols / 256;
+    // Keep every element index below 2^62 and the launch grid below 2^31 workgroups.
+    if (rows > (INT64_C(1) << 40) / bpr || batch > (INT64_C(1) << 40) / (rows * bpr))
+        return IQ_ERR_SHAPE;
+    g->blocks_per_row = bpr;
+    g->blocks_per_batch = rows * bpr;
+    g->nblocks = batch * rows * bpr;
+    g->cols = cols;
+    if (g->nblocks > (INT64_C(1) << 34)) return IQ_ERR_SHAPE;
+    return IQ_OK;
+}
+
+iq_status_t from_hip(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+iq_status_t iq_format_info(iq_format_t fmt, iq_format_info_t* out)
+{
+    if (!out) return IQ_ERR_NULL;
+    if (fmt == IQ_FMT_IQ1_S) {
+        *out = iq_format_info_t{256, 50, 8, 11, 2048, 8, 16};
+    } else if (fmt == IQ_FMT_IQ2_XS) {
+        *out = iq_format_info_t{256, 74, 8, 9, 512, 16, 16};
+    } else {
+        return IQ_ERR_FORMAT;
+    }
+    return IQ_OK;
+}
+
+const char* iq_status_str(iq_status_t st)
+{
+    switch (st) {
+    case IQ_OK: return "ok";
+    case IQ_ERR_NULL: return "a required pointer is NULL";
+    case IQ_ERR_FORMAT: return "unknown or unsupported format";
+    case IQ_ERR_SHAPE: return "bad shape (empty, or cols not a multiple of 256, or too large)";
+    case IQ_ERR_GRID: return "bad grid (size out of range, or values the format does not allow)";
+    case IQ_ERR_NONFINITE: return "non-finite weight";
+    case IQ_ERR_IMPORTANCE: return "negative or non-finite importance";
+    case IQ_ERR_SCALE_RANGE: return "super-block scale out of fp16 range";
+    case IQ_ERR_ARG: return "argument out of range";
+    case IQ_ERR_CODE: return "payload grid index beyond the grid";
+    case IQ_ERR_HIP: return "HIP runtime error";
+    case IQ_ERR_DEVICE: return "current device is not gfx950";
+    }
+    return "unknown status";
+}
+
+iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t rows, int64_t cols,
+                      const float* importance, const float* grid, int32_t grid_size,
+                      const uint16_t* scales, const int32_t* choices, uint8_t* out,
+                      int32_t* status, hipStream_t stream)
+{
+    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    if (!w || !grid || !out || !status) return IQ_ERR_NULL;
+    iqk::BlockGeom g;
+    iq_status_t st = geometry(batch, rows, cols, &g);
+    if (st) return st;
+    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
+    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
+    if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
+        !aligned(out, 2) || (scales && !aligned(scales, 2)) || (choices && !aligned(choices, 4)) ||
+        !aligned(status, 4))
+        return IQ_ERR_ARG;
+    st = check_device();
+    if (st) return st;
+    hipError_t e = fmt == IQ_FMT_IQ1_S
+        ? iqk::launch_iq1s_encode(w, importance, grid, grid_size, scales, choices, out, status, g, stream)
+        : iqk::launch_iq2xs_encode(w, importance, grid, grid_size, scales, choices, out, status, g, stream);
+    return from_hip(e);
+}
+
+iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, int64_t rows,
+                       int64_t cols, const float* grid, int32_t grid_size, float* out,
+                       int32_t* status, hipStream_t stream)
+{
+    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    if (!packed || !grid || !out || !status) return IQ_ERR_NULL;
+    iqk::BlockGeom g;
+    iq_status_t st = geometry(batch, rows, cols, &g);
+    if (st) return st;
+    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
+    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
+    if (!aligned(grid, 16) || !aligned(out, 16) || !aligned(status, 4)) return IQ_ERR_ARG;
+    st = check_device();
+    if (st) return st;
+    return from_hip(iqk::launch_dequant((int)fmt, packed, grid, grid_size, out, status, g, stream));
+}
+
+iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, int64_t cols,
+                                 const float* importance, const float* grid, int32_t grid_size,
+                                 int32_t top_c, float* cand_err, int32_t* cand_choice,
+                                 uint16_t* cand_codes, int32_t* status, hipStream_t stream)
+{
+    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    if (fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    if (!w || !grid || !cand_err || !cand_choice || !status) return IQ_ERR_NULL;
+    iqk::BlockGeom g;
+    iq_status_t st = geometry(1, rows, cols, &g);
+    if (st) return st;
+    if (grid_size < 1 || grid_size > 512) return IQ_ERR_GRID;
+    if (top_c < 1 || top_c > 16) return IQ_ERR_ARG;
+    if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
+        !aligned(cand_err, 16) || !aligned(cand_choice, 4) ||
+        (cand_codes && !aligned(cand_codes, 2)) || !aligned(status, 4))
+        return IQ_ERR_ARG;
+    st = check_device();
+    if (st) return st;
+    return from_hip(iqk::launch_iq2xs_candidates(w, importance, grid, grid_size, top_c, cand_err,
+                                                 cand_choice, cand_codes, status, g, stream));
+}
+
+iq_status_t iq_choice_search(const float* H, const float* cand_err, int64_t rows, int32_t G,
+                             int32_t C, int32_t sweeps, int32_t* picks, int32_t* trace,
+                             hipStream_t stream)
+{
+    if (!H || !cand_err || !picks) return IQ_ERR_NULL;
+    if (rows <= 0 || rows > (INT64_C(1) << 34)) return IQ_ERR_SHAPE;
+    if ((G != 8 && G != 16) || C < 1 || C > 16 || sweeps < 0 || sweeps > 8) return IQ_ERR_ARG;
+    if (!aligned(H, 4) || !aligned(cand_err, 4) || !aligned(picks, 4) || (trace && !aligned(trace, 4)))
+        return IQ_ERR_ARG;
+    iq_status_t st = check_device();
+    if (st) return st;
+    return from_hip(iqk::launch_choice_search(H, cand_err, rows, G, C, sweeps, picks, trace, stream));
+}
+
+}  // extern "C"

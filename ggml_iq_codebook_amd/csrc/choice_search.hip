@@ -1,0 +1,191 @@
+// choice_search.hip -- local-Hessian choice search of one 256-column block on
+// gfx950, in one launch.
+//
+// The method (NVIDIA Model-Optimizer, "[1/4] Calibrate GGML IQ formats with
+// local_hessian" #3158, steps 2-3; "[4/4] Run the local-Hessian choice search
+// as one CUDA kernel" #3218): every group of a row has C candidate error
+// vectors e_gc (from the every-choice encode); step 2 gives each group the
+// candidate with the least e^T H_gg e; step 3 visits the groups twice, in
+// order, and moves a group to the candidate that most lowers the row's
+// e^T H e with the others held, if it lowers it at all.  With r = H e, the
+// change of the row's objective when group g takes candidate c is
+// score_c - score_cur, score_c = e_c^T H_gg e_c + 2 e_c^T (r_g - H_gg e_cur).
+//
+// Layout: a 256-thread workgroup runs R rows in lockstep; thread t owns
+// column t of r for all R rows (registers), so the rank-L update
+// r += H[:, g] (e_new - e_cur) reads L rows of the symmetric H, coalesced, once
+// per workgroup and step.  The diagonal blocks H_gg, the rows' current errors,
+// e_c^T H_gg e_c and the per-step vectors live in LDS.  Rows are independent,
+// so the grid is rows / R workgroups.
+#include <hip/hip_runtime.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace iqk {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRows = 8;         // rows per workgroup
+constexpr int kMaxL = 32;        // 256 / G for G = 8
+constexpr int kMaxGC = 256;      // G * C <= 16 * 16
+
+struct SearchArgs {
+    const float* H;
+    const float* cand;
+    int32_t* picks;
+    int32_t* trace;
+    int64_t rows;
+    int G, C, L, sweeps;
+};
+
+__global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
+{
+    __shared__ float hdiag[256 * kMaxL];          // H_gg blocks: [g][i][j], L*L each
+    __shared__ float ecur[kRows][256];
+    __shared__ float qself[kRows][kMaxGC];        // e_gc^T H_gg e_gc, [g*C + c]
+    __shared__ float rg[kRows][kMaxL];            // r restricted to group g
+    __shared__ float rest[kRows][kMaxL];
+    __shared__ float dlt[kRows][kMaxL];           // e_new - e_cur of group g
+    __shared__ float score[kRows][16];
+    __shared__ int pick[kRows][16];
+    __shared__ int changed[kRows];
+
+    const int t = threadIdx.x;
+    const int G = a.G, C = a.C, L = a.L;
+    const int64_t row0 = (int64_t)blockIdx.x * kRows;
+    const int nrows = (int)((a.rows - row0) < kRows ? (a.rows - row0) : kRows);
+    const int64_t cstride = (int64_t)G * C * L;   // floats per row of cand
+
+    // Diagonal blocks of H.
+    for (int i = t; i < G * L * L; i += kThreads) {
+        const int g = i / (L * L), rem = i % (L * L), ii = rem / L, jj = rem % L;
+        hdiag[i] = a.H[(int64_t)(g * L + ii) * 256 + g * L + jj];
+    }
+    __syncthreads();
+
+    // e_gc^T H_gg e_gc for every (row, group, candidate).
+    for (int it = t; it < kRows * G * C; it += kThreads) {
+        const int rr = it / (G * C), gc = it % (G * C), g = gc / C;
+        float q = 0.0f;
+        if (rr < nrows) {
+            const float* e = a.cand + (row0 + rr) * cstride + (int64_t)gc * L;
+            const float* hb = hdiag + g * L * L;
+            for (int i = 0; i < L; ++i) {
+                float y = 0.0f;
+                for (int j = 0; j < L; ++j) y = __builtin_fmaf(hb[i * L + j], e[j], y);
+                q = __builtin_fmaf(e[i], y, q);
+            }
+        }
+        qself[rr][gc] = q;
+    }
+    __syncthreads();
+
+    // Step 2: each group's best candidate under its own block (lowest index on ties).
+    for (int it = t; it < kRows * G; it += kThreads) {
+        const int rr = it / G, g = it % G;
+        int best = 0;
+        for (int c = 1; c < C; ++c)
+            if (qself[rr][g * C + c] < qself[rr][g * C + best]) best = c;
+        pick[rr][g] = best;
+        if (rr < nrows) {
+            const float* e = a.cand + (row0 + rr) * cstride + ((int64_t)g * C + best) * L;
+            for (int i = 0; i < L; ++i) ecur[rr][g * L + i] = e[i];
+        } else {
+            for (int i = 0; i < L; ++i) ecur[rr][g * L + i] = 0.0f;
+        }
+    }
+    __syncthreads();
+    if (a.trace)
+        for (int it = t; it < nrows * G; it += kThreads)
+            a.trace[(row0 + it / G) * G + it % G] = pick[it / G][it % G];
+
+    // r = H e (thread t owns column t; H is symmetric, so H[u][t] is read).
+    float r[kRows];
+#pragma unroll
+    for (int rr = 0; rr < kRows; ++rr) r[rr] = 0.0f;
+    for (int u = 0; u < 256; ++u) {
+        const float h = a.H[(int64_t)u * 256 + t];
+#pragma unroll
+        for (int rr = 0; rr < kRows; ++rr) r[rr] = __builtin_fmaf(h, ecur[rr][u], r[rr]);
+    }
+
+    for (int sw = 0; sw < a.sweeps; ++sw) {
+        for (int g = 0; g < G; ++g) {
+            // r of group g to LDS.
+            if (t >= g * L && t < g * L + L) {
+#pragma unroll
+                for (int rr = 0; rr < kRows; ++rr) rg[rr][t - g * L] = r[rr];
+            }
+            __syncthreads();
+            // rest = r_g - H_gg e_cur,g
+            for (int it = t; it < kRows * L; it += kThreads) {
+                const int rr = it / L, i = it % L;
+                const float* hb = hdiag + g * L * L + i * L;
+                float y = 0.0f;
+                for (int j = 0; j < L; ++j) y = __builtin_fmaf(hb[j], ecur[rr][g * L + j], y);
+                rest[rr][i] = rg[rr][i] - y;
+            }
+            __syncthreads();
+            // score_c = e_c^T H_gg e_c + 2 e_c . rest
+            for (int it = t; it < kRows * C; it += kThreads) {
+                const int rr = it / C, c = it % C;
+                float dot = 0.0f;
+                if (rr < nrows) {
+                    const float* e = a.cand + (row0 + rr) * cstride + ((int64_t)g * C + c) * L;
+                    for (int i = 0; i < L; ++i) dot = __builtin_fmaf(e[i], rest[rr][i], dot);
+                }
+                score[rr][c] = __builtin_fmaf(2.0f, dot, qself[rr][g * C + c]);
+            }
+            __syncthreads();
+            // Decision: the lowest-index minimum, taken only on a strict improvement.
+            if (t < kRows) {
+                const int rr = t;
+                int best = 0;
+                for (int c = 1; c < C; ++c)
+                    if (score[rr][c] < score[rr][best]) best = c;
+                const int cur = pick[rr][g];
+                const bool move = rr < nrows && score[rr][best] < score[rr][cur];
+                changed[rr] = move;
+                if (move) {
+                    const float* e = a.cand + (row0 + rr) * cstride + ((int64_t)g * C + best) * L;
+                    for (int i = 0; i < L; ++i) {
+                        dlt[rr][i] = e[i] - ecur[rr][g * L + i];
+                        ecur[rr][g * L + i] = e[i];
+                    }
+                    pick[rr][g] = best;
+                }
+            }
+            __syncthreads();
+            // r += H[:, g-block] * delta for the rows that moved.
+#pragma unroll
+            for (int rr = 0; rr < kRows; ++rr) {
+                if (changed[rr]) {
+                    float acc = r[rr];
+                    for (int i = 0; i < L; ++i)
+                        acc = __builtin_fmaf(a.H[(int64_t)(g * L + i) * 256 + t], dlt[rr][i], acc);
+                    r[rr] = acc;
+                }
+            }
+            __syncthreads();
+        }
+        if (a.trace)
+            for (int it = t; it < nrows * G; it += kThreads)
+                a.trace[((int64_t)(sw + 1) * a.rows + row0 + it / G) * G + it % G] = pick[it / G][it % G];
+    }
+    for (int it = t; it < nrows * G; it += kThreads)
+        a.picks[(row0 + it / G) * G + it % G] = pick[it / G][it % G];
+}
+
+}  // namespace
+
+hipError_t launch_choice_search(const float* H, const float* cand, int64_t rows, int G, int C,
+                                int sweeps, int32_t* picks, int32_t* trace, hipStream_t stream)
+{
+    SearchArgs a{H, cand, picks, trace, rows, G, C, 256 / G, sweeps};
+    const int64_t wgs = (rows + kRows - 1) / kRows;
+    hipLaunchKernelGGL(choice_search_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace iqk

@@ -1,0 +1,63 @@
+// device_common.hpp -- small device helpers shared by the HIP kernels of
+// libiqcodec.so: fp16 conversion, status reporting, block geometry.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "iq_codec.h"
+
+namespace iqk {
+
+constexpr int kWave = 64;
+constexpr int kBlockElems = 256;
+
+// float32 -> IEEE binary16 bits, round to nearest, ties to even, done with
+// integer operations so the result does not depend on the FP mode registers.
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f)
+{
+    const uint32_t x = __float_as_uint(f);
+    const uint32_t sign = (x >> 16) & 0x8000u;
+    const uint32_t a = x & 0x7fffffffu;
+    if (a >= 0x7f800000u) return sign | 0x7c00u | (a > 0x7f800000u ? 0x200u : 0u);
+    if (a >= 0x477ff000u) return sign | 0x7c00u;          // rounds past 65504
+    if (a < 0x38800000u) {                                 // binary16 subnormal range
+        // a = 1.m * 2^(E-127); the subnormal mantissa is value * 2^24.
+        const int E = (int)(a >> 23);
+        if (E < 102) return sign;                          // below half of 2^-24
+        const uint32_t m = (a & 0x7fffffu) | 0x800000u;    // 24-bit significand
+        const int shift = 126 - E;                         // value*2^24 = m >> shift
+        const uint32_t q = m >> shift;
+        const uint32_t rem = m & ((1u << shift) - 1u);
+        const uint32_t half = 1u << (shift - 1);
+        const uint32_t r = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);
+        return sign | r;
+    }
+    const uint32_t h = ((((a >> 23) - 112u) << 10) | ((a & 0x7fffffu) >> 13));
+    const uint32_t rem = a & 0x1fffu;
+    return sign | (h + ((rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ? 1u : 0u));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
+{
+    const uint32_t e = (h >> 10) & 0x1fu;
+    const uint32_t m = h & 0x3ffu;
+    float v;
+    if (e == 0) v = (float)m * 5.9604644775390625e-8f;     // m * 2^-24, exact
+    else if (e == 31) v = __uint_as_float(0x7f800000u | (m << 13));
+    else v = __uint_as_float(((e + 112u) << 23) | (m << 13));
+    return (h & 0x8000u) ? -v : v;
+}
+
+// First data error of a call: only a zero status is replaced.
+__device__ __forceinline__ void report(int32_t* status, int code)
+{
+    atomicCAS(status, 0, code);
+}
+
+__device__ __forceinline__ bool finite_f32(float v)
+{
+    return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u;
+}
+
+}  // namespace iqk

@@ -1,0 +1,39 @@
+// launch.hpp -- host-side launchers of the HIP kernels, called by the C-ABI
+// entry points in api.hip after argument validation.  Each returns the
+// hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace iqk {
+
+// Geometry of the weight/payload being processed.  Blocks are numbered
+// row-major over [batch][rows][cols/256].
+struct BlockGeom {
+    int64_t nblocks;          // batch * rows * (cols / 256)
+    int64_t blocks_per_row;   // cols / 256
+    int64_t blocks_per_batch; // rows * (cols / 256)
+    int64_t cols;
+};
+
+hipError_t launch_iq1s_encode(const float* w, const float* imp, const float* grid, int grid_size,
+                              const uint16_t* scales, const int32_t* choices, uint8_t* out,
+                              int32_t* status, const BlockGeom& g, hipStream_t stream);
+
+hipError_t launch_iq2xs_encode(const float* w, const float* imp, const float* grid, int grid_size,
+                               const uint16_t* scales, const int32_t* choices, uint8_t* out,
+                               int32_t* status, const BlockGeom& g, hipStream_t stream);
+
+hipError_t launch_iq2xs_candidates(const float* w, const float* imp, const float* grid,
+                                   int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
+                                   uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
+                                   hipStream_t stream);
+
+hipError_t launch_dequant(int fmt, const uint8_t* packed, const float* grid, int grid_size,
+                          float* out, int32_t* status, const BlockGeom& g, hipStream_t stream);
+
+hipError_t launch_choice_search(const float* H, const float* cand, int64_t rows, int G, int C,
+                                int sweeps, int32_t* picks, int32_t* trace, hipStream_t stream);
+
+}  // namespace iqk

@@ -1,0 +1,172 @@
+/*
+ * iq_codec.h -- C-ABI of libiqcodec.so: the importance-weighted codebook-search
+ * encode of the GGML IQ1_S and IQ2_XS weight formats, their decode, the top-C
+ * candidate emission and the local-Hessian choice search, as hand-written HIP
+ * kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Sources: the NVIDIA Model-Optimizer pull-request pages
+ *   - "Add IQ tests and release notes" (#2450), code review: block layouts,
+ *     scale predictor, 16-way choice, tie rule, worked decode example;
+ *   - "Weight the IQ1 encoders by the square root of GPTQ's Hessian diagonal"
+ *     (#2723): the weighted objective sum w*(x - s*(q + delta))^2 and the rule
+ *     that uniform importance reproduces the unweighted payload;
+ *   - "Register each GGML IQ format once" (#2525), IQ2_S commit body,
+ *     "What's distinctive about it": IQ2_XS's parity-coded signs;
+ *   - "[4/4] Run the local-Hessian choice search as one CUDA kernel" (#3218)
+ *     with the embedded #3157 (fixed choices), #3158 (local_hessian steps 1-3)
+ *     and #3159 (every-choice encode) bodies.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise; the caller
+ *     allocates and owns every buffer.  The library allocates no device memory.
+ *   - Calls are asynchronous and ordered on `stream` (NULL = the null stream).
+ *     Argument and shape errors are returned synchronously before any launch,
+ *     and nothing is written.  Data errors found on the device (non-finite
+ *     weight, bad importance, scale out of fp16 range, payload index beyond the
+ *     grid) are written to `*status` with an atomic compare-and-swap from 0, so
+ *     the first code to land sticks; the library never clears `*status`: the
+ *     caller zeroes it.  Blocks with a data error are written as zeros.
+ *   - Concurrent calls that share `status` or an output buffer race.
+ *   - Layouts are row-major and contiguous.  Weights are fp32 [batch][rows][cols]
+ *     with cols a positive multiple of 256; a 256-value block is cols/256 of a
+ *     row; the packed payload is [batch][rows][cols/256][block_bytes] uint8.
+ */
+#ifndef IQ_CODEC_H
+#define IQ_CODEC_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    IQ_FMT_IQ1_S = 0,   /* 2048-entry ternary grid, 50-byte blocks (1.5625 bpw) */
+    IQ_FMT_IQ2_XS = 1   /* 512-entry magnitude grid, 74-byte blocks (2.3125 bpw) */
+} iq_format_t;
+
+typedef enum {
+    IQ_OK = 0,
+    IQ_ERR_NULL = 1,          /* a required pointer is NULL */
+    IQ_ERR_FORMAT = 2,        /* unknown format, or not supported by this call */
+    IQ_ERR_SHAPE = 3,         /* empty tensor, cols not a multiple of 256, size overflow */
+    IQ_ERR_GRID = 4,          /* grid_size outside [1, 2^index_bits], or (device) a grid
+                                 value that is not ternary (IQ1_S) / not finite and >= 0 (IQ2_XS) */
+    IQ_ERR_NONFINITE = 5,     /* (device) a weight is NaN or infinite */
+    IQ_ERR_IMPORTANCE = 6,    /* (device) an importance value is negative or not finite */
+    IQ_ERR_SCALE_RANGE = 7,   /* (device) super-block scale beyond fp16, or a pinned scale
+                                 that is negative, infinite or NaN */
+    IQ_ERR_ARG = 8,           /* a count out of range (top_c, G, C, sweeps, choice values) */
+    IQ_ERR_CODE = 9,          /* (device) a payload grid index beyond grid_size */
+    IQ_ERR_HIP = 10,          /* a HIP runtime call or kernel launch failed */
+    IQ_ERR_DEVICE = 11        /* the current device is not a gfx950 GPU */
+} iq_status_t;
+
+typedef struct {
+    int32_t block_elems;    /* 256 values per super-block */
+    int32_t block_bytes;    /* 50 (IQ1_S) or 74 (IQ2_XS) */
+    int32_t group;          /* 8 values per grid entry */
+    int32_t index_bits;     /* 11 (IQ1_S) or 9 (IQ2_XS) */
+    int32_t grid_max;       /* 2048 or 512 entries at most */
+    int32_t choice_groups;  /* choice groups per block: 8 sub-blocks of 32 (IQ1_S),
+                               16 scale groups of 16 (IQ2_XS) */
+    int32_t num_choices;    /* 16: IQ1_S k + 8*deltabit, IQ2_XS local scale k */
+} iq_format_info_t;
+
+/* Geometry of a format (#2450 review: 50/74-byte blocks; #3157: choice_groups
+ * and num_choices recorded per format).  `out` is a HOST pointer. */
+iq_status_t iq_format_info(iq_format_t fmt, iq_format_info_t* out);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* iq_status_str(iq_status_t st);
+
+/*
+ * iq_encode -- importance-weighted exhaustive codebook-search encode (#2450
+ * review: scale predictor, 16-way choice, lowest index wins; #2723: objective
+ * sum w*(x - s*(q+delta))^2 with the local scale and delta shared by the 4
+ * groups of a 32-value sub-block; #2525/#2512: IQ2_XS signs with the weakest
+ * element flipped for even parity).
+ *
+ *   w          [batch][rows][cols] fp32 weights.
+ *   importance NULL (uniform) or [batch][cols] fp32, finite and >= 0, one value
+ *              per input column (#2723).
+ *   grid       [grid_size][8] fp32.  IQ1_S: values in {-1, 0, +1};
+ *              IQ2_XS: finite magnitudes >= 0.
+ *   scales     NULL (predict d = fp16((amax/16.875)*0.61) for IQ1_S,
+ *              fp16((amax/155)*0.61) for IQ2_XS) or pinned fp16 bits
+ *              [batch][rows][cols/256] (#3197 static scales).
+ *   choices    NULL (search every choice) or forced per-choice-group picks
+ *              [batch][rows][cols/256][choice_groups] int32 in [0, 16) (#3157):
+ *              IQ1_S c = k + 8*deltabit, IQ2_XS c = k.  Only the grid entries
+ *              are searched then.
+ *   out        [batch][rows][cols/256][block_bytes] uint8.
+ *   status     one int32 (see the conventions above); required.
+ * Errors: IQ_ERR_NULL, IQ_ERR_FORMAT, IQ_ERR_SHAPE, IQ_ERR_GRID, IQ_ERR_DEVICE,
+ * IQ_ERR_HIP synchronously; the device codes through *status.
+ */
+iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t rows, int64_t cols,
+                      const float* importance, const float* grid, int32_t grid_size,
+                      const uint16_t* scales, const int32_t* choices, uint8_t* out,
+                      int32_t* status, hipStream_t stream);
+
+/*
+ * iq_dequant -- decode a payload to fp32 (#2450 review worked example:
+ * IQ1_S value = d*(2k+1)*(q + delta), delta = -1/8 when bit 15 is set;
+ * IQ2_XS value = d*(2k+1)*sign*q with the 8th sign of a group implied by even
+ * parity).  Every decoded value is exact in fp32.
+ *
+ *   packed  [batch][rows][cols/256][block_bytes] uint8.
+ *   grid    [grid_size][8] fp32 (the grid the payload was encoded with).
+ *   out     [batch][rows][cols] fp32.
+ *   status  one int32, required; IQ_ERR_CODE if an index is >= grid_size (that
+ *           group decodes to zeros).
+ */
+iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, int64_t rows,
+                       int64_t cols, const float* grid, int32_t grid_size, float* out,
+                       int32_t* status, hipStream_t stream);
+
+/*
+ * iq_encode_candidates -- the encode's sweep with a candidate epilogue, the
+ * input of the local-Hessian choice search (#3158 step 1, #3159 every-choice
+ * encode): for every IQ2_XS scale group (16 columns) of every 256-column block,
+ * the top_c local scales ordered by (weighted cost, k), each with its two
+ * codes and its error vector xhat - x over the 16 columns.
+ *
+ *   w           [rows][cols] fp32; importance NULL or [cols]; grid as iq_encode.
+ *   top_c       1..16.
+ *   cand_err    [rows][cols/256][16][top_c][16] fp32.
+ *   cand_choice [rows][cols/256][16][top_c] int32 (the local scale k).
+ *   cand_codes  NULL or [rows][cols/256][16][top_c][2] uint16 (index | mask<<9).
+ *   status      one int32, required.
+ * Only IQ_FMT_IQ2_XS is supported (IQ_ERR_FORMAT otherwise).
+ */
+iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, int64_t cols,
+                                 const float* importance, const float* grid, int32_t grid_size,
+                                 int32_t top_c, float* cand_err, int32_t* cand_choice,
+                                 uint16_t* cand_codes, int32_t* status, hipStream_t stream);
+
+/*
+ * iq_choice_search -- local-Hessian choice search of one 256-column block
+ * (#3158 steps 2-3; #3218 one launch per block): per row, give each group the
+ * candidate with the least e^T H_gg e, then visit the groups in ascending
+ * order `sweeps` times, each taking the candidate that most lowers the row's
+ * e^T H e with the other groups held, only on a strict improvement; ties go to
+ * the lowest candidate index.
+ *
+ *   H        [256][256] fp32, symmetric (the caller damps it).
+ *   cand_err [rows][G][C][256/G] fp32 candidate error vectors.
+ *   G        8 or 16 groups; C in 1..16 candidates; sweeps in 0..8.
+ *   picks    [rows][G] int32 output, candidate indices.
+ *   trace    NULL or [sweeps+1][rows][G] int32: picks after step 2 and after
+ *            every sweep.
+ */
+iq_status_t iq_choice_search(const float* H, const float* cand_err, int64_t rows, int32_t G,
+                             int32_t C, int32_t sweeps, int32_t* picks, int32_t* trace,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IQ_CODEC_H */

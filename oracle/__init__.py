@@ -80,8 +80,15 @@ def lib():
         L.orc_choice_replay.argtypes = [P, P, i32, i32, i32, P, ctypes.c_double,
                                         ctypes.POINTER(ctypes.c_double)]
         L.orc_choice_replay.restype = ctypes.c_int
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
 
 
 def _ptr(a):
@@ -150,6 +157,44 @@ def encode(fmt: str, w, grid, importance=None, scales=None, choices=None) -> np.
     if st:
         raise OracleError(ERRORS.get(st, "error %d" % st))
     return out.reshape(B, R, C // 256, nb)
+
+
+def encode_blocks(fmt: str, x, grid, imp=None, scales=None) -> np.ndarray:
+    """Encode independent 256-value blocks: x [n, 256], imp None or [n, 256]
+    (each block's own importance slice), scales None or fp16 bits [n].
+    Returns [n, block_bytes]."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, 256)
+    n = x.shape[0]
+    imp = None if imp is None else np.ascontiguousarray(imp, dtype=np.float32).reshape(n, 256)
+    grid = np.ascontiguousarray(grid, dtype=np.float32)
+    nb = BLOCK_BYTES[fmt]
+    out = np.zeros((n, nb), dtype=np.uint8)
+    sc = None if scales is None else np.ascontiguousarray(scales, dtype=np.uint16).reshape(n)
+    f = lib().orc_iq1s_encode if fmt == "iq1_s" else lib().orc_iq2xs_encode
+    st = f(_ptr(x), _ptr(imp), n, _ptr(grid), grid.shape[0], _ptr(sc), None, _ptr(out))
+    if st:
+        raise OracleError(ERRORS.get(st, "error %d" % st))
+    return out
+
+
+def block_errors(fmt: str, packed_blocks, x, grid, imp=None) -> np.ndarray:
+    """Weighted squared error per choice group of independent blocks:
+    packed_blocks [n, bytes], x [n, 256], imp None or [n, 256] -> [n, G]."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, 256)
+    n = x.shape[0]
+    nb = BLOCK_BYTES[fmt]
+    xhat = decode(fmt, np.ascontiguousarray(packed_blocks).reshape(n, 1, nb), grid).reshape(n, 256)
+    wt = np.ones((n, 256)) if imp is None else np.asarray(imp, dtype=np.float64).reshape(n, 256)
+    e = wt * (x.astype(np.float64) - xhat) ** 2
+    G = NUM_CHOICE_GROUPS[fmt]
+    return e.reshape(n, G, 256 // G).sum(axis=2)
+
+
+def predict_scales(fmt: str, w) -> np.ndarray:
+    """fp16 bits of the predicted scale of every 256-value block of w."""
+    x = np.ascontiguousarray(w, dtype=np.float32).reshape(-1, 256)
+    amax = np.abs(x).max(axis=1)
+    return np.array([predict_scale_bits(a, fmt) for a in amax], dtype=np.uint16)
 
 
 def decode(fmt: str, packed, grid, strict: bool = True) -> np.ndarray:

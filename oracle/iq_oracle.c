@@ -52,6 +52,7 @@
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -755,4 +756,10 @@ int orc_choice_replay(const float* H, const float* cand_row, int32_t G, int32_t 
 #undef CANDR
     *worst = wv;
     return fail;
+}
+
+/* Threads an OpenMP parallel region of this library uses. */
+int orc_num_threads(void)
+{
+    return omp_get_max_threads();
 }

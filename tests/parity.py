@@ -1,0 +1,53 @@
+"""Comparison of HIP payloads with the oracle's, under the tie rule.
+
+Codes must be bit-exact, except on floating-point ties: where a choice group
+(IQ1_S 32-value sub-block, IQ2_XS 16-value scale group) differs, the float64
+weighted error of the HIP pick must agree with the oracle's within 1e-6
+relative.  The scale bytes must always be bit-exact.
+"""
+
+import numpy as np
+
+import oracle
+
+TIE_RTOL = 1e-6
+
+
+def unit_codes(fmt, packed):
+    """Per choice group, the bytes that encode it: [n, G, k] uint8."""
+    p = np.ascontiguousarray(packed).reshape(-1, oracle.BLOCK_BYTES[fmt])
+    if fmt == "iq1_s":
+        low = p[:, 2:34].reshape(-1, 8, 4)
+        qh = p[:, 34:50].reshape(-1, 8, 2)
+        return np.concatenate([low, qh], axis=2)
+    codes = p[:, 2:66].reshape(-1, 16, 4)
+    nib = p[:, 66:74]
+    scales = np.stack([nib & 15, nib >> 4], axis=2).reshape(-1, 16, 1)
+    return np.concatenate([codes, scales.astype(np.uint8)], axis=2)
+
+
+def compare_payloads(fmt, got, ref, x, grid, imp=None, max_tie_frac=0.005):
+    """got/ref [n, bytes]; x [n, 256]; imp None or [n, 256].  Returns the number
+    of tie units; raises AssertionError on a real mismatch."""
+    nb = oracle.BLOCK_BYTES[fmt]
+    got = np.ascontiguousarray(got).reshape(-1, nb)
+    ref = np.ascontiguousarray(ref).reshape(-1, nb)
+    assert got.shape == ref.shape
+    np.testing.assert_array_equal(got[:, :2], ref[:, :2], err_msg="scale bytes differ")
+    diff = np.any(unit_codes(fmt, got) != unit_codes(fmt, ref), axis=2)     # [n, G]
+    nd = int(diff.sum())
+    if nd == 0:
+        return 0
+    rows = np.nonzero(diff.any(axis=1))[0]
+    xi = np.asarray(x, dtype=np.float32).reshape(-1, 256)[rows]
+    ii = None if imp is None else np.asarray(imp, dtype=np.float32).reshape(-1, 256)[rows]
+    eg = oracle.block_errors(fmt, got[rows], xi, grid, ii)
+    er = oracle.block_errors(fmt, ref[rows], xi, grid, ii)
+    d = diff[rows]
+    rel = np.abs(eg - er) / np.maximum(er, 1e-300)
+    worst = float(rel[d].max())
+    assert worst <= TIE_RTOL, (
+        "%d differing units, worst relative error gap %.3g (> %g); first block %d"
+        % (nd, worst, TIE_RTOL, int(rows[0])))
+    assert nd <= max_tie_frac * diff.size, "%d tie units of %d" % (nd, diff.size)
+    return nd

@@ -1,0 +1,91 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/iq_codec.h declares, reports format geometry, and rejects bad
+arguments synchronously before any device work (no GPU needed for those)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "iq_codec.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(iq_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import ggml_iq_codebook_amd as iq
+    return iq.load(build_if_missing=True)
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "iq_choice_search", "iq_dequant", "iq_encode", "iq_encode_candidates",
+        "iq_format_info", "iq_status_str"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_format_info(lib):
+    import ggml_iq_codebook_amd as iq
+    assert iq.format_info("iq1_s") == dict(block_elems=256, block_bytes=50, group=8, index_bits=11,
+                                           grid_max=2048, choice_groups=8, num_choices=16)
+    assert iq.format_info("iq2_xs") == dict(block_elems=256, block_bytes=74, group=8, index_bits=9,
+                                            grid_max=512, choice_groups=16, num_choices=16)
+    info = iq._FormatInfo()
+    assert lib.iq_format_info(7, ctypes.byref(info)) == 2          # IQ_ERR_FORMAT
+    assert lib.iq_format_info(0, None) == 1                         # IQ_ERR_NULL
+
+
+def test_status_strings(lib):
+    for code in range(12):
+        assert lib.iq_status_str(code)
+    assert lib.iq_status_str(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x100000)      # never dereferenced: validation fails before any device access
+
+
+def test_encode_argument_errors_need_no_gpu(lib):
+    enc = lib.iq_encode
+    # fmt, w, batch, rows, cols, imp, grid, grid_size, scales, choices, out, status, stream
+    assert enc(5, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 2
+    assert enc(0, None, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 1
+    assert enc(0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None, None) == 1
+    assert enc(0, FAKE, 1, 1, 200, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
+    assert enc(0, FAKE, 1, 0, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
+    assert enc(0, FAKE, 0, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
+    assert enc(0, FAKE, 1, 1 << 40, 1 << 20, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
+    assert enc(0, FAKE, 1, 1, 256, None, FAKE, 0, None, None, FAKE, FAKE, None) == 4
+    assert enc(0, FAKE, 1, 1, 256, None, FAKE, 2049, None, None, FAKE, FAKE, None) == 4
+    assert enc(1, FAKE, 1, 1, 256, None, FAKE, 513, None, None, FAKE, FAKE, None) == 4
+    assert enc(0, P(0x100004), 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 8
+
+
+def test_other_entry_points_argument_errors_need_no_gpu(lib):
+    deq = lib.iq_dequant
+    assert deq(0, None, 1, 1, 256, FAKE, 16, FAKE, FAKE, None) == 1
+    assert deq(0, FAKE, 1, 1, 100, FAKE, 16, FAKE, FAKE, None) == 3
+    assert deq(1, FAKE, 1, 1, 256, FAKE, 600, FAKE, FAKE, None) == 4
+    cand = lib.iq_encode_candidates
+    assert cand(0, FAKE, 1, 256, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 2
+    assert cand(1, FAKE, 1, 256, None, FAKE, 16, 0, FAKE, FAKE, None, FAKE, None) == 8
+    assert cand(1, FAKE, 1, 256, None, FAKE, 16, 17, FAKE, FAKE, None, FAKE, None) == 8
+    assert cand(1, FAKE, 1, 250, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 3
+    cs = lib.iq_choice_search
+    assert cs(FAKE, FAKE, 4, 12, 8, 2, FAKE, None, None) == 8
+    assert cs(FAKE, FAKE, 4, 16, 0, 2, FAKE, None, None) == 8
+    assert cs(FAKE, FAKE, 4, 16, 17, 2, FAKE, None, None) == 8
+    assert cs(FAKE, FAKE, 4, 16, 8, 9, FAKE, None, None) == 8
+    assert cs(FAKE, FAKE, 0, 16, 8, 2, FAKE, None, None) == 3
+    assert cs(None, FAKE, 4, 16, 8, 2, FAKE, None, None) == 1

@@ -1,0 +1,264 @@
+"""HIP encode / decode parity against the oracle, through the C-ABI.
+
+Every test runs the HIP kernels of libiqcodec.so on a gfx950 GPU and compares
+with the CPU oracle on the same seeded inputs: bit-exact scales, bit-exact
+codes except on floating-point ties (then the float64 weighted errors agree
+within 1e-6 relative), bit-exact decoded values.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import compare_payloads
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # the CPU suite deselects these with -m "not gpu"
+    pytest.skip("no GPU", allow_module_level=True)
+
+import ggml_iq_codebook_amd as iq  # noqa: E402
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write("\n[gpu] %s\n" % request.node.nodeid)
+    sys.__stderr__.flush()
+    yield
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _block_imp(imp, B, R, C):
+    if imp is None:
+        return None
+    imp = np.asarray(imp, np.float32).reshape(B, C)
+    return np.broadcast_to(imp[:, None, :], (B, R, C)).reshape(-1, 256)
+
+
+def _gpu_encode(fmt, w, grid, imp=None, **kw):
+    out = iq.encode(_dev(w), _dev(grid), None if imp is None else _dev(imp), fmt=fmt, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check_full(fmt, w, grid, imp=None):
+    B, R, C = w.shape
+    got = _gpu_encode(fmt, w, grid, imp)
+    ref = oracle.encode(fmt, w, grid, imp)
+    return compare_payloads(fmt, got, ref, w.reshape(-1, 256), grid, _block_imp(imp, B, R, C))
+
+
+def test_library_is_the_hip_build():
+    L = iq.load(build_if_missing=False)
+    assert L._name.endswith("libiqcodec.so")
+    assert torch.cuda.get_device_properties(0).gcnArchName.startswith("gfx950")
+
+
+@pytest.mark.parametrize("uniform", [None, "ones"])
+def test_c1_iq1s_small_matches_oracle(uniform):
+    c = workloads.c1_iq1s_small()
+    imp = None if uniform is None else np.ones((1, 256), np.float32)
+    _check_full("iq1_s", c["w"], c["grid"], imp)
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("shape,n", [((2, 13, 768), None), ((1, 5, 256), 1000), ((1, 3, 512), 37),
+                                     ((1, 2, 256), 1), ((3, 1, 1024), 33)])
+def test_ragged_shapes_and_grid_sizes(fmt, shape, n):
+    gmax = 2048 if fmt == "iq1_s" else 512
+    n = min(n or gmax, gmax)
+    grid = workloads.iq1s_grid(n, seed=3) if fmt == "iq1_s" else workloads.iq2xs_grid(n, seed=3)
+    w = workloads.student_t_weight(shape, 17)
+    imp = workloads.lognormal_importance((shape[0], shape[2]), 18)
+    _check_full(fmt, w, grid, imp)
+
+
+def test_c3_iq2xs_rows_match_oracle():
+    c = workloads.c3_iq2xs_4096()
+    w = c["w"][:, :24, :]
+    _check_full("iq2_xs", w, c["grid"], c["importance"])
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+def test_uniform_importance_reproduces_unweighted_payload(fmt):
+    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    w = workloads.normal_weight((1, 32, 512), 5)
+    p0 = _gpu_encode(fmt, w, grid)
+    for c in (1.0, 4.0, 0.125):
+        p = _gpu_encode(fmt, w, grid, np.full((1, 512), c, np.float32))
+        np.testing.assert_array_equal(p, p0)
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+def test_dequant_is_exact(fmt):
+    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    w = workloads.normal_weight((2, 7, 512), 6)
+    p = oracle.encode(fmt, w, grid)
+    out = iq.dequant(_dev(p), _dev(grid), fmt=fmt)
+    torch.cuda.synchronize()
+    want = oracle.decode(fmt, p, grid)
+    np.testing.assert_array_equal(out.cpu().numpy().astype(np.float64), want)
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+def test_decode_reencode_round_trip_under_pinned_scales(fmt):
+    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    w = workloads.normal_weight((1, 16, 512), 7)
+    imp = workloads.lognormal_importance((1, 512), 8)
+    p = _gpu_encode(fmt, w, grid, imp)
+    xhat = iq.dequant(_dev(p), _dev(grid), fmt=fmt)
+    d = torch.from_numpy(p[..., 0].astype(np.int16) | (p[..., 1].astype(np.int16) << 8)).to(DEV)
+    p2 = iq.encode(xhat, _dev(grid), _dev(imp), fmt=fmt, scales=d.contiguous())
+    x2 = iq.dequant(p2, _dev(grid), fmt=fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(x2, xhat)
+    same = (p2.cpu().numpy().reshape(-1, p.shape[-1]) == p.reshape(-1, p.shape[-1])).all(axis=1)
+    assert same.mean() >= 0.9
+    # pinned scales match the oracle's pinned encode
+    ref = oracle.encode(fmt, xhat.cpu().numpy(), grid, imp, scales=d.cpu().numpy().view(np.uint16))
+    compare_payloads(fmt, p2.cpu().numpy(), ref, xhat.cpu().numpy().reshape(-1, 256), grid,
+                     _block_imp(imp, 1, 16, 512))
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+def test_forced_choices_match_oracle(fmt):
+    grid = workloads.iq1s_grid(512) if fmt == "iq1_s" else workloads.iq2xs_grid(256)
+    w = workloads.normal_weight((1, 6, 512), 9)
+    imp = workloads.lognormal_importance((1, 512), 10)
+    G = 8 if fmt == "iq1_s" else 16
+    ch = np.random.default_rng(11).integers(0, 16, (1, 6, 2, G)).astype(np.int32)
+    got = _gpu_encode(fmt, w, grid, imp, choices=_dev(ch))
+    ref = oracle.encode(fmt, w, grid, imp, choices=ch)
+    compare_payloads(fmt, got, ref, w.reshape(-1, 256), grid, _block_imp(imp, 1, 6, 512))
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+def test_determinism_and_launch_partition_invariance(fmt):
+    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    w = workloads.normal_weight((1, 40, 1024), 12)
+    imp = workloads.lognormal_importance((1, 1024), 13)
+    a = _gpu_encode(fmt, w, grid, imp)
+    b = _gpu_encode(fmt, w, grid, imp)
+    np.testing.assert_array_equal(a, b)
+    parts = [_gpu_encode(fmt, w[:, r0:r0 + 7], grid, imp) for r0 in range(0, 40, 7)]
+    np.testing.assert_array_equal(np.concatenate(parts, axis=1), a)
+
+
+def test_zero_and_underflow_blocks():
+    for fmt in ("iq1_s", "iq2_xs"):
+        grid = workloads.iq1s_grid(64) if fmt == "iq1_s" else workloads.iq2xs_grid(64)
+        w = workloads.normal_weight((1, 3, 256), 81)
+        w[0, 0] = 0.0
+        w[0, 1] *= 1e-7
+        got = _gpu_encode(fmt, w, grid)
+        np.testing.assert_array_equal(got, oracle.encode(fmt, w, grid))
+        assert not got[0, 0].any() and not got[0, 1].any()
+
+
+def _status_of(fn):
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    fn(st)
+    torch.cuda.synchronize()
+    return int(st.item())
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+def test_device_data_errors_are_reported(fmt):
+    grid = workloads.iq1s_grid(64) if fmt == "iq1_s" else workloads.iq2xs_grid(64)
+    w = workloads.normal_weight((1, 4, 512), 91)
+    bad = w.copy()
+    bad[0, 2, 300] = np.nan
+    out = torch.full((1, 4, 2, iq.BLOCK_BYTES[fmt]), 7, dtype=torch.uint8, device=DEV)
+    st = _status_of(lambda s: iq.encode(_dev(bad), _dev(grid), fmt=fmt, out=out, status=s, check=False))
+    assert st == 5                                   # IQ_ERR_NONFINITE
+    o = out.cpu().numpy()
+    assert not o[0, 2, 1].any()                      # the bad block is zeroed
+    np.testing.assert_array_equal(np.delete(o.reshape(8, -1), 5, axis=0),
+                                  np.delete(oracle.encode(fmt, w, grid).reshape(8, -1), 5, axis=0))
+    imp = np.ones((1, 512), np.float32)
+    imp[0, 17] = -1.0
+    st = _status_of(lambda s: iq.encode(_dev(w), _dev(grid), _dev(imp), fmt=fmt, status=s, check=False))
+    assert st == 6                                   # IQ_ERR_IMPORTANCE
+    st = _status_of(lambda s: iq.encode(_dev(w * 1e9), _dev(grid), fmt=fmt, status=s, check=False))
+    assert st == 7                                   # IQ_ERR_SCALE_RANGE
+    g2 = grid.copy()
+    g2[3, 4] = 2.0 if fmt == "iq1_s" else -1.0
+    st = _status_of(lambda s: iq.encode(_dev(w), _dev(g2), fmt=fmt, status=s, check=False))
+    assert st == 4                                   # IQ_ERR_GRID
+    with pytest.raises(iq.IQError) as ei:
+        iq.encode(_dev(bad), _dev(grid), fmt=fmt)
+    assert ei.value.code == 5
+
+
+def test_synchronous_argument_errors():
+    grid = _dev(workloads.iq1s_grid(64))
+    w = _dev(workloads.normal_weight((1, 4, 256), 1))
+    with pytest.raises(iq.IQError) as ei:
+        iq.encode(_dev(workloads.normal_weight((1, 4, 200), 1)), grid)
+    assert ei.value.code == 3                        # IQ_ERR_SHAPE
+    big = np.concatenate([workloads.iq1s_grid(2048), workloads.iq1s_grid(1)])
+    with pytest.raises(iq.IQError) as ei:
+        iq.encode(w, _dev(big))
+    assert ei.value.code == 4                        # IQ_ERR_GRID
+    with pytest.raises(iq.IQError) as ei:
+        iq.encode_candidates(w[0], grid, fmt="iq1_s")
+    assert ei.value.code == 2                        # IQ_ERR_FORMAT
+
+
+def test_dequant_reports_indices_beyond_the_grid():
+    grid = workloads.iq1s_grid(1500)
+    p = oracle.encode("iq1_s", workloads.normal_weight((1, 1, 256), 72), grid)
+    p[0, 0, 0, 34 + 2 * 3 + 1] |= 0x0E
+    out = torch.empty((1, 1, 256), dtype=torch.float32, device=DEV)
+    st = _status_of(lambda s: iq.dequant(_dev(p), _dev(grid), fmt="iq1_s", out=out, status=s,
+                                         check=False))
+    assert st == 9                                   # IQ_ERR_CODE
+    want = oracle.decode("iq1_s", p, grid, strict=False).reshape(256)
+    np.testing.assert_array_equal(out.cpu().numpy().reshape(256).astype(np.float64), want)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled against the oracle
+# ---------------------------------------------------------------------------
+
+
+def _sampled(fmt, cfg, nsamp, seed):
+    w, grid, imp = cfg["w"], cfg["grid"], cfg["importance"]
+    B, R, C = w.shape
+    got = _gpu_encode(fmt, w, grid, imp).reshape(-1, iq.BLOCK_BYTES[fmt])
+    nblk = got.shape[0]
+    # every scale is checked against the closed-form predictor
+    np.testing.assert_array_equal(got[:, 0].astype(np.uint16) | (got[:, 1].astype(np.uint16) << 8),
+                                  oracle.predict_scales(fmt, w))
+    rng = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([[0, nblk - 1], rng.integers(0, nblk, nsamp)]))
+    x = w.reshape(-1, 256)[idx]
+    ib = None if imp is None else _block_imp(imp, B, R, C)[idx]
+    ref = oracle.encode_blocks(fmt, x, grid, ib)
+    return got, compare_payloads(fmt, got[idx], ref, x, grid, ib)
+
+
+def test_c2_iq1s_4096_sampled():
+    _sampled("iq1_s", workloads.c2_iq1s_4096(), 384, 21)
+
+
+def test_c3_iq2xs_4096_sampled():
+    _sampled("iq2_xs", workloads.c3_iq2xs_4096(), 768, 22)
+
+
+def test_c4_moe_batch_equals_per_expert_calls_and_oracle():
+    cfg = workloads.c4_moe_batch()
+    got, _ = _sampled("iq1_s", cfg, 384, 23)
+    got = got.reshape(16, 1536, 16, 50)
+    for e in (0, 7, 15):
+        one = _gpu_encode("iq1_s", cfg["w"][e:e + 1], cfg["grid"], cfg["importance"][e:e + 1])
+        np.testing.assert_array_equal(one[0], got[e])

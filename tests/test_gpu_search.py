@@ -1,0 +1,134 @@
+"""HIP candidate emission and local-Hessian choice search against the oracle.
+
+Candidates: per IQ2_XS scale group, the top-C local scales in (cost, k) order
+with their error vectors; the HIP and oracle lists must agree exactly except
+where near-tied costs swap (then the float64 weighted errors agree within
+1e-6 relative).  Choice search: the HIP and oracle searches consume the same
+candidate array; rows whose decision traces differ must pass the oracle's
+replay check (every HIP decision optimal within 1e-6 of the row's objective).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import ggml_iq_codebook_amd as iq  # noqa: E402
+
+DEV = "cuda:0"
+REPLAY_TOL = 1e-6
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write("\n[gpu] %s\n" % request.node.nodeid)
+    sys.__stderr__.flush()
+    yield
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _check_candidates(w, grid, imp, top_c):
+    """w [rows, 256]."""
+    err, ch, codes = iq.encode_candidates(_dev(w), _dev(grid), None if imp is None else _dev(imp),
+                                          top_c=top_c, codes=True)
+    torch.cuda.synchronize()
+    err = err.cpu().numpy().reshape(-1, 16, top_c, 16)
+    ch = ch.cpu().numpy().reshape(-1, 16, top_c)
+    codes = codes.cpu().numpy().view(np.uint16).reshape(-1, 16, top_c, 2)
+    rerr, rch, rcodes = oracle.iq2xs_candidates(w[None], grid, None if imp is None else imp[None],
+                                                top_c=top_c)
+    same = (ch == rch)
+    wt = np.ones(256) if imp is None else imp.astype(np.float64).reshape(256)
+    wt = wt.reshape(16, 16)
+    e_got = (wt[None, :, None, :] * err.astype(np.float64) ** 2).sum(axis=3)
+    e_ref = (wt[None, :, None, :] * rerr.astype(np.float64) ** 2).sum(axis=3)
+    # where the choice agrees, codes and error vectors are bit-exact, or the
+    # entries are a tie
+    ok = same & np.all(codes == rcodes, axis=3)
+    np.testing.assert_array_equal(err[ok], rerr[ok])
+    bad = ~ok
+    if bad.any():
+        rel = np.abs(e_got[bad] - e_ref[bad]) / np.maximum(e_ref[bad], 1e-300)
+        assert rel.max() <= 1e-6, "candidate mismatch beyond ties: %g" % rel.max()
+        assert bad.mean() < 0.01
+    return err, ch
+
+
+def test_candidates_small_rows():
+    grid = workloads.iq2xs_grid()
+    w = workloads.student_t_weight((40, 256), 31)
+    imp = workloads.lognormal_importance((256,), 32)
+    _check_candidates(w, grid, imp, 8)
+    _check_candidates(w[:5], grid, None, 16)
+    _check_candidates(w[:3], workloads.iq2xs_grid(77), imp, 1)
+
+
+def test_candidates_zero_block():
+    grid = workloads.iq2xs_grid()
+    w = workloads.student_t_weight((3, 256), 33)
+    w[1] = 0.0
+    err, ch = _check_candidates(w, grid, None, 8)
+    assert np.all(ch[16:32] == np.arange(8))
+
+
+def _search_parity(H, cand, sweeps=2):
+    picks, trace = iq.choice_search(_dev(H), _dev(cand), sweeps=sweeps, trace=True)
+    torch.cuda.synchronize()
+    picks = picks.cpu().numpy()
+    trace = trace.cpu().numpy()
+    np.testing.assert_array_equal(picks, trace[-1])
+    rpicks, rtrace = oracle.choice_search(H, cand, sweeps=sweeps)
+    differ = np.nonzero(np.any(trace != rtrace, axis=(0, 2)))[0]
+    for r in differ:
+        fail, worst = oracle.choice_replay(H, cand[r], trace[:, r, :], REPLAY_TOL)
+        assert fail == 0, "row %d: decision %d off by %.3g of J" % (r, fail - 1, worst)
+    assert len(differ) <= max(2, 0.01 * cand.shape[0])
+    return trace, rtrace, len(differ)
+
+
+@pytest.mark.parametrize("G,C,rows", [(16, 8, 37), (8, 4, 20), (16, 16, 9), (8, 16, 11), (16, 1, 5)])
+def test_choice_search_random_candidates(G, C, rows):
+    H = workloads.block_hessian(256, 7)
+    rng = np.random.default_rng(G * 100 + C)
+    cand = (0.01 * rng.standard_normal((rows, G, C, 256 // G))).astype(np.float32)
+    _search_parity(H, cand)
+    _search_parity(H, cand, sweeps=0)
+    _search_parity(H, cand, sweeps=3)
+
+
+def test_identity_hessian_keeps_the_encoders_own_choices():
+    grid = workloads.iq2xs_grid()
+    w = workloads.student_t_weight((16, 256), 141)
+    err, ch, _ = iq.encode_candidates(_dev(w), _dev(grid), None, top_c=8)
+    picks, trace = iq.choice_search(torch.eye(256, device=DEV), err.reshape(16, 16, 8, 16).contiguous(),
+                                    trace=True)
+    torch.cuda.synchronize()
+    assert int(trace.abs().sum().item()) == 0
+
+
+def test_c5_choice_search_full():
+    cfg = workloads.c5_choice_search()
+    H, w, grid, imp = cfg["H"], cfg["w"][0], cfg["grid"], cfg["importance"][0]
+    err, ch, _ = iq.encode_candidates(_dev(w), _dev(grid), _dev(imp), top_c=8)
+    cand = err.reshape(4096, 16, 8, 16).contiguous()
+    # candidates of a sample of rows against the oracle
+    rows = np.random.default_rng(5).integers(0, 4096, 64)
+    _check_candidates(w[rows], grid, imp, 8)
+    cand_np = cand.cpu().numpy()
+    trace, rtrace, nd = _search_parity(H, cand_np)
+    # the sweeps change picks on this workload (a search that skipped them fails)
+    assert np.any(trace[0] != trace[2])
+    J = [oracle.choice_objective(H, cand_np, trace[s]) for s in range(3)]
+    assert np.all(J[1] <= J[0] * (1 + 1e-6)) and np.all(J[2] <= J[1] * (1 + 1e-6))
