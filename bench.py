@@ -58,18 +58,70 @@ WORKLOADS = {
 }
 
 KERNEL_SOURCES = {
-    "iq1_s": "ggml_iq_codebook_amd/csrc/iq1s_encode.hip",
-    "iq2_xs": "ggml_iq_codebook_amd/csrc/iq2xs_encode.hip",
+    "iq1_s": ["ggml_iq_codebook_amd/csrc/iq1s_encode.hip",
+              "ggml_iq_codebook_amd/csrc/device_common.hpp"],
+    "iq2_xs": ["ggml_iq_codebook_amd/csrc/iq2xs_encode.hip",
+               "ggml_iq_codebook_amd/csrc/device_common.hpp"],
 }
+KERNEL_NAMES = {"iq1_s": "iq1s_encode_kernel", "iq2_xs": "iq2xs_kernel<false>"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(rels):
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_kib(csv_path, kernel_substr, counter):
+    """Mean per-dispatch value of a rocprofv3 counter for the matching kernel."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit("no %s samples for %s in %s" % (counter, kernel_substr, csv_path))
+    return sum(vals) / len(vals), len(vals)
+
+
+def record_traffic(name, fmt, pmc_dir):
+    """Turn the FETCH_SIZE / WRITE_SIZE counter runs of the encode and of a plain
+    256 MiB copy into HBM bytes per launch, written to profiles/traffic_<name>.json.
+
+    pmc_dir holds pmc_FETCH_SIZE/enc_counter_collection.csv,
+    pmc_WRITE_SIZE/enc_counter_collection.csv and the copy runs
+    pmc_copy_FETCH_SIZE/copy_counter_collection.csv, pmc_copy_WRITE_SIZE/...
+    The copy reads and writes exactly 268435456 bytes; each counter is scaled by
+    known bytes / (counted KiB * 1024) of that copy."""
+    kname = KERNEL_NAMES[fmt].split("<")[0]
+    known = 64 * 1024 * 1024 * 4
+    f_enc, nf = _counter_kib(os.path.join(pmc_dir, "pmc_FETCH_SIZE", "enc_counter_collection.csv"),
+                             kname, "FETCH_SIZE")
+    w_enc, nw = _counter_kib(os.path.join(pmc_dir, "pmc_WRITE_SIZE", "enc_counter_collection.csv"),
+                             kname, "WRITE_SIZE")
+    f_cp, _ = _counter_kib(os.path.join(pmc_dir, "pmc_copy_FETCH_SIZE", "copy_counter_collection.csv"),
+                           "copyBuffer", "FETCH_SIZE")
+    w_cp, _ = _counter_kib(os.path.join(pmc_dir, "pmc_copy_WRITE_SIZE", "copy_counter_collection.csv"),
+                           "copyBuffer", "WRITE_SIZE")
+    ff, wf = known / (f_cp * 1024), known / (w_cp * 1024)
+    rec = {
+        "kernel": KERNEL_NAMES[fmt],
+        "kernel_source_sha": source_sha(KERNEL_SOURCES[fmt]),
+        "fetch_kib_per_launch": f_enc, "fetch_dispatches": nf,
+        "write_kib_per_launch": w_enc, "write_dispatches": nw,
+        "copy_known_bytes": known, "copy_fetch_kib": f_cp, "copy_write_kib": w_cp,
+        "fetch_scale": ff, "write_scale": wf,
+        "hbm_bytes_per_launch": int(round(f_enc * 1024 * ff + w_enc * 1024 * wf)),
+    }
+    out = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def traffic_for(name, sha):
@@ -96,9 +148,9 @@ def cpu_baseline(cfg, fmt, budget_s=15.0):
         t0 = time.perf_counter()
         oracle.encode(fmt, sub, grid, None if imp is None else imp[:1])
         dt = time.perf_counter() - t0
-        if dt >= budget_s / 3 or rows * 2 > w.shape[1]:
+        if dt >= 0.6 * budget_s or rows >= w.shape[1]:
             break
-        rows = min(w.shape[1], max(rows * 2, int(rows * budget_s / 2 / max(dt, 1e-3))))
+        rows = min(w.shape[1], max(rows * 2, int(rows * budget_s / max(dt, 1e-3))))
     nbytes = sub.size * 4
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "first %d rows x %d cols of the workload (%d blocks), %.1f s"
@@ -109,12 +161,21 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (for counter calibration) and exit")
+    ap.add_argument("--record-traffic", metavar="PMC_DIR",
+                    help="convert rocprofv3 counter CSVs under PMC_DIR into "
+                         "profiles/traffic_<kernel>_<config>.json and exit (no GPU needed)")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        fmt = "iq2_xs" if args.config == "c3" else "iq1_s"
+        record_traffic("%s_encode_%s" % (fmt.replace("_", ""), args.config), fmt,
+                       args.record_traffic)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the encode shards by rows/experts with no "

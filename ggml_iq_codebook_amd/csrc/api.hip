@@ -94,10 +94,10 @@ iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t ro
                       int32_t* status, hipStream_t stream)
 {
     if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
-    if (!w || !grid || !out || !status) return IQ_ERR_NULL;
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
+    if (!w || !grid || !out || !status) return IQ_ERR_NULL;
     const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
     if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
@@ -117,10 +117,10 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
                        int32_t* status, hipStream_t stream)
 {
     if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
-    if (!packed || !grid || !out || !status) return IQ_ERR_NULL;
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
+    if (!packed || !grid || !out || !status) return IQ_ERR_NULL;
     const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
     if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
     if (!aligned(grid, 16) || !aligned(out, 16) || !aligned(status, 4)) return IQ_ERR_ARG;
@@ -136,10 +136,10 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, 
 {
     if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
     if (fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
-    if (!w || !grid || !cand_err || !cand_choice || !status) return IQ_ERR_NULL;
     iqk::BlockGeom g;
     iq_status_t st = geometry(1, rows, cols, &g);
     if (st) return st;
+    if (!w || !grid || !cand_err || !cand_choice || !status) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > 512) return IQ_ERR_GRID;
     if (top_c < 1 || top_c > 16) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
@@ -156,8 +156,8 @@ iq_status_t iq_choice_search(const float* H, const float* cand_err, int64_t rows
                              int32_t C, int32_t sweeps, int32_t* picks, int32_t* trace,
                              hipStream_t stream)
 {
-    if (!H || !cand_err || !picks) return IQ_ERR_NULL;
     if (rows <= 0 || rows > (INT64_C(1) << 34)) return IQ_ERR_SHAPE;
+    if (!H || !cand_err || !picks) return IQ_ERR_NULL;
     if ((G != 8 && G != 16) || C < 1 || C > 16 || sweeps < 0 || sweeps > 8) return IQ_ERR_ARG;
     if (!aligned(H, 4) || !aligned(cand_err, 4) || !aligned(picks, 4) || (trace && !aligned(trace, 4)))
         return IQ_ERR_ARG;

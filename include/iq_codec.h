@@ -21,11 +21,14 @@
  *     allocates and owns every buffer.  The library allocates no device memory.
  *   - Calls are asynchronous and ordered on `stream` (NULL = the null stream).
  *     Argument and shape errors are returned synchronously before any launch,
- *     and nothing is written.  Data errors found on the device (non-finite
- *     weight, bad importance, scale out of fp16 range, payload index beyond the
- *     grid) are written to `*status` with an atomic compare-and-swap from 0, so
- *     the first code to land sticks; the library never clears `*status`: the
- *     caller zeroes it.  Blocks with a data error are written as zeros.
+ *     and nothing is written; the format is checked first, then the shape,
+ *     then the pointers, then sizes and alignment (fp32 arrays read or
+ *     written as vectors need 16-byte alignment, 16-bit arrays 2-byte
+ *     alignment).  Data errors found on the device (non-finite weight, bad
+ *     importance, scale out of fp16 range, payload index beyond the grid) are
+ *     written to `*status` with an atomic compare-and-swap from 0, so the first
+ *     code to land sticks; the library never clears `*status`: the caller
+ *     zeroes it.  Blocks with a data error are written as zeros.
  *   - Concurrent calls that share `status` or an output buffer race.
  *   - Layouts are row-major and contiguous.  Weights are fp32 [batch][rows][cols]
  *     with cols a positive multiple of 256; a 256-value block is cols/256 of a
@@ -99,7 +102,8 @@ const char* iq_status_str(iq_status_t st);
  *   choices    NULL (search every choice) or forced per-choice-group picks
  *              [batch][rows][cols/256][choice_groups] int32 in [0, 16) (#3157):
  *              IQ1_S c = k + 8*deltabit, IQ2_XS c = k.  Only the grid entries
- *              are searched then.
+ *              are searched then; a value outside [0, 16) zeroes its block and
+ *              sets *status = IQ_ERR_ARG.
  *   out        [batch][rows][cols/256][block_bytes] uint8.
  *   status     one int32 (see the conventions above); required.
  * Errors: IQ_ERR_NULL, IQ_ERR_FORMAT, IQ_ERR_SHAPE, IQ_ERR_GRID, IQ_ERR_DEVICE,
