@@ -1,5 +1,5 @@
 // iq1s_encode.hip -- importance-weighted exhaustive codebook search for IQ1_S
-// on gfx950.
+// on gfx950, with the weighted dot products on the matrix cores.
 //
 // The format (NVIDIA Model-Optimizer, "Add IQ tests and release notes" #2450,
 // code review; "Weight the IQ1 encoders by the square root of GPTQ's Hessian
@@ -9,24 +9,27 @@
 // local scale s = d*(2k+1), k = 0..7, and delta = +-1/8.  The codes minimise
 // sum w*(x - s*(q+delta))^2, lowest index winning ties.
 //
-// Kernel layout (MI355X-first, not the CUDA prior art's one-block-per-row):
-//  * one lane = one 8-value group, a 64-lane wave = two 256-value blocks,
-//    a 512-thread workgroup = 16 blocks; weights and importance are read once,
-//    two float4 per lane, fully coalesced;
-//  * the grid (64 KiB for 2048 entries) is staged once per workgroup in LDS
-//    (160 KiB per CU on CDNA4) and read as wave-uniform broadcasts;
-//  * per (group, entry) the three weighted dot products A = sum wx*q,
-//    M = sum w*q, N = sum w*|q| give U(delta) = sum w*(q+delta)^2 and
-//    V(delta) = sum wx*(q+delta); the key of local scale s_k is
-//    s_k*U - 2V (the error divided by s_k, minus a constant), one FMA each;
-//  * the 16 per-choice minima are tracked by value only (v_min3 over two
-//    entries); the 32-entry chunk that last lowered each minimum is recorded,
-//    and after the sub-block's choice is known each lane rescans only its
-//    winning chunk with the identical instruction sequence to recover the
-//    lowest entry index whose key equals the minimum;
-//  * the 4 lanes of a sub-block sum their minima with xor-shuffles (identical
-//    in every lane), pick the lowest-cost choice, and the block is packed in
-//    LDS and stored as 16-bit words.
+// For a group and a grid entry the error is, up to a constant,
+//   s^2 * U(delta) - 2 s * V(delta),  U = N + 2 delta M + delta^2 W,
+//   V = A + delta B,  A = sum wx*q, M = sum w*q, N = sum w*|q|.
+// A, M and N for 16 grid entries x 16 groups are three small products
+// [16 entries x 8] x [8 x 16 groups], run as v_mfma_f32_16x16x32_bf16: the
+// ternary entries are exact in bf16, and the group side (w*x and w) is split
+// into three bf16 parts whose sum is exactly the fp32 value, so the products
+// are exact and only the fp32 accumulation rounds.  The VALU then forms U, V
+// and the 16 choice keys s_k*U - 2V (one FMA each) and keeps value-only
+// minima (v_min3 over two entries).
+//
+// Layout: a wave owns 16 groups (half a block): matrix column j = lane%16 is
+// group j; the lane's four accumulator rows are 4*(lane/16)+r of every
+// 16-entry tile, so the four lanes of a column cover disjoint quarters of the
+// grid.  A 512-thread workgroup runs 8 waves = 4 blocks per pass and 4 passes
+// (16 blocks), with the grid staged once in LDS as bf16 (q and |q|, 64 KiB).
+// Index recovery: each lane records the 128-entry chunk that last lowered each
+// of its 16 minima; once the sub-block's choice is fixed, the lane rescans its
+// 32 entries of that chunk on the VALU (fp32 dot products) and takes the lowest
+// entry of least key; the four lanes of a column then keep the one whose
+// matrix-core minimum is least (lowest index on equal minima).
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -35,11 +38,17 @@
 namespace iqk {
 namespace {
 
-constexpr int kBlocksPerWave = 2;
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
 constexpr int kWavesPerWG = 8;
-constexpr int kBlocksPerWG = kBlocksPerWave * kWavesPerWG;   // 16
-constexpr int kThreads = kWave * kWavesPerWG;                 // 512
-constexpr int kChunk = 32;                                    // entries per tracking chunk
+constexpr int kThreads = kWave * kWavesPerWG;        // 512
+constexpr int kBlocksPerPass = kWavesPerWG / 2;      // two waves per block
+constexpr int kPasses = 4;
+constexpr int kBlocksPerWG = kBlocksPerPass * kPasses;   // 16
+constexpr int kTile = 16;                            // grid entries per matrix tile
+constexpr int kChunkTiles = 8;                       // tiles per tracking chunk
+constexpr int kChunk = kTile * kChunkTiles;          // 128 entries
 constexpr int kMaxGrid = 2048;
 constexpr int kBlockBytes = 50;
 
@@ -55,42 +64,59 @@ struct Iq1sArgs {
     int grid_size;
 };
 
-struct GroupTerms {
-    float up, um;     // U(+1/8), U(-1/8)
-    float vnp, vnm;   // -2*V(+1/8), -2*V(-1/8)
-};
-
-// Terms of one grid entry for one group.  Used by the sweep and the rescan, so
-// both produce bit-identical keys.
-__device__ __forceinline__ GroupTerms entry_terms(const float4* __restrict__ sg, int e,
-                                                  const float (&wx)[8], const float (&w)[8],
-                                                  float w64, float b4)
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float f)
 {
-    const float4 q0 = sg[2 * e];
-    const float4 q1 = sg[2 * e + 1];
-    const float q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    float A = wx[0] * q[0];
-    float M = w[0] * q[0];
-    float N = w[0] * fabsf(q[0]);
-#pragma unroll
-    for (int j = 1; j < 8; ++j) {
-        A = __builtin_fmaf(wx[j], q[j], A);
-        M = __builtin_fmaf(w[j], q[j], M);
-        N = __builtin_fmaf(w[j], fabsf(q[j]), N);
-    }
-    // U(delta) = N + 2*delta*M + delta^2*W,  V(delta) = A + delta*B
-    const float T = N + w64;
-    GroupTerms t;
-    t.up = __builtin_fmaf(M, 0.25f, T);
-    t.um = __builtin_fmaf(M, -0.25f, T);
-    t.vnp = __builtin_fmaf(A, -2.0f, -b4);
-    t.vnm = __builtin_fmaf(A, -2.0f, b4);
-    return t;
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-__global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Part p (0, 1, 2) of the exact three-way bf16 split of v: v = hi + mid + lo.
+__device__ __forceinline__ uint32_t split_part(float v, int p)
 {
-    __shared__ float4 sgrid[kMaxGrid * 2];
+    const uint32_t hi = bf16_bits(v);
+    const float r1 = v - bf16_to_f32(hi);
+    const uint32_t mid = bf16_bits(r1);
+    const float r2 = r1 - bf16_to_f32(mid);
+    return p == 0 ? hi : (p == 1 ? mid : bf16_bits(r2));
+}
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 u)
+{
+    return __builtin_bit_cast(v8bf, u);
+}
+
+// The 8 values and importance weights of group g of a block (zeros and ones
+// for a rejected block, so the sweep stays finite).
+__device__ __forceinline__ void load_group(const float* xblk, const float* wblk, int g, bool zero,
+                                           float (&x)[8], float (&w)[8])
+{
+    if (zero) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { x[j] = 0.0f; w[j] = 1.0f; }
+        return;
+    }
+    const float4* xp = reinterpret_cast<const float4*>(xblk + g * 8);
+    const float4 x0 = xp[0], x1 = xp[1];
+    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    if (wblk) {
+        const float4* wp = reinterpret_cast<const float4*>(wblk + g * 8);
+        const float4 w0 = wp[0], w1 = wp[1];
+        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = 1.0f;
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 4) void iq1s_encode_kernel(Iq1sArgs a)
+{
+    __shared__ uint4 sq[kMaxGrid];       // entry e: q[0..7] as bf16
+    __shared__ uint4 sa[kMaxGrid];       // entry e: |q[0..7]| as bf16
     __shared__ uint16_t sout16[kBlocksPerWG * kBlockBytes / 2];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
@@ -105,20 +131,26 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     if (tid == 0) sgrid_bad = 0;
     for (int i = tid; i < kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
-    // Stage the grid; entries past the end repeat the last one (their keys can
-    // never beat the real entry, which comes first).
+    // Stage the grid as bf16 (exact for ternary values); entries past the end
+    // repeat the last one, which always comes first in index order.
     {
         const float4* gsrc = reinterpret_cast<const float4*>(a.grid);
         int bad = 0;
-        for (int i = tid; i < npad * 2; i += kThreads) {
-            const int e = i >> 1;
+        for (int e = tid; e < npad; e += kThreads) {
             const int src = e < n ? e : n - 1;
-            const float4 v = gsrc[2 * src + (i & 1)];
-            const float vv[4] = {v.x, v.y, v.z, v.w};
+            const float4 v0 = gsrc[2 * src], v1 = gsrc[2 * src + 1];
+            const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t h[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bad |= !(vv[j] == 0.0f || vv[j] == 1.0f || vv[j] == -1.0f);
-            sgrid[i] = v;
+            for (int t = 0; t < 8; ++t) {
+                bad |= !(v[t] == 0.0f || v[t] == 1.0f || v[t] == -1.0f);
+                h[t] = bf16_bits(v[t]);
+            }
+            const uint4 packed = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                            h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            sq[e] = packed;
+            sa[e] = make_uint4(packed.x & 0x7fff7fffu, packed.y & 0x7fff7fffu,
+                               packed.z & 0x7fff7fffu, packed.w & 0x7fff7fffu);
         }
         if (bad) sgrid_bad = 1;
     }
@@ -126,186 +158,222 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     const bool grid_bad = sgrid_bad != 0;
     if (grid_bad && tid == 0) report(a.status, IQ_ERR_GRID);
 
-    const int slot = wave * kBlocksPerWave + (lane >> 5);     // block slot in this WG
-    const int64_t blk = (int64_t)blockIdx.x * kBlocksPerWG + slot;
-    const bool valid = blk < a.g.nblocks;
-    const int g = lane & 31;                                   // group in block
-    const int sub = g >> 2;                                    // sub-block
-    const int lq = g & 3;                                      // group in sub-block
+    const int col = lane & 15;          // matrix column = group within the half block
+    const int kb = lane >> 4;           // K slice of the operands / row quarter of the result
+    const int half = wave & 1;
+    const int g = half * 16 + col;      // group in block
+    const int sub = g >> 2;
+    const int lq = g & 3;
 
-    float x[8], w[8];
-    if (valid) {
-        const float4* xp = reinterpret_cast<const float4*>(a.w + blk * kBlockElems + g * 8);
-        const float4 x0 = xp[0], x1 = xp[1];
-        x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-        x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-        if (a.imp) {
-            const int64_t bt = blk / a.g.blocks_per_batch;
-            const int64_t cb = blk % a.g.blocks_per_row;
-            const float4* wp = reinterpret_cast<const float4*>(a.imp + bt * a.g.cols + cb * kBlockElems + g * 8);
-            const float4 w0 = wp[0], w1 = wp[1];
-            w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-            w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w[j] = 1.0f;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { x[j] = 0.0f; w[j] = 1.0f; }
-    }
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int slot = pass * kBlocksPerPass + (wave >> 1);
+        const int64_t blk = (int64_t)blockIdx.x * kBlocksPerWG + slot;
+        if (blk >= a.g.nblocks) continue;                      // wave-uniform
+        const int64_t bt = blk / a.g.blocks_per_batch;
+        const int64_t cb = blk % a.g.blocks_per_row;
+        const float* xblk = a.w + blk * kBlockElems;
+        const float* wblk = a.imp ? a.imp + bt * a.g.cols + cb * kBlockElems : nullptr;
 
-    // Input checks: a non-finite weight or a negative / non-finite importance
-    // value zeroes the whole block and is reported.
-    int err = 0;
-    float amax = 0.0f;
+        // Whole-block checks and amax (each lane reads 4 of the 256 values).
+        int err = 0;
+        float amax = 0.0f;
+        {
+            const float4 xv = reinterpret_cast<const float4*>(xblk)[lane];
+            const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (!finite_f32(x[j])) err = IQ_ERR_NONFINITE;
-        amax = fmaxf(amax, fabsf(x[j]));
-    }
-    if (!err) {
+            for (int t = 0; t < 4; ++t) {
+                if (!finite_f32(xs[t])) err = IQ_ERR_NONFINITE;
+                amax = fmaxf(amax, fabsf(xs[t]));
+            }
+            if (wblk && !err) {
+                const float4 wv = reinterpret_cast<const float4*>(wblk)[lane];
+                const float ws[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (!(w[j] >= 0.0f) || !finite_f32(w[j])) err = IQ_ERR_IMPORTANCE;
-    }
-    if (err && valid) report(a.status, err);
-    const uint64_t bad_lanes = __ballot(err != 0);
-    const uint32_t bad_half = (lane >> 5) ? (uint32_t)(bad_lanes >> 32) : (uint32_t)bad_lanes;
-
-    // Block amax over the 32 lanes of this half-wave.
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-
-    // Super-block scale: fp32 divide, fp32 multiply (no contraction), fp16 RNE.
-    uint32_t dh;
-    if (a.scales) {
-        dh = valid ? (uint32_t)a.scales[blk] : 0u;
-    } else {
-        const float t = amax / 16.875f;
-        const float u = t * 0.61f;
-        dh = f32_to_f16_bits(u);
-    }
-    bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
-    dh &= 0x7fffu;
-    if (scale_bad && valid && g == 0 && bad_half == 0) report(a.status, IQ_ERR_SCALE_RANGE);
-    const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
-
-    // Forced choice of this sub-block, if any.
-    int forced = -1;
-    if (a.choices && valid) {
-        forced = a.choices[blk * 8 + sub];
-        if (forced < 0 || forced > 15) {
-            if (lq == 0) report(a.status, IQ_ERR_ARG);
-            forced = -2;
-        }
-    }
-    const uint64_t badc_lanes = __ballot(forced == -2);
-    const uint32_t badc_half = (lane >> 5) ? (uint32_t)(badc_lanes >> 32) : (uint32_t)badc_lanes;
-
-    const bool zero_block = !valid || grid_bad || bad_half != 0 || scale_bad || dh == 0u ||
-                            badc_half != 0;
-
-    // Per-group sums.
-    float wx[8];
-    float W = 0.0f, B = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        wx[j] = w[j] * x[j];
-        W += w[j];
-        B += wx[j];
-    }
-    const float w64 = W * 0.015625f;
-    const float b4 = B * 0.25f;
-    float s[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s[k] = d * (float)(2 * k + 1);
-
-    // Sweep: value-only minima of the 16 choices, chunk of the last improvement.
-    float best[16], snap[16];
-    int chunk_of[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) { best[c] = __builtin_inff(); snap[c] = best[c]; chunk_of[c] = 0; }
-
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int e0 = ch * kChunk;
-#pragma unroll 2
-        for (int e = e0; e < e0 + kChunk; e += 2) {
-            const GroupTerms t0 = entry_terms(sgrid, e, wx, w, w64, b4);
-            const GroupTerms t1 = entry_terms(sgrid, e + 1, wx, w, w64, b4);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float p0 = __builtin_fmaf(s[k], t0.up, t0.vnp);
-                const float p1 = __builtin_fmaf(s[k], t1.up, t1.vnp);
-                best[k] = fminf(fminf(best[k], p0), p1);
-                const float m0 = __builtin_fmaf(s[k], t0.um, t0.vnm);
-                const float m1 = __builtin_fmaf(s[k], t1.um, t1.vnm);
-                best[8 + k] = fminf(fminf(best[8 + k], m0), m1);
+                for (int t = 0; t < 4; ++t)
+                    if (!(ws[t] >= 0.0f) || !finite_f32(ws[t])) err = IQ_ERR_IMPORTANCE;
             }
         }
+        if (err && half == 0) report(a.status, err);
+        const bool block_bad = __ballot(err != 0) != 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+
+        uint32_t dh;
+        if (a.scales) {
+            dh = (uint32_t)a.scales[blk];
+        } else {
+            const float t = amax / 16.875f;
+            const float u = t * 0.61f;
+            dh = f32_to_f16_bits(u);
+        }
+        const bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
+        dh &= 0x7fffu;
+        if (scale_bad && !block_bad && half == 0 && lane == 0) report(a.status, IQ_ERR_SCALE_RANGE);
+        const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
+
+        // Forced choices: every wave of the block checks all 8 of them.
+        int forced = -1;
+        bool choice_bad = false;
+        if (a.choices) {
+            const int cv = lane < 8 ? a.choices[blk * 8 + lane] : 0;
+            const bool bad = cv < 0 || cv > 15;
+            if (bad && half == 0) report(a.status, IQ_ERR_ARG);
+            choice_bad = __ballot(bad) != 0;
+            forced = a.choices[blk * 8 + sub];
+        }
+        const bool zero_block = grid_bad || block_bad || scale_bad || dh == 0u || choice_bad;
+        if (choice_bad) forced = -1;
+
+        // The lane's group: values, weights, sums, and its K slice of the
+        // three-way bf16 split of w*x and w (slice 3 is zero padding).
+        float x[8], w[8];
+        load_group(xblk, wblk, g, zero_block, x, w);
+        float W = 0.0f, B = 0.0f;
+        uint32_t bwx[8], bw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float wxj = w[j] * x[j];
+            W += w[j];
+            B += wxj;
+            bwx[j] = kb < 3 ? split_part(wxj, kb) : 0u;
+            bw[j] = kb < 3 ? split_part(w[j], kb) : 0u;
+        }
+        const v8bf opwx = as_v8bf(make_uint4(bwx[0] | (bwx[1] << 16), bwx[2] | (bwx[3] << 16),
+                                             bwx[4] | (bwx[5] << 16), bwx[6] | (bwx[7] << 16)));
+        const v8bf opw = as_v8bf(make_uint4(bw[0] | (bw[1] << 16), bw[2] | (bw[3] << 16),
+                                            bw[4] | (bw[5] << 16), bw[6] | (bw[7] << 16)));
+        const float w64 = W * 0.015625f;
+        const float b4 = B * 0.25f;
+        float s[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s[k] = d * (float)(2 * k + 1);
+
+        // Sweep.
+        // chunk_of: 4-bit chunk index of choice c in bits 4*(c%8) of word c/8.
+        float best[16], snap[16];
+        uint32_t chunk_of[2] = {0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 16; ++c) { best[c] = __builtin_inff(); snap[c] = best[c]; }
+        const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ch = 0; ch < nchunks; ++ch) {
+            for (int tt = 0; tt < kChunkTiles; ++tt) {
+                const int e = (ch * kChunkTiles + tt) * kTile + col;
+                const v8bf aq = as_v8bf(sq[e]);
+                const v8bf aa = as_v8bf(sa[e]);
+                const v4f accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opwx, zero4, 0, 0, 0);
+                const v4f accM = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opw, zero4, 0, 0, 0);
+                const v4f accN = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, opw, zero4, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; r += 2) {
+                    const float T0 = accN[r] + w64, T1 = accN[r + 1] + w64;
+                    const float up0 = __builtin_fmaf(accM[r], 0.25f, T0);
+                    const float um0 = __builtin_fmaf(accM[r], -0.25f, T0);
+                    const float up1 = __builtin_fmaf(accM[r + 1], 0.25f, T1);
+                    const float um1 = __builtin_fmaf(accM[r + 1], -0.25f, T1);
+                    const float vnp0 = __builtin_fmaf(accA[r], -2.0f, -b4);
+                    const float vnm0 = __builtin_fmaf(accA[r], -2.0f, b4);
+                    const float vnp1 = __builtin_fmaf(accA[r + 1], -2.0f, -b4);
+                    const float vnm1 = __builtin_fmaf(accA[r + 1], -2.0f, b4);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        best[k] = fminf(fminf(best[k], __builtin_fmaf(s[k], up0, vnp0)),
+                                        __builtin_fmaf(s[k], up1, vnp1));
+                        best[8 + k] = fminf(fminf(best[8 + k], __builtin_fmaf(s[k], um0, vnm0)),
+                                            __builtin_fmaf(s[k], um1, vnm1));
+                    }
+                }
+            }
+            const uint32_t chrep = (uint32_t)ch * 0x11111111u;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const uint32_t m = best[c] < snap[c] ? (0xfu << (4 * (c & 7))) : 0u;
+                chunk_of[c >> 3] = (chunk_of[c >> 3] & ~m) | (chrep & m);
+                snap[c] = best[c];
+            }
+        }
+
+        // Sub-block choice: per group, the least minimum of its four lanes; per
+        // sub-block, s_k times the sum over its four groups (identical float sum
+        // in every lane of the sub-block).
+        int cstar = 0;
+        float cbest = 0.0f;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            chunk_of[c] = best[c] < snap[c] ? ch : chunk_of[c];
-            snap[c] = best[c];
+            float m = best[c];
+            m = fminf(m, __shfl_xor(m, 16));
+            m = fminf(m, __shfl_xor(m, 32));
+            float v = m + __shfl_xor(m, 1);
+            v += __shfl_xor(v, 2);
+            const float cost = s[c & 7] * v;
+            if (c == 0 || cost < cbest) { cbest = cost; cstar = c; }
         }
-    }
+        if (forced >= 0) cstar = forced;
 
-    // Sub-block cost of each choice: s_k * (sum of the 4 groups' minima); the
-    // xor-butterfly gives the same float sum in all 4 lanes.
-    int cstar = 0;
-    float cbest = 0.0f;
+        // Rescan this lane's entries of the chunk that holds its minimum of the
+        // chosen choice, on the VALU.
+        float lane_min = best[0];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        float v = best[c];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        const float cost = s[c & 7] * v;
-        if (c == 0 || cost < cbest) { cbest = cost; cstar = c; }
-    }
-    if (forced >= 0) cstar = forced;
-
-    // Rescan the winning chunk of the chosen choice for the lowest entry index.
-    float target = best[0];
-    int tchunk = chunk_of[0];
+        for (int c = 1; c < 16; ++c)
+            if (cstar == c) lane_min = best[c];
+        const int tchunk = (int)((chunk_of[cstar >> 3] >> (4 * (cstar & 7))) & 0xfu);
+        load_group(xblk, wblk, g, zero_block, x, w);
+        const int kstar = cstar & 7;
+        const int dbit = cstar >> 3;
+        float sk = s[0];
 #pragma unroll
-    for (int c = 1; c < 16; ++c)
-        if (cstar == c) { target = best[c]; tchunk = chunk_of[c]; }
-    const int kstar = cstar & 7;
-    const int dbit = cstar >> 3;
-    float sk = s[0];
+        for (int k = 1; k < 8; ++k)
+            if (kstar == k) sk = s[k];
+        const float dl = dbit ? -0.25f : 0.25f;      // 2*delta
+        const float bd = dbit ? b4 : -b4;
+        int idx = -1;
+        float vbest = 0.0f;
+        for (int tt = 0; tt < kChunkTiles; ++tt) {
 #pragma unroll
-    for (int k = 1; k < 8; ++k)
-        if (kstar == k) sk = s[k];
-    int found = -1;
-    {
-        const int e0 = tchunk * kChunk;
-        for (int i = 0; i < kChunk; ++i) {
-            const GroupTerms t = entry_terms(sgrid, e0 + i, wx, w, w64, b4);
-            const float key = dbit ? __builtin_fmaf(sk, t.um, t.vnm) : __builtin_fmaf(sk, t.up, t.vnp);
-            if (found < 0 && key == target) found = e0 + i;
+            for (int r = 0; r < 4; ++r) {
+                const int e = (tchunk * kChunkTiles + tt) * kTile + 4 * kb + r;
+                const uint4 u = sq[e];
+                const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+                float A = 0.0f, M = 0.0f, N = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                    A = __builtin_fmaf(w[j] * x[j], q, A);
+                    M = __builtin_fmaf(w[j], q, M);
+                    N = __builtin_fmaf(w[j], fabsf(q), N);
+                }
+                const float U = __builtin_fmaf(M, dl, N + w64);
+                const float key = __builtin_fmaf(sk, U, __builtin_fmaf(A, -2.0f, bd));
+                if (idx < 0 || key < vbest) { vbest = key; idx = e; }
+            }
         }
-    }
-    int idx = found < 0 ? 0 : (found < n ? found : n - 1);
-
-    // Pack: low byte per group, qh word per sub-block, d per block.
-    int hi = ((idx >> 8) & 7) << (3 * lq);
-    hi |= __shfl_xor(hi, 1);
-    hi |= __shfl_xor(hi, 2);
-    if (!zero_block) {
-        uint8_t* ob = sout + slot * kBlockBytes;
-        ob[2 + 4 * sub + lq] = (uint8_t)(idx & 0xff);
-        if (lq == 0) {
-            const uint32_t qh = (uint32_t)hi | ((uint32_t)kstar << 12) | ((uint32_t)dbit << 15);
-            ob[34 + 2 * sub] = (uint8_t)(qh & 0xff);
-            ob[35 + 2 * sub] = (uint8_t)(qh >> 8);
+        // Keep the lane of the column whose matrix-core minimum is least.
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+            const float om = __shfl_xor(lane_min, o);
+            const int oi = __shfl_xor(idx, o);
+            if (om < lane_min || (om == lane_min && oi < idx)) { lane_min = om; idx = oi; }
         }
-        if (g == 0) {
-            ob[0] = (uint8_t)(dh & 0xff);
-            ob[1] = (uint8_t)(dh >> 8);
+        idx = idx < n ? idx : n - 1;
+
+        // Pack: low byte per group, qh word per sub-block, d per block.
+        int hi = ((idx >> 8) & 7) << (3 * lq);
+        hi |= __shfl_xor(hi, 1);
+        hi |= __shfl_xor(hi, 2);
+        if (!zero_block && kb == 0) {
+            uint8_t* ob = sout + slot * kBlockBytes;
+            ob[2 + 4 * sub + lq] = (uint8_t)(idx & 0xff);
+            if (lq == 0) {
+                const uint32_t qh = (uint32_t)hi | ((uint32_t)kstar << 12) | ((uint32_t)dbit << 15);
+                ob[34 + 2 * sub] = (uint8_t)(qh & 0xff);
+                ob[35 + 2 * sub] = (uint8_t)(qh >> 8);
+            }
+            if (g == 0) {
+                ob[0] = (uint8_t)(dh & 0xff);
+                ob[1] = (uint8_t)(dh >> 8);
+            }
         }
     }
     __syncthreads();
-    // Coalesced store of this workgroup's blocks as 16-bit words.
     const int64_t first = (int64_t)blockIdx.x * kBlocksPerWG;
     const int64_t left = a.g.nblocks - first;
     const int nb = left < kBlocksPerWG ? (int)left : kBlocksPerWG;
