@@ -10,21 +10,28 @@
 // sum w*(x - s*(q+delta))^2, lowest index winning ties.
 //
 // For a group and a grid entry the error is, up to a constant,
-//   s^2 * U(delta) - 2 s * V(delta),  U = N + 2 delta M + delta^2 W,
-//   V = A + delta B,  A = sum wx*q, M = sum w*q, N = sum w*|q|.
-// A, M and N for 16 grid entries x 16 groups are three small products
-// [16 entries x 8] x [8 x 16 groups], run as v_mfma_f32_16x16x32_bf16: the
-// ternary entries are exact in bf16, and the group side (w*x and w) is split
-// into three bf16 parts whose sum is exactly the fp32 value, so the products
-// are exact and only the fp32 accumulation rounds.  The VALU then forms U, V
-// and the 16 choice keys s_k*U - 2V (one FMA each) and keeps value-only
-// minima (v_min3 over two entries).
+//   s^2 * U(delta) - 2 s * V(delta),  U(delta) = sum w*(q+delta)^2,
+//   V(delta) = sum wx*(q+delta).
+// U(+1/8), U(-1/8), -2V(+1/8) and -2V(-1/8) for 16 grid entries x 16 groups
+// are four small products [16 entries x 8] x [8 x 16 groups], run as
+// v_mfma_f32_16x16x32_bf16: the entry side (q+delta)^2 and q is exact in bf16
+// (values like 81/64 need 7 mantissa bits), the group side (w and -2*w*x) is
+// split into three bf16 parts whose sum is exactly the fp32 value, so the
+// products are exact and only the fp32 accumulation rounds; the constant
+// -2*delta*sum(wx) of V enters as the accumulator input.  Everything is
+// divided by the block scale d (the V side carries 1/d), so the key of local
+// scale s_k = d*(2k+1) is (2k+1)*U - 2V/d: one FMA with a literal multiplier
+// (v_fmamk_f32, two register operands, which pairs well with v_min3 in the
+// dual-issue VALU); the choice cost of a sub-block is (2k+1) times the sum of
+// its groups' minima (the common factor d^2 dropped).  The VALU keeps
+// value-only minima (v_min3 over two entries).
 //
 // Layout: a wave owns 16 groups (half a block): matrix column j = lane%16 is
 // group j; the lane's four accumulator rows are 4*(lane/16)+r of every
 // 16-entry tile, so the four lanes of a column cover disjoint quarters of the
-// grid.  A 512-thread workgroup runs 8 waves = 4 blocks per pass and 4 passes
-// (16 blocks), with the grid staged once in LDS as bf16 (q and |q|, 64 KiB).
+// grid.  A 1024-thread workgroup runs 16 waves = 8 blocks per pass and 2
+// passes (16 blocks), with the grid staged once in LDS as bf16 ((q+1/8)^2,
+// (q-1/8)^2 and q, 96 KiB; one workgroup per CU, 4 waves per SIMD).
 // Index recovery: each lane records the 128-entry chunk that last lowered each
 // of its 16 minima; once the sub-block's choice is fixed, the lane rescans its
 // 32 entries of that chunk on the VALU (fp32 dot products) and takes the lowest
@@ -41,10 +48,10 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int kWavesPerWG = 8;
-constexpr int kThreads = kWave * kWavesPerWG;        // 512
+constexpr int kWavesPerWG = 16;
+constexpr int kThreads = kWave * kWavesPerWG;        // 1024
 constexpr int kBlocksPerPass = kWavesPerWG / 2;      // two waves per block
-constexpr int kPasses = 4;
+constexpr int kPasses = 2;
 constexpr int kBlocksPerWG = kBlocksPerPass * kPasses;   // 16
 constexpr int kTile = 16;                            // grid entries per matrix tile
 constexpr int kChunkTiles = 8;                       // tiles per tracking chunk
@@ -113,10 +120,11 @@ __device__ __forceinline__ void load_group(const float* xblk, const float* wblk,
     }
 }
 
-__global__ __launch_bounds__(kThreads, 4) void iq1s_encode_kernel(Iq1sArgs a)
+__global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 {
+    __shared__ uint4 sp[kMaxGrid];       // entry e: (q[0..7] + 1/8)^2 as bf16
+    __shared__ uint4 sm[kMaxGrid];       // entry e: (q[0..7] - 1/8)^2 as bf16
     __shared__ uint4 sq[kMaxGrid];       // entry e: q[0..7] as bf16
-    __shared__ uint4 sa[kMaxGrid];       // entry e: |q[0..7]| as bf16
     __shared__ uint16_t sout16[kBlocksPerWG * kBlockBytes / 2];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
@@ -140,17 +148,21 @@ __global__ __launch_bounds__(kThreads, 4) void iq1s_encode_kernel(Iq1sArgs a)
             const int src = e < n ? e : n - 1;
             const float4 v0 = gsrc[2 * src], v1 = gsrc[2 * src + 1];
             const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            uint32_t h[8];
+            uint32_t h[8], hp[8], hm[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
                 bad |= !(v[t] == 0.0f || v[t] == 1.0f || v[t] == -1.0f);
                 h[t] = bf16_bits(v[t]);
+                const float p = v[t] + 0.125f, m = v[t] - 0.125f;
+                hp[t] = bf16_bits(p * p);          // exact: 81/64, 1/64, 49/64
+                hm[t] = bf16_bits(m * m);
             }
-            const uint4 packed = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                            h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-            sq[e] = packed;
-            sa[e] = make_uint4(packed.x & 0x7fff7fffu, packed.y & 0x7fff7fffu,
-                               packed.z & 0x7fff7fffu, packed.w & 0x7fff7fffu);
+            sq[e] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                               h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            sp[e] = make_uint4(hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16),
+                               hp[4] | (hp[5] << 16), hp[6] | (hp[7] << 16));
+            sm[e] = make_uint4(hm[0] | (hm[1] << 16), hm[2] | (hm[3] << 16),
+                               hm[4] | (hm[5] << 16), hm[6] | (hm[7] << 16));
         }
         if (bad) sgrid_bad = 1;
     }
@@ -225,9 +237,10 @@ __global__ __launch_bounds__(kThreads, 4) void iq1s_encode_kernel(Iq1sArgs a)
         if (choice_bad) forced = -1;
 
         // The lane's group: values, weights, sums, and its K slice of the
-        // three-way bf16 split of w*x and w (slice 3 is zero padding).
+        // three-way bf16 split of -2*w*x and w (slice 3 is zero padding).
         float x[8], w[8];
         load_group(xblk, wblk, g, zero_block, x, w);
+        const float inv_d = zero_block ? 1.0f : 1.0f / d;
         float W = 0.0f, B = 0.0f;
         uint32_t bwx[8], bw[8];
 #pragma unroll
@@ -235,18 +248,18 @@ __global__ __launch_bounds__(kThreads, 4) void iq1s_encode_kernel(Iq1sArgs a)
             const float wxj = w[j] * x[j];
             W += w[j];
             B += wxj;
-            bwx[j] = kb < 3 ? split_part(wxj, kb) : 0u;
+            bwx[j] = kb < 3 ? split_part(-2.0f * (wxj * inv_d), kb) : 0u;
             bw[j] = kb < 3 ? split_part(w[j], kb) : 0u;
         }
-        const v8bf opwx = as_v8bf(make_uint4(bwx[0] | (bwx[1] << 16), bwx[2] | (bwx[3] << 16),
-                                             bwx[4] | (bwx[5] << 16), bwx[6] | (bwx[7] << 16)));
+        const v8bf opn2wx = as_v8bf(make_uint4(bwx[0] | (bwx[1] << 16), bwx[2] | (bwx[3] << 16),
+                                               bwx[4] | (bwx[5] << 16), bwx[6] | (bwx[7] << 16)));
         const v8bf opw = as_v8bf(make_uint4(bw[0] | (bw[1] << 16), bw[2] | (bw[3] << 16),
                                             bw[4] | (bw[5] << 16), bw[6] | (bw[7] << 16)));
         const float w64 = W * 0.015625f;
         const float b4 = B * 0.25f;
-        float s[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) s[k] = d * (float)(2 * k + 1);
+        const float b4d = b4 * inv_d;
+        const v4f cnp = {-b4d, -b4d, -b4d, -b4d};     // -2*(+1/8)*B/d
+        const v4f cnm = {b4d, b4d, b4d, b4d};         // -2*(-1/8)*B/d
 
         // Sweep.
         // chunk_of: 4-bit chunk index of choice c in bits 4*(c%8) of word c/8.
@@ -258,29 +271,26 @@ __global__ __launch_bounds__(kThreads, 4) void iq1s_encode_kernel(Iq1sArgs a)
         for (int ch = 0; ch < nchunks; ++ch) {
             for (int tt = 0; tt < kChunkTiles; ++tt) {
                 const int e = (ch * kChunkTiles + tt) * kTile + col;
+                const v8bf ap = as_v8bf(sp[e]);
+                const v8bf am = as_v8bf(sm[e]);
                 const v8bf aq = as_v8bf(sq[e]);
-                const v8bf aa = as_v8bf(sa[e]);
-                const v4f accA = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opwx, zero4, 0, 0, 0);
-                const v4f accM = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opw, zero4, 0, 0, 0);
-                const v4f accN = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, opw, zero4, 0, 0, 0);
+                const v4f up = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, opw, zero4, 0, 0, 0);
+                const v4f um = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, opw, zero4, 0, 0, 0);
+                const v4f vnp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opn2wx, cnp, 0, 0, 0);
+                const v4f vnm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opn2wx, cnm, 0, 0, 0);
 #pragma unroll
-                for (int r = 0; r < 4; r += 2) {
-                    const float T0 = accN[r] + w64, T1 = accN[r + 1] + w64;
-                    const float up0 = __builtin_fmaf(accM[r], 0.25f, T0);
-                    const float um0 = __builtin_fmaf(accM[r], -0.25f, T0);
-                    const float up1 = __builtin_fmaf(accM[r + 1], 0.25f, T1);
-                    const float um1 = __builtin_fmaf(accM[r + 1], -0.25f, T1);
-                    const float vnp0 = __builtin_fmaf(accA[r], -2.0f, -b4);
-                    const float vnm0 = __builtin_fmaf(accA[r], -2.0f, b4);
-                    const float vnp1 = __builtin_fmaf(accA[r + 1], -2.0f, -b4);
-                    const float vnm1 = __builtin_fmaf(accA[r + 1], -2.0f, b4);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        best[k] = fminf(fminf(best[k], __builtin_fmaf(s[k], up0, vnp0)),
-                                        __builtin_fmaf(s[k], up1, vnp1));
-                        best[8 + k] = fminf(fminf(best[8 + k], __builtin_fmaf(s[k], um0, vnm0)),
-                                            __builtin_fmaf(s[k], um1, vnm1));
-                    }
+                for (int k = 0; k < 8; ++k) {
+                    const float mk = (float)(2 * k + 1);
+                    const float p0 = __builtin_fmaf(up[0], mk, vnp[0]);
+                    const float p1 = __builtin_fmaf(up[1], mk, vnp[1]);
+                    const float p2 = __builtin_fmaf(up[2], mk, vnp[2]);
+                    const float p3 = __builtin_fmaf(up[3], mk, vnp[3]);
+                    const float m0 = __builtin_fmaf(um[0], mk, vnm[0]);
+                    const float m1 = __builtin_fmaf(um[1], mk, vnm[1]);
+                    const float m2 = __builtin_fmaf(um[2], mk, vnm[2]);
+                    const float m3 = __builtin_fmaf(um[3], mk, vnm[3]);
+                    best[k] = fminf(best[k], fminf(fminf(fminf(p0, p1), p2), p3));
+                    best[8 + k] = fminf(best[8 + k], fminf(fminf(fminf(m0, m1), m2), m3));
                 }
             }
             const uint32_t chrep = (uint32_t)ch * 0x11111111u;
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 4) void iq1s_encode_kernel(Iq1sArgs a)
             m = fminf(m, __shfl_xor(m, 32));
             float v = m + __shfl_xor(m, 1);
             v += __shfl_xor(v, 2);
-            const float cost = s[c & 7] * v;
+            const float cost = (float)(2 * (c & 7) + 1) * v;
             if (c == 0 || cost < cbest) { cbest = cost; cstar = c; }
         }
         if (forced >= 0) cstar = forced;
@@ -316,13 +326,11 @@ __global__ __launch_bounds__(kThreads, 4) void iq1s_encode_kernel(Iq1sArgs a)
         for (int c = 1; c < 16; ++c)
             if (cstar == c) lane_min = best[c];
         const int tchunk = (int)((chunk_of[cstar >> 3] >> (4 * (cstar & 7))) & 0xfu);
+        __asm__ volatile("" ::: "memory");    // reload x and w instead of keeping them live
         load_group(xblk, wblk, g, zero_block, x, w);
         const int kstar = cstar & 7;
         const int dbit = cstar >> 3;
-        float sk = s[0];
-#pragma unroll
-        for (int k = 1; k < 8; ++k)
-            if (kstar == k) sk = s[k];
+        const float mk = (float)(2 * kstar + 1);
         const float dl = dbit ? -0.25f : 0.25f;      // 2*delta
         const float bd = dbit ? b4 : -b4;
         int idx = -1;
@@ -342,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 4) void iq1s_encode_kernel(Iq1sArgs a)
                     N = __builtin_fmaf(w[j], fabsf(q), N);
                 }
                 const float U = __builtin_fmaf(M, dl, N + w64);
-                const float key = __builtin_fmaf(sk, U, __builtin_fmaf(A, -2.0f, bd));
+                const float key = __builtin_fmaf(U, mk, __builtin_fmaf(A, -2.0f, bd) * inv_d);
                 if (idx < 0 || key < vbest) { vbest = key; idx = e; }
             }
         }
