@@ -15,12 +15,21 @@
 // their (cost, k) and the first top_c are emitted with their codes and error
 // vectors xhat - x ("[2/4] Encode every GGML IQ choice in one pass" #3159).
 //
-// Kernel layout: one lane = one group, a wave = two blocks, a 512-thread
-// workgroup = 16 blocks.  The grid and its squares are staged in LDS (32 KiB).
-// Per (group, entry): P = sum (w*sign*x)*q and N = sum w*q^2, 16 keys
-// s_k*N - 2P (one FMA each), value-only minima with chunked index recovery as
-// in the IQ1_S kernel; the two lanes of a scale group add their minima with an
-// xor-shuffle.
+// With the signs fixed, the error of a group and an entry is, up to a
+// constant, s^2*N - 2s*P with N = sum w*q^2 and P = sum (w*sign*x)*q.  P and
+// N for 16 entries x 16 groups are two [16 x 8] x [8 x 16] products on the
+// matrix cores (v_mfma_f32_16x16x4_f32, fp32 operands, so any magnitude grid
+// is used as given).  Dividing by d, the key of local scale k is
+// (2k+1)*N - 2P/d: one FMA with a literal multiplier; the choice cost of a
+// scale group is (2k+1) times the sum of its two groups' minima.
+//
+// Layout: a wave owns 16 groups (half a block); matrix column j = lane%16 is
+// group j, the lane's accumulator rows are entries 4*(lane/16)+r of each
+// 16-entry tile.  A 1024-thread workgroup runs 8 blocks per pass and 2 passes
+// with the grid staged once in LDS (q and q^2 as fp32, 64 KiB).  Value-only minima (v_min3);
+// each lane records the chunk that last lowered each minimum and rescans its
+// entries of the winning chunk on the VALU; the four lanes of a column keep
+// the one whose matrix-core minimum is least (lowest index on equal minima).
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -29,11 +38,14 @@
 namespace iqk {
 namespace {
 
-constexpr int kBlocksPerWave = 2;
-constexpr int kWavesPerWG = 8;
-constexpr int kBlocksPerWG = kBlocksPerWave * kWavesPerWG;   // 16
-constexpr int kThreads = kWave * kWavesPerWG;                 // 512
-constexpr int kChunk = 32;
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWavesPerWG = 16;
+constexpr int kThreads = kWave * kWavesPerWG;        // 1024
+constexpr int kBlocksPerPass = kWavesPerWG / 2;
+constexpr int kPasses = 2;
+constexpr int kBlocksPerWG = kBlocksPerPass * kPasses;   // 16
+constexpr int kTile = 16;
 constexpr int kMaxGrid = 512;
 constexpr int kBlockBytes = 74;
 
@@ -53,58 +65,100 @@ struct Iq2xsArgs {
     int top_c;
 };
 
-struct EntryTerms {
-    float pn;   // -2 * sum (w*sign*x) * q
-    float n;    // sum w * q^2
-};
-
-// Terms of one grid entry; shared by the sweep and the rescan so both give
-// bit-identical keys.  sg holds, per entry, q[0..7] then q^2[0..7].
-__device__ __forceinline__ EntryTerms entry_terms(const float4* __restrict__ sg, int e,
-                                                  const float (&wxs)[8], const float (&w)[8])
+__device__ __forceinline__ void load_group(const float* xblk, const float* wblk, int g, bool zero,
+                                           float (&x)[8], float (&w)[8])
 {
-    const float4 a0 = sg[4 * e], a1 = sg[4 * e + 1], b0 = sg[4 * e + 2], b1 = sg[4 * e + 3];
-    const float q[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const float q2[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-    float P = wxs[0] * q[0];
-    float N = w[0] * q2[0];
+    if (zero) {
 #pragma unroll
-    for (int j = 1; j < 8; ++j) {
-        P = __builtin_fmaf(wxs[j], q[j], P);
-        N = __builtin_fmaf(w[j], q2[j], N);
+        for (int j = 0; j < 8; ++j) { x[j] = 0.0f; w[j] = 1.0f; }
+        return;
     }
-    EntryTerms t;
-    t.pn = -2.0f * P;
-    t.n = N;
-    return t;
+    const float4* xp = reinterpret_cast<const float4*>(xblk + g * 8);
+    const float4 x0 = xp[0], x1 = xp[1];
+    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    if (wblk) {
+        const float4* wp = reinterpret_cast<const float4*>(wblk + g * 8);
+        const float4 w0 = wp[0], w1 = wp[1];
+        w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+        w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = 1.0f;
+    }
 }
 
-// Lowest entry index of choice k whose key equals the sweep's minimum: rescan
-// the chunk that last lowered that minimum with the sweep's own arithmetic.
-__device__ __forceinline__ int rescan(const float4* __restrict__ sg, int k, const float (&best)[16],
-                                      const int (&chunk_of)[16], const float (&s)[16],
-                                      const float (&wxs)[8], const float (&w)[8], int n)
+// Input signs with the weakest element (smallest (w*x)*x, lowest index)
+// flipped when the count of negatives is odd.  Bit j set = element j negative.
+__device__ __forceinline__ int group_signs(const float (&x)[8], const float (&w)[8])
 {
-    float target = best[0];
-    int tchunk = chunk_of[0];
-    float sk = s[0];
+    int neg = 0;
 #pragma unroll
-    for (int c = 1; c < 16; ++c)
-        if (k == c) { target = best[c]; tchunk = chunk_of[c]; sk = s[c]; }
-    int found = -1;
-    const int e0 = tchunk * kChunk;
-    for (int i = 0; i < kChunk; ++i) {
-        const EntryTerms t = entry_terms(sg, e0 + i, wxs, w);
-        const float key = __builtin_fmaf(sk, t.n, t.pn);
-        if (found < 0 && key == target) found = e0 + i;
+    for (int j = 0; j < 8; ++j)
+        if (x[j] < 0.0f) neg |= 1 << j;
+    if (__popc(neg) & 1) {
+        int jw = 0;
+        float wk = (w[0] * x[0]) * x[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) {
+            const float v = (w[j] * x[j]) * x[j];
+            if (v < wk) { wk = v; jw = j; }
+        }
+        neg ^= 1 << jw;
     }
-    return found < 0 ? 0 : (found < n ? found : n - 1);
+    return neg;
+}
+
+// Per-entry fp32 copy of the grid for the VALU rescans: q[0..7], q^2[0..7],
+// padded to 18 floats so the four entries the four lanes of a column read
+// together (4 apart) fall in different LDS banks.
+constexpr int kEntryStride = 18;
+
+// VALU rescan: the lowest entry of least key (2k+1)*N - 2P/d among this lane's
+// entries of one chunk.
+template <int kChunkTiles>
+__device__ __forceinline__ int rescan(const float* __restrict__ sg, int chunk, int kb, int k,
+                                      const float (&wxs)[8], const float (&w)[8], float inv_d)
+{
+    const float mk = (float)(2 * k + 1);
+    int idx = -1;
+    float vbest = 0.0f;
+    for (int tt = 0; tt < kChunkTiles; ++tt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = (chunk * kChunkTiles + tt) * kTile + 4 * kb + r;
+            const float2* p = reinterpret_cast<const float2*>(sg + kEntryStride * e);
+            float q[8], q2[8];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float2 u = p[t], v = p[4 + t];
+                q[2 * t] = u.x; q[2 * t + 1] = u.y;
+                q2[2 * t] = v.x; q2[2 * t + 1] = v.y;
+            }
+            float P = 0.0f, N = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                P = __builtin_fmaf(wxs[j], q[j], P);
+                N = __builtin_fmaf(w[j], q2[j], N);
+            }
+            const float key = __builtin_fmaf(N, mk, (-2.0f * P) * inv_d);
+            if (idx < 0 || key < vbest) { vbest = key; idx = e; }
+        }
+    }
+    return idx;
 }
 
 template <bool kCandidates>
 __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 {
-    __shared__ float4 sgrid[kMaxGrid * 4];
+    // Tiles per tracking chunk: 4 (64 entries) for the encode, 2 (32
+    // entries) for the candidates, whose epilogue rescans top_c choices.
+    constexpr int kChunkTiles = kCandidates ? 2 : 4;
+    constexpr int kChunk = kTile * kChunkTiles;
+
+    __shared__ float sgrid[kMaxGrid * kEntryStride];    // entry e: q[0..7], q^2[0..7]
+    __shared__ float2 sq[kMaxGrid * 4];                 // entry e, slice kb: (q[kb], q[kb+4])
+    __shared__ float2 sq2[kMaxGrid * 4];                // same for q^2
     __shared__ uint16_t sout16[kBlocksPerWG * kBlockBytes / 2];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
@@ -121,16 +175,20 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         for (int i = tid; i < kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     {
-        const float4* gsrc = reinterpret_cast<const float4*>(a.grid);
         int bad = 0;
-        for (int i = tid; i < npad * 2; i += kThreads) {
-            const int e = i >> 1;
+        // One (entry, slice) pair per thread: consecutive threads write
+        // consecutive LDS words.
+        for (int i = tid; i < npad * 4; i += kThreads) {
+            const int e = i >> 2, t = i & 3;
             const int src = e < n ? e : n - 1;
-            const float4 v = gsrc[2 * src + (i & 1)];
-            bad |= !(v.x >= 0.0f && v.y >= 0.0f && v.z >= 0.0f && v.w >= 0.0f);
-            bad |= !(finite_f32(v.x) && finite_f32(v.y) && finite_f32(v.z) && finite_f32(v.w));
-            sgrid[4 * e + (i & 1)] = v;
-            sgrid[4 * e + 2 + (i & 1)] = make_float4(v.x * v.x, v.y * v.y, v.z * v.z, v.w * v.w);
+            const float a0 = a.grid[8 * src + 2 * t], a1 = a.grid[8 * src + 2 * t + 1];
+            const float b0 = a.grid[8 * src + t], b1 = a.grid[8 * src + t + 4];
+            bad |= !(a0 >= 0.0f && finite_f32(a0) && a1 >= 0.0f && finite_f32(a1));
+            float2* ge = reinterpret_cast<float2*>(sgrid + kEntryStride * e);
+            ge[t] = make_float2(a0, a1);
+            ge[4 + t] = make_float2(a0 * a0, a1 * a1);
+            sq[i] = make_float2(b0, b1);
+            sq2[i] = make_float2(b0 * b0, b1 * b1);
         }
         if (bad) sgrid_bad = 1;
     }
@@ -138,221 +196,231 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
     const bool grid_bad = sgrid_bad != 0;
     if (grid_bad && tid == 0) report(a.status, IQ_ERR_GRID);
 
-    const int slot = wave * kBlocksPerWave + (lane >> 5);
-    const int64_t blk = (int64_t)blockIdx.x * kBlocksPerWG + slot;
-    const bool valid = blk < a.g.nblocks;
-    const int g = lane & 31;          // group in block
-    const int m = g >> 1;             // scale group
-    const int h = g & 1;              // group in scale group
+    const int col = lane & 15;
+    const int kb = lane >> 4;
+    const int half = wave & 1;
+    const int g = half * 16 + col;          // group in block
+    const int m = g >> 1;                   // scale group
+    const int h = g & 1;                    // group in scale group
 
-    float x[8], w[8];
-    if (valid) {
-        const float4* xp = reinterpret_cast<const float4*>(a.w + blk * kBlockElems + g * 8);
-        const float4 x0 = xp[0], x1 = xp[1];
-        x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-        x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-        if (a.imp) {
-            const int64_t bt = blk / a.g.blocks_per_batch;
-            const int64_t cb = blk % a.g.blocks_per_row;
-            const float4* wp = reinterpret_cast<const float4*>(a.imp + bt * a.g.cols + cb * kBlockElems + g * 8);
-            const float4 w0 = wp[0], w1 = wp[1];
-            w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
-            w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+    for (int pass = 0; pass < kPasses; ++pass) {
+        const int slot = pass * kBlocksPerPass + (wave >> 1);
+        const int64_t blk = (int64_t)blockIdx.x * kBlocksPerWG + slot;
+        if (blk >= a.g.nblocks) continue;                      // wave-uniform
+        const int64_t bt = blk / a.g.blocks_per_batch;
+        const int64_t cb = blk % a.g.blocks_per_row;
+        const float* xblk = a.w + blk * kBlockElems;
+        const float* wblk = a.imp ? a.imp + bt * a.g.cols + cb * kBlockElems : nullptr;
+
+        int err = 0;
+        float amax = 0.0f;
+        {
+            const float4 xv = reinterpret_cast<const float4*>(xblk)[lane];
+            const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (!finite_f32(xs[t])) err = IQ_ERR_NONFINITE;
+                amax = fmaxf(amax, fabsf(xs[t]));
+            }
+            if (wblk && !err) {
+                const float4 wv = reinterpret_cast<const float4*>(wblk)[lane];
+                const float ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (!(ws[t] >= 0.0f) || !finite_f32(ws[t])) err = IQ_ERR_IMPORTANCE;
+            }
+        }
+        if (err && half == 0) report(a.status, err);
+        const bool block_bad = __ballot(err != 0) != 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+
+        uint32_t dh;
+        if (!kCandidates && a.scales) {
+            dh = (uint32_t)a.scales[blk];
         } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w[j] = 1.0f;
+            const float t = amax / 155.0f;
+            const float u = t * 0.61f;
+            dh = f32_to_f16_bits(u);
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { x[j] = 0.0f; w[j] = 1.0f; }
-    }
+        const bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
+        dh &= 0x7fffu;
+        if (scale_bad && !block_bad && half == 0 && lane == 0) report(a.status, IQ_ERR_SCALE_RANGE);
+        const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
 
-    int err = 0;
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (!finite_f32(x[j])) err = IQ_ERR_NONFINITE;
-        amax = fmaxf(amax, fabsf(x[j]));
-    }
-    if (!err) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (!(w[j] >= 0.0f) || !finite_f32(w[j])) err = IQ_ERR_IMPORTANCE;
-    }
-    if (err && valid) report(a.status, err);
-    const uint64_t bad_lanes = __ballot(err != 0);
-    const uint32_t bad_half = (lane >> 5) ? (uint32_t)(bad_lanes >> 32) : (uint32_t)bad_lanes;
-
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-
-    uint32_t dh;
-    if (!kCandidates && a.scales) {
-        dh = valid ? (uint32_t)a.scales[blk] : 0u;
-    } else {
-        const float t = amax / 155.0f;
-        const float u = t * 0.61f;
-        dh = f32_to_f16_bits(u);
-    }
-    const bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
-    dh &= 0x7fffu;
-    if (scale_bad && valid && g == 0 && bad_half == 0) report(a.status, IQ_ERR_SCALE_RANGE);
-    const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
-
-    int forced = -1;
-    if (!kCandidates && a.choices && valid) {
-        forced = a.choices[blk * 16 + m];
-        if (forced < 0 || forced > 15) {
-            if (h == 0) report(a.status, IQ_ERR_ARG);
-            forced = -2;
+        int forced = -1;
+        bool choice_bad = false;
+        if (!kCandidates && a.choices) {
+            const int cv = lane < 16 ? a.choices[blk * 16 + lane] : 0;
+            const bool bad = cv < 0 || cv > 15;
+            if (bad && half == 0) report(a.status, IQ_ERR_ARG);
+            choice_bad = __ballot(bad) != 0;
+            forced = choice_bad ? -1 : a.choices[blk * 16 + m];
         }
-    }
-    const uint64_t badc_lanes = __ballot(forced == -2);
-    const uint32_t badc_half = (lane >> 5) ? (uint32_t)(badc_lanes >> 32) : (uint32_t)badc_lanes;
-    const bool bad_block = !valid || grid_bad || bad_half != 0 || scale_bad || badc_half != 0;
-    const bool zero_scale = dh == 0u;
+        const bool bad_block = grid_bad || block_bad || scale_bad || choice_bad;
+        const bool zero_scale = dh == 0u;
+        const bool skip = bad_block || zero_scale;
 
-    // Signs: input signs, the weakest element (smallest (w*x)*x, lowest index)
-    // flipped when the count of negatives is odd.
-    float wx[8];
-    int negmask = 0;
+        // The lane's group: signs, signed weighted values, and the lane's K
+        // slice (elements kb and kb+4) of the two group-side operands.
+        float x[8], w[8];
+        load_group(xblk, wblk, g, skip, x, w);
+        const int neg = group_signs(x, w);
+        const float inv_d = skip ? 1.0f : 1.0f / d;
+        float wxs[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        wx[j] = w[j] * x[j];
-        if (x[j] < 0.0f) negmask |= 1 << j;
-    }
-    if (__popc(negmask) & 1) {
-        int jw = 0;
-        float wk = wx[0] * x[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) {
-            const float v = wx[j] * x[j];
-            if (v < wk) { wk = v; jw = j; }
+        for (int j = 0; j < 8; ++j) {
+            const float wx = w[j] * x[j];
+            wxs[j] = ((neg >> j) & 1) ? -wx : wx;
         }
-        negmask ^= 1 << jw;
-    }
-    const int mask7 = negmask & 0x7f;
-    float wxs[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wxs[j] = ((negmask >> j) & 1) ? -wx[j] : wx[j];
+        // Elements kb and kb+4, read again rather than selected from registers.
+        float bw0 = 1.0f, bw1 = 1.0f, bx0 = 0.0f, bx1 = 0.0f;
+        if (!skip) {
+            bx0 = xblk[g * 8 + kb];
+            bx1 = xblk[g * 8 + kb + 4];
+            if (wblk) { bw0 = wblk[g * 8 + kb]; bw1 = wblk[g * 8 + kb + 4]; }
+        }
+        float bp0 = bw0 * bx0, bp1 = bw1 * bx1;
+        if ((neg >> kb) & 1) bp0 = -bp0;
+        if ((neg >> (kb + 4)) & 1) bp1 = -bp1;
+        bp0 = -2.0f * (bp0 * inv_d);
+        bp1 = -2.0f * (bp1 * inv_d);
 
-    float s[16];
+        // Sweep.  chunk_of: 4-bit chunk index of choice k at bits 4*(k%8) of word k/8.
+        float best[16], snap[16];
+        uint32_t chunk_of[2] = {0u, 0u};
 #pragma unroll
-    for (int k = 0; k < 16; ++k) s[k] = d * (float)(2 * k + 1);
-
-    float best[16], snap[16];
-    int chunk_of[16];
+        for (int k = 0; k < 16; ++k) { best[k] = __builtin_inff(); snap[k] = best[k]; }
+        const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ch = 0; ch < nchunks; ++ch) {
+            for (int tt = 0; tt < kChunkTiles; ++tt) {
+                const int e = (ch * kChunkTiles + tt) * kTile + col;
+                const float2 aq = sq[4 * e + kb];
+                const float2 aq2 = sq2[4 * e + kb];
+                v4f pn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.x, bp0, zero4, 0, 0, 0);
+                pn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.y, bp1, pn, 0, 0, 0);
+                v4f nn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq2.x, bw0, zero4, 0, 0, 0);
+                nn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq2.y, bw1, nn, 0, 0, 0);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) { best[k] = __builtin_inff(); snap[k] = best[k]; chunk_of[k] = 0; }
-
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int e0 = ch * kChunk;
-#pragma unroll 2
-        for (int e = e0; e < e0 + kChunk; e += 2) {
-            const EntryTerms t0 = entry_terms(sgrid, e, wxs, w);
-            const EntryTerms t1 = entry_terms(sgrid, e + 1, wxs, w);
+                for (int k = 0; k < 16; ++k) {
+                    const float mk = (float)(2 * k + 1);
+                    const float k0 = __builtin_fmaf(nn[0], mk, pn[0]);
+                    const float k1 = __builtin_fmaf(nn[1], mk, pn[1]);
+                    const float k2 = __builtin_fmaf(nn[2], mk, pn[2]);
+                    const float k3 = __builtin_fmaf(nn[3], mk, pn[3]);
+                    best[k] = fminf(best[k], fminf(fminf(fminf(k0, k1), k2), k3));
+                }
+            }
+            const uint32_t chrep = (uint32_t)ch * 0x11111111u;
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-                const float k0 = __builtin_fmaf(s[k], t0.n, t0.pn);
-                const float k1 = __builtin_fmaf(s[k], t1.n, t1.pn);
-                best[k] = fminf(fminf(best[k], k0), k1);
+                const uint32_t msk = best[k] < snap[k] ? (0xfu << (4 * (k & 7))) : 0u;
+                chunk_of[k >> 3] = (chunk_of[k >> 3] & ~msk) | (chrep & msk);
+                snap[k] = best[k];
             }
         }
+
+        // Scale-group cost of every local scale: the least minimum of each
+        // group's four lanes, summed over the two groups, times 2k+1.
+        float cost[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            chunk_of[k] = best[k] < snap[k] ? ch : chunk_of[k];
-            snap[k] = best[k];
+            float v = best[k];
+            v = fminf(v, __shfl_xor(v, 16));
+            v = fminf(v, __shfl_xor(v, 32));
+            cost[k] = (float)(2 * k + 1) * (v + __shfl_xor(v, 1));
         }
-    }
 
-    // Scale-group cost of every local scale (same float sum in both lanes).
-    float cost[16];
+        // Entry of local scale k for this lane's group: rescan the lane's part
+        // of its winning chunk, then keep the lane of least matrix-core minimum.
+        auto pick = [&](int k) -> int {
+            float lm = best[0];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        float v = best[k];
-        v += __shfl_xor(v, 1);
-        cost[k] = s[k] * v;
-    }
+            for (int c = 1; c < 16; ++c)
+                if (k == c) lm = best[c];
+            const int tchunk = (int)((chunk_of[k >> 3] >> (4 * (k & 7))) & 0xfu);
+            int idx = rescan<kChunkTiles>(sgrid, tchunk, kb, k, wxs, w, inv_d);
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) {
+                const float om = __shfl_xor(lm, o);
+                const int oi = __shfl_xor(idx, o);
+                if (om < lm || (om == lm && oi < idx)) { lm = om; idx = oi; }
+            }
+            return idx < n ? idx : n - 1;
+        };
 
-    if (!kCandidates) {
-        int kstar = 0;
-        float cb = cost[0];
+        if (!kCandidates) {
+            int kstar = 0;
+            float cbv = cost[0];
 #pragma unroll
-        for (int k = 1; k < 16; ++k)
-            if (cost[k] < cb) { cb = cost[k]; kstar = k; }
-        if (forced >= 0) kstar = forced;
-        const int idx = rescan(sgrid, kstar, best, chunk_of, s, wxs, w, n);
-        // byte 66 + m/2 holds scale group m in its low (even m) or high (odd m) nibble
-        const int kodd = __shfl_xor(kstar, 2);
-        if (!bad_block && !zero_scale) {
-            uint8_t* ob = sout + slot * kBlockBytes;
-            const uint32_t code = (uint32_t)idx | ((uint32_t)mask7 << 9);
-            ob[2 + 2 * g] = (uint8_t)(code & 0xff);
-            ob[3 + 2 * g] = (uint8_t)(code >> 8);
-            if ((g & 3) == 0) ob[66 + (m >> 1)] = (uint8_t)(kstar | (kodd << 4));
-            if (g == 0) {
-                ob[0] = (uint8_t)(dh & 0xff);
-                ob[1] = (uint8_t)(dh >> 8);
+            for (int k = 1; k < 16; ++k)
+                if (cost[k] < cbv) { cbv = cost[k]; kstar = k; }
+            if (forced >= 0) kstar = forced;
+            const int idx = pick(kstar);
+            const int kodd = __shfl_xor(kstar, 2);
+            if (!skip && kb == 0) {
+                uint8_t* ob = sout + slot * kBlockBytes;
+                const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
+                ob[2 + 2 * g] = (uint8_t)(code & 0xff);
+                ob[3 + 2 * g] = (uint8_t)(code >> 8);
+                if ((g & 3) == 0) ob[66 + (m >> 1)] = (uint8_t)(kstar | (kodd << 4));
+                if (g == 0) {
+                    ob[0] = (uint8_t)(dh & 0xff);
+                    ob[1] = (uint8_t)(dh >> 8);
+                }
+            }
+        } else {
+            // Top-C local scales by (cost, k); a zero scale makes every choice
+            // decode to zero with entry 0 and no signs, so the order is k = 0, 1, ...
+            const int C = a.top_c;
+            float xo[8], wo[8];
+            load_group(xblk, wblk, g, bad_block, xo, wo);   // the original values
+            int used = 0;
+            for (int r = 0; r < C; ++r) {
+                int kr = -1;
+                float cr = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const bool free_k = !((used >> k) & 1);
+                    const bool better = zero_scale ? (kr < 0) : (kr < 0 || cost[k] < cr);
+                    if (free_k && better) { kr = k; cr = cost[k]; }
+                }
+                used |= 1 << kr;
+                int idx = pick(kr);
+                int msk = neg & 0x7f;
+                if (zero_scale) { idx = 0; msk = 0; }
+                if (kb == 0) {
+                    const int64_t base = (blk * 16 + m) * C + r;     // [block][m][r]
+                    float ev[8];
+                    if (bad_block) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) ev[j] = 0.0f;
+                    } else {
+                        const float sk = d * (float)(2 * kr + 1);
+                        const float* q = sgrid + kEntryStride * idx;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float sg = (!zero_scale && ((neg >> j) & 1)) ? -1.0f : 1.0f;
+                            ev[j] = (sk * sg) * q[j] - xo[j];
+                        }
+                    }
+                    float4* ep = reinterpret_cast<float4*>(a.cand_err + base * 16 + h * 8);
+                    ep[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
+                    ep[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
+                    if (h == 0) a.cand_choice[base] = kr;
+                    if (a.cand_codes)
+                        a.cand_codes[base * 2 + h] = bad_block ? (uint16_t)0 : (uint16_t)(idx | (msk << 9));
+                }
             }
         }
+    }
+    if (!kCandidates) {
         __syncthreads();
         const int64_t first = (int64_t)blockIdx.x * kBlocksPerWG;
         const int64_t left = a.g.nblocks - first;
         const int nb = left < kBlocksPerWG ? (int)left : kBlocksPerWG;
         uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + first * kBlockBytes);
         for (int i = tid; i < nb * (kBlockBytes / 2); i += kThreads) o16[i] = sout16[i];
-    } else {
-        // Top-C local scales by (cost, k); a zero scale makes every choice decode
-        // to zero with entry 0 and no signs, so the order is k = 0, 1, ...
-        const int C = a.top_c;
-        int used = 0;
-        for (int r = 0; r < C; ++r) {
-            int kr = -1;
-            float cr = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const bool free_k = !((used >> k) & 1);
-                const bool better = zero_scale ? (kr < 0) : (kr < 0 || cost[k] < cr);
-                if (free_k && better) { kr = k; cr = cost[k]; }
-            }
-            used |= 1 << kr;
-            int idx = rescan(sgrid, kr, best, chunk_of, s, wxs, w, n);
-            int msk = mask7;
-            float sg[8];
-            if (zero_scale) {
-                idx = 0;
-                msk = 0;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sg[j] = 1.0f;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) sg[j] = ((negmask >> j) & 1) ? -1.0f : 1.0f;
-            }
-            if (valid) {
-                const int64_t base = (blk * 16 + m) * C + r;     // [block][m][r]
-                float ev[8];
-                if (bad_block) {
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) ev[j] = 0.0f;
-                } else {
-                    float sk = s[0];
-#pragma unroll
-                    for (int c = 1; c < 16; ++c)
-                        if (kr == c) sk = s[c];
-                    const float4 q0 = sgrid[4 * idx], q1 = sgrid[4 * idx + 1];
-                    const float q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) ev[j] = (sk * sg[j]) * q[j] - x[j];
-                }
-                float4* ep = reinterpret_cast<float4*>(a.cand_err + base * 16 + h * 8);
-                ep[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
-                ep[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
-                if (h == 0) a.cand_choice[base] = kr;
-                if (a.cand_codes)
-                    a.cand_codes[base * 2 + h] =
-                        bad_block ? (uint16_t)0 : (uint16_t)(idx | (msk << 9));
-            }
-        }
     }
 }
 
