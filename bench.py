@@ -92,17 +92,26 @@ def record_traffic(name, fmt, pmc_dir):
     """Turn the FETCH_SIZE / WRITE_SIZE counter runs of the encode and of a plain
     256 MiB copy into HBM bytes per launch, written to profiles/traffic_<name>.json.
 
-    pmc_dir holds pmc_FETCH_SIZE/enc_counter_collection.csv,
-    pmc_WRITE_SIZE/enc_counter_collection.csv and the copy runs
+    pmc_dir holds pmc_FETCH_SIZE/enc_counter_collection.csv and
+    pmc_WRITE_SIZE/enc_counter_collection.csv (or pmc_<config>_FETCH_SIZE/...
+    for a workload other than c2) and the copy runs
     pmc_copy_FETCH_SIZE/copy_counter_collection.csv, pmc_copy_WRITE_SIZE/...
     The copy reads and writes exactly 268435456 bytes; each counter is scaled by
     known bytes / (counted KiB * 1024) of that copy."""
     kname = KERNEL_NAMES[fmt].split("<")[0]
     known = 64 * 1024 * 1024 * 4
-    f_enc, nf = _counter_kib(os.path.join(pmc_dir, "pmc_FETCH_SIZE", "enc_counter_collection.csv"),
-                             kname, "FETCH_SIZE")
-    w_enc, nw = _counter_kib(os.path.join(pmc_dir, "pmc_WRITE_SIZE", "enc_counter_collection.csv"),
-                             kname, "WRITE_SIZE")
+    cfg = name.rsplit("_", 1)[-1]
+
+    def enc_csv(counter):
+        # pmc_<config>_<COUNTER>/ if present, else pmc_<COUNTER>/ (the c2 run)
+        for d in ("pmc_%s_%s" % (cfg, counter), "pmc_%s" % counter):
+            path = os.path.join(pmc_dir, d, "enc_counter_collection.csv")
+            if os.path.exists(path):
+                return path
+        raise SystemExit("no %s counter run under %s" % (counter, pmc_dir))
+
+    f_enc, nf = _counter_kib(enc_csv("FETCH_SIZE"), kname, "FETCH_SIZE")
+    w_enc, nw = _counter_kib(enc_csv("WRITE_SIZE"), kname, "WRITE_SIZE")
     f_cp, _ = _counter_kib(os.path.join(pmc_dir, "pmc_copy_FETCH_SIZE", "copy_counter_collection.csv"),
                            "copyBuffer", "FETCH_SIZE")
     w_cp, _ = _counter_kib(os.path.join(pmc_dir, "pmc_copy_WRITE_SIZE", "copy_counter_collection.csv"),
