@@ -11,12 +11,14 @@
 // change of the row's objective when group g takes candidate c is
 // score_c - score_cur, score_c = e_c^T H_gg e_c + 2 e_c^T (r_g - H_gg e_cur).
 //
-// Layout: a 256-thread workgroup runs R rows in lockstep; thread t owns
-// column t of r for all R rows (registers), so the rank-L update
+// Layout: a 256-thread workgroup runs 16 rows in lockstep; thread t owns
+// column t of r for all 16 rows (registers), so the rank-L update
 // r += H[:, g] (e_new - e_cur) reads L rows of the symmetric H, coalesced, once
 // per workgroup and step.  The diagonal blocks H_gg, the rows' current errors,
-// e_c^T H_gg e_c and the per-step vectors live in LDS.  Rows are independent,
-// so the grid is rows / R workgroups.
+// e_c^T H_gg e_c and the per-step vectors live in LDS.  The 32 steps of a row
+// are serial, so every global read on the step path is issued one step ahead
+// (the next group's H rows and candidate vectors) and arrives while the
+// current step computes.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -26,9 +28,8 @@ namespace iqk {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 8;         // rows per workgroup
-constexpr int kMaxL = 32;        // 256 / G for G = 8
-constexpr int kMaxGC = 256;      // G * C <= 16 * 16
+constexpr int kRows = 16;        // rows per workgroup
+constexpr int kMaxC = 16;
 
 struct SearchArgs {
     const float* H;
@@ -36,28 +37,30 @@ struct SearchArgs {
     int32_t* picks;
     int32_t* trace;
     int64_t rows;
-    int G, C, L, sweeps;
+    int C, sweeps;
 };
 
+template <int L>
 __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
 {
-    __shared__ float hdiag[256 * kMaxL];          // H_gg blocks: [g][i][j], L*L each
+    constexpr int G = 256 / L;
+    __shared__ float hdiag[G * L * L];          // H_gg blocks: [g][i][j]
     __shared__ float ecur[kRows][256];
-    __shared__ float qself[kRows][kMaxGC];        // e_gc^T H_gg e_gc, [g*C + c]
-    __shared__ float rg[kRows][kMaxL];            // r restricted to group g
-    __shared__ float rest[kRows][kMaxL];
-    __shared__ float dlt[kRows][kMaxL];           // e_new - e_cur of group g
-    __shared__ float score[kRows][16];
-    __shared__ int pick[kRows][16];
+    __shared__ float qself[kRows][G * kMaxC];   // e_gc^T H_gg e_gc, [g*C + c]
+    __shared__ float cst[kRows][kMaxC][L];      // candidate vectors of the current group
+    __shared__ float rg[kRows][L];              // r restricted to group g
+    __shared__ float rest[kRows][L];
+    __shared__ float dlt[kRows][L];             // e_new - e_cur of group g
+    __shared__ float score[kRows][kMaxC];
+    __shared__ int pick[kRows][G];
     __shared__ int changed[kRows];
 
     const int t = threadIdx.x;
-    const int G = a.G, C = a.C, L = a.L;
+    const int C = a.C;
     const int64_t row0 = (int64_t)blockIdx.x * kRows;
     const int nrows = (int)((a.rows - row0) < kRows ? (a.rows - row0) : kRows);
     const int64_t cstride = (int64_t)G * C * L;   // floats per row of cand
 
-    // Diagonal blocks of H.
     for (int i = t; i < G * L * L; i += kThreads) {
         const int g = i / (L * L), rem = i % (L * L), ii = rem / L, jj = rem % L;
         hdiag[i] = a.H[(int64_t)(g * L + ii) * 256 + g * L + jj];
@@ -69,10 +72,15 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         const int rr = it / (G * C), gc = it % (G * C), g = gc / C;
         float q = 0.0f;
         if (rr < nrows) {
-            const float* e = a.cand + (row0 + rr) * cstride + (int64_t)gc * L;
+            const float* ep = a.cand + (row0 + rr) * cstride + (int64_t)gc * L;
+            float e[L];
+#pragma unroll
+            for (int j = 0; j < L; ++j) e[j] = ep[j];
             const float* hb = hdiag + g * L * L;
+#pragma unroll 4
             for (int i = 0; i < L; ++i) {
                 float y = 0.0f;
+#pragma unroll
                 for (int j = 0; j < L; ++j) y = __builtin_fmaf(hb[i * L + j], e[j], y);
                 q = __builtin_fmaf(e[i], y, q);
             }
@@ -89,9 +97,11 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             if (qself[rr][g * C + c] < qself[rr][g * C + best]) best = c;
         pick[rr][g] = best;
         if (rr < nrows) {
-            const float* e = a.cand + (row0 + rr) * cstride + ((int64_t)g * C + best) * L;
-            for (int i = 0; i < L; ++i) ecur[rr][g * L + i] = e[i];
+            const float* ep = a.cand + (row0 + rr) * cstride + ((int64_t)g * C + best) * L;
+#pragma unroll
+            for (int i = 0; i < L; ++i) ecur[rr][g * L + i] = ep[i];
         } else {
+#pragma unroll
             for (int i = 0; i < L; ++i) ecur[rr][g * L + i] = 0.0f;
         }
     }
@@ -100,45 +110,75 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         for (int it = t; it < nrows * G; it += kThreads)
             a.trace[(row0 + it / G) * G + it % G] = pick[it / G][it % G];
 
-    // r = H e (thread t owns column t; H is symmetric, so H[u][t] is read).
+    // r = H e (thread t owns column t; H is symmetric, so H[u][t] is read),
+    // 16 rows of H in flight at a time.
     float r[kRows];
 #pragma unroll
     for (int rr = 0; rr < kRows; ++rr) r[rr] = 0.0f;
-    for (int u = 0; u < 256; ++u) {
-        const float h = a.H[(int64_t)u * 256 + t];
+    for (int u0 = 0; u0 < 256; u0 += 16) {
+        float h[16];
 #pragma unroll
-        for (int rr = 0; rr < kRows; ++rr) r[rr] = __builtin_fmaf(h, ecur[rr][u], r[rr]);
+        for (int i = 0; i < 16; ++i) h[i] = a.H[(int64_t)(u0 + i) * 256 + t];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int rr = 0; rr < kRows; ++rr) r[rr] = __builtin_fmaf(h[i], ecur[rr][u0 + i], r[rr]);
     }
+
+    // Score threads: (row, candidate) = (t / C, t % C).  Their candidate vector
+    // of the current group and the H rows of the current group are loaded one
+    // step ahead.
+    const bool scorer = t < kRows * C;
+    const int srow = scorer ? t / C : 0;
+    const int scand = scorer ? t % C : 0;
+    const bool srow_ok = scorer && srow < nrows;
+    float cv[L];
+    float hrow[L];
+    auto load_step = [&](int g) {
+        if (srow_ok) {
+            const float* ep = a.cand + (row0 + srow) * cstride + ((int64_t)g * C + scand) * L;
+#pragma unroll
+            for (int i = 0; i < L; ++i) cv[i] = ep[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i) cv[i] = 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < L; ++i) hrow[i] = a.H[(int64_t)(g * L + i) * 256 + t];
+    };
+    load_step(0);
 
     for (int sw = 0; sw < a.sweeps; ++sw) {
         for (int g = 0; g < G; ++g) {
-            // r of group g to LDS.
+            // A: r of group g to LDS.
             if (t >= g * L && t < g * L + L) {
 #pragma unroll
                 for (int rr = 0; rr < kRows; ++rr) rg[rr][t - g * L] = r[rr];
             }
             __syncthreads();
-            // rest = r_g - H_gg e_cur,g
+            // B: rest = r_g - H_gg e_cur,g
             for (int it = t; it < kRows * L; it += kThreads) {
                 const int rr = it / L, i = it % L;
                 const float* hb = hdiag + g * L * L + i * L;
                 float y = 0.0f;
+#pragma unroll
                 for (int j = 0; j < L; ++j) y = __builtin_fmaf(hb[j], ecur[rr][g * L + j], y);
                 rest[rr][i] = rg[rr][i] - y;
             }
             __syncthreads();
-            // score_c = e_c^T H_gg e_c + 2 e_c . rest
-            for (int it = t; it < kRows * C; it += kThreads) {
-                const int rr = it / C, c = it % C;
+            // C: score_c = e_c^T H_gg e_c + 2 e_c . rest; the candidate vector
+            // goes to LDS for the decision.
+            if (scorer) {
                 float dot = 0.0f;
-                if (rr < nrows) {
-                    const float* e = a.cand + (row0 + rr) * cstride + ((int64_t)g * C + c) * L;
-                    for (int i = 0; i < L; ++i) dot = __builtin_fmaf(e[i], rest[rr][i], dot);
+#pragma unroll
+                for (int i = 0; i < L; ++i) {
+                    dot = __builtin_fmaf(cv[i], rest[srow][i], dot);
+                    cst[srow][scand][i] = cv[i];
                 }
-                score[rr][c] = __builtin_fmaf(2.0f, dot, qself[rr][g * C + c]);
+                score[srow][scand] = __builtin_fmaf(2.0f, dot, qself[srow][g * C + scand]);
             }
             __syncthreads();
-            // Decision: the lowest-index minimum, taken only on a strict improvement.
+            // D: the lowest-index minimum, taken only on a strict improvement.
             if (t < kRows) {
                 const int rr = t;
                 int best = 0;
@@ -148,31 +188,35 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
                 const bool move = rr < nrows && score[rr][best] < score[rr][cur];
                 changed[rr] = move;
                 if (move) {
-                    const float* e = a.cand + (row0 + rr) * cstride + ((int64_t)g * C + best) * L;
+#pragma unroll
                     for (int i = 0; i < L; ++i) {
-                        dlt[rr][i] = e[i] - ecur[rr][g * L + i];
-                        ecur[rr][g * L + i] = e[i];
+                        const float en = cst[rr][best][i];
+                        dlt[rr][i] = en - ecur[rr][g * L + i];
+                        ecur[rr][g * L + i] = en;
                     }
                     pick[rr][g] = best;
                 }
             }
             __syncthreads();
-            // r += H[:, g-block] * delta for the rows that moved.
+            // E: r += H[:, g-block] * delta for the rows that moved, then the
+            // next step's H rows and candidate vectors are requested.
 #pragma unroll
             for (int rr = 0; rr < kRows; ++rr) {
                 if (changed[rr]) {
                     float acc = r[rr];
-                    for (int i = 0; i < L; ++i)
-                        acc = __builtin_fmaf(a.H[(int64_t)(g * L + i) * 256 + t], dlt[rr][i], acc);
+#pragma unroll
+                    for (int i = 0; i < L; ++i) acc = __builtin_fmaf(hrow[i], dlt[rr][i], acc);
                     r[rr] = acc;
                 }
             }
-            __syncthreads();
+            load_step(g + 1 < G ? g + 1 : 0);
         }
+        __syncthreads();
         if (a.trace)
             for (int it = t; it < nrows * G; it += kThreads)
                 a.trace[((int64_t)(sw + 1) * a.rows + row0 + it / G) * G + it % G] = pick[it / G][it % G];
     }
+    __syncthreads();
     for (int it = t; it < nrows * G; it += kThreads)
         a.picks[(row0 + it / G) * G + it % G] = pick[it / G][it % G];
 }
@@ -182,9 +226,12 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
 hipError_t launch_choice_search(const float* H, const float* cand, int64_t rows, int G, int C,
                                 int sweeps, int32_t* picks, int32_t* trace, hipStream_t stream)
 {
-    SearchArgs a{H, cand, picks, trace, rows, G, C, 256 / G, sweeps};
+    SearchArgs a{H, cand, picks, trace, rows, C, sweeps};
     const int64_t wgs = (rows + kRows - 1) / kRows;
-    hipLaunchKernelGGL(choice_search_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    if (G == 16)
+        hipLaunchKernelGGL(choice_search_kernel<16>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(choice_search_kernel<32>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

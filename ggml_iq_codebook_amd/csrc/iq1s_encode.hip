@@ -122,9 +122,13 @@ __device__ __forceinline__ void load_group(const float* xblk, const float* wblk,
 
 __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 {
-    __shared__ uint4 sp[kMaxGrid];       // entry e: (q[0..7] + 1/8)^2 as bf16
-    __shared__ uint4 sm[kMaxGrid];       // entry e: (q[0..7] - 1/8)^2 as bf16
-    __shared__ uint4 sq[kMaxGrid];       // entry e: q[0..7] as bf16
+    // Entry e sits at e + e/kChunk: one spare slot per 128-entry chunk, so the
+    // lanes of a rescan that read different chunks (512 words apart without
+    // the slot, a multiple of the 64 banks) spread over the banks.
+    constexpr int kSlots = kMaxGrid + kMaxGrid / kChunk;
+    __shared__ uint4 sp[kSlots];         // (q[0..7] + 1/8)^2 as bf16
+    __shared__ uint4 sm[kSlots];         // (q[0..7] - 1/8)^2 as bf16
+    __shared__ uint4 sq[kSlots];         // q[0..7] as bf16
     __shared__ uint16_t sout16[kBlocksPerWG * kBlockBytes / 2];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
@@ -157,12 +161,13 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 hp[t] = bf16_bits(p * p);          // exact: 81/64, 1/64, 49/64
                 hm[t] = bf16_bits(m * m);
             }
-            sq[e] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                               h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-            sp[e] = make_uint4(hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16),
-                               hp[4] | (hp[5] << 16), hp[6] | (hp[7] << 16));
-            sm[e] = make_uint4(hm[0] | (hm[1] << 16), hm[2] | (hm[3] << 16),
-                               hm[4] | (hm[5] << 16), hm[6] | (hm[7] << 16));
+            const int at = e + e / kChunk;
+            sq[at] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                  h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            sp[at] = make_uint4(hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16),
+                                  hp[4] | (hp[5] << 16), hp[6] | (hp[7] << 16));
+            sm[at] = make_uint4(hm[0] | (hm[1] << 16), hm[2] | (hm[3] << 16),
+                                  hm[4] | (hm[5] << 16), hm[6] | (hm[7] << 16));
         }
         if (bad) sgrid_bad = 1;
     }
@@ -270,10 +275,10 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int ch = 0; ch < nchunks; ++ch) {
             for (int tt = 0; tt < kChunkTiles; ++tt) {
-                const int e = (ch * kChunkTiles + tt) * kTile + col;
-                const v8bf ap = as_v8bf(sp[e]);
-                const v8bf am = as_v8bf(sm[e]);
-                const v8bf aq = as_v8bf(sq[e]);
+                const int at = (ch * kChunkTiles + tt) * kTile + col + ch;
+                const v8bf ap = as_v8bf(sp[at]);
+                const v8bf am = as_v8bf(sm[at]);
+                const v8bf aq = as_v8bf(sq[at]);
                 const v4f up = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, opw, zero4, 0, 0, 0);
                 const v4f um = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, opw, zero4, 0, 0, 0);
                 const v4f vnp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opn2wx, cnp, 0, 0, 0);
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int e = (tchunk * kChunkTiles + tt) * kTile + 4 * kb + r;
-                const uint4 u = sq[e];
+                const uint4 u = sq[e + tchunk];
                 const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
                 float A = 0.0f, M = 0.0f, N = 0.0f;
 #pragma unroll

@@ -113,6 +113,12 @@ __device__ __forceinline__ int group_signs(const float (&x)[8], const float (&w)
 // padded to 18 floats so the four entries the four lanes of a column read
 // together (4 apart) fall in different LDS banks.
 constexpr int kEntryStride = 18;
+// Tracking chunks are 32 or 64 entries, a multiple of the 64 LDS banks apart
+// at that stride, so lanes rescanning different chunks would all hit the same
+// banks; every chunk therefore starts 2 floats later than the stride alone
+// puts it.
+template <int kChunk>
+__device__ __forceinline__ int entry_off(int e) { return kEntryStride * e + 2 * (e / kChunk); }
 
 // VALU rescan: the lowest entry of least key (2k+1)*N - 2P/d among this lane's
 // entries of one chunk.
@@ -127,7 +133,7 @@ __device__ __forceinline__ int rescan(const float* __restrict__ sg, int chunk, i
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = (chunk * kChunkTiles + tt) * kTile + 4 * kb + r;
-            const float2* p = reinterpret_cast<const float2*>(sg + kEntryStride * e);
+            const float2* p = reinterpret_cast<const float2*>(sg + entry_off<kChunkTiles * kTile>(e));
             float q[8], q2[8];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
     constexpr int kChunkTiles = kCandidates ? 2 : 4;
     constexpr int kChunk = kTile * kChunkTiles;
 
-    __shared__ float sgrid[kMaxGrid * kEntryStride];    // entry e: q[0..7], q^2[0..7]
+    __shared__ float sgrid[kMaxGrid * kEntryStride + 2 * (kMaxGrid / 32)];  // q[0..7], q^2[0..7]
     __shared__ float2 sq[kMaxGrid * 4];                 // entry e, slice kb: (q[kb], q[kb+4])
     __shared__ float2 sq2[kMaxGrid * 4];                // same for q^2
     __shared__ uint16_t sout16[kBlocksPerWG * kBlockBytes / 2];
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             const float a0 = a.grid[8 * src + 2 * t], a1 = a.grid[8 * src + 2 * t + 1];
             const float b0 = a.grid[8 * src + t], b1 = a.grid[8 * src + t + 4];
             bad |= !(a0 >= 0.0f && finite_f32(a0) && a1 >= 0.0f && finite_f32(a1));
-            float2* ge = reinterpret_cast<float2*>(sgrid + kEntryStride * e);
+            float2* ge = reinterpret_cast<float2*>(sgrid + entry_off<kChunk>(e));
             ge[t] = make_float2(a0, a1);
             ge[4 + t] = make_float2(a0 * a0, a1 * a1);
             sq[i] = make_float2(b0, b1);
@@ -267,12 +273,6 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         load_group(xblk, wblk, g, skip, x, w);
         const int neg = group_signs(x, w);
         const float inv_d = skip ? 1.0f : 1.0f / d;
-        float wxs[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float wx = w[j] * x[j];
-            wxs[j] = ((neg >> j) & 1) ? -wx : wx;
-        }
         // Elements kb and kb+4, read again rather than selected from registers.
         float bw0 = 1.0f, bw1 = 1.0f, bx0 = 0.0f, bx1 = 0.0f;
         if (!skip) {
@@ -318,6 +318,17 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
                 chunk_of[k >> 3] = (chunk_of[k >> 3] & ~msk) | (chrep & msk);
                 snap[k] = best[k];
             }
+        }
+
+        // The rescans need the signed weighted values again; they are
+        // rebuilt from memory rather than held through the sweep.
+        __asm__ volatile("" ::: "memory");
+        load_group(xblk, wblk, g, skip, x, w);
+        float wxs[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float wx = w[j] * x[j];
+            wxs[j] = ((neg >> j) & 1) ? -wx : wx;
         }
 
         // Scale-group cost of every local scale: the least minimum of each
@@ -397,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
                         for (int j = 0; j < 8; ++j) ev[j] = 0.0f;
                     } else {
                         const float sk = d * (float)(2 * kr + 1);
-                        const float* q = sgrid + kEntryStride * idx;
+                        const float* q = sgrid + entry_off<kChunk>(idx);
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
                             const float sg = (!zero_scale && ((neg >> j) & 1)) ? -1.0f : 1.0f;
