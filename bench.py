@@ -55,6 +55,13 @@ WORKLOADS = {
                            "batched call, per-expert importance"),
     "c5": ("c5_choice_search", "IQ2_XS top-8 candidate encode + local-Hessian choice search, "
                                "4096 rows x one 256-column block, 2 sweeps"),
+    # The same IQ1_S 4096x4096 weighted workload through the other encode outputs.
+    "c2_every": ("c2_iq1s_4096", "IQ1_S weighted every-choice encode (16 payloads from one sweep) "
+                                 "of a 4096x4096 fp32 weight"),
+    "c2_fake": ("c2_iq1s_4096", "IQ1_S weighted fused encode+decode (fake quant, fp32 out) of a "
+                                "4096x4096 fp32 weight"),
+    "c2_pinned": ("c2_iq1s_4096", "IQ1_S weighted re-encode of a 4096x4096 fp32 weight under "
+                                  "pinned super-block scales"),
 }
 
 KERNEL_SOURCES = {
@@ -63,7 +70,7 @@ KERNEL_SOURCES = {
     "iq2_xs": ["ggml_iq_codebook_amd/csrc/iq2xs_encode.hip",
                "ggml_iq_codebook_amd/csrc/device_common.hpp"],
 }
-KERNEL_NAMES = {"iq1_s": "iq1s_encode_kernel", "iq2_xs": "iq2xs_kernel<false>"}
+KERNEL_NAMES = {"iq1_s": "iq1s_encode_kernel<0>", "iq2_xs": "iq2xs_kernel<0>"}
 
 
 def log(*a):
@@ -229,12 +236,30 @@ def main():
         def step():
             err, ch, _ = iq.encode_candidates(w2, grid, imp2, top_c=8, status=status, check=False)
             iq.choice_search(H, err.view(w2.shape[0], 16, 8, 16), sweeps=2)
+    elif args.config.endswith("_every"):
+        B, R, C = w.shape
+        out = torch.empty((16, B, R, C // 256, iq.BLOCK_BYTES[fmt]), dtype=torch.uint8, device=dev)
+
+        def step():
+            iq.encode_every_choice(w, grid, imp, fmt=fmt, out=out, status=status, check=False)
+    elif args.config.endswith("_fake"):
+        xhat = torch.empty_like(w)
+
+        def step():
+            iq.fake_quant(w, grid, imp, fmt=fmt, out=xhat, status=status, check=False)
     else:
         B, R, C = w.shape
         out = torch.empty((B, R, C // 256, iq.BLOCK_BYTES[fmt]), dtype=torch.uint8, device=dev)
+        scales = None
+        if args.config.endswith("_pinned"):
+            # the scales a previous encode chose, as a QAD re-encode pins them
+            iq.encode(w, grid, imp, fmt=fmt, out=out)
+            o = out.view(-1, iq.BLOCK_BYTES[fmt])
+            scales = (o[:, 0].to(torch.int32) | (o[:, 1].to(torch.int32) << 8)).to(torch.int16)
+            scales = scales.view(B, R, C // 256).contiguous()
 
         def step():
-            iq.encode(w, grid, imp, fmt=fmt, out=out, status=status, check=False)
+            iq.encode(w, grid, imp, fmt=fmt, scales=scales, out=out, status=status, check=False)
 
     for _ in range(args.warmup):
         step()

@@ -65,6 +65,10 @@ def load(build_if_missing: bool = True):
     L.iq_status_str.restype = ctypes.c_char_p
     L.iq_encode.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, i32, P, P, P, P, P]
     L.iq_encode.restype = ctypes.c_int
+    L.iq_encode_every_choice.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, i32, P, P, P, P]
+    L.iq_encode_every_choice.restype = ctypes.c_int
+    L.iq_fake_quant.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, i32, P, P, P, P, P, P]
+    L.iq_fake_quant.restype = ctypes.c_int
     L.iq_dequant.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i32, P, P, P]
     L.iq_dequant.restype = ctypes.c_int
     L.iq_encode_candidates.argtypes = [ctypes.c_int, P, i64, i64, P, P, i32, i32, P, P, P, P, P]
@@ -132,16 +136,8 @@ def _raise_on_status(status, where):
         raise IQError(code, where)
 
 
-def encode(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, out=None,
-           status=None, check=True):
-    """Encode a [batch, rows, cols] (or [rows, cols]) fp32 weight.
-
-    Returns the packed payload [batch, rows, cols/256, block_bytes] uint8 (the
-    batch dimension is dropped again for a 2-D weight).  ``importance`` is
-    [batch, cols] / [cols]; ``scales`` pinned fp16 bits [batch, rows, cols/256]
-    (int16/uint16 tensor); ``choices`` forced picks [batch, rows, cols/256, G].
-    With ``check`` the call synchronizes and raises IQError on a data error.
-    """
+def _encode_args(w, grid, importance, fmt, scales, choices):
+    """Checks shared by the encode calls; returns (fmt code, B, R, C, squeeze, scales)."""
     f = _fmt(fmt)
     _dev_tensor(w, torch.float32, "w")
     squeeze = w.dim() == 2
@@ -166,14 +162,33 @@ def encode(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, 
         _dev_tensor(choices, torch.int32, "choices")
         if choices.numel() != B * R * (C // 256) * CHOICE_GROUPS[fmt]:
             raise ValueError("choices must have %d values per block" % CHOICE_GROUPS[fmt])
-    nb = BLOCK_BYTES[fmt]
-    shape = (B, R, C // 256, nb) if C % 256 == 0 else (B, R, 0, nb)
+    return f, B, R, C, squeeze, scales
+
+
+def _out_tensor(out, shape, dtype, device, name):
+    n = 1
+    for v in shape:
+        n *= v
     if out is None:
-        out = torch.empty(shape, dtype=torch.uint8, device=w.device)
-    else:
-        _dev_tensor(out, torch.uint8, "out")
-        if out.numel() != B * R * (C // 256) * nb:
-            raise ValueError("out has the wrong size")
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev_tensor(out, dtype, name)
+    if out.numel() != n:
+        raise ValueError("%s has the wrong size" % name)
+    return out
+
+
+def encode(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, out=None,
+           status=None, check=True):
+    """Encode a [batch, rows, cols] (or [rows, cols]) fp32 weight.
+
+    Returns the packed payload [batch, rows, cols/256, block_bytes] uint8 (the
+    batch dimension is dropped again for a 2-D weight).  ``importance`` is
+    [batch, cols] / [cols]; ``scales`` pinned fp16 bits [batch, rows, cols/256]
+    (int16/uint16 tensor); ``choices`` forced picks [batch, rows, cols/256, G].
+    With ``check`` the call synchronizes and raises IQError on a data error.
+    """
+    f, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, choices)
+    out = _out_tensor(out, (B, R, C // 256, BLOCK_BYTES[fmt]), torch.uint8, w.device, "out")
     status, own = _status_tensor(status, w.device)
     code = load().iq_encode(f, _ptr(w), B, R, C, _ptr(importance), _ptr(grid), grid.shape[0],
                             _ptr(scales), _ptr(choices), _ptr(out), _ptr(status), _stream())
@@ -181,6 +196,49 @@ def encode(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, 
     if check:
         _raise_on_status(status, "iq_encode")
     return out[0] if squeeze else out
+
+
+def encode_every_choice(w, grid, importance=None, *, fmt="iq1_s", scales=None, out=None,
+                        status=None, check=True):
+    """The payload under every one of the 16 choices, from one sweep.
+
+    Returns [16, batch, rows, cols/256, block_bytes] uint8 (no batch dimension
+    for a 2-D weight); entry c equals ``encode(..., choices=full(c))``.
+    """
+    f, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, None)
+    out = _out_tensor(out, (16, B, R, C // 256, BLOCK_BYTES[fmt]), torch.uint8, w.device, "out")
+    status, own = _status_tensor(status, w.device)
+    code = load().iq_encode_every_choice(f, _ptr(w), B, R, C, _ptr(importance), _ptr(grid),
+                                         grid.shape[0], _ptr(scales), _ptr(out), _ptr(status),
+                                         _stream())
+    _check(code, "iq_encode_every_choice")
+    if check:
+        _raise_on_status(status, "iq_encode_every_choice")
+    return out[:, 0] if squeeze else out
+
+
+def fake_quant(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, out=None,
+               packed=False, status=None, check=True):
+    """Encode and decode in one pass: the fp32 weight the payload stands for.
+
+    Returns xhat shaped like ``w`` (bit for bit ``dequant(encode(...))``), or
+    (xhat, payload) with ``packed=True``.
+    """
+    f, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, choices)
+    xhat = _out_tensor(out, (B, R, C), torch.float32, w.device, "out")
+    pk = (torch.empty((B, R, C // 256, BLOCK_BYTES[fmt]), dtype=torch.uint8, device=w.device)
+          if packed else None)
+    status, own = _status_tensor(status, w.device)
+    code = load().iq_fake_quant(f, _ptr(w), B, R, C, _ptr(importance), _ptr(grid), grid.shape[0],
+                                _ptr(scales), _ptr(choices), _ptr(xhat), _ptr(pk), _ptr(status),
+                                _stream())
+    _check(code, "iq_fake_quant")
+    if check:
+        _raise_on_status(status, "iq_fake_quant")
+    if squeeze:
+        xhat = xhat[0]
+        pk = None if pk is None else pk[0]
+    return (xhat, pk) if packed else xhat
 
 
 def dequant(packed, grid, *, fmt="iq1_s", out=None, status=None, check=True):

@@ -52,6 +52,18 @@ iq_status_t geometry(int64_t batch, int64_t rows, int64_t cols, iqk::BlockGeom* 
 
 iq_status_t from_hip(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_HIP; }
 
+hipError_t launch_encode(iq_format_t fmt, const float* w, const float* importance, const float* grid,
+                         int32_t grid_size, const uint16_t* scales, const int32_t* choices,
+                         uint8_t* out, float* xhat, int mode, int32_t* status,
+                         const iqk::BlockGeom& g, hipStream_t stream)
+{
+    return fmt == IQ_FMT_IQ1_S
+        ? iqk::launch_iq1s_encode(w, importance, grid, grid_size, scales, choices, out, xhat, mode,
+                                  status, g, stream)
+        : iqk::launch_iq2xs_encode(w, importance, grid, grid_size, scales, choices, out, xhat, mode,
+                                   status, g, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,10 +118,56 @@ iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t ro
         return IQ_ERR_ARG;
     st = check_device();
     if (st) return st;
-    hipError_t e = fmt == IQ_FMT_IQ1_S
-        ? iqk::launch_iq1s_encode(w, importance, grid, grid_size, scales, choices, out, status, g, stream)
-        : iqk::launch_iq2xs_encode(w, importance, grid, grid_size, scales, choices, out, status, g, stream);
-    return from_hip(e);
+    return from_hip(launch_encode(fmt, w, importance, grid, grid_size, scales, choices, out,
+                                  nullptr, iqk::kModePayload, status, g, stream));
+}
+
+iq_status_t iq_encode_every_choice(iq_format_t fmt, const float* w, int64_t batch, int64_t rows,
+                                   int64_t cols, const float* importance, const float* grid,
+                                   int32_t grid_size, const uint16_t* scales, uint8_t* out,
+                                   int32_t* status, hipStream_t stream)
+{
+    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    iqk::BlockGeom g;
+    iq_status_t st = geometry(batch, rows, cols, &g);
+    if (st) return st;
+    if (!w || !grid || !out || !status) return IQ_ERR_NULL;
+    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
+    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
+    if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
+        !aligned(out, 2) || (scales && !aligned(scales, 2)) || !aligned(status, 4))
+        return IQ_ERR_ARG;
+    st = check_device();
+    if (st) return st;
+    return from_hip(launch_encode(fmt, w, importance, grid, grid_size, scales, nullptr, out,
+                                  nullptr, iqk::kModeEvery, status, g, stream));
+}
+
+iq_status_t iq_fake_quant(iq_format_t fmt, const float* w, int64_t batch, int64_t rows,
+                          int64_t cols, const float* importance, const float* grid,
+                          int32_t grid_size, const uint16_t* scales, const int32_t* choices,
+                          float* xhat, uint8_t* out, int32_t* status, hipStream_t stream)
+{
+    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    iqk::BlockGeom g;
+    iq_status_t st = geometry(batch, rows, cols, &g);
+    if (st) return st;
+    if (!w || !grid || !xhat || !status) return IQ_ERR_NULL;
+    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
+    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
+    if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
+        !aligned(xhat, 16) || (out && !aligned(out, 2)) || (scales && !aligned(scales, 2)) ||
+        (choices && !aligned(choices, 4)) || !aligned(status, 4))
+        return IQ_ERR_ARG;
+    // The decoded values may not overlap the weights: a block's values are
+    // written while the other half of the block may still be reading them.
+    const uintptr_t w0 = reinterpret_cast<uintptr_t>(w), x0 = reinterpret_cast<uintptr_t>(xhat);
+    const uintptr_t bytes = static_cast<uintptr_t>(g.nblocks) * 256u * sizeof(float);
+    if (x0 < w0 + bytes && w0 < x0 + bytes) return IQ_ERR_ARG;
+    st = check_device();
+    if (st) return st;
+    return from_hip(launch_encode(fmt, w, importance, grid, grid_size, scales, choices, out, xhat,
+                                  iqk::kModeFake, status, g, stream));
 }
 
 iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, int64_t rows,

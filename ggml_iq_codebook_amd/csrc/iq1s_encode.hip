@@ -65,7 +65,9 @@ struct Iq1sArgs {
     const float* grid;
     const uint16_t* scales;
     const int32_t* choices;
-    uint8_t* out;
+    uint8_t* out;            // payload: [nblocks][50]; every choice: [16][nblocks][50]; may be
+                             // NULL for the fake-quant output
+    float* xhat;             // fake quant: decoded values [nblocks][256]
     int32_t* status;
     BlockGeom g;
     int grid_size;
@@ -120,8 +122,49 @@ __device__ __forceinline__ void load_group(const float* xblk, const float* wblk,
     }
 }
 
+// VALU rescan for choice cs = k + 8*deltabit: the lowest of this lane's
+// entries of chunk tchunk with the least key (2k+1)*U - 2V/d, recomputed in
+// fp32 from the group's values and weights (read again from memory rather
+// than held through the sweep).
+__device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, int kb, int cs,
+                                      const float* xblk, const float* wblk, int g, bool zero_block,
+                                      float w64, float b4, float inv_d)
+{
+    float x[8], w[8];
+    __asm__ volatile("" ::: "memory");
+    load_group(xblk, wblk, g, zero_block, x, w);
+    const float mk = (float)(2 * (cs & 7) + 1);
+    const float dl = (cs >> 3) ? -0.25f : 0.25f;      // 2*delta
+    const float bd = (cs >> 3) ? b4 : -b4;
+    int idx = -1;
+    float vbest = 0.0f;
+    for (int tt = 0; tt < kChunkTiles; ++tt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = (tchunk * kChunkTiles + tt) * kTile + 4 * kb + r;
+            const uint4 u = sq[e + tchunk];
+            const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+            float A = 0.0f, M = 0.0f, N = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                A = __builtin_fmaf(w[j] * x[j], q, A);
+                M = __builtin_fmaf(w[j], q, M);
+                N = __builtin_fmaf(w[j], fabsf(q), N);
+            }
+            const float U = __builtin_fmaf(M, dl, N + w64);
+            const float key = __builtin_fmaf(U, mk, __builtin_fmaf(A, -2.0f, bd) * inv_d);
+            if (idx < 0 || key < vbest) { vbest = key; idx = e; }
+        }
+    }
+    return idx;
+}
+
+template <int kMode>
 __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 {
+    // Payloads staged in LDS: one per block, or one per block and choice.
+    constexpr int kPayloads = kMode == kModeEvery ? 16 : 1;
     // Entry e sits at e + e/kChunk: one spare slot per 128-entry chunk, so the
     // lanes of a rescan that read different chunks (512 words apart without
     // the slot, a multiple of the 64 banks) spread over the banks.
@@ -129,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     __shared__ uint4 sp[kSlots];         // (q[0..7] + 1/8)^2 as bf16
     __shared__ uint4 sm[kSlots];         // (q[0..7] - 1/8)^2 as bf16
     __shared__ uint4 sq[kSlots];         // q[0..7] as bf16
-    __shared__ uint16_t sout16[kBlocksPerWG * kBlockBytes / 2];
+    __shared__ uint16_t sout16[kPayloads * kBlocksPerWG * kBlockBytes / 2];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
 
@@ -141,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     const int npad = nchunks * kChunk;
 
     if (tid == 0) sgrid_bad = 0;
-    for (int i = tid; i < kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
+    for (int i = tid; i < kPayloads * kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     // Stage the grid as bf16 (exact for ternary values); entries past the end
     // repeat the last one, which always comes first in index order.
@@ -231,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         // Forced choices: every wave of the block checks all 8 of them.
         int forced = -1;
         bool choice_bad = false;
-        if (a.choices) {
+        if (kMode != kModeEvery && a.choices) {
             const int cv = lane < 8 ? a.choices[blk * 8 + lane] : 0;
             const bool bad = cv < 0 || cv > 15;
             if (bad && half == 0) report(a.status, IQ_ERR_ARG);
@@ -324,85 +367,97 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         }
         if (forced >= 0) cstar = forced;
 
-        // Rescan this lane's entries of the chunk that holds its minimum of the
-        // chosen choice, on the VALU.
-        float lane_min = best[0];
+        // Entry of choice cs for this lane's group: the lane rescans its
+        // entries of the chunk that holds its minimum of that choice, then the
+        // lane of the column whose matrix-core minimum is least is kept; the
+        // payload takes the low byte per group, the qh word per sub-block and
+        // d per block.
+        for (int it = 0; it < (kMode == kModeEvery ? 16 : 1); ++it) {
+            const int cs = kMode == kModeEvery ? it : cstar;
+            float lane_min = best[0];
 #pragma unroll
-        for (int c = 1; c < 16; ++c)
-            if (cstar == c) lane_min = best[c];
-        const int tchunk = (int)((chunk_of[cstar >> 3] >> (4 * (cstar & 7))) & 0xfu);
-        __asm__ volatile("" ::: "memory");    // reload x and w instead of keeping them live
-        load_group(xblk, wblk, g, zero_block, x, w);
-        const int kstar = cstar & 7;
-        const int dbit = cstar >> 3;
-        const float mk = (float)(2 * kstar + 1);
-        const float dl = dbit ? -0.25f : 0.25f;      // 2*delta
-        const float bd = dbit ? b4 : -b4;
-        int idx = -1;
-        float vbest = 0.0f;
-        for (int tt = 0; tt < kChunkTiles; ++tt) {
+            for (int c = 1; c < 16; ++c)
+                if (cs == c) lane_min = best[c];
+            const int tchunk = (int)((chunk_of[cs >> 3] >> (4 * (cs & 7))) & 0xfu);
+            int idx = rescan(sq, tchunk, kb, cs, xblk, wblk, g, zero_block, w64, b4, inv_d);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int e = (tchunk * kChunkTiles + tt) * kTile + 4 * kb + r;
-                const uint4 u = sq[e + tchunk];
+            for (int o = 16; o <= 32; o <<= 1) {
+                const float om = __shfl_xor(lane_min, o);
+                const int oi = __shfl_xor(idx, o);
+                if (om < lane_min || (om == lane_min && oi < idx)) { lane_min = om; idx = oi; }
+            }
+            idx = idx < n ? idx : n - 1;
+            int hi = ((idx >> 8) & 7) << (3 * lq);
+            hi |= __shfl_xor(hi, 1);
+            hi |= __shfl_xor(hi, 2);
+            if (!zero_block && kb == 0) {
+                uint8_t* ob = sout + (it * kBlocksPerWG + slot) * kBlockBytes;
+                ob[2 + 4 * sub + lq] = (uint8_t)(idx & 0xff);
+                if (lq == 0) {
+                    const uint32_t qh = (uint32_t)hi | ((uint32_t)cs << 12);
+                    ob[34 + 2 * sub] = (uint8_t)(qh & 0xff);
+                    ob[35 + 2 * sub] = (uint8_t)(qh >> 8);
+                }
+                if (g == 0) {
+                    ob[0] = (uint8_t)(dh & 0xff);
+                    ob[1] = (uint8_t)(dh >> 8);
+                }
+            }
+            if (kMode == kModeFake && kb == 0) {
+                // The decoded group, d*(2k+1)*(q + delta) with the payload's
+                // fields (a zero block decodes as the all-zero payload does;
+                // a rejected block is written as zeros).
+                const uint32_t dz = zero_block ? 0u : dh;
+                const int ez = zero_block ? 0 : idx;
+                const int cz = zero_block ? 0 : cs;
+                const float sk = f16_bits_to_f32(dz) * (float)(2 * (cz & 7) + 1);
+                const float delta = (cz >> 3) ? -0.125f : 0.125f;
+                const uint4 u = sq[ez + ez / kChunk];
                 const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-                float A = 0.0f, M = 0.0f, N = 0.0f;
+                const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
+                float v[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-                    A = __builtin_fmaf(w[j] * x[j], q, A);
-                    M = __builtin_fmaf(w[j], q, M);
-                    N = __builtin_fmaf(w[j], fabsf(q), N);
+                    v[j] = rejected ? 0.0f : sk * (q + delta);
                 }
-                const float U = __builtin_fmaf(M, dl, N + w64);
-                const float key = __builtin_fmaf(U, mk, __builtin_fmaf(A, -2.0f, bd) * inv_d);
-                if (idx < 0 || key < vbest) { vbest = key; idx = e; }
-            }
-        }
-        // Keep the lane of the column whose matrix-core minimum is least.
-#pragma unroll
-        for (int o = 16; o <= 32; o <<= 1) {
-            const float om = __shfl_xor(lane_min, o);
-            const int oi = __shfl_xor(idx, o);
-            if (om < lane_min || (om == lane_min && oi < idx)) { lane_min = om; idx = oi; }
-        }
-        idx = idx < n ? idx : n - 1;
-
-        // Pack: low byte per group, qh word per sub-block, d per block.
-        int hi = ((idx >> 8) & 7) << (3 * lq);
-        hi |= __shfl_xor(hi, 1);
-        hi |= __shfl_xor(hi, 2);
-        if (!zero_block && kb == 0) {
-            uint8_t* ob = sout + slot * kBlockBytes;
-            ob[2 + 4 * sub + lq] = (uint8_t)(idx & 0xff);
-            if (lq == 0) {
-                const uint32_t qh = (uint32_t)hi | ((uint32_t)kstar << 12) | ((uint32_t)dbit << 15);
-                ob[34 + 2 * sub] = (uint8_t)(qh & 0xff);
-                ob[35 + 2 * sub] = (uint8_t)(qh >> 8);
-            }
-            if (g == 0) {
-                ob[0] = (uint8_t)(dh & 0xff);
-                ob[1] = (uint8_t)(dh >> 8);
+                float4* o = reinterpret_cast<float4*>(a.xhat + blk * kBlockElems + g * 8);
+                o[0] = make_float4(v[0], v[1], v[2], v[3]);
+                o[1] = make_float4(v[4], v[5], v[6], v[7]);
             }
         }
     }
-    __syncthreads();
-    const int64_t first = (int64_t)blockIdx.x * kBlocksPerWG;
-    const int64_t left = a.g.nblocks - first;
-    const int nb = left < kBlocksPerWG ? (int)left : kBlocksPerWG;
-    uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + first * kBlockBytes);
-    for (int i = tid; i < nb * (kBlockBytes / 2); i += kThreads) o16[i] = sout16[i];
+    if (a.out) {
+        __syncthreads();
+        const int64_t first = (int64_t)blockIdx.x * kBlocksPerWG;
+        const int64_t left = a.g.nblocks - first;
+        const int nb = left < kBlocksPerWG ? (int)left : kBlocksPerWG;
+        for (int cs = 0; cs < kPayloads; ++cs) {
+            uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (cs * a.g.nblocks + first) * kBlockBytes);
+            const uint16_t* s16 = sout16 + cs * kBlocksPerWG * (kBlockBytes / 2);
+            for (int i = tid; i < nb * (kBlockBytes / 2); i += kThreads) o16[i] = s16[i];
+        }
+    }
 }
 
 }  // namespace
 
 hipError_t launch_iq1s_encode(const float* w, const float* imp, const float* grid, int grid_size,
                               const uint16_t* scales, const int32_t* choices, uint8_t* out,
-                              int32_t* status, const BlockGeom& g, hipStream_t stream)
+                              float* xhat, int mode, int32_t* status, const BlockGeom& g,
+                              hipStream_t stream)
 {
-    Iq1sArgs a{w, imp, grid, scales, choices, out, status, g, grid_size};
+    Iq1sArgs a{w, imp, grid, scales, choices, out, xhat, status, g, grid_size};
     const int64_t wgs = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
-    hipLaunchKernelGGL(iq1s_encode_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    if (mode == kModeEvery)
+        hipLaunchKernelGGL(iq1s_encode_kernel<kModeEvery>, dim3((unsigned)wgs), dim3(kThreads), 0,
+                           stream, a);
+    else if (mode == kModeFake)
+        hipLaunchKernelGGL(iq1s_encode_kernel<kModeFake>, dim3((unsigned)wgs), dim3(kThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(iq1s_encode_kernel<kModePayload>, dim3((unsigned)wgs), dim3(kThreads), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -55,7 +55,9 @@ struct Iq2xsArgs {
     const float* grid;
     const uint16_t* scales;
     const int32_t* choices;
-    uint8_t* out;            // encode: packed payload
+    uint8_t* out;            // payload [nblocks][74], every choice [16][nblocks][74]; may be
+                             // NULL for the fake-quant output
+    float* xhat;             // fake quant: decoded values [nblocks][256]
     float* cand_err;         // candidates
     int32_t* cand_choice;
     uint16_t* cand_codes;
@@ -154,9 +156,11 @@ __device__ __forceinline__ int rescan(const float* __restrict__ sg, int chunk, i
     return idx;
 }
 
-template <bool kCandidates>
+template <int kMode>
 __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 {
+    constexpr bool kCandidates = kMode == kModeCandidates;
+    constexpr int kPayloads = kMode == kModeEvery ? 16 : 1;
     // Tiles per tracking chunk: 4 (64 entries) for the encode, 2 (32
     // entries) for the candidates, whose epilogue rescans top_c choices.
     constexpr int kChunkTiles = kCandidates ? 2 : 4;
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
     __shared__ float sgrid[kMaxGrid * kEntryStride + 2 * (kMaxGrid / 32)];  // q[0..7], q^2[0..7]
     __shared__ float2 sq[kMaxGrid * 4];                 // entry e, slice kb: (q[kb], q[kb+4])
     __shared__ float2 sq2[kMaxGrid * 4];                // same for q^2
-    __shared__ uint16_t sout16[kBlocksPerWG * kBlockBytes / 2];
+    __shared__ uint16_t sout16[kPayloads * kBlocksPerWG * kBlockBytes / 2];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
 
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 
     if (tid == 0) sgrid_bad = 0;
     if (!kCandidates)
-        for (int i = tid; i < kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
+        for (int i = tid; i < kPayloads * kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     {
         int bad = 0;
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 
         int forced = -1;
         bool choice_bad = false;
-        if (!kCandidates && a.choices) {
+        if ((kMode == kModePayload || kMode == kModeFake) && a.choices) {
             const int cv = lane < 16 ? a.choices[blk * 16 + lane] : 0;
             const bool bad = cv < 0 || cv > 15;
             if (bad && half == 0) report(a.status, IQ_ERR_ARG);
@@ -360,7 +364,23 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             return idx < n ? idx : n - 1;
         };
 
-        if (!kCandidates) {
+        if (kMode == kModeEvery) {
+            // Every local scale k for every scale group: the payload forced to k.
+            for (int k = 0; k < 16; ++k) {
+                const int idx = pick(k);
+                if (!skip && kb == 0) {
+                    uint8_t* ob = sout + (k * kBlocksPerWG + slot) * kBlockBytes;
+                    const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
+                    ob[2 + 2 * g] = (uint8_t)(code & 0xff);
+                    ob[3 + 2 * g] = (uint8_t)(code >> 8);
+                    if ((g & 3) == 0) ob[66 + (m >> 1)] = (uint8_t)(k | (k << 4));
+                    if (g == 0) {
+                        ob[0] = (uint8_t)(dh & 0xff);
+                        ob[1] = (uint8_t)(dh >> 8);
+                    }
+                }
+            }
+        } else if (!kCandidates) {
             int kstar = 0;
             float cbv = cost[0];
 #pragma unroll
@@ -369,9 +389,9 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             if (forced >= 0) kstar = forced;
             const int idx = pick(kstar);
             const int kodd = __shfl_xor(kstar, 2);
+            const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
             if (!skip && kb == 0) {
                 uint8_t* ob = sout + slot * kBlockBytes;
-                const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
                 ob[2 + 2 * g] = (uint8_t)(code & 0xff);
                 ob[3 + 2 * g] = (uint8_t)(code >> 8);
                 if ((g & 3) == 0) ob[66 + (m >> 1)] = (uint8_t)(kstar | (kodd << 4));
@@ -379,6 +399,25 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
                     ob[0] = (uint8_t)(dh & 0xff);
                     ob[1] = (uint8_t)(dh >> 8);
                 }
+            }
+            if (kMode == kModeFake && kb == 0) {
+                // The decoded group, d*(2k+1)*sign*q with the payload's fields
+                // (the 8th sign from even parity of the 7-bit mask; a zero
+                // block decodes as the all-zero payload does; a rejected block
+                // is written as zeros).
+                const uint32_t cz = skip ? 0u : code;
+                const int kz = skip ? 0 : kstar;
+                const float sk = f16_bits_to_f32(skip ? 0u : dh) * (float)(2 * kz + 1);
+                const uint32_t mask = cz >> 9;
+                const uint32_t signs = mask | ((__popc(mask) & 1u) << 7);
+                const float* q = sgrid + entry_off<kChunk>((int)(cz & 0x1ffu));
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[j] = bad_block ? 0.0f : (((signs >> j) & 1u) ? -sk : sk) * q[j];
+                float4* o = reinterpret_cast<float4*>(a.xhat + blk * kBlockElems + g * 8);
+                o[0] = make_float4(v[0], v[1], v[2], v[3]);
+                o[1] = make_float4(v[4], v[5], v[6], v[7]);
             }
         } else {
             // Top-C local scales by (cost, k); a zero scale makes every choice
@@ -425,13 +464,16 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             }
         }
     }
-    if (!kCandidates) {
+    if (!kCandidates && a.out) {
         __syncthreads();
         const int64_t first = (int64_t)blockIdx.x * kBlocksPerWG;
         const int64_t left = a.g.nblocks - first;
         const int nb = left < kBlocksPerWG ? (int)left : kBlocksPerWG;
-        uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + first * kBlockBytes);
-        for (int i = tid; i < nb * (kBlockBytes / 2); i += kThreads) o16[i] = sout16[i];
+        for (int k = 0; k < kPayloads; ++k) {
+            uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (k * a.g.nblocks + first) * kBlockBytes);
+            const uint16_t* s16 = sout16 + k * kBlocksPerWG * (kBlockBytes / 2);
+            for (int i = tid; i < nb * (kBlockBytes / 2); i += kThreads) o16[i] = s16[i];
+        }
     }
 }
 
@@ -439,12 +481,18 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 
 hipError_t launch_iq2xs_encode(const float* w, const float* imp, const float* grid, int grid_size,
                                const uint16_t* scales, const int32_t* choices, uint8_t* out,
-                               int32_t* status, const BlockGeom& g, hipStream_t stream)
+                               float* xhat, int mode, int32_t* status, const BlockGeom& g,
+                               hipStream_t stream)
 {
-    Iq2xsArgs a{w, imp, grid, scales, choices, out, nullptr, nullptr, nullptr, status, g,
+    Iq2xsArgs a{w, imp, grid, scales, choices, out, xhat, nullptr, nullptr, nullptr, status, g,
                 grid_size, 0};
     const int64_t wgs = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
-    hipLaunchKernelGGL(iq2xs_kernel<false>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    if (mode == kModeEvery)
+        hipLaunchKernelGGL(iq2xs_kernel<kModeEvery>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    else if (mode == kModeFake)
+        hipLaunchKernelGGL(iq2xs_kernel<kModeFake>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(iq2xs_kernel<kModePayload>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -453,10 +501,10 @@ hipError_t launch_iq2xs_candidates(const float* w, const float* imp, const float
                                    uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
                                    hipStream_t stream)
 {
-    Iq2xsArgs a{w, imp, grid, nullptr, nullptr, nullptr, cand_err, cand_choice, cand_codes,
-                status, g, grid_size, top_c};
+    Iq2xsArgs a{w, imp, grid, nullptr, nullptr, nullptr, nullptr, cand_err, cand_choice,
+                cand_codes, status, g, grid_size, top_c};
     const int64_t wgs = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
-    hipLaunchKernelGGL(iq2xs_kernel<true>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(iq2xs_kernel<kModeCandidates>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -17,13 +17,20 @@ struct BlockGeom {
     int64_t cols;
 };
 
+// What an encode launch writes: the payload; the payload under every one of
+// the 16 choices ([16][nblocks][block_bytes]); the decoded values (and the
+// payload when `out` is given); or the top-C candidates.
+enum EncodeMode { kModePayload = 0, kModeEvery = 1, kModeFake = 2, kModeCandidates = 3 };
+
 hipError_t launch_iq1s_encode(const float* w, const float* imp, const float* grid, int grid_size,
                               const uint16_t* scales, const int32_t* choices, uint8_t* out,
-                              int32_t* status, const BlockGeom& g, hipStream_t stream);
+                              float* xhat, int mode, int32_t* status, const BlockGeom& g,
+                              hipStream_t stream);
 
 hipError_t launch_iq2xs_encode(const float* w, const float* imp, const float* grid, int grid_size,
                                const uint16_t* scales, const int32_t* choices, uint8_t* out,
-                               int32_t* status, const BlockGeom& g, hipStream_t stream);
+                               float* xhat, int mode, int32_t* status, const BlockGeom& g,
+                               hipStream_t stream);
 
 hipError_t launch_iq2xs_candidates(const float* w, const float* imp, const float* grid,
                                    int grid_size, int top_c, float* cand_err, int32_t* cand_choice,

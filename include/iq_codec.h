@@ -115,6 +115,40 @@ iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t ro
                       int32_t* status, hipStream_t stream);
 
 /*
+ * iq_encode_every_choice -- the payload under every choice from one sweep
+ * ("[2/4] Encode every GGML IQ choice in one pass" #3159): out[c] is, byte for
+ * byte, the iq_encode payload with every choice group forced to c.  The input
+ * of the local-Hessian search, which scores each choice's decoded error.
+ *
+ *   w, importance, grid, scales, status: as iq_encode.
+ *   out  [16][batch][rows][cols/256][block_bytes] uint8 (choice-major).
+ * Errors as iq_encode; a block with a data error is zero in all 16 payloads.
+ */
+iq_status_t iq_encode_every_choice(iq_format_t fmt, const float* w, int64_t batch, int64_t rows,
+                                   int64_t cols, const float* importance, const float* grid,
+                                   int32_t grid_size, const uint16_t* scales, uint8_t* out,
+                                   int32_t* status, hipStream_t stream);
+
+/*
+ * iq_fake_quant -- encode and decode in one pass: the fp32 weights the
+ * payload stands for, which the fake-quant forward uses and re-encodes after
+ * every optimizer step ("Re-encode GGML weights after every optimizer step, so
+ * Megatron QAD updates their codes" #3210, with the static scales of #3197:
+ * re-encode under pinned d).  xhat is, bit for bit,
+ * iq_dequant(iq_encode(...)) with the same arguments.
+ *
+ *   w, importance, grid, scales, choices, status: as iq_encode.
+ *   xhat  [batch][rows][cols] fp32 output; may not overlap w.
+ *   out   NULL, or the payload [batch][rows][cols/256][block_bytes] as well.
+ * Errors as iq_encode (IQ_ERR_ARG also when xhat overlaps w); a block with a
+ * data error decodes to zeros.
+ */
+iq_status_t iq_fake_quant(iq_format_t fmt, const float* w, int64_t batch, int64_t rows,
+                          int64_t cols, const float* importance, const float* grid,
+                          int32_t grid_size, const uint16_t* scales, const int32_t* choices,
+                          float* xhat, uint8_t* out, int32_t* status, hipStream_t stream);
+
+/*
  * iq_dequant -- decode a payload to fp32 (#2450 review worked example:
  * IQ1_S value = d*(2k+1)*(q + delta), delta = -1/8 when bit 15 is set;
  * IQ2_XS value = d*(2k+1)*sign*q with the 8th sign of a group implied by even

@@ -159,6 +159,25 @@ def encode(fmt: str, w, grid, importance=None, scales=None, choices=None) -> np.
     return out.reshape(B, R, C // 256, nb)
 
 
+def encode_every_choice(fmt: str, w, grid, importance=None, scales=None) -> np.ndarray:
+    """The payload under every choice: [16, B, R, C/256, bytes], entry c being
+    the encode with every choice group forced to c, which is how the
+    every-choice encode is defined ("[2/4] Encode every GGML IQ choice in one
+    pass" #3159, usage: packed[c] equals the forced encode with choices full
+    of c)."""
+    B, R, C = np.shape(w)
+    G = NUM_CHOICE_GROUPS[fmt]
+    return np.stack([encode(fmt, w, grid, importance, scales,
+                            choices=np.full((B, R, C // 256, G), c, dtype=np.int32))
+                     for c in range(16)])
+
+
+def fake_quant(fmt: str, w, grid, importance=None, scales=None, choices=None) -> np.ndarray:
+    """The decoded encode, float64 [B, R, C]: what a fake-quant forward uses
+    ("Re-encode GGML weights after every optimizer step" #3210)."""
+    return decode(fmt, encode(fmt, w, grid, importance, scales, choices), grid)
+
+
 def encode_blocks(fmt: str, x, grid, imp=None, scales=None) -> np.ndarray:
     """Encode independent 256-value blocks: x [n, 256], imp None or [n, 256]
     (each block's own importance slice), scales None or fp16 bits [n].

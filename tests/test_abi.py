@@ -27,7 +27,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "iq_choice_search", "iq_dequant", "iq_encode", "iq_encode_candidates",
-        "iq_format_info", "iq_status_str"])
+        "iq_encode_every_choice", "iq_fake_quant", "iq_format_info", "iq_status_str"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -89,3 +89,20 @@ def test_other_entry_points_argument_errors_need_no_gpu(lib):
     assert cs(FAKE, FAKE, 4, 16, 8, 9, FAKE, None, None) == 8
     assert cs(FAKE, FAKE, 0, 16, 8, 2, FAKE, None, None) == 3
     assert cs(None, FAKE, 4, 16, 8, 2, FAKE, None, None) == 1
+
+
+def test_every_choice_and_fake_quant_argument_errors_need_no_gpu(lib):
+    ev = lib.iq_encode_every_choice
+    # fmt, w, batch, rows, cols, imp, grid, grid_size, scales, out, status, stream
+    assert ev(7, FAKE, 1, 1, 256, None, FAKE, 16, None, FAKE, FAKE, None) == 2
+    assert ev(0, FAKE, 1, 1, 300, None, FAKE, 16, None, FAKE, FAKE, None) == 3
+    assert ev(1, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None) == 1
+    assert ev(1, FAKE, 1, 1, 256, None, FAKE, 513, None, FAKE, FAKE, None) == 4
+    fq = lib.iq_fake_quant
+    # fmt, w, batch, rows, cols, imp, grid, grid_size, scales, choices, xhat, out, status, stream
+    assert fq(0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, None, None, FAKE, None) == 1
+    assert fq(0, FAKE, 1, 1, 0, None, FAKE, 16, None, None, P(0x200000), None, FAKE, None) == 3
+    assert fq(0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, P(0x200008), None, FAKE, None) == 8
+    # the decoded values may not overlap the weights (checked before any device access)
+    assert fq(0, FAKE, 1, 2, 256, None, FAKE, 16, None, None, P(0x100400), None, FAKE, None) == 8
+    assert fq(0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None, FAKE, None) == 8

@@ -470,6 +470,66 @@ def test_forced_choices_reproduce_the_free_encode(fmt):
 
 
 # --------------------------------------------------------------------------
+# every-choice payloads and the decoded encode (fake quant)
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+def test_every_choice_payloads_carry_their_choice_and_contain_the_free_encode(fmt):
+    # #3159: packed[c] is the encode with every choice group forced to c.  So
+    # every unit of packed[c] carries choice c, and per unit the least weighted
+    # error over c is the free encode's, reached first at the free encode's
+    # own choice (the free encode is pinned by brute force above).
+    grid = workloads.iq1s_grid(192) if fmt == "iq1_s" else workloads.iq2xs_grid(96)
+    w = workloads.normal_weight((2, 3, 256), 131)
+    w[1, 2] = 0.0                                    # a zero block: all-zero in every payload
+    imp = workloads.lognormal_importance((2, 256), 132)
+    every = oracle.encode_every_choice(fmt, w, grid, imp)
+    assert every.shape == (16, 2, 3, 1, oracle.BLOCK_BYTES[fmt])
+    free = oracle.encode(fmt, w, grid, imp)
+    assert not every[:, 1, 2].any()
+    live = np.ones((6,), bool)
+    live[5] = False
+    for c in range(16):
+        if fmt == "iq1_s":
+            d, _, k, sgn = iq1s_fields(every[c])
+            assert np.all((k + 8 * sgn)[live] == c)
+        else:
+            d, _, _, sc = iq2xs_fields(every[c])
+            assert np.all(sc[live] == c)
+        np.testing.assert_array_equal(d, iq1s_fields(free)[0] if fmt == "iq1_s" else iq2xs_fields(free)[0])
+    errs = np.stack([oracle.unit_errors(fmt, every[c], w, grid, imp) for c in range(16)])
+    e_free = oracle.unit_errors(fmt, free, w, grid, imp)
+    np.testing.assert_allclose(errs.min(axis=0), e_free, rtol=1e-12, atol=0)
+    if fmt == "iq1_s":
+        _, _, k, sgn = iq1s_fields(free)
+        c_free = (k + 8 * sgn).reshape(e_free.shape)
+    else:
+        c_free = iq2xs_fields(free)[3].reshape(e_free.shape)
+    first = np.argmax(errs <= e_free[None] * (1 + 1e-12), axis=0)
+    live_units = np.repeat(live, e_free.shape[-1] if e_free.ndim == 2 else 1).reshape(c_free.shape)
+    np.testing.assert_array_equal(first[live_units], c_free[live_units])
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+def test_fake_quant_is_the_decoded_encode(fmt):
+    # The fake-quant weight is decode(encode(w)); decoding the printed worked
+    # example is pinned above, so here its error must be the unit errors the
+    # encode reports, and re-encoding it under its own scales is a fixed point.
+    grid = workloads.iq1s_grid(256) if fmt == "iq1_s" else workloads.iq2xs_grid(128)
+    w = workloads.normal_weight((1, 4, 512), 141)
+    imp = workloads.lognormal_importance((1, 512), 142)
+    xh = oracle.fake_quant(fmt, w, grid, imp)
+    p = oracle.encode(fmt, w, grid, imp)
+    wt = np.broadcast_to(imp.astype(np.float64)[:, None, :], w.shape)
+    e = (wt * (w.astype(np.float64) - xh) ** 2).reshape(-1, 256 // oracle.NUM_CHOICE_GROUPS[fmt]).sum(1)
+    np.testing.assert_allclose(e, oracle.unit_errors(fmt, p, w, grid, imp).reshape(-1), rtol=1e-12)
+    d = oracle.predict_scales(fmt, w).reshape(1, 4, 2)
+    again = oracle.fake_quant(fmt, xh.astype(np.float32), grid, imp, scales=d)
+    np.testing.assert_array_equal(again, xh)
+
+
+# --------------------------------------------------------------------------
 # candidates (top-C choices per IQ2_XS scale group)
 # --------------------------------------------------------------------------
 
