@@ -75,6 +75,8 @@ def load(build_if_missing: bool = True):
     L.iq_encode_candidates.restype = ctypes.c_int
     L.iq_choice_search.argtypes = [P, P, i64, i32, i32, i32, P, P, P]
     L.iq_choice_search.restype = ctypes.c_int
+    L.iq_choice_search_blocks.argtypes = [P, P, i64, i64, i32, i32, i32, P, P, P]
+    L.iq_choice_search_blocks.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -268,11 +270,12 @@ def dequant(packed, grid, *, fmt="iq1_s", out=None, status=None, check=True):
 
 def encode_candidates(w, grid, importance=None, *, fmt="iq2_xs", top_c=8, codes=False,
                       status=None, check=True):
-    """Top-C choices per scale group of every 256-column block of [rows, cols].
+    """Top-C choices per choice group of every 256-column block of [rows, cols].
 
-    Returns (cand_err [rows, cols/256, 16, top_c, 16] fp32, cand_choice
-    [rows, cols/256, 16, top_c] int32, cand_codes [..., 2] uint16 view as int16
-    or None).
+    IQ2_XS: 16 scale groups of 16 columns; IQ1_S: 8 sub-blocks of 32 columns.
+    Returns (cand_err [rows, cols/256, G, top_c, 256/G] fp32, cand_choice
+    [rows, cols/256, G, top_c] int32, cand_codes [..., 2 (IQ2_XS) or 4 (IQ1_S)]
+    uint16 viewed as int16, or None).
     """
     f = _fmt(fmt)
     _dev_tensor(w, torch.float32, "w")
@@ -285,9 +288,13 @@ def encode_candidates(w, grid, importance=None, *, fmt="iq2_xs", top_c=8, codes=
         if importance.numel() != C:
             raise ValueError("importance must have cols values")
     NB = C // 256
-    err = torch.empty((R, NB, 16, top_c, 16), dtype=torch.float32, device=w.device)
-    ch = torch.empty((R, NB, 16, top_c), dtype=torch.int32, device=w.device)
-    cc = torch.empty((R, NB, 16, top_c, 2), dtype=torch.int16, device=w.device) if codes else None
+    G = CHOICE_GROUPS[fmt]
+    tc = max(int(top_c), 0)
+    err = torch.empty((R, NB, G, tc, 256 // G), dtype=torch.float32, device=w.device)
+    ch = torch.empty((R, NB, G, tc), dtype=torch.int32, device=w.device)
+    ncode = 2 if fmt == "iq2_xs" else 4
+    cc = (torch.empty((R, NB, G, tc, ncode), dtype=torch.int16, device=w.device)
+          if codes else None)
     status, own = _status_tensor(status, w.device)
     code = load().iq_encode_candidates(f, _ptr(w), R, C, _ptr(importance), _ptr(grid),
                                        grid.shape[0], int(top_c), _ptr(err), _ptr(ch), _ptr(cc),
@@ -299,21 +306,35 @@ def encode_candidates(w, grid, importance=None, *, fmt="iq2_xs", top_c=8, codes=
 
 
 def choice_search(H, cand_err, *, sweeps=2, trace=False):
-    """Local-Hessian choice search of one 256-column block.
+    """Local-Hessian choice search.
 
-    H [256, 256] fp32 symmetric; cand_err [rows, G, C, 256/G] fp32.
-    Returns picks [rows, G] int32 (and the trace [sweeps+1, rows, G] if asked).
+    One block: H [256, 256] fp32 symmetric, cand_err [rows, G, C, 256/G];
+    returns picks [rows, G] int32 (and the trace [sweeps+1, rows, G]).
+    Many blocks in one launch: H [nblk, 256, 256], cand_err
+    [rows, nblk, G, C, 256/G]; returns picks [rows, nblk, G] (and the trace
+    [sweeps+1, rows, nblk, G]).
     """
     _dev_tensor(H, torch.float32, "H")
     _dev_tensor(cand_err, torch.float32, "cand_err")
-    if H.shape != (256, 256):
-        raise ValueError("H must be [256, 256]")
-    if cand_err.dim() != 4 or cand_err.shape[1] * cand_err.shape[3] != 256:
-        raise ValueError("cand_err must be [rows, G, C, 256/G]")
-    R, G, C, _ = cand_err.shape
-    picks = torch.empty((R, G), dtype=torch.int32, device=H.device)
-    tr = torch.empty((sweeps + 1, R, G), dtype=torch.int32, device=H.device) if trace else None
-    code = load().iq_choice_search(_ptr(H), _ptr(cand_err), R, G, C, int(sweeps), _ptr(picks),
-                                   _ptr(tr), _stream())
-    _check(code, "iq_choice_search")
+    if H.dim() == 2:
+        if H.shape != (256, 256):
+            raise ValueError("H must be [256, 256]")
+        if cand_err.dim() != 4 or cand_err.shape[1] * cand_err.shape[3] != 256:
+            raise ValueError("cand_err must be [rows, G, C, 256/G]")
+        R, G, C, _ = cand_err.shape
+        NB = 1
+        pshape, tshape = (R, G), (sweeps + 1, R, G)
+    else:
+        if H.dim() != 3 or H.shape[1:] != (256, 256):
+            raise ValueError("H must be [nblk, 256, 256]")
+        if (cand_err.dim() != 5 or cand_err.shape[1] != H.shape[0]
+                or cand_err.shape[2] * cand_err.shape[4] != 256):
+            raise ValueError("cand_err must be [rows, nblk, G, C, 256/G]")
+        R, NB, G, C, _ = cand_err.shape
+        pshape, tshape = (R, NB, G), (sweeps + 1, R, NB, G)
+    picks = torch.empty(pshape, dtype=torch.int32, device=H.device)
+    tr = torch.empty(tshape, dtype=torch.int32, device=H.device) if trace else None
+    code = load().iq_choice_search_blocks(_ptr(H), _ptr(cand_err), R, NB, G, C, int(sweeps),
+                                          _ptr(picks), _ptr(tr), _stream())
+    _check(code, "iq_choice_search_blocks")
     return (picks, tr) if trace else picks

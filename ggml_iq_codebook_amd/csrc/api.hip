@@ -193,12 +193,12 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, 
                                  uint16_t* cand_codes, int32_t* status, hipStream_t stream)
 {
     if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
-    if (fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
     iqk::BlockGeom g;
     iq_status_t st = geometry(1, rows, cols, &g);
     if (st) return st;
     if (!w || !grid || !cand_err || !cand_choice || !status) return IQ_ERR_NULL;
-    if (grid_size < 1 || grid_size > 512) return IQ_ERR_GRID;
+    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
+    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
     if (top_c < 1 || top_c > 16) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(cand_err, 16) || !aligned(cand_choice, 4) ||
@@ -206,6 +206,9 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, 
         return IQ_ERR_ARG;
     st = check_device();
     if (st) return st;
+    if (fmt == IQ_FMT_IQ1_S)
+        return from_hip(iqk::launch_iq1s_candidates(w, importance, grid, grid_size, top_c, cand_err,
+                                                    cand_choice, cand_codes, status, g, stream));
     return from_hip(iqk::launch_iq2xs_candidates(w, importance, grid, grid_size, top_c, cand_err,
                                                  cand_choice, cand_codes, status, g, stream));
 }
@@ -214,14 +217,24 @@ iq_status_t iq_choice_search(const float* H, const float* cand_err, int64_t rows
                              int32_t C, int32_t sweeps, int32_t* picks, int32_t* trace,
                              hipStream_t stream)
 {
-    if (rows <= 0 || rows > (INT64_C(1) << 34)) return IQ_ERR_SHAPE;
+    return iq_choice_search_blocks(H, cand_err, rows, 1, G, C, sweeps, picks, trace, stream);
+}
+
+iq_status_t iq_choice_search_blocks(const float* H, const float* cand_err, int64_t rows,
+                                    int64_t nblk, int32_t G, int32_t C, int32_t sweeps,
+                                    int32_t* picks, int32_t* trace, hipStream_t stream)
+{
+    if (rows <= 0 || rows > (INT64_C(1) << 34) || nblk <= 0 || nblk > 65535 ||
+        rows * nblk > (INT64_C(1) << 34))
+        return IQ_ERR_SHAPE;
     if (!H || !cand_err || !picks) return IQ_ERR_NULL;
     if ((G != 8 && G != 16) || C < 1 || C > 16 || sweeps < 0 || sweeps > 8) return IQ_ERR_ARG;
     if (!aligned(H, 4) || !aligned(cand_err, 4) || !aligned(picks, 4) || (trace && !aligned(trace, 4)))
         return IQ_ERR_ARG;
     iq_status_t st = check_device();
     if (st) return st;
-    return from_hip(iqk::launch_choice_search(H, cand_err, rows, G, C, sweeps, picks, trace, stream));
+    return from_hip(iqk::launch_choice_search(H, cand_err, rows, nblk, G, C, sweeps, picks, trace,
+                                              stream));
 }
 
 }  // extern "C"

@@ -32,11 +32,12 @@ constexpr int kRows = 16;        // rows per workgroup
 constexpr int kMaxC = 16;
 
 struct SearchArgs {
-    const float* H;
-    const float* cand;
-    int32_t* picks;
-    int32_t* trace;
+    const float* H;          // [nblk][256][256]
+    const float* cand;       // [rows][nblk][G][C][L]
+    int32_t* picks;          // [rows][nblk][G]
+    int32_t* trace;          // NULL or [sweeps+1][rows][nblk][G]
     int64_t rows;
+    int64_t nblk;
     int C, sweeps;
 };
 
@@ -59,11 +60,18 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     const int C = a.C;
     const int64_t row0 = (int64_t)blockIdx.x * kRows;
     const int nrows = (int)((a.rows - row0) < kRows ? (a.rows - row0) : kRows);
-    const int64_t cstride = (int64_t)G * C * L;   // floats per row of cand
+    // This workgroup's 256-column block: its H and its slice of every row.
+    const int64_t blk = blockIdx.y;
+    const float* __restrict__ Hb = a.H + blk * 65536;
+    const int64_t cstride = a.nblk * G * C * L;   // floats per row of cand
+    const float* __restrict__ cb = a.cand + blk * (int64_t)G * C * L;
+    auto out_index = [&](int64_t sweep_slot, int64_t row, int g) -> int64_t {
+        return ((sweep_slot * a.rows + row) * a.nblk + blk) * G + g;
+    };
 
     for (int i = t; i < G * L * L; i += kThreads) {
         const int g = i / (L * L), rem = i % (L * L), ii = rem / L, jj = rem % L;
-        hdiag[i] = a.H[(int64_t)(g * L + ii) * 256 + g * L + jj];
+        hdiag[i] = Hb[(g * L + ii) * 256 + g * L + jj];
     }
     __syncthreads();
 
@@ -72,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         const int rr = it / (G * C), gc = it % (G * C), g = gc / C;
         float q = 0.0f;
         if (rr < nrows) {
-            const float* ep = a.cand + (row0 + rr) * cstride + (int64_t)gc * L;
+            const float* ep = cb + (row0 + rr) * cstride + (int64_t)gc * L;
             float e[L];
 #pragma unroll
             for (int j = 0; j < L; ++j) e[j] = ep[j];
@@ -97,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             if (qself[rr][g * C + c] < qself[rr][g * C + best]) best = c;
         pick[rr][g] = best;
         if (rr < nrows) {
-            const float* ep = a.cand + (row0 + rr) * cstride + ((int64_t)g * C + best) * L;
+            const float* ep = cb + (row0 + rr) * cstride + ((int64_t)g * C + best) * L;
 #pragma unroll
             for (int i = 0; i < L; ++i) ecur[rr][g * L + i] = ep[i];
         } else {
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     __syncthreads();
     if (a.trace)
         for (int it = t; it < nrows * G; it += kThreads)
-            a.trace[(row0 + it / G) * G + it % G] = pick[it / G][it % G];
+            a.trace[out_index(0, row0 + it / G, it % G)] = pick[it / G][it % G];
 
     // r = H e (thread t owns column t; H is symmetric, so H[u][t] is read),
     // 16 rows of H in flight at a time.
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     for (int u0 = 0; u0 < 256; u0 += 16) {
         float h[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) h[i] = a.H[(int64_t)(u0 + i) * 256 + t];
+        for (int i = 0; i < 16; ++i) h[i] = Hb[(u0 + i) * 256 + t];
 #pragma unroll
         for (int i = 0; i < 16; ++i)
 #pragma unroll
@@ -136,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     float hrow[L];
     auto load_step = [&](int g) {
         if (srow_ok) {
-            const float* ep = a.cand + (row0 + srow) * cstride + ((int64_t)g * C + scand) * L;
+            const float* ep = cb + (row0 + srow) * cstride + ((int64_t)g * C + scand) * L;
 #pragma unroll
             for (int i = 0; i < L; ++i) cv[i] = ep[i];
         } else {
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             for (int i = 0; i < L; ++i) cv[i] = 0.0f;
         }
 #pragma unroll
-        for (int i = 0; i < L; ++i) hrow[i] = a.H[(int64_t)(g * L + i) * 256 + t];
+        for (int i = 0; i < L; ++i) hrow[i] = Hb[(g * L + i) * 256 + t];
     };
     load_step(0);
 
@@ -214,24 +222,25 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         __syncthreads();
         if (a.trace)
             for (int it = t; it < nrows * G; it += kThreads)
-                a.trace[((int64_t)(sw + 1) * a.rows + row0 + it / G) * G + it % G] = pick[it / G][it % G];
+                a.trace[out_index(sw + 1, row0 + it / G, it % G)] = pick[it / G][it % G];
     }
     __syncthreads();
     for (int it = t; it < nrows * G; it += kThreads)
-        a.picks[(row0 + it / G) * G + it % G] = pick[it / G][it % G];
+        a.picks[((row0 + it / G) * a.nblk + blk) * G + it % G] = pick[it / G][it % G];
 }
 
 }  // namespace
 
-hipError_t launch_choice_search(const float* H, const float* cand, int64_t rows, int G, int C,
-                                int sweeps, int32_t* picks, int32_t* trace, hipStream_t stream)
+hipError_t launch_choice_search(const float* H, const float* cand, int64_t rows, int64_t nblk,
+                                int G, int C, int sweeps, int32_t* picks, int32_t* trace,
+                                hipStream_t stream)
 {
-    SearchArgs a{H, cand, picks, trace, rows, C, sweeps};
-    const int64_t wgs = (rows + kRows - 1) / kRows;
+    SearchArgs a{H, cand, picks, trace, rows, nblk, C, sweeps};
+    const dim3 grid((unsigned)((rows + kRows - 1) / kRows), (unsigned)nblk);
     if (G == 16)
-        hipLaunchKernelGGL(choice_search_kernel<16>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(choice_search_kernel<16>, grid, dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(choice_search_kernel<32>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(choice_search_kernel<32>, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

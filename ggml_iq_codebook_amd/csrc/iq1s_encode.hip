@@ -68,9 +68,13 @@ struct Iq1sArgs {
     uint8_t* out;            // payload: [nblocks][50]; every choice: [16][nblocks][50]; may be
                              // NULL for the fake-quant output
     float* xhat;             // fake quant: decoded values [nblocks][256]
+    float* cand_err;         // candidates: [nblocks][8][top_c][32]
+    int32_t* cand_choice;    // [nblocks][8][top_c]
+    uint16_t* cand_codes;    // NULL or [nblocks][8][top_c][4]
     int32_t* status;
     BlockGeom g;
     int grid_size;
+    int top_c;
 };
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
@@ -184,7 +188,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     const int npad = nchunks * kChunk;
 
     if (tid == 0) sgrid_bad = 0;
-    for (int i = tid; i < kPayloads * kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
+    if (kMode != kModeCandidates)
+        for (int i = tid; i < kPayloads * kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     // Stage the grid as bf16 (exact for ternary values); entries past the end
     // repeat the last one, which always comes first in index order.
@@ -355,6 +360,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         // in every lane of the sub-block).
         int cstar = 0;
         float cbest = 0.0f;
+        float cost[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
             float m = best[c];
@@ -362,18 +368,35 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             m = fminf(m, __shfl_xor(m, 32));
             float v = m + __shfl_xor(m, 1);
             v += __shfl_xor(v, 2);
-            const float cost = (float)(2 * (c & 7) + 1) * v;
-            if (c == 0 || cost < cbest) { cbest = cost; cstar = c; }
+            cost[c] = (float)(2 * (c & 7) + 1) * v;
+            if (c == 0 || cost[c] < cbest) { cbest = cost[c]; cstar = c; }
         }
         if (forced >= 0) cstar = forced;
+        // Candidates: the top_c choices by (cost, c); with a zero scale every
+        // choice decodes to zero with entry 0, so the order is c = 0, 1, ...
+        const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
+        const bool zero_scale = !rejected && dh == 0u;
+        int used = 0;
 
         // Entry of choice cs for this lane's group: the lane rescans its
         // entries of the chunk that holds its minimum of that choice, then the
         // lane of the column whose matrix-core minimum is least is kept; the
         // payload takes the low byte per group, the qh word per sub-block and
         // d per block.
-        for (int it = 0; it < (kMode == kModeEvery ? 16 : 1); ++it) {
-            const int cs = kMode == kModeEvery ? it : cstar;
+        const int nloop = kMode == kModeEvery ? 16 : (kMode == kModeCandidates ? a.top_c : 1);
+        for (int it = 0; it < nloop; ++it) {
+            int cs = kMode == kModeEvery ? it : cstar;
+            if (kMode == kModeCandidates) {
+                int cr = -1;
+                float vr = 0.0f;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const bool better = zero_scale ? (cr < 0) : (cr < 0 || cost[c] < vr);
+                    if (!((used >> c) & 1) && better) { cr = c; vr = cost[c]; }
+                }
+                used |= 1 << cr;
+                cs = cr;
+            }
             float lane_min = best[0];
 #pragma unroll
             for (int c = 1; c < 16; ++c)
@@ -387,6 +410,33 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 if (om < lane_min || (om == lane_min && oi < idx)) { lane_min = om; idx = oi; }
             }
             idx = idx < n ? idx : n - 1;
+            if (kMode == kModeCandidates) {
+                // One lane per group writes its 8 errors xhat - x (xhat exact
+                // in fp32, one rounding), its entry and, once per sub-block,
+                // the choice.
+                if (zero_scale) idx = 0;
+                if (kb == 0) {
+                    const int64_t base = (blk * 8 + sub) * a.top_c + it;     // [block][sub][r]
+                    float xo[8], wo[8];
+                    load_group(xblk, wblk, g, rejected, xo, wo);
+                    const float sk = f16_bits_to_f32(dh) * (float)(2 * (cs & 7) + 1);
+                    const float delta = (cs >> 3) ? -0.125f : 0.125f;
+                    const uint4 u = sq[idx + idx / kChunk];
+                    const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+                    float ev[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                        ev[j] = rejected ? 0.0f : sk * (q + delta) - xo[j];
+                    }
+                    float4* ep = reinterpret_cast<float4*>(a.cand_err + base * 32 + lq * 8);
+                    ep[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
+                    ep[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
+                    if (lq == 0) a.cand_choice[base] = cs;
+                    if (a.cand_codes) a.cand_codes[base * 4 + lq] = rejected ? (uint16_t)0 : (uint16_t)idx;
+                }
+                continue;
+            }
             int hi = ((idx >> 8) & 7) << (3 * lq);
             hi |= __shfl_xor(hi, 1);
             hi |= __shfl_xor(hi, 2);
@@ -427,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             }
         }
     }
-    if (a.out) {
+    if (kMode != kModeCandidates && a.out) {
         __syncthreads();
         const int64_t first = (int64_t)blockIdx.x * kBlocksPerWG;
         const int64_t left = a.g.nblocks - first;
@@ -447,7 +497,8 @@ hipError_t launch_iq1s_encode(const float* w, const float* imp, const float* gri
                               float* xhat, int mode, int32_t* status, const BlockGeom& g,
                               hipStream_t stream)
 {
-    Iq1sArgs a{w, imp, grid, scales, choices, out, xhat, status, g, grid_size};
+    Iq1sArgs a{w, imp, grid, scales, choices, out, xhat, nullptr, nullptr, nullptr, status, g,
+               grid_size, 0};
     const int64_t wgs = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
     if (mode == kModeEvery)
         hipLaunchKernelGGL(iq1s_encode_kernel<kModeEvery>, dim3((unsigned)wgs), dim3(kThreads), 0,
@@ -458,6 +509,19 @@ hipError_t launch_iq1s_encode(const float* w, const float* imp, const float* gri
     else
         hipLaunchKernelGGL(iq1s_encode_kernel<kModePayload>, dim3((unsigned)wgs), dim3(kThreads), 0,
                            stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_iq1s_candidates(const float* w, const float* imp, const float* grid,
+                                  int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
+                                  uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
+                                  hipStream_t stream)
+{
+    Iq1sArgs a{w, imp, grid, nullptr, nullptr, nullptr, nullptr, cand_err, cand_choice, cand_codes,
+               status, g, grid_size, top_c};
+    const int64_t wgs = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
+    hipLaunchKernelGGL(iq1s_encode_kernel<kModeCandidates>, dim3((unsigned)wgs), dim3(kThreads), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

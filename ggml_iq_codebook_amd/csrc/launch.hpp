@@ -32,6 +32,11 @@ hipError_t launch_iq2xs_encode(const float* w, const float* imp, const float* gr
                                float* xhat, int mode, int32_t* status, const BlockGeom& g,
                                hipStream_t stream);
 
+hipError_t launch_iq1s_candidates(const float* w, const float* imp, const float* grid,
+                                  int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
+                                  uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
+                                  hipStream_t stream);
+
 hipError_t launch_iq2xs_candidates(const float* w, const float* imp, const float* grid,
                                    int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
                                    uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
@@ -40,7 +45,8 @@ hipError_t launch_iq2xs_candidates(const float* w, const float* imp, const float
 hipError_t launch_dequant(int fmt, const uint8_t* packed, const float* grid, int grid_size,
                           float* out, int32_t* status, const BlockGeom& g, hipStream_t stream);
 
-hipError_t launch_choice_search(const float* H, const float* cand, int64_t rows, int G, int C,
-                                int sweeps, int32_t* picks, int32_t* trace, hipStream_t stream);
+hipError_t launch_choice_search(const float* H, const float* cand, int64_t rows, int64_t nblk,
+                                int G, int C, int sweeps, int32_t* picks, int32_t* trace,
+                                hipStream_t stream);
 
 }  // namespace iqk

@@ -167,17 +167,20 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
 /*
  * iq_encode_candidates -- the encode's sweep with a candidate epilogue, the
  * input of the local-Hessian choice search (#3158 step 1, #3159 every-choice
- * encode): for every IQ2_XS scale group (16 columns) of every 256-column block,
- * the top_c local scales ordered by (weighted cost, k), each with its two
- * codes and its error vector xhat - x over the 16 columns.
+ * encode): for every choice group of every 256-column block (IQ2_XS: 16 scale
+ * groups of 16 columns, choice = local scale k; IQ1_S: 8 sub-blocks of 32
+ * columns, choice c = k + 8*deltabit), the top_c choices ordered by
+ * (weighted cost, choice), each with its grid codes and its error vector
+ * xhat - x over the group's columns (xhat exact in fp32, one rounding).  A
+ * zero super-block scale orders the choices 0, 1, ... with entry 0.
  *
  *   w           [rows][cols] fp32; importance NULL or [cols]; grid as iq_encode.
  *   top_c       1..16.
- *   cand_err    [rows][cols/256][16][top_c][16] fp32.
- *   cand_choice [rows][cols/256][16][top_c] int32 (the local scale k).
- *   cand_codes  NULL or [rows][cols/256][16][top_c][2] uint16 (index | mask<<9).
- *   status      one int32, required.
- * Only IQ_FMT_IQ2_XS is supported (IQ_ERR_FORMAT otherwise).
+ *   cand_err    IQ2_XS [rows][cols/256][16][top_c][16], IQ1_S [rows][cols/256][8][top_c][32] fp32.
+ *   cand_choice [rows][cols/256][G][top_c] int32 (G = 16 or 8).
+ *   cand_codes  NULL, or IQ2_XS [..][top_c][2] uint16 (index | mask<<9 per group),
+ *               IQ1_S [..][top_c][4] uint16 (the grid index of each group).
+ *   status      one int32, required; a block with a data error is all zeros.
  */
 iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, int64_t cols,
                                  const float* importance, const float* grid, int32_t grid_size,
@@ -202,6 +205,24 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, 
 iq_status_t iq_choice_search(const float* H, const float* cand_err, int64_t rows, int32_t G,
                              int32_t C, int32_t sweeps, int32_t* picks, int32_t* trace,
                              hipStream_t stream);
+
+/*
+ * iq_choice_search_blocks -- the same search for many 256-column blocks in
+ * one launch, each block with its own H ("[4/4] Run the local-Hessian choice
+ * search as one CUDA kernel" #3218 fuses the search of one block; the pages'
+ * MoE calibration has many small blocks, where per-block launches dominate).
+ * iq_choice_search is this call with nblk = 1.
+ *
+ *   H        [nblk][256][256] fp32, each symmetric.
+ *   cand_err [rows][nblk][G][C][256/G] fp32: what iq_encode_candidates writes
+ *            for a [rows][256*nblk] weight.
+ *   nblk     1..65535 (IQ_ERR_SHAPE otherwise).
+ *   picks    [rows][nblk][G] int32; trace NULL or [sweeps+1][rows][nblk][G].
+ * G, C, sweeps and the errors as iq_choice_search.
+ */
+iq_status_t iq_choice_search_blocks(const float* H, const float* cand_err, int64_t rows,
+                                    int64_t nblk, int32_t G, int32_t C, int32_t sweeps,
+                                    int32_t* picks, int32_t* trace, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -73,6 +73,8 @@ def lib():
             f.restype = ctypes.c_int
         L.orc_iq2xs_candidates.argtypes = [P, P, i64, P, i32, i32, P, P, P]
         L.orc_iq2xs_candidates.restype = ctypes.c_int
+        L.orc_iq1s_candidates.argtypes = [P, P, i64, P, i32, i32, P, P, P]
+        L.orc_iq1s_candidates.restype = ctypes.c_int
         L.orc_choice_search.argtypes = [P, P, i64, i32, i32, i32, P, P]
         L.orc_choice_search.restype = ctypes.c_int
         L.orc_choice_objective.argtypes = [P, P, i32, i32, P]
@@ -249,6 +251,33 @@ def iq2xs_candidates(w, grid, importance=None, top_c: int = 8):
     if st:
         raise OracleError(ERRORS.get(st, "error %d" % st))
     return err, ch, codes
+
+
+def iq1s_candidates(w, grid, importance=None, top_c: int = 8):
+    """Top-C choices c = k + 8*deltabit per 32-column IQ1_S sub-block with their
+    error vectors.
+
+    Returns cand_err [B*R*C/256, 8, top_c, 32] float32 (xhat - x),
+    cand_choice [.., 8, top_c] int32 and cand_codes [.., 8, top_c, 4] uint16
+    (the four grid entries).
+    """
+    shape, x, imp = _blocks(w, importance)
+    nblk = x.shape[0]
+    grid = np.ascontiguousarray(grid, dtype=np.float32)
+    err = np.zeros((nblk, 8, top_c, 32), dtype=np.float32)
+    ch = np.zeros((nblk, 8, top_c), dtype=np.int32)
+    codes = np.zeros((nblk, 8, top_c, 4), dtype=np.uint16)
+    st = lib().orc_iq1s_candidates(_ptr(x), _ptr(imp), nblk, _ptr(grid), grid.shape[0], top_c,
+                                   _ptr(err), _ptr(ch), _ptr(codes))
+    if st:
+        raise OracleError(ERRORS.get(st, "error %d" % st))
+    return err, ch, codes
+
+
+def candidates(fmt: str, w, grid, importance=None, top_c: int = 8):
+    """The top-C candidates of either format (see iq1s_candidates / iq2xs_candidates)."""
+    f = iq1s_candidates if fmt == "iq1_s" else iq2xs_candidates
+    return f(w, grid, importance, top_c)
 
 
 # --------------------------------------------------------------------------

@@ -472,6 +472,65 @@ static int iq2xs_candidates_block(const float* x, const float* w, const float* g
     return ORC_OK;
 }
 
+/* Top-C candidates of every sub-block of one IQ1_S block (#3158 step 1 with
+ * IQ1_S's choice c = k + 8*deltabit, #3159): the C lowest (cost, c) choices of
+ * each 32-value sub-block, their four entries and their error vectors
+ * xhat - x over the 32 columns.  A zero scale makes every choice decode to
+ * zero, so the order is c = 0, 1, ... with entries 0. */
+static int iq1s_candidates_block(const float* x, const float* w, const float* grid, int n,
+                                 int top_c, float* cand_err, int32_t* cand_choice,
+                                 uint16_t* cand_codes)
+{
+    int st = check_block_inputs(x, w, 256);
+    if (st) return st;
+    uint16_t dh;
+    st = block_scale(x, IQ1S_DIVISOR, NULL, &dh);
+    if (st) return st;
+    double d = orc_f16_to_f64(dh);
+    for (int i = 0; i < 8; ++i) {
+        double cost[16];
+        int ent[16][4];
+        for (int c = 0; c < 16; ++c) {
+            int k = c & 7, dbit = c >> 3;
+            double s = d * (double)(2 * k + 1);
+            double delta = dbit ? -0.125 : 0.125;
+            cost[c] = 0.0;
+            for (int l = 0; l < 4; ++l) {
+                int off = 32 * i + 8 * l;
+                double ge;
+                ent[c][l] = iq1s_best_entry(x + off, w ? w + off : NULL, grid, n, s, delta, &ge);
+                cost[c] += ge;
+            }
+            if (dh == 0) {
+                cost[c] = 0.0;
+                for (int l = 0; l < 4; ++l) ent[c][l] = 0;
+            }
+        }
+        int used[16] = {0};
+        for (int r = 0; r < top_c; ++r) {
+            int cb = -1;
+            for (int c = 0; c < 16; ++c) {
+                if (used[c]) continue;
+                if (cb < 0 || cost[c] < cost[cb]) cb = c;
+            }
+            used[cb] = 1;
+            cand_choice[i * top_c + r] = cb;
+            double s = d * (double)(2 * (cb & 7) + 1);
+            double delta = (cb >> 3) ? -0.125 : 0.125;
+            for (int l = 0; l < 4; ++l) {
+                const float* q = grid + 8 * ent[cb][l];
+                if (cand_codes) cand_codes[(i * top_c + r) * 4 + l] = (uint16_t)ent[cb][l];
+                for (int j = 0; j < 8; ++j) {
+                    int col = 32 * i + 8 * l + j;
+                    double xhat = s * ((double)q[j] + delta);
+                    cand_err[(i * top_c + r) * 32 + 8 * l + j] = (float)(xhat - (double)x[col]);
+                }
+            }
+        }
+    }
+    return ORC_OK;
+}
+
 /* ---------------------------------------------------------------------- */
 /* Batched entry points (OpenMP over blocks).                              */
 /* x: [nblk][256]; imp: NULL or [nblk][256]; scales: NULL or [nblk];       */
@@ -552,6 +611,25 @@ int orc_iq2xs_candidates(const float* x, const float* imp, int64_t nblk, const f
                                        cand_err + (size_t)b * 16 * top_c * 16,
                                        cand_choice + (size_t)b * 16 * top_c,
                                        cand_codes ? cand_codes + (size_t)b * 16 * top_c * 2 : NULL);
+    int r = first_error(st, nblk);
+    free(st);
+    return r;
+}
+
+/* cand_err: [nblk][8][top_c][32] float; cand_choice: [nblk][8][top_c];
+ * cand_codes: NULL or [nblk][8][top_c][4] (the four grid entries). */
+int orc_iq1s_candidates(const float* x, const float* imp, int64_t nblk, const float* grid,
+                        int32_t n, int32_t top_c, float* cand_err, int32_t* cand_choice,
+                        uint16_t* cand_codes)
+{
+    if (n <= 0 || n > 2048 || top_c < 1 || top_c > 16) return ORC_ERR_ARG;
+    int* st = (int*)calloc((size_t)(nblk > 0 ? nblk : 1), sizeof(int));
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < nblk; ++b)
+        st[b] = iq1s_candidates_block(x + 256 * b, imp ? imp + 256 * b : NULL, grid, n, top_c,
+                                      cand_err + (size_t)b * 8 * top_c * 32,
+                                      cand_choice + (size_t)b * 8 * top_c,
+                                      cand_codes ? cand_codes + (size_t)b * 8 * top_c * 4 : NULL);
     int r = first_error(st, nblk);
     free(st);
     return r;

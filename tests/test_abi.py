@@ -26,7 +26,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "iq_choice_search", "iq_dequant", "iq_encode", "iq_encode_candidates",
+        "iq_choice_search", "iq_choice_search_blocks", "iq_dequant", "iq_encode",
+        "iq_encode_candidates",
         "iq_encode_every_choice", "iq_fake_quant", "iq_format_info", "iq_status_str"])
 
 
@@ -78,7 +79,9 @@ def test_other_entry_points_argument_errors_need_no_gpu(lib):
     assert deq(0, FAKE, 1, 1, 100, FAKE, 16, FAKE, FAKE, None) == 3
     assert deq(1, FAKE, 1, 1, 256, FAKE, 600, FAKE, FAKE, None) == 4
     cand = lib.iq_encode_candidates
-    assert cand(0, FAKE, 1, 256, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 2
+    assert cand(7, FAKE, 1, 256, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 2
+    assert cand(0, FAKE, 1, 256, None, FAKE, 2049, 8, FAKE, FAKE, None, FAKE, None) == 4
+    assert cand(0, FAKE, 1, 256, None, FAKE, 16, 17, FAKE, FAKE, None, FAKE, None) == 8
     assert cand(1, FAKE, 1, 256, None, FAKE, 16, 0, FAKE, FAKE, None, FAKE, None) == 8
     assert cand(1, FAKE, 1, 256, None, FAKE, 16, 17, FAKE, FAKE, None, FAKE, None) == 8
     assert cand(1, FAKE, 1, 250, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 3
@@ -106,3 +109,13 @@ def test_every_choice_and_fake_quant_argument_errors_need_no_gpu(lib):
     # the decoded values may not overlap the weights (checked before any device access)
     assert fq(0, FAKE, 1, 2, 256, None, FAKE, 16, None, None, P(0x100400), None, FAKE, None) == 8
     assert fq(0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None, FAKE, None) == 8
+
+
+def test_batched_search_argument_errors_need_no_gpu(lib):
+    cs = lib.iq_choice_search_blocks
+    # H, cand, rows, nblk, G, C, sweeps, picks, trace, stream
+    assert cs(FAKE, FAKE, 4, 0, 16, 8, 2, FAKE, None, None) == 3
+    assert cs(FAKE, FAKE, 4, 65536, 16, 8, 2, FAKE, None, None) == 3
+    assert cs(FAKE, FAKE, 0, 3, 16, 8, 2, FAKE, None, None) == 3
+    assert cs(FAKE, FAKE, 4, 3, 4, 8, 2, FAKE, None, None) == 8
+    assert cs(FAKE, None, 4, 3, 8, 8, 2, FAKE, None, None) == 1

@@ -210,8 +210,8 @@ def test_synchronous_argument_errors():
         iq.encode(w, _dev(big))
     assert ei.value.code == 4                        # IQ_ERR_GRID
     with pytest.raises(iq.IQError) as ei:
-        iq.encode_candidates(w[0], grid, fmt="iq1_s")
-    assert ei.value.code == 2                        # IQ_ERR_FORMAT
+        iq.encode_candidates(w[0], grid, fmt="iq1_s", top_c=17)
+    assert ei.value.code == 8                        # IQ_ERR_ARG
 
 
 def test_dequant_reports_indices_beyond_the_grid():

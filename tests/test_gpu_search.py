@@ -39,19 +39,21 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def _check_candidates(w, grid, imp, top_c):
+def _check_candidates(w, grid, imp, top_c, fmt="iq2_xs"):
     """w [rows, 256]."""
+    G = 16 if fmt == "iq2_xs" else 8
+    L, nc = 256 // G, (2 if fmt == "iq2_xs" else 4)
     err, ch, codes = iq.encode_candidates(_dev(w), _dev(grid), None if imp is None else _dev(imp),
-                                          top_c=top_c, codes=True)
+                                          fmt=fmt, top_c=top_c, codes=True)
     torch.cuda.synchronize()
-    err = err.cpu().numpy().reshape(-1, 16, top_c, 16)
-    ch = ch.cpu().numpy().reshape(-1, 16, top_c)
-    codes = codes.cpu().numpy().view(np.uint16).reshape(-1, 16, top_c, 2)
-    rerr, rch, rcodes = oracle.iq2xs_candidates(w[None], grid, None if imp is None else imp[None],
-                                                top_c=top_c)
+    err = err.cpu().numpy().reshape(-1, G, top_c, L)
+    ch = ch.cpu().numpy().reshape(-1, G, top_c)
+    codes = codes.cpu().numpy().view(np.uint16).reshape(-1, G, top_c, nc)
+    rerr, rch, rcodes = oracle.candidates(fmt, w[None], grid, None if imp is None else imp[None],
+                                          top_c=top_c)
     same = (ch == rch)
     wt = np.ones(256) if imp is None else imp.astype(np.float64).reshape(256)
-    wt = wt.reshape(16, 16)
+    wt = wt.reshape(G, L)
     e_got = (wt[None, :, None, :] * err.astype(np.float64) ** 2).sum(axis=3)
     e_ref = (wt[None, :, None, :] * rerr.astype(np.float64) ** 2).sum(axis=3)
     # where the choice agrees, codes and error vectors are bit-exact, or the
@@ -80,7 +82,8 @@ def test_candidates_zero_block():
     w = workloads.student_t_weight((3, 256), 33)
     w[1] = 0.0
     err, ch = _check_candidates(w, grid, None, 8)
-    assert np.all(ch[16:32] == np.arange(8))
+    assert ch.shape == (3, 16, 8) and np.all(ch[1] == np.arange(8))
+    np.testing.assert_array_equal(err[1], np.broadcast_to(-w[1].reshape(16, 1, 16), (16, 8, 16)))
 
 
 def _search_parity(H, cand, sweeps=2):
@@ -132,3 +135,66 @@ def test_c5_choice_search_full():
     assert np.any(trace[0] != trace[2])
     J = [oracle.choice_objective(H, cand_np, trace[s]) for s in range(3)]
     assert np.all(J[1] <= J[0] * (1 + 1e-6)) and np.all(J[2] <= J[1] * (1 + 1e-6))
+
+
+def test_iq1s_candidates_small_rows():
+    grid = workloads.iq1s_grid()
+    w = workloads.normal_weight((24, 256), 34)
+    imp = workloads.lognormal_importance((256,), 35)
+    _check_candidates(w, grid, imp, 8, fmt="iq1_s")
+    _check_candidates(w[:6], grid, None, 16, fmt="iq1_s")
+    _check_candidates(w[:4], workloads.iq1s_grid(333), imp, 1, fmt="iq1_s")
+
+
+def test_iq1s_candidates_zero_and_rejected_blocks():
+    grid = workloads.iq1s_grid(256)
+    w = workloads.normal_weight((3, 512), 36)
+    w[1, :256] = 0.0
+    err, ch = _check_candidates(w[:, :256], grid, None, 8, fmt="iq1_s")
+    assert ch.shape == (3, 8, 8) and np.all(ch[1] == np.arange(8))
+    np.testing.assert_array_equal(err[1], np.broadcast_to(-w[1, :256].reshape(8, 1, 32), (8, 8, 32)))
+    bad = w.copy()
+    bad[2, 300] = np.nan
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    e2, c2, k2 = iq.encode_candidates(_dev(bad), _dev(grid), fmt="iq1_s", top_c=4, codes=True,
+                                      status=st, check=False)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 5
+    assert not e2[2, 1].abs().sum().item() and not k2[2, 1].abs().sum().item()
+
+
+def test_iq1s_candidates_and_search():
+    # IQ1_S: G = 8 sub-blocks of 32 columns, C = 8 and 16 candidates.
+    H = workloads.block_hessian(256, 11)
+    grid = workloads.iq1s_grid()
+    w = workloads.normal_weight((1, 96, 256), 37)[0]
+    imp = np.sqrt(np.diag(H).astype(np.float64)).astype(np.float32)
+    for top_c in (8, 16):
+        err, ch = _check_candidates(w, grid, imp, top_c, fmt="iq1_s")
+        cand = np.ascontiguousarray(err.reshape(96, 8, top_c, 32))
+        trace, rtrace, nd = _search_parity(H, cand)
+        J = [oracle.choice_objective(H, cand, trace[s]) for s in range(3)]
+        assert np.all(J[1] <= J[0] * (1 + 1e-6)) and np.all(J[2] <= J[1] * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("fmt", ["iq2_xs", "iq1_s"])
+def test_batched_block_search_equals_per_block_searches(fmt):
+    # Three 256-column blocks of one weight, each with its own H, in one launch.
+    G = 16 if fmt == "iq2_xs" else 8
+    grid = workloads.iq2xs_grid() if fmt == "iq2_xs" else workloads.iq1s_grid()
+    Hs = np.stack([workloads.block_hessian(256, s) for s in (7, 8, 9)])
+    w = workloads.student_t_weight((1, 70, 768), 38)[0]
+    imp = np.sqrt(np.concatenate([np.diag(h) for h in Hs]).astype(np.float64)).astype(np.float32)
+    err, ch, _ = iq.encode_candidates(_dev(w), _dev(grid), _dev(imp), fmt=fmt, top_c=6)
+    cand = err.reshape(70, 3, G, 6, 256 // G).contiguous()
+    picks, trace = iq.choice_search(_dev(Hs), cand, trace=True)
+    torch.cuda.synchronize()
+    assert picks.shape == (70, 3, G) and trace.shape == (3, 70, 3, G)
+    cand_np = cand.cpu().numpy()
+    for b in range(3):
+        cb = np.ascontiguousarray(cand_np[:, b])
+        p1, t1 = iq.choice_search(_dev(Hs[b]), _dev(cb), trace=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(picks[:, b].cpu().numpy(), p1.cpu().numpy())
+        np.testing.assert_array_equal(trace[:, :, b].cpu().numpy(), t1.cpu().numpy())
+        _search_parity(Hs[b], cb)

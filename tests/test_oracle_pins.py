@@ -558,6 +558,31 @@ def test_candidates_are_the_sorted_choices_of_the_encode():
         np.testing.assert_array_equal(err[:, :, r, :], (xf - w.reshape(-1, 16, 16)).astype(np.float32))
 
 
+def test_iq1s_candidates_are_the_sorted_choices_of_the_encode():
+    grid = workloads.iq1s_grid(512)
+    w = workloads.normal_weight((1, 5, 256), 113)
+    w[0, 4] = 0.0                                       # zero block: c = 0, 1, ..., error -x
+    imp = workloads.lognormal_importance((1, 256), 114)
+    err, ch, codes = oracle.iq1s_candidates(w, grid, imp, top_c=6)
+    assert err.shape == (5, 8, 6, 32) and codes.shape == (5, 8, 6, 4)
+    p = oracle.encode("iq1_s", w, grid, imp)
+    d, entries, k, sgn = iq1s_fields(p)
+    np.testing.assert_array_equal(ch[:4, :, 0], (k + 8 * sgn)[:4])   # top-1 = the encoder's pick
+    np.testing.assert_array_equal(codes[:4, :, 0, :], entries[:4])
+    xh = oracle.decode("iq1_s", p, grid).reshape(-1, 8, 32)
+    np.testing.assert_array_equal(err[:, :, 0, :], (xh - w.reshape(-1, 8, 32)).astype(np.float32))
+    np.testing.assert_array_equal(ch[4], np.tile(np.arange(6), (8, 1)))
+    np.testing.assert_array_equal(err[4], np.broadcast_to(-w.reshape(-1, 8, 1, 32)[4], (8, 6, 32)))
+    wt = imp.reshape(8, 32).astype(np.float64)
+    e = (wt[None, :, None, :] * err.astype(np.float64) ** 2).sum(axis=3)
+    assert np.all(np.diff(e[:4], axis=2) >= -1e-9 * e[:4, :, 1:])
+    assert all(len(set(r)) == 6 for r in ch.reshape(-1, 6))
+    for r in (1, 5):                                    # = the forced encode with that choice
+        pf = oracle.encode("iq1_s", w, grid, imp, choices=ch[:, :, r].reshape(1, 5, 1, 8))
+        xf = oracle.decode("iq1_s", pf, grid).reshape(-1, 8, 32)
+        np.testing.assert_array_equal(err[:, :, r, :], (xf - w.reshape(-1, 8, 32)).astype(np.float32))
+
+
 # --------------------------------------------------------------------------
 # choice search
 # --------------------------------------------------------------------------
