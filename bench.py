@@ -55,6 +55,11 @@ WORKLOADS = {
                            "batched call, per-expert importance"),
     "c5": ("c5_choice_search", "IQ2_XS top-8 candidate encode + local-Hessian choice search, "
                                "4096 rows x one 256-column block, 2 sweeps"),
+    "c5_iq1s": ("c5_iq1s_choice_search", "IQ1_S top-8 candidate encode + local-Hessian choice "
+                                         "search (G=8), 4096 rows x one 256-column block, 2 sweeps"),
+    "c5_weight": ("c5_weight_choice_search", "IQ2_XS top-8 candidate encode + local-Hessian choice "
+                                             "search of a whole 4096x4096 weight: 16 blocks, one H "
+                                             "each, searched in one launch, 2 sweeps"),
     # The same IQ1_S 4096x4096 weighted workload through the other encode outputs.
     "c2_every": ("c2_iq1s_4096", "IQ1_S weighted every-choice encode (16 payloads from one sweep) "
                                  "of a 4096x4096 fp32 weight"),
@@ -228,14 +233,18 @@ def main():
     stream = torch.cuda.current_stream()
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    if args.config == "c5":
+    if args.config.startswith("c5"):
         H = torch.from_numpy(cfg["H"]).to(dev)
         w2 = w[0].contiguous()
         imp2 = imp[0].contiguous()
+        G = iq.CHOICE_GROUPS[fmt]
+        R, C = w2.shape
+        shape = (R, G, 8, 256 // G) if H.dim() == 2 else (R, C // 256, G, 8, 256 // G)
 
         def step():
-            err, ch, _ = iq.encode_candidates(w2, grid, imp2, top_c=8, status=status, check=False)
-            iq.choice_search(H, err.view(w2.shape[0], 16, 8, 16), sweeps=2)
+            err, ch, _ = iq.encode_candidates(w2, grid, imp2, fmt=fmt, top_c=8, status=status,
+                                              check=False)
+            iq.choice_search(H, err.view(shape), sweeps=2)
     elif args.config.endswith("_every"):
         B, R, C = w.shape
         out = torch.empty((16, B, R, C // 256, iq.BLOCK_BYTES[fmt]), dtype=torch.uint8, device=dev)
@@ -302,7 +311,7 @@ def main():
                    "cols": int(w_np.shape[-1]), "batch": int(w_np.shape[0]),
                    "weights_per_sec": round(nweights / (ms_per_step * 1e-3), 1)},
     }
-    if args.config != "c5":
+    if not args.config.startswith("c5"):
         groups = nweights // 8
         weighted = imp is not None
         flops = groups * cfg["grid"].shape[0] * FLOPS_PER_GROUP_ENTRY[(fmt, weighted)]

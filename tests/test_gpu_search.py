@@ -198,3 +198,42 @@ def test_batched_block_search_equals_per_block_searches(fmt):
         np.testing.assert_array_equal(picks[:, b].cpu().numpy(), p1.cpu().numpy())
         np.testing.assert_array_equal(trace[:, :, b].cpu().numpy(), t1.cpu().numpy())
         _search_parity(Hs[b], cb)
+
+
+def test_c5_iq1s_choice_search_full():
+    cfg = workloads.c5_iq1s_choice_search()
+    H, w, grid, imp = cfg["H"], cfg["w"][0], cfg["grid"], cfg["importance"][0]
+    err, ch, _ = iq.encode_candidates(_dev(w), _dev(grid), _dev(imp), fmt="iq1_s", top_c=8)
+    cand = err.reshape(4096, 8, 8, 32).contiguous()
+    rows = np.random.default_rng(6).integers(0, 4096, 48)
+    _check_candidates(w[rows], grid, imp, 8, fmt="iq1_s")
+    cand_np = cand.cpu().numpy()
+    trace, rtrace, nd = _search_parity(H, cand_np)
+    assert np.any(trace[0] != trace[2])
+
+
+def test_c5_weight_batched_search_sampled():
+    # The whole 4096x4096 IQ2_XS weight: candidates of all 16 blocks in one
+    # launch, the 16 blocks searched in one launch; sampled rows of every
+    # block against the oracle (the search is independent per row).
+    cfg = workloads.c5_weight_choice_search()
+    Hs, w, grid, imp = cfg["H"], cfg["w"][0], cfg["grid"], cfg["importance"][0]
+    err, ch, _ = iq.encode_candidates(_dev(w), _dev(grid), _dev(imp), top_c=8)
+    cand = err.reshape(4096, 16, 16, 8, 16)
+    picks, trace = iq.choice_search(_dev(Hs), cand, trace=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.random.default_rng(7).integers(0, 4096, 24))
+    cand_np = cand[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    tr = trace.cpu().numpy()[:, rows]
+    for b in range(16):
+        cb = np.ascontiguousarray(cand_np[:, b])
+        rpicks, rtrace = oracle.choice_search(Hs[b], cb, sweeps=2)
+        differ = np.nonzero(np.any(tr[:, :, b] != rtrace, axis=(0, 2)))[0]
+        for r in differ:
+            fail, worst = oracle.choice_replay(Hs[b], cb[r], tr[:, r, b, :], REPLAY_TOL)
+            assert fail == 0, "block %d row %d: decision %d off by %.3g" % (b, r, fail - 1, worst)
+        assert len(differ) <= 2
+    # candidates of a few rows of a few blocks against the oracle
+    for b in (0, 7, 15):
+        _check_candidates(np.ascontiguousarray(w[rows[:8], 256 * b:256 * (b + 1)]), grid,
+                          np.ascontiguousarray(imp[256 * b:256 * (b + 1)]), 8)

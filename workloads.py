@@ -113,10 +113,34 @@ def c5_choice_search():
             "top_c": 8, "sweeps": 2}
 
 
+def c5_iq1s_choice_search():
+    """The search workload for IQ1_S: 4096 rows x the first 256 columns of the
+    IQ1_S weight (seed 1), H from seed 7, importance sqrt(diag H), top-8 of the
+    16 (k, delta) choices per 32-column sub-block (G = 8)."""
+    h = block_hessian(256, 7)
+    w = normal_weight((1, 4096, 4096), 1)[:, :, :256].copy()
+    imp = np.sqrt(np.diag(h).astype(np.float64)).astype(np.float32)[None, :]
+    return {"fmt": "iq1_s", "w": w, "importance": imp, "grid": iq1s_grid(), "H": h,
+            "top_c": 8, "sweeps": 2}
+
+
+def c5_weight_choice_search():
+    """Local-Hessian calibration of a whole IQ2_XS weight: the 4096x4096 weight
+    of c3 (seed 3), one H per 256-column block (seeds 7..22), importance
+    sqrt(diag H) per column, top-8 candidates, 16 blocks searched in one launch."""
+    hs = np.stack([block_hessian(256, 7 + b) for b in range(16)])
+    w = student_t_weight((1, 4096, 4096), 3)
+    imp = np.sqrt(np.concatenate([np.diag(h) for h in hs]).astype(np.float64)).astype(np.float32)
+    return {"fmt": "iq2_xs", "w": w, "importance": imp[None, :], "grid": iq2xs_grid(), "H": hs,
+            "top_c": 8, "sweeps": 2}
+
+
 CONFIGS = {
     "c1": c1_iq1s_small,
     "c2": c2_iq1s_4096,
     "c3": c3_iq2xs_4096,
     "c4": c4_moe_batch,
     "c5": c5_choice_search,
+    "c5_iq1s": c5_iq1s_choice_search,
+    "c5_weight": c5_weight_choice_search,
 }
