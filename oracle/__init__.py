@@ -24,8 +24,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "iq_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-BLOCK_BYTES = {"iq1_s": 50, "iq2_xs": 74}
-NUM_CHOICE_GROUPS = {"iq1_s": 8, "iq2_xs": 16}
+BLOCK_BYTES = {"iq1_s": 50, "iq2_xs": 74, "iq1_m": 56}
+NUM_CHOICE_GROUPS = {"iq1_s": 8, "iq2_xs": 16, "iq1_m": 16}
+NUM_CHOICES = {"iq1_s": 16, "iq2_xs": 16, "iq1_m": 8}
+_ENCODE = {"iq1_s": "orc_iq1s_encode", "iq2_xs": "orc_iq2xs_encode", "iq1_m": "orc_iq1m_encode"}
+_DECODE = {"iq1_s": "orc_iq1s_decode", "iq2_xs": "orc_iq2xs_decode", "iq1_m": "orc_iq1m_decode"}
 
 ERRORS = {1: "non-finite weight", 2: "negative or non-finite importance",
           3: "scale out of fp16 range", 4: "bad argument", 5: "grid index beyond the grid"}
@@ -63,14 +66,20 @@ def lib():
         L.orc_f16_to_f64.restype = ctypes.c_double
         L.orc_predict_scale.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.c_float]
         L.orc_predict_scale.restype = ctypes.c_uint16
-        for name in ("orc_iq1s_encode", "orc_iq2xs_encode"):
+        for name in _ENCODE.values():
             f = getattr(L, name)
             f.argtypes = [P, P, i64, P, i32, P, P, P]
             f.restype = ctypes.c_int
-        for name in ("orc_iq1s_decode", "orc_iq2xs_decode"):
+        for name in _DECODE.values():
             f = getattr(L, name)
             f.argtypes = [P, i64, P, i32, P]
             f.restype = ctypes.c_int
+        L.orc_iq1m_candidates.argtypes = [P, P, i64, P, i32, i32, P, P, P]
+        L.orc_iq1m_candidates.restype = ctypes.c_int
+        L.orc_iq1m_anchor.argtypes = [P, ctypes.c_float]
+        L.orc_iq1m_anchor.restype = ctypes.c_float
+        L.orc_iq1m_predict.argtypes = [P, i64, P]
+        L.orc_iq1m_predict.restype = None
         L.orc_iq2xs_candidates.argtypes = [P, P, i64, P, i32, i32, P, P, P]
         L.orc_iq2xs_candidates.restype = ctypes.c_int
         L.orc_iq1s_candidates.argtypes = [P, P, i64, P, i32, i32, P, P, P]
@@ -126,9 +135,15 @@ def f16_bits_to_float(h: int) -> float:
 
 
 def predict_scale_bits(amax: float, fmt: str = "iq1_s") -> int:
-    """fp16 bits of (amax / divisor) * 0.61, computed in fp32."""
+    """fp16 bits of (amax / divisor) * 0.61, computed in fp32 (IQ1_S, IQ2_XS)."""
     divisor = 16.875 if fmt == "iq1_s" else 155.0
     return int(lib().orc_predict_scale(float(amax), divisor, 0.61))
+
+
+def iq1m_anchor(block) -> float:
+    """The IQ1_M peak-to-RMS anchor of one 256-value block (fp32)."""
+    x = np.ascontiguousarray(block, dtype=np.float32).reshape(256)
+    return float(lib().orc_iq1m_anchor(_ptr(x), float(np.abs(x).max())))
 
 
 # --------------------------------------------------------------------------
@@ -152,9 +167,9 @@ def encode(fmt: str, w, grid, importance=None, scales=None, choices=None) -> np.
     if choices is not None:
         G = NUM_CHOICE_GROUPS[fmt]
         ch = np.ascontiguousarray(choices, dtype=np.int32).reshape(nblk, G)
-        if ch.min() < 0 or ch.max() >= 16:
+        if ch.min() < 0 or ch.max() >= NUM_CHOICES[fmt]:
             raise OracleError("choice out of range")
-    f = lib().orc_iq1s_encode if fmt == "iq1_s" else lib().orc_iq2xs_encode
+    f = getattr(lib(), _ENCODE[fmt])
     st = f(_ptr(x), _ptr(imp), nblk, _ptr(grid), grid.shape[0], _ptr(sc), _ptr(ch), _ptr(out))
     if st:
         raise OracleError(ERRORS.get(st, "error %d" % st))
@@ -171,7 +186,7 @@ def encode_every_choice(fmt: str, w, grid, importance=None, scales=None) -> np.n
     G = NUM_CHOICE_GROUPS[fmt]
     return np.stack([encode(fmt, w, grid, importance, scales,
                             choices=np.full((B, R, C // 256, G), c, dtype=np.int32))
-                     for c in range(16)])
+                     for c in range(NUM_CHOICES[fmt])])
 
 
 def fake_quant(fmt: str, w, grid, importance=None, scales=None, choices=None) -> np.ndarray:
@@ -191,7 +206,7 @@ def encode_blocks(fmt: str, x, grid, imp=None, scales=None) -> np.ndarray:
     nb = BLOCK_BYTES[fmt]
     out = np.zeros((n, nb), dtype=np.uint8)
     sc = None if scales is None else np.ascontiguousarray(scales, dtype=np.uint16).reshape(n)
-    f = lib().orc_iq1s_encode if fmt == "iq1_s" else lib().orc_iq2xs_encode
+    f = getattr(lib(), _ENCODE[fmt])
     st = f(_ptr(x), _ptr(imp), n, _ptr(grid), grid.shape[0], _ptr(sc), None, _ptr(out))
     if st:
         raise OracleError(ERRORS.get(st, "error %d" % st))
@@ -214,6 +229,10 @@ def block_errors(fmt: str, packed_blocks, x, grid, imp=None) -> np.ndarray:
 def predict_scales(fmt: str, w) -> np.ndarray:
     """fp16 bits of the predicted scale of every 256-value block of w."""
     x = np.ascontiguousarray(w, dtype=np.float32).reshape(-1, 256)
+    if fmt == "iq1_m":
+        out = np.zeros(x.shape[0], dtype=np.uint16)
+        lib().orc_iq1m_predict(_ptr(x), x.shape[0], _ptr(out))
+        return out
     amax = np.abs(x).max(axis=1)
     return np.array([predict_scale_bits(a, fmt) for a in amax], dtype=np.uint16)
 
@@ -227,7 +246,7 @@ def decode(fmt: str, packed, grid, strict: bool = True) -> np.ndarray:
     nblk = p.size // nb
     grid = np.ascontiguousarray(grid, dtype=np.float32)
     out = np.zeros((nblk, 256), dtype=np.float64)
-    f = lib().orc_iq1s_decode if fmt == "iq1_s" else lib().orc_iq2xs_decode
+    f = getattr(lib(), _DECODE[fmt])
     st = f(_ptr(p), nblk, _ptr(grid), grid.shape[0], _ptr(out))
     if st and strict:
         raise OracleError(ERRORS.get(st, "error %d" % st))
@@ -274,9 +293,30 @@ def iq1s_candidates(w, grid, importance=None, top_c: int = 8):
     return err, ch, codes
 
 
+def iq1m_candidates(w, grid, importance=None, top_c: int = 8):
+    """Top-C local scales k (of 8) per 16-column IQ1_M scale group with their
+    error vectors (each group's shift is searched freely under k).
+
+    Returns cand_err [B*R*C/256, 16, top_c, 16] float32, cand_choice
+    [.., 16, top_c] int32 and cand_codes [.., 16, top_c, 2] uint16
+    (entry | shift << 11).
+    """
+    shape, x, imp = _blocks(w, importance)
+    nblk = x.shape[0]
+    grid = np.ascontiguousarray(grid, dtype=np.float32)
+    err = np.zeros((nblk, 16, top_c, 16), dtype=np.float32)
+    ch = np.zeros((nblk, 16, top_c), dtype=np.int32)
+    codes = np.zeros((nblk, 16, top_c, 2), dtype=np.uint16)
+    st = lib().orc_iq1m_candidates(_ptr(x), _ptr(imp), nblk, _ptr(grid), grid.shape[0], top_c,
+                                   _ptr(err), _ptr(ch), _ptr(codes))
+    if st:
+        raise OracleError(ERRORS.get(st, "error %d" % st))
+    return err, ch, codes
+
+
 def candidates(fmt: str, w, grid, importance=None, top_c: int = 8):
-    """The top-C candidates of either format (see iq1s_candidates / iq2xs_candidates)."""
-    f = iq1s_candidates if fmt == "iq1_s" else iq2xs_candidates
+    """The top-C candidates of any format (see the per-format functions)."""
+    f = {"iq1_s": iq1s_candidates, "iq2_xs": iq2xs_candidates, "iq1_m": iq1m_candidates}[fmt]
     return f(w, grid, importance, top_c)
 
 
@@ -326,7 +366,7 @@ def choice_replay(H, cand_row, trace_row, tol: float):
 # --------------------------------------------------------------------------
 
 def unit_errors(fmt: str, packed, w, grid, importance=None) -> np.ndarray:
-    """Weighted squared error per choice group (IQ1_S: 32 values, IQ2_XS: 16).
+    """Weighted squared error per choice group (IQ1_S: 32 values, IQ2_XS and IQ1_M: 16).
 
     Returns [nblk, G] float64: sum over the unit of w * (x - xhat)^2.
     """

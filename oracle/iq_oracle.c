@@ -25,6 +25,13 @@
  *  - "Register each GGML IQ format once" (#2525), IQ2_S commit body, section
  *    "What's distinctive about it": IQ2_XS stores a 7-bit parity-coded sign
  *    index and flips the weakest element to fix parity.
+ *  - "Register each GGML IQ format once" (#2525), IQ1_M commit bodies (#2513
+ *    "What's distinctive about it", "A scale-anchor correction"; #2595 "The
+ *    kernel"): IQ1_M has no leading scale field, its fp16 d is reassembled
+ *    from the top nibbles of four 16-bit scale words; a local scale per two
+ *    groups and a delta shift per group, both searched with the IQ1_S grid;
+ *    ties prefer the lower shift, then the lower entry; the anchor is
+ *    clamp(0.58 + 0.035 * peak_to_rms, 0.65, 0.95) instead of 0.61.
  *  - "[4/4] Run the local-Hessian choice search as one CUDA kernel" (#3218)
  *    and the embedded "[1/4] ... local_hessian" body (#3158), steps 1-3: encode
  *    under every choice, give each group its best choice under its own H_gg,
@@ -46,7 +53,17 @@
  *  - IQ2_XS scale nibble of scale group m: low half of byte 66 + m/2 for even
  *    m, high half for odd m;
  *  - choice search: ties go to the lowest candidate index; a sweep changes a
- *    group only on a strict improvement; groups are visited in ascending order.
+ *    group only on a strict improvement; groups are visited in ascending order;
+ *  - IQ1_M: 56 bytes = 32 low index bytes, 16 bytes holding one nibble per
+ *    group (3 high index bits, then the shift bit: set = -1/8; even group in
+ *    the low nibble), then four little-endian 16-bit scale words; word w holds
+ *    the 3-bit local scales k of scale groups 4w..4w+3 at bits 0, 3, 6, 9 and
+ *    nibble w of d's fp16 bits at bits 12-15; s = d*(2k+1), k = 0..7; the
+ *    predictor divisor is 16.875 as for IQ1_S; peak_to_rms = amax / sqrt(mean
+ *    of squares) in fp32, the squares summed in a fixed order (64 partial sums
+ *    of 4 consecutive squares, then pairwise at distances 1, 2, 4, ..., 32),
+ *    the anchor 0.58 + 0.035 * ratio (multiply, then add) clamped to
+ *    [0.65, 0.95]; an all-zero block has d = 0.
  *
  * All search arithmetic is float64 in the direct form sum_j w_j (x_j - xhat_j)^2.
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared.
@@ -275,6 +292,217 @@ static int iq1s_decode_block(const uint8_t* blk, const float* grid, int n, doubl
         }
     }
     return st;
+}
+
+/* ---------------------------------------------------------------------- */
+/* IQ1_M                                                                   */
+/* ---------------------------------------------------------------------- */
+
+#define IQ1M_DIVISOR 16.875f
+
+/* The peak-to-RMS anchor of one block, in fp32 with the fixed summation order
+ * (every operation rounded to fp32: volatile, and no contraction). */
+float orc_iq1m_anchor(const float* x, float amax)
+{
+    volatile float p[64], q[64];
+    for (int l = 0; l < 64; ++l) {
+        volatile float a0 = x[4 * l] * x[4 * l];
+        volatile float a1 = x[4 * l + 1] * x[4 * l + 1];
+        volatile float a2 = x[4 * l + 2] * x[4 * l + 2];
+        volatile float a3 = x[4 * l + 3] * x[4 * l + 3];
+        volatile float s = a0 + a1;
+        s = s + a2;
+        s = s + a3;
+        p[l] = s;
+    }
+    for (int o = 1; o < 64; o <<= 1) {
+        for (int l = 0; l < 64; ++l) q[l] = p[l] + p[l ^ o];
+        for (int l = 0; l < 64; ++l) p[l] = q[l];
+    }
+    volatile float mean = p[0] / 256.0f;
+    volatile float rms = sqrtf(mean);
+    volatile float ratio = amax / rms;
+    volatile float t = 0.035f * ratio;
+    volatile float a = 0.58f + t;
+    if (a < 0.65f) a = 0.65f;
+    if (a > 0.95f) a = 0.95f;
+    return a;
+}
+
+static int iq1m_block_scale(const float* x, const uint16_t* pinned, uint16_t* dh)
+{
+    uint16_t h;
+    if (pinned) {
+        h = *pinned;
+    } else {
+        float amax = block_amax(x, 256);
+        h = amax > 0.0f ? orc_predict_scale(amax, IQ1M_DIVISOR, orc_iq1m_anchor(x, amax)) : 0;
+    }
+    if ((h & 0x7c00u) == 0x7c00u) return ORC_ERR_SCALE_RANGE;
+    if ((h & 0x8000u) && (h & 0x7fffu)) return ORC_ERR_SCALE_RANGE;
+    *dh = (uint16_t)(h & 0x7fffu);
+    return ORC_OK;
+}
+
+/* Best (shift, entry) of one group for local scale s: the least error, then
+ * the lower shift (delta = +1/8 first), then the lower entry. */
+static void iq1m_best_group(const float* x, const float* w, const float* grid, int n, double s,
+                            int* dbit, int* ent, double* err)
+{
+    double be = INFINITY;
+    int bd = 0, bi = 0;
+    for (int sh = 0; sh < 2; ++sh) {
+        double delta = sh ? -0.125 : 0.125;
+        double ge;
+        int e = iq1s_best_entry(x, w, grid, n, s, delta, &ge);
+        if (ge < be) { be = ge; bd = sh; bi = e; }
+    }
+    *dbit = bd;
+    *ent = bi;
+    *err = be;
+}
+
+static void iq1m_pack_group(uint8_t* blk, int g, int ent, int dbit)
+{
+    blk[g] = (uint8_t)(ent & 0xff);
+    uint32_t nib = (uint32_t)((ent >> 8) & 7) | ((uint32_t)dbit << 3);
+    blk[32 + g / 2] |= (uint8_t)(nib << (4 * (g & 1)));
+}
+
+static void iq1m_pack_scales(uint8_t* blk, const int k[16], uint16_t dh)
+{
+    for (int wd = 0; wd < 4; ++wd) {
+        uint32_t v = 0;
+        for (int t = 0; t < 4; ++t) v |= (uint32_t)(k[4 * wd + t] & 7) << (3 * t);
+        v |= (uint32_t)((dh >> (4 * wd)) & 0xf) << 12;
+        blk[48 + 2 * wd] = (uint8_t)(v & 0xff);
+        blk[49 + 2 * wd] = (uint8_t)(v >> 8);
+    }
+}
+
+/* choices: NULL or 16 forced local scales k in 0..7 (one per scale group). */
+static int iq1m_encode_block(const float* x, const float* w, const float* grid, int n,
+                             const uint16_t* pinned, const int32_t* choices, uint8_t* blk)
+{
+    memset(blk, 0, 56);
+    int st = check_block_inputs(x, w, 256);
+    if (st) return st;
+    uint16_t dh;
+    st = iq1m_block_scale(x, pinned, &dh);
+    if (st) return st;
+    if (dh == 0) return ORC_OK;
+    double d = orc_f16_to_f64(dh);
+    int kk[16];
+    for (int m = 0; m < 16; ++m) {
+        int k_lo = 0, k_hi = 8;
+        if (choices) { k_lo = choices[m]; k_hi = k_lo + 1; }
+        double best_cost = INFINITY;
+        int best_k = k_lo, best_d[2] = {0, 0}, best_e[2] = {0, 0};
+        for (int k = k_lo; k < k_hi; ++k) {
+            double s = d * (double)(2 * k + 1);
+            double cost = 0.0;
+            int db[2], en[2];
+            for (int h = 0; h < 2; ++h) {
+                int off = 16 * m + 8 * h;
+                double ge;
+                iq1m_best_group(x + off, w ? w + off : NULL, grid, n, s, &db[h], &en[h], &ge);
+                cost += ge;
+            }
+            if (cost < best_cost) {
+                best_cost = cost;
+                best_k = k;
+                best_d[0] = db[0]; best_d[1] = db[1];
+                best_e[0] = en[0]; best_e[1] = en[1];
+            }
+        }
+        kk[m] = best_k;
+        for (int h = 0; h < 2; ++h) iq1m_pack_group(blk, 2 * m + h, best_e[h], best_d[h]);
+    }
+    iq1m_pack_scales(blk, kk, dh);
+    return ORC_OK;
+}
+
+static int iq1m_decode_block(const uint8_t* blk, const float* grid, int n, double* out)
+{
+    int st = ORC_OK;
+    uint32_t sc[4];
+    for (int wd = 0; wd < 4; ++wd) sc[wd] = (uint32_t)blk[48 + 2 * wd] | ((uint32_t)blk[49 + 2 * wd] << 8);
+    /* d from the top nibble of each scale word, as the IQ1_M page prints it */
+    uint16_t dh = (uint16_t)((sc[0] >> 12) | ((sc[1] >> 8) & 0x00f0u) | ((sc[2] >> 4) & 0x0f00u) |
+                             (sc[3] & 0xf000u));
+    double d = orc_f16_to_f64(dh);
+    for (int g = 0; g < 32; ++g) {
+        int m = g / 2;
+        int k = (int)((sc[m / 4] >> (3 * (m % 4))) & 7u);
+        uint32_t nib = (blk[32 + g / 2] >> (4 * (g & 1))) & 0xfu;
+        int e = blk[g] | (int)((nib & 7u) << 8);
+        double delta = (nib & 8u) ? -0.125 : 0.125;
+        double s = d * (double)(2 * k + 1);
+        if (e >= n) {
+            st = ORC_ERR_CODE;
+            for (int j = 0; j < 8; ++j) out[8 * g + j] = 0.0;
+            continue;
+        }
+        for (int j = 0; j < 8; ++j) out[8 * g + j] = s * ((double)grid[8 * e + j] + delta);
+    }
+    return st;
+}
+
+/* Top-C local scales of every scale group of one IQ1_M block, ordered by
+ * (cost, k); each with its two codes (entry | shift << 11) and its error
+ * vector xhat - x over the 16 columns.  A zero scale orders k = 0, 1, ... with
+ * entry 0 and shift +1/8. */
+static int iq1m_candidates_block(const float* x, const float* w, const float* grid, int n,
+                                 int top_c, float* cand_err, int32_t* cand_choice,
+                                 uint16_t* cand_codes)
+{
+    int st = check_block_inputs(x, w, 256);
+    if (st) return st;
+    uint16_t dh;
+    st = iq1m_block_scale(x, NULL, &dh);
+    if (st) return st;
+    double d = orc_f16_to_f64(dh);
+    for (int m = 0; m < 16; ++m) {
+        double cost[8];
+        int db[8][2], en[8][2];
+        for (int k = 0; k < 8; ++k) {
+            double s = d * (double)(2 * k + 1);
+            cost[k] = 0.0;
+            for (int h = 0; h < 2; ++h) {
+                int off = 16 * m + 8 * h;
+                double ge;
+                iq1m_best_group(x + off, w ? w + off : NULL, grid, n, s, &db[k][h], &en[k][h], &ge);
+                cost[k] += ge;
+            }
+            if (dh == 0) {
+                cost[k] = 0.0;
+                db[k][0] = db[k][1] = en[k][0] = en[k][1] = 0;
+            }
+        }
+        int used[8] = {0};
+        for (int r = 0; r < top_c; ++r) {
+            int kb = -1;
+            for (int k = 0; k < 8; ++k) {
+                if (used[k]) continue;
+                if (kb < 0 || cost[k] < cost[kb]) kb = k;
+            }
+            used[kb] = 1;
+            cand_choice[m * top_c + r] = kb;
+            double s = d * (double)(2 * kb + 1);
+            for (int h = 0; h < 2; ++h) {
+                const float* q = grid + 8 * en[kb][h];
+                double delta = db[kb][h] ? -0.125 : 0.125;
+                if (cand_codes)
+                    cand_codes[(m * top_c + r) * 2 + h] = (uint16_t)(en[kb][h] | (db[kb][h] << 11));
+                for (int j = 0; j < 8; ++j) {
+                    int col = 16 * m + 8 * h + j;
+                    double xhat = s * ((double)q[j] + delta);
+                    cand_err[(m * top_c + r) * 16 + 8 * h + j] = (float)(xhat - (double)x[col]);
+                }
+            }
+        }
+    }
+    return ORC_OK;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -573,6 +801,61 @@ int orc_iq2xs_encode(const float* x, const float* imp, int64_t nblk, const float
     int r = first_error(st, nblk);
     free(st);
     return r;
+}
+
+int orc_iq1m_encode(const float* x, const float* imp, int64_t nblk, const float* grid,
+                    int32_t n, const uint16_t* scales, const int32_t* choices, uint8_t* out)
+{
+    if (n <= 0 || n > 2048) return ORC_ERR_ARG;
+    int* st = (int*)calloc((size_t)(nblk > 0 ? nblk : 1), sizeof(int));
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < nblk; ++b)
+        st[b] = iq1m_encode_block(x + 256 * b, imp ? imp + 256 * b : NULL, grid, n,
+                                  scales ? scales + b : NULL, choices ? choices + 16 * b : NULL,
+                                  out + 56 * b);
+    int r = first_error(st, nblk);
+    free(st);
+    return r;
+}
+
+int orc_iq1m_decode(const uint8_t* packed, int64_t nblk, const float* grid, int32_t n, double* out)
+{
+    int* st = (int*)calloc((size_t)(nblk > 0 ? nblk : 1), sizeof(int));
+    #pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblk; ++b)
+        st[b] = iq1m_decode_block(packed + 56 * b, grid, n, out + 256 * b);
+    int r = first_error(st, nblk);
+    free(st);
+    return r;
+}
+
+/* cand_err: [nblk][16][top_c][16] float; cand_choice: [nblk][16][top_c];
+ * cand_codes: NULL or [nblk][16][top_c][2] (entry | shift << 11). */
+int orc_iq1m_candidates(const float* x, const float* imp, int64_t nblk, const float* grid,
+                        int32_t n, int32_t top_c, float* cand_err, int32_t* cand_choice,
+                        uint16_t* cand_codes)
+{
+    if (n <= 0 || n > 2048 || top_c < 1 || top_c > 8) return ORC_ERR_ARG;
+    int* st = (int*)calloc((size_t)(nblk > 0 ? nblk : 1), sizeof(int));
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < nblk; ++b)
+        st[b] = iq1m_candidates_block(x + 256 * b, imp ? imp + 256 * b : NULL, grid, n, top_c,
+                                      cand_err + (size_t)b * 16 * top_c * 16,
+                                      cand_choice + (size_t)b * 16 * top_c,
+                                      cand_codes ? cand_codes + (size_t)b * 16 * top_c * 2 : NULL);
+    int r = first_error(st, nblk);
+    free(st);
+    return r;
+}
+
+/* fp16 bits of the predicted IQ1_M scale of each block (0 for amax = 0). */
+void orc_iq1m_predict(const float* x, int64_t nblk, uint16_t* out)
+{
+    for (int64_t b = 0; b < nblk; ++b) {
+        const float* xb = x + 256 * b;
+        float amax = block_amax(xb, 256);
+        out[b] = amax > 0.0f ? orc_predict_scale(amax, IQ1M_DIVISOR, orc_iq1m_anchor(xb, amax)) : 0;
+    }
 }
 
 int orc_iq1s_decode(const uint8_t* packed, int64_t nblk, const float* grid, int32_t n, double* out)

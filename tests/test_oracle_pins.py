@@ -54,6 +54,43 @@ def iq2xs_fields(packed):
     return d, codes & 0x1FF, codes >> 9, scales
 
 
+def iq1m_fields(packed):
+    """IQ1_M fields: d reassembled from the top nibbles of the four scale words
+    as the IQ1_M page prints it; per group the entry and the shift bit; per
+    scale group the 3-bit local scale."""
+    b = packed.reshape(-1, 56).astype(np.int64)
+    sc = b[:, 48:56:2] | (b[:, 49:56:2] << 8)
+    d = (sc[:, 0] >> 12) | ((sc[:, 1] >> 8) & 0x00F0) | ((sc[:, 2] >> 4) & 0x0F00) | (sc[:, 3] & 0xF000)
+    nib = np.stack([b[:, 32:48] & 15, b[:, 32:48] >> 4], axis=2).reshape(-1, 32)
+    ent = b[:, 0:32] | ((nib & 7) << 8)
+    k = np.stack([(sc >> (3 * t)) & 7 for t in range(4)], axis=2).reshape(-1, 16)
+    return d, ent, nib >> 3, k
+
+
+def payload_d(fmt, p):
+    """fp16 bits of every block's d."""
+    if fmt == "iq1_m":
+        return iq1m_fields(p)[0]
+    b = p.reshape(-1, oracle.BLOCK_BYTES[fmt]).astype(np.int64)
+    return b[:, 0] | (b[:, 1] << 8)
+
+
+def payload_choices(fmt, p):
+    """Per choice group, the choice the payload carries."""
+    if fmt == "iq1_s":
+        _, _, k, sgn = iq1s_fields(p)
+        return k + 8 * sgn
+    if fmt == "iq2_xs":
+        return iq2xs_fields(p)[3]
+    return iq1m_fields(p)[3]
+
+
+def fmt_grid(fmt, n=None):
+    if fmt == "iq2_xs":
+        return workloads.iq2xs_grid(n or 512)
+    return workloads.iq1s_grid(n or 2048)
+
+
 # --------------------------------------------------------------------------
 # fp16 conversion and the scale predictor
 # --------------------------------------------------------------------------
@@ -300,10 +337,10 @@ def test_iq2xs_sign_parity_is_even_and_matches_input_signs():
 # --------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs", "iq1_m"])
 def test_uniform_importance_reproduces_the_unweighted_payload(fmt):
     # #2723: uniform importance reproduces the unweighted payload exactly.
-    grid = workloads.iq1s_grid(256) if fmt == "iq1_s" else workloads.iq2xs_grid(128)
+    grid = fmt_grid(fmt, 128 if fmt == "iq2_xs" else 256)
     w = workloads.normal_weight((1, 8, 512), 31)
     p0 = oracle.encode(fmt, w, grid)
     for c in (1.0, 4.0, 0.25):
@@ -311,15 +348,15 @@ def test_uniform_importance_reproduces_the_unweighted_payload(fmt):
         np.testing.assert_array_equal(p, p0)
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs", "iq1_m"])
 def test_weighted_encode_lowers_the_weighted_error(fmt):
-    grid = workloads.iq1s_grid(512) if fmt == "iq1_s" else workloads.iq2xs_grid(256)
+    grid = fmt_grid(fmt, 256 if fmt == "iq2_xs" else 512)
     w = workloads.normal_weight((1, 16, 512), 41)
     imp = workloads.lognormal_importance((1, 512), 42) ** 4
     pw = oracle.encode(fmt, w, grid, imp)
     pu = oracle.encode(fmt, w, grid)
     # same d on both (the predictor is unweighted)
-    np.testing.assert_array_equal(pw[..., :2], pu[..., :2])
+    np.testing.assert_array_equal(payload_d(fmt, pw), payload_d(fmt, pu))
     ew = oracle.unit_errors(fmt, pw, w, grid, imp)
     eu = oracle.unit_errors(fmt, pu, w, grid, imp)
     if fmt == "iq2_xs":
@@ -356,16 +393,16 @@ def test_iq1s_payload_beats_random_single_code_perturbations():
         assert e[b, i] >= base[b, i] * (1 - 1e-12)
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs", "iq1_m"])
 def test_decode_then_reencode_under_its_own_scales(fmt):
     # #3197: a decoding re-encodes exactly under its own pinned scales.
-    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    grid = fmt_grid(fmt)
     w = workloads.normal_weight((1, 8, 512), 61)
     imp = workloads.lognormal_importance((1, 512), 62)
     p = oracle.encode(fmt, w, grid, imp)
     xhat = oracle.decode(fmt, p, grid).astype(np.float32)
     assert np.array_equal(xhat.astype(np.float64), oracle.decode(fmt, p, grid))  # exact in fp32
-    d = (p[..., 0].astype(np.uint16) | (p[..., 1].astype(np.uint16) << 8))
+    d = payload_d(fmt, p).astype(np.uint16).reshape(1, 8, 2)
     p2 = oracle.encode(fmt, xhat, grid, imp, scales=d)
     # the re-encode reproduces the values exactly; bytes match unless another
     # code decodes to the very same values (then the lower choice index wins)
@@ -400,9 +437,9 @@ def test_range_checks_bite_with_truncated_grids():
     assert len(np.unique(sc)) > 1 and np.all(d > 0)
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs", "iq1_m"])
 def test_zero_and_underflow_blocks_are_all_zero_bytes(fmt):
-    grid = workloads.iq1s_grid(64) if fmt == "iq1_s" else workloads.iq2xs_grid(64)
+    grid = fmt_grid(fmt, 64)
     w = workloads.normal_weight((1, 3, 256), 81)
     w[0, 0] = 0.0
     w[0, 1] *= 1e-7                              # amax ~ 1e-8: d underflows to fp16 zero
@@ -410,9 +447,9 @@ def test_zero_and_underflow_blocks_are_all_zero_bytes(fmt):
     assert not p[0, 0].any() and not p[0, 1].any() and p[0, 2].any()
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs", "iq1_m"])
 def test_rejects_bad_inputs(fmt):
-    grid = workloads.iq1s_grid(64) if fmt == "iq1_s" else workloads.iq2xs_grid(64)
+    grid = fmt_grid(fmt, 64)
     w = workloads.normal_weight((1, 2, 256), 91)
     bad = w.copy()
     bad[0, 1, 7] = np.nan
@@ -447,26 +484,25 @@ def test_sanity_bounds():
     assert ((x - xh2) ** 2).sum() < ((x - xh) ** 2).sum()
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs", "iq1_m"])
 def test_forced_choices_reproduce_the_free_encode(fmt):
     # #3157: a fixed choice reproduces, group by group, the payload encoded with
     # that choice; forcing the free encode's own picks reproduces it.
-    grid = workloads.iq1s_grid(256) if fmt == "iq1_s" else workloads.iq2xs_grid(128)
+    grid = fmt_grid(fmt, 128 if fmt == "iq2_xs" else 256)
     w = workloads.normal_weight((1, 4, 512), 101)
     imp = workloads.lognormal_importance((1, 512), 102)
     p = oracle.encode(fmt, w, grid, imp)
-    if fmt == "iq1_s":
-        _, _, k, sgn = iq1s_fields(p)
-        ch = (k + 8 * sgn).reshape(1, 4, 2, 8)
-    else:
-        _, _, _, sc = iq2xs_fields(p)
-        ch = sc.reshape(1, 4, 2, 16)
+    G = oracle.NUM_CHOICE_GROUPS[fmt]
+    ch = payload_choices(fmt, p).reshape(1, 4, 2, G)
     np.testing.assert_array_equal(oracle.encode(fmt, w, grid, imp, choices=ch), p)
     # every group forced to one choice: each unit's error >= the free optimum
-    for c in (0, 5, 11):
+    for c in (0, 5, 7 if fmt == "iq1_m" else 11):
         pc = oracle.encode(fmt, w, grid, imp, choices=np.full_like(ch, c))
+        assert np.all(payload_choices(fmt, pc) == c)
         assert np.all(oracle.unit_errors(fmt, pc, w, grid, imp)
                       >= oracle.unit_errors(fmt, p, w, grid, imp) * (1 - 1e-12))
+    with pytest.raises(oracle.OracleError):
+        oracle.encode(fmt, w, grid, imp, choices=np.full_like(ch, oracle.NUM_CHOICES[fmt]))
 
 
 # --------------------------------------------------------------------------
@@ -474,49 +510,41 @@ def test_forced_choices_reproduce_the_free_encode(fmt):
 # --------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs", "iq1_m"])
 def test_every_choice_payloads_carry_their_choice_and_contain_the_free_encode(fmt):
     # #3159: packed[c] is the encode with every choice group forced to c.  So
     # every unit of packed[c] carries choice c, and per unit the least weighted
     # error over c is the free encode's, reached first at the free encode's
     # own choice (the free encode is pinned by brute force above).
-    grid = workloads.iq1s_grid(192) if fmt == "iq1_s" else workloads.iq2xs_grid(96)
+    grid = fmt_grid(fmt, 96 if fmt == "iq2_xs" else 192)
+    nc = oracle.NUM_CHOICES[fmt]
     w = workloads.normal_weight((2, 3, 256), 131)
     w[1, 2] = 0.0                                    # a zero block: all-zero in every payload
     imp = workloads.lognormal_importance((2, 256), 132)
     every = oracle.encode_every_choice(fmt, w, grid, imp)
-    assert every.shape == (16, 2, 3, 1, oracle.BLOCK_BYTES[fmt])
+    assert every.shape == (nc, 2, 3, 1, oracle.BLOCK_BYTES[fmt])
     free = oracle.encode(fmt, w, grid, imp)
     assert not every[:, 1, 2].any()
     live = np.ones((6,), bool)
     live[5] = False
-    for c in range(16):
-        if fmt == "iq1_s":
-            d, _, k, sgn = iq1s_fields(every[c])
-            assert np.all((k + 8 * sgn)[live] == c)
-        else:
-            d, _, _, sc = iq2xs_fields(every[c])
-            assert np.all(sc[live] == c)
-        np.testing.assert_array_equal(d, iq1s_fields(free)[0] if fmt == "iq1_s" else iq2xs_fields(free)[0])
-    errs = np.stack([oracle.unit_errors(fmt, every[c], w, grid, imp) for c in range(16)])
+    for c in range(nc):
+        assert np.all(payload_choices(fmt, every[c])[live] == c)
+        np.testing.assert_array_equal(payload_d(fmt, every[c]), payload_d(fmt, free))
+    errs = np.stack([oracle.unit_errors(fmt, every[c], w, grid, imp) for c in range(nc)])
     e_free = oracle.unit_errors(fmt, free, w, grid, imp)
     np.testing.assert_allclose(errs.min(axis=0), e_free, rtol=1e-12, atol=0)
-    if fmt == "iq1_s":
-        _, _, k, sgn = iq1s_fields(free)
-        c_free = (k + 8 * sgn).reshape(e_free.shape)
-    else:
-        c_free = iq2xs_fields(free)[3].reshape(e_free.shape)
+    c_free = payload_choices(fmt, free).reshape(e_free.shape)
     first = np.argmax(errs <= e_free[None] * (1 + 1e-12), axis=0)
-    live_units = np.repeat(live, e_free.shape[-1] if e_free.ndim == 2 else 1).reshape(c_free.shape)
+    live_units = np.repeat(live, e_free.shape[-1]).reshape(c_free.shape)
     np.testing.assert_array_equal(first[live_units], c_free[live_units])
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs", "iq1_m"])
 def test_fake_quant_is_the_decoded_encode(fmt):
     # The fake-quant weight is decode(encode(w)); decoding the printed worked
     # example is pinned above, so here its error must be the unit errors the
     # encode reports, and re-encoding it under its own scales is a fixed point.
-    grid = workloads.iq1s_grid(256) if fmt == "iq1_s" else workloads.iq2xs_grid(128)
+    grid = fmt_grid(fmt, 128 if fmt == "iq2_xs" else 256)
     w = workloads.normal_weight((1, 4, 512), 141)
     imp = workloads.lognormal_importance((1, 512), 142)
     xh = oracle.fake_quant(fmt, w, grid, imp)
@@ -698,3 +726,124 @@ def test_replay_accepts_the_oracles_trace_and_rejects_a_bad_one():
     bad[0, 0] = int(np.argmax(q))
     fail, _ = oracle.choice_replay(H, cand[0], bad, 1e-6)
     assert fail == 1
+
+
+# --------------------------------------------------------------------------
+# IQ1_M (#2525 IQ1_M commit bodies #2513, #2595)
+# --------------------------------------------------------------------------
+
+
+def test_iq1m_hand_block_decodes_as_worked_out():
+    g = load("iq1m_hand_block.txt")
+    grid = np.zeros((300, 8), np.float32)
+    grid[1] = g["grid_row_1"]
+    grid[257] = g["grid_row_257"]
+    blk = np.zeros(56, np.uint8)
+    blk[0] = blk[1] = blk[8] = blk[31] = 1
+    blk[32] = 0x90
+    blk[36] = 0x08
+    blk[47] = 0x10
+    for w_, v in enumerate(g["scale_words"]):
+        blk[48 + 2 * w_] = int(v) & 0xFF
+        blk[49 + 2 * w_] = int(v) >> 8
+    d, ent, shift, k = iq1m_fields(blk)
+    assert int(d[0]) == int(g["d_fp16_bits"]) and f16(int(d[0])) == 0.5
+    out = oracle.decode("iq1_m", blk.reshape(1, 1, 1, 56), grid).reshape(32, 8)
+    for grp in (0, 1, 2, 8, 31):
+        np.testing.assert_array_equal(out[grp], g["expected_group%d" % grp])
+    assert oracle.BLOCK_BYTES["iq1_m"] * 8 / 256 == 1.75
+
+
+def test_iq1m_scale_anchor_follows_peak_to_rms():
+    # #2513 "A scale-anchor correction": clamp(0.58 + 0.035 * peak_to_rms, 0.65,
+    # 0.95).  Blocks of n equal spikes have peak-to-RMS sqrt(256/n) exactly:
+    # 1, 4, 8, 16 reach both clamps and two points of the slope.
+    for n_spk, ratio in ((256, 1.0), (16, 4.0), (4, 8.0), (1, 16.0)):
+        x = np.zeros(256, np.float32)
+        x[::256 // n_spk] = 0.5
+        want = np.float32(0.58) + np.float32(np.float32(0.035) * np.float32(ratio))
+        want = min(max(want, np.float32(0.65)), np.float32(0.95))
+        assert oracle.iq1m_anchor(x) == want
+        t = np.float32(np.float32(0.5) / np.float32(16.875)) * want
+        bits = int(np.array([np.float32(t)]).astype(np.float16).view(np.uint16)[0])
+        assert int(oracle.predict_scales("iq1_m", x)[0]) == bits
+    assert oracle.iq1m_anchor(np.full(256, 0.25, np.float32)) == np.float32(0.65)
+    # a Gaussian block sits on the slope, above IQ1_S's flat 0.61
+    a = oracle.iq1m_anchor(workloads.normal_weight((256,), 151))
+    assert 0.65 < a < 0.8
+
+
+def _iq1m_brute_force_scale_group(x, w, grid, d):
+    """Every (k, shift0, e0, shift1, e1) of a scale group jointly; the
+    lexicographically first minimiser of the summed weighted error."""
+    n = grid.shape[0]
+    x = x.astype(np.float64).reshape(2, 8)
+    w = w.astype(np.float64).reshape(2, 8)
+    E = np.empty((8, 2, 2, n))                                   # [k, group, shift, entry]
+    for k in range(8):
+        s = d * (2 * k + 1)
+        for sh in range(2):
+            xhat = s * (grid.astype(np.float64) + (-0.125 if sh else 0.125))
+            E[k, :, sh] = (w[:, None, :] * (x[:, None, :] - xhat[None]) ** 2).sum(axis=2)
+    tot = E[:, 0, :, :, None, None] + E[:, 1, None, None, :, :]
+    k, s0, e0, s1, e1 = np.unravel_index(int(np.argmin(tot.reshape(-1))), tot.shape)
+    return int(k), [int(s0), int(s1)], [int(e0), int(e1)]
+
+
+@pytest.mark.parametrize("n,dup", [(3, False), (6, True)])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_iq1m_matches_joint_brute_force(n, dup, weighted):
+    grid = workloads.iq1s_grid(n, seed=n + 20)
+    if dup:
+        grid[4] = grid[1]
+    w = workloads.normal_weight((1, 2, 256), 500 + n)
+    imp = workloads.lognormal_importance((1, 256), 600 + n) if weighted else None
+    p = oracle.encode("iq1_m", w, grid, imp)
+    d, ent, shift, k = iq1m_fields(p)
+    wt = np.ones(256, np.float32) if imp is None else imp[0]
+    for b in range(2):
+        for m in range(16):
+            kk, sh, es = _iq1m_brute_force_scale_group(w[0, b, 16 * m:16 * m + 16],
+                                                       wt[16 * m:16 * m + 16], grid, f16(int(d[b])))
+            assert int(k[b, m]) == kk
+            assert [int(shift[b, 2 * m]), int(shift[b, 2 * m + 1])] == sh
+            assert [int(ent[b, 2 * m]), int(ent[b, 2 * m + 1])] == es
+            if dup:
+                assert 4 not in es
+
+
+def test_iq1m_candidates_are_the_sorted_choices_of_the_encode():
+    grid = workloads.iq1s_grid(384)
+    w = workloads.normal_weight((1, 5, 256), 161)
+    w[0, 4] = 0.0
+    imp = workloads.lognormal_importance((1, 256), 162)
+    err, ch, codes = oracle.iq1m_candidates(w, grid, imp, top_c=5)
+    assert err.shape == (5, 16, 5, 16) and codes.shape == (5, 16, 5, 2)
+    p = oracle.encode("iq1_m", w, grid, imp)
+    d, ent, shift, k = iq1m_fields(p)
+    np.testing.assert_array_equal(ch[:4, :, 0], k[:4])
+    np.testing.assert_array_equal(codes[:4, :, 0, 0], (ent | (shift << 11))[:4, 0::2])
+    np.testing.assert_array_equal(codes[:4, :, 0, 1], (ent | (shift << 11))[:4, 1::2])
+    xh = oracle.decode("iq1_m", p, grid).reshape(-1, 16, 16)
+    np.testing.assert_array_equal(err[:, :, 0, :], (xh - w.reshape(-1, 16, 16)).astype(np.float32))
+    np.testing.assert_array_equal(ch[4], np.tile(np.arange(5), (16, 1)))
+    assert all(len(set(r)) == 5 for r in ch.reshape(-1, 5))
+    for r in (1, 4):
+        pf = oracle.encode("iq1_m", w, grid, imp, choices=ch[:, :, r].reshape(1, 5, 1, 16))
+        xf = oracle.decode("iq1_m", pf, grid).reshape(-1, 16, 16)
+        np.testing.assert_array_equal(err[:, :, r, :], (xf - w.reshape(-1, 16, 16)).astype(np.float32))
+
+
+def test_iq1m_is_finer_than_iq1s_and_keeps_ranges():
+    # 1.75 bits against 1.5625: a lower error on the same weight; the range
+    # checks bite with a truncated grid; the shifts and scales vary.
+    w = workloads.normal_weight((1, 16, 256), 171)
+    x = w.reshape(-1).astype(np.float64)
+    g = workloads.iq1s_grid()
+    e_s = ((oracle.decode("iq1_s", oracle.encode("iq1_s", w, g), g).reshape(-1) - x) ** 2).sum()
+    p = oracle.encode("iq1_m", w, g)
+    e_m = ((oracle.decode("iq1_m", p, g).reshape(-1) - x) ** 2).sum()
+    assert e_m < e_s and e_m / (x ** 2).sum() < 0.25
+    _, ent, shift, k = iq1m_fields(oracle.encode("iq1_m", w, workloads.iq1s_grid(1500)))
+    assert 1024 < ent.max() < 1500
+    assert len(np.unique(k)) > 1 and 0 < shift.mean() < 1
