@@ -19,9 +19,10 @@ import torch  # noqa: F401  (device memory and streams; loads the HIP runtime fi
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libiqcodec.so")
 
-FORMATS = {"iq1_s": 0, "iq2_xs": 1}
-BLOCK_BYTES = {"iq1_s": 50, "iq2_xs": 74}
-CHOICE_GROUPS = {"iq1_s": 8, "iq2_xs": 16}
+FORMATS = {"iq1_s": 0, "iq2_xs": 1, "iq1_m": 2}
+BLOCK_BYTES = {"iq1_s": 50, "iq2_xs": 74, "iq1_m": 56}
+CHOICE_GROUPS = {"iq1_s": 8, "iq2_xs": 16, "iq1_m": 16}
+NUM_CHOICES = {"iq1_s": 16, "iq2_xs": 16, "iq1_m": 8}
 
 STATUS = {
     0: "IQ_OK", 1: "IQ_ERR_NULL", 2: "IQ_ERR_FORMAT", 3: "IQ_ERR_SHAPE", 4: "IQ_ERR_GRID",
@@ -202,13 +203,14 @@ def encode(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, 
 
 def encode_every_choice(w, grid, importance=None, *, fmt="iq1_s", scales=None, out=None,
                         status=None, check=True):
-    """The payload under every one of the 16 choices, from one sweep.
+    """The payload under every choice (16, or 8 for IQ1_M), from one sweep.
 
-    Returns [16, batch, rows, cols/256, block_bytes] uint8 (no batch dimension
-    for a 2-D weight); entry c equals ``encode(..., choices=full(c))``.
+    Returns [num_choices, batch, rows, cols/256, block_bytes] uint8 (no batch
+    dimension for a 2-D weight); entry c equals ``encode(..., choices=full(c))``.
     """
     f, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, None)
-    out = _out_tensor(out, (16, B, R, C // 256, BLOCK_BYTES[fmt]), torch.uint8, w.device, "out")
+    out = _out_tensor(out, (NUM_CHOICES[fmt], B, R, C // 256, BLOCK_BYTES[fmt]), torch.uint8,
+                      w.device, "out")
     status, own = _status_tensor(status, w.device)
     code = load().iq_encode_every_choice(f, _ptr(w), B, R, C, _ptr(importance), _ptr(grid),
                                          grid.shape[0], _ptr(scales), _ptr(out), _ptr(status),
@@ -272,10 +274,10 @@ def encode_candidates(w, grid, importance=None, *, fmt="iq2_xs", top_c=8, codes=
                       status=None, check=True):
     """Top-C choices per choice group of every 256-column block of [rows, cols].
 
-    IQ2_XS: 16 scale groups of 16 columns; IQ1_S: 8 sub-blocks of 32 columns.
-    Returns (cand_err [rows, cols/256, G, top_c, 256/G] fp32, cand_choice
-    [rows, cols/256, G, top_c] int32, cand_codes [..., 2 (IQ2_XS) or 4 (IQ1_S)]
-    uint16 viewed as int16, or None).
+    IQ2_XS, IQ1_M: 16 scale groups of 16 columns; IQ1_S: 8 sub-blocks of 32
+    columns.  Returns (cand_err [rows, cols/256, G, top_c, 256/G] fp32,
+    cand_choice [rows, cols/256, G, top_c] int32, cand_codes [..., 2 (IQ2_XS,
+    IQ1_M) or 4 (IQ1_S)] uint16 viewed as int16, or None).
     """
     f = _fmt(fmt)
     _dev_tensor(w, torch.float32, "w")
@@ -292,7 +294,7 @@ def encode_candidates(w, grid, importance=None, *, fmt="iq2_xs", top_c=8, codes=
     tc = max(int(top_c), 0)
     err = torch.empty((R, NB, G, tc, 256 // G), dtype=torch.float32, device=w.device)
     ch = torch.empty((R, NB, G, tc), dtype=torch.int32, device=w.device)
-    ncode = 2 if fmt == "iq2_xs" else 4
+    ncode = 4 if fmt == "iq1_s" else 2
     cc = (torch.empty((R, NB, G, tc, ncode), dtype=torch.int16, device=w.device)
           if codes else None)
     status, own = _status_tensor(status, w.device)

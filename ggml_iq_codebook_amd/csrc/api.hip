@@ -52,16 +52,25 @@ iq_status_t geometry(int64_t batch, int64_t rows, int64_t cols, iqk::BlockGeom* 
 
 iq_status_t from_hip(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_HIP; }
 
+bool known_format(iq_format_t fmt)
+{
+    return fmt == IQ_FMT_IQ1_S || fmt == IQ_FMT_IQ2_XS || fmt == IQ_FMT_IQ1_M;
+}
+
+int grid_max(iq_format_t fmt) { return fmt == IQ_FMT_IQ2_XS ? 512 : 2048; }
+
+int num_choices(iq_format_t fmt) { return fmt == IQ_FMT_IQ1_M ? 8 : 16; }
+
 hipError_t launch_encode(iq_format_t fmt, const float* w, const float* importance, const float* grid,
                          int32_t grid_size, const uint16_t* scales, const int32_t* choices,
                          uint8_t* out, float* xhat, int mode, int32_t* status,
                          const iqk::BlockGeom& g, hipStream_t stream)
 {
-    return fmt == IQ_FMT_IQ1_S
-        ? iqk::launch_iq1s_encode(w, importance, grid, grid_size, scales, choices, out, xhat, mode,
-                                  status, g, stream)
-        : iqk::launch_iq2xs_encode(w, importance, grid, grid_size, scales, choices, out, xhat, mode,
-                                   status, g, stream);
+    return fmt == IQ_FMT_IQ2_XS
+        ? iqk::launch_iq2xs_encode(w, importance, grid, grid_size, scales, choices, out, xhat, mode,
+                                   status, g, stream)
+        : iqk::launch_iq1_encode((int)fmt, w, importance, grid, grid_size, scales, choices, out,
+                                 xhat, mode, status, g, stream);
 }
 
 }  // namespace
@@ -75,6 +84,8 @@ iq_status_t iq_format_info(iq_format_t fmt, iq_format_info_t* out)
         *out = iq_format_info_t{256, 50, 8, 11, 2048, 8, 16};
     } else if (fmt == IQ_FMT_IQ2_XS) {
         *out = iq_format_info_t{256, 74, 8, 9, 512, 16, 16};
+    } else if (fmt == IQ_FMT_IQ1_M) {
+        *out = iq_format_info_t{256, 56, 8, 11, 2048, 16, 8};
     } else {
         return IQ_ERR_FORMAT;
     }
@@ -105,13 +116,12 @@ iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t ro
                       const uint16_t* scales, const int32_t* choices, uint8_t* out,
                       int32_t* status, hipStream_t stream)
 {
-    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    if (!known_format(fmt)) return IQ_ERR_FORMAT;
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
     if (!w || !grid || !out || !status) return IQ_ERR_NULL;
-    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
-    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
+    if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(out, 2) || (scales && !aligned(scales, 2)) || (choices && !aligned(choices, 4)) ||
         !aligned(status, 4))
@@ -127,13 +137,12 @@ iq_status_t iq_encode_every_choice(iq_format_t fmt, const float* w, int64_t batc
                                    int32_t grid_size, const uint16_t* scales, uint8_t* out,
                                    int32_t* status, hipStream_t stream)
 {
-    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    if (!known_format(fmt)) return IQ_ERR_FORMAT;
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
     if (!w || !grid || !out || !status) return IQ_ERR_NULL;
-    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
-    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
+    if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(out, 2) || (scales && !aligned(scales, 2)) || !aligned(status, 4))
         return IQ_ERR_ARG;
@@ -148,13 +157,12 @@ iq_status_t iq_fake_quant(iq_format_t fmt, const float* w, int64_t batch, int64_
                           int32_t grid_size, const uint16_t* scales, const int32_t* choices,
                           float* xhat, uint8_t* out, int32_t* status, hipStream_t stream)
 {
-    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    if (!known_format(fmt)) return IQ_ERR_FORMAT;
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
     if (!w || !grid || !xhat || !status) return IQ_ERR_NULL;
-    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
-    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
+    if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(xhat, 16) || (out && !aligned(out, 2)) || (scales && !aligned(scales, 2)) ||
         (choices && !aligned(choices, 4)) || !aligned(status, 4))
@@ -174,13 +182,12 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
                        int64_t cols, const float* grid, int32_t grid_size, float* out,
                        int32_t* status, hipStream_t stream)
 {
-    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    if (!known_format(fmt)) return IQ_ERR_FORMAT;
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
     if (!packed || !grid || !out || !status) return IQ_ERR_NULL;
-    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
-    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
+    if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (!aligned(grid, 16) || !aligned(out, 16) || !aligned(status, 4)) return IQ_ERR_ARG;
     st = check_device();
     if (st) return st;
@@ -192,23 +199,23 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, 
                                  int32_t top_c, float* cand_err, int32_t* cand_choice,
                                  uint16_t* cand_codes, int32_t* status, hipStream_t stream)
 {
-    if (fmt != IQ_FMT_IQ1_S && fmt != IQ_FMT_IQ2_XS) return IQ_ERR_FORMAT;
+    if (!known_format(fmt)) return IQ_ERR_FORMAT;
     iqk::BlockGeom g;
     iq_status_t st = geometry(1, rows, cols, &g);
     if (st) return st;
     if (!w || !grid || !cand_err || !cand_choice || !status) return IQ_ERR_NULL;
-    const int gmax = fmt == IQ_FMT_IQ1_S ? 2048 : 512;
-    if (grid_size < 1 || grid_size > gmax) return IQ_ERR_GRID;
-    if (top_c < 1 || top_c > 16) return IQ_ERR_ARG;
+    if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
+    if (top_c < 1 || top_c > num_choices(fmt)) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(cand_err, 16) || !aligned(cand_choice, 4) ||
         (cand_codes && !aligned(cand_codes, 2)) || !aligned(status, 4))
         return IQ_ERR_ARG;
     st = check_device();
     if (st) return st;
-    if (fmt == IQ_FMT_IQ1_S)
-        return from_hip(iqk::launch_iq1s_candidates(w, importance, grid, grid_size, top_c, cand_err,
-                                                    cand_choice, cand_codes, status, g, stream));
+    if (fmt != IQ_FMT_IQ2_XS)
+        return from_hip(iqk::launch_iq1_candidates((int)fmt, w, importance, grid, grid_size, top_c,
+                                                   cand_err, cand_choice, cand_codes, status, g,
+                                                   stream));
     return from_hip(iqk::launch_iq2xs_candidates(w, importance, grid, grid_size, top_c, cand_err,
                                                  cand_choice, cand_codes, status, g, stream));
 }

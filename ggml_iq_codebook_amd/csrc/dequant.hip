@@ -91,6 +91,48 @@ __global__ __launch_bounds__(kThreads) void dequant_iq2xs_kernel(const uint8_t* 
     o[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// IQ1_M (#2525 IQ1_M codec body): d reassembled from the top nibbles of the
+// four scale words; the 3-bit local scale of the group's scale group; the
+// group's nibble gives the 3 high index bits and the shift.
+__global__ __launch_bounds__(kThreads) void dequant_iq1m_kernel(const uint8_t* __restrict__ packed,
+                                                                const float* __restrict__ grid, int n,
+                                                                float* __restrict__ out,
+                                                                int32_t* status, int64_t ngroups)
+{
+    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= ngroups) return;
+    const int64_t blk = gid >> 5;
+    const int g = (int)(gid & 31);
+    const int m = g >> 1;
+    const uint8_t* b = packed + blk * 56;
+    uint32_t sc[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) sc[w] = (uint32_t)b[48 + 2 * w] | ((uint32_t)b[49 + 2 * w] << 8);
+    const uint32_t dh = (sc[0] >> 12) | ((sc[1] >> 8) & 0x00f0u) | ((sc[2] >> 4) & 0x0f00u) |
+                        (sc[3] & 0xf000u);
+    const int k = (int)((sc[m >> 2] >> (3 * (m & 3))) & 7u);
+    const uint32_t nib = ((uint32_t)b[32 + (g >> 1)] >> (4 * (g & 1))) & 0xfu;
+    const int e = (int)b[g] | (int)((nib & 7u) << 8);
+    const float delta = (nib & 8u) ? -0.125f : 0.125f;
+    const float s = f16_bits_to_f32(dh) * (float)(2 * k + 1);
+    float v[8];
+    if (e < n) {
+        const float4* q4 = reinterpret_cast<const float4*>(grid + 8 * e);
+        const float4 q0 = q4[0], q1 = q4[1];
+        v[0] = s * (q0.x + delta); v[1] = s * (q0.y + delta);
+        v[2] = s * (q0.z + delta); v[3] = s * (q0.w + delta);
+        v[4] = s * (q1.x + delta); v[5] = s * (q1.y + delta);
+        v[6] = s * (q1.z + delta); v[7] = s * (q1.w + delta);
+    } else {
+        report(status, IQ_ERR_CODE);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+    float4* o = reinterpret_cast<float4*>(out + gid * 8);
+    o[0] = make_float4(v[0], v[1], v[2], v[3]);
+    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 }  // namespace
 
 hipError_t launch_dequant(int fmt, const uint8_t* packed, const float* grid, int grid_size,
@@ -100,6 +142,9 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, const float* grid, int
     const int64_t wgs = (ngroups + kThreads - 1) / kThreads;
     if (fmt == IQ_FMT_IQ1_S)
         hipLaunchKernelGGL(dequant_iq1s_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream,
+                           packed, grid, grid_size, out, status, ngroups);
+    else if (fmt == IQ_FMT_IQ1_M)
+        hipLaunchKernelGGL(dequant_iq1m_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream,
                            packed, grid, grid_size, out, status, ngroups);
     else
         hipLaunchKernelGGL(dequant_iq2xs_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream,

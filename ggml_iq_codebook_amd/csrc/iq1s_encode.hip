@@ -58,6 +58,7 @@ constexpr int kChunkTiles = 8;                       // tiles per tracking chunk
 constexpr int kChunk = kTile * kChunkTiles;          // 128 entries
 constexpr int kMaxGrid = 2048;
 constexpr int kBlockBytes = 50;
+constexpr int kBlockBytesM = 56;
 
 struct Iq1sArgs {
     const float* w;
@@ -164,11 +165,18 @@ __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, 
     return idx;
 }
 
-template <int kMode>
+template <int kFmt, int kMode>
 __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 {
+    // IQ1_M: 56-byte blocks, 8 local scales per two groups (16 choice
+    // groups), a shift per group.  IQ1_S: 50 bytes, 16 (k, shift) choices per
+    // sub-block of four groups.
+    constexpr bool kM = kFmt == IQ_FMT_IQ1_M;
+    constexpr int kBB = kM ? kBlockBytesM : kBlockBytes;
+    constexpr int kChoices = kM ? 8 : 16;
+    constexpr int kGroups = kM ? 16 : 8;          // choice groups per block
     // Payloads staged in LDS: one per block, or one per block and choice.
-    constexpr int kPayloads = kMode == kModeEvery ? 16 : 1;
+    constexpr int kPayloads = kMode == kModeEvery ? kChoices : 1;
     // Entry e sits at e + e/kChunk: one spare slot per 128-entry chunk, so the
     // lanes of a rescan that read different chunks (512 words apart without
     // the slot, a multiple of the 64 banks) spread over the banks.
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     __shared__ uint4 sp[kSlots];         // (q[0..7] + 1/8)^2 as bf16
     __shared__ uint4 sm[kSlots];         // (q[0..7] - 1/8)^2 as bf16
     __shared__ uint4 sq[kSlots];         // q[0..7] as bf16
-    __shared__ uint16_t sout16[kPayloads * kBlocksPerWG * kBlockBytes / 2];
+    __shared__ uint16_t sout16[kPayloads * kBlocksPerWG * kBB / 2];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
 
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 
     if (tid == 0) sgrid_bad = 0;
     if (kMode != kModeCandidates)
-        for (int i = tid; i < kPayloads * kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
+        for (int i = tid; i < kPayloads * kBlocksPerWG * kBB / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     // Stage the grid as bf16 (exact for ternary values); entries past the end
     // repeat the last one, which always comes first in index order.
@@ -239,9 +247,11 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         const float* xblk = a.w + blk * kBlockElems;
         const float* wblk = a.imp ? a.imp + bt * a.g.cols + cb * kBlockElems : nullptr;
 
-        // Whole-block checks and amax (each lane reads 4 of the 256 values).
+        // Whole-block checks and amax (each lane reads 4 of the 256 values);
+        // IQ1_M also sums the squares: per lane ((x0^2 + x1^2) + x2^2) + x3^2,
+        // then pairwise across lanes at distances 1, 2, ..., 32.
         int err = 0;
-        float amax = 0.0f;
+        float amax = 0.0f, ssq = 0.0f;
         {
             const float4 xv = reinterpret_cast<const float4*>(xblk)[lane];
             const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -250,6 +260,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 if (!finite_f32(xs[t])) err = IQ_ERR_NONFINITE;
                 amax = fmaxf(amax, fabsf(xs[t]));
             }
+            if (kM) ssq = ((xs[0] * xs[0] + xs[1] * xs[1]) + xs[2] * xs[2]) + xs[3] * xs[3];
             if (wblk && !err) {
                 const float4 wv = reinterpret_cast<const float4*>(wblk)[lane];
                 const float ws[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -262,10 +273,27 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         const bool block_bad = __ballot(err != 0) != 0;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        if (kM) {
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) ssq = ssq + __shfl_xor(ssq, o);
+        }
 
         uint32_t dh;
         if (a.scales) {
             dh = (uint32_t)a.scales[blk];
+        } else if (kM) {
+            // anchor clamp(0.58 + 0.035 * amax / rms, 0.65, 0.95); d = 0 for an
+            // all-zero block
+            dh = 0u;
+            if (amax > 0.0f) {
+                const float rms = __builtin_sqrtf(ssq / 256.0f);
+                const float ratio = amax / rms;
+                const float tk = 0.035f * ratio;
+                const float an = fminf(fmaxf(0.58f + tk, 0.65f), 0.95f);
+                const float t = amax / 16.875f;
+                const float u = t * an;
+                dh = f32_to_f16_bits(u);
+            }
         } else {
             const float t = amax / 16.875f;
             const float u = t * 0.61f;
@@ -276,15 +304,15 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         if (scale_bad && !block_bad && half == 0 && lane == 0) report(a.status, IQ_ERR_SCALE_RANGE);
         const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
 
-        // Forced choices: every wave of the block checks all 8 of them.
+        // Forced choices: every wave of the block checks all of them.
         int forced = -1;
         bool choice_bad = false;
-        if (kMode != kModeEvery && a.choices) {
-            const int cv = lane < 8 ? a.choices[blk * 8 + lane] : 0;
-            const bool bad = cv < 0 || cv > 15;
+        if ((kMode == kModePayload || kMode == kModeFake) && a.choices) {
+            const int cv = lane < kGroups ? a.choices[blk * kGroups + lane] : 0;
+            const bool bad = cv < 0 || cv >= kChoices;
             if (bad && half == 0) report(a.status, IQ_ERR_ARG);
             choice_bad = __ballot(bad) != 0;
-            forced = a.choices[blk * 8 + sub];
+            forced = a.choices[blk * kGroups + (kM ? (g >> 1) : sub)];
         }
         const bool zero_block = grid_bad || block_bad || scale_bad || dh == 0u || choice_bad;
         if (choice_bad) forced = -1;
@@ -355,48 +383,66 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             }
         }
 
-        // Sub-block choice: per group, the least minimum of its four lanes; per
-        // sub-block, s_k times the sum over its four groups (identical float sum
-        // in every lane of the sub-block).
-        int cstar = 0;
+        // Choice costs.  IQ1_S: per sub-block and choice c = k + 8*shift,
+        // (2k+1) times the sum of its four groups' least keys (identical float
+        // sums in every lane of the sub-block).  IQ1_M: per group and local
+        // scale k, the lesser of its two shifts' least keys (the lower shift
+        // on equal keys); per scale group, (2k+1) times the sum over its two
+        // groups.  A group's least key is the least over its four lanes.
+        int cstar = 0;               // IQ1_S: the sub-block's choice; IQ1_M: the local scale
         float cbest = 0.0f;
         float cost[16];
+        uint32_t shbits = 0u;        // IQ1_M: bit k = this group's shift under local scale k
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
             float m = best[c];
             m = fminf(m, __shfl_xor(m, 16));
             m = fminf(m, __shfl_xor(m, 32));
-            float v = m + __shfl_xor(m, 1);
-            v += __shfl_xor(v, 2);
-            cost[c] = (float)(2 * (c & 7) + 1) * v;
-            if (c == 0 || cost[c] < cbest) { cbest = cost[c]; cstar = c; }
+            if (kM) {
+                cost[c] = m;
+            } else {
+                float v = m + __shfl_xor(m, 1);
+                v += __shfl_xor(v, 2);
+                cost[c] = (float)(2 * (c & 7) + 1) * v;
+                if (c == 0 || cost[c] < cbest) { cbest = cost[c]; cstar = c; }
+            }
+        }
+        if (kM) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const bool sh = cost[8 + k] < cost[k];
+                shbits |= (uint32_t)sh << k;
+                const float v = sh ? cost[8 + k] : cost[k];
+                cost[k] = (float)(2 * k + 1) * (v + __shfl_xor(v, 1));
+                if (k == 0 || cost[k] < cbest) { cbest = cost[k]; cstar = k; }
+            }
         }
         if (forced >= 0) cstar = forced;
-        // Candidates: the top_c choices by (cost, c); with a zero scale every
-        // choice decodes to zero with entry 0, so the order is c = 0, 1, ...
+        // Candidates: the top_c choices by (cost, choice); with a zero scale
+        // every choice decodes to zero with entry 0, so the order is 0, 1, ...
         const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
         const bool zero_scale = !rejected && dh == 0u;
         int used = 0;
 
-        // Entry of choice cs for this lane's group: the lane rescans its
-        // entries of the chunk that holds its minimum of that choice, then the
-        // lane of the column whose matrix-core minimum is least is kept; the
-        // payload takes the low byte per group, the qh word per sub-block and
-        // d per block.
-        const int nloop = kMode == kModeEvery ? 16 : (kMode == kModeCandidates ? a.top_c : 1);
+        // For each choice to emit: this group's (k, shift) choice cs, its
+        // entry (the lane rescans its entries of the chunk that holds its
+        // minimum of cs, then the lane of the column whose matrix-core minimum
+        // is least is kept), and the payload, decoded values or candidate.
+        const int nloop = kMode == kModeEvery ? kChoices : (kMode == kModeCandidates ? a.top_c : 1);
         for (int it = 0; it < nloop; ++it) {
-            int cs = kMode == kModeEvery ? it : cstar;
+            int ch = kMode == kModeEvery ? it : cstar;
             if (kMode == kModeCandidates) {
                 int cr = -1;
                 float vr = 0.0f;
 #pragma unroll
-                for (int c = 0; c < 16; ++c) {
+                for (int c = 0; c < kChoices; ++c) {
                     const bool better = zero_scale ? (cr < 0) : (cr < 0 || cost[c] < vr);
                     if (!((used >> c) & 1) && better) { cr = c; vr = cost[c]; }
                 }
                 used |= 1 << cr;
-                cs = cr;
+                ch = cr;
             }
+            const int cs = kM ? ch + 8 * (int)((shbits >> ch) & 1u) : ch;
             float lane_min = best[0];
 #pragma unroll
             for (int c = 1; c < 16; ++c)
@@ -412,11 +458,13 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             idx = idx < n ? idx : n - 1;
             if (kMode == kModeCandidates) {
                 // One lane per group writes its 8 errors xhat - x (xhat exact
-                // in fp32, one rounding), its entry and, once per sub-block,
+                // in fp32, one rounding), its code and, once per choice group,
                 // the choice.
                 if (zero_scale) idx = 0;
                 if (kb == 0) {
-                    const int64_t base = (blk * 8 + sub) * a.top_c + it;     // [block][sub][r]
+                    const int unit = kM ? (g >> 1) : sub;
+                    const int part = kM ? (g & 1) : lq;
+                    const int64_t base = (blk * kGroups + unit) * a.top_c + it;    // [block][unit][r]
                     float xo[8], wo[8];
                     load_group(xblk, wblk, g, rejected, xo, wo);
                     const float sk = f16_bits_to_f32(dh) * (float)(2 * (cs & 7) + 1);
@@ -429,28 +477,54 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                         const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
                         ev[j] = rejected ? 0.0f : sk * (q + delta) - xo[j];
                     }
-                    float4* ep = reinterpret_cast<float4*>(a.cand_err + base * 32 + lq * 8);
+                    float4* ep = reinterpret_cast<float4*>(a.cand_err + base * (256 / kGroups) + part * 8);
                     ep[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
                     ep[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
-                    if (lq == 0) a.cand_choice[base] = cs;
-                    if (a.cand_codes) a.cand_codes[base * 4 + lq] = rejected ? (uint16_t)0 : (uint16_t)idx;
+                    if (part == 0) a.cand_choice[base] = ch;
+                    if (a.cand_codes) {
+                        const int shc = (kM && !zero_scale) ? (cs >> 3) : 0;
+                        const uint16_t code = kM ? (uint16_t)(idx | (shc << 11)) : (uint16_t)idx;
+                        a.cand_codes[base * (kM ? 2 : 4) + part] = rejected ? (uint16_t)0 : code;
+                    }
                 }
                 continue;
             }
-            int hi = ((idx >> 8) & 7) << (3 * lq);
-            hi |= __shfl_xor(hi, 1);
-            hi |= __shfl_xor(hi, 2);
-            if (!zero_block && kb == 0) {
-                uint8_t* ob = sout + (it * kBlocksPerWG + slot) * kBlockBytes;
-                ob[2 + 4 * sub + lq] = (uint8_t)(idx & 0xff);
-                if (lq == 0) {
-                    const uint32_t qh = (uint32_t)hi | ((uint32_t)cs << 12);
-                    ob[34 + 2 * sub] = (uint8_t)(qh & 0xff);
-                    ob[35 + 2 * sub] = (uint8_t)(qh >> 8);
+            uint8_t* ob = sout + (it * kBlocksPerWG + slot) * kBB;
+            if (kM) {
+                // IQ1_M: low byte per group; one nibble per group (3 high
+                // bits, shift bit); four scale words with the 3-bit local
+                // scales of four scale groups and one nibble of d each.
+                const int nib = ((idx >> 8) & 7) | ((cs >> 3) << 3);
+                const int nib_odd = __shfl_xor(nib, 1);
+                int kk = (cs & 7) << (3 * ((g >> 1) & 3));
+                kk |= __shfl_xor(kk, 2);
+                kk |= __shfl_xor(kk, 4);
+                if (!zero_block && kb == 0) {
+                    ob[g] = (uint8_t)(idx & 0xff);
+                    if ((g & 1) == 0) ob[32 + (g >> 1)] = (uint8_t)(nib | (nib_odd << 4));
+                    if ((g & 7) == 0) {
+                        const int wd = g >> 3;
+                        const uint32_t v = (uint32_t)kk | (((dh >> (4 * wd)) & 0xfu) << 12);
+                        ob[48 + 2 * wd] = (uint8_t)(v & 0xff);
+                        ob[49 + 2 * wd] = (uint8_t)(v >> 8);
+                    }
                 }
-                if (g == 0) {
-                    ob[0] = (uint8_t)(dh & 0xff);
-                    ob[1] = (uint8_t)(dh >> 8);
+            } else {
+                // IQ1_S: low byte per group, qh word per sub-block, d per block.
+                int hi = ((idx >> 8) & 7) << (3 * lq);
+                hi |= __shfl_xor(hi, 1);
+                hi |= __shfl_xor(hi, 2);
+                if (!zero_block && kb == 0) {
+                    ob[2 + 4 * sub + lq] = (uint8_t)(idx & 0xff);
+                    if (lq == 0) {
+                        const uint32_t qh = (uint32_t)hi | ((uint32_t)cs << 12);
+                        ob[34 + 2 * sub] = (uint8_t)(qh & 0xff);
+                        ob[35 + 2 * sub] = (uint8_t)(qh >> 8);
+                    }
+                    if (g == 0) {
+                        ob[0] = (uint8_t)(dh & 0xff);
+                        ob[1] = (uint8_t)(dh >> 8);
+                    }
                 }
             }
             if (kMode == kModeFake && kb == 0) {
@@ -464,7 +538,6 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 const float delta = (cz >> 3) ? -0.125f : 0.125f;
                 const uint4 u = sq[ez + ez / kChunk];
                 const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-                const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
                 float v[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
@@ -483,46 +556,52 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         const int64_t left = a.g.nblocks - first;
         const int nb = left < kBlocksPerWG ? (int)left : kBlocksPerWG;
         for (int cs = 0; cs < kPayloads; ++cs) {
-            uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (cs * a.g.nblocks + first) * kBlockBytes);
-            const uint16_t* s16 = sout16 + cs * kBlocksPerWG * (kBlockBytes / 2);
-            for (int i = tid; i < nb * (kBlockBytes / 2); i += kThreads) o16[i] = s16[i];
+            uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (cs * a.g.nblocks + first) * kBB);
+            const uint16_t* s16 = sout16 + cs * kBlocksPerWG * (kBB / 2);
+            for (int i = tid; i < nb * (kBB / 2); i += kThreads) o16[i] = s16[i];
         }
     }
 }
 
-}  // namespace
-
-hipError_t launch_iq1s_encode(const float* w, const float* imp, const float* grid, int grid_size,
-                              const uint16_t* scales, const int32_t* choices, uint8_t* out,
-                              float* xhat, int mode, int32_t* status, const BlockGeom& g,
-                              hipStream_t stream)
+template <int kFmt>
+hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
 {
-    Iq1sArgs a{w, imp, grid, scales, choices, out, xhat, nullptr, nullptr, nullptr, status, g,
-               grid_size, 0};
-    const int64_t wgs = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
+    const dim3 grid((unsigned)((a.g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG));
     if (mode == kModeEvery)
-        hipLaunchKernelGGL(iq1s_encode_kernel<kModeEvery>, dim3((unsigned)wgs), dim3(kThreads), 0,
-                           stream, a);
+        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeEvery>), grid, dim3(kThreads), 0, stream, a);
     else if (mode == kModeFake)
-        hipLaunchKernelGGL(iq1s_encode_kernel<kModeFake>, dim3((unsigned)wgs), dim3(kThreads), 0,
+        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeFake>), grid, dim3(kThreads), 0, stream, a);
+    else if (mode == kModeCandidates)
+        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeCandidates>), grid, dim3(kThreads), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL(iq1s_encode_kernel<kModePayload>, dim3((unsigned)wgs), dim3(kThreads), 0,
-                           stream, a);
+        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModePayload>), grid, dim3(kThreads), 0, stream,
+                           a);
     return hipGetLastError();
 }
 
-hipError_t launch_iq1s_candidates(const float* w, const float* imp, const float* grid,
-                                  int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
-                                  uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
-                                  hipStream_t stream)
+}  // namespace
+
+hipError_t launch_iq1_encode(int fmt, const float* w, const float* imp, const float* grid,
+                             int grid_size, const uint16_t* scales, const int32_t* choices,
+                             uint8_t* out, float* xhat, int mode, int32_t* status,
+                             const BlockGeom& g, hipStream_t stream)
+{
+    Iq1sArgs a{w, imp, grid, scales, choices, out, xhat, nullptr, nullptr, nullptr, status, g,
+               grid_size, 0};
+    return fmt == IQ_FMT_IQ1_M ? launch_fmt<IQ_FMT_IQ1_M>(a, mode, stream)
+                               : launch_fmt<IQ_FMT_IQ1_S>(a, mode, stream);
+}
+
+hipError_t launch_iq1_candidates(int fmt, const float* w, const float* imp, const float* grid,
+                                 int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
+                                 uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
+                                 hipStream_t stream)
 {
     Iq1sArgs a{w, imp, grid, nullptr, nullptr, nullptr, nullptr, cand_err, cand_choice, cand_codes,
                status, g, grid_size, top_c};
-    const int64_t wgs = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
-    hipLaunchKernelGGL(iq1s_encode_kernel<kModeCandidates>, dim3((unsigned)wgs), dim3(kThreads), 0,
-                       stream, a);
-    return hipGetLastError();
+    return fmt == IQ_FMT_IQ1_M ? launch_fmt<IQ_FMT_IQ1_M>(a, kModeCandidates, stream)
+                               : launch_fmt<IQ_FMT_IQ1_S>(a, kModeCandidates, stream);
 }
 
 }  // namespace iqk

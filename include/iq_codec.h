@@ -46,7 +46,9 @@ extern "C" {
 
 typedef enum {
     IQ_FMT_IQ1_S = 0,   /* 2048-entry ternary grid, 50-byte blocks (1.5625 bpw) */
-    IQ_FMT_IQ2_XS = 1   /* 512-entry magnitude grid, 74-byte blocks (2.3125 bpw) */
+    IQ_FMT_IQ2_XS = 1,  /* 512-entry magnitude grid, 74-byte blocks (2.3125 bpw) */
+    IQ_FMT_IQ1_M = 2    /* the IQ1_S grid, 56-byte blocks (1.75 bpw): a 3-bit local scale per
+                           16 values, a shift per group, d in the top nibbles of the scale words */
 } iq_format_t;
 
 typedef enum {
@@ -70,15 +72,17 @@ typedef struct {
     int32_t block_elems;    /* 256 values per super-block */
     int32_t block_bytes;    /* 50 (IQ1_S) or 74 (IQ2_XS) */
     int32_t group;          /* 8 values per grid entry */
-    int32_t index_bits;     /* 11 (IQ1_S) or 9 (IQ2_XS) */
+    int32_t index_bits;     /* 11 (IQ1_S, IQ1_M) or 9 (IQ2_XS) */
     int32_t grid_max;       /* 2048 or 512 entries at most */
     int32_t choice_groups;  /* choice groups per block: 8 sub-blocks of 32 (IQ1_S),
-                               16 scale groups of 16 (IQ2_XS) */
-    int32_t num_choices;    /* 16: IQ1_S k + 8*deltabit, IQ2_XS local scale k */
+                               16 scale groups of 16 (IQ2_XS, IQ1_M) */
+    int32_t num_choices;    /* 16: IQ1_S k + 8*deltabit, IQ2_XS local scale k;
+                               8: IQ1_M local scale k (the shift is free per group) */
 } iq_format_info_t;
 
-/* Geometry of a format (#2450 review: 50/74-byte blocks; #3157: choice_groups
- * and num_choices recorded per format).  `out` is a HOST pointer. */
+/* Geometry of a format (#2450 review: 50/74-byte blocks; #2525 IQ1_M bodies:
+ * 1.75 bpw; #3157: choice_groups and num_choices recorded per format).  `out`
+ * is a HOST pointer. */
 iq_status_t iq_format_info(iq_format_t fmt, iq_format_info_t* out);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -97,13 +101,18 @@ const char* iq_status_str(iq_status_t st);
  *   grid       [grid_size][8] fp32.  IQ1_S: values in {-1, 0, +1};
  *              IQ2_XS: finite magnitudes >= 0.
  *   scales     NULL (predict d = fp16((amax/16.875)*0.61) for IQ1_S,
- *              fp16((amax/155)*0.61) for IQ2_XS) or pinned fp16 bits
+ *              fp16((amax/155)*0.61) for IQ2_XS, and for IQ1_M
+ *              fp16((amax/16.875)*clamp(0.58 + 0.035*amax/rms, 0.65, 0.95))
+ *              with rms over the block's 256 values, #2525 IQ1_M body "A
+ *              scale-anchor correction") or pinned fp16 bits
  *              [batch][rows][cols/256] (#3197 static scales).
  *   choices    NULL (search every choice) or forced per-choice-group picks
- *              [batch][rows][cols/256][choice_groups] int32 in [0, 16) (#3157):
- *              IQ1_S c = k + 8*deltabit, IQ2_XS c = k.  Only the grid entries
- *              are searched then; a value outside [0, 16) zeroes its block and
- *              sets *status = IQ_ERR_ARG.
+ *              [batch][rows][cols/256][choice_groups] int32 in [0, num_choices)
+ *              (#3157): IQ1_S c = k + 8*deltabit, IQ2_XS and IQ1_M c = k (IQ1_M
+ *              keeps each group's shift free).  Only the rest is searched then;
+ *              a value out of range zeroes its block and sets
+ *              *status = IQ_ERR_ARG.
+ * IQ1_M ties: the lower shift, then the lower entry (#2525 IQ1_M CUDA body).
  *   out        [batch][rows][cols/256][block_bytes] uint8.
  *   status     one int32 (see the conventions above); required.
  * Errors: IQ_ERR_NULL, IQ_ERR_FORMAT, IQ_ERR_SHAPE, IQ_ERR_GRID, IQ_ERR_DEVICE,
@@ -121,7 +130,8 @@ iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t ro
  * of the local-Hessian search, which scores each choice's decoded error.
  *
  *   w, importance, grid, scales, status: as iq_encode.
- *   out  [16][batch][rows][cols/256][block_bytes] uint8 (choice-major).
+ *   out  [num_choices][batch][rows][cols/256][block_bytes] uint8 (choice-major;
+ *        16 payloads for IQ1_S and IQ2_XS, 8 for IQ1_M).
  * Errors as iq_encode; a block with a data error is zero in all 16 payloads.
  */
 iq_status_t iq_encode_every_choice(iq_format_t fmt, const float* w, int64_t batch, int64_t rows,
@@ -152,7 +162,10 @@ iq_status_t iq_fake_quant(iq_format_t fmt, const float* w, int64_t batch, int64_
  * iq_dequant -- decode a payload to fp32 (#2450 review worked example:
  * IQ1_S value = d*(2k+1)*(q + delta), delta = -1/8 when bit 15 is set;
  * IQ2_XS value = d*(2k+1)*sign*q with the 8th sign of a group implied by even
- * parity).  Every decoded value is exact in fp32.
+ * parity; IQ1_M value = d*(2k+1)*(q + delta) with d reassembled from the scale
+ * words' top nibbles, k per 16 values and delta per group).  Every decoded
+ * value is exact in fp32 (IQ2_XS: for grid magnitudes of at most 8
+ * significant bits).
  *
  *   packed  [batch][rows][cols/256][block_bytes] uint8.
  *   grid    [grid_size][8] fp32 (the grid the payload was encoded with).
@@ -167,18 +180,20 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
 /*
  * iq_encode_candidates -- the encode's sweep with a candidate epilogue, the
  * input of the local-Hessian choice search (#3158 step 1, #3159 every-choice
- * encode): for every choice group of every 256-column block (IQ2_XS: 16 scale
- * groups of 16 columns, choice = local scale k; IQ1_S: 8 sub-blocks of 32
- * columns, choice c = k + 8*deltabit), the top_c choices ordered by
+ * encode): for every choice group of every 256-column block (IQ2_XS and
+ * IQ1_M: 16 scale groups of 16 columns, choice = local scale k; IQ1_S: 8
+ * sub-blocks of 32 columns, choice c = k + 8*deltabit), the top_c choices ordered by
  * (weighted cost, choice), each with its grid codes and its error vector
  * xhat - x over the group's columns (xhat exact in fp32, one rounding).  A
  * zero super-block scale orders the choices 0, 1, ... with entry 0.
  *
  *   w           [rows][cols] fp32; importance NULL or [cols]; grid as iq_encode.
- *   top_c       1..16.
- *   cand_err    IQ2_XS [rows][cols/256][16][top_c][16], IQ1_S [rows][cols/256][8][top_c][32] fp32.
+ *   top_c       1..num_choices (16, or 8 for IQ1_M).
+ *   cand_err    IQ2_XS, IQ1_M [rows][cols/256][16][top_c][16],
+ *               IQ1_S [rows][cols/256][8][top_c][32] fp32.
  *   cand_choice [rows][cols/256][G][top_c] int32 (G = 16 or 8).
  *   cand_codes  NULL, or IQ2_XS [..][top_c][2] uint16 (index | mask<<9 per group),
+ *               IQ1_M [..][top_c][2] (index | shift<<11 per group),
  *               IQ1_S [..][top_c][4] uint16 (the grid index of each group).
  *   status      one int32, required; a block with a data error is all zeros.
  */

@@ -1,7 +1,7 @@
 """Comparison of HIP payloads with the oracle's, under the tie rule.
 
 Codes must be bit-exact, except on floating-point ties: where a choice group
-(IQ1_S 32-value sub-block, IQ2_XS 16-value scale group) differs, the float64
+(IQ1_S 32-value sub-block, IQ2_XS and IQ1_M 16-value scale group) differs, the float64
 weighted error of the HIP pick must agree with the oracle's within 1e-6
 relative.  The scale bytes must always be bit-exact.
 """
@@ -13,9 +13,34 @@ import oracle
 TIE_RTOL = 1e-6
 
 
+def scale_bits(fmt, packed):
+    """fp16 bits of every block's d: bytes 0-1, or for IQ1_M the top nibbles of
+    its four scale words."""
+    p = np.ascontiguousarray(packed).reshape(-1, oracle.BLOCK_BYTES[fmt]).astype(np.int64)
+    if fmt == "iq1_m":
+        sc = p[:, 48:56:2] | (p[:, 49:56:2] << 8)
+        return ((sc[:, 0] >> 12) | ((sc[:, 1] >> 8) & 0x00F0) | ((sc[:, 2] >> 4) & 0x0F00)
+                | (sc[:, 3] & 0xF000))
+    return p[:, 0] | (p[:, 1] << 8)
+
+
+def grid_for(fmt, n=None, seed=0):
+    """The seeded grid of a format (IQ1_M uses the IQ1_S grid)."""
+    import workloads
+    if fmt == "iq2_xs":
+        return workloads.iq2xs_grid(min(n or 512, 512), seed=seed)
+    return workloads.iq1s_grid(min(n or 2048, 2048), seed=seed)
+
+
 def unit_codes(fmt, packed):
     """Per choice group, the bytes that encode it: [n, G, k] uint8."""
     p = np.ascontiguousarray(packed).reshape(-1, oracle.BLOCK_BYTES[fmt])
+    if fmt == "iq1_m":
+        qs = p[:, 0:32].reshape(-1, 16, 2)
+        nib = p[:, 32:48].reshape(-1, 16, 1)
+        sc = p[:, 48:56:2].astype(np.int64) | (p[:, 49:56:2].astype(np.int64) << 8)
+        k = np.stack([(sc >> (3 * t)) & 7 for t in range(4)], axis=2).reshape(-1, 16, 1)
+        return np.concatenate([qs, nib, k.astype(np.uint8)], axis=2)
     if fmt == "iq1_s":
         low = p[:, 2:34].reshape(-1, 8, 4)
         qh = p[:, 34:50].reshape(-1, 8, 2)
@@ -33,7 +58,8 @@ def compare_payloads(fmt, got, ref, x, grid, imp=None, max_tie_frac=0.005):
     got = np.ascontiguousarray(got).reshape(-1, nb)
     ref = np.ascontiguousarray(ref).reshape(-1, nb)
     assert got.shape == ref.shape
-    np.testing.assert_array_equal(got[:, :2], ref[:, :2], err_msg="scale bytes differ")
+    np.testing.assert_array_equal(scale_bits(fmt, got), scale_bits(fmt, ref),
+                                  err_msg="scale bits differ")
     diff = np.any(unit_codes(fmt, got) != unit_codes(fmt, ref), axis=2)     # [n, G]
     nd = int(diff.sum())
     if nd == 0:

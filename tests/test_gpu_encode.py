@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity import compare_payloads
+from tests.parity import compare_payloads, grid_for, scale_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -24,6 +24,7 @@ if not torch.cuda.is_available():  # the CPU suite deselects these with -m "not 
 import ggml_iq_codebook_amd as iq  # noqa: E402
 
 DEV = "cuda:0"
+FMTS = ["iq1_s", "iq2_xs", "iq1_m"]
 
 
 @pytest.fixture(autouse=True)
@@ -70,13 +71,11 @@ def test_c1_iq1s_small_matches_oracle(uniform):
     _check_full("iq1_s", c["w"], c["grid"], imp)
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape,n", [((2, 13, 768), None), ((1, 5, 256), 1000), ((1, 3, 512), 37),
                                      ((1, 2, 256), 1), ((3, 1, 1024), 33)])
 def test_ragged_shapes_and_grid_sizes(fmt, shape, n):
-    gmax = 2048 if fmt == "iq1_s" else 512
-    n = min(n or gmax, gmax)
-    grid = workloads.iq1s_grid(n, seed=3) if fmt == "iq1_s" else workloads.iq2xs_grid(n, seed=3)
+    grid = grid_for(fmt, n, seed=3)
     w = workloads.student_t_weight(shape, 17)
     imp = workloads.lognormal_importance((shape[0], shape[2]), 18)
     _check_full(fmt, w, grid, imp)
@@ -88,9 +87,9 @@ def test_c3_iq2xs_rows_match_oracle():
     _check_full("iq2_xs", w, c["grid"], c["importance"])
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_uniform_importance_reproduces_unweighted_payload(fmt):
-    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    grid = grid_for(fmt)
     w = workloads.normal_weight((1, 32, 512), 5)
     p0 = _gpu_encode(fmt, w, grid)
     for c in (1.0, 4.0, 0.125):
@@ -98,9 +97,9 @@ def test_uniform_importance_reproduces_unweighted_payload(fmt):
         np.testing.assert_array_equal(p, p0)
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_dequant_is_exact(fmt):
-    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    grid = grid_for(fmt)
     w = workloads.normal_weight((2, 7, 512), 6)
     p = oracle.encode(fmt, w, grid)
     out = iq.dequant(_dev(p), _dev(grid), fmt=fmt)
@@ -109,14 +108,14 @@ def test_dequant_is_exact(fmt):
     np.testing.assert_array_equal(out.cpu().numpy().astype(np.float64), want)
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_decode_reencode_round_trip_under_pinned_scales(fmt):
-    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    grid = grid_for(fmt)
     w = workloads.normal_weight((1, 16, 512), 7)
     imp = workloads.lognormal_importance((1, 512), 8)
     p = _gpu_encode(fmt, w, grid, imp)
     xhat = iq.dequant(_dev(p), _dev(grid), fmt=fmt)
-    d = torch.from_numpy(p[..., 0].astype(np.int16) | (p[..., 1].astype(np.int16) << 8)).to(DEV)
+    d = torch.from_numpy(scale_bits(fmt, p).astype(np.uint16).view(np.int16).reshape(1, 16, 2)).to(DEV)
     p2 = iq.encode(xhat, _dev(grid), _dev(imp), fmt=fmt, scales=d.contiguous())
     x2 = iq.dequant(p2, _dev(grid), fmt=fmt)
     torch.cuda.synchronize()
@@ -129,21 +128,21 @@ def test_decode_reencode_round_trip_under_pinned_scales(fmt):
                      _block_imp(imp, 1, 16, 512))
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_forced_choices_match_oracle(fmt):
-    grid = workloads.iq1s_grid(512) if fmt == "iq1_s" else workloads.iq2xs_grid(256)
+    grid = grid_for(fmt, 256 if fmt == "iq2_xs" else 512)
     w = workloads.normal_weight((1, 6, 512), 9)
     imp = workloads.lognormal_importance((1, 512), 10)
-    G = 8 if fmt == "iq1_s" else 16
-    ch = np.random.default_rng(11).integers(0, 16, (1, 6, 2, G)).astype(np.int32)
+    G = iq.CHOICE_GROUPS[fmt]
+    ch = np.random.default_rng(11).integers(0, iq.NUM_CHOICES[fmt], (1, 6, 2, G)).astype(np.int32)
     got = _gpu_encode(fmt, w, grid, imp, choices=_dev(ch))
     ref = oracle.encode(fmt, w, grid, imp, choices=ch)
     compare_payloads(fmt, got, ref, w.reshape(-1, 256), grid, _block_imp(imp, 1, 6, 512))
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_determinism_and_launch_partition_invariance(fmt):
-    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    grid = grid_for(fmt)
     w = workloads.normal_weight((1, 40, 1024), 12)
     imp = workloads.lognormal_importance((1, 1024), 13)
     a = _gpu_encode(fmt, w, grid, imp)
@@ -154,8 +153,8 @@ def test_determinism_and_launch_partition_invariance(fmt):
 
 
 def test_zero_and_underflow_blocks():
-    for fmt in ("iq1_s", "iq2_xs"):
-        grid = workloads.iq1s_grid(64) if fmt == "iq1_s" else workloads.iq2xs_grid(64)
+    for fmt in FMTS:
+        grid = grid_for(fmt, 64)
         w = workloads.normal_weight((1, 3, 256), 81)
         w[0, 0] = 0.0
         w[0, 1] *= 1e-7
@@ -171,9 +170,9 @@ def _status_of(fn):
     return int(st.item())
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_device_data_errors_are_reported(fmt):
-    grid = workloads.iq1s_grid(64) if fmt == "iq1_s" else workloads.iq2xs_grid(64)
+    grid = grid_for(fmt, 64)
     w = workloads.normal_weight((1, 4, 512), 91)
     bad = w.copy()
     bad[0, 2, 300] = np.nan
@@ -191,7 +190,7 @@ def test_device_data_errors_are_reported(fmt):
     st = _status_of(lambda s: iq.encode(_dev(w * 1e9), _dev(grid), fmt=fmt, status=s, check=False))
     assert st == 7                                   # IQ_ERR_SCALE_RANGE
     g2 = grid.copy()
-    g2[3, 4] = 2.0 if fmt == "iq1_s" else -1.0
+    g2[3, 4] = -1.0 if fmt == "iq2_xs" else 2.0
     st = _status_of(lambda s: iq.encode(_dev(w), _dev(g2), fmt=fmt, status=s, check=False))
     assert st == 4                                   # IQ_ERR_GRID
     with pytest.raises(iq.IQError) as ei:
@@ -237,8 +236,7 @@ def _sampled(fmt, cfg, nsamp, seed):
     got = _gpu_encode(fmt, w, grid, imp).reshape(-1, iq.BLOCK_BYTES[fmt])
     nblk = got.shape[0]
     # every scale is checked against the closed-form predictor
-    np.testing.assert_array_equal(got[:, 0].astype(np.uint16) | (got[:, 1].astype(np.uint16) << 8),
-                                  oracle.predict_scales(fmt, w))
+    np.testing.assert_array_equal(scale_bits(fmt, got), oracle.predict_scales(fmt, w))
     rng = np.random.default_rng(seed)
     idx = np.unique(np.concatenate([[0, nblk - 1], rng.integers(0, nblk, nsamp)]))
     x = w.reshape(-1, 256)[idx]
@@ -253,6 +251,12 @@ def test_c2_iq1s_4096_sampled():
 
 def test_c3_iq2xs_4096_sampled():
     _sampled("iq2_xs", workloads.c3_iq2xs_4096(), 768, 22)
+
+
+def test_iq1m_4096_sampled():
+    # IQ1_M on the IQ1_S workload's 4096x4096 weight: every block's d (peak-to-
+    # RMS anchor, fp32) bit-exact, sampled blocks against the oracle.
+    _sampled("iq1_m", dict(workloads.c2_iq1s_4096(), fmt="iq1_m"), 384, 24)
 
 
 def test_c4_moe_batch_equals_per_expert_calls_and_oracle():

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity import compare_payloads
+from tests.parity import compare_payloads, grid_for
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +26,8 @@ if not torch.cuda.is_available():  # the CPU suite deselects these with -m "not 
 import ggml_iq_codebook_amd as iq  # noqa: E402
 
 DEV = "cuda:0"
-G = {"iq1_s": 8, "iq2_xs": 16}
+G = {"iq1_s": 8, "iq2_xs": 16, "iq1_m": 16}
+FMTS = ["iq1_s", "iq2_xs", "iq1_m"]
 
 
 @pytest.fixture(autouse=True)
@@ -53,22 +54,21 @@ def _bits(t):
     return t.contiguous().view(torch.int32).cpu().numpy()
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape,n", [((2, 5, 512), None), ((1, 3, 768), 301)])
 def test_every_choice_equals_the_forced_encodes(fmt, shape, n):
-    gmax = 2048 if fmt == "iq1_s" else 512
-    n = n or gmax
-    grid = workloads.iq1s_grid(n, seed=5) if fmt == "iq1_s" else workloads.iq2xs_grid(n, seed=5)
+    grid = grid_for(fmt, n, seed=5)
     w = workloads.student_t_weight(shape, 201)
     w[0, 1, :256] = 0.0                              # a zero block
     imp = workloads.lognormal_importance((shape[0], shape[2]), 202)
     B, R, C = shape
     every = iq.encode_every_choice(_dev(w), _dev(grid), _dev(imp), fmt=fmt)
     torch.cuda.synchronize()
-    assert every.shape == (16, B, R, C // 256, iq.BLOCK_BYTES[fmt])
+    nc = iq.NUM_CHOICES[fmt]
+    assert every.shape == (nc, B, R, C // 256, iq.BLOCK_BYTES[fmt])
     ev = every.cpu().numpy()
     ref = oracle.encode_every_choice(fmt, w, grid, imp)
-    for c in range(16):
+    for c in range(nc):
         full = torch.full((B, R, C // 256, G[fmt]), c, dtype=torch.int32, device=DEV)
         forced = iq.encode(_dev(w), _dev(grid), _dev(imp), fmt=fmt, choices=full)
         torch.cuda.synchronize()
@@ -76,22 +76,22 @@ def test_every_choice_equals_the_forced_encodes(fmt, shape, n):
         compare_payloads(fmt, ev[c], ref[c], w.reshape(-1, 256), grid, _block_imp(imp, B, R, C))
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_every_choice_under_pinned_scales_and_without_importance(fmt):
-    grid = workloads.iq1s_grid() if fmt == "iq1_s" else workloads.iq2xs_grid()
+    grid = grid_for(fmt)
     w = workloads.normal_weight((1, 4, 512), 203)
     d = oracle.predict_scales(fmt, w * np.float32(0.75)).reshape(1, 4, 2)
     sc = torch.from_numpy(d.view(np.int16)).to(DEV)
     every = iq.encode_every_choice(_dev(w), _dev(grid), fmt=fmt, scales=sc)
     torch.cuda.synchronize()
     ref = oracle.encode_every_choice(fmt, w, grid, None, scales=d)
-    for c in range(16):
+    for c in range(iq.NUM_CHOICES[fmt]):
         compare_payloads(fmt, every[c].cpu().numpy(), ref[c], w.reshape(-1, 256), grid)
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_every_choice_zeroes_rejected_blocks_in_every_payload(fmt):
-    grid = workloads.iq1s_grid(64) if fmt == "iq1_s" else workloads.iq2xs_grid(64)
+    grid = grid_for(fmt, 64)
     w = workloads.normal_weight((1, 3, 512), 204)
     w[0, 1, 260] = np.inf
     st = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -104,7 +104,8 @@ def test_every_choice_zeroes_rejected_blocks_in_every_payload(fmt):
     ok[0, 1, 256:] = 0.0
     ref = oracle.encode_every_choice(fmt, ok, grid)
     keep = [0, 1, 2, 4, 5]                           # blocks other than the rejected one
-    np.testing.assert_array_equal(ev.reshape(16, 6, -1)[:, keep], ref.reshape(16, 6, -1)[:, keep])
+    nc = iq.NUM_CHOICES[fmt]
+    np.testing.assert_array_equal(ev.reshape(nc, 6, -1)[:, keep], ref.reshape(nc, 6, -1)[:, keep])
 
 
 def test_every_choice_c2_sampled():
@@ -126,10 +127,10 @@ def test_every_choice_c2_sampled():
         compare_payloads("iq1_s", ev[c, idx], ref, x, grid, ib)
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("mode", ["free", "pinned", "forced", "uniform"])
 def test_fake_quant_is_bitwise_the_decoded_payload(fmt, mode):
-    grid = workloads.iq1s_grid(1200) if fmt == "iq1_s" else workloads.iq2xs_grid(300)
+    grid = grid_for(fmt, 300 if fmt == "iq2_xs" else 1200)
     w = workloads.normal_weight((2, 6, 512), 211)
     w[1, 3, 256:] = 0.0                              # a zero block (decodes to signed zeros)
     imp = None if mode == "uniform" else workloads.lognormal_importance((2, 512), 212)
@@ -138,8 +139,8 @@ def test_fake_quant_is_bitwise_the_decoded_payload(fmt, mode):
         kw["scales"] = torch.from_numpy(oracle.predict_scales(fmt, w * np.float32(1.3))
                                         .reshape(2, 6, 2).view(np.int16)).to(DEV)
     if mode == "forced":
-        kw["choices"] = _dev(np.random.default_rng(213).integers(0, 16, (2, 6, 2, G[fmt]))
-                             .astype(np.int32))
+        kw["choices"] = _dev(np.random.default_rng(213).integers(0, iq.NUM_CHOICES[fmt],
+                                                                 (2, 6, 2, G[fmt])).astype(np.int32))
     wi = None if imp is None else _dev(imp)
     xh, pk = iq.fake_quant(_dev(w), _dev(grid), wi, fmt=fmt, packed=True, **kw)
     p = iq.encode(_dev(w), _dev(grid), wi, fmt=fmt, **kw)
@@ -157,9 +158,9 @@ def test_fake_quant_is_bitwise_the_decoded_payload(fmt, mode):
                      None if imp is None else _block_imp(imp, 2, 6, 512))
 
 
-@pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_fake_quant_writes_zeros_for_rejected_blocks(fmt):
-    grid = workloads.iq1s_grid(128) if fmt == "iq1_s" else workloads.iq2xs_grid(128)
+    grid = grid_for(fmt, 128)
     w = workloads.normal_weight((1, 2, 512), 214)
     w[0, 1, 3] = np.nan
     out = torch.full((1, 2, 512), 5.0, dtype=torch.float32, device=DEV)

@@ -41,8 +41,8 @@ def _dev(a):
 
 def _check_candidates(w, grid, imp, top_c, fmt="iq2_xs"):
     """w [rows, 256]."""
-    G = 16 if fmt == "iq2_xs" else 8
-    L, nc = 256 // G, (2 if fmt == "iq2_xs" else 4)
+    G = iq.CHOICE_GROUPS[fmt]
+    L, nc = 256 // G, (4 if fmt == "iq1_s" else 2)
     err, ch, codes = iq.encode_candidates(_dev(w), _dev(grid), None if imp is None else _dev(imp),
                                           fmt=fmt, top_c=top_c, codes=True)
     torch.cuda.synchronize()
@@ -237,3 +237,23 @@ def test_c5_weight_batched_search_sampled():
     for b in (0, 7, 15):
         _check_candidates(np.ascontiguousarray(w[rows[:8], 256 * b:256 * (b + 1)]), grid,
                           np.ascontiguousarray(imp[256 * b:256 * (b + 1)]), 8)
+
+
+def test_iq1m_candidates_and_search():
+    # IQ1_M: 16 scale groups of 16 columns, 8 local scales (the shift is free
+    # per group); candidates against the oracle, then the G = 16 search.
+    H = workloads.block_hessian(256, 12)
+    grid = workloads.iq1s_grid()
+    w = workloads.normal_weight((1, 80, 256), 39)[0]
+    w[3] = 0.0
+    imp = np.sqrt(np.diag(H).astype(np.float64)).astype(np.float32)
+    err, ch = _check_candidates(w, grid, imp, 8, fmt="iq1_m")
+    assert np.all(ch[3] == np.arange(8))
+    _check_candidates(w[:7], workloads.iq1s_grid(999), None, 3, fmt="iq1_m")
+    cand = np.ascontiguousarray(err.reshape(80, 16, 8, 16))
+    trace, rtrace, nd = _search_parity(H, cand)
+    J = [oracle.choice_objective(H, cand, trace[s]) for s in range(3)]
+    assert np.all(J[1] <= J[0] * (1 + 1e-6)) and np.all(J[2] <= J[1] * (1 + 1e-6))
+    with pytest.raises(iq.IQError) as ei:
+        iq.encode_candidates(_dev(w), _dev(grid), fmt="iq1_m", top_c=9)
+    assert ei.value.code == 8
