@@ -37,9 +37,11 @@ sys.path.insert(0, ROOT)
 #   IQ1_S weighted: 3 weighted dot products of 8 (48) + the delta terms of
 #   U(+-1/8), V(+-1/8) (10) + 16 choice keys, one FMA each (32) = 90;
 #   IQ1_S unweighted: the entry norms do not depend on the group (16 + 10 + 32) = 58;
-#   IQ2_XS weighted: 2 dot products (32) + 1 + 16 keys (32) = 65.
+#   IQ2_XS weighted: 2 dot products (32) + 1 + 16 keys (32) = 65;
+#   IQ1_M: the IQ1_S search (16 (k, shift) keys per group and entry): 90 / 58.
 FLOPS_PER_GROUP_ENTRY = {("iq1_s", True): 90, ("iq1_s", False): 58,
-                         ("iq2_xs", True): 65, ("iq2_xs", False): 65}
+                         ("iq2_xs", True): 65, ("iq2_xs", False): 65,
+                         ("iq1_m", True): 90, ("iq1_m", False): 58}
 
 PEAK_FP32_VECTOR_TFLOPS = 157.3     # MI355X: 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
 PEAK_HBM_GBPS = 8000.0
@@ -67,15 +69,20 @@ WORKLOADS = {
                                 "4096x4096 fp32 weight"),
     "c2_pinned": ("c2_iq1s_4096", "IQ1_S weighted re-encode of a 4096x4096 fp32 weight under "
                                   "pinned super-block scales"),
+    "c2_iq1m": ("c2_iq1m_4096", "IQ1_M weighted encode of a 4096x4096 fp32 weight, N(0,0.02), "
+                                "per-column sqrt-lognormal importance, seeded 2048x8 ternary grid"),
 }
 
 KERNEL_SOURCES = {
     "iq1_s": ["ggml_iq_codebook_amd/csrc/iq1s_encode.hip",
               "ggml_iq_codebook_amd/csrc/device_common.hpp"],
+    "iq1_m": ["ggml_iq_codebook_amd/csrc/iq1s_encode.hip",
+              "ggml_iq_codebook_amd/csrc/device_common.hpp"],
     "iq2_xs": ["ggml_iq_codebook_amd/csrc/iq2xs_encode.hip",
                "ggml_iq_codebook_amd/csrc/device_common.hpp"],
 }
-KERNEL_NAMES = {"iq1_s": "iq1s_encode_kernel<0>", "iq2_xs": "iq2xs_kernel<0>"}
+KERNEL_NAMES = {"iq1_s": "iq1s_encode_kernel<0, 0>", "iq2_xs": "iq2xs_kernel<0>",
+                "iq1_m": "iq1s_encode_kernel<2, 0>"}
 
 
 def log(*a):

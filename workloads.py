@@ -135,6 +135,12 @@ def c5_weight_choice_search():
             "top_c": 8, "sweeps": 2}
 
 
+def c2_iq1m_4096():
+    """IQ1_M weighted encode of the IQ1_S workload's 4096x4096 weight (seed 1),
+    importance seed 2, the IQ1_S grid (IQ1_M shares it)."""
+    return dict(c2_iq1s_4096(), fmt="iq1_m")
+
+
 CONFIGS = {
     "c1": c1_iq1s_small,
     "c2": c2_iq1s_4096,
@@ -143,4 +149,5 @@ CONFIGS = {
     "c5": c5_choice_search,
     "c5_iq1s": c5_iq1s_choice_search,
     "c5_weight": c5_weight_choice_search,
+    "c2_iq1m": c2_iq1m_4096,
 }
