@@ -127,13 +127,16 @@ __device__ __forceinline__ void load_group(const float* xblk, const float* wblk,
     }
 }
 
-// VALU rescan for choice cs = k + 8*deltabit: the lowest of this lane's
-// entries of chunk tchunk with the least key (2k+1)*U - 2V/d, recomputed in
-// fp32 from the group's values and weights (read again from memory rather
-// than held through the sweep).
-__device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, int kb, int cs,
-                                      const float* xblk, const float* wblk, int g, bool zero_block,
-                                      float w64, float b4, float inv_d)
+// VALU rescan for choice cs = k + 8*deltabit over tiles t0 .. t0+nt-1 of chunk
+// tchunk, rows 4*kbs .. 4*kbs+3 of each tile (the entries one lane of a
+// column covers): the lowest entry with the least key (2k+1)*U - 2V/d,
+// recomputed in fp32 from the group's values and weights (read again from
+// memory rather than held through the sweep).  Returns the entry, writes its
+// key.
+__device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, int kbs, int t0,
+                                      int nt, int cs, const float* xblk, const float* wblk, int g,
+                                      bool zero_block, float w64, float b4, float inv_d,
+                                      float* key_out)
 {
     float x[8], w[8];
     __asm__ volatile("" ::: "memory");
@@ -143,10 +146,10 @@ __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, 
     const float bd = (cs >> 3) ? b4 : -b4;
     int idx = -1;
     float vbest = 0.0f;
-    for (int tt = 0; tt < kChunkTiles; ++tt) {
+    for (int tt = t0; tt < t0 + nt; ++tt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int e = (tchunk * kChunkTiles + tt) * kTile + 4 * kb + r;
+            const int e = (tchunk * kChunkTiles + tt) * kTile + 4 * kbs + r;
             const uint4 u = sq[e + tchunk];
             const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
             float A = 0.0f, M = 0.0f, N = 0.0f;
@@ -162,6 +165,7 @@ __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, 
             if (idx < 0 || key < vbest) { vbest = key; idx = e; }
         }
     }
+    *key_out = vbest;
     return idx;
 }
 
@@ -448,12 +452,38 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             for (int c = 1; c < 16; ++c)
                 if (cs == c) lane_min = best[c];
             const int tchunk = (int)((chunk_of[cs >> 3] >> (4 * (cs & 7))) & 0xfu);
-            int idx = rescan(sq, tchunk, kb, cs, xblk, wblk, g, zero_block, w64, b4, inv_d);
+            // The lane of the column whose matrix-core minimum is least holds
+            // the entry.  Unless two lanes of some column hold equal minima,
+            // the four lanes split that lane's entries of its chunk between
+            // them (kChunkTiles/4 tiles each) and keep the least key, lowest
+            // entry on equal keys; with equal minima every lane rescans its own
+            // entries and the lane of least minimum, then lowest entry, wins.
+            float cm = fminf(lane_min, __shfl_xor(lane_min, 16));
+            cm = fminf(cm, __shfl_xor(cm, 32));
+            const uint64_t holders = (__ballot(lane_min == cm) >> col) & 0x0001000100010001ull;
+            const bool tie = __ballot(__popcll(holders) > 1) != 0;      // wave-uniform
+            int idx;
+            float key;
+            if (!tie) {
+                const int kbs = __builtin_ctzll(holders) >> 4;
+                const int tch = __shfl(tchunk, col + 16 * kbs);
+                idx = rescan(sq, tch, kbs, kb * (kChunkTiles / 4), kChunkTiles / 4, cs, xblk, wblk, g,
+                             zero_block, w64, b4, inv_d, &key);
 #pragma unroll
-            for (int o = 16; o <= 32; o <<= 1) {
-                const float om = __shfl_xor(lane_min, o);
-                const int oi = __shfl_xor(idx, o);
-                if (om < lane_min || (om == lane_min && oi < idx)) { lane_min = om; idx = oi; }
+                for (int o = 16; o <= 32; o <<= 1) {
+                    const float ok = __shfl_xor(key, o);
+                    const int oi = __shfl_xor(idx, o);
+                    if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
+                }
+            } else {
+                idx = rescan(sq, tchunk, kb, 0, kChunkTiles, cs, xblk, wblk, g, zero_block, w64, b4,
+                             inv_d, &key);
+#pragma unroll
+                for (int o = 16; o <= 32; o <<= 1) {
+                    const float om = __shfl_xor(lane_min, o);
+                    const int oi = __shfl_xor(idx, o);
+                    if (om < lane_min || (om == lane_min && oi < idx)) { lane_min = om; idx = oi; }
+                }
             }
             idx = idx < n ? idx : n - 1;
             if (kMode == kModeCandidates) {

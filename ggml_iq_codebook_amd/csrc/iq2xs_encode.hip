@@ -122,37 +122,38 @@ constexpr int kEntryStride = 18;
 template <int kChunk>
 __device__ __forceinline__ int entry_off(int e) { return kEntryStride * e + 2 * (e / kChunk); }
 
-// VALU rescan: the lowest entry of least key (2k+1)*N - 2P/d among this lane's
-// entries of one chunk.
+// VALU rescan for local scale k: positions p0 .. p0+np-1 of the entries one
+// lane of a column covers in chunk `chunk` (position p = tile p/4 of the
+// chunk, row 4*kbs + p%4): the lowest entry with the least key
+// (2k+1)*N - 2P/d.  Returns the entry, writes its key.
 template <int kChunkTiles>
-__device__ __forceinline__ int rescan(const float* __restrict__ sg, int chunk, int kb, int k,
-                                      const float (&wxs)[8], const float (&w)[8], float inv_d)
+__device__ __forceinline__ int rescan(const float* __restrict__ sg, int chunk, int kbs, int p0,
+                                      int np, int k, const float (&wxs)[8], const float (&w)[8],
+                                      float inv_d, float* key_out)
 {
     const float mk = (float)(2 * k + 1);
     int idx = -1;
     float vbest = 0.0f;
-    for (int tt = 0; tt < kChunkTiles; ++tt) {
+    for (int pp = p0; pp < p0 + np; ++pp) {
+        const int e = (chunk * kChunkTiles + (pp >> 2)) * kTile + 4 * kbs + (pp & 3);
+        const float2* p = reinterpret_cast<const float2*>(sg + entry_off<kChunkTiles * kTile>(e));
+        float q[8], q2[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int e = (chunk * kChunkTiles + tt) * kTile + 4 * kb + r;
-            const float2* p = reinterpret_cast<const float2*>(sg + entry_off<kChunkTiles * kTile>(e));
-            float q[8], q2[8];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float2 u = p[t], v = p[4 + t];
-                q[2 * t] = u.x; q[2 * t + 1] = u.y;
-                q2[2 * t] = v.x; q2[2 * t + 1] = v.y;
-            }
-            float P = 0.0f, N = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                P = __builtin_fmaf(wxs[j], q[j], P);
-                N = __builtin_fmaf(w[j], q2[j], N);
-            }
-            const float key = __builtin_fmaf(N, mk, (-2.0f * P) * inv_d);
-            if (idx < 0 || key < vbest) { vbest = key; idx = e; }
+        for (int t = 0; t < 4; ++t) {
+            const float2 u = p[t], v = p[4 + t];
+            q[2 * t] = u.x; q[2 * t + 1] = u.y;
+            q2[2 * t] = v.x; q2[2 * t + 1] = v.y;
         }
+        float P = 0.0f, N = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            P = __builtin_fmaf(wxs[j], q[j], P);
+            N = __builtin_fmaf(w[j], q2[j], N);
+        }
+        const float key = __builtin_fmaf(N, mk, (-2.0f * P) * inv_d);
+        if (idx < 0 || key < vbest) { vbest = key; idx = e; }
     }
+    *key_out = vbest;
     return idx;
 }
 
@@ -354,12 +355,38 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             for (int c = 1; c < 16; ++c)
                 if (k == c) lm = best[c];
             const int tchunk = (int)((chunk_of[k >> 3] >> (4 * (k & 7))) & 0xfu);
-            int idx = rescan<kChunkTiles>(sgrid, tchunk, kb, k, wxs, w, inv_d);
+            // The lane of the column whose matrix-core minimum is least holds
+            // the entry.  Unless two lanes of some column hold equal minima,
+            // the four lanes split that lane's entries of its chunk and keep
+            // the least key, lowest entry on equal keys; with equal minima
+            // every lane rescans its own entries and the lane of least
+            // minimum, then lowest entry, wins.
+            constexpr int kPer = kChunkTiles;          // 4*kChunkTiles entries over 4 lanes
+            float cm = fminf(lm, __shfl_xor(lm, 16));
+            cm = fminf(cm, __shfl_xor(cm, 32));
+            const uint64_t holders = (__ballot(lm == cm) >> col) & 0x0001000100010001ull;
+            const bool tie = __ballot(__popcll(holders) > 1) != 0;      // wave-uniform
+            int idx;
+            float key;
+            if (!tie) {
+                const int kbs = __builtin_ctzll(holders) >> 4;
+                const int tch = __shfl(tchunk, col + 16 * kbs);
+                idx = rescan<kChunkTiles>(sgrid, tch, kbs, kb * kPer, kPer, k, wxs, w, inv_d, &key);
 #pragma unroll
-            for (int o = 16; o <= 32; o <<= 1) {
-                const float om = __shfl_xor(lm, o);
-                const int oi = __shfl_xor(idx, o);
-                if (om < lm || (om == lm && oi < idx)) { lm = om; idx = oi; }
+                for (int o = 16; o <= 32; o <<= 1) {
+                    const float ok = __shfl_xor(key, o);
+                    const int oi = __shfl_xor(idx, o);
+                    if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
+                }
+            } else {
+                idx = rescan<kChunkTiles>(sgrid, tchunk, kb, 0, 4 * kChunkTiles, k, wxs, w, inv_d,
+                                          &key);
+#pragma unroll
+                for (int o = 16; o <= 32; o <<= 1) {
+                    const float om = __shfl_xor(lm, o);
+                    const int oi = __shfl_xor(idx, o);
+                    if (om < lm || (om == lm && oi < idx)) { lm = om; idx = oi; }
+                }
             }
             return idx < n ? idx : n - 1;
         };
