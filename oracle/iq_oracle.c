@@ -1042,8 +1042,9 @@ double orc_choice_objective(const float* H, const float* cand_row, int32_t G, in
 int orc_choice_replay(const float* H, const float* cand_row, int32_t G, int32_t C,
                       int32_t sweeps, const int32_t* trace_row, double tol, double* worst)
 {
+    if ((G != 8 && G != 16) || C < 1 || C > 16) { *worst = INFINITY; return -1; }
     int L = 256 / G;
-    double e[256], r[256], rest[16], score[16];
+    double e[256], r[256], rest[32], score[16];   /* L is 16 or 32 */
     int p[16];
     double wv = 0.0;
     int fail = 0;

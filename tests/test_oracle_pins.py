@@ -728,6 +728,20 @@ def test_replay_accepts_the_oracles_trace_and_rejects_a_bad_one():
     assert fail == 1
 
 
+def test_replay_handles_32_column_groups():
+    # G = 8 (IQ1_S sub-blocks): the replay's per-group vectors hold 32 values.
+    H = workloads.block_hessian(256, 7)
+    grid = workloads.iq1s_grid(512)
+    w = workloads.normal_weight((1, 48, 256), 181)
+    imp = np.sqrt(np.diag(H).astype(np.float64)).astype(np.float32)[None]
+    err, _, _ = oracle.iq1s_candidates(w, grid, imp, top_c=8)
+    for cand in (err, _random_cand(48, 8, 16, 182)):
+        picks, trace = oracle.choice_search(H, cand, sweeps=2)
+        for r in range(cand.shape[0]):
+            fail, worst = oracle.choice_replay(H, cand[r], trace[:, r, :], 1e-9)
+            assert fail == 0 and worst <= 1e-12, (r, fail, worst)
+
+
 # --------------------------------------------------------------------------
 # IQ1_M (#2525 IQ1_M commit bodies #2513, #2595)
 # --------------------------------------------------------------------------
