@@ -104,7 +104,6 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     constexpr int G = 256 / L;
     constexpr int KS = L / 4;                   // matrix-core K steps per group
     constexpr int KH = L / 16;                  // 16-column tiles per group
-    constexpr int KSH = KS / KH;                // K steps per 16 columns
     // LDS rows are padded (and stay 16-byte aligned) so that the lanes of a
     // wave reading rows, blocks or columns together fall in different banks.
     constexpr int kHR = L + 4;                  // H_gg row stride
@@ -153,17 +152,20 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     // used.
     {
         constexpr int kJB = 8;
-        const int ncols = kRows * C;
-        const int ntile = (ncols + 15) / 16;
+        const int ntile = C;                      // 16*C (row, cand) columns in tiles of 16
         const int njobs = G * ntile;
+        // v / C for 0 <= v < 2^16 without an integer divide: (v + 1/2)/C lies
+        // at least 1/(2C) away from an integer, far beyond the float error.
+        const float invC = 1.0f / (float)C;
+        auto divC = [&](int v) { return (int)(((float)v + 0.5f) * invC); };
         float4 Ec[kJB][KH], En[kJB][KH];
         auto load_batch = [&](int j0, float4 (&E)[kJB][KH]) {
 #pragma unroll
             for (int b = 0; b < kJB; ++b) {
                 const int job = j0 + 4 * b;
-                const int g = job / ntile, n = (job % ntile) * 16 + lc;
-                const int rr = n / C, c = n % C;
-                const bool live = job < njobs && n < ncols && rr < nrows;
+                const int g = divC(job), n = (job - g * C) * 16 + lc;
+                const int rr = divC(n), c = n - rr * C;
+                const bool live = job < njobs && rr < nrows;
                 const float* ep = live ? cand_ptr(rr, g, c) : nullptr;
 #pragma unroll
                 for (int h = 0; h < KH; ++h) {
@@ -179,11 +181,11 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         load_batch(wave, Ec);
         for (int j0 = wave; j0 < njobs; j0 += 4 * kJB) {           // wave-uniform
             load_batch(j0 + 4 * kJB, En);
+            float qv[kJB];
 #pragma unroll
             for (int b = 0; b < kJB; ++b) {
                 const int job = j0 + 4 * b;
-                if (job >= njobs) break;                           // wave-uniform
-                const int g = job / ntile, n = (job % ntile) * 16 + lc;
+                const int g = divC(job < njobs ? job : 0);
                 float q = 0.0f;
 #pragma unroll
                 for (int ih = 0; ih < KH; ++ih) {                  // rows 16ih.. of Y
@@ -203,9 +205,20 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
                     q = __builtin_fmaf(ed.z, y[2], q);
                     q = __builtin_fmaf(ed.w, y[3], q);
                 }
-                q += __shfl_xor(q, 16);
-                q += __shfl_xor(q, 32);
-                if (lq == 0 && n < ncols) qself[(n / C) * kQS + g * C + n % C] = q;
+                qv[b] = q;
+            }
+            // The column sums over the four lanes of each column, all jobs of
+            // the batch together.
+#pragma unroll
+            for (int b = 0; b < kJB; ++b) qv[b] += __shfl_xor(qv[b], 16);
+#pragma unroll
+            for (int b = 0; b < kJB; ++b) qv[b] += __shfl_xor(qv[b], 32);
+#pragma unroll
+            for (int b = 0; b < kJB; ++b) {
+                const int job = j0 + 4 * b;
+                const int g = divC(job), n = (job - g * C) * 16 + lc;
+                const int rr = divC(n);
+                if (job < njobs && lq == 0) qself[rr * kQS + g * C + (n - rr * C)] = qv[b];
             }
 #pragma unroll
             for (int b = 0; b < kJB; ++b)
