@@ -1,5 +1,6 @@
 // device_common.hpp -- small device helpers shared by the HIP kernels of
-// libiqcodec.so: fp16 conversion, status reporting, block geometry.
+// libiqcodec.so: fp16 conversion, bf16 operand splitting, status reporting,
+// block geometry.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,6 +59,34 @@ __device__ __forceinline__ void report(int32_t* status, int code)
 __device__ __forceinline__ bool finite_f32(float v)
 {
     return (__float_as_uint(v) & 0x7f800000u) != 0x7f800000u;
+}
+
+// bf16 operands of the matrix cores: the exact three-way split of an fp32
+// value into bf16 parts, so that products with bf16-exact values are exact.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Part p (0, 1, 2) of the exact three-way bf16 split of v: v = hi + mid + lo.
+__device__ __forceinline__ uint32_t split_part(float v, int p)
+{
+    const uint32_t hi = bf16_bits(v);
+    const float r1 = v - bf16_to_f32(hi);
+    const uint32_t mid = bf16_bits(r1);
+    const float r2 = r1 - bf16_to_f32(mid);
+    return p == 0 ? hi : (p == 1 ? mid : bf16_bits(r2));
+}
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 u)
+{
+    return __builtin_bit_cast(v8bf, u);
 }
 
 }  // namespace iqk

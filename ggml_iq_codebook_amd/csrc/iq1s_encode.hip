@@ -46,7 +46,6 @@ namespace iqk {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kWavesPerWG = 16;
 constexpr int kThreads = kWave * kWavesPerWG;        // 1024
@@ -77,30 +76,6 @@ struct Iq1sArgs {
     int grid_size;
     int top_c;
 };
-
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_bits(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
-
-// Part p (0, 1, 2) of the exact three-way bf16 split of v: v = hi + mid + lo.
-__device__ __forceinline__ uint32_t split_part(float v, int p)
-{
-    const uint32_t hi = bf16_bits(v);
-    const float r1 = v - bf16_to_f32(hi);
-    const uint32_t mid = bf16_bits(r1);
-    const float r2 = r1 - bf16_to_f32(mid);
-    return p == 0 ? hi : (p == 1 ? mid : bf16_bits(r2));
-}
-
-__device__ __forceinline__ v8bf as_v8bf(uint4 u)
-{
-    return __builtin_bit_cast(v8bf, u);
-}
 
 // The 8 values and importance weights of group g of a block (zeros and ones
 // for a rejected block, so the sweep stays finite).
@@ -167,6 +142,28 @@ __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, 
     }
     *key_out = vbest;
     return idx;
+}
+
+// Weighted squared error of group g against d*(2k+1)*(q + delta) for entry
+// e and choice cs = k + 8*shift, in fp64 from its definition: the sum of
+// w*(x - s*(q + delta))^2, delta = +1/8 for shift 0 and -1/8 for shift 1.
+__device__ __forceinline__ double group_error64(const float* xblk, const float* wblk, int g,
+                                                bool zero, const uint4* sq, int e, int cs, float d)
+{
+    float x[8], w[8];
+    load_group(xblk, wblk, g, zero, x, w);
+    const uint4 u = sq[e + e / kChunk];
+    const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+    const double sc = (double)d * (double)(2 * (cs & 7) + 1);
+    const double delta = (cs >> 3) ? -0.125 : 0.125;
+    double err = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double q = (double)bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+        const double r = (double)x[j] - sc * (q + delta);
+        err += (double)w[j] * r * r;
+    }
+    return err;
 }
 
 template <int kFmt, int kMode>
@@ -422,6 +419,27 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             }
         }
         if (forced >= 0) cstar = forced;
+        // Payload and fake quant with free choices: the runner-up choice.  The
+        // fp32 costs carry rounding of the size of the sums they cancel, so
+        // when the runner-up is within 2^-18 of the best's magnitude (32 to 64
+        // ulps), both are evaluated again in fp64 from the error's definition
+        // with their own entries: the lower error wins, the lower choice on
+        // equal errors.  The runner-up goes first through the loop below, as
+        // an extra pass.
+        constexpr bool kDecides = kMode == kModePayload || kMode == kModeFake;
+        int c2 = 0;
+        bool near = false;
+        if (kDecides && forced < 0) {              // wave-uniform
+            float v2 = 0.0f;
+            c2 = -1;
+#pragma unroll
+            for (int c = 0; c < kChoices; ++c)
+                if (c != cstar && (c2 < 0 || cost[c] < v2)) { c2 = c; v2 = cost[c]; }
+            near = !zero_block && v2 - cbest <= 0x1p-18f * fabsf(cbest);
+        }
+        const bool refine = kDecides && __ballot(near) != 0;      // wave-uniform
+        int idx_alt = 0;
+        double err_alt = 0.0;
         // Candidates: the top_c choices by (cost, choice); with a zero scale
         // every choice decodes to zero with entry 0, so the order is 0, 1, ...
         const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
@@ -432,9 +450,11 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         // entry (the lane rescans its entries of the chunk that holds its
         // minimum of cs, then the lane of the column whose matrix-core minimum
         // is least is kept), and the payload, decoded values or candidate.
-        const int nloop = kMode == kModeEvery ? kChoices : (kMode == kModeCandidates ? a.top_c : 1);
+        const int nloop = kMode == kModeEvery ? kChoices
+                        : (kMode == kModeCandidates ? a.top_c : (refine ? 2 : 1));
         for (int it = 0; it < nloop; ++it) {
             int ch = kMode == kModeEvery ? it : cstar;
+            if (refine && it == 0 && near) ch = c2;
             if (kMode == kModeCandidates) {
                 int cr = -1;
                 float vr = 0.0f;
@@ -446,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 used |= 1 << cr;
                 ch = cr;
             }
-            const int cs = kM ? ch + 8 * (int)((shbits >> ch) & 1u) : ch;
+            int cs = kM ? ch + 8 * (int)((shbits >> ch) & 1u) : ch;
             float lane_min = best[0];
 #pragma unroll
             for (int c = 1; c < 16; ++c)
@@ -486,6 +506,19 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 }
             }
             idx = idx < n ? idx : n - 1;
+            if (refine) {
+                // The choice unit's fp64 error: its four groups (IQ1_S
+                // sub-block) or two (IQ1_M scale group), adjacent columns.
+                double e = group_error64(xblk, wblk, g, zero_block, sq, idx, cs, d);
+                e += __shfl_xor(e, 1);
+                if (!kM) e += __shfl_xor(e, 2);
+                if (it == 0) { idx_alt = idx; err_alt = e; continue; }
+                if (near && (err_alt < e || (err_alt == e && c2 < cstar))) {
+                    ch = c2;
+                    cs = kM ? ch + 8 * (int)((shbits >> ch) & 1u) : ch;
+                    idx = idx_alt;
+                }
+            }
             if (kMode == kModeCandidates) {
                 // One lane per group writes its 8 errors xhat - x (xhat exact
                 // in fp32, one rounding), its code and, once per choice group,
@@ -519,7 +552,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 }
                 continue;
             }
-            uint8_t* ob = sout + (it * kBlocksPerWG + slot) * kBB;
+            // every choice: payload it; otherwise the one payload
+            uint8_t* ob = sout + ((kMode == kModeEvery ? it : 0) * kBlocksPerWG + slot) * kBB;
             if (kM) {
                 // IQ1_M: low byte per group; one nibble per group (3 high
                 // bits, shift bit); four scale words with the 3-bit local

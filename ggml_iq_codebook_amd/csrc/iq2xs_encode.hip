@@ -18,15 +18,20 @@
 // With the signs fixed, the error of a group and an entry is, up to a
 // constant, s^2*N - 2s*P with N = sum w*q^2 and P = sum (w*sign*x)*q.  P and
 // N for 16 entries x 16 groups are two [16 x 8] x [8 x 16] products on the
-// matrix cores (v_mfma_f32_16x16x4_f32, fp32 operands, so any magnitude grid
-// is used as given).  Dividing by d, the key of local scale k is
-// (2k+1)*N - 2P/d: one FMA with a literal multiplier; the choice cost of a
-// scale group is (2k+1) times the sum of its two groups' minima.
+// matrix cores.  When every grid value and its square are exact in bf16 (the
+// odd-integer grids {1,3,5} among them), each is one v_mfma_f32_16x16x32_bf16
+// with the group side split in three bf16 parts whose sum is the fp32 value,
+// so the products are exact; any other magnitude grid is used as given with
+// fp32 operands (two v_mfma_f32_16x16x4_f32 each, four times the matrix-core
+// time).  Dividing by d, the key of local scale k is (2k+1)*N - 2P/d: one FMA
+// with a literal multiplier; the choice cost of a scale group is (2k+1) times
+// the sum of its two groups' minima.
 //
 // Layout: a wave owns 16 groups (half a block); matrix column j = lane%16 is
 // group j, the lane's accumulator rows are entries 4*(lane/16)+r of each
 // 16-entry tile.  A 1024-thread workgroup runs 8 blocks per pass and 2 passes
-// with the grid staged once in LDS (q and q^2 as fp32, 64 KiB).  Value-only minima (v_min3);
+// with the grid staged once in LDS (q and q^2 as fp32 and as bf16, and a
+// padded fp32 copy for the rescans: 85 KiB).  Value-only minima (v_min3);
 // each lane records the chunk that last lowered each minimum and rescans its
 // entries of the winning chunk on the VALU; the four lanes of a column keep
 // the one whose matrix-core minimum is least (lowest index on equal minima).
@@ -111,6 +116,59 @@ __device__ __forceinline__ int group_signs(const float (&x)[8], const float (&w)
     return neg;
 }
 
+// True when v and v*v are both exact in bf16 (then v*v is exact in fp32 too:
+// at most 16 significant bits, and the range keeps it normal).
+__device__ __forceinline__ bool bf16_exact_with_square(float v)
+{
+    const bool range = v == 0.0f || (v >= 0x1p-60f && v <= 0x1p60f);
+    const float v2 = v * v;
+    return range && bf16_to_f32(bf16_bits(v)) == v && bf16_to_f32(bf16_bits(v2)) == v2;
+}
+
+// One matrix tile of P' = -2P/d and N: the 16 keys (2k+1)*N + P' of the
+// lane's 4 entries folded into the running minima.
+__device__ __forceinline__ void fold_tile(const v4f& pn, const v4f& nn, float (&best)[16])
+{
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const float mk = (float)(2 * k + 1);
+        const float k0 = __builtin_fmaf(nn[0], mk, pn[0]);
+        const float k1 = __builtin_fmaf(nn[1], mk, pn[1]);
+        const float k2 = __builtin_fmaf(nn[2], mk, pn[2]);
+        const float k3 = __builtin_fmaf(nn[3], mk, pn[3]);
+        best[k] = fminf(best[k], fminf(fminf(fminf(k0, k1), k2), k3));
+    }
+}
+
+// After chunk ch: record ch (4 bits at bits 4*(k%8) of word k/8) for every
+// minimum that it lowered.
+__device__ __forceinline__ void track_chunk(int ch, const float (&best)[16], float (&snap)[16],
+                                            uint32_t (&chunk_of)[2])
+{
+    const uint32_t chrep = (uint32_t)ch * 0x11111111u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const uint32_t msk = best[k] < snap[k] ? (0xfu << (4 * (k & 7))) : 0u;
+        chunk_of[k >> 3] = (chunk_of[k >> 3] & ~msk) | (chrep & msk);
+        snap[k] = best[k];
+    }
+}
+
+// Weighted squared error of a group against s*sign*q in fp64, from its
+// definition: sum of w*(x - s*sign*q)^2.
+__device__ __forceinline__ double group_error64(const float (&x)[8], const float (&w)[8], int neg,
+                                                const float* q, double s)
+{
+    double e = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double sq = s * (double)q[j];
+        const double r = (double)x[j] - (((neg >> j) & 1) ? -sq : sq);
+        e += (double)w[j] * r * r;
+    }
+    return e;
+}
+
 // Per-entry fp32 copy of the grid for the VALU rescans: q[0..7], q^2[0..7],
 // padded to 18 floats so the four entries the four lanes of a column read
 // together (4 apart) fall in different LDS banks.
@@ -170,6 +228,9 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
     __shared__ float sgrid[kMaxGrid * kEntryStride + 2 * (kMaxGrid / 32)];  // q[0..7], q^2[0..7]
     __shared__ float2 sq[kMaxGrid * 4];                 // entry e, slice kb: (q[kb], q[kb+4])
     __shared__ float2 sq2[kMaxGrid * 4];                // same for q^2
+    __shared__ uint4 sbq[kMaxGrid];                     // entry e: q[0..7] as bf16
+    __shared__ uint4 sbq2[kMaxGrid];                    // entry e: q^2[0..7] as bf16
+    __shared__ int sgrid_inexact;
     __shared__ uint16_t sout16[kPayloads * kBlocksPerWG * kBlockBytes / 2];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
@@ -181,12 +242,12 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
     const int nchunks = (n + kChunk - 1) / kChunk;
     const int npad = nchunks * kChunk;
 
-    if (tid == 0) sgrid_bad = 0;
+    if (tid == 0) { sgrid_bad = 0; sgrid_inexact = 0; }
     if (!kCandidates)
         for (int i = tid; i < kPayloads * kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     {
-        int bad = 0;
+        int bad = 0, inexact = 0;
         // One (entry, slice) pair per thread: consecutive threads write
         // consecutive LDS words.
         for (int i = tid; i < npad * 4; i += kThreads) {
@@ -200,11 +261,17 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             ge[4 + t] = make_float2(a0 * a0, a1 * a1);
             sq[i] = make_float2(b0, b1);
             sq2[i] = make_float2(b0 * b0, b1 * b1);
+            // Word t of the bf16 rows: elements 2t and 2t+1.
+            inexact |= !(bf16_exact_with_square(a0) && bf16_exact_with_square(a1));
+            reinterpret_cast<uint32_t*>(sbq)[i] = bf16_bits(a0) | (bf16_bits(a1) << 16);
+            reinterpret_cast<uint32_t*>(sbq2)[i] = bf16_bits(a0 * a0) | (bf16_bits(a1 * a1) << 16);
         }
         if (bad) sgrid_bad = 1;
+        if (inexact) sgrid_inexact = 1;
     }
     __syncthreads();
     const bool grid_bad = sgrid_bad != 0;
+    const bool grid_exact = sgrid_inexact == 0;     // workgroup-uniform
     if (grid_bad && tid == 0) report(a.status, IQ_ERR_GRID);
 
     const int col = lane & 15;
@@ -272,56 +339,70 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         const bool zero_scale = dh == 0u;
         const bool skip = bad_block || zero_scale;
 
-        // The lane's group: signs, signed weighted values, and the lane's K
-        // slice (elements kb and kb+4) of the two group-side operands.
+        // The lane's group: values, weights and signs.
         float x[8], w[8];
         load_group(xblk, wblk, g, skip, x, w);
         const int neg = group_signs(x, w);
         const float inv_d = skip ? 1.0f : 1.0f / d;
-        // Elements kb and kb+4, read again rather than selected from registers.
-        float bw0 = 1.0f, bw1 = 1.0f, bx0 = 0.0f, bx1 = 0.0f;
-        if (!skip) {
-            bx0 = xblk[g * 8 + kb];
-            bx1 = xblk[g * 8 + kb + 4];
-            if (wblk) { bw0 = wblk[g * 8 + kb]; bw1 = wblk[g * 8 + kb + 4]; }
-        }
-        float bp0 = bw0 * bx0, bp1 = bw1 * bx1;
-        if ((neg >> kb) & 1) bp0 = -bp0;
-        if ((neg >> (kb + 4)) & 1) bp1 = -bp1;
-        bp0 = -2.0f * (bp0 * inv_d);
-        bp1 = -2.0f * (bp1 * inv_d);
 
-        // Sweep.  chunk_of: 4-bit chunk index of choice k at bits 4*(k%8) of word k/8.
+        // Sweep.
         float best[16], snap[16];
         uint32_t chunk_of[2] = {0u, 0u};
 #pragma unroll
         for (int k = 0; k < 16; ++k) { best[k] = __builtin_inff(); snap[k] = best[k]; }
         const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int ch = 0; ch < nchunks; ++ch) {
-            for (int tt = 0; tt < kChunkTiles; ++tt) {
-                const int e = (ch * kChunkTiles + tt) * kTile + col;
-                const float2 aq = sq[4 * e + kb];
-                const float2 aq2 = sq2[4 * e + kb];
-                v4f pn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.x, bp0, zero4, 0, 0, 0);
-                pn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.y, bp1, pn, 0, 0, 0);
-                v4f nn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq2.x, bw0, zero4, 0, 0, 0);
-                nn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq2.y, bw1, nn, 0, 0, 0);
+        if (grid_exact) {
+            // The lane's K slice kb of the group side: part kb of the exact
+            // three-way bf16 split of -2*(w*sign*x)/d and of w, for all 8
+            // elements (slice 3 is zero padding).
+            uint32_t hp[8], hw[8];
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const float mk = (float)(2 * k + 1);
-                    const float k0 = __builtin_fmaf(nn[0], mk, pn[0]);
-                    const float k1 = __builtin_fmaf(nn[1], mk, pn[1]);
-                    const float k2 = __builtin_fmaf(nn[2], mk, pn[2]);
-                    const float k3 = __builtin_fmaf(nn[3], mk, pn[3]);
-                    best[k] = fminf(best[k], fminf(fminf(fminf(k0, k1), k2), k3));
-                }
+            for (int j = 0; j < 8; ++j) {
+                float v = w[j] * x[j];
+                if ((neg >> j) & 1) v = -v;
+                v = -2.0f * (v * inv_d);
+                hp[j] = kb < 3 ? split_part(v, kb) : 0u;
+                hw[j] = kb < 3 ? split_part(w[j], kb) : 0u;
             }
-            const uint32_t chrep = (uint32_t)ch * 0x11111111u;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const uint32_t msk = best[k] < snap[k] ? (0xfu << (4 * (k & 7))) : 0u;
-                chunk_of[k >> 3] = (chunk_of[k >> 3] & ~msk) | (chrep & msk);
-                snap[k] = best[k];
+            const v8bf opp = as_v8bf(make_uint4(hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16),
+                                                hp[4] | (hp[5] << 16), hp[6] | (hp[7] << 16)));
+            const v8bf opw = as_v8bf(make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
+                                                hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16)));
+            for (int ch = 0; ch < nchunks; ++ch) {
+                for (int tt = 0; tt < kChunkTiles; ++tt) {
+                    const int e = (ch * kChunkTiles + tt) * kTile + col;
+                    const v4f pn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(sbq[e]), opp, zero4, 0, 0, 0);
+                    const v4f nn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(sbq2[e]), opw, zero4, 0, 0, 0);
+                    fold_tile(pn, nn, best);
+                }
+                track_chunk(ch, best, snap, chunk_of);
+            }
+        } else {
+            // fp32 operands: elements kb and kb+4 of the group side, read
+            // again rather than selected from registers.
+            float bw0 = 1.0f, bw1 = 1.0f, bx0 = 0.0f, bx1 = 0.0f;
+            if (!skip) {
+                bx0 = xblk[g * 8 + kb];
+                bx1 = xblk[g * 8 + kb + 4];
+                if (wblk) { bw0 = wblk[g * 8 + kb]; bw1 = wblk[g * 8 + kb + 4]; }
+            }
+            float bp0 = bw0 * bx0, bp1 = bw1 * bx1;
+            if ((neg >> kb) & 1) bp0 = -bp0;
+            if ((neg >> (kb + 4)) & 1) bp1 = -bp1;
+            bp0 = -2.0f * (bp0 * inv_d);
+            bp1 = -2.0f * (bp1 * inv_d);
+            for (int ch = 0; ch < nchunks; ++ch) {
+                for (int tt = 0; tt < kChunkTiles; ++tt) {
+                    const int e = (ch * kChunkTiles + tt) * kTile + col;
+                    const float2 aq = sq[4 * e + kb];
+                    const float2 aq2 = sq2[4 * e + kb];
+                    v4f pn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.x, bp0, zero4, 0, 0, 0);
+                    pn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.y, bp1, pn, 0, 0, 0);
+                    v4f nn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq2.x, bw0, zero4, 0, 0, 0);
+                    nn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq2.y, bw1, nn, 0, 0, 0);
+                    fold_tile(pn, nn, best);
+                }
+                track_chunk(ch, best, snap, chunk_of);
             }
         }
 
@@ -413,8 +494,43 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 #pragma unroll
             for (int k = 1; k < 16; ++k)
                 if (cost[k] < cbv) { cbv = cost[k]; kstar = k; }
-            if (forced >= 0) kstar = forced;
-            const int idx = pick(kstar);
+            int idx;
+            if (forced >= 0) {                      // wave-uniform
+                kstar = forced;
+                idx = pick(kstar);
+            } else {
+                // The runner-up local scale.  The fp32 costs carry rounding
+                // of the size of the sums they cancel, so when the runner-up
+                // is within 2^-18 of the best's magnitude (32 to 64 ulps) both
+                // are evaluated again in fp64 from the error's definition,
+                // with their own entries; the lower error wins, the lower k on
+                // equal errors.
+                int k2 = kstar == 0 ? 1 : 0;
+                float c2 = cost[k2];
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    if (k != kstar && cost[k] < c2) { c2 = cost[k]; k2 = k; }
+                const bool near = !skip && c2 - cbv <= 0x1p-18f * fabsf(cbv);
+                if (__ballot(near) == 0) {
+                    idx = pick(kstar);
+                } else {
+                    const int i1 = pick(kstar);
+                    const int i2 = pick(k2);
+                    __asm__ volatile("" ::: "memory");
+                    float xr[8], wr[8];
+                    load_group(xblk, wblk, g, skip, xr, wr);
+                    const double dd = (double)d;
+                    double e1 = group_error64(xr, wr, neg, sgrid + entry_off<kChunk>(i1),
+                                              dd * (double)(2 * kstar + 1));
+                    double e2 = group_error64(xr, wr, neg, sgrid + entry_off<kChunk>(i2),
+                                              dd * (double)(2 * k2 + 1));
+                    e1 += __shfl_xor(e1, 1);        // the other group of the scale group
+                    e2 += __shfl_xor(e2, 1);
+                    const bool take2 = near && (e2 < e1 || (e2 == e1 && k2 < kstar));
+                    idx = take2 ? i2 : i1;
+                    if (take2) kstar = k2;
+                }
+            }
             const int kodd = __shfl_xor(kstar, 2);
             const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
             if (!skip && kb == 0) {
@@ -473,12 +589,14 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 #pragma unroll
                         for (int j = 0; j < 8; ++j) ev[j] = 0.0f;
                     } else {
-                        const float sk = d * (float)(2 * kr + 1);
+                        // xhat in fp64 (exact: d*(2k+1) has at most 16
+                        // significant bits), one rounding of xhat - x to fp32.
+                        const double sk = (double)d * (double)(2 * kr + 1);
                         const float* q = sgrid + entry_off<kChunk>(idx);
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
-                            const float sg = (!zero_scale && ((neg >> j) & 1)) ? -1.0f : 1.0f;
-                            ev[j] = (sk * sg) * q[j] - xo[j];
+                            const double sg = (!zero_scale && ((neg >> j) & 1)) ? -sk : sk;
+                            ev[j] = (float)(sg * (double)q[j] - (double)xo[j]);
                         }
                     }
                     float4* ep = reinterpret_cast<float4*>(a.cand_err + base * 16 + h * 8);

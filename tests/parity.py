@@ -77,3 +77,69 @@ def compare_payloads(fmt, got, ref, x, grid, imp=None, max_tie_frac=0.005):
         % (nd, worst, TIE_RTOL, int(rows[0])))
     assert nd <= max_tie_frac * diff.size, "%d tie units of %d" % (nd, diff.size)
     return nd
+
+
+def near_tie_blocks(fmt, nblk=32, seed=0, weighted=True, steps=40):
+    """Blocks built so that one choice group's best two choices differ by a
+    weighted error just above the tie bar: the values of that group are scaled
+    by a factor found by bisection (every block's d pinned) until the oracle's
+    runner-up choice costs between 1.1e-6 and 4e-6 relative more than its
+    best.  A search whose choice between the two is decided by fp32 rounding
+    gets some of these wrong.  Returns (w [1, nblk, 256], grid, imp or None,
+    scales [1, nblk] uint16, unit per block, relative gap per block: inf where
+    no factor in [0.6, 1.6] reorders the two)."""
+    import workloads
+    grid = grid_for(fmt, None, seed)
+    w0 = workloads.student_t_weight((1, nblk, 256), 100 + seed)
+    imp = workloads.lognormal_importance((1, 256), 200 + seed) if weighted else None
+    d = oracle.predict_scales(fmt, w0).reshape(1, nblk)
+    G = oracle.NUM_CHOICE_GROUPS[fmt]
+    L = 256 // G
+    nc = oracle.NUM_CHOICES[fmt]
+    unit = np.arange(nblk) % G
+    target = 1.1e-6 * (4.0 / 1.1) ** ((np.arange(nblk) % 8) / 7.0)
+    sel = np.zeros((nblk, 256), bool)
+    for b in range(nblk):
+        sel[b, L * unit[b]:L * (unit[b] + 1)] = True
+    ib = None if imp is None else np.broadcast_to(imp.reshape(1, 256), (nblk, 256))
+
+    def scaled(alpha):
+        x = w0.reshape(nblk, 256).astype(np.float64)
+        x = np.where(sel, x * alpha[:, None], x).astype(np.float32)
+        return x.reshape(1, nblk, 256)
+
+    def unit_errors(w, ch):
+        # weighted error of every block's target unit with its choices forced to ch
+        c = np.broadcast_to(ch[:, None], (nblk, G)).reshape(1, nblk, 1, G).astype(np.int32)
+        p = oracle.encode(fmt, w, grid, imp, scales=d, choices=c).reshape(nblk, -1)
+        return oracle.block_errors(fmt, p, w.reshape(nblk, 256), grid, ib)[np.arange(nblk), unit]
+
+    def all_errors(w):
+        ev = oracle.encode_every_choice(fmt, w, grid, imp, scales=d).reshape(nc, nblk, -1)
+        return np.stack([oracle.block_errors(fmt, ev[c], w.reshape(nblk, 256), grid, ib)
+                         [np.arange(nblk), unit] for c in range(nc)], 1)      # [nblk, nc]
+
+    def excess(w, c1, c2):
+        e1 = unit_errors(w, c1)
+        return (unit_errors(w, c2) - e1) / e1 - target
+
+    e = all_errors(w0)
+    order = np.argsort(e, axis=1, kind="stable")
+    c1, c2 = order[:, 0], order[:, 1]
+    lo = np.ones(nblk)
+    hi = np.full(nblk, np.nan)
+    for f in (0.98, 1.02, 0.95, 1.05, 0.9, 1.1, 0.8, 1.25, 0.6, 1.6):
+        a = np.where(np.isnan(hi), f, hi)
+        below = excess(scaled(a), c1, c2) < 0
+        hi = np.where(np.isnan(hi) & below, f, hi)
+    ok = ~np.isnan(hi) & (excess(scaled(lo), c1, c2) > 0)
+    hi = np.where(ok, hi, 1.0)
+    for _ in range(steps):
+        mid = 0.5 * (lo + hi)
+        below = excess(scaled(mid), c1, c2) < 0
+        hi = np.where(below, mid, hi)
+        lo = np.where(below, lo, mid)
+    w = scaled(lo)
+    e = np.sort(all_errors(w), axis=1)
+    gap = (e[:, 1] - e[:, 0]) / e[:, 0]
+    return w, grid, imp, d.astype(np.uint16), unit, np.where(ok, gap, np.inf)

@@ -81,6 +81,28 @@ def test_ragged_shapes_and_grid_sizes(fmt, shape, n):
     _check_full(fmt, w, grid, imp)
 
 
+def _iq2xs_grid_kind(kind, n, seed):
+    if kind == "wide":
+        return workloads.iq2xs_wide_grid(n, seed)
+    if kind == "real":
+        return workloads.iq2xs_real_grid(n, seed)
+    grid = workloads.iq2xs_grid(n, seed)          # "one_off": one value off bf16
+    grid[-1, 7] = np.float32(5.0 + 2.0 ** -18)
+    return grid
+
+
+@pytest.mark.parametrize("kind", ["wide", "real", "one_off"])
+@pytest.mark.parametrize("shape,n", [((2, 5, 768), 512), ((1, 3, 512), 37), ((1, 4, 256), 100)])
+def test_iq2xs_grids_not_exact_in_bf16(kind, shape, n):
+    # Grids whose values or squares bf16 cannot hold take the fp32-operand
+    # sweep; the payload must match the oracle as for the {1,3,5} grids.
+    grid = _iq2xs_grid_kind(kind, n, 41)
+    w = workloads.student_t_weight(shape, 42)
+    imp = workloads.lognormal_importance((shape[0], shape[2]), 43)
+    _check_full("iq2_xs", w, grid, imp)
+    _check_full("iq2_xs", w, grid, None)
+
+
 def test_c3_iq2xs_rows_match_oracle():
     c = workloads.c3_iq2xs_4096()
     w = c["w"][:, :24, :]
@@ -266,3 +288,23 @@ def test_c4_moe_batch_equals_per_expert_calls_and_oracle():
     for e in (0, 7, 15):
         one = _gpu_encode("iq1_s", cfg["w"][e:e + 1], cfg["grid"], cfg["importance"][e:e + 1])
         np.testing.assert_array_equal(one[0], got[e])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("weighted", [True, False])
+def test_near_tied_choices_follow_the_oracle(fmt, weighted):
+    # One choice group per block whose two best choices differ by 1.1e-6 to
+    # 4e-6 of its error: above the tie bar, so the kernel must pick the better
+    # one, though fp32 rounding of the costs alone could order them either way.
+    from tests.parity import near_tie_blocks
+    w, grid, imp, d, unit, gap = near_tie_blocks(fmt, 64, 1, weighted)
+    assert ((gap > 1e-6) & (gap < 1e-5)).sum() >= 40
+    sc = torch.from_numpy(d.view(np.int16)).to(DEV)
+    wi = None if imp is None else _dev(imp)
+    got = iq.encode(_dev(w), _dev(grid), wi, fmt=fmt, scales=sc)
+    xh, pk = iq.fake_quant(_dev(w), _dev(grid), wi, fmt=fmt, scales=sc, packed=True)
+    torch.cuda.synchronize()
+    ref = oracle.encode(fmt, w, grid, imp, scales=d)
+    ib = _block_imp(imp, 1, 64, 256)
+    compare_payloads(fmt, got.cpu().numpy(), ref, w.reshape(-1, 256), grid, ib, max_tie_frac=1.0)
+    np.testing.assert_array_equal(pk.cpu().numpy(), got.cpu().numpy())

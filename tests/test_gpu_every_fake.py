@@ -175,6 +175,30 @@ def test_fake_quant_writes_zeros_for_rejected_blocks(fmt):
     np.testing.assert_array_equal(np.delete(o.reshape(4, 256), 2, axis=0).astype(np.float64), want)
 
 
+@pytest.mark.parametrize("kind", ["wide", "real"])
+def test_iq2xs_every_choice_and_fake_quant_with_grids_not_exact_in_bf16(kind):
+    # The fp32-operand sweep: every-choice payloads equal the forced encodes
+    # and the oracle; the fused decode is bitwise the decode of the payload.
+    grid = (workloads.iq2xs_wide_grid if kind == "wide" else workloads.iq2xs_real_grid)(300, 6)
+    w = workloads.student_t_weight((1, 4, 512), 216)
+    imp = workloads.lognormal_importance((1, 512), 217)
+    every = iq.encode_every_choice(_dev(w), _dev(grid), _dev(imp), fmt="iq2_xs")
+    xh, pk = iq.fake_quant(_dev(w), _dev(grid), _dev(imp), fmt="iq2_xs", packed=True)
+    xd = iq.dequant(pk, _dev(grid), fmt="iq2_xs")
+    torch.cuda.synchronize()
+    ev = every.cpu().numpy()
+    ref = oracle.encode_every_choice("iq2_xs", w, grid, imp)
+    for c in range(16):
+        full = torch.full((1, 4, 2, 16), c, dtype=torch.int32, device=DEV)
+        forced = iq.encode(_dev(w), _dev(grid), _dev(imp), fmt="iq2_xs", choices=full)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(ev[c], forced.cpu().numpy(), err_msg="choice %d" % c)
+        compare_payloads("iq2_xs", ev[c], ref[c], w.reshape(-1, 256), grid, _block_imp(imp, 1, 4, 512))
+    np.testing.assert_array_equal(_bits(xh), _bits(xd))
+    compare_payloads("iq2_xs", pk.cpu().numpy(), oracle.encode("iq2_xs", w, grid, imp),
+                     w.reshape(-1, 256), grid, _block_imp(imp, 1, 4, 512))
+
+
 def test_fake_quant_rejects_output_overlapping_the_weight():
     grid = _dev(workloads.iq1s_grid(64))
     w = _dev(workloads.normal_weight((1, 4, 256), 215))

@@ -77,6 +77,15 @@ def test_candidates_small_rows():
     _check_candidates(w[:3], workloads.iq2xs_grid(77), imp, 1)
 
 
+def test_candidates_with_grids_not_exact_in_bf16():
+    # The fp32-operand sweep of the candidates kernel.
+    w = workloads.student_t_weight((24, 256), 35)
+    imp = workloads.lognormal_importance((256,), 36)
+    _check_candidates(w, workloads.iq2xs_wide_grid(), imp, 8)
+    _check_candidates(w[:6], workloads.iq2xs_real_grid(200, 3), imp, 16)
+    _check_candidates(w[:4], workloads.iq2xs_real_grid(45, 4), None, 3)
+
+
 def test_candidates_zero_block():
     grid = workloads.iq2xs_grid()
     w = workloads.student_t_weight((3, 256), 33)

@@ -50,6 +50,21 @@ def iq2xs_grid(n: int = IQ2XS_GRID_SIZE, seed: int = 0) -> np.ndarray:
     return (2 * d + 1).astype(np.float32)
 
 
+def iq2xs_wide_grid(n: int = IQ2XS_GRID_SIZE, seed: int = 0) -> np.ndarray:
+    """[n, 8] float32 magnitude grid with values in {8, 25, 43}, distinct rows:
+    integer magnitudes whose squares (625, 1849) need more than bf16's 8
+    significant bits."""
+    d = _ternary_patterns(n, seed)
+    return np.array([8.0, 25.0, 43.0], np.float32)[d]
+
+
+def iq2xs_real_grid(n: int = IQ2XS_GRID_SIZE, seed: int = 0) -> np.ndarray:
+    """[n, 8] float32 magnitude grid of arbitrary positive values, uniform in
+    [0.25, 6)."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(0.25, 6.0, size=(n, 8)).astype(np.float32)
+
+
 def normal_weight(shape, seed: int, std: float = 0.02) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return (std * rng.standard_normal(size=shape)).astype(np.float32)
