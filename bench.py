@@ -189,7 +189,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 10 and at least 1 s of them, "
+                         "so the clocks have settled; the count run is reported)")
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -277,8 +279,17 @@ def main():
         def step():
             iq.encode(w, grid, imp, fmt=fmt, scales=scales, out=out, status=status, check=False)
 
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:
+        nwarm, tw = 0, time.perf_counter()
+        while nwarm < 10 or time.perf_counter() - tw < 1.0:
+            step()
+            nwarm += 1
+            if nwarm % 10 == 0:
+                torch.cuda.synchronize()
+        args.warmup = nwarm
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise SystemExit("encode reported status %d" % int(status.item()))

@@ -14,10 +14,13 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-// Per device: 0 = not checked, 1 = gfx950, 2 = other.
+// Per device: 0 = not checked, 1 = gfx950, 2 = other; and its compute units.
 std::atomic<int> g_device_kind[kMaxDevices];
+std::atomic<int> g_device_cus[kMaxDevices];
 
-iq_status_t check_device()
+// Also records the device's compute units in g (when given): persistent
+// launches size their grid by it.
+iq_status_t check_device(iqk::BlockGeom* g = nullptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return IQ_ERR_HIP;
@@ -27,8 +30,11 @@ iq_status_t check_device()
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return IQ_ERR_HIP;
         kind = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1,
+                                std::memory_order_relaxed);
         g_device_kind[dev].store(kind, std::memory_order_release);
     }
+    if (g) g->cus = g_device_cus[dev].load(std::memory_order_relaxed);
     return kind == 1 ? IQ_OK : IQ_ERR_DEVICE;
 }
 
@@ -46,6 +52,7 @@ iq_status_t geometry(int64_t batch, int64_t rows, int64_t cols, iqk::BlockGeom* 
     g->blocks_per_batch = rows * bpr;
     g->nblocks = batch * rows * bpr;
     g->cols = cols;
+    g->cus = 1;
     if (g->nblocks > (INT64_C(1) << 34)) return IQ_ERR_SHAPE;
     return IQ_OK;
 }
@@ -126,7 +133,7 @@ iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t ro
         !aligned(out, 2) || (scales && !aligned(scales, 2)) || (choices && !aligned(choices, 4)) ||
         !aligned(status, 4))
         return IQ_ERR_ARG;
-    st = check_device();
+    st = check_device(&g);
     if (st) return st;
     return from_hip(launch_encode(fmt, w, importance, grid, grid_size, scales, choices, out,
                                   nullptr, iqk::kModePayload, status, g, stream));
@@ -146,7 +153,7 @@ iq_status_t iq_encode_every_choice(iq_format_t fmt, const float* w, int64_t batc
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(out, 2) || (scales && !aligned(scales, 2)) || !aligned(status, 4))
         return IQ_ERR_ARG;
-    st = check_device();
+    st = check_device(&g);
     if (st) return st;
     return from_hip(launch_encode(fmt, w, importance, grid, grid_size, scales, nullptr, out,
                                   nullptr, iqk::kModeEvery, status, g, stream));
@@ -172,7 +179,7 @@ iq_status_t iq_fake_quant(iq_format_t fmt, const float* w, int64_t batch, int64_
     const uintptr_t w0 = reinterpret_cast<uintptr_t>(w), x0 = reinterpret_cast<uintptr_t>(xhat);
     const uintptr_t bytes = static_cast<uintptr_t>(g.nblocks) * 256u * sizeof(float);
     if (x0 < w0 + bytes && w0 < x0 + bytes) return IQ_ERR_ARG;
-    st = check_device();
+    st = check_device(&g);
     if (st) return st;
     return from_hip(launch_encode(fmt, w, importance, grid, grid_size, scales, choices, out, xhat,
                                   iqk::kModeFake, status, g, stream));
@@ -189,7 +196,7 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
     if (!packed || !grid || !out || !status) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (!aligned(grid, 16) || !aligned(out, 16) || !aligned(status, 4)) return IQ_ERR_ARG;
-    st = check_device();
+    st = check_device(&g);
     if (st) return st;
     return from_hip(iqk::launch_dequant((int)fmt, packed, grid, grid_size, out, status, g, stream));
 }
@@ -210,7 +217,7 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, 
         !aligned(cand_err, 16) || !aligned(cand_choice, 4) ||
         (cand_codes && !aligned(cand_codes, 2)) || !aligned(status, 4))
         return IQ_ERR_ARG;
-    st = check_device();
+    st = check_device(&g);
     if (st) return st;
     if (fmt != IQ_FMT_IQ2_XS)
         return from_hip(iqk::launch_iq1_candidates((int)fmt, w, importance, grid, grid_size, top_c,

@@ -30,13 +30,14 @@
 // group j; the lane's four accumulator rows are 4*(lane/16)+r of every
 // 16-entry tile, so the four lanes of a column cover disjoint quarters of the
 // grid.  A 1024-thread workgroup runs 16 waves = 8 blocks per pass and 2
-// passes (16 blocks), with the grid staged once in LDS as bf16 ((q+1/8)^2,
-// (q-1/8)^2 and q, 96 KiB; one workgroup per CU, 4 waves per SIMD).
-// Index recovery: each lane records the 128-entry chunk that last lowered each
-// of its 16 minima; once the sub-block's choice is fixed, the lane rescans its
-// 32 entries of that chunk on the VALU (fp32 dot products) and takes the lowest
-// entry of least key; the four lanes of a column then keep the one whose
-// matrix-core minimum is least (lowest index on equal minima).
+// passes per set of 16 blocks; the workgroups are persistent (one per CU, 4
+// waves per SIMD) and stage the grid once in LDS as bf16 ((q+1/8)^2,
+// (q-1/8)^2 and q, 96 KiB).
+// Index recovery: each lane records the chunk (128 or 256 entries) that last
+// lowered each of its 16 minima; once the choice is fixed, the lane of each
+// column whose matrix-core minimum is least is found, and the four lanes of
+// the column split its entries of that chunk between them and rescan them on
+// the VALU (fp32 dot products), lowest entry of least key.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -53,8 +54,17 @@ constexpr int kBlocksPerPass = kWavesPerWG / 2;      // two waves per block
 constexpr int kPasses = 2;
 constexpr int kBlocksPerWG = kBlocksPerPass * kPasses;   // 16
 constexpr int kTile = 16;                            // grid entries per matrix tile
-constexpr int kChunkTiles = 8;                       // tiles per tracking chunk
-constexpr int kChunk = kTile * kChunkTiles;          // 128 entries
+// Tiles per tracking chunk.  Recording chunks costs the sweep about 4
+// instructions per choice and chunk; each pick rescans one lane's entries of
+// a chunk, 4 per tile.  IQ1_S with one pick per group (payload, fake quant):
+// 16 tiles (256 entries), measured 3 % faster than 8; otherwise 8 (128
+// entries), as small as 4-bit chunk numbers allow for 2048 entries (IQ1_M
+// measured 3 % slower with 16).
+template <int kFmt, int kMode>
+constexpr int chunk_tiles()
+{
+    return (kFmt == IQ_FMT_IQ1_S && (kMode == kModePayload || kMode == kModeFake)) ? 16 : 8;
+}
 constexpr int kMaxGrid = 2048;
 constexpr int kBlockBytes = 50;
 constexpr int kBlockBytesM = 56;
@@ -108,6 +118,7 @@ __device__ __forceinline__ void load_group(const float* xblk, const float* wblk,
 // recomputed in fp32 from the group's values and weights (read again from
 // memory rather than held through the sweep).  Returns the entry, writes its
 // key.
+template <int kChunkTiles>
 __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, int kbs, int t0,
                                       int nt, int cs, const float* xblk, const float* wblk, int g,
                                       bool zero_block, float w64, float b4, float inv_d,
@@ -147,6 +158,7 @@ __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, 
 // Weighted squared error of group g against d*(2k+1)*(q + delta) for entry
 // e and choice cs = k + 8*shift, in fp64 from its definition: the sum of
 // w*(x - s*(q + delta))^2, delta = +1/8 for shift 0 and -1/8 for shift 1.
+template <int kChunk>
 __device__ __forceinline__ double group_error64(const float* xblk, const float* wblk, int g,
                                                 bool zero, const uint4* sq, int e, int cs, float d)
 {
@@ -178,9 +190,11 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     constexpr int kGroups = kM ? 16 : 8;          // choice groups per block
     // Payloads staged in LDS: one per block, or one per block and choice.
     constexpr int kPayloads = kMode == kModeEvery ? kChoices : 1;
-    // Entry e sits at e + e/kChunk: one spare slot per 128-entry chunk, so the
-    // lanes of a rescan that read different chunks (512 words apart without
-    // the slot, a multiple of the 64 banks) spread over the banks.
+    constexpr int kChunkTiles = chunk_tiles<kFmt, kMode>();
+    constexpr int kChunk = kTile * kChunkTiles;
+    // Entry e sits at e + e/kChunk: one spare slot per chunk, so the lanes of
+    // a rescan that read different chunks (a multiple of the 64 banks apart
+    // without the slot) spread over the banks.
     constexpr int kSlots = kMaxGrid + kMaxGrid / kChunk;
     __shared__ uint4 sp[kSlots];         // (q[0..7] + 1/8)^2 as bf16
     __shared__ uint4 sm[kSlots];         // (q[0..7] - 1/8)^2 as bf16
@@ -239,9 +253,14 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     const int sub = g >> 2;
     const int lq = g & 3;
 
+    // Persistent workgroups: the grid is staged once, then each workgroup
+    // takes every gridDim.x-th set of 16 blocks.
+    const int64_t nsets = (a.g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
+    for (int64_t set = blockIdx.x; set < nsets; set += gridDim.x) {
+    if (set != blockIdx.x) __syncthreads();     // the previous set's payloads are out
     for (int pass = 0; pass < kPasses; ++pass) {
         const int slot = pass * kBlocksPerPass + (wave >> 1);
-        const int64_t blk = (int64_t)blockIdx.x * kBlocksPerWG + slot;
+        const int64_t blk = set * kBlocksPerWG + slot;
         if (blk >= a.g.nblocks) continue;                      // wave-uniform
         const int64_t bt = blk / a.g.blocks_per_batch;
         const int64_t cb = blk % a.g.blocks_per_row;
@@ -487,8 +506,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             if (!tie) {
                 const int kbs = __builtin_ctzll(holders) >> 4;
                 const int tch = __shfl(tchunk, col + 16 * kbs);
-                idx = rescan(sq, tch, kbs, kb * (kChunkTiles / 4), kChunkTiles / 4, cs, xblk, wblk, g,
-                             zero_block, w64, b4, inv_d, &key);
+                idx = rescan<kChunkTiles>(sq, tch, kbs, kb * (kChunkTiles / 4), kChunkTiles / 4, cs,
+                                          xblk, wblk, g, zero_block, w64, b4, inv_d, &key);
 #pragma unroll
                 for (int o = 16; o <= 32; o <<= 1) {
                     const float ok = __shfl_xor(key, o);
@@ -496,8 +515,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                     if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
                 }
             } else {
-                idx = rescan(sq, tchunk, kb, 0, kChunkTiles, cs, xblk, wblk, g, zero_block, w64, b4,
-                             inv_d, &key);
+                idx = rescan<kChunkTiles>(sq, tchunk, kb, 0, kChunkTiles, cs, xblk, wblk, g,
+                                          zero_block, w64, b4, inv_d, &key);
 #pragma unroll
                 for (int o = 16; o <= 32; o <<= 1) {
                     const float om = __shfl_xor(lane_min, o);
@@ -509,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             if (refine) {
                 // The choice unit's fp64 error: its four groups (IQ1_S
                 // sub-block) or two (IQ1_M scale group), adjacent columns.
-                double e = group_error64(xblk, wblk, g, zero_block, sq, idx, cs, d);
+                double e = group_error64<kChunk>(xblk, wblk, g, zero_block, sq, idx, cs, d);
                 e += __shfl_xor(e, 1);
                 if (!kM) e += __shfl_xor(e, 2);
                 if (it == 0) { idx_alt = idx; err_alt = e; continue; }
@@ -615,22 +634,31 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         }
     }
     if (kMode != kModeCandidates && a.out) {
+        // Copy the staged payloads out and clear what was copied (each word
+        // by the thread that copied it) for the next set.
         __syncthreads();
-        const int64_t first = (int64_t)blockIdx.x * kBlocksPerWG;
+        const int64_t first = set * kBlocksPerWG;
         const int64_t left = a.g.nblocks - first;
         const int nb = left < kBlocksPerWG ? (int)left : kBlocksPerWG;
         for (int cs = 0; cs < kPayloads; ++cs) {
             uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (cs * a.g.nblocks + first) * kBB);
-            const uint16_t* s16 = sout16 + cs * kBlocksPerWG * (kBB / 2);
-            for (int i = tid; i < nb * (kBB / 2); i += kThreads) o16[i] = s16[i];
+            uint16_t* s16 = sout16 + cs * kBlocksPerWG * (kBB / 2);
+            for (int i = tid; i < nb * (kBB / 2); i += kThreads) {
+                o16[i] = s16[i];
+                s16[i] = 0;
+            }
         }
+    }
     }
 }
 
 template <int kFmt>
 hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((a.g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG));
+    // One workgroup per compute unit (the LDS holds one), or one per set of
+    // 16 blocks when there are fewer sets.
+    const int64_t sets = (a.g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
+    const dim3 grid((unsigned)(sets < a.g.cus ? sets : a.g.cus));
     if (mode == kModeEvery)
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeEvery>), grid, dim3(kThreads), 0, stream, a);
     else if (mode == kModeFake)

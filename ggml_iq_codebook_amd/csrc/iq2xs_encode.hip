@@ -30,11 +30,13 @@
 // Layout: a wave owns 16 groups (half a block); matrix column j = lane%16 is
 // group j, the lane's accumulator rows are entries 4*(lane/16)+r of each
 // 16-entry tile.  A 1024-thread workgroup runs 8 blocks per pass and 2 passes
-// with the grid staged once in LDS (q and q^2 as fp32 and as bf16, and a
-// padded fp32 copy for the rescans: 85 KiB).  Value-only minima (v_min3);
-// each lane records the chunk that last lowered each minimum and rescans its
-// entries of the winning chunk on the VALU; the four lanes of a column keep
-// the one whose matrix-core minimum is least (lowest index on equal minima).
+// per set of 16 blocks; the workgroups are persistent (one per CU) and stage
+// the grid once in LDS (q and q^2 as fp32 and as bf16, and a padded fp32 copy
+// for the rescans: 85 KiB).  Value-only minima (v_min3); each lane records
+// the chunk that last lowered each minimum; the lane of each column whose
+// matrix-core minimum is least is found, and the four lanes of the column
+// split its entries of that chunk and rescan them on the VALU (lowest entry
+// of least key).
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -220,9 +222,12 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 {
     constexpr bool kCandidates = kMode == kModeCandidates;
     constexpr int kPayloads = kMode == kModeEvery ? 16 : 1;
-    // Tiles per tracking chunk: 4 (64 entries) for the encode, 2 (32
-    // entries) for the candidates, whose epilogue rescans top_c choices.
-    constexpr int kChunkTiles = kCandidates ? 2 : 4;
+    // Tiles per tracking chunk.  Recording chunks costs the sweep about 4
+    // instructions per choice and chunk; each pick rescans one lane's
+    // entries of a chunk, 4 per tile.  One pick per group (payload, fake
+    // quant): 8 tiles (128 entries); top_c picks (candidates): 4; 16 picks
+    // (every choice): 2.
+    constexpr int kChunkTiles = kCandidates ? 4 : (kMode == kModeEvery ? 2 : 8);
     constexpr int kChunk = kTile * kChunkTiles;
 
     __shared__ float sgrid[kMaxGrid * kEntryStride + 2 * (kMaxGrid / 32)];  // q[0..7], q^2[0..7]
@@ -281,9 +286,14 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
     const int m = g >> 1;                   // scale group
     const int h = g & 1;                    // group in scale group
 
+    // Persistent workgroups: the grid is staged once, then each workgroup
+    // takes every gridDim.x-th set of 16 blocks.
+    const int64_t nsets = (a.g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
+    for (int64_t set = blockIdx.x; set < nsets; set += gridDim.x) {
+    if (set != blockIdx.x) __syncthreads();     // the previous set's payloads are out
     for (int pass = 0; pass < kPasses; ++pass) {
         const int slot = pass * kBlocksPerPass + (wave >> 1);
-        const int64_t blk = (int64_t)blockIdx.x * kBlocksPerWG + slot;
+        const int64_t blk = set * kBlocksPerWG + slot;
         if (blk >= a.g.nblocks) continue;                      // wave-uniform
         const int64_t bt = blk / a.g.blocks_per_batch;
         const int64_t cb = blk % a.g.blocks_per_row;
@@ -610,16 +620,30 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         }
     }
     if (!kCandidates && a.out) {
+        // Copy the staged payloads out and clear what was copied (each word
+        // by the thread that copied it) for the next set.
         __syncthreads();
-        const int64_t first = (int64_t)blockIdx.x * kBlocksPerWG;
+        const int64_t first = set * kBlocksPerWG;
         const int64_t left = a.g.nblocks - first;
         const int nb = left < kBlocksPerWG ? (int)left : kBlocksPerWG;
         for (int k = 0; k < kPayloads; ++k) {
             uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (k * a.g.nblocks + first) * kBlockBytes);
-            const uint16_t* s16 = sout16 + k * kBlocksPerWG * (kBlockBytes / 2);
-            for (int i = tid; i < nb * (kBlockBytes / 2); i += kThreads) o16[i] = s16[i];
+            uint16_t* s16 = sout16 + k * kBlocksPerWG * (kBlockBytes / 2);
+            for (int i = tid; i < nb * (kBlockBytes / 2); i += kThreads) {
+                o16[i] = s16[i];
+                s16[i] = 0;
+            }
         }
     }
+    }
+}
+
+// One workgroup per compute unit (the LDS holds one), or one per set of 16
+// blocks when there are fewer sets.
+unsigned persistent_wgs(const BlockGeom& g)
+{
+    const int64_t sets = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
+    return (unsigned)(sets < g.cus ? sets : g.cus);
 }
 
 }  // namespace
@@ -631,13 +655,13 @@ hipError_t launch_iq2xs_encode(const float* w, const float* imp, const float* gr
 {
     Iq2xsArgs a{w, imp, grid, scales, choices, out, xhat, nullptr, nullptr, nullptr, status, g,
                 grid_size, 0};
-    const int64_t wgs = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
+    const unsigned wgs = persistent_wgs(g);
     if (mode == kModeEvery)
-        hipLaunchKernelGGL(iq2xs_kernel<kModeEvery>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(iq2xs_kernel<kModeEvery>, dim3(wgs), dim3(kThreads), 0, stream, a);
     else if (mode == kModeFake)
-        hipLaunchKernelGGL(iq2xs_kernel<kModeFake>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(iq2xs_kernel<kModeFake>, dim3(wgs), dim3(kThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(iq2xs_kernel<kModePayload>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(iq2xs_kernel<kModePayload>, dim3(wgs), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -648,8 +672,8 @@ hipError_t launch_iq2xs_candidates(const float* w, const float* imp, const float
 {
     Iq2xsArgs a{w, imp, grid, nullptr, nullptr, nullptr, nullptr, cand_err, cand_choice,
                 cand_codes, status, g, grid_size, top_c};
-    const int64_t wgs = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
-    hipLaunchKernelGGL(iq2xs_kernel<kModeCandidates>, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    const unsigned wgs = persistent_wgs(g);
+    hipLaunchKernelGGL(iq2xs_kernel<kModeCandidates>, dim3(wgs), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ struct BlockGeom {
     int64_t blocks_per_row;   // cols / 256
     int64_t blocks_per_batch; // rows * (cols / 256)
     int64_t cols;
+    int cus;                  // compute units of the device (sizes persistent grids)
 };
 
 // What an encode launch writes: the payload; the payload under every one of
