@@ -50,9 +50,13 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
     return (h & 0x8000u) ? -v : v;
 }
 
-// First data error of a call: only a zero status is replaced.
+// First data error of a call: only a zero status is replaced.  The pointer
+// and the code pass through an empty asm so that the atomic's operands are
+// formed here, on this rare path, and not held (or spilled) for the whole
+// kernel.
 __device__ __forceinline__ void report(int32_t* status, int code)
 {
+    __asm__ volatile("" : "+s"(status), "+v"(code));
     atomicCAS(status, 0, code);
 }
 

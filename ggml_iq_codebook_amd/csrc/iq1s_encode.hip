@@ -328,7 +328,9 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         int forced = -1;
         bool choice_bad = false;
         if ((kMode == kModePayload || kMode == kModeFake) && a.choices) {
-            const int cv = lane < kGroups ? a.choices[blk * kGroups + lane] : 0;
+            int ln = lane;                  // opaque: the address is formed here, not hoisted
+            __asm__ volatile("" : "+v"(ln));
+            const int cv = ln < kGroups ? a.choices[blk * kGroups + ln] : 0;
             const bool bad = cv < 0 || cv >= kChoices;
             if (bad && half == 0) report(a.status, IQ_ERR_ARG);
             choice_bad = __ballot(bad) != 0;
@@ -643,7 +645,11 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         for (int cs = 0; cs < kPayloads; ++cs) {
             uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (cs * a.g.nblocks + first) * kBB);
             uint16_t* s16 = sout16 + cs * kBlocksPerWG * (kBB / 2);
-            for (int i = tid; i < nb * (kBB / 2); i += kThreads) {
+            // An opaque copy of the thread index: the offsets derived from it are
+            // recomputed here rather than held (and spilled) across the sets.
+            int t0 = tid;
+            __asm__ volatile("" : "+v"(t0));
+            for (int i = t0; i < nb * (kBB / 2); i += kThreads) {
                 o16[i] = s16[i];
                 s16[i] = 0;
             }

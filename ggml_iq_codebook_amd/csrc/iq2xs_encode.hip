@@ -339,7 +339,9 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         int forced = -1;
         bool choice_bad = false;
         if ((kMode == kModePayload || kMode == kModeFake) && a.choices) {
-            const int cv = lane < 16 ? a.choices[blk * 16 + lane] : 0;
+            int ln = lane;                  // opaque: the address is formed here, not hoisted
+            __asm__ volatile("" : "+v"(ln));
+            const int cv = ln < 16 ? a.choices[blk * 16 + ln] : 0;
             const bool bad = cv < 0 || cv > 15;
             if (bad && half == 0) report(a.status, IQ_ERR_ARG);
             choice_bad = __ballot(bad) != 0;
@@ -629,7 +631,11 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         for (int k = 0; k < kPayloads; ++k) {
             uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (k * a.g.nblocks + first) * kBlockBytes);
             uint16_t* s16 = sout16 + k * kBlocksPerWG * (kBlockBytes / 2);
-            for (int i = tid; i < nb * (kBlockBytes / 2); i += kThreads) {
+            // An opaque copy of the thread index: the offsets derived from it are
+            // recomputed here rather than held (and spilled) across the sets.
+            int t0 = tid;
+            __asm__ volatile("" : "+v"(t0));
+            for (int i = t0; i < nb * (kBlockBytes / 2); i += kThreads) {
                 o16[i] = s16[i];
                 s16[i] = 0;
             }
