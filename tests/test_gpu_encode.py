@@ -248,7 +248,8 @@ def test_dequant_reports_indices_beyond_the_grid():
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads, sampled against the oracle
+# full-size workloads against the oracle (all blocks, or sampled where the
+# oracle would take minutes)
 # ---------------------------------------------------------------------------
 
 
@@ -267,12 +268,22 @@ def _sampled(fmt, cfg, nsamp, seed):
     return got, compare_payloads(fmt, got[idx], ref, x, grid, ib)
 
 
-def test_c2_iq1s_4096_sampled():
-    _sampled("iq1_s", workloads.c2_iq1s_4096(), 384, 21)
+def _full(fmt, cfg):
+    # every block of the workload, in the launch bench.py times, against the
+    # oracle's encode of the whole weight
+    w, grid, imp = cfg["w"], cfg["grid"], cfg["importance"]
+    B, R, C = w.shape
+    got = _gpu_encode(fmt, w, grid, imp)
+    ref = oracle.encode(fmt, w, grid, imp)
+    return compare_payloads(fmt, got, ref, w.reshape(-1, 256), grid, _block_imp(imp, B, R, C))
 
 
-def test_c3_iq2xs_4096_sampled():
-    _sampled("iq2_xs", workloads.c3_iq2xs_4096(), 768, 22)
+def test_c2_iq1s_4096_full():
+    _full("iq1_s", workloads.c2_iq1s_4096())
+
+
+def test_c3_iq2xs_4096_full():
+    _full("iq2_xs", workloads.c3_iq2xs_4096())
 
 
 def test_iq1m_4096_sampled():
