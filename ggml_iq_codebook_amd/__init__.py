@@ -64,15 +64,18 @@ def load(build_if_missing: bool = True):
     L.iq_format_info.restype = ctypes.c_int
     L.iq_status_str.argtypes = [ctypes.c_int]
     L.iq_status_str.restype = ctypes.c_char_p
-    L.iq_encode.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, i32, P, P, P, P, P]
+    L.iq_encode.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, P, i32, P, P, P, P, P]
     L.iq_encode.restype = ctypes.c_int
-    L.iq_encode_every_choice.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, i32, P, P, P, P]
+    L.iq_encode_every_choice.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, P, i32,
+                                         P, P, P, P]
     L.iq_encode_every_choice.restype = ctypes.c_int
-    L.iq_fake_quant.argtypes = [ctypes.c_int, P, i64, i64, i64, P, P, i32, P, P, P, P, P, P]
+    L.iq_fake_quant.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, i64, P, P, i32, P, P, P,
+                                P, P, P]
     L.iq_fake_quant.restype = ctypes.c_int
     L.iq_dequant.argtypes = [ctypes.c_int, P, i64, i64, i64, P, i32, P, P, P]
     L.iq_dequant.restype = ctypes.c_int
-    L.iq_encode_candidates.argtypes = [ctypes.c_int, P, i64, i64, P, P, i32, i32, P, P, P, P, P]
+    L.iq_encode_candidates.argtypes = [ctypes.c_int, ctypes.c_int, P, i64, i64, P, P, i32, i32, P,
+                                       P, P, P, P]
     L.iq_encode_candidates.restype = ctypes.c_int
     L.iq_choice_search.argtypes = [P, P, i64, i32, i32, i32, P, P, P]
     L.iq_choice_search.restype = ctypes.c_int
@@ -139,10 +142,26 @@ def _raise_on_status(status, where):
         raise IQError(code, where)
 
 
+# Storage types of the weight (iq_dtype_t): the encode reads each value as
+# fp32 (exactly, or rounded to nearest even from fp64).
+WEIGHT_DTYPES = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2, torch.float64: 3}
+
+
+def _weight(w):
+    """The iq_dtype_t code of a weight tensor, after the device checks."""
+    if not isinstance(w, torch.Tensor):
+        raise TypeError("w must be a torch.Tensor")
+    if w.dtype not in WEIGHT_DTYPES:
+        raise TypeError("w must be float32, bfloat16, float16 or float64, got %s" % (w.dtype,))
+    _dev_tensor(w, w.dtype, "w")
+    return WEIGHT_DTYPES[w.dtype]
+
+
 def _encode_args(w, grid, importance, fmt, scales, choices):
-    """Checks shared by the encode calls; returns (fmt code, B, R, C, squeeze, scales)."""
+    """Checks shared by the encode calls; returns (fmt code, dtype code, B, R, C,
+    squeeze, scales)."""
     f = _fmt(fmt)
-    _dev_tensor(w, torch.float32, "w")
+    dt = _weight(w)
     squeeze = w.dim() == 2
     if w.dim() not in (2, 3):
         raise ValueError("w must be [rows, cols] or [batch, rows, cols]")
@@ -165,7 +184,7 @@ def _encode_args(w, grid, importance, fmt, scales, choices):
         _dev_tensor(choices, torch.int32, "choices")
         if choices.numel() != B * R * (C // 256) * CHOICE_GROUPS[fmt]:
             raise ValueError("choices must have %d values per block" % CHOICE_GROUPS[fmt])
-    return f, B, R, C, squeeze, scales
+    return f, dt, B, R, C, squeeze, scales
 
 
 def _out_tensor(out, shape, dtype, device, name):
@@ -182,7 +201,8 @@ def _out_tensor(out, shape, dtype, device, name):
 
 def encode(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, out=None,
            status=None, check=True):
-    """Encode a [batch, rows, cols] (or [rows, cols]) fp32 weight.
+    """Encode a [batch, rows, cols] (or [rows, cols]) weight (fp32, bf16, fp16 or
+    fp64, read as fp32).
 
     Returns the packed payload [batch, rows, cols/256, block_bytes] uint8 (the
     batch dimension is dropped again for a 2-D weight).  ``importance`` is
@@ -190,10 +210,10 @@ def encode(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, 
     (int16/uint16 tensor); ``choices`` forced picks [batch, rows, cols/256, G].
     With ``check`` the call synchronizes and raises IQError on a data error.
     """
-    f, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, choices)
+    f, dt, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, choices)
     out = _out_tensor(out, (B, R, C // 256, BLOCK_BYTES[fmt]), torch.uint8, w.device, "out")
     status, own = _status_tensor(status, w.device)
-    code = load().iq_encode(f, _ptr(w), B, R, C, _ptr(importance), _ptr(grid), grid.shape[0],
+    code = load().iq_encode(f, dt, _ptr(w), B, R, C, _ptr(importance), _ptr(grid), grid.shape[0],
                             _ptr(scales), _ptr(choices), _ptr(out), _ptr(status), _stream())
     _check(code, "iq_encode")
     if check:
@@ -208,11 +228,11 @@ def encode_every_choice(w, grid, importance=None, *, fmt="iq1_s", scales=None, o
     Returns [num_choices, batch, rows, cols/256, block_bytes] uint8 (no batch
     dimension for a 2-D weight); entry c equals ``encode(..., choices=full(c))``.
     """
-    f, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, None)
+    f, dt, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, None)
     out = _out_tensor(out, (NUM_CHOICES[fmt], B, R, C // 256, BLOCK_BYTES[fmt]), torch.uint8,
                       w.device, "out")
     status, own = _status_tensor(status, w.device)
-    code = load().iq_encode_every_choice(f, _ptr(w), B, R, C, _ptr(importance), _ptr(grid),
+    code = load().iq_encode_every_choice(f, dt, _ptr(w), B, R, C, _ptr(importance), _ptr(grid),
                                          grid.shape[0], _ptr(scales), _ptr(out), _ptr(status),
                                          _stream())
     _check(code, "iq_encode_every_choice")
@@ -223,19 +243,20 @@ def encode_every_choice(w, grid, importance=None, *, fmt="iq1_s", scales=None, o
 
 def fake_quant(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, out=None,
                packed=False, status=None, check=True):
-    """Encode and decode in one pass: the fp32 weight the payload stands for.
+    """Encode and decode in one pass: the fp32 weight the payload stands for
+    (fp32 whatever the weight's storage type).
 
     Returns xhat shaped like ``w`` (bit for bit ``dequant(encode(...))``), or
     (xhat, payload) with ``packed=True``.
     """
-    f, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, choices)
+    f, dt, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, choices)
     xhat = _out_tensor(out, (B, R, C), torch.float32, w.device, "out")
     pk = (torch.empty((B, R, C // 256, BLOCK_BYTES[fmt]), dtype=torch.uint8, device=w.device)
           if packed else None)
     status, own = _status_tensor(status, w.device)
-    code = load().iq_fake_quant(f, _ptr(w), B, R, C, _ptr(importance), _ptr(grid), grid.shape[0],
-                                _ptr(scales), _ptr(choices), _ptr(xhat), _ptr(pk), _ptr(status),
-                                _stream())
+    code = load().iq_fake_quant(f, dt, _ptr(w), B, R, C, _ptr(importance), _ptr(grid),
+                                grid.shape[0], _ptr(scales), _ptr(choices), _ptr(xhat), _ptr(pk),
+                                _ptr(status), _stream())
     _check(code, "iq_fake_quant")
     if check:
         _raise_on_status(status, "iq_fake_quant")
@@ -280,7 +301,7 @@ def encode_candidates(w, grid, importance=None, *, fmt="iq2_xs", top_c=8, codes=
     IQ1_M) or 4 (IQ1_S)] uint16 viewed as int16, or None).
     """
     f = _fmt(fmt)
-    _dev_tensor(w, torch.float32, "w")
+    dt = _weight(w)
     if w.dim() != 2:
         raise ValueError("w must be [rows, cols]")
     R, C = w.shape
@@ -298,7 +319,7 @@ def encode_candidates(w, grid, importance=None, *, fmt="iq2_xs", top_c=8, codes=
     cc = (torch.empty((R, NB, G, tc, ncode), dtype=torch.int16, device=w.device)
           if codes else None)
     status, own = _status_tensor(status, w.device)
-    code = load().iq_encode_candidates(f, _ptr(w), R, C, _ptr(importance), _ptr(grid),
+    code = load().iq_encode_candidates(f, dt, _ptr(w), R, C, _ptr(importance), _ptr(grid),
                                        grid.shape[0], int(top_c), _ptr(err), _ptr(ch), _ptr(cc),
                                        _ptr(status), _stream())
     _check(code, "iq_encode_candidates")

@@ -68,16 +68,29 @@ int grid_max(iq_format_t fmt) { return fmt == IQ_FMT_IQ2_XS ? 512 : 2048; }
 
 int num_choices(iq_format_t fmt) { return fmt == IQ_FMT_IQ1_M ? 8 : 16; }
 
-hipError_t launch_encode(iq_format_t fmt, const float* w, const float* importance, const float* grid,
-                         int32_t grid_size, const uint16_t* scales, const int32_t* choices,
-                         uint8_t* out, float* xhat, int mode, int32_t* status,
-                         const iqk::BlockGeom& g, hipStream_t stream)
+// Bytes per weight value, 0 for an unknown type.
+size_t dtype_bytes(iq_dtype_t t)
+{
+    switch (t) {
+    case IQ_DTYPE_F32: return 4;
+    case IQ_DTYPE_BF16: return 2;
+    case IQ_DTYPE_F16: return 2;
+    case IQ_DTYPE_F64: return 8;
+    }
+    return 0;
+}
+
+hipError_t launch_encode(iq_format_t fmt, iq_dtype_t wdtype, const void* w,
+                         const float* importance, const float* grid, int32_t grid_size,
+                         const uint16_t* scales, const int32_t* choices, uint8_t* out,
+                         float* xhat, int mode, int32_t* status, const iqk::BlockGeom& g,
+                         hipStream_t stream)
 {
     return fmt == IQ_FMT_IQ2_XS
-        ? iqk::launch_iq2xs_encode(w, importance, grid, grid_size, scales, choices, out, xhat, mode,
-                                   status, g, stream)
-        : iqk::launch_iq1_encode((int)fmt, w, importance, grid, grid_size, scales, choices, out,
-                                 xhat, mode, status, g, stream);
+        ? iqk::launch_iq2xs_encode((int)wdtype, w, importance, grid, grid_size, scales, choices,
+                                   out, xhat, mode, status, g, stream)
+        : iqk::launch_iq1_encode((int)fmt, (int)wdtype, w, importance, grid, grid_size, scales,
+                                 choices, out, xhat, mode, status, g, stream);
 }
 
 }  // namespace
@@ -118,10 +131,10 @@ const char* iq_status_str(iq_status_t st)
     return "unknown status";
 }
 
-iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t rows, int64_t cols,
-                      const float* importance, const float* grid, int32_t grid_size,
-                      const uint16_t* scales, const int32_t* choices, uint8_t* out,
-                      int32_t* status, hipStream_t stream)
+iq_status_t iq_encode(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t batch,
+                      int64_t rows, int64_t cols, const float* importance, const float* grid,
+                      int32_t grid_size, const uint16_t* scales, const int32_t* choices,
+                      uint8_t* out, int32_t* status, hipStream_t stream)
 {
     if (!known_format(fmt)) return IQ_ERR_FORMAT;
     iqk::BlockGeom g;
@@ -129,20 +142,22 @@ iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t ro
     if (st) return st;
     if (!w || !grid || !out || !status) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
+    if (dtype_bytes(wdtype) == 0) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(out, 2) || (scales && !aligned(scales, 2)) || (choices && !aligned(choices, 4)) ||
         !aligned(status, 4))
         return IQ_ERR_ARG;
     st = check_device(&g);
     if (st) return st;
-    return from_hip(launch_encode(fmt, w, importance, grid, grid_size, scales, choices, out,
-                                  nullptr, iqk::kModePayload, status, g, stream));
+    return from_hip(launch_encode(fmt, wdtype, w, importance, grid, grid_size, scales, choices,
+                                  out, nullptr, iqk::kModePayload, status, g, stream));
 }
 
-iq_status_t iq_encode_every_choice(iq_format_t fmt, const float* w, int64_t batch, int64_t rows,
-                                   int64_t cols, const float* importance, const float* grid,
-                                   int32_t grid_size, const uint16_t* scales, uint8_t* out,
-                                   int32_t* status, hipStream_t stream)
+iq_status_t iq_encode_every_choice(iq_format_t fmt, iq_dtype_t wdtype, const void* w,
+                                   int64_t batch, int64_t rows, int64_t cols,
+                                   const float* importance, const float* grid, int32_t grid_size,
+                                   const uint16_t* scales, uint8_t* out, int32_t* status,
+                                   hipStream_t stream)
 {
     if (!known_format(fmt)) return IQ_ERR_FORMAT;
     iqk::BlockGeom g;
@@ -150,17 +165,18 @@ iq_status_t iq_encode_every_choice(iq_format_t fmt, const float* w, int64_t batc
     if (st) return st;
     if (!w || !grid || !out || !status) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
+    if (dtype_bytes(wdtype) == 0) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(out, 2) || (scales && !aligned(scales, 2)) || !aligned(status, 4))
         return IQ_ERR_ARG;
     st = check_device(&g);
     if (st) return st;
-    return from_hip(launch_encode(fmt, w, importance, grid, grid_size, scales, nullptr, out,
-                                  nullptr, iqk::kModeEvery, status, g, stream));
+    return from_hip(launch_encode(fmt, wdtype, w, importance, grid, grid_size, scales, nullptr,
+                                  out, nullptr, iqk::kModeEvery, status, g, stream));
 }
 
-iq_status_t iq_fake_quant(iq_format_t fmt, const float* w, int64_t batch, int64_t rows,
-                          int64_t cols, const float* importance, const float* grid,
+iq_status_t iq_fake_quant(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t batch,
+                          int64_t rows, int64_t cols, const float* importance, const float* grid,
                           int32_t grid_size, const uint16_t* scales, const int32_t* choices,
                           float* xhat, uint8_t* out, int32_t* status, hipStream_t stream)
 {
@@ -170,6 +186,7 @@ iq_status_t iq_fake_quant(iq_format_t fmt, const float* w, int64_t batch, int64_
     if (st) return st;
     if (!w || !grid || !xhat || !status) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
+    if (dtype_bytes(wdtype) == 0) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(xhat, 16) || (out && !aligned(out, 2)) || (scales && !aligned(scales, 2)) ||
         (choices && !aligned(choices, 4)) || !aligned(status, 4))
@@ -177,12 +194,13 @@ iq_status_t iq_fake_quant(iq_format_t fmt, const float* w, int64_t batch, int64_
     // The decoded values may not overlap the weights: a block's values are
     // written while the other half of the block may still be reading them.
     const uintptr_t w0 = reinterpret_cast<uintptr_t>(w), x0 = reinterpret_cast<uintptr_t>(xhat);
-    const uintptr_t bytes = static_cast<uintptr_t>(g.nblocks) * 256u * sizeof(float);
-    if (x0 < w0 + bytes && w0 < x0 + bytes) return IQ_ERR_ARG;
+    const uintptr_t wbytes = static_cast<uintptr_t>(g.nblocks) * 256u * dtype_bytes(wdtype);
+    const uintptr_t xbytes = static_cast<uintptr_t>(g.nblocks) * 256u * sizeof(float);
+    if (x0 < w0 + wbytes && w0 < x0 + xbytes) return IQ_ERR_ARG;
     st = check_device(&g);
     if (st) return st;
-    return from_hip(launch_encode(fmt, w, importance, grid, grid_size, scales, choices, out, xhat,
-                                  iqk::kModeFake, status, g, stream));
+    return from_hip(launch_encode(fmt, wdtype, w, importance, grid, grid_size, scales, choices,
+                                  out, xhat, iqk::kModeFake, status, g, stream));
 }
 
 iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, int64_t rows,
@@ -201,10 +219,11 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
     return from_hip(iqk::launch_dequant((int)fmt, packed, grid, grid_size, out, status, g, stream));
 }
 
-iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, int64_t cols,
-                                 const float* importance, const float* grid, int32_t grid_size,
-                                 int32_t top_c, float* cand_err, int32_t* cand_choice,
-                                 uint16_t* cand_codes, int32_t* status, hipStream_t stream)
+iq_status_t iq_encode_candidates(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t rows,
+                                 int64_t cols, const float* importance, const float* grid,
+                                 int32_t grid_size, int32_t top_c, float* cand_err,
+                                 int32_t* cand_choice, uint16_t* cand_codes, int32_t* status,
+                                 hipStream_t stream)
 {
     if (!known_format(fmt)) return IQ_ERR_FORMAT;
     iqk::BlockGeom g;
@@ -213,6 +232,7 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, 
     if (!w || !grid || !cand_err || !cand_choice || !status) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (top_c < 1 || top_c > num_choices(fmt)) return IQ_ERR_ARG;
+    if (dtype_bytes(wdtype) == 0) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(cand_err, 16) || !aligned(cand_choice, 4) ||
         (cand_codes && !aligned(cand_codes, 2)) || !aligned(status, 4))
@@ -220,11 +240,12 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, 
     st = check_device(&g);
     if (st) return st;
     if (fmt != IQ_FMT_IQ2_XS)
-        return from_hip(iqk::launch_iq1_candidates((int)fmt, w, importance, grid, grid_size, top_c,
-                                                   cand_err, cand_choice, cand_codes, status, g,
-                                                   stream));
-    return from_hip(iqk::launch_iq2xs_candidates(w, importance, grid, grid_size, top_c, cand_err,
-                                                 cand_choice, cand_codes, status, g, stream));
+        return from_hip(iqk::launch_iq1_candidates((int)fmt, (int)wdtype, w, importance, grid,
+                                                   grid_size, top_c, cand_err, cand_choice,
+                                                   cand_codes, status, g, stream));
+    return from_hip(iqk::launch_iq2xs_candidates((int)wdtype, w, importance, grid, grid_size, top_c,
+                                                 cand_err, cand_choice, cand_codes, status, g,
+                                                 stream));
 }
 
 iq_status_t iq_choice_search(const float* H, const float* cand_err, int64_t rows, int32_t G,

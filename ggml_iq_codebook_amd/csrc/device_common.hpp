@@ -1,6 +1,6 @@
 // device_common.hpp -- small device helpers shared by the HIP kernels of
 // libiqcodec.so: fp16 conversion, bf16 operand splitting, status reporting,
-// block geometry.
+// block geometry, reading weights of every storage type as fp32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -92,5 +92,95 @@ __device__ __forceinline__ v8bf as_v8bf(uint4 u)
 {
     return __builtin_bit_cast(v8bf, u);
 }
+
+// One 256-value block of the weight in its storage type (iq_dtype_t), read as
+// fp32: bf16 and fp16 convert exactly, fp64 rounds to nearest even.  quad(q)
+// reads values 4q..4q+3, group(g, v) values 8g..8g+7, one(i) value i (the
+// block start is 16-byte aligned in every type).
+template <int kDT>
+struct WeightBlock;
+
+template <>
+struct WeightBlock<IQ_DTYPE_F32> {
+    const float* p;
+    __device__ __forceinline__ WeightBlock(const void* base, int64_t blk)
+        : p(static_cast<const float*>(base) + blk * kBlockElems) {}
+    __device__ __forceinline__ float one(int i) const { return p[i]; }
+    __device__ __forceinline__ float4 quad(int q) const
+    {
+        return reinterpret_cast<const float4*>(p)[q];
+    }
+    __device__ __forceinline__ void group(int g, float (&v)[8]) const
+    {
+        const float4* xp = reinterpret_cast<const float4*>(p + g * 8);
+        const float4 a = xp[0], b = xp[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
+template <>
+struct WeightBlock<IQ_DTYPE_BF16> {
+    const uint16_t* p;
+    __device__ __forceinline__ WeightBlock(const void* base, int64_t blk)
+        : p(static_cast<const uint16_t*>(base) + blk * kBlockElems) {}
+    __device__ __forceinline__ static float lo(uint32_t u) { return __uint_as_float(u << 16); }
+    __device__ __forceinline__ static float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+    __device__ __forceinline__ float one(int i) const { return lo(p[i]); }
+    __device__ __forceinline__ float4 quad(int q) const
+    {
+        const uint2 u = reinterpret_cast<const uint2*>(p)[q];
+        return make_float4(lo(u.x), hi(u.x), lo(u.y), hi(u.y));
+    }
+    __device__ __forceinline__ void group(int g, float (&v)[8]) const
+    {
+        const uint4 u = reinterpret_cast<const uint4*>(p)[g];
+        v[0] = lo(u.x); v[1] = hi(u.x); v[2] = lo(u.y); v[3] = hi(u.y);
+        v[4] = lo(u.z); v[5] = hi(u.z); v[6] = lo(u.w); v[7] = hi(u.w);
+    }
+};
+
+template <>
+struct WeightBlock<IQ_DTYPE_F16> {
+    const uint16_t* p;
+    __device__ __forceinline__ WeightBlock(const void* base, int64_t blk)
+        : p(static_cast<const uint16_t*>(base) + blk * kBlockElems) {}
+    __device__ __forceinline__ static float cv(uint32_t h)
+    {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
+    }
+    __device__ __forceinline__ float one(int i) const { return cv(p[i]); }
+    __device__ __forceinline__ float4 quad(int q) const
+    {
+        const uint2 u = reinterpret_cast<const uint2*>(p)[q];
+        return make_float4(cv(u.x), cv(u.x >> 16), cv(u.y), cv(u.y >> 16));
+    }
+    __device__ __forceinline__ void group(int g, float (&v)[8]) const
+    {
+        const uint4 u = reinterpret_cast<const uint4*>(p)[g];
+        v[0] = cv(u.x); v[1] = cv(u.x >> 16); v[2] = cv(u.y); v[3] = cv(u.y >> 16);
+        v[4] = cv(u.z); v[5] = cv(u.z >> 16); v[6] = cv(u.w); v[7] = cv(u.w >> 16);
+    }
+};
+
+template <>
+struct WeightBlock<IQ_DTYPE_F64> {
+    const double* p;
+    __device__ __forceinline__ WeightBlock(const void* base, int64_t blk)
+        : p(static_cast<const double*>(base) + blk * kBlockElems) {}
+    __device__ __forceinline__ float one(int i) const { return (float)p[i]; }
+    __device__ __forceinline__ float4 quad(int q) const
+    {
+        const double2* dp = reinterpret_cast<const double2*>(p) + 2 * q;
+        const double2 a = dp[0], b = dp[1];
+        return make_float4((float)a.x, (float)a.y, (float)b.x, (float)b.y);
+    }
+    __device__ __forceinline__ void group(int g, float (&v)[8]) const
+    {
+        const float4 a = quad(2 * g), b = quad(2 * g + 1);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
 
 }  // namespace iqk

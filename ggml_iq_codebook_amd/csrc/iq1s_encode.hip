@@ -70,7 +70,7 @@ constexpr int kBlockBytes = 50;
 constexpr int kBlockBytesM = 56;
 
 struct Iq1sArgs {
-    const float* w;
+    const void* w;           // weights in the storage type the kernel is built for
     const float* imp;
     const float* grid;
     const uint16_t* scales;
@@ -89,7 +89,8 @@ struct Iq1sArgs {
 
 // The 8 values and importance weights of group g of a block (zeros and ones
 // for a rejected block, so the sweep stays finite).
-__device__ __forceinline__ void load_group(const float* xblk, const float* wblk, int g, bool zero,
+template <class XB>
+__device__ __forceinline__ void load_group(const XB& xb, const float* wblk, int g, bool zero,
                                            float (&x)[8], float (&w)[8])
 {
     if (zero) {
@@ -97,10 +98,7 @@ __device__ __forceinline__ void load_group(const float* xblk, const float* wblk,
         for (int j = 0; j < 8; ++j) { x[j] = 0.0f; w[j] = 1.0f; }
         return;
     }
-    const float4* xp = reinterpret_cast<const float4*>(xblk + g * 8);
-    const float4 x0 = xp[0], x1 = xp[1];
-    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    xb.group(g, x);
     if (wblk) {
         const float4* wp = reinterpret_cast<const float4*>(wblk + g * 8);
         const float4 w0 = wp[0], w1 = wp[1];
@@ -118,15 +116,15 @@ __device__ __forceinline__ void load_group(const float* xblk, const float* wblk,
 // recomputed in fp32 from the group's values and weights (read again from
 // memory rather than held through the sweep).  Returns the entry, writes its
 // key.
-template <int kChunkTiles>
+template <int kChunkTiles, class XB>
 __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, int kbs, int t0,
-                                      int nt, int cs, const float* xblk, const float* wblk, int g,
+                                      int nt, int cs, const XB& xb, const float* wblk, int g,
                                       bool zero_block, float w64, float b4, float inv_d,
                                       float* key_out)
 {
     float x[8], w[8];
     __asm__ volatile("" ::: "memory");
-    load_group(xblk, wblk, g, zero_block, x, w);
+    load_group(xb, wblk, g, zero_block, x, w);
     const float mk = (float)(2 * (cs & 7) + 1);
     const float dl = (cs >> 3) ? -0.25f : 0.25f;      // 2*delta
     const float bd = (cs >> 3) ? b4 : -b4;
@@ -158,12 +156,12 @@ __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, 
 // Weighted squared error of group g against d*(2k+1)*(q + delta) for entry
 // e and choice cs = k + 8*shift, in fp64 from its definition: the sum of
 // w*(x - s*(q + delta))^2, delta = +1/8 for shift 0 and -1/8 for shift 1.
-template <int kChunk>
-__device__ __forceinline__ double group_error64(const float* xblk, const float* wblk, int g,
+template <int kChunk, class XB>
+__device__ __forceinline__ double group_error64(const XB& xb, const float* wblk, int g,
                                                 bool zero, const uint4* sq, int e, int cs, float d)
 {
     float x[8], w[8];
-    load_group(xblk, wblk, g, zero, x, w);
+    load_group(xb, wblk, g, zero, x, w);
     const uint4 u = sq[e + e / kChunk];
     const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
     const double sc = (double)d * (double)(2 * (cs & 7) + 1);
@@ -178,7 +176,9 @@ __device__ __forceinline__ double group_error64(const float* xblk, const float* 
     return err;
 }
 
-template <int kFmt, int kMode>
+// kFmt: IQ_FMT_IQ1_S or IQ_FMT_IQ1_M; kMode: EncodeMode; kDT: the weight's
+// iq_dtype_t.
+template <int kFmt, int kMode, int kDT>
 __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 {
     // IQ1_M: 56-byte blocks, 8 local scales per two groups (16 choice
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         if (blk >= a.g.nblocks) continue;                      // wave-uniform
         const int64_t bt = blk / a.g.blocks_per_batch;
         const int64_t cb = blk % a.g.blocks_per_row;
-        const float* xblk = a.w + blk * kBlockElems;
+        const WeightBlock<kDT> xb(a.w, blk);
         const float* wblk = a.imp ? a.imp + bt * a.g.cols + cb * kBlockElems : nullptr;
 
         // Whole-block checks and amax (each lane reads 4 of the 256 values);
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         int err = 0;
         float amax = 0.0f, ssq = 0.0f;
         {
-            const float4 xv = reinterpret_cast<const float4*>(xblk)[lane];
+            const float4 xv = xb.quad(lane);
             const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         // The lane's group: values, weights, sums, and its K slice of the
         // three-way bf16 split of -2*w*x and w (slice 3 is zero padding).
         float x[8], w[8];
-        load_group(xblk, wblk, g, zero_block, x, w);
+        load_group(xb, wblk, g, zero_block, x, w);
         const float inv_d = zero_block ? 1.0f : 1.0f / d;
         float W = 0.0f, B = 0.0f;
         uint32_t bwx[8], bw[8];
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 const int kbs = __builtin_ctzll(holders) >> 4;
                 const int tch = __shfl(tchunk, col + 16 * kbs);
                 idx = rescan<kChunkTiles>(sq, tch, kbs, kb * (kChunkTiles / 4), kChunkTiles / 4, cs,
-                                          xblk, wblk, g, zero_block, w64, b4, inv_d, &key);
+                                          xb, wblk, g, zero_block, w64, b4, inv_d, &key);
 #pragma unroll
                 for (int o = 16; o <= 32; o <<= 1) {
                     const float ok = __shfl_xor(key, o);
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                     if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
                 }
             } else {
-                idx = rescan<kChunkTiles>(sq, tchunk, kb, 0, kChunkTiles, cs, xblk, wblk, g,
+                idx = rescan<kChunkTiles>(sq, tchunk, kb, 0, kChunkTiles, cs, xb, wblk, g,
                                           zero_block, w64, b4, inv_d, &key);
 #pragma unroll
                 for (int o = 16; o <= 32; o <<= 1) {
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             if (refine) {
                 // The choice unit's fp64 error: its four groups (IQ1_S
                 // sub-block) or two (IQ1_M scale group), adjacent columns.
-                double e = group_error64<kChunk>(xblk, wblk, g, zero_block, sq, idx, cs, d);
+                double e = group_error64<kChunk>(xb, wblk, g, zero_block, sq, idx, cs, d);
                 e += __shfl_xor(e, 1);
                 if (!kM) e += __shfl_xor(e, 2);
                 if (it == 0) { idx_alt = idx; err_alt = e; continue; }
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                     const int part = kM ? (g & 1) : lq;
                     const int64_t base = (blk * kGroups + unit) * a.top_c + it;    // [block][unit][r]
                     float xo[8], wo[8];
-                    load_group(xblk, wblk, g, rejected, xo, wo);
+                    load_group(xb, wblk, g, rejected, xo, wo);
                     const float sk = f16_bits_to_f32(dh) * (float)(2 * (cs & 7) + 1);
                     const float delta = (cs >> 3) ? -0.125f : 0.125f;
                     const uint4 u = sq[idx + idx / kChunk];
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     }
 }
 
-template <int kFmt>
+template <int kFmt, int kDT>
 hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
 {
     // One workgroup per compute unit (the LDS holds one), or one per set of
@@ -666,40 +666,53 @@ hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
     const int64_t sets = (a.g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
     const dim3 grid((unsigned)(sets < a.g.cus ? sets : a.g.cus));
     if (mode == kModeEvery)
-        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeEvery>), grid, dim3(kThreads), 0, stream, a);
-    else if (mode == kModeFake)
-        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeFake>), grid, dim3(kThreads), 0, stream, a);
-    else if (mode == kModeCandidates)
-        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeCandidates>), grid, dim3(kThreads), 0,
+        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeEvery, kDT>), grid, dim3(kThreads), 0,
                            stream, a);
+    else if (mode == kModeFake)
+        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeFake, kDT>), grid, dim3(kThreads), 0,
+                           stream, a);
+    else if (mode == kModeCandidates)
+        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeCandidates, kDT>), grid, dim3(kThreads),
+                           0, stream, a);
     else
-        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModePayload>), grid, dim3(kThreads), 0, stream,
-                           a);
+        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModePayload, kDT>), grid, dim3(kThreads), 0,
+                           stream, a);
     return hipGetLastError();
+}
+
+template <int kFmt>
+hipError_t launch_dtype(const Iq1sArgs& a, int wdtype, int mode, hipStream_t stream)
+{
+    switch (wdtype) {
+    case IQ_DTYPE_BF16: return launch_fmt<kFmt, IQ_DTYPE_BF16>(a, mode, stream);
+    case IQ_DTYPE_F16: return launch_fmt<kFmt, IQ_DTYPE_F16>(a, mode, stream);
+    case IQ_DTYPE_F64: return launch_fmt<kFmt, IQ_DTYPE_F64>(a, mode, stream);
+    default: return launch_fmt<kFmt, IQ_DTYPE_F32>(a, mode, stream);
+    }
 }
 
 }  // namespace
 
-hipError_t launch_iq1_encode(int fmt, const float* w, const float* imp, const float* grid,
-                             int grid_size, const uint16_t* scales, const int32_t* choices,
-                             uint8_t* out, float* xhat, int mode, int32_t* status,
-                             const BlockGeom& g, hipStream_t stream)
+hipError_t launch_iq1_encode(int fmt, int wdtype, const void* w, const float* imp,
+                             const float* grid, int grid_size, const uint16_t* scales,
+                             const int32_t* choices, uint8_t* out, float* xhat, int mode,
+                             int32_t* status, const BlockGeom& g, hipStream_t stream)
 {
     Iq1sArgs a{w, imp, grid, scales, choices, out, xhat, nullptr, nullptr, nullptr, status, g,
                grid_size, 0};
-    return fmt == IQ_FMT_IQ1_M ? launch_fmt<IQ_FMT_IQ1_M>(a, mode, stream)
-                               : launch_fmt<IQ_FMT_IQ1_S>(a, mode, stream);
+    return fmt == IQ_FMT_IQ1_M ? launch_dtype<IQ_FMT_IQ1_M>(a, wdtype, mode, stream)
+                               : launch_dtype<IQ_FMT_IQ1_S>(a, wdtype, mode, stream);
 }
 
-hipError_t launch_iq1_candidates(int fmt, const float* w, const float* imp, const float* grid,
-                                 int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
-                                 uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
-                                 hipStream_t stream)
+hipError_t launch_iq1_candidates(int fmt, int wdtype, const void* w, const float* imp,
+                                 const float* grid, int grid_size, int top_c, float* cand_err,
+                                 int32_t* cand_choice, uint16_t* cand_codes, int32_t* status,
+                                 const BlockGeom& g, hipStream_t stream)
 {
     Iq1sArgs a{w, imp, grid, nullptr, nullptr, nullptr, nullptr, cand_err, cand_choice, cand_codes,
                status, g, grid_size, top_c};
-    return fmt == IQ_FMT_IQ1_M ? launch_fmt<IQ_FMT_IQ1_M>(a, kModeCandidates, stream)
-                               : launch_fmt<IQ_FMT_IQ1_S>(a, kModeCandidates, stream);
+    return fmt == IQ_FMT_IQ1_M ? launch_dtype<IQ_FMT_IQ1_M>(a, wdtype, kModeCandidates, stream)
+                               : launch_dtype<IQ_FMT_IQ1_S>(a, wdtype, kModeCandidates, stream);
 }
 
 }  // namespace iqk

@@ -57,7 +57,7 @@ constexpr int kMaxGrid = 512;
 constexpr int kBlockBytes = 74;
 
 struct Iq2xsArgs {
-    const float* w;
+    const void* w;           // weights in the storage type the kernel is built for
     const float* imp;
     const float* grid;
     const uint16_t* scales;
@@ -74,7 +74,8 @@ struct Iq2xsArgs {
     int top_c;
 };
 
-__device__ __forceinline__ void load_group(const float* xblk, const float* wblk, int g, bool zero,
+template <class XB>
+__device__ __forceinline__ void load_group(const XB& xb, const float* wblk, int g, bool zero,
                                            float (&x)[8], float (&w)[8])
 {
     if (zero) {
@@ -82,10 +83,7 @@ __device__ __forceinline__ void load_group(const float* xblk, const float* wblk,
         for (int j = 0; j < 8; ++j) { x[j] = 0.0f; w[j] = 1.0f; }
         return;
     }
-    const float4* xp = reinterpret_cast<const float4*>(xblk + g * 8);
-    const float4 x0 = xp[0], x1 = xp[1];
-    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    xb.group(g, x);
     if (wblk) {
         const float4* wp = reinterpret_cast<const float4*>(wblk + g * 8);
         const float4 w0 = wp[0], w1 = wp[1];
@@ -217,7 +215,8 @@ __device__ __forceinline__ int rescan(const float* __restrict__ sg, int chunk, i
     return idx;
 }
 
-template <int kMode>
+// kMode: EncodeMode; kDT: the weight's iq_dtype_t.
+template <int kMode, int kDT>
 __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 {
     constexpr bool kCandidates = kMode == kModeCandidates;
@@ -297,13 +296,13 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         if (blk >= a.g.nblocks) continue;                      // wave-uniform
         const int64_t bt = blk / a.g.blocks_per_batch;
         const int64_t cb = blk % a.g.blocks_per_row;
-        const float* xblk = a.w + blk * kBlockElems;
+        const WeightBlock<kDT> xb(a.w, blk);
         const float* wblk = a.imp ? a.imp + bt * a.g.cols + cb * kBlockElems : nullptr;
 
         int err = 0;
         float amax = 0.0f;
         {
-            const float4 xv = reinterpret_cast<const float4*>(xblk)[lane];
+            const float4 xv = xb.quad(lane);
             const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -353,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 
         // The lane's group: values, weights and signs.
         float x[8], w[8];
-        load_group(xblk, wblk, g, skip, x, w);
+        load_group(xb, wblk, g, skip, x, w);
         const int neg = group_signs(x, w);
         const float inv_d = skip ? 1.0f : 1.0f / d;
 
@@ -394,8 +393,8 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             // again rather than selected from registers.
             float bw0 = 1.0f, bw1 = 1.0f, bx0 = 0.0f, bx1 = 0.0f;
             if (!skip) {
-                bx0 = xblk[g * 8 + kb];
-                bx1 = xblk[g * 8 + kb + 4];
+                bx0 = xb.one(g * 8 + kb);
+                bx1 = xb.one(g * 8 + kb + 4);
                 if (wblk) { bw0 = wblk[g * 8 + kb]; bw1 = wblk[g * 8 + kb + 4]; }
             }
             float bp0 = bw0 * bx0, bp1 = bw1 * bx1;
@@ -421,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         // The rescans need the signed weighted values again; they are
         // rebuilt from memory rather than held through the sweep.
         __asm__ volatile("" ::: "memory");
-        load_group(xblk, wblk, g, skip, x, w);
+        load_group(xb, wblk, g, skip, x, w);
         float wxs[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -530,7 +529,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
                     const int i2 = pick(k2);
                     __asm__ volatile("" ::: "memory");
                     float xr[8], wr[8];
-                    load_group(xblk, wblk, g, skip, xr, wr);
+                    load_group(xb, wblk, g, skip, xr, wr);
                     const double dd = (double)d;
                     double e1 = group_error64(xr, wr, neg, sgrid + entry_off<kChunk>(i1),
                                               dd * (double)(2 * kstar + 1));
@@ -579,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             // decode to zero with entry 0 and no signs, so the order is k = 0, 1, ...
             const int C = a.top_c;
             float xo[8], wo[8];
-            load_group(xblk, wblk, g, bad_block, xo, wo);   // the original values
+            load_group(xb, wblk, g, bad_block, xo, wo);   // the original values
             int used = 0;
             for (int r = 0; r < C; ++r) {
                 int kr = -1;
@@ -652,35 +651,53 @@ unsigned persistent_wgs(const BlockGeom& g)
     return (unsigned)(sets < g.cus ? sets : g.cus);
 }
 
-}  // namespace
-
-hipError_t launch_iq2xs_encode(const float* w, const float* imp, const float* grid, int grid_size,
-                               const uint16_t* scales, const int32_t* choices, uint8_t* out,
-                               float* xhat, int mode, int32_t* status, const BlockGeom& g,
-                               hipStream_t stream)
+template <int kDT>
+hipError_t launch_mode(const Iq2xsArgs& a, int mode, hipStream_t stream)
 {
-    Iq2xsArgs a{w, imp, grid, scales, choices, out, xhat, nullptr, nullptr, nullptr, status, g,
-                grid_size, 0};
-    const unsigned wgs = persistent_wgs(g);
+    const unsigned wgs = persistent_wgs(a.g);
     if (mode == kModeEvery)
-        hipLaunchKernelGGL(iq2xs_kernel<kModeEvery>, dim3(wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((iq2xs_kernel<kModeEvery, kDT>), dim3(wgs), dim3(kThreads), 0, stream, a);
     else if (mode == kModeFake)
-        hipLaunchKernelGGL(iq2xs_kernel<kModeFake>, dim3(wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((iq2xs_kernel<kModeFake, kDT>), dim3(wgs), dim3(kThreads), 0, stream, a);
+    else if (mode == kModeCandidates)
+        hipLaunchKernelGGL((iq2xs_kernel<kModeCandidates, kDT>), dim3(wgs), dim3(kThreads), 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL(iq2xs_kernel<kModePayload>, dim3(wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((iq2xs_kernel<kModePayload, kDT>), dim3(wgs), dim3(kThreads), 0, stream,
+                           a);
     return hipGetLastError();
 }
 
-hipError_t launch_iq2xs_candidates(const float* w, const float* imp, const float* grid,
+hipError_t launch_dtype(const Iq2xsArgs& a, int wdtype, int mode, hipStream_t stream)
+{
+    switch (wdtype) {
+    case IQ_DTYPE_BF16: return launch_mode<IQ_DTYPE_BF16>(a, mode, stream);
+    case IQ_DTYPE_F16: return launch_mode<IQ_DTYPE_F16>(a, mode, stream);
+    case IQ_DTYPE_F64: return launch_mode<IQ_DTYPE_F64>(a, mode, stream);
+    default: return launch_mode<IQ_DTYPE_F32>(a, mode, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_iq2xs_encode(int wdtype, const void* w, const float* imp, const float* grid,
+                               int grid_size, const uint16_t* scales, const int32_t* choices,
+                               uint8_t* out, float* xhat, int mode, int32_t* status,
+                               const BlockGeom& g, hipStream_t stream)
+{
+    Iq2xsArgs a{w, imp, grid, scales, choices, out, xhat, nullptr, nullptr, nullptr, status, g,
+                grid_size, 0};
+    return launch_dtype(a, wdtype, mode, stream);
+}
+
+hipError_t launch_iq2xs_candidates(int wdtype, const void* w, const float* imp, const float* grid,
                                    int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
                                    uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
                                    hipStream_t stream)
 {
     Iq2xsArgs a{w, imp, grid, nullptr, nullptr, nullptr, nullptr, cand_err, cand_choice,
                 cand_codes, status, g, grid_size, top_c};
-    const unsigned wgs = persistent_wgs(g);
-    hipLaunchKernelGGL(iq2xs_kernel<kModeCandidates>, dim3(wgs), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch_dtype(a, wdtype, kModeCandidates, stream);
 }
 
 }  // namespace iqk

@@ -24,22 +24,23 @@ struct BlockGeom {
 enum EncodeMode { kModePayload = 0, kModeEvery = 1, kModeFake = 2, kModeCandidates = 3 };
 
 // IQ1_S and IQ1_M (fmt = IQ_FMT_IQ1_S or IQ_FMT_IQ1_M) share one kernel.
-hipError_t launch_iq1_encode(int fmt, const float* w, const float* imp, const float* grid,
-                             int grid_size, const uint16_t* scales, const int32_t* choices,
-                             uint8_t* out, float* xhat, int mode, int32_t* status,
-                             const BlockGeom& g, hipStream_t stream);
+// wdtype: the weight's iq_dtype_t (w points at values of that type).
+hipError_t launch_iq1_encode(int fmt, int wdtype, const void* w, const float* imp,
+                             const float* grid, int grid_size, const uint16_t* scales,
+                             const int32_t* choices, uint8_t* out, float* xhat, int mode,
+                             int32_t* status, const BlockGeom& g, hipStream_t stream);
 
-hipError_t launch_iq2xs_encode(const float* w, const float* imp, const float* grid, int grid_size,
-                               const uint16_t* scales, const int32_t* choices, uint8_t* out,
-                               float* xhat, int mode, int32_t* status, const BlockGeom& g,
-                               hipStream_t stream);
+hipError_t launch_iq2xs_encode(int wdtype, const void* w, const float* imp, const float* grid,
+                               int grid_size, const uint16_t* scales, const int32_t* choices,
+                               uint8_t* out, float* xhat, int mode, int32_t* status,
+                               const BlockGeom& g, hipStream_t stream);
 
-hipError_t launch_iq1_candidates(int fmt, const float* w, const float* imp, const float* grid,
-                                 int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
-                                 uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
-                                 hipStream_t stream);
+hipError_t launch_iq1_candidates(int fmt, int wdtype, const void* w, const float* imp,
+                                 const float* grid, int grid_size, int top_c, float* cand_err,
+                                 int32_t* cand_choice, uint16_t* cand_codes, int32_t* status,
+                                 const BlockGeom& g, hipStream_t stream);
 
-hipError_t launch_iq2xs_candidates(const float* w, const float* imp, const float* grid,
+hipError_t launch_iq2xs_candidates(int wdtype, const void* w, const float* imp, const float* grid,
                                    int grid_size, int top_c, float* cand_err, int32_t* cand_choice,
                                    uint16_t* cand_codes, int32_t* status, const BlockGeom& g,
                                    hipStream_t stream);

@@ -30,9 +30,10 @@
  *     code to land sticks; the library never clears `*status`: the caller
  *     zeroes it.  Blocks with a data error are written as zeros.
  *   - Concurrent calls that share `status` or an output buffer race.
- *   - Layouts are row-major and contiguous.  Weights are fp32 [batch][rows][cols]
- *     with cols a positive multiple of 256; a 256-value block is cols/256 of a
- *     row; the packed payload is [batch][rows][cols/256][block_bytes] uint8.
+ *   - Layouts are row-major and contiguous.  Weights are [batch][rows][cols]
+ *     with cols a positive multiple of 256, stored as fp32, bf16, fp16 or fp64
+ *     (iq_dtype_t); a 256-value block is cols/256 of a row; the packed payload
+ *     is [batch][rows][cols/256][block_bytes] uint8.
  */
 #ifndef IQ_CODEC_H
 #define IQ_CODEC_H
@@ -51,6 +52,18 @@ typedef enum {
                            16 values, a shift per group, d in the top nibbles of the scale words */
 } iq_format_t;
 
+/* Storage type of the weights given to the encode calls (#2450 code review:
+ * the encoders take float32, float64, float16 and bfloat16 weights).  Every
+ * value is read as fp32 -- exactly for bf16 and fp16, rounded to nearest even
+ * for fp64 (an fp64 value beyond fp32's range becomes infinite and its block
+ * is rejected as non-finite) -- and the encode is that of the fp32 values. */
+typedef enum {
+    IQ_DTYPE_F32 = 0,
+    IQ_DTYPE_BF16 = 1,
+    IQ_DTYPE_F16 = 2,
+    IQ_DTYPE_F64 = 3
+} iq_dtype_t;
+
 typedef enum {
     IQ_OK = 0,
     IQ_ERR_NULL = 1,          /* a required pointer is NULL */
@@ -62,7 +75,8 @@ typedef enum {
     IQ_ERR_IMPORTANCE = 6,    /* (device) an importance value is negative or not finite */
     IQ_ERR_SCALE_RANGE = 7,   /* (device) super-block scale beyond fp16, or a pinned scale
                                  that is negative, infinite or NaN */
-    IQ_ERR_ARG = 8,           /* a count out of range (top_c, G, C, sweeps, choice values) */
+    IQ_ERR_ARG = 8,           /* a count out of range (top_c, G, C, sweeps, choice values),
+                                 an unknown weight dtype, a misaligned pointer */
     IQ_ERR_CODE = 9,          /* (device) a payload grid index beyond grid_size */
     IQ_ERR_HIP = 10,          /* a HIP runtime call or kernel launch failed */
     IQ_ERR_DEVICE = 11        /* the current device is not a gfx950 GPU */
@@ -95,7 +109,8 @@ const char* iq_status_str(iq_status_t st);
  * groups of a 32-value sub-block; #2525/#2512: IQ2_XS signs with the weakest
  * element flipped for even parity).
  *
- *   w          [batch][rows][cols] fp32 weights.
+ *   wdtype     the storage type of w (see iq_dtype_t).
+ *   w          [batch][rows][cols] weights in wdtype, 16-byte aligned.
  *   importance NULL (uniform) or [batch][cols] fp32, finite and >= 0, one value
  *              per input column (#2723).
  *   grid       [grid_size][8] fp32.  IQ1_S: values in {-1, 0, +1};
@@ -118,10 +133,10 @@ const char* iq_status_str(iq_status_t st);
  * Errors: IQ_ERR_NULL, IQ_ERR_FORMAT, IQ_ERR_SHAPE, IQ_ERR_GRID, IQ_ERR_DEVICE,
  * IQ_ERR_HIP synchronously; the device codes through *status.
  */
-iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t rows, int64_t cols,
-                      const float* importance, const float* grid, int32_t grid_size,
-                      const uint16_t* scales, const int32_t* choices, uint8_t* out,
-                      int32_t* status, hipStream_t stream);
+iq_status_t iq_encode(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t batch,
+                      int64_t rows, int64_t cols, const float* importance, const float* grid,
+                      int32_t grid_size, const uint16_t* scales, const int32_t* choices,
+                      uint8_t* out, int32_t* status, hipStream_t stream);
 
 /*
  * iq_encode_every_choice -- the payload under every choice from one sweep
@@ -129,15 +144,16 @@ iq_status_t iq_encode(iq_format_t fmt, const float* w, int64_t batch, int64_t ro
  * byte, the iq_encode payload with every choice group forced to c.  The input
  * of the local-Hessian search, which scores each choice's decoded error.
  *
- *   w, importance, grid, scales, status: as iq_encode.
+ *   wdtype, w, importance, grid, scales, status: as iq_encode.
  *   out  [num_choices][batch][rows][cols/256][block_bytes] uint8 (choice-major;
  *        16 payloads for IQ1_S and IQ2_XS, 8 for IQ1_M).
  * Errors as iq_encode; a block with a data error is zero in all 16 payloads.
  */
-iq_status_t iq_encode_every_choice(iq_format_t fmt, const float* w, int64_t batch, int64_t rows,
-                                   int64_t cols, const float* importance, const float* grid,
-                                   int32_t grid_size, const uint16_t* scales, uint8_t* out,
-                                   int32_t* status, hipStream_t stream);
+iq_status_t iq_encode_every_choice(iq_format_t fmt, iq_dtype_t wdtype, const void* w,
+                                   int64_t batch, int64_t rows, int64_t cols,
+                                   const float* importance, const float* grid, int32_t grid_size,
+                                   const uint16_t* scales, uint8_t* out, int32_t* status,
+                                   hipStream_t stream);
 
 /*
  * iq_fake_quant -- encode and decode in one pass: the fp32 weights the
@@ -147,14 +163,15 @@ iq_status_t iq_encode_every_choice(iq_format_t fmt, const float* w, int64_t batc
  * re-encode under pinned d).  xhat is, bit for bit,
  * iq_dequant(iq_encode(...)) with the same arguments.
  *
- *   w, importance, grid, scales, choices, status: as iq_encode.
- *   xhat  [batch][rows][cols] fp32 output; may not overlap w.
+ *   wdtype, w, importance, grid, scales, choices, status: as iq_encode.
+ *   xhat  [batch][rows][cols] fp32 output (whatever wdtype is); may not
+ *         overlap w.
  *   out   NULL, or the payload [batch][rows][cols/256][block_bytes] as well.
  * Errors as iq_encode (IQ_ERR_ARG also when xhat overlaps w); a block with a
  * data error decodes to zeros.
  */
-iq_status_t iq_fake_quant(iq_format_t fmt, const float* w, int64_t batch, int64_t rows,
-                          int64_t cols, const float* importance, const float* grid,
+iq_status_t iq_fake_quant(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t batch,
+                          int64_t rows, int64_t cols, const float* importance, const float* grid,
                           int32_t grid_size, const uint16_t* scales, const int32_t* choices,
                           float* xhat, uint8_t* out, int32_t* status, hipStream_t stream);
 
@@ -182,12 +199,15 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
  * input of the local-Hessian choice search (#3158 step 1, #3159 every-choice
  * encode): for every choice group of every 256-column block (IQ2_XS and
  * IQ1_M: 16 scale groups of 16 columns, choice = local scale k; IQ1_S: 8
- * sub-blocks of 32 columns, choice c = k + 8*deltabit), the top_c choices ordered by
- * (weighted cost, choice), each with its grid codes and its error vector
- * xhat - x over the group's columns (xhat exact in fp32, one rounding).  A
- * zero super-block scale orders the choices 0, 1, ... with entry 0.
+ * sub-blocks of 32 columns, choice c = k + 8*deltabit), the top_c choices
+ * ordered by (weighted cost, choice), each with its grid codes and its error
+ * vector xhat - x over the group's columns (xhat formed exactly, one rounding
+ * of xhat - x).  A zero super-block scale orders the choices 0, 1, ... with
+ * entry 0.
  *
- *   w           [rows][cols] fp32; importance NULL or [cols]; grid as iq_encode.
+ *   wdtype, w   [rows][cols] weights in wdtype (as iq_encode); importance NULL
+ *               or [cols]; grid as iq_encode.  x in xhat - x is the weight read
+ *               as fp32.
  *   top_c       1..num_choices (16, or 8 for IQ1_M).
  *   cand_err    IQ2_XS, IQ1_M [rows][cols/256][16][top_c][16],
  *               IQ1_S [rows][cols/256][8][top_c][32] fp32.
@@ -197,10 +217,11 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
  *               IQ1_S [..][top_c][4] uint16 (the grid index of each group).
  *   status      one int32, required; a block with a data error is all zeros.
  */
-iq_status_t iq_encode_candidates(iq_format_t fmt, const float* w, int64_t rows, int64_t cols,
-                                 const float* importance, const float* grid, int32_t grid_size,
-                                 int32_t top_c, float* cand_err, int32_t* cand_choice,
-                                 uint16_t* cand_codes, int32_t* status, hipStream_t stream);
+iq_status_t iq_encode_candidates(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t rows,
+                                 int64_t cols, const float* importance, const float* grid,
+                                 int32_t grid_size, int32_t top_c, float* cand_err,
+                                 int32_t* cand_choice, uint16_t* cand_codes, int32_t* status,
+                                 hipStream_t stream);
 
 /*
  * iq_choice_search -- local-Hessian choice search of one 256-column block

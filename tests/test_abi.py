@@ -59,18 +59,24 @@ FAKE = P(0x100000)      # never dereferenced: validation fails before any device
 
 def test_encode_argument_errors_need_no_gpu(lib):
     enc = lib.iq_encode
-    # fmt, w, batch, rows, cols, imp, grid, grid_size, scales, choices, out, status, stream
-    assert enc(5, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 2
-    assert enc(0, None, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 1
-    assert enc(0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None, None) == 1
-    assert enc(0, FAKE, 1, 1, 200, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
-    assert enc(0, FAKE, 1, 0, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
-    assert enc(0, FAKE, 0, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
-    assert enc(0, FAKE, 1, 1 << 40, 1 << 20, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
-    assert enc(0, FAKE, 1, 1, 256, None, FAKE, 0, None, None, FAKE, FAKE, None) == 4
-    assert enc(0, FAKE, 1, 1, 256, None, FAKE, 2049, None, None, FAKE, FAKE, None) == 4
-    assert enc(1, FAKE, 1, 1, 256, None, FAKE, 513, None, None, FAKE, FAKE, None) == 4
-    assert enc(0, P(0x100004), 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 8
+    # fmt, wdtype, w, batch, rows, cols, imp, grid, grid_size, scales, choices, out, status,
+    # stream
+    assert enc(5, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 2
+    assert enc(0, 0, None, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 1
+    assert enc(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None, None) == 1
+    assert enc(0, 0, FAKE, 1, 1, 200, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
+    assert enc(0, 0, FAKE, 1, 0, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
+    assert enc(0, 0, FAKE, 0, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
+    assert enc(0, 0, FAKE, 1, 1 << 40, 1 << 20, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
+    assert enc(0, 0, FAKE, 1, 1, 256, None, FAKE, 0, None, None, FAKE, FAKE, None) == 4
+    assert enc(0, 0, FAKE, 1, 1, 256, None, FAKE, 2049, None, None, FAKE, FAKE, None) == 4
+    assert enc(1, 0, FAKE, 1, 1, 256, None, FAKE, 513, None, None, FAKE, FAKE, None) == 4
+    assert enc(0, 0, P(0x100004), 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 8
+    # weight storage types: 0 fp32, 1 bf16, 2 fp16, 3 fp64; anything else is IQ_ERR_ARG,
+    # and bf16 weights still need 16-byte alignment
+    assert enc(0, 4, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 8
+    assert enc(1, -1, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 8
+    assert enc(0, 1, P(0x100008), 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 8
 
 
 def test_other_entry_points_argument_errors_need_no_gpu(lib):
@@ -79,12 +85,13 @@ def test_other_entry_points_argument_errors_need_no_gpu(lib):
     assert deq(0, FAKE, 1, 1, 100, FAKE, 16, FAKE, FAKE, None) == 3
     assert deq(1, FAKE, 1, 1, 256, FAKE, 600, FAKE, FAKE, None) == 4
     cand = lib.iq_encode_candidates
-    assert cand(7, FAKE, 1, 256, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 2
-    assert cand(0, FAKE, 1, 256, None, FAKE, 2049, 8, FAKE, FAKE, None, FAKE, None) == 4
-    assert cand(0, FAKE, 1, 256, None, FAKE, 16, 17, FAKE, FAKE, None, FAKE, None) == 8
-    assert cand(1, FAKE, 1, 256, None, FAKE, 16, 0, FAKE, FAKE, None, FAKE, None) == 8
-    assert cand(1, FAKE, 1, 256, None, FAKE, 16, 17, FAKE, FAKE, None, FAKE, None) == 8
-    assert cand(1, FAKE, 1, 250, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 3
+    assert cand(7, 0, FAKE, 1, 256, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 2
+    assert cand(0, 0, FAKE, 1, 256, None, FAKE, 2049, 8, FAKE, FAKE, None, FAKE, None) == 4
+    assert cand(0, 0, FAKE, 1, 256, None, FAKE, 16, 17, FAKE, FAKE, None, FAKE, None) == 8
+    assert cand(1, 0, FAKE, 1, 256, None, FAKE, 16, 0, FAKE, FAKE, None, FAKE, None) == 8
+    assert cand(1, 0, FAKE, 1, 256, None, FAKE, 16, 17, FAKE, FAKE, None, FAKE, None) == 8
+    assert cand(1, 0, FAKE, 1, 250, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 3
+    assert cand(1, 5, FAKE, 1, 256, None, FAKE, 16, 8, FAKE, FAKE, None, FAKE, None) == 8
     cs = lib.iq_choice_search
     assert cs(FAKE, FAKE, 4, 12, 8, 2, FAKE, None, None) == 8
     assert cs(FAKE, FAKE, 4, 16, 0, 2, FAKE, None, None) == 8
@@ -96,19 +103,23 @@ def test_other_entry_points_argument_errors_need_no_gpu(lib):
 
 def test_every_choice_and_fake_quant_argument_errors_need_no_gpu(lib):
     ev = lib.iq_encode_every_choice
-    # fmt, w, batch, rows, cols, imp, grid, grid_size, scales, out, status, stream
-    assert ev(7, FAKE, 1, 1, 256, None, FAKE, 16, None, FAKE, FAKE, None) == 2
-    assert ev(0, FAKE, 1, 1, 300, None, FAKE, 16, None, FAKE, FAKE, None) == 3
-    assert ev(1, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None) == 1
-    assert ev(1, FAKE, 1, 1, 256, None, FAKE, 513, None, FAKE, FAKE, None) == 4
+    # fmt, wdtype, w, batch, rows, cols, imp, grid, grid_size, scales, out, status, stream
+    assert ev(7, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, FAKE, FAKE, None) == 2
+    assert ev(0, 0, FAKE, 1, 1, 300, None, FAKE, 16, None, FAKE, FAKE, None) == 3
+    assert ev(1, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None) == 1
+    assert ev(1, 0, FAKE, 1, 1, 256, None, FAKE, 513, None, FAKE, FAKE, None) == 4
     fq = lib.iq_fake_quant
-    # fmt, w, batch, rows, cols, imp, grid, grid_size, scales, choices, xhat, out, status, stream
-    assert fq(0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, None, None, FAKE, None) == 1
-    assert fq(0, FAKE, 1, 1, 0, None, FAKE, 16, None, None, P(0x200000), None, FAKE, None) == 3
-    assert fq(0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, P(0x200008), None, FAKE, None) == 8
+    # fmt, wdtype, w, batch, rows, cols, imp, grid, grid_size, scales, choices, xhat, out,
+    # status, stream
+    assert fq(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, None, None, FAKE, None) == 1
+    assert fq(0, 0, FAKE, 1, 1, 0, None, FAKE, 16, None, None, P(0x200000), None, FAKE, None) == 3
+    assert fq(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, P(0x200008), None, FAKE, None) == 8
     # the decoded values may not overlap the weights (checked before any device access)
-    assert fq(0, FAKE, 1, 2, 256, None, FAKE, 16, None, None, P(0x100400), None, FAKE, None) == 8
-    assert fq(0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None, FAKE, None) == 8
+    assert fq(0, 0, FAKE, 1, 2, 256, None, FAKE, 16, None, None, P(0x100400), None, FAKE, None) == 8
+    assert fq(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None, FAKE, None) == 8
+    # overlap is judged on the weight's own size: one fp64 row spans 2 KiB
+    assert fq(0, 3, FAKE, 1, 1, 256, None, FAKE, 16, None, None, P(0x100400), None, FAKE, None) == 8
+    assert fq(2, 9, FAKE, 1, 1, 256, None, FAKE, 16, None, None, P(0x200000), None, FAKE, None) == 8
 
 
 def test_batched_search_argument_errors_need_no_gpu(lib):
