@@ -53,8 +53,23 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
 // First data error of a call: only a zero status is replaced.  The pointer
 // and the code pass through an empty asm so that the atomic's operands are
 // formed here, on this rare path, and not held (or spilled) for the whole
-// kernel.
+// kernel.  report() then uses the pointer as a global-memory pointer, so the
+// atomic is a global one; report_generic() leaves it generic (a flat atomic,
+// which the compiler also counts as a pending LDS access).  The atomic only
+// runs on errors, but the choice changes the code generated around it: the
+// IQ1 kernels measured 3 % faster on IQ1_M with the generic form, the IQ2_XS
+// kernel 1.5 % faster with the global one.
 __device__ __forceinline__ void report(int32_t* status, int code)
+{
+    uint64_t p = reinterpret_cast<uint64_t>(status);
+    __asm__ volatile("" : "+s"(p), "+v"(code));
+    typedef __attribute__((address_space(1))) int32_t global_i32;
+    int32_t expected = 0;
+    __atomic_compare_exchange_n(reinterpret_cast<global_i32*>(p), &expected, code, false,
+                                __ATOMIC_RELAXED, __ATOMIC_RELAXED);
+}
+
+__device__ __forceinline__ void report_generic(int32_t* status, int code)
 {
     __asm__ volatile("" : "+s"(status), "+v"(code));
     atomicCAS(status, 0, code);

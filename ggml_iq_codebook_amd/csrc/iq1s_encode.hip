@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     }
     __syncthreads();
     const bool grid_bad = sgrid_bad != 0;
-    if (grid_bad && tid == 0) report(a.status, IQ_ERR_GRID);
+    if (grid_bad && tid == 0) report_generic(a.status, IQ_ERR_GRID);
 
     const int col = lane & 15;          // matrix column = group within the half block
     const int kb = lane >> 4;           // K slice of the operands / row quarter of the result
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                     if (!(ws[t] >= 0.0f) || !finite_f32(ws[t])) err = IQ_ERR_IMPORTANCE;
             }
         }
-        if (err && half == 0) report(a.status, err);
+        if (err && half == 0) report_generic(a.status, err);
         const bool block_bad = __ballot(err != 0) != 0;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
@@ -321,7 +321,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         }
         const bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
         dh &= 0x7fffu;
-        if (scale_bad && !block_bad && half == 0 && lane == 0) report(a.status, IQ_ERR_SCALE_RANGE);
+        if (scale_bad && !block_bad && half == 0 && lane == 0)
+            report_generic(a.status, IQ_ERR_SCALE_RANGE);
         const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
 
         // Forced choices: every wave of the block checks all of them.
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             __asm__ volatile("" : "+v"(ln));
             const int cv = ln < kGroups ? a.choices[blk * kGroups + ln] : 0;
             const bool bad = cv < 0 || cv >= kChoices;
-            if (bad && half == 0) report(a.status, IQ_ERR_ARG);
+            if (bad && half == 0) report_generic(a.status, IQ_ERR_ARG);
             choice_bad = __ballot(bad) != 0;
             forced = a.choices[blk * kGroups + (kM ? (g >> 1) : sub)];
         }
