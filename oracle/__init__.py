@@ -51,13 +51,20 @@ def build(force: bool = True) -> str:
 
 _lib = None
 
+# A test build of the oracle to load instead of liboracle.so: the mutation
+# tests point this at copies of iq_oracle.c with a planted mistake.
+_LIB_OVERRIDE = os.environ.get("IQ_ORACLE_LIB")
+
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=False)
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=False)
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         i64, i32 = ctypes.c_int64, ctypes.c_int32
         L.orc_f32_to_f16.argtypes = [ctypes.c_float]

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity import compare_payloads, grid_for, scale_bits
+from tests.parity import compare_payloads, grid_for, scale_bits, unit_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -101,6 +101,29 @@ def test_iq2xs_grids_not_exact_in_bf16(kind, shape, n):
     imp = workloads.lognormal_importance((shape[0], shape[2]), 43)
     _check_full("iq2_xs", w, grid, imp)
     _check_full("iq2_xs", w, grid, None)
+
+
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq1_m"])
+def test_zero_choice_group_in_a_live_block_takes_the_lowest_choice(fmt):
+    # delta = +1/8 and -1/8 tie exactly on an all-zero choice group when the
+    # grid holds the all-zero entry: the lowest choice and the zero entry win,
+    # as in the oracle (the pin of the same name).
+    grid = grid_for(fmt, 300)
+    grid[7] = 0.0
+    w = workloads.normal_weight((1, 2, 256), 83)
+    L = 32 if fmt == "iq1_s" else 16
+    w[0, 0, :L] = 0.0
+    w[0, 1, 256 - L:] = 0.0
+    imp = workloads.lognormal_importance((1, 256), 84)
+    G = 8 if fmt == "iq1_s" else 16
+    for im in (None, imp):
+        got = _gpu_encode(fmt, w, grid, im)
+        ref = oracle.encode(fmt, w, grid, im)
+        compare_payloads(fmt, got, ref, w.reshape(-1, 256), grid, _block_imp(im, 1, 2, 256))
+        u_got = unit_codes(fmt, got).reshape(2, G, -1)
+        u_ref = unit_codes(fmt, ref).reshape(2, G, -1)
+        np.testing.assert_array_equal(u_got[0, 0], u_ref[0, 0])
+        np.testing.assert_array_equal(u_got[1, -1], u_ref[1, -1])
 
 
 def test_c3_iq2xs_rows_match_oracle():

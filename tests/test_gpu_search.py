@@ -130,6 +130,31 @@ def test_identity_hessian_keeps_the_encoders_own_choices():
     assert int(trace.abs().sum().item()) == 0
 
 
+def test_search_keeps_the_pick_on_an_exact_tie():
+    # Exact arithmetic (the oracle pin of the same name): group 0's two
+    # candidates tie at score 4 in the first sweep; the strict-improvement
+    # rule keeps step 2's candidate 1.  Rows of the 16-row workgroup differ
+    # only in which of the other groups carry nonzero, untied candidates.
+    G, C, L = 16, 2, 16
+    H = np.eye(256, dtype=np.float32)
+    H[0, 16] = H[16, 0] = 0.5
+    cand = np.zeros((20, G, C, L), np.float32)
+    cand[:, 0, 0, :2] = (-2.0, 2.0)
+    cand[:, 0, 1, :2] = (0.0, 2.0)
+    cand[:, 1, 0, 0] = 2.0
+    cand[:, 1, 1, 0] = 3.0
+    for r in range(20):
+        g = 2 + r % 14
+        cand[r, g, 0, 3] = 1.0 + r           # candidate 1 (zero) is better in group g
+    picks, trace = iq.choice_search(_dev(H), _dev(cand), sweeps=2, trace=True)
+    torch.cuda.synchronize()
+    picks = picks.cpu().numpy()
+    assert np.all(picks[:, 0] == 1) and np.all(picks[:, 1] == 0)
+    rpicks, rtrace = oracle.choice_search(H, cand, sweeps=2)
+    np.testing.assert_array_equal(picks, rpicks)
+    np.testing.assert_array_equal(trace.cpu().numpy(), rtrace)
+
+
 def test_c5_choice_search_full():
     cfg = workloads.c5_choice_search()
     H, w, grid, imp = cfg["H"], cfg["w"][0], cfg["grid"], cfg["importance"][0]

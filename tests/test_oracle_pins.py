@@ -447,6 +447,35 @@ def test_zero_and_underflow_blocks_are_all_zero_bytes(fmt):
     assert not p[0, 0].any() and not p[0, 1].any() and p[0, 2].any()
 
 
+@pytest.mark.parametrize("fmt", ["iq1_s", "iq1_m"])
+def test_zero_choice_group_in_a_live_block_takes_the_lowest_choice(fmt):
+    # An all-zero choice group inside a block with a nonzero d: with the
+    # all-zero grid entry, delta = +1/8 and -1/8 give exactly the same error
+    # (s/8 per value either way), so the tie rule decides: the lowest choice
+    # (IQ1_S c = 0: k = 0, delta bit 0; IQ1_M k = 0 and shift 0) and the
+    # zero entry.
+    grid = fmt_grid(fmt, 300)
+    grid[7] = 0.0
+    zero = int(np.nonzero(~grid.any(axis=1))[0][0])      # the first all-zero entry
+    w = workloads.normal_weight((1, 2, 256), 83)
+    L = 32 if fmt == "iq1_s" else 16
+    w[0, 0, :L] = 0.0
+    w[0, 1, 256 - L:] = 0.0
+    imp = workloads.lognormal_importance((1, 256), 84)
+    for im in (None, imp):
+        p = oracle.encode(fmt, w, grid, im)
+        ch = payload_choices(fmt, p).reshape(2, -1)
+        assert ch[0, 0] == 0 and ch[1, -1] == 0
+        if fmt == "iq1_s":
+            ent = iq1s_fields(p)[1].reshape(2, 8, 4)
+            assert np.all(ent[0, 0] == zero) and np.all(ent[1, -1] == zero)
+        else:
+            _, ent, shift, _ = iq1m_fields(p)
+            ent, shift = ent.reshape(2, 32), shift.reshape(2, 32)
+            assert np.all(ent[0, :2] == zero) and np.all(ent[1, -2:] == zero)
+            assert not shift[0, :2].any() and not shift[1, -2:].any()
+
+
 @pytest.mark.parametrize("fmt", ["iq1_s", "iq2_xs", "iq1_m"])
 def test_rejects_bad_inputs(fmt):
     grid = fmt_grid(fmt, 64)
@@ -671,6 +700,28 @@ def test_choice_search_sweeps_change_picks_and_lower_J():
     assert np.all(J[1] <= J[0] * (1 + 1e-12)) and np.all(J[2] <= J[1] * (1 + 1e-12))
     assert np.any(trace[0] != trace[2])
     assert np.mean(J[2] < J[0]) > 0.5
+
+
+def test_choice_search_keeps_the_pick_on_an_exact_tie():
+    # #3158 step 3 moves a group only on a strict improvement.  Exact
+    # arithmetic: H = I plus a coupling of 1/2 between element 0 of groups 0
+    # and 1.  Step 2 gives group 0 candidate 1 (e^T e = 4 against 8) and
+    # group 1 candidate 0 (4 against 9).  In the first sweep group 0 sees
+    # rest = (1, 0, ...), so both its candidates score exactly 4: it keeps
+    # candidate 1, though candidate 0 is the lower index of the least score.
+    G, C, L = 16, 2, 16
+    H = np.eye(256, dtype=np.float32)
+    H[0, 16] = H[16, 0] = 0.5
+    cand = np.zeros((1, G, C, L), np.float32)
+    cand[0, 0, 0, :2] = (-2.0, 2.0)
+    cand[0, 0, 1, :2] = (0.0, 2.0)
+    cand[0, 1, 0, 0] = 2.0
+    cand[0, 1, 1, 0] = 3.0
+    picks, trace = oracle.choice_search(H, cand, sweeps=2)
+    assert list(trace[0, 0, :2]) == [1, 0]
+    assert list(picks[0, :2]) == [1, 0] and not picks[0, 2:].any()
+    J = [oracle.choice_objective(H, cand, trace[s]) for s in range(3)]
+    assert J[0][0] == J[2][0]
 
 
 def test_identity_hessian_keeps_the_encoders_own_choices():
