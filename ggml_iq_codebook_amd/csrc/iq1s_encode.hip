@@ -110,21 +110,80 @@ __device__ __forceinline__ void load_group(const XB& xb, const float* wblk, int 
     }
 }
 
+// The 8 values and weights of the wave's local group c (0..15) from the
+// wave's LDS copy of its half block: 32 float4 of values, then 32 of
+// weights (zeros and ones for a rejected block).
+__device__ __forceinline__ void load_group_lds(const float4* s, int c, bool zero, float (&x)[8],
+                                               float (&w)[8])
+{
+    if (zero) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { x[j] = 0.0f; w[j] = 1.0f; }
+        return;
+    }
+    const float4 x0 = s[2 * c], x1 = s[2 * c + 1], w0 = s[32 + 2 * c], w1 = s[33 + 2 * c];
+    x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+    x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+    w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+    w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+}
+
+// The status atomic: the global form in the modes that stage the block in
+// LDS (a generic atomic counts as a pending LDS access and would make the
+// sweep wait for all of its LDS reads at once), the generic form otherwise
+// (with which the payload and fake-quant kernels measured fastest).
+template <bool kGlobal>
+__device__ __forceinline__ void report_status(int32_t* status, int code)
+{
+    if constexpr (kGlobal) report(status, code);
+    else report_generic(status, code);
+}
+
+// Where a lane's group values and weights are read again after the sweep:
+// global memory (GlobalGroup), or the wave's LDS copy of its half block
+// (LdsGroup), which the modes that pick many choices use.
+template <class XB>
+struct GlobalGroup {
+    XB xb;
+    const float* wblk;
+    int g;
+    __device__ __forceinline__ void load(bool zero, float (&x)[8], float (&w)[8]) const
+    {
+        load_group(xb, wblk, g, zero, x, w);
+    }
+};
+
+struct LdsGroup {
+    const float4* s;
+    int c;
+    __device__ __forceinline__ void load(bool zero, float (&x)[8], float (&w)[8]) const
+    {
+        load_group_lds(s, c, zero, x, w);
+    }
+};
+
+template <bool kLds, class XB>
+__device__ __forceinline__ auto group_source(const XB& xb, const float* wblk, int g,
+                                             const float4* s, int c)
+{
+    if constexpr (kLds) return LdsGroup{s, c};
+    else return GlobalGroup<XB>{xb, wblk, g};
+}
+
 // VALU rescan for choice cs = k + 8*deltabit over tiles t0 .. t0+nt-1 of chunk
 // tchunk, rows 4*kbs .. 4*kbs+3 of each tile (the entries one lane of a
 // column covers): the lowest entry with the least key (2k+1)*U - 2V/d,
 // recomputed in fp32 from the group's values and weights (read again from
 // memory rather than held through the sweep).  Returns the entry, writes its
 // key.
-template <int kChunkTiles, class XB>
+template <int kChunkTiles, class GS>
 __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, int kbs, int t0,
-                                      int nt, int cs, const XB& xb, const float* wblk, int g,
-                                      bool zero_block, float w64, float b4, float inv_d,
-                                      float* key_out)
+                                      int nt, int cs, const GS& src, bool zero_block, float w64,
+                                      float b4, float inv_d, float* key_out)
 {
     float x[8], w[8];
     __asm__ volatile("" ::: "memory");
-    load_group(xb, wblk, g, zero_block, x, w);
+    src.load(zero_block, x, w);
     const float mk = (float)(2 * (cs & 7) + 1);
     const float dl = (cs >> 3) ? -0.25f : 0.25f;      // 2*delta
     const float bd = (cs >> 3) ? b4 : -b4;
@@ -156,12 +215,12 @@ __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, 
 // Weighted squared error of group g against d*(2k+1)*(q + delta) for entry
 // e and choice cs = k + 8*shift, in fp64 from its definition: the sum of
 // w*(x - s*(q + delta))^2, delta = +1/8 for shift 0 and -1/8 for shift 1.
-template <int kChunk, class XB>
-__device__ __forceinline__ double group_error64(const XB& xb, const float* wblk, int g,
-                                                bool zero, const uint4* sq, int e, int cs, float d)
+template <int kChunk, class GS>
+__device__ __forceinline__ double group_error64(const GS& src, bool zero, const uint4* sq, int e,
+                                                int cs, float d)
 {
     float x[8], w[8];
-    load_group(xb, wblk, g, zero, x, w);
+    src.load(zero, x, w);
     const uint4 u = sq[e + e / kChunk];
     const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
     const double sc = (double)d * (double)(2 * (cs & 7) + 1);
@@ -191,6 +250,11 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     // Payloads staged in LDS: one per block, or one per block and choice.
     constexpr int kPayloads = kMode == kModeEvery ? kChoices : 1;
     constexpr int kChunkTiles = chunk_tiles<kFmt, kMode>();
+    // The modes that pick several choices per group keep each wave's half
+    // block in LDS for their rescans (measured: candidates 5 % faster); the
+    // payload and fake-quant modes read global memory again, which kept their
+    // sweep's code as it was (the staging variant cost the c2 payload 3 %).
+    constexpr bool kStage = kMode == kModeEvery || kMode == kModeCandidates;
     constexpr int kChunk = kTile * kChunkTiles;
     // Entry e sits at e + e/kChunk: one spare slot per chunk, so the lanes of
     // a rescan that read different chunks (a multiple of the 64 banks apart
@@ -200,6 +264,9 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     __shared__ uint4 sm[kSlots];         // (q[0..7] - 1/8)^2 as bf16
     __shared__ uint4 sq[kSlots];         // q[0..7] as bf16
     __shared__ uint16_t sout16[kPayloads * kBlocksPerWG * kBB / 2];
+    // Per wave, its half block's values and weights as fp32 (32 + 32 float4),
+    // read back by the rescans instead of global memory (kStage modes).
+    __shared__ float4 sxw_all[kStage ? kWavesPerWG * 64 : 1];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
 
@@ -244,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     }
     __syncthreads();
     const bool grid_bad = sgrid_bad != 0;
-    if (grid_bad && tid == 0) report_generic(a.status, IQ_ERR_GRID);
+    if (grid_bad && tid == 0) report_status<kStage>(a.status, IQ_ERR_GRID);
 
     const int col = lane & 15;          // matrix column = group within the half block
     const int kb = lane >> 4;           // K slice of the operands / row quarter of the result
@@ -265,7 +332,9 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         const int64_t bt = blk / a.g.blocks_per_batch;
         const int64_t cb = blk % a.g.blocks_per_row;
         const WeightBlock<kDT> xb(a.w, blk);
+        float4* sxw = sxw_all + (kStage ? wave * 64 : 0);
         const float* wblk = a.imp ? a.imp + bt * a.g.cols + cb * kBlockElems : nullptr;
+        const auto src = group_source<kStage>(xb, wblk, g, sxw, col);
 
         // Whole-block checks and amax (each lane reads 4 of the 256 values);
         // IQ1_M also sums the squares: per lane ((x0^2 + x1^2) + x2^2) + x3^2,
@@ -281,7 +350,22 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 amax = fmaxf(amax, fabsf(xs[t]));
             }
             if (kM) ssq = ((xs[0] * xs[0] + xs[1] * xs[1]) + xs[2] * xs[2]) + xs[3] * xs[3];
-            if (wblk && !err) {
+            if (kStage) {
+                float4 wv = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                if (wblk) {
+                    wv = reinterpret_cast<const float4*>(wblk)[lane];
+                    const float ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (!err && (!(ws[t] >= 0.0f) || !finite_f32(ws[t])))
+                            err = IQ_ERR_IMPORTANCE;
+                }
+                // The lanes holding this wave's half block keep it in LDS.
+                if ((lane >> 5) == half) {
+                    sxw[lane & 31] = xv;
+                    sxw[32 + (lane & 31)] = wv;
+                }
+            } else if (wblk && !err) {
                 const float4 wv = reinterpret_cast<const float4*>(wblk)[lane];
                 const float ws[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
@@ -289,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                     if (!(ws[t] >= 0.0f) || !finite_f32(ws[t])) err = IQ_ERR_IMPORTANCE;
             }
         }
-        if (err && half == 0) report_generic(a.status, err);
+        if (err && half == 0) report_status<kStage>(a.status, err);
         const bool block_bad = __ballot(err != 0) != 0;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
@@ -322,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         const bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
         dh &= 0x7fffu;
         if (scale_bad && !block_bad && half == 0 && lane == 0)
-            report_generic(a.status, IQ_ERR_SCALE_RANGE);
+            report_status<kStage>(a.status, IQ_ERR_SCALE_RANGE);
         const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
 
         // Forced choices: every wave of the block checks all of them.
@@ -333,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             __asm__ volatile("" : "+v"(ln));
             const int cv = ln < kGroups ? a.choices[blk * kGroups + ln] : 0;
             const bool bad = cv < 0 || cv >= kChoices;
-            if (bad && half == 0) report_generic(a.status, IQ_ERR_ARG);
+            if (bad && half == 0) report_status<kStage>(a.status, IQ_ERR_ARG);
             choice_bad = __ballot(bad) != 0;
             forced = a.choices[blk * kGroups + (kM ? (g >> 1) : sub)];
         }
@@ -343,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         // The lane's group: values, weights, sums, and its K slice of the
         // three-way bf16 split of -2*w*x and w (slice 3 is zero padding).
         float x[8], w[8];
-        load_group(xb, wblk, g, zero_block, x, w);
+        src.load(zero_block, x, w);
         const float inv_d = zero_block ? 1.0f : 1.0f / d;
         float W = 0.0f, B = 0.0f;
         uint32_t bwx[8], bw[8];
@@ -510,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 const int kbs = __builtin_ctzll(holders) >> 4;
                 const int tch = __shfl(tchunk, col + 16 * kbs);
                 idx = rescan<kChunkTiles>(sq, tch, kbs, kb * (kChunkTiles / 4), kChunkTiles / 4, cs,
-                                          xb, wblk, g, zero_block, w64, b4, inv_d, &key);
+                                          src, zero_block, w64, b4, inv_d, &key);
 #pragma unroll
                 for (int o = 16; o <= 32; o <<= 1) {
                     const float ok = __shfl_xor(key, o);
@@ -518,8 +602,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                     if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
                 }
             } else {
-                idx = rescan<kChunkTiles>(sq, tchunk, kb, 0, kChunkTiles, cs, xb, wblk, g,
-                                          zero_block, w64, b4, inv_d, &key);
+                idx = rescan<kChunkTiles>(sq, tchunk, kb, 0, kChunkTiles, cs, src, zero_block, w64,
+                                          b4, inv_d, &key);
 #pragma unroll
                 for (int o = 16; o <= 32; o <<= 1) {
                     const float om = __shfl_xor(lane_min, o);
@@ -531,7 +615,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             if (refine) {
                 // The choice unit's fp64 error: its four groups (IQ1_S
                 // sub-block) or two (IQ1_M scale group), adjacent columns.
-                double e = group_error64<kChunk>(xb, wblk, g, zero_block, sq, idx, cs, d);
+                double e = group_error64<kChunk>(src, zero_block, sq, idx, cs, d);
                 e += __shfl_xor(e, 1);
                 if (!kM) e += __shfl_xor(e, 2);
                 if (it == 0) { idx_alt = idx; err_alt = e; continue; }
@@ -551,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                     const int part = kM ? (g & 1) : lq;
                     const int64_t base = (blk * kGroups + unit) * a.top_c + it;    // [block][unit][r]
                     float xo[8], wo[8];
-                    load_group(xb, wblk, g, rejected, xo, wo);
+                    src.load(rejected, xo, wo);
                     const float sk = f16_bits_to_f32(dh) * (float)(2 * (cs & 7) + 1);
                     const float delta = (cs >> 3) ? -0.125f : 0.125f;
                     const uint4 u = sq[idx + idx / kChunk];
