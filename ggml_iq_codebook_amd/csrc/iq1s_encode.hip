@@ -12,15 +12,17 @@
 // For a group and a grid entry the error is, up to a constant,
 //   s^2 * U(delta) - 2 s * V(delta),  U(delta) = sum w*(q+delta)^2,
 //   V(delta) = sum wx*(q+delta).
-// U(+1/8), U(-1/8), -2V(+1/8) and -2V(-1/8) for 16 grid entries x 16 groups
-// are four small products [16 entries x 8] x [8 x 16 groups], run as
+// U(+1/8), U(-1/8) and -2*sum(wx*q) for 16 grid entries x 16 groups are
+// three small products [16 entries x 8] x [8 x 16 groups], run as
 // v_mfma_f32_16x16x32_bf16: the entry side (q+delta)^2 and q is exact in bf16
 // (values like 81/64 need 7 mantissa bits), the group side (w and -2*w*x) is
 // split into three bf16 parts whose sum is exactly the fp32 value, so the
-// products are exact and only the fp32 accumulation rounds; the constant
-// -2*delta*sum(wx) of V enters as the accumulator input.  Everything is
-// divided by the block scale d (the V side carries 1/d), so the key of local
-// scale s_k = d*(2k+1) is (2k+1)*U - 2V/d: one FMA with a literal multiplier
+// products are exact and only the fp32 accumulation rounds.  The rest of
+// -2V(delta), -2*delta*sum(wx), is the same for every entry of a group and
+// shift, so it does not move the sweep's minima between entries: it is added
+// to them once after the sweep.  Everything is divided by the block scale d
+// (the V side carries 1/d), so the sweep key of local scale s_k = d*(2k+1) is
+// (2k+1)*U - 2*sum(wx*q)/d: one FMA with a literal multiplier
 // (v_fmamk_f32, two register operands, which pairs well with v_min3 in the
 // dual-issue VALU); the choice cost of a sub-block is (2k+1) times the sum of
 // its groups' minima (the common factor d^2 dropped).  The VALU keeps
@@ -445,9 +447,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                                             bw[4] | (bw[5] << 16), bw[6] | (bw[7] << 16)));
         const float w64 = W * 0.015625f;
         const float b4 = B * 0.25f;
-        const float b4d = b4 * inv_d;
-        const v4f cnp = {-b4d, -b4d, -b4d, -b4d};     // -2*(+1/8)*B/d
-        const v4f cnm = {b4d, b4d, b4d, b4d};         // -2*(-1/8)*B/d
+        const float b4d = b4 * inv_d;                 // -2*(-1/8)*B/d; +1/8 takes -b4d
 
         // Sweep.
         // chunk_of: 4-bit chunk index of choice c in bits 4*(c%8) of word c/8.
@@ -464,19 +464,18 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 const v8bf aq = as_v8bf(sq[at]);
                 const v4f up = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap, opw, zero4, 0, 0, 0);
                 const v4f um = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, opw, zero4, 0, 0, 0);
-                const v4f vnp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opn2wx, cnp, 0, 0, 0);
-                const v4f vnm = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opn2wx, cnm, 0, 0, 0);
+                const v4f vq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, opn2wx, zero4, 0, 0, 0);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const float mk = (float)(2 * k + 1);
-                    const float p0 = __builtin_fmaf(up[0], mk, vnp[0]);
-                    const float p1 = __builtin_fmaf(up[1], mk, vnp[1]);
-                    const float p2 = __builtin_fmaf(up[2], mk, vnp[2]);
-                    const float p3 = __builtin_fmaf(up[3], mk, vnp[3]);
-                    const float m0 = __builtin_fmaf(um[0], mk, vnm[0]);
-                    const float m1 = __builtin_fmaf(um[1], mk, vnm[1]);
-                    const float m2 = __builtin_fmaf(um[2], mk, vnm[2]);
-                    const float m3 = __builtin_fmaf(um[3], mk, vnm[3]);
+                    const float p0 = __builtin_fmaf(up[0], mk, vq[0]);
+                    const float p1 = __builtin_fmaf(up[1], mk, vq[1]);
+                    const float p2 = __builtin_fmaf(up[2], mk, vq[2]);
+                    const float p3 = __builtin_fmaf(up[3], mk, vq[3]);
+                    const float m0 = __builtin_fmaf(um[0], mk, vq[0]);
+                    const float m1 = __builtin_fmaf(um[1], mk, vq[1]);
+                    const float m2 = __builtin_fmaf(um[2], mk, vq[2]);
+                    const float m3 = __builtin_fmaf(um[3], mk, vq[3]);
                     best[k] = fminf(best[k], fminf(fminf(fminf(p0, p1), p2), p3));
                     best[8 + k] = fminf(best[8 + k], fminf(fminf(fminf(m0, m1), m2), m3));
                 }
@@ -495,7 +494,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         // sums in every lane of the sub-block).  IQ1_M: per group and local
         // scale k, the lesser of its two shifts' least keys (the lower shift
         // on equal keys); per scale group, (2k+1) times the sum over its two
-        // groups.  A group's least key is the least over its four lanes.
+        // groups.  A group's least key is the least over its four lanes, plus
+        // the -2*delta*sum(wx)/d the sweep left out.
         int cstar = 0;               // IQ1_S: the sub-block's choice; IQ1_M: the local scale
         float cbest = 0.0f;
         float cost[16];
@@ -505,6 +505,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             float m = best[c];
             m = fminf(m, __shfl_xor(m, 16));
             m = fminf(m, __shfl_xor(m, 32));
+            m += c < 8 ? -b4d : b4d;
             if (kM) {
                 cost[c] = m;
             } else {
