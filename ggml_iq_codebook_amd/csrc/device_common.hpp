@@ -93,14 +93,19 @@ __device__ __forceinline__ uint32_t bf16_bits(float f)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Part p (0, 1, 2) of the exact three-way bf16 split of v: v = hi + mid + lo.
+// Part p (0, 1, 2) of the exact three-way bf16 split of v: v = hi + mid + lo,
+// each part the leading 8 significant bits of what the earlier parts leave
+// (truncation: hi keeps v's top 8 bits, v - hi is exact with at most 16
+// significant bits, mid keeps its top 8, and the last 8 fit lo exactly).
+// Half the instructions of a split by rounding to nearest, and the same sum.
 __device__ __forceinline__ uint32_t split_part(float v, int p)
 {
-    const uint32_t hi = bf16_bits(v);
-    const float r1 = v - bf16_to_f32(hi);
-    const uint32_t mid = bf16_bits(r1);
-    const float r2 = r1 - bf16_to_f32(mid);
-    return p == 0 ? hi : (p == 1 ? mid : bf16_bits(r2));
+    const uint32_t u0 = __float_as_uint(v);
+    const float r1 = v - __uint_as_float(u0 & 0xffff0000u);
+    const uint32_t u1 = __float_as_uint(r1);
+    const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
+    const uint32_t u2 = __float_as_uint(r2);
+    return (p == 0 ? u0 : (p == 1 ? u1 : u2)) >> 16;
 }
 
 __device__ __forceinline__ v8bf as_v8bf(uint4 u)
