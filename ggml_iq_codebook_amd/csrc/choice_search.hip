@@ -12,19 +12,22 @@
 // score_c - score_cur, score_c = e_c^T H_gg e_c + 2 e_c^T (r_g - H_gg e_cur).
 //
 // Layout: a 256-thread workgroup runs 16 rows of one block in lockstep
-// (grid.y = the block).  r (256 columns x 16 rows) lives in registers in the
-// matrix-core accumulator layout: wave w holds columns 64w..64w+63 as four
-// 16x16 tiles, lane l holding columns 4(l/16)..4(l/16)+3 of a tile for row
-// l%16.  The products with H run on the matrix cores (v_mfma_f32_16x16x4_f32,
-// fp32 operands): e_c^T H_gg e_c for every candidate, the initial r = H e, each
-// step's rank-L update r += H[:,g] de, and the next group's
-// rest = r_g - H_gg e_cur,g (by the wave that owns that group's columns).  The
-// decision runs in the scorer layout, lane (row, candidate) = (t/16, t%16):
-// each lane scores its candidate from its own error vector and the row's rest;
-// DPP reductions across the row's 16 lanes give the lowest index of least
-// score and the current pick's score (each lane keeps a bit mask of the groups
-// whose pick is its candidate).  Two barriers per step; the next step's H rows
-// and candidate vectors are requested a step ahead.
+// (grid.y = the block).  The products with H run on the matrix cores
+// (v_mfma_f32_16x16x4_f32, fp32 operands): e_c^T H_gg e_c for every
+// candidate, and for each step the rest of the next group gn,
+// r_gn - H_gn,gn e_gn = sum over the other groups h of H_gn,h e_h, formed
+// afresh from the current errors (no running r = H e is kept): the four waves
+// sum their quarters of K, leaving out gn and the group being decided, while
+// that group is decided, and the wave of each of gn's 16-column tiles adds
+// the decided group's part after.
+// The decision runs in the scorer layout, lane (row, candidate) =
+// (t/16, t%16): each lane scores its candidate from its own error vector and
+// the row's rest; one DPP reduction across the row's 16 lanes gives the lowest
+// index of least score, the current pick winning the ties it is in (each lane
+// keeps a bit mask of the groups whose pick is its candidate).  Two barriers
+// per step; the next step's H operands and candidate vectors are requested a
+// step ahead.
+
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -63,33 +66,11 @@ __device__ __forceinline__ float dpp_f(float v)
                                                                  kCtrl, 0xf, 0xf, false));
 }
 
-template <int kCtrl>
-__device__ __forceinline__ int dpp_i(int v)
-{
-    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
-}
-
 constexpr int kRor8 = 0x128, kRor4 = 0x124, kXor2 = 0x4e, kXor1 = 0xb1;
 
-template <int kCtrl>
-__device__ __forceinline__ void argmin_step(float& v, int& i)
-{
-    const float ov = dpp_f<kCtrl>(v);
-    const int oi = dpp_i<kCtrl>(i);
-    if (ov < v || (ov == v && oi < i)) { v = ov; i = oi; }
-}
-
-// Least value over the 16 lanes of a row, lowest index among equal values;
-// every lane of the row ends with the result (the four steps reach lanes
-// +8, +4, ^2, ^1 away, which together cover the row).
-__device__ __forceinline__ void row_argmin(float& v, int& i)
-{
-    argmin_step<kRor8>(v, i);
-    argmin_step<kRor4>(v, i);
-    argmin_step<kXor2>(v, i);
-    argmin_step<kXor1>(v, i);
-}
-
+// Least value over the 16 lanes of a row; every lane of the row ends with it
+// (the four steps reach lanes +8, +4, ^2, ^1 away, which together cover the
+// row).
 __device__ __forceinline__ float row_min(float v)
 {
     v = fminf(v, dpp_f<kRor8>(v));
@@ -110,8 +91,8 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     constexpr int kHB = L * kHR + 4;            // H_gg block stride
     constexpr int kQS = G * kMaxC + 16;         // qself row stride
     __shared__ __align__(16) float hdiag[G * kHB];        // H_gg blocks [g][i][j]
-    __shared__ __align__(16) float ecurT[256 * kRows];    // current errors, [column][row]
-    __shared__ __align__(16) float dltT[L * kRows];       // e_new - e_cur of the group, [i][row]
+    __shared__ __align__(16) float ecurT[256 * kRows];      // current errors, [column][row]
+    __shared__ __align__(16) float part[4 * KH * 64 * 4]; // the waves' partial rest tiles
     __shared__ __align__(16) float rest[kRows * kHR];     // r_g - H_gg e_cur,g, [row][i]
     __shared__ __align__(16) float qself[kRows * kQS];    // e_gc^T H_gg e_gc, [row][g*C + c]
     __shared__ int pick0[kRows * G];                      // step-2 picks
@@ -252,67 +233,86 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     uint32_t pmask = 0u;
     for (int g = 0; g < G; ++g) pmask |= (uint32_t)(pick0[srow * G + g] == scand) << g;
 
-    // r = H e on the matrix cores: wave w's tiles j = 0..3 (columns
-    // 64w + 16j ..), K over all 256 columns in 64 steps of 4; the H operand
-    // (H symmetric: H[k][column]) streamed from L2 eight steps at a time, one
-    // batch ahead.
-    v4f r[4];
+    // The rest of group gn for the 16 rows, r_gn - H_gn,gn e_gn: the sum over
+    // the other groups h of H_gn,h e_h, formed afresh for every step on the
+    // matrix cores (no running r = H e is kept).  Output tile ih holds the
+    // columns gn*L + 16ih .. + 15 (lane: columns 4lq..4lq+3 of the tile, row
+    // lc).  The part that does not depend on the group gx being decided runs
+    // before its decision: wave w takes the K range 64w .. 64w + 63 in steps
+    // of 4 (k = 64w + 4s + lq) with the columns of gn and gx left out, and puts
+    // its partial tiles in LDS.  After the decision, wave ih adds the four
+    // partials of tile ih in a fixed order, then H_gn,gx e_gx with the errors
+    // just decided, and writes the rest.  The H operands (H symmetric:
+    // H[k][column]) are requested a step ahead.
+    constexpr int kPS = 16;                     // K steps per wave
+    float hP[KH][kPS], hPn[KH][kPS];            // H[64w + 4s + lq][gn*L + 16ih + lc]
+    float hX[KS], hXn[KS];                      // H[gx*L + 4s + lq][gn*L + 16w + lc], w < KH
+    auto load_hP = [&](int gn, float (&h)[KH][kPS]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    {
-        constexpr int kB = 16;
-        float ha[4][kB], hn[4][kB];
-        auto load_batch = [&](int s0, float (&h)[4][kB]) {
+        for (int ih = 0; ih < KH; ++ih)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int s = 0; s < kPS; ++s)
+                h[ih][s] = Hb[(64 * wave + 4 * s + lq) * 256 + gn * L + 16 * ih + lc];
+    };
+    auto load_hX = [&](int gn, int gx, float (&h)[KS]) {
+        if (wave >= KH) return;                                 // wave-uniform
 #pragma unroll
-                for (int s = 0; s < kB; ++s)
-                    h[j][s] = Hb[(4 * (s0 + s) + lq) * 256 + 64 * wave + 16 * j + lc];
-        };
-        load_batch(0, ha);
-        for (int s0 = 0; s0 < 64; s0 += kB) {
-            load_batch(s0 + kB < 64 ? s0 + kB : s0, hn);
+        for (int s = 0; s < KS; ++s) h[s] = Hb[(gx * L + 4 * s + lq) * 256 + gn * L + 16 * wave + lc];
+    };
+    // The wave's partial tiles, columns of gn and gx (gx < 0: none) left out
+    // (wave-uniform branches; the errors of gx may be changing in LDS
+    // meanwhile, and what is read there is not used).  All B operands are read
+    // before the products start.
+    auto partial = [&](int gn, int gx, v4f (&p)[KH]) {
+        float bv[kPS];
 #pragma unroll
-            for (int s = 0; s < kB; ++s) {
-                const float bv = ecurT[(4 * (s0 + s) + lq) * kRows + lc];
+        for (int s = 0; s < kPS; ++s) bv[s] = ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) r[j] = mfma4(ha[j][s], bv, r[j]);
+        for (int ih = 0; ih < KH; ++ih) p[ih] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < kPS; ++s) {
+            const int kg = (64 * wave + 4 * s) / L;             // wave-uniform
+            if (kg != gn && kg != gx) {
+#pragma unroll
+                for (int ih = 0; ih < KH; ++ih) p[ih] = mfma4(hP[ih][s], bv[s], p[ih]);
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int s = 0; s < kB; ++s) ha[j][s] = hn[j][s];
-        }
-    }
-
-    // rest of group gn = r_gn - H_gn,gn e_cur,gn on the matrix cores (the
-    // accumulator starts from the r tile), by the wave that owns the group's
-    // columns, written to LDS.
-    auto make_rest = [&](int gn) {
-        if (wave != ((gn * L) >> 6)) return;                    // wave-uniform
-#pragma unroll
-        for (int ih = 0; ih < KH; ++ih) {
-            const int jt = ((gn * L) & 63) / 16 + ih;
-            v4f d = r[0];
-#pragma unroll
-            for (int j = 1; j < 4; ++j)
-                if (jt == j) d = r[j];
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int k = 4 * s + lq;
-                const float A = -hdiag[gn * kHB + (16 * ih + lc) * kHR + k];
-                d = mfma4(A, ecurT[(gn * L + k) * kRows + lc], d);
-            }
-            *reinterpret_cast<float4*>(&rest[lc * kHR + 16 * ih + 4 * lq]) =
-                make_float4(d[0], d[1], d[2], d[3]);
         }
     };
-    make_rest(0);
+    auto store_partial = [&](const v4f (&p)[KH]) {
+#pragma unroll
+        for (int ih = 0; ih < KH; ++ih)
+            *reinterpret_cast<v4f*>(&part[((wave * KH + ih) * 64 + lane) * 4]) = p[ih];
+    };
+    auto finish_rest = [&](int gx) {
+        if (wave >= KH) return;                                 // wave-uniform
+        const int ih = wave;
+        v4f d = *reinterpret_cast<const v4f*>(&part[(ih * 64 + lane) * 4]);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            const v4f o = *reinterpret_cast<const v4f*>(&part[((w * KH + ih) * 64 + lane) * 4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[i] += o[i];
+        }
+        if (gx >= 0) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) d = mfma4(hX[s], ecurT[(gx * L + 4 * s + lq) * kRows + lc], d);
+        }
+        *reinterpret_cast<float4*>(&rest[lc * kHR + 16 * ih + 4 * lq]) =
+            make_float4(d[0], d[1], d[2], d[3]);
+    };
 
-    // The step operands, one group ahead: the scorer's candidate vector and
-    // the group's H rows for the update.
+    // The first group's rest (no group being decided).
+    v4f pp[KH];
+    load_hP(0, hP);
+    partial(0, -1, pp);
+    store_partial(pp);
+    __syncthreads();
+    finish_rest(-1);
+
+    // The step operands, one step ahead: the scorer's candidate vector and the
+    // H operands of the next rest.
     float cv[L], cvn[L];
-    float hA[4][KS], hAn[4][KS];
     auto load_cv = [&](int g, float (&v)[L]) {
         if (scorer) {
             const float* ep = cand_ptr(srow, g, scand);
@@ -323,22 +323,21 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             for (int i = 0; i < L; ++i) v[i] = 0.0f;
         }
     };
-    auto load_hA = [&](int g, float (&h)[4][KS]) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                h[j][s] = Hb[(g * L + 4 * s + lq) * 256 + 64 * wave + 16 * j + lc];
-    };
     load_cv(0, cv);
-    load_hA(0, hA);
+    load_hP(1, hP);
+    load_hX(1, 0, hX);
     __syncthreads();
 
     for (int sw = 0; sw < a.sweeps; ++sw) {
         for (int g = 0; g < G; ++g) {
             const int gn = g + 1 < G ? g + 1 : 0;
-            // Scores, the decision and the error update of group g.
+            const int gnn = gn + 1 < G ? gn + 1 : 0;
             load_cv(gn, cvn);
+            // The next group's rest without group g, while group g is decided.
+            partial(gn, g, pp);
+            load_hP(gnn, hPn);
+            load_hX(gnn, gn, hXn);
+            // Scores, the decision and the error update of group g.
             float sc = __builtin_inff();
             if (scorer) {
                 float dot = 0.0f;
@@ -346,43 +345,35 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
                 for (int i = 0; i < L; ++i) dot = __builtin_fmaf(cv[i], rest[srow * kHR + i], dot);
                 sc = __builtin_fmaf(2.0f, dot, qself[srow * kQS + g * C + scand]);
             }
+            // The least score of the row (DPP), then the row's lanes that hold
+            // it (a ballot, 16 bits per row): the group keeps its pick if the
+            // pick holds it (only a strictly lower score moves it), else moves
+            // to the lowest candidate that does.
             const bool mine = (pmask >> g) & 1u;
-            const float scur = row_min(mine ? sc : __builtin_inff());
-            float bs = sc;
-            int bc = scand;
-            row_argmin(bs, bc);
-            const bool move = bs < scur;          // a strict improvement only
+            const float m = row_min(sc);
+            const int rsh = 16 * (lane >> 4);
+            const uint32_t req = (uint32_t)(__ballot(sc == m) >> rsh) & 0xffffu;
+            const uint32_t rcur = (uint32_t)(__ballot(mine) >> rsh) & 0xffffu;
+            const bool move = req != 0u && (req & rcur) == 0u;
+            const int bc = __builtin_ctz(req | 0x10000u);
             if (move && scand == bc) {
 #pragma unroll
-                for (int i = 0; i < L; ++i) {
-                    const int at = (g * L + i) * kRows + srow;
-                    dltT[i * kRows + srow] = cv[i] - ecurT[at];
-                    ecurT[at] = cv[i];
-                }
-            } else if (!move && scand == 0) {
-#pragma unroll
-                for (int i = 0; i < L; ++i) dltT[i * kRows + srow] = 0.0f;
+                for (int i = 0; i < L; ++i) ecurT[(g * L + i) * kRows + srow] = cv[i];
             }
             if (move) pmask = (pmask & ~(1u << g)) | ((uint32_t)(scand == bc) << g);
+            store_partial(pp);
 #pragma unroll
             for (int i = 0; i < L; ++i) cv[i] = cvn[i];
             __syncthreads();
 
-            // r += H[:, g] de on the matrix cores; the owner of the next group
-            // then forms its rest.
-            load_hA(gn, hAn);
-            float bdl[KS];
+            // The rest of gn with the errors of g just decided.
+            finish_rest(g);
 #pragma unroll
-            for (int s = 0; s < KS; ++s) bdl[s] = dltT[(4 * s + lq) * kRows + lc];
+            for (int ih = 0; ih < KH; ++ih)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int s = 0; s < kPS; ++s) hP[ih][s] = hPn[ih][s];
 #pragma unroll
-                for (int s = 0; s < KS; ++s) r[j] = mfma4(hA[j][s], bdl[s], r[j]);
-            make_rest(gn);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int s = 0; s < KS; ++s) hA[j][s] = hAn[j][s];
+            for (int s = 0; s < KS; ++s) hX[s] = hXn[s];
             __syncthreads();
         }
         if (a.trace && srow < nrows)
