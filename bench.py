@@ -209,7 +209,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the encode shards by rows/experts with no "
-              "exchange, and this build runs on a single MI355X (--gpus 1).", file=sys.stderr)
+              "exchange, and it is measured here on a single MI355X (--gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -120,7 +120,9 @@ def test_f16_to_float_is_exact():
 @pytest.mark.parametrize("fmt,divisor", [("iq1_s", 16.875), ("iq2_xs", 155.0)])
 def test_scale_predictor_closed_form(fmt, divisor):
     # #2450 review: d = (amax / 16.875) * 0.61 with fp16 rounding (IQ1_S);
-    # the IQ2_XS divisor 31*5 is this build's reading.
+    # the IQ2_XS divisor 31*5 follows the same pattern (top local multiplier
+    # times the largest grid value); #2513 "Testing" names an IQ2_XS clamp
+    # without printing its value.
     rng = np.random.default_rng(1)
     amaxes = np.abs(rng.standard_normal(5000) * 10.0 ** rng.integers(-7, 4, 5000)).astype(np.float32)
     for a in amaxes:
