@@ -260,13 +260,16 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         for (int s = 0; s < KS; ++s) h[s] = Hb[(gx * L + 4 * s + lq) * 256 + gn * L + 16 * wave + lc];
     };
     // The wave's partial tiles, columns of gn and gx (gx < 0: none) left out
-    // (wave-uniform branches; the errors of gx may be changing in LDS
-    // meanwhile, and what is read there is not used).  All B operands are read
-    // before the products start.
+    // (wave-uniform conditions).  The errors of gx are being decided and
+    // rewritten in LDS meanwhile, so they are not read.  All B operands are
+    // read before the products start.
     auto partial = [&](int gn, int gx, v4f (&p)[KH]) {
         float bv[kPS];
 #pragma unroll
-        for (int s = 0; s < kPS; ++s) bv[s] = ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
+        for (int s = 0; s < kPS; ++s) {
+            const int kg = (64 * wave + 4 * s) / L;             // wave-uniform
+            bv[s] = kg == gx ? 0.0f : ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ih = 0; ih < KH; ++ih) p[ih] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
