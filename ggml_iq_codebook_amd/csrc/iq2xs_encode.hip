@@ -599,6 +599,17 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
                     if (bad_block) {
 #pragma unroll
                         for (int j = 0; j < 8; ++j) ev[j] = 0.0f;
+                    } else if (grid_exact) {
+                        // xhat exact in fp32: d*(2k+1) has at most 16
+                        // significant bits and a bf16-exact q at most 8, so
+                        // the product has at most 24; one rounding of xhat - x.
+                        const float sk = d * (float)(2 * kr + 1);
+                        const float* q = sgrid + entry_off<kChunk>(idx);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float sg = (!zero_scale && ((neg >> j) & 1)) ? -sk : sk;
+                            ev[j] = sg * q[j] - xo[j];
+                        }
                     } else {
                         // xhat in fp64 (exact: d*(2k+1) has at most 16
                         // significant bits), one rounding of xhat - x to fp32.
