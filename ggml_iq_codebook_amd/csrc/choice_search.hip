@@ -93,6 +93,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     __shared__ __align__(16) float hdiag[G * kHB];        // H_gg blocks [g][i][j]
     __shared__ __align__(16) float ecurT[256 * kRows];      // current errors, [column][row]
     __shared__ __align__(16) float part[4 * KH * 64 * 4]; // the waves' partial rest tiles
+    __shared__ __align__(16) float enew[L * kRows];       // the decided group's errors, [i][row]
     __shared__ __align__(16) float rest[kRows * kHR];     // r_g - H_gg e_cur,g, [row][i]
     __shared__ __align__(16) float qself[kRows * kQS];    // e_gc^T H_gg e_gc, [row][g*C + c]
     __shared__ int pick0[kRows * G];                      // step-2 picks
@@ -260,16 +261,14 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         for (int s = 0; s < KS; ++s) h[s] = Hb[(gx * L + 4 * s + lq) * 256 + gn * L + 16 * wave + lc];
     };
     // The wave's partial tiles, columns of gn and gx (gx < 0: none) left out
-    // (wave-uniform conditions).  The errors of gx are being decided and
-    // rewritten in LDS meanwhile, so they are not read.  All B operands are
-    // read before the products start.
+    // (wave-uniform conditions).  The errors in LDS do not change while this
+    // runs: a decision stages its group's new errors apart and they are copied
+    // in after the next barrier.  All B operands are read before the products
+    // start.
     auto partial = [&](int gn, int gx, v4f (&p)[KH]) {
         float bv[kPS];
 #pragma unroll
-        for (int s = 0; s < kPS; ++s) {
-            const int kg = (64 * wave + 4 * s) / L;             // wave-uniform
-            bv[s] = kg == gx ? 0.0f : ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
-        }
+        for (int s = 0; s < kPS; ++s) bv[s] = ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ih = 0; ih < KH; ++ih) p[ih] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -299,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         }
         if (gx >= 0) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) d = mfma4(hX[s], ecurT[(gx * L + 4 * s + lq) * kRows + lc], d);
+            for (int s = 0; s < KS; ++s) d = mfma4(hX[s], enew[(4 * s + lq) * kRows + lc], d);
         }
         *reinterpret_cast<float4*>(&rest[lc * kHR + 16 * ih + 4 * lq]) =
             make_float4(d[0], d[1], d[2], d[3]);
@@ -359,18 +358,25 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             const uint32_t rcur = (uint32_t)(__ballot(mine) >> rsh) & 0xffffu;
             const bool move = req != 0u && (req & rcur) == 0u;
             const int bc = __builtin_ctz(req | 0x10000u);
+            // The row's new errors of group g (the new pick's, or the current
+            // pick's when it stays), staged for the rest of gn.
+            if (move ? scand == bc : mine) {
+#pragma unroll
+                for (int i = 0; i < L; ++i) enew[i * kRows + srow] = cv[i];
+            }
+            if (move) pmask = (pmask & ~(1u << g)) | ((uint32_t)(scand == bc) << g);
+            store_partial(pp);
+            __syncthreads();
+
+            // The rest of gn with the errors of g just decided; the rows that
+            // moved update their errors of g.
+            finish_rest(g);
             if (move && scand == bc) {
 #pragma unroll
                 for (int i = 0; i < L; ++i) ecurT[(g * L + i) * kRows + srow] = cv[i];
             }
-            if (move) pmask = (pmask & ~(1u << g)) | ((uint32_t)(scand == bc) << g);
-            store_partial(pp);
 #pragma unroll
             for (int i = 0; i < L; ++i) cv[i] = cvn[i];
-            __syncthreads();
-
-            // The rest of gn with the errors of g just decided.
-            finish_rest(g);
 #pragma unroll
             for (int ih = 0; ih < KH; ++ih)
 #pragma unroll
