@@ -27,9 +27,13 @@
 // with a literal multiplier; the choice cost of a scale group is (2k+1) times
 // the sum of its two groups' minima.
 //
-// Layout: a wave owns 16 groups (half a block); matrix column j = lane%16 is
-// group j, the lane's accumulator rows are entries 4*(lane/16)+r of each
-// 16-entry tile.  A 1024-thread workgroup runs 8 blocks per pass and 2 passes
+// Two kernels.  The payload encode (iq2xs_payload_wide_kernel, below) runs
+// 32 x 32 matrix tiles with a wave per block.  The other outputs (every
+// choice, fake quant, candidates) run iq2xs_kernel with 16 x 16 tiles.
+//
+// Layout of iq2xs_kernel: a wave owns 16 groups (half a block); matrix
+// column j = lane%16 is group j, the lane's accumulator rows are entries
+// 4*(lane/16)+r of each 16-entry tile.  A 1024-thread workgroup runs 8 blocks per pass and 2 passes
 // per set of 16 blocks; the workgroups are persistent (one per CU) and stage
 // the grid once in LDS (q and q^2 as fp32 and as bf16, and a padded fp32 copy
 // for the rescans: 85 KiB).  Value-only minima (v_min3); each lane records
@@ -654,6 +658,390 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Payload encode in 32 x 32 matrix tiles: a wave owns a whole block.
+//
+// v_mfma_f32_32x32x16_bf16 takes the 32 groups of the block as the 32 columns
+// (lane l: column l%32) and 32 grid entries as the rows; the lane holds 16 of
+// the rows (8*(v/4) + 4*(l/32) + v%4, v = 0..15), so each group is covered by
+// two lanes instead of four, and the per-group work outside the sweep (signs,
+// split, costs, choice, packing) is repeated twice instead of four times.  K
+// is 16 per product: the three bf16 parts of the group side go in two
+// products per output (parts 0 and 1 in the lanes' two K halves, then part 2
+// and zeros).  The payload is written straight from the lanes (coalesced
+// 16-bit codes), so waves never wait for each other after the grid staging.
+// ---------------------------------------------------------------------------
+typedef float v16f __attribute__((ext_vector_type(16)));
+constexpr int kWTile = 32;                 // entries per wide tile
+constexpr int kWChunkTiles = 2;            // wide tiles per tracking chunk
+constexpr int kWChunk = kWTile * kWChunkTiles;
+
+__device__ __forceinline__ v16f mfma32(v8bf a, v8bf b, v16f c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The 16 keys (2k+1)*N + P' of the lane's 16 entries folded into the minima
+// (a tree of three-input minima: 8 per local scale).
+__device__ __forceinline__ void fold_wide(const v16f& pn, const v16f& nn, float (&best)[16])
+{
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const float mk = (float)(2 * k + 1);
+        float key[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) key[v] = __builtin_fmaf(nn[v], mk, pn[v]);
+        const float a0 = fminf(fminf(key[0], key[1]), key[2]);
+        const float a1 = fminf(fminf(key[3], key[4]), key[5]);
+        const float a2 = fminf(fminf(key[6], key[7]), key[8]);
+        const float a3 = fminf(fminf(key[9], key[10]), key[11]);
+        const float a4 = fminf(fminf(key[12], key[13]), key[14]);
+        const float a5 = fminf(fminf(key[15], best[k]), a0);
+        best[k] = fminf(fminf(fminf(fminf(a1, a2), a3), a4), a5);
+    }
+}
+
+// After chunk ch: record ch for every minimum it lowered, against the
+// snapshot of the minima kept in LDS (four float4 per lane).
+__device__ __forceinline__ void track_chunk_lds(int ch, const float (&best)[16], float4* snap,
+                                                uint32_t (&chunk_of)[2])
+{
+    const uint32_t chrep = (uint32_t)ch * 0x11111111u;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 o = snap[q4 * kThreads];
+        const float old[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = 4 * q4 + i;
+            const uint32_t msk = best[k] < old[i] ? (0xfu << (4 * (k & 7))) : 0u;
+            chunk_of[k >> 3] = (chunk_of[k >> 3] & ~msk) | (chrep & msk);
+        }
+        snap[q4 * kThreads] = make_float4(best[4 * q4], best[4 * q4 + 1], best[4 * q4 + 2], best[4 * q4 + 3]);
+    }
+}
+
+// Entry of lane row v (0..15) of wide tile t for the lane half hl.
+__device__ __forceinline__ int wide_entry(int t, int hl, int v)
+{
+    return kWTile * t + 8 * (v >> 2) + 4 * hl + (v & 3);
+}
+
+// VALU rescan for local scale k over rows v0 .. v0+nv-1 of half hs in both
+// tiles of chunk `chunk`: the lowest entry with the least key.
+__device__ __forceinline__ int rescan_wide(const float* __restrict__ sg, int chunk, int hs, int v0,
+                                           int nv, int k, const float (&wxs)[8],
+                                           const float (&w)[8], float inv_d, float* key_out)
+{
+    const float mk = (float)(2 * k + 1);
+    int idx = -1;
+    float vbest = 0.0f;
+    for (int tt = 0; tt < kWChunkTiles; ++tt) {
+        for (int v = v0; v < v0 + nv; ++v) {
+            const int e = wide_entry(chunk * kWChunkTiles + tt, hs, v);
+            const float2* p = reinterpret_cast<const float2*>(sg + entry_off<kWChunk>(e));
+            float q[8], q2[8];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float2 u = p[t], u2 = p[4 + t];
+                q[2 * t] = u.x; q[2 * t + 1] = u.y;
+                q2[2 * t] = u2.x; q2[2 * t + 1] = u2.y;
+            }
+            float P = 0.0f, N = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                P = __builtin_fmaf(wxs[j], q[j], P);
+                N = __builtin_fmaf(w[j], q2[j], N);
+            }
+            const float key = __builtin_fmaf(N, mk, (-2.0f * P) * inv_d);
+            if (idx < 0 || key < vbest || (key == vbest && e < idx)) { vbest = key; idx = e; }
+        }
+    }
+    *key_out = vbest;
+    return idx;
+}
+
+template <int kDT>
+__global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs a)
+{
+    __shared__ float sgrid[kMaxGrid * kEntryStride + 2 * (kMaxGrid / 32)];  // q[0..7], q^2[0..7]
+    __shared__ uint4 sbq[kMaxGrid];                     // entry e: q[0..7] as bf16
+    __shared__ uint4 sbq2[kMaxGrid];                    // entry e: q^2[0..7] as bf16
+    __shared__ int sgrid_bad, sgrid_inexact;
+    __shared__ float4 ssnap[4 * kThreads];              // per lane: the minima at the last chunk end
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int n = a.grid_size;
+    const int nchunks = (n + kWChunk - 1) / kWChunk;
+    const int npad = nchunks * kWChunk;
+
+    if (tid == 0) { sgrid_bad = 0; sgrid_inexact = 0; }
+    __syncthreads();
+    {
+        int bad = 0, inexact = 0;
+        for (int i = tid; i < npad * 4; i += kThreads) {
+            const int e = i >> 2, t = i & 3;
+            const int src = e < n ? e : n - 1;
+            const float a0 = a.grid[8 * src + 2 * t], a1 = a.grid[8 * src + 2 * t + 1];
+            bad |= !(a0 >= 0.0f && finite_f32(a0) && a1 >= 0.0f && finite_f32(a1));
+            float2* ge = reinterpret_cast<float2*>(sgrid + entry_off<kWChunk>(e));
+            ge[t] = make_float2(a0, a1);
+            ge[4 + t] = make_float2(a0 * a0, a1 * a1);
+            inexact |= !(bf16_exact_with_square(a0) && bf16_exact_with_square(a1));
+            reinterpret_cast<uint32_t*>(sbq)[i] = bf16_bits(a0) | (bf16_bits(a1) << 16);
+            reinterpret_cast<uint32_t*>(sbq2)[i] = bf16_bits(a0 * a0) | (bf16_bits(a1 * a1) << 16);
+        }
+        if (bad) sgrid_bad = 1;
+        if (inexact) sgrid_inexact = 1;
+    }
+    __syncthreads();
+    const bool grid_bad = sgrid_bad != 0;
+    const bool grid_exact = sgrid_inexact == 0;     // workgroup-uniform
+    if (grid_bad && tid == 0) report(a.status, IQ_ERR_GRID);
+
+    // Persistent workgroups: the grid is staged once, then each wave takes
+    // blocks kWavesPerWG apart.
+    for (int64_t blk = (int64_t)blockIdx.x * kWavesPerWG + wave; blk < a.g.nblocks;
+         blk += (int64_t)gridDim.x * kWavesPerWG) {
+        // The lane's indices, formed in every block from an opaque copy of
+        // the lane number: offsets derived from them are recomputed here
+        // rather than held (and spilled) across the blocks.
+        int ln = lane;
+        __asm__ volatile("" : "+v"(ln));
+        const int g = ln & 31;              // group in block = matrix column
+        const int hl = ln >> 5;             // K half of the operands / row half of the result
+        const int m = g >> 1;               // scale group
+        const int64_t bt = blk / a.g.blocks_per_batch;
+        const int64_t cb = blk % a.g.blocks_per_row;
+        const WeightBlock<kDT> xb(a.w, blk);
+        const float* wblk = a.imp ? a.imp + bt * a.g.cols + cb * kBlockElems : nullptr;
+
+        int err = 0;
+        float amax = 0.0f;
+        {
+            const float4 xv = xb.quad(lane);
+            const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (!finite_f32(xs[t])) err = IQ_ERR_NONFINITE;
+                amax = fmaxf(amax, fabsf(xs[t]));
+            }
+            if (wblk && !err) {
+                const float4 wv = reinterpret_cast<const float4*>(wblk)[lane];
+                const float ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (!(ws[t] >= 0.0f) || !finite_f32(ws[t])) err = IQ_ERR_IMPORTANCE;
+            }
+        }
+        if (err) report(a.status, err);
+        const bool block_bad = __ballot(err != 0) != 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+
+        uint32_t dh;
+        if (a.scales) {
+            dh = (uint32_t)a.scales[blk];
+        } else {
+            const float t = amax / 155.0f;
+            const float u = t * 0.61f;
+            dh = f32_to_f16_bits(u);
+        }
+        const bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
+        dh &= 0x7fffu;
+        if (scale_bad && !block_bad && lane == 0) report(a.status, IQ_ERR_SCALE_RANGE);
+        const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
+
+        int forced = -1;
+        bool choice_bad = false;
+        if (a.choices) {
+            int ln = lane;                  // opaque: the address is formed here, not hoisted
+            __asm__ volatile("" : "+v"(ln));
+            const int cv = ln < 16 ? a.choices[blk * 16 + ln] : 0;
+            const bool bad = cv < 0 || cv > 15;
+            if (bad) report(a.status, IQ_ERR_ARG);
+            choice_bad = __ballot(bad) != 0;
+            forced = choice_bad ? -1 : a.choices[blk * 16 + m];
+        }
+        const bool bad_block = grid_bad || block_bad || scale_bad || choice_bad;
+        const bool zero_scale = dh == 0u;
+        const bool skip = bad_block || zero_scale;
+
+        float x[8], w[8];
+        load_group(xb, wblk, g, skip, x, w);
+        const int neg = group_signs(x, w);
+        const float inv_d = skip ? 1.0f : 1.0f / d;
+
+        float best[16];
+        uint32_t chunk_of[2] = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 16; ++k) best[k] = __builtin_inff();
+        float4* snap = ssnap + tid;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) snap[q4 * kThreads] = make_float4(best[0], best[0], best[0], best[0]);
+        const v16f zero16 = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
+                             0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        if (grid_exact) {
+            // The lane's K half: part hl of the exact three-way bf16 split of
+            // -2*(w*sign*x)/d and of w (first product), part 2 or zeros
+            // (second product).
+            uint32_t hp1[8], hp2[8], hw1[8], hw2[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float v = w[j] * x[j];
+                if ((neg >> j) & 1) v = -v;
+                v = -2.0f * (v * inv_d);
+                hp1[j] = split_part(v, hl);
+                hp2[j] = hl == 0 ? split_part(v, 2) : 0u;
+                hw1[j] = split_part(w[j], hl);
+                hw2[j] = hl == 0 ? split_part(w[j], 2) : 0u;
+            }
+            const v8bf opp1 = as_v8bf(make_uint4(hp1[0] | (hp1[1] << 16), hp1[2] | (hp1[3] << 16),
+                                                 hp1[4] | (hp1[5] << 16), hp1[6] | (hp1[7] << 16)));
+            const v8bf opp2 = as_v8bf(make_uint4(hp2[0] | (hp2[1] << 16), hp2[2] | (hp2[3] << 16),
+                                                 hp2[4] | (hp2[5] << 16), hp2[6] | (hp2[7] << 16)));
+            const v8bf opw1 = as_v8bf(make_uint4(hw1[0] | (hw1[1] << 16), hw1[2] | (hw1[3] << 16),
+                                                 hw1[4] | (hw1[5] << 16), hw1[6] | (hw1[7] << 16)));
+            const v8bf opw2 = as_v8bf(make_uint4(hw2[0] | (hw2[1] << 16), hw2[2] | (hw2[3] << 16),
+                                                 hw2[4] | (hw2[5] << 16), hw2[6] | (hw2[7] << 16)));
+            for (int ch = 0; ch < nchunks; ++ch) {
+                for (int tt = 0; tt < kWChunkTiles; ++tt) {
+                    const int e = (ch * kWChunkTiles + tt) * kWTile + g;
+                    const v8bf aq = as_v8bf(sbq[e]), aq2 = as_v8bf(sbq2[e]);
+                    const v16f pn = mfma32(aq, opp2, mfma32(aq, opp1, zero16));
+                    const v16f nn = mfma32(aq2, opw2, mfma32(aq2, opw1, zero16));
+                    fold_wide(pn, nn, best);
+                }
+                track_chunk_lds(ch, best, snap, chunk_of);
+            }
+        } else {
+            // fp32 operands (v_mfma_f32_32x32x2_f32, K = 2): product s takes
+            // elements 2s + hl of the group and of the entries.
+            float bp[4], bw[4];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int j = 2 * s2 + hl;
+                float v = w[j] * x[j];
+                if ((neg >> j) & 1) v = -v;
+                bp[s2] = -2.0f * (v * inv_d);
+                bw[s2] = w[j];
+            }
+            for (int ch = 0; ch < nchunks; ++ch) {
+                for (int tt = 0; tt < kWChunkTiles; ++tt) {
+                    const int e = (ch * kWChunkTiles + tt) * kWTile + g;
+                    const float* q = sgrid + entry_off<kWChunk>(e);
+                    v16f pn = zero16, nn = zero16;
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        pn = __builtin_amdgcn_mfma_f32_32x32x2f32(q[2 * s2 + hl], bp[s2], pn, 0, 0, 0);
+                        nn = __builtin_amdgcn_mfma_f32_32x32x2f32(q[8 + 2 * s2 + hl], bw[s2], nn, 0, 0, 0);
+                    }
+                    fold_wide(pn, nn, best);
+                }
+                track_chunk_lds(ch, best, snap, chunk_of);
+            }
+        }
+
+        // The signed weighted values again, rebuilt from memory.
+        __asm__ volatile("" ::: "memory");
+        load_group(xb, wblk, g, skip, x, w);
+        float wxs[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float wx = w[j] * x[j];
+            wxs[j] = ((neg >> j) & 1) ? -wx : wx;
+        }
+
+        // Scale-group costs: the lesser minimum of each group's two lanes,
+        // summed over the two groups, times 2k+1.
+        float cost[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            float v = fminf(best[k], __shfl_xor(best[k], 32));
+            cost[k] = (float)(2 * k + 1) * (v + __shfl_xor(v, 1));
+        }
+
+        // Entry of local scale k for this lane's group: the lane of the
+        // column whose minimum is least holds it; both lanes rescan half of
+        // its chunk's entries (lowest entry of least key).  With equal minima
+        // in the two lanes of any column, every lane rescans its own entries
+        // and the lane of least minimum, then lowest entry, wins.
+        auto pick = [&](int k) -> int {
+            float lm = best[0];
+#pragma unroll
+            for (int c = 1; c < 16; ++c)
+                if (k == c) lm = best[c];
+            const int tchunk = (int)((chunk_of[k >> 3] >> (4 * (k & 7))) & 0xfu);
+            const float om = __shfl_xor(lm, 32);
+            const bool tie = __ballot(om == lm) != 0;                // wave-uniform
+            int idx;
+            float key;
+            if (!tie) {
+                const int hs = (om < lm) ? (hl ^ 1) : hl;             // holder half
+                const int tch = __shfl(tchunk, g + 32 * hs);
+                idx = rescan_wide(sgrid, tch, hs, 8 * hl, 8, k, wxs, w, inv_d, &key);
+                const float ok = __shfl_xor(key, 32);
+                const int oi = __shfl_xor(idx, 32);
+                if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
+            } else {
+                idx = rescan_wide(sgrid, tchunk, hl, 0, 16, k, wxs, w, inv_d, &key);
+                const int oi = __shfl_xor(idx, 32);
+                if (om < lm || (om == lm && oi < idx)) idx = oi;
+            }
+            return idx < n ? idx : n - 1;
+        };
+
+        int kstar = 0;
+        float cbv = cost[0];
+#pragma unroll
+        for (int k = 1; k < 16; ++k)
+            if (cost[k] < cbv) { cbv = cost[k]; kstar = k; }
+        int idx;
+        if (forced >= 0) {                      // wave-uniform
+            kstar = forced;
+            idx = pick(kstar);
+        } else {
+            int k2 = kstar == 0 ? 1 : 0;
+            float c2 = cost[k2];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (k != kstar && cost[k] < c2) { c2 = cost[k]; k2 = k; }
+            const bool near = !skip && c2 - cbv <= 0x1p-18f * fabsf(cbv);
+            if (__ballot(near) == 0) {
+                idx = pick(kstar);
+            } else {
+                const int i1 = pick(kstar);
+                const int i2 = pick(k2);
+                __asm__ volatile("" ::: "memory");
+                float xr[8], wr[8];
+                load_group(xb, wblk, g, skip, xr, wr);
+                const double dd = (double)d;
+                double e1 = group_error64(xr, wr, neg, sgrid + entry_off<kWChunk>(i1),
+                                          dd * (double)(2 * kstar + 1));
+                double e2 = group_error64(xr, wr, neg, sgrid + entry_off<kWChunk>(i2),
+                                          dd * (double)(2 * k2 + 1));
+                e1 += __shfl_xor(e1, 1);        // the other group of the scale group
+                e2 += __shfl_xor(e2, 1);
+                const bool take2 = near && (e2 < e1 || (e2 == e1 && k2 < kstar));
+                idx = take2 ? i2 : i1;
+                if (take2) kstar = k2;
+            }
+        }
+        const int kodd = __shfl_xor(kstar, 2);
+        const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
+        if (hl == 0 && a.out) {
+            // d, the 32 codes (16-bit, one per lane, contiguous) and the 16
+            // scale nibbles; a rejected or zero-scale block is all zeros.
+            uint8_t* ob = a.out + blk * kBlockBytes;
+            *reinterpret_cast<uint16_t*>(ob + 2 + 2 * g) = skip ? (uint16_t)0 : (uint16_t)code;
+            if ((g & 3) == 0) ob[66 + (g >> 2)] = skip ? (uint8_t)0 : (uint8_t)(kstar | (kodd << 4));
+            if (g == 0) *reinterpret_cast<uint16_t*>(ob) = skip ? (uint16_t)0 : (uint16_t)dh;
+        }
+    }
+}
+
 // One workgroup per compute unit (the LDS holds one), or one per set of 16
 // blocks when there are fewer sets.
 unsigned persistent_wgs(const BlockGeom& g)
@@ -674,8 +1062,7 @@ hipError_t launch_mode(const Iq2xsArgs& a, int mode, hipStream_t stream)
         hipLaunchKernelGGL((iq2xs_kernel<kModeCandidates, kDT>), dim3(wgs), dim3(kThreads), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((iq2xs_kernel<kModePayload, kDT>), dim3(wgs), dim3(kThreads), 0, stream,
-                           a);
+        hipLaunchKernelGGL((iq2xs_payload_wide_kernel<kDT>), dim3(wgs), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
