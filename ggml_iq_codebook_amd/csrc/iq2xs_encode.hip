@@ -721,6 +721,29 @@ __device__ __forceinline__ void track_chunk_lds(int ch, const float (&best)[16],
     }
 }
 
+// Exchange with the lane 1 or 2 away inside a quad (DPP quad_perm): no
+// address register, unlike a shuffle.
+template <int kCtrl>
+__device__ __forceinline__ float quad_xchg(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                                 0xf, 0xf, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ int quad_xchg(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ double quad_xchg(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)quad_xchg<kCtrl>((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)quad_xchg<kCtrl>((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e;
+
 // Entry of lane row v (0..15) of wide tile t for the lane half hl.
 __device__ __forceinline__ int wide_entry(int t, int hl, int v)
 {
@@ -769,15 +792,17 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
     __shared__ uint4 sbq2[kMaxGrid];                    // entry e: q^2[0..7] as bf16
     __shared__ int sgrid_bad, sgrid_inexact;
     __shared__ float4 ssnap[4 * kThreads];              // per lane: the minima at the last chunk end
+    __shared__ uint16_t sout16[kWavesPerWG * kBlockBytes / 2];    // the set's payloads
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: block pointers in SGPRs
     const int n = a.grid_size;
     const int nchunks = (n + kWChunk - 1) / kWChunk;
     const int npad = nchunks * kWChunk;
 
     if (tid == 0) { sgrid_bad = 0; sgrid_inexact = 0; }
+    for (int i = tid; i < kWavesPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     {
         int bad = 0, inexact = 0;
@@ -801,10 +826,14 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
     const bool grid_exact = sgrid_inexact == 0;     // workgroup-uniform
     if (grid_bad && tid == 0) report(a.status, IQ_ERR_GRID);
 
-    // Persistent workgroups: the grid is staged once, then each wave takes
-    // blocks kWavesPerWG apart.
-    for (int64_t blk = (int64_t)blockIdx.x * kWavesPerWG + wave; blk < a.g.nblocks;
-         blk += (int64_t)gridDim.x * kWavesPerWG) {
+    // Persistent workgroups: the grid is staged once, then each workgroup
+    // takes every gridDim.x-th set of 16 blocks, a block per wave; the set's
+    // payloads are staged in LDS and stored together (whole cache lines).
+    const int64_t nsets = (a.g.nblocks + kWavesPerWG - 1) / kWavesPerWG;
+    for (int64_t set = blockIdx.x; set < nsets; set += gridDim.x) {
+    if (set != blockIdx.x) __syncthreads();     // the previous set's payloads are out
+    const int64_t blk = set * kWavesPerWG + wave;
+    if (blk < a.g.nblocks) {                    // wave-uniform
         // The lane's indices, formed in every block from an opaque copy of
         // the lane number: offsets derived from them are recomputed here
         // rather than held (and spilled) across the blocks.
@@ -852,9 +881,9 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
         const bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
         dh &= 0x7fffu;
         if (scale_bad && !block_bad && lane == 0) report(a.status, IQ_ERR_SCALE_RANGE);
+        dh = __builtin_amdgcn_readfirstlane(dh);           // the same in every lane
         const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
 
-        int forced = -1;
         bool choice_bad = false;
         if (a.choices) {
             int ln = lane;                  // opaque: the address is formed here, not hoisted
@@ -863,7 +892,6 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
             const bool bad = cv < 0 || cv > 15;
             if (bad) report(a.status, IQ_ERR_ARG);
             choice_bad = __ballot(bad) != 0;
-            forced = choice_bad ? -1 : a.choices[blk * 16 + m];
         }
         const bool bad_block = grid_bad || block_bad || scale_bad || choice_bad;
         const bool zero_scale = dh == 0u;
@@ -944,14 +972,17 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
             }
         }
 
-        // The signed weighted values again, rebuilt from memory.
+        // The values, the signs and the forced choice again, rebuilt from
+        // memory rather than held through the sweep.
         __asm__ volatile("" ::: "memory");
         load_group(xb, wblk, g, skip, x, w);
+        const int neg2 = group_signs(x, w);
+        const int forced = (a.choices && !choice_bad) ? a.choices[blk * 16 + m] : -1;
         float wxs[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float wx = w[j] * x[j];
-            wxs[j] = ((neg >> j) & 1) ? -wx : wx;
+            wxs[j] = ((neg2 >> j) & 1) ? -wx : wx;
         }
 
         // Scale-group costs: the lesser minimum of each group's two lanes,
@@ -960,7 +991,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             float v = fminf(best[k], __shfl_xor(best[k], 32));
-            cost[k] = (float)(2 * k + 1) * (v + __shfl_xor(v, 1));
+            cost[k] = (float)(2 * k + 1) * (v + quad_xchg<kQuadXor1>(v));
         }
 
         // Entry of local scale k for this lane's group: the lane of the
@@ -1018,27 +1049,47 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
                 float xr[8], wr[8];
                 load_group(xb, wblk, g, skip, xr, wr);
                 const double dd = (double)d;
-                double e1 = group_error64(xr, wr, neg, sgrid + entry_off<kWChunk>(i1),
+                double e1 = group_error64(xr, wr, neg2, sgrid + entry_off<kWChunk>(i1),
                                           dd * (double)(2 * kstar + 1));
-                double e2 = group_error64(xr, wr, neg, sgrid + entry_off<kWChunk>(i2),
+                double e2 = group_error64(xr, wr, neg2, sgrid + entry_off<kWChunk>(i2),
                                           dd * (double)(2 * k2 + 1));
-                e1 += __shfl_xor(e1, 1);        // the other group of the scale group
-                e2 += __shfl_xor(e2, 1);
+                e1 += quad_xchg<kQuadXor1>(e1);  // the other group of the scale group
+                e2 += quad_xchg<kQuadXor1>(e2);
                 const bool take2 = near && (e2 < e1 || (e2 == e1 && k2 < kstar));
                 idx = take2 ? i2 : i1;
                 if (take2) kstar = k2;
             }
         }
-        const int kodd = __shfl_xor(kstar, 2);
-        const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
-        if (hl == 0 && a.out) {
-            // d, the 32 codes (16-bit, one per lane, contiguous) and the 16
-            // scale nibbles; a rejected or zero-scale block is all zeros.
-            uint8_t* ob = a.out + blk * kBlockBytes;
-            *reinterpret_cast<uint16_t*>(ob + 2 + 2 * g) = skip ? (uint16_t)0 : (uint16_t)code;
-            if ((g & 3) == 0) ob[66 + (g >> 2)] = skip ? (uint8_t)0 : (uint8_t)(kstar | (kodd << 4));
-            if (g == 0) *reinterpret_cast<uint16_t*>(ob) = skip ? (uint16_t)0 : (uint16_t)dh;
+        const int kodd = quad_xchg<kQuadXor2>(kstar);
+        const uint32_t code = (uint32_t)idx | ((uint32_t)(neg2 & 0x7f) << 9);
+        if (hl == 0 && !skip) {
+            // d, the 32 codes and the 16 scale nibbles into the wave's staged
+            // block (a rejected or zero-scale block stays all zeros).
+            uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBlockBytes;
+            ob[2 + 2 * g] = (uint8_t)(code & 0xff);
+            ob[3 + 2 * g] = (uint8_t)(code >> 8);
+            if ((g & 3) == 0) ob[66 + (g >> 2)] = (uint8_t)(kstar | (kodd << 4));
+            if (g == 0) {
+                ob[0] = (uint8_t)(dh & 0xff);
+                ob[1] = (uint8_t)(dh >> 8);
+            }
         }
+    }
+    if (a.out) {
+        // Copy the set's payloads out and clear what was copied (each word
+        // by the thread that copied it) for the next set.
+        __syncthreads();
+        const int64_t first = set * kWavesPerWG;
+        const int64_t left = a.g.nblocks - first;
+        const int nb = left < kWavesPerWG ? (int)left : kWavesPerWG;
+        uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + first * kBlockBytes);
+        int t0 = tid;
+        __asm__ volatile("" : "+v"(t0));
+        for (int i = t0; i < nb * (kBlockBytes / 2); i += kThreads) {
+            o16[i] = sout16[i];
+            sout16[i] = 0;
+        }
+    }
     }
 }
 
