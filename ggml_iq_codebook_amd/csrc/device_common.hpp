@@ -113,6 +113,39 @@ __device__ __forceinline__ v8bf as_v8bf(uint4 u)
     return __builtin_bit_cast(v8bf, u);
 }
 
+// 32 x 32 matrix tiles (v_mfma_f32_32x32x16_bf16): lane l supplies row and
+// column l%32 of its operands with K elements 8*(l/32) .. +7, and holds rows
+// 8*(v/4) + 4*(l/32) + v%4 of column l%32 of the result in v = 0..15.
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ v16f mfma32(v8bf a, v8bf b, v16f c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Exchange with the lane 1 or 2 away inside a quad (DPP quad_perm): no
+// address register, unlike a shuffle.
+template <int kCtrl>
+__device__ __forceinline__ float quad_xchg(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                                 0xf, 0xf, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ int quad_xchg(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ double quad_xchg(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)quad_xchg<kCtrl>((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)quad_xchg<kCtrl>((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e;
+
 // One 256-value block of the weight in its storage type (iq_dtype_t), read as
 // fp32: bf16 and fp16 convert exactly, fp64 rounds to nearest even.  quad(q)
 // reads values 4q..4q+3, group(g, v) values 8g..8g+7, one(i) value i (the

@@ -744,6 +744,403 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// IQ1_S payload encode in 32 x 32 matrix tiles: a wave owns a whole block.
+//
+// v_mfma_f32_32x32x16_bf16 takes the block's 32 groups as the columns and 32
+// grid entries as the rows (the lane holds 16 of them), so each group is
+// covered by two lanes instead of four.  Two operand tables, (q+1/8)^2 and q
+// (the LDS holds the 64 KiB snapshot of the minima beside them): per tile,
+// V = -2*sum(wx*q)/d and U(+1/8) from two products each (the group side's
+// three exact bf16 parts in the two K halves of the first product and the
+// first K half of the second), the 8 keys of shift +1/8 folded, then
+// U(-1/8) = U(+1/8) + sum(q*(-w/2)) by two more products on the same
+// accumulator, and the 8 keys of shift -1/8.
+// ---------------------------------------------------------------------------
+constexpr int kW1Tile = 32;
+constexpr int kW1ChunkTiles = 4;                       // 128-entry chunks (16 for 2048 entries)
+constexpr int kW1Chunk = kW1Tile * kW1ChunkTiles;
+constexpr int kW1Slots = kMaxGrid + kMaxGrid / kW1Chunk;
+
+// The 8 keys (2k+1)*U + V of the lane's 16 entries for k = 0..7 folded into
+// best[kBase + k] (a tree of three-input minima).
+template <int kBase>
+__device__ __forceinline__ void fold_wide8(const v16f& u, const v16f& v, float (&best)[16])
+{
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float mk = (float)(2 * k + 1);
+        float key[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) key[r] = __builtin_fmaf(u[r], mk, v[r]);
+        const float a0 = fminf(fminf(key[0], key[1]), key[2]);
+        const float a1 = fminf(fminf(key[3], key[4]), key[5]);
+        const float a2 = fminf(fminf(key[6], key[7]), key[8]);
+        const float a3 = fminf(fminf(key[9], key[10]), key[11]);
+        const float a4 = fminf(fminf(key[12], key[13]), key[14]);
+        const float a5 = fminf(fminf(key[15], best[kBase + k]), a0);
+        best[kBase + k] = fminf(fminf(fminf(fminf(a1, a2), a3), a4), a5);
+    }
+}
+
+// After chunk ch: record ch for every minimum it lowered, against the
+// snapshot of the minima kept in LDS (four float4 per lane).
+__device__ __forceinline__ void track_chunk_lds1(int ch, const float (&best)[16], float4* snap,
+                                                 uint32_t (&chunk_of)[2])
+{
+    const uint32_t chrep = (uint32_t)ch * 0x11111111u;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 o = snap[q4 * kThreads];
+        const float old[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 4 * q4 + i;
+            const uint32_t msk = best[c] < old[i] ? (0xfu << (4 * (c & 7))) : 0u;
+            chunk_of[c >> 3] = (chunk_of[c >> 3] & ~msk) | (chrep & msk);
+        }
+        snap[q4 * kThreads] = make_float4(best[4 * q4], best[4 * q4 + 1], best[4 * q4 + 2], best[4 * q4 + 3]);
+    }
+}
+
+// VALU rescan for choice cs = k + 8*deltabit over rows v0 .. v0+nv-1 of half
+// hs in the tiles of chunk `chunk`: the lowest entry with the least key
+// (2k+1)*U - 2V/d, recomputed in fp32 from the group's values and weights.
+template <class GS>
+__device__ __forceinline__ int rescan_w1(const uint4* __restrict__ sq, int chunk, int hs, int v0,
+                                         int nv, int cs, const GS& src, bool zero_block, float w64,
+                                         float b4, float inv_d, float* key_out)
+{
+    float x[8], w[8];
+    __asm__ volatile("" ::: "memory");
+    src.load(zero_block, x, w);
+    const float mk = (float)(2 * (cs & 7) + 1);
+    const float dl = (cs >> 3) ? -0.25f : 0.25f;      // 2*delta
+    const float bd = (cs >> 3) ? b4 : -b4;
+    int idx = -1;
+    float vbest = 0.0f;
+    for (int tt = 0; tt < kW1ChunkTiles; ++tt) {
+        for (int v = v0; v < v0 + nv; ++v) {
+            const int e = kW1Tile * (chunk * kW1ChunkTiles + tt) + 8 * (v >> 2) + 4 * hs + (v & 3);
+            const uint4 u = sq[e + chunk];
+            const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+            float A = 0.0f, M = 0.0f, N = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                A = __builtin_fmaf(w[j] * x[j], q, A);
+                M = __builtin_fmaf(w[j], q, M);
+                N = __builtin_fmaf(w[j], fabsf(q), N);
+            }
+            const float U = __builtin_fmaf(M, dl, N + w64);
+            const float key = __builtin_fmaf(U, mk, __builtin_fmaf(A, -2.0f, bd) * inv_d);
+            if (idx < 0 || key < vbest) { vbest = key; idx = e; }
+        }
+    }
+    *key_out = vbest;
+    return idx;
+}
+
+// fp64 error of group g against entry e under choice cs (as group_error64,
+// with the wide kernel's table skew).
+template <class GS>
+__device__ __forceinline__ double group_error64_w1(const GS& src, bool zero, const uint4* sq, int e,
+                                                   int cs, float d)
+{
+    float x[8], w[8];
+    src.load(zero, x, w);
+    const uint4 u = sq[e + e / kW1Chunk];
+    const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+    const double sc = (double)d * (double)(2 * (cs & 7) + 1);
+    const double delta = (cs >> 3) ? -0.125 : 0.125;
+    double err = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double q = (double)bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+        const double r = (double)x[j] - sc * (q + delta);
+        err += (double)w[j] * r * r;
+    }
+    return err;
+}
+
+template <int kDT>
+__global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
+{
+    __shared__ uint4 wsp[kW1Slots];                    // (q[0..7] + 1/8)^2 as bf16
+    __shared__ uint4 wsq[kW1Slots];                    // q[0..7] as bf16
+    __shared__ float4 ssnap[4 * kThreads];             // per lane: the minima at the last chunk end
+    __shared__ uint16_t sout16[kWavesPerWG * kBlockBytes / 2];   // the set's payloads
+    __shared__ int sgrid_bad;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: block pointers in SGPRs
+    const int n = a.grid_size;
+    const int nchunks = (n + kW1Chunk - 1) / kW1Chunk;
+    const int npad = nchunks * kW1Chunk;
+
+    if (tid == 0) sgrid_bad = 0;
+    for (int i = tid; i < kWavesPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
+    __syncthreads();
+    {
+        const float4* gsrc = reinterpret_cast<const float4*>(a.grid);
+        int bad = 0;
+        for (int e = tid; e < npad; e += kThreads) {
+            const int src = e < n ? e : n - 1;
+            const float4 v0 = gsrc[2 * src], v1 = gsrc[2 * src + 1];
+            const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t h[8], hp[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                bad |= !(v[t] == 0.0f || v[t] == 1.0f || v[t] == -1.0f);
+                h[t] = bf16_bits(v[t]);
+                const float pp = v[t] + 0.125f;
+                hp[t] = bf16_bits(pp * pp);        // exact: 81/64, 1/64, 49/64
+            }
+            const int at = e + e / kW1Chunk;
+            wsq[at] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                 h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+            wsp[at] = make_uint4(hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16),
+                                 hp[4] | (hp[5] << 16), hp[6] | (hp[7] << 16));
+        }
+        if (bad) sgrid_bad = 1;
+    }
+    __syncthreads();
+    const bool grid_bad = sgrid_bad != 0;
+    if (grid_bad && tid == 0) report(a.status, IQ_ERR_GRID);
+
+    const int64_t nsets = (a.g.nblocks + kWavesPerWG - 1) / kWavesPerWG;
+    for (int64_t set = blockIdx.x; set < nsets; set += gridDim.x) {
+    if (set != blockIdx.x) __syncthreads();     // the previous set's payloads are out
+    const int64_t blk = set * kWavesPerWG + wave;
+    if (blk < a.g.nblocks) {                    // wave-uniform
+        int ln = lane;                          // opaque: lane offsets are formed per block
+        __asm__ volatile("" : "+v"(ln));
+        const int g = ln & 31;                  // group = matrix column
+        const int hl = ln >> 5;                 // K half / row half
+        const int sub = g >> 2;
+        const int lq = g & 3;
+        const int64_t bt = blk / a.g.blocks_per_batch;
+        const int64_t cb = blk % a.g.blocks_per_row;
+        const WeightBlock<kDT> xb(a.w, blk);
+        const float* wblk = a.imp ? a.imp + bt * a.g.cols + cb * kBlockElems : nullptr;
+        const GlobalGroup<WeightBlock<kDT>> src{xb, wblk, g};
+
+        int err = 0;
+        float amax = 0.0f;
+        {
+            const float4 xv = xb.quad(lane);
+            const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (!finite_f32(xs[t])) err = IQ_ERR_NONFINITE;
+                amax = fmaxf(amax, fabsf(xs[t]));
+            }
+            if (wblk && !err) {
+                const float4 wv = reinterpret_cast<const float4*>(wblk)[lane];
+                const float ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (!(ws[t] >= 0.0f) || !finite_f32(ws[t])) err = IQ_ERR_IMPORTANCE;
+            }
+        }
+        if (err) report(a.status, err);
+        const bool block_bad = __ballot(err != 0) != 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+
+        uint32_t dh;
+        if (a.scales) {
+            dh = (uint32_t)a.scales[blk];
+        } else {
+            const float t = amax / 16.875f;
+            const float u = t * 0.61f;
+            dh = f32_to_f16_bits(u);
+        }
+        dh = __builtin_amdgcn_readfirstlane(dh);            // the same in every lane
+        const bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
+        dh &= 0x7fffu;
+        if (scale_bad && !block_bad && lane == 0) report(a.status, IQ_ERR_SCALE_RANGE);
+        const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
+
+        bool choice_bad = false;
+        if (a.choices) {
+            int lc = lane;                      // opaque: the address is formed here, not hoisted
+            __asm__ volatile("" : "+v"(lc));
+            const int cv = lc < 8 ? a.choices[blk * 8 + lc] : 0;
+            const bool bad = cv < 0 || cv >= 16;
+            if (bad) report(a.status, IQ_ERR_ARG);
+            choice_bad = __ballot(bad) != 0;
+        }
+        const bool zero_block = grid_bad || block_bad || scale_bad || dh == 0u || choice_bad;
+
+        // The lane's group: its K half of the three-way bf16 split of
+        // -2*w*x/d, of w, and of -w/2.
+        float x[8], w[8];
+        src.load(zero_block, x, w);
+        const float inv_d = zero_block ? 1.0f : 1.0f / d;
+        float W = 0.0f, B = 0.0f;
+        uint32_t n1[8], n2[8], w1[8], w2[8], h1[8], h2[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float wxj = w[j] * x[j];
+            W += w[j];
+            B += wxj;
+            const float vn = -2.0f * (wxj * inv_d);
+            const float vh = -0.5f * w[j];
+            n1[j] = split_part(vn, hl);
+            n2[j] = hl == 0 ? split_part(vn, 2) : 0u;
+            w1[j] = split_part(w[j], hl);
+            w2[j] = hl == 0 ? split_part(w[j], 2) : 0u;
+            h1[j] = split_part(vh, hl);
+            h2[j] = hl == 0 ? split_part(vh, 2) : 0u;
+        }
+        auto pack = [](const uint32_t (&b)[8]) {
+            return as_v8bf(make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                                      b[6] | (b[7] << 16)));
+        };
+        const v8bf on1 = pack(n1), on2 = pack(n2), ow1 = pack(w1), ow2 = pack(w2);
+        const v8bf oh1 = pack(h1), oh2 = pack(h2);
+        const float w64 = W * 0.015625f;
+        const float b4 = B * 0.25f;
+        const float b4d = b4 * inv_d;               // -2*(-1/8)*B/d; +1/8 takes -b4d
+
+        float best[16];
+        uint32_t chunk_of[2] = {0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 16; ++c) best[c] = __builtin_inff();
+        float4* snap = ssnap + tid;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) snap[q4 * kThreads] = make_float4(best[0], best[0], best[0], best[0]);
+        const v16f zero16 = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
+                             0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ch = 0; ch < nchunks; ++ch) {
+            for (int tt = 0; tt < kW1ChunkTiles; ++tt) {
+                const int at = (ch * kW1ChunkTiles + tt) * kW1Tile + g + ch;
+                const v8bf ap = as_v8bf(wsp[at]), aq = as_v8bf(wsq[at]);
+                const v16f vq = mfma32(aq, on2, mfma32(aq, on1, zero16));
+                v16f uu = mfma32(ap, ow2, mfma32(ap, ow1, zero16));
+                fold_wide8<0>(uu, vq, best);
+                uu = mfma32(aq, oh2, mfma32(aq, oh1, uu));          // U(-1/8)
+                fold_wide8<8>(uu, vq, best);
+            }
+            track_chunk_lds1(ch, best, snap, chunk_of);
+        }
+
+        // Choice costs per sub-block: (2k+1) times the sum of its four groups'
+        // least keys (each the lesser of the group's two lanes, plus the
+        // -2*delta*sum(wx)/d the sweep left out).
+        int cstar = 0;
+        float cbest = 0.0f;
+        float cost[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            float m = fminf(best[c], __shfl_xor(best[c], 32));
+            m += c < 8 ? -b4d : b4d;
+            float v = m + quad_xchg<kQuadXor1>(m);
+            v += quad_xchg<kQuadXor2>(v);
+            cost[c] = (float)(2 * (c & 7) + 1) * v;
+            if (c == 0 || cost[c] < cbest) { cbest = cost[c]; cstar = c; }
+        }
+        const int forced = (a.choices && !choice_bad) ? a.choices[blk * 8 + sub] : -1;
+        if (forced >= 0) cstar = forced;
+        int c2 = 0;
+        bool near = false;
+        if (forced < 0) {                           // wave-uniform
+            float v2 = 0.0f;
+            c2 = -1;
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                if (c != cstar && (c2 < 0 || cost[c] < v2)) { c2 = c; v2 = cost[c]; }
+            near = !zero_block && v2 - cbest <= 0x1p-18f * fabsf(cbest);
+        }
+        const bool refine = __ballot(near) != 0;  // wave-uniform
+
+        // Entry for choice cs: the lane of the column whose minimum is least
+        // holds it; the two lanes split its entries of the chunk.  With equal
+        // minima in the two lanes of any column, every lane rescans its own
+        // entries and the lane of least minimum, then lowest entry, wins.
+        auto pick = [&](int cs) -> int {
+            float lm = best[0];
+#pragma unroll
+            for (int c = 1; c < 16; ++c)
+                if (cs == c) lm = best[c];
+            const int tchunk = (int)((chunk_of[cs >> 3] >> (4 * (cs & 7))) & 0xfu);
+            const float om = __shfl_xor(lm, 32);
+            const bool tie = __ballot(om == lm) != 0;                // wave-uniform
+            int idx;
+            float key;
+            if (!tie) {
+                const int hs = (om < lm) ? (hl ^ 1) : hl;             // holder half
+                const int tch = __shfl(tchunk, g + 32 * hs);
+                idx = rescan_w1(wsq, tch, hs, 8 * hl, 8, cs, src, zero_block, w64, b4, inv_d, &key);
+                const float ok = __shfl_xor(key, 32);
+                const int oi = __shfl_xor(idx, 32);
+                if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
+            } else {
+                idx = rescan_w1(wsq, tchunk, hl, 0, 16, cs, src, zero_block, w64, b4, inv_d, &key);
+                const int oi = __shfl_xor(idx, 32);
+                if (om < lm || (om == lm && oi < idx)) idx = oi;
+            }
+            return idx < n ? idx : n - 1;
+        };
+
+        int cs = cstar;
+        int idx;
+        if (!refine) {
+            idx = pick(cs);
+        } else {
+            // The runner-up within 2^-18 of the best: both in fp64 from the
+            // error's definition, summed over the sub-block; the lower error
+            // wins, the lower choice on equal errors.
+            const int i2 = pick(near ? c2 : cstar);
+            const int i1 = pick(cstar);
+            double e2 = group_error64_w1(src, zero_block, wsq, i2, near ? c2 : cstar, d);
+            double e1 = group_error64_w1(src, zero_block, wsq, i1, cstar, d);
+            e2 += quad_xchg<kQuadXor1>(e2);
+            e2 += quad_xchg<kQuadXor2>(e2);
+            e1 += quad_xchg<kQuadXor1>(e1);
+            e1 += quad_xchg<kQuadXor2>(e1);
+            idx = i1;
+            if (near && (e2 < e1 || (e2 == e1 && c2 < cstar))) { cs = c2; idx = i2; }
+        }
+
+        // IQ1_S: low byte per group, qh word per sub-block, d per block.
+        int hi = ((idx >> 8) & 7) << (3 * lq);
+        hi |= quad_xchg<kQuadXor1>(hi);
+        hi |= quad_xchg<kQuadXor2>(hi);
+        if (!zero_block && hl == 0) {
+            uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBlockBytes;
+            ob[2 + g] = (uint8_t)(idx & 0xff);
+            if (lq == 0) {
+                const uint32_t qh = (uint32_t)hi | ((uint32_t)cs << 12);
+                ob[34 + 2 * sub] = (uint8_t)(qh & 0xff);
+                ob[35 + 2 * sub] = (uint8_t)(qh >> 8);
+            }
+            if (g == 0) {
+                ob[0] = (uint8_t)(dh & 0xff);
+                ob[1] = (uint8_t)(dh >> 8);
+            }
+        }
+    }
+    if (a.out) {
+        // Copy the set's payloads out and clear what was copied (each word by
+        // the thread that copied it) for the next set.
+        __syncthreads();
+        const int64_t first = set * kWavesPerWG;
+        const int64_t left = a.g.nblocks - first;
+        const int nb = left < kWavesPerWG ? (int)left : kWavesPerWG;
+        uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + first * kBlockBytes);
+        int t0 = tid;
+        __asm__ volatile("" : "+v"(t0));
+        for (int i = t0; i < nb * (kBlockBytes / 2); i += kThreads) {
+            o16[i] = sout16[i];
+            sout16[i] = 0;
+        }
+    }
+    }
+}
+
 template <int kFmt, int kDT>
 hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
 {
@@ -760,6 +1157,8 @@ hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
     else if (mode == kModeCandidates)
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeCandidates, kDT>), grid, dim3(kThreads),
                            0, stream, a);
+    else if (kFmt == IQ_FMT_IQ1_S)
+        hipLaunchKernelGGL((iq1s_payload_wide_kernel<kDT>), grid, dim3(kThreads), 0, stream, a);
     else
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModePayload, kDT>), grid, dim3(kThreads), 0,
                            stream, a);

@@ -671,15 +671,9 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
 // and zeros).  The payload is written straight from the lanes (coalesced
 // 16-bit codes), so waves never wait for each other after the grid staging.
 // ---------------------------------------------------------------------------
-typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kWTile = 32;                 // entries per wide tile
 constexpr int kWChunkTiles = 2;            // wide tiles per tracking chunk
 constexpr int kWChunk = kWTile * kWChunkTiles;
-
-__device__ __forceinline__ v16f mfma32(v8bf a, v8bf b, v16f c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // The 16 keys (2k+1)*N + P' of the lane's 16 entries folded into the minima
 // (a tree of three-input minima: 8 per local scale).
@@ -720,29 +714,6 @@ __device__ __forceinline__ void track_chunk_lds(int ch, const float (&best)[16],
         snap[q4 * kThreads] = make_float4(best[4 * q4], best[4 * q4 + 1], best[4 * q4 + 2], best[4 * q4 + 3]);
     }
 }
-
-// Exchange with the lane 1 or 2 away inside a quad (DPP quad_perm): no
-// address register, unlike a shuffle.
-template <int kCtrl>
-__device__ __forceinline__ float quad_xchg(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
-                                                                 0xf, 0xf, false));
-}
-template <int kCtrl>
-__device__ __forceinline__ int quad_xchg(int v)
-{
-    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, false);
-}
-template <int kCtrl>
-__device__ __forceinline__ double quad_xchg(double v)
-{
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = (uint32_t)quad_xchg<kCtrl>((int)(uint32_t)u);
-    const uint32_t hi = (uint32_t)quad_xchg<kCtrl>((int)(uint32_t)(u >> 32));
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e;
 
 // Entry of lane row v (0..15) of wide tile t for the lane half hl.
 __device__ __forceinline__ int wide_entry(int t, int hl, int v)
