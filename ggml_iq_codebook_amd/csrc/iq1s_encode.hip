@@ -749,8 +749,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 //
 // v_mfma_f32_32x32x16_bf16 takes the block's 32 groups as the columns and 32
 // grid entries as the rows (the lane holds 16 of them), so each group is
-// covered by two lanes instead of four.  Two operand tables, (q+1/8)^2 and q
-// (the LDS holds the 64 KiB snapshot of the minima beside them): per tile,
+// covered by two lanes instead of four.  Two operand tables, (q+1/8)^2 and q,
+// in LDS; per tile,
 // V = -2*sum(wx*q)/d and U(+1/8) from two products each (the group side's
 // three exact bf16 parts in the two K halves of the first product and the
 // first K half of the second), the 8 keys of shift +1/8 folded, then
@@ -780,26 +780,6 @@ __device__ __forceinline__ void fold_wide8(const v16f& u, const v16f& v, float (
         const float a4 = fminf(fminf(key[12], key[13]), key[14]);
         const float a5 = fminf(fminf(key[15], best[kBase + k]), a0);
         best[kBase + k] = fminf(fminf(fminf(fminf(a1, a2), a3), a4), a5);
-    }
-}
-
-// After chunk ch: record ch for every minimum it lowered, against the
-// snapshot of the minima kept in LDS (four float4 per lane).
-__device__ __forceinline__ void track_chunk_lds1(int ch, const float (&best)[16], float4* snap,
-                                                 uint32_t (&chunk_of)[2])
-{
-    const uint32_t chrep = (uint32_t)ch * 0x11111111u;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 o = snap[q4 * kThreads];
-        const float old[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = 4 * q4 + i;
-            const uint32_t msk = best[c] < old[i] ? (0xfu << (4 * (c & 7))) : 0u;
-            chunk_of[c >> 3] = (chunk_of[c >> 3] & ~msk) | (chrep & msk);
-        }
-        snap[q4 * kThreads] = make_float4(best[4 * q4], best[4 * q4 + 1], best[4 * q4 + 2], best[4 * q4 + 3]);
     }
 }
 
@@ -868,7 +848,6 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
 {
     __shared__ uint4 wsp[kW1Slots];                    // (q[0..7] + 1/8)^2 as bf16
     __shared__ uint4 wsq[kW1Slots];                    // q[0..7] as bf16
-    __shared__ float4 ssnap[4 * kThreads];             // per lane: the minima at the last chunk end
     __shared__ uint16_t sout16[kWavesPerWG * kBlockBytes / 2];   // the set's payloads
     __shared__ int sgrid_bad;
 
@@ -947,7 +926,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         if (err) report(a.status, err);
         const bool block_bad = __ballot(err != 0) != 0;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl(amax, ln ^ o));
 
         uint32_t dh;
         if (a.scales) {
@@ -979,13 +958,10 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         float x[8], w[8];
         src.load(zero_block, x, w);
         const float inv_d = zero_block ? 1.0f : 1.0f / d;
-        float W = 0.0f, B = 0.0f;
         uint32_t n1[8], n2[8], w1[8], w2[8], h1[8], h2[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float wxj = w[j] * x[j];
-            W += w[j];
-            B += wxj;
             const float vn = -2.0f * (wxj * inv_d);
             const float vh = -0.5f * w[j];
             n1[j] = split_part(vn, hl);
@@ -1001,17 +977,12 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         };
         const v8bf on1 = pack(n1), on2 = pack(n2), ow1 = pack(w1), ow2 = pack(w2);
         const v8bf oh1 = pack(h1), oh2 = pack(h2);
-        const float w64 = W * 0.015625f;
-        const float b4 = B * 0.25f;
-        const float b4d = b4 * inv_d;               // -2*(-1/8)*B/d; +1/8 takes -b4d
 
-        float best[16];
+        // chunk_of: 4-bit chunk index of choice c in bits 4*(c%8) of word c/8.
+        float best[16], snap[16];
         uint32_t chunk_of[2] = {0u, 0u};
 #pragma unroll
-        for (int c = 0; c < 16; ++c) best[c] = __builtin_inff();
-        float4* snap = ssnap + tid;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) snap[q4 * kThreads] = make_float4(best[0], best[0], best[0], best[0]);
+        for (int c = 0; c < 16; ++c) { best[c] = __builtin_inff(); snap[c] = best[c]; }
         const v16f zero16 = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
                              0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
         for (int ch = 0; ch < nchunks; ++ch) {
@@ -1024,8 +995,38 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
                 uu = mfma32(aq, oh2, mfma32(aq, oh1, uu));          // U(-1/8)
                 fold_wide8<8>(uu, vq, best);
             }
-            track_chunk_lds1(ch, best, snap, chunk_of);
+            const uint32_t chrep = (uint32_t)ch * 0x11111111u;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                const uint32_t msk = best[c] < snap[c] ? (0xfu << (4 * (c & 7))) : 0u;
+                chunk_of[c >> 3] = (chunk_of[c >> 3] & ~msk) | (chrep & msk);
+                snap[c] = best[c];
+            }
         }
+
+        // Lane-derived values for the rest of the block, formed here from an
+        // opaque lane id so that none is held (or spilled) through the sweep.
+        int ln2 = lane;
+        __asm__ volatile("" : "+v"(ln2) :: "memory");
+        const int g2 = ln2 & 31;
+        const int hl2 = ln2 >> 5;
+        const int sub2 = g2 >> 2;
+        const int lq2 = g2 & 3;
+        const GlobalGroup<WeightBlock<kDT>> src2{xb, wblk, g2};
+        float w64, b4;
+        {
+            float W = 0.0f, B = 0.0f;
+            src2.load(zero_block, x, w);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float wxj = w[j] * x[j];
+                W += w[j];
+                B += wxj;
+            }
+            w64 = W * 0.015625f;
+            b4 = B * 0.25f;
+        }
+        const float b4d = b4 * inv_d;               // -2*(-1/8)*B/d; +1/8 takes -b4d
 
         // Choice costs per sub-block: (2k+1) times the sum of its four groups'
         // least keys (each the lesser of the group's two lanes, plus the
@@ -1035,14 +1036,14 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         float cost[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            float m = fminf(best[c], __shfl_xor(best[c], 32));
+            float m = fminf(best[c], __shfl(best[c], ln2 ^ 32));
             m += c < 8 ? -b4d : b4d;
             float v = m + quad_xchg<kQuadXor1>(m);
             v += quad_xchg<kQuadXor2>(v);
             cost[c] = (float)(2 * (c & 7) + 1) * v;
             if (c == 0 || cost[c] < cbest) { cbest = cost[c]; cstar = c; }
         }
-        const int forced = (a.choices && !choice_bad) ? a.choices[blk * 8 + sub] : -1;
+        const int forced = (a.choices && !choice_bad) ? a.choices[blk * 8 + sub2] : -1;
         if (forced >= 0) cstar = forced;
         int c2 = 0;
         bool near = false;
@@ -1066,20 +1067,20 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
             for (int c = 1; c < 16; ++c)
                 if (cs == c) lm = best[c];
             const int tchunk = (int)((chunk_of[cs >> 3] >> (4 * (cs & 7))) & 0xfu);
-            const float om = __shfl_xor(lm, 32);
+            const float om = __shfl(lm, ln2 ^ 32);
             const bool tie = __ballot(om == lm) != 0;                // wave-uniform
             int idx;
             float key;
             if (!tie) {
-                const int hs = (om < lm) ? (hl ^ 1) : hl;             // holder half
-                const int tch = __shfl(tchunk, g + 32 * hs);
-                idx = rescan_w1(wsq, tch, hs, 8 * hl, 8, cs, src, zero_block, w64, b4, inv_d, &key);
-                const float ok = __shfl_xor(key, 32);
-                const int oi = __shfl_xor(idx, 32);
+                const int hs = (om < lm) ? (hl2 ^ 1) : hl2;             // holder half
+                const int tch = __shfl(tchunk, g2 + 32 * hs);
+                idx = rescan_w1(wsq, tch, hs, 8 * hl2, 8, cs, src2, zero_block, w64, b4, inv_d, &key);
+                const float ok = __shfl(key, ln2 ^ 32);
+                const int oi = __shfl(idx, ln2 ^ 32);
                 if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
             } else {
-                idx = rescan_w1(wsq, tchunk, hl, 0, 16, cs, src, zero_block, w64, b4, inv_d, &key);
-                const int oi = __shfl_xor(idx, 32);
+                idx = rescan_w1(wsq, tchunk, hl2, 0, 16, cs, src2, zero_block, w64, b4, inv_d, &key);
+                const int oi = __shfl(idx, ln2 ^ 32);
                 if (om < lm || (om == lm && oi < idx)) idx = oi;
             }
             return idx < n ? idx : n - 1;
@@ -1095,8 +1096,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
             // wins, the lower choice on equal errors.
             const int i2 = pick(near ? c2 : cstar);
             const int i1 = pick(cstar);
-            double e2 = group_error64_w1(src, zero_block, wsq, i2, near ? c2 : cstar, d);
-            double e1 = group_error64_w1(src, zero_block, wsq, i1, cstar, d);
+            double e2 = group_error64_w1(src2, zero_block, wsq, i2, near ? c2 : cstar, d);
+            double e1 = group_error64_w1(src2, zero_block, wsq, i1, cstar, d);
             e2 += quad_xchg<kQuadXor1>(e2);
             e2 += quad_xchg<kQuadXor2>(e2);
             e1 += quad_xchg<kQuadXor1>(e1);
@@ -1106,18 +1107,18 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         }
 
         // IQ1_S: low byte per group, qh word per sub-block, d per block.
-        int hi = ((idx >> 8) & 7) << (3 * lq);
+        int hi = ((idx >> 8) & 7) << (3 * lq2);
         hi |= quad_xchg<kQuadXor1>(hi);
         hi |= quad_xchg<kQuadXor2>(hi);
-        if (!zero_block && hl == 0) {
+        if (!zero_block && hl2 == 0) {
             uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBlockBytes;
-            ob[2 + g] = (uint8_t)(idx & 0xff);
-            if (lq == 0) {
+            ob[2 + g2] = (uint8_t)(idx & 0xff);
+            if (lq2 == 0) {
                 const uint32_t qh = (uint32_t)hi | ((uint32_t)cs << 12);
-                ob[34 + 2 * sub] = (uint8_t)(qh & 0xff);
-                ob[35 + 2 * sub] = (uint8_t)(qh >> 8);
+                ob[34 + 2 * sub2] = (uint8_t)(qh & 0xff);
+                ob[35 + 2 * sub2] = (uint8_t)(qh >> 8);
             }
-            if (g == 0) {
+            if (g2 == 0) {
                 ob[0] = (uint8_t)(dh & 0xff);
                 ob[1] = (uint8_t)(dh >> 8);
             }
