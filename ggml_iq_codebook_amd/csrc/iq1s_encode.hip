@@ -745,7 +745,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// IQ1_S payload encode in 32 x 32 matrix tiles: a wave owns a whole block.
+// IQ1_S payload encode and fake quant in 32 x 32 matrix tiles: a wave owns a
+// whole block.
 //
 // v_mfma_f32_32x32x16_bf16 takes the block's 32 groups as the columns and 32
 // grid entries as the rows (the lane holds 16 of them), so each group is
@@ -843,7 +844,8 @@ __device__ __forceinline__ double group_error64_w1(const GS& src, bool zero, con
     return err;
 }
 
-template <int kDT>
+// kMode: kModePayload or kModeFake; kDT: the weight's iq_dtype_t.
+template <int kMode, int kDT>
 __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
 {
     __shared__ uint4 wsp[kW1Slots];                    // (q[0..7] + 1/8)^2 as bf16
@@ -1123,6 +1125,29 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
                 ob[1] = (uint8_t)(dh >> 8);
             }
         }
+        if (kMode == kModeFake && hl2 == 0) {
+            // The decoded group, d*(2k+1)*(q + delta) with the payload's
+            // fields, the expression the decode kernel uses (a zero block
+            // decodes as the all-zero payload does; a rejected block is
+            // written as zeros).
+            const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
+            const uint32_t dz = zero_block ? 0u : dh;
+            const int ez = zero_block ? 0 : idx;
+            const int cz = zero_block ? 0 : cs;
+            const float sk = f16_bits_to_f32(dz) * (float)(2 * (cz & 7) + 1);
+            const float delta = (cz >> 3) ? -0.125f : 0.125f;
+            const uint4 u = wsq[ez + ez / kW1Chunk];
+            const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                v[j] = rejected ? 0.0f : sk * (q + delta);
+            }
+            float4* o = reinterpret_cast<float4*>(a.xhat + blk * kBlockElems + g2 * 8);
+            o[0] = make_float4(v[0], v[1], v[2], v[3]);
+            o[1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
     }
     if (a.out) {
         // Copy the set's payloads out and clear what was copied (each word by
@@ -1152,6 +1177,9 @@ hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
     if (mode == kModeEvery)
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeEvery, kDT>), grid, dim3(kThreads), 0,
                            stream, a);
+    else if (mode == kModeFake && kFmt == IQ_FMT_IQ1_S)
+        hipLaunchKernelGGL((iq1s_payload_wide_kernel<kModeFake, kDT>), grid, dim3(kThreads), 0,
+                           stream, a);
     else if (mode == kModeFake)
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeFake, kDT>), grid, dim3(kThreads), 0,
                            stream, a);
@@ -1159,7 +1187,8 @@ hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeCandidates, kDT>), grid, dim3(kThreads),
                            0, stream, a);
     else if (kFmt == IQ_FMT_IQ1_S)
-        hipLaunchKernelGGL((iq1s_payload_wide_kernel<kDT>), grid, dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((iq1s_payload_wide_kernel<kModePayload, kDT>), grid, dim3(kThreads), 0,
+                           stream, a);
     else
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModePayload, kDT>), grid, dim3(kThreads), 0,
                            stream, a);
