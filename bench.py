@@ -81,8 +81,8 @@ KERNEL_SOURCES = {
     "iq2_xs": ["ggml_iq_codebook_amd/csrc/iq2xs_encode.hip",
                "ggml_iq_codebook_amd/csrc/device_common.hpp"],
 }
-KERNEL_NAMES = {"iq1_s": "iq1s_payload_wide_kernel<0, 0>", "iq2_xs": "iq2xs_payload_wide_kernel<0>",
-                "iq1_m": "iq1s_encode_kernel<2, 0, 0>"}
+KERNEL_NAMES = {"iq1_s": "iq1s_payload_wide_kernel<0, 0, 0>", "iq2_xs": "iq2xs_payload_wide_kernel<0>",
+                "iq1_m": "iq1s_payload_wide_kernel<2, 0, 0>"}
 
 
 def log(*a):

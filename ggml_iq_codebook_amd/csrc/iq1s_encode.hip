@@ -844,13 +844,20 @@ __device__ __forceinline__ double group_error64_w1(const GS& src, bool zero, con
     return err;
 }
 
+// kFmt: IQ_FMT_IQ1_S (payload or fake quant) or IQ_FMT_IQ1_M (payload);
 // kMode: kModePayload or kModeFake; kDT: the weight's iq_dtype_t.
-template <int kMode, int kDT>
+template <int kFmt, int kMode, int kDT>
 __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
 {
+    // IQ1_M: 56-byte blocks, a local scale per two groups (16 choice groups
+    // of 8 choices), the shift free per group.
+    constexpr bool kM = kFmt == IQ_FMT_IQ1_M;
+    constexpr int kBB = kM ? kBlockBytesM : kBlockBytes;
+    constexpr int kCG = kM ? 16 : 8;         // choice groups per block
+    constexpr int kNC = kM ? 8 : 16;         // choices per choice group
     __shared__ uint4 wsp[kW1Slots];                    // (q[0..7] + 1/8)^2 as bf16
     __shared__ uint4 wsq[kW1Slots];                    // q[0..7] as bf16
-    __shared__ uint16_t sout16[kWavesPerWG * kBlockBytes / 2];   // the set's payloads
+    __shared__ uint16_t sout16[kWavesPerWG * kBB / 2];   // the set's payloads
     __shared__ int sgrid_bad;
 
     const int tid = threadIdx.x;
@@ -861,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
     const int npad = nchunks * kW1Chunk;
 
     if (tid == 0) sgrid_bad = 0;
-    for (int i = tid; i < kWavesPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
+    for (int i = tid; i < kWavesPerWG * kBB / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     {
         const float4* gsrc = reinterpret_cast<const float4*>(a.grid);
@@ -908,7 +915,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         const GlobalGroup<WeightBlock<kDT>> src{xb, wblk, g};
 
         int err = 0;
-        float amax = 0.0f;
+        float amax = 0.0f, ssq = 0.0f;
         {
             const float4 xv = xb.quad(lane);
             const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
@@ -917,6 +924,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
                 if (!finite_f32(xs[t])) err = IQ_ERR_NONFINITE;
                 amax = fmaxf(amax, fabsf(xs[t]));
             }
+            if (kM) ssq = ((xs[0] * xs[0] + xs[1] * xs[1]) + xs[2] * xs[2]) + xs[3] * xs[3];
             if (wblk && !err) {
                 const float4 wv = reinterpret_cast<const float4*>(wblk)[lane];
                 const float ws[4] = {wv.x, wv.y, wv.z, wv.w};
@@ -929,10 +937,29 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         const bool block_bad = __ballot(err != 0) != 0;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl(amax, ln ^ o));
+        if (kM) {
+            // the sum of squares in the fixed order the IQ1_M predictor uses:
+            // per lane left to right, then pairwise at distances 1, 2, ..., 32
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) ssq = ssq + __shfl(ssq, ln ^ o);
+        }
 
         uint32_t dh;
         if (a.scales) {
             dh = (uint32_t)a.scales[blk];
+        } else if (kM) {
+            // anchor clamp(0.58 + 0.035 * amax / rms, 0.65, 0.95); d = 0 for
+            // an all-zero block
+            dh = 0u;
+            if (amax > 0.0f) {
+                const float rms = __builtin_sqrtf(ssq / 256.0f);
+                const float ratio = amax / rms;
+                const float tk = 0.035f * ratio;
+                const float an = fminf(fmaxf(0.58f + tk, 0.65f), 0.95f);
+                const float t = amax / 16.875f;
+                const float u = t * an;
+                dh = f32_to_f16_bits(u);
+            }
         } else {
             const float t = amax / 16.875f;
             const float u = t * 0.61f;
@@ -948,8 +975,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         if (a.choices) {
             int lc = lane;                      // opaque: the address is formed here, not hoisted
             __asm__ volatile("" : "+v"(lc));
-            const int cv = lc < 8 ? a.choices[blk * 8 + lc] : 0;
-            const bool bad = cv < 0 || cv >= 16;
+            const int cv = lc < kCG ? a.choices[blk * kCG + lc] : 0;
+            const bool bad = cv < 0 || cv >= kNC;
             if (bad) report(a.status, IQ_ERR_ARG);
             choice_bad = __ballot(bad) != 0;
         }
@@ -1033,19 +1060,37 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         // Choice costs per sub-block: (2k+1) times the sum of its four groups'
         // least keys (each the lesser of the group's two lanes, plus the
         // -2*delta*sum(wx)/d the sweep left out).
+        // IQ1_M: per group and local scale k, the lesser of its two shifts'
+        // least keys (the lower shift on equal keys); per scale group, (2k+1)
+        // times the sum over its two groups.
         int cstar = 0;
         float cbest = 0.0f;
         float cost[16];
+        uint32_t shbits = 0u;        // IQ1_M: bit k = this group's shift under local scale k
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
             float m = fminf(best[c], __shfl(best[c], ln2 ^ 32));
             m += c < 8 ? -b4d : b4d;
-            float v = m + quad_xchg<kQuadXor1>(m);
-            v += quad_xchg<kQuadXor2>(v);
-            cost[c] = (float)(2 * (c & 7) + 1) * v;
-            if (c == 0 || cost[c] < cbest) { cbest = cost[c]; cstar = c; }
+            if (kM) {
+                cost[c] = m;
+            } else {
+                float v = m + quad_xchg<kQuadXor1>(m);
+                v += quad_xchg<kQuadXor2>(v);
+                cost[c] = (float)(2 * (c & 7) + 1) * v;
+                if (c == 0 || cost[c] < cbest) { cbest = cost[c]; cstar = c; }
+            }
         }
-        const int forced = (a.choices && !choice_bad) ? a.choices[blk * 8 + sub2] : -1;
+        if (kM) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const bool sh = cost[8 + k] < cost[k];
+                shbits |= (uint32_t)sh << k;
+                const float v = sh ? cost[8 + k] : cost[k];
+                cost[k] = (float)(2 * k + 1) * (v + quad_xchg<kQuadXor1>(v));
+                if (k == 0 || cost[k] < cbest) { cbest = cost[k]; cstar = k; }
+            }
+        }
+        const int forced = (a.choices && !choice_bad) ? a.choices[blk * kCG + (kM ? (g2 >> 1) : sub2)] : -1;
         if (forced >= 0) cstar = forced;
         int c2 = 0;
         bool near = false;
@@ -1053,7 +1098,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
             float v2 = 0.0f;
             c2 = -1;
 #pragma unroll
-            for (int c = 0; c < 16; ++c)
+            for (int c = 0; c < kNC; ++c)
                 if (c != cstar && (c2 < 0 || cost[c] < v2)) { c2 = c; v2 = cost[c]; }
             near = !zero_block && v2 - cbest <= 0x1p-18f * fabsf(cbest);
         }
@@ -1088,7 +1133,10 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
             return idx < n ? idx : n - 1;
         };
 
-        int cs = cstar;
+        // IQ1_M: the (k, shift) choice of this group under its scale group's k
+        auto full = [&](int k) { return kM ? k + 8 * (int)((shbits >> k) & 1u) : k; };
+        int ch = cstar;
+        int cs = full(cstar);
         int idx;
         if (!refine) {
             idx = pick(cs);
@@ -1096,24 +1144,48 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
             // The runner-up within 2^-18 of the best: both in fp64 from the
             // error's definition, summed over the sub-block; the lower error
             // wins, the lower choice on equal errors.
-            const int i2 = pick(near ? c2 : cstar);
-            const int i1 = pick(cstar);
-            double e2 = group_error64_w1(src2, zero_block, wsq, i2, near ? c2 : cstar, d);
-            double e1 = group_error64_w1(src2, zero_block, wsq, i1, cstar, d);
+            const int cs2 = full(near ? c2 : cstar);
+            const int i2 = pick(cs2);
+            const int i1 = pick(cs);
+            double e2 = group_error64_w1(src2, zero_block, wsq, i2, cs2, d);
+            double e1 = group_error64_w1(src2, zero_block, wsq, i1, cs, d);
             e2 += quad_xchg<kQuadXor1>(e2);
-            e2 += quad_xchg<kQuadXor2>(e2);
             e1 += quad_xchg<kQuadXor1>(e1);
-            e1 += quad_xchg<kQuadXor2>(e1);
+            if (!kM) {
+                e2 += quad_xchg<kQuadXor2>(e2);
+                e1 += quad_xchg<kQuadXor2>(e1);
+            }
             idx = i1;
-            if (near && (e2 < e1 || (e2 == e1 && c2 < cstar))) { cs = c2; idx = i2; }
+            if (near && (e2 < e1 || (e2 == e1 && c2 < cstar))) { ch = c2; cs = cs2; idx = i2; }
         }
 
+        if (kM) {
+            // IQ1_M: low byte per group; one nibble per group (3 high bits,
+            // shift bit); four scale words with the 3-bit local scales of four
+            // scale groups and one nibble of d each.
+            const int nib = ((idx >> 8) & 7) | ((cs >> 3) << 3);
+            const int nib_odd = quad_xchg<kQuadXor1>(nib);
+            int kk = (ch & 7) << (3 * ((g2 >> 1) & 3));
+            kk |= quad_xchg<kQuadXor2>(kk);
+            kk |= __shfl(kk, ln2 ^ 4);
+            if (!zero_block && hl2 == 0) {
+                uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBB;
+                ob[g2] = (uint8_t)(idx & 0xff);
+                if ((g2 & 1) == 0) ob[32 + (g2 >> 1)] = (uint8_t)(nib | (nib_odd << 4));
+                if ((g2 & 7) == 0) {
+                    const int wd = g2 >> 3;
+                    const uint32_t v = (uint32_t)kk | (((dh >> (4 * wd)) & 0xfu) << 12);
+                    ob[48 + 2 * wd] = (uint8_t)(v & 0xff);
+                    ob[49 + 2 * wd] = (uint8_t)(v >> 8);
+                }
+            }
+        }
         // IQ1_S: low byte per group, qh word per sub-block, d per block.
         int hi = ((idx >> 8) & 7) << (3 * lq2);
         hi |= quad_xchg<kQuadXor1>(hi);
         hi |= quad_xchg<kQuadXor2>(hi);
-        if (!zero_block && hl2 == 0) {
-            uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBlockBytes;
+        if (!kM && !zero_block && hl2 == 0) {
+            uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBB;
             ob[2 + g2] = (uint8_t)(idx & 0xff);
             if (lq2 == 0) {
                 const uint32_t qh = (uint32_t)hi | ((uint32_t)cs << 12);
@@ -1156,10 +1228,10 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         const int64_t first = set * kWavesPerWG;
         const int64_t left = a.g.nblocks - first;
         const int nb = left < kWavesPerWG ? (int)left : kWavesPerWG;
-        uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + first * kBlockBytes);
+        uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + first * kBB);
         int t0 = tid;
         __asm__ volatile("" : "+v"(t0));
-        for (int i = t0; i < nb * (kBlockBytes / 2); i += kThreads) {
+        for (int i = t0; i < nb * (kBB / 2); i += kThreads) {
             o16[i] = sout16[i];
             sout16[i] = 0;
         }
@@ -1174,24 +1246,25 @@ hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
     // 16 blocks when there are fewer sets.
     const int64_t sets = (a.g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
     const dim3 grid((unsigned)(sets < a.g.cus ? sets : a.g.cus));
-    if (mode == kModeEvery)
+    // The payload (both formats) and IQ1_S fake quant run the 32 x 32 kernel;
+    // every choice, candidates and IQ1_M fake quant the 16 x 16 one.
+    if (mode == kModeEvery) {
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeEvery, kDT>), grid, dim3(kThreads), 0,
                            stream, a);
-    else if (mode == kModeFake && kFmt == IQ_FMT_IQ1_S)
-        hipLaunchKernelGGL((iq1s_payload_wide_kernel<kModeFake, kDT>), grid, dim3(kThreads), 0,
-                           stream, a);
-    else if (mode == kModeFake)
-        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeFake, kDT>), grid, dim3(kThreads), 0,
-                           stream, a);
-    else if (mode == kModeCandidates)
+    } else if (mode == kModeFake) {
+        if constexpr (kFmt == IQ_FMT_IQ1_S)
+            hipLaunchKernelGGL((iq1s_payload_wide_kernel<kFmt, kModeFake, kDT>), grid,
+                               dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeFake, kDT>), grid, dim3(kThreads), 0,
+                               stream, a);
+    } else if (mode == kModeCandidates) {
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeCandidates, kDT>), grid, dim3(kThreads),
                            0, stream, a);
-    else if (kFmt == IQ_FMT_IQ1_S)
-        hipLaunchKernelGGL((iq1s_payload_wide_kernel<kModePayload, kDT>), grid, dim3(kThreads), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModePayload, kDT>), grid, dim3(kThreads), 0,
-                           stream, a);
+    } else {
+        hipLaunchKernelGGL((iq1s_payload_wide_kernel<kFmt, kModePayload, kDT>), grid,
+                           dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
