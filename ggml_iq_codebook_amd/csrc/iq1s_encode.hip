@@ -28,6 +28,12 @@
 // its groups' minima (the common factor d^2 dropped).  The VALU keeps
 // value-only minima (v_min3 over two entries).
 //
+// Two kernels run this search.  iq1s_payload_wide_kernel (32 x 32 tiles, a
+// wave per block, defined further down) gives the payload of both formats and
+// the IQ1_S fake quant; iq1s_encode_kernel (16 x 16 tiles, described here)
+// gives every choice, the candidates and the IQ1_M fake quant, whose many
+// picks per group rescan fewer entries per lane in this layout.
+//
 // Layout: a wave owns 16 groups (half a block): matrix column j = lane%16 is
 // group j; the lane's four accumulator rows are 4*(lane/16)+r of every
 // 16-entry tile, so the four lanes of a column cover disjoint quarters of the
@@ -58,10 +64,10 @@ constexpr int kBlocksPerWG = kBlocksPerPass * kPasses;   // 16
 constexpr int kTile = 16;                            // grid entries per matrix tile
 // Tiles per tracking chunk.  Recording chunks costs the sweep about 4
 // instructions per choice and chunk; each pick rescans one lane's entries of
-// a chunk, 4 per tile.  IQ1_S with one pick per group (payload, fake quant):
-// 16 tiles (256 entries), measured 3 % faster than 8; otherwise 8 (128
-// entries), as small as 4-bit chunk numbers allow for 2048 entries (IQ1_M
-// measured 3 % slower with 16).
+// a chunk, 4 per tile.  IQ1_S with one pick per group (payload, fake quant,
+// when this kernel ran them): 16 tiles (256 entries), measured 3 % faster
+// than 8; otherwise 8 (128 entries), as small as 4-bit chunk numbers allow
+// for 2048 entries (IQ1_M measured 3 % slower with 16).
 template <int kFmt, int kMode>
 constexpr int chunk_tiles()
 {
