@@ -8,14 +8,20 @@ per-column lognormal importance.  Inputs are resident in HBM before the timed
 region.  The JSON line carries:
 
 * value: fp32 input bytes encoded per second (GB/s), whole job;
-* roofline: the encode kernel's algorithmic FP32 flops per launch divided by
-  its average launch time (HIP events on the launch stream), against the
-  MI355X FP32 vector peak, plus the HBM traffic of one launch from the
-  committed rocprofv3 counter summary when it was taken on the current source;
-* cpu_baseline: the CPU oracle timed on a bounded sample of the same workload
-  on this host's cores.
+* roofline: for the encode kernel, its average launch time (HIP events on the
+  launch stream) against the two bounds of the search's arithmetic -- the
+  elementwise part (the 16 choice keys and the shift terms, fp32) at the
+  MI355X FP32 vector peak, and the dot products (a contraction) at the bf16
+  matrix-core peak -- whose larger time is the kernel's bound; `frac` is the
+  elementwise part's achieved rate over the FP32 vector peak (that part sets
+  the bound), `mfma` the contraction's over the matrix-core peak.  The VALU
+  issue and matrix-core busy fractions, and the HBM traffic, come from the
+  committed rocprofv3 counter summaries when they were taken on the current
+  kernel source;
+* cpu_baseline: the CPU oracle timed on the whole workload on this host's
+  cores (with the host's CPU model and core count).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c1|c3|c4|c5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c1|c3|...]
 """
 
 from __future__ import annotations
@@ -32,18 +38,30 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# Algorithmic FP32 work of the exhaustive search per (8-value group, grid entry),
-# counted once (FMA = 2 flops, compares excluded):
-#   IQ1_S weighted: 3 weighted dot products of 8 (48) + the delta terms of
-#   U(+-1/8), V(+-1/8) (10) + 16 choice keys, one FMA each (32) = 90;
-#   IQ1_S unweighted: the entry norms do not depend on the group (16 + 10 + 32) = 58;
+# Algorithmic work of the exhaustive search per (8-value group, grid entry),
+# counted once (FMA = 2 flops, compares excluded), split into the contraction
+# (the weighted dot products over the group's 8 values, a [entries x 8] by
+# [8 x groups] product) and the elementwise rest (the shift terms that turn
+# the dot products into U(+-1/8) and V(+-1/8), and the 16 choice keys, one FMA
+# each):
+#   IQ1_S weighted: 3 dot products of 8 (48) + shift terms (10) + 16 keys (32) = 90;
+#   IQ1_S unweighted: the entry norms do not depend on the group: 1 dot product
+#   (16) + 10 + 32 = 58;
 #   IQ2_XS weighted: 2 dot products (32) + 1 + 16 keys (32) = 65;
-#   IQ1_M: the IQ1_S search (16 (k, shift) keys per group and entry): 90 / 58.
-FLOPS_PER_GROUP_ENTRY = {("iq1_s", True): 90, ("iq1_s", False): 58,
-                         ("iq2_xs", True): 65, ("iq2_xs", False): 65,
-                         ("iq1_m", True): 90, ("iq1_m", False): 58}
+#   IQ1_M: the IQ1_S search (16 (k, shift) keys per group and entry).
+CONTRACTION_FLOPS = {("iq1_s", True): 48, ("iq1_s", False): 16, ("iq2_xs", True): 32,
+                     ("iq2_xs", False): 32, ("iq1_m", True): 48, ("iq1_m", False): 16}
+ELEMENTWISE_FLOPS = {("iq1_s", True): 42, ("iq1_s", False): 42, ("iq2_xs", True): 33,
+                     ("iq2_xs", False): 33, ("iq1_m", True): 42, ("iq1_m", False): 42}
+FLOPS_PER_GROUP_ENTRY = {k: CONTRACTION_FLOPS[k] + ELEMENTWISE_FLOPS[k] for k in CONTRACTION_FLOPS}
 
-PEAK_FP32_VECTOR_TFLOPS = 157.3     # MI355X: 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2 (packed) x 2.4 GHz
+# MI355X published peaks.  FP32 vector: 256 CU x 4 SIMD x 16 lanes x 2 (FMA) x 2
+# x 2.4 GHz; the last factor 2 is packed FP32 or the dual issue of two VALU
+# instructions from different waves; this library is built without packed
+# FP32, so dual issue is the only way to it.  bf16 dense matrix cores:
+# 2.5 PFLOP/s.  HBM3E: 8 TB/s.
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 
 WORKLOADS = {
@@ -71,6 +89,11 @@ WORKLOADS = {
                                   "pinned super-block scales"),
     "c2_iq1m": ("c2_iq1m_4096", "IQ1_M weighted encode of a 4096x4096 fp32 weight, N(0,0.02), "
                                 "per-column sqrt-lognormal importance, seeded 2048x8 ternary grid"),
+    # Decode of the payloads the c2 and c3 encodes write (HBM-bound).
+    "c2_dequant": ("c2_iq1s_4096", "IQ1_S decode of the 4096x4096 weighted encode's payload "
+                                   "(3.28 MB) to fp32 (67.1 MB)"),
+    "c3_dequant": ("c3_iq2xs_4096", "IQ2_XS decode of the 4096x4096 weighted encode's payload "
+                                    "(4.85 MB) to fp32 (67.1 MB)"),
 }
 
 KERNEL_SOURCES = {
@@ -81,8 +104,12 @@ KERNEL_SOURCES = {
     "iq2_xs": ["ggml_iq_codebook_amd/csrc/iq2xs_encode.hip",
                "ggml_iq_codebook_amd/csrc/device_common.hpp"],
 }
-KERNEL_NAMES = {"iq1_s": "iq1s_payload_wide_kernel<0, 0, 0>", "iq2_xs": "iq2xs_payload_wide_kernel<0>",
+KERNEL_NAMES = {"iq1_s": "iq1s_payload_wide_kernel<0, 0, 0>", "iq2_xs": "iq2xs_wide_kernel<0, 0>",
                 "iq1_m": "iq1s_payload_wide_kernel<2, 0, 0>"}
+DEQUANT_KERNELS = {"iq1_s": "dequant_iq1s_kernel", "iq2_xs": "dequant_iq2xs_kernel",
+                   "iq1_m": "dequant_iq1m_kernel"}
+DEQUANT_SOURCES = ["ggml_iq_codebook_amd/csrc/dequant.hip",
+                   "ggml_iq_codebook_amd/csrc/device_common.hpp"]
 
 
 def log(*a):
@@ -97,7 +124,7 @@ def source_sha(rels):
     return h.hexdigest()[:16]
 
 
-def _counter_kib(csv_path, kernel_substr, counter):
+def _counter_mean(csv_path, kernel_substr, counter):
     """Mean per-dispatch value of a rocprofv3 counter for the matching kernel."""
     import csv
     vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
@@ -107,38 +134,70 @@ def _counter_kib(csv_path, kernel_substr, counter):
     return sum(vals) / len(vals), len(vals)
 
 
-def record_traffic(name, fmt, pmc_dir):
-    """Turn the FETCH_SIZE / WRITE_SIZE counter runs of the encode and of a plain
-    256 MiB copy into HBM bytes per launch, written to profiles/traffic_<name>.json.
+CONFIG_FMT = {"c1": "iq1_s", "c2": "iq1_s", "c3": "iq2_xs", "c4": "iq1_s", "c5": "iq2_xs",
+              "c5_iq1s": "iq1_s", "c5_weight": "iq2_xs", "c2_every": "iq1_s", "c2_fake": "iq1_s",
+              "c2_pinned": "iq1_s", "c2_iq1m": "iq1_m", "c2_dequant": "iq1_s",
+              "c3_dequant": "iq2_xs"}
 
-    pmc_dir holds pmc_FETCH_SIZE/enc_counter_collection.csv and
-    pmc_WRITE_SIZE/enc_counter_collection.csv (or pmc_<config>_FETCH_SIZE/...
-    for a workload other than c2) and the copy runs
+# The kernel each workload's counters and traffic records belong to (the
+# dominant kernel of its step): (record name, kernel name, sources).
+_IQ1 = KERNEL_SOURCES["iq1_s"]
+_IQ2 = KERNEL_SOURCES["iq2_xs"]
+PROFILED = {
+    "c1": ("iq1s_encode_c1", KERNEL_NAMES["iq1_s"], _IQ1),
+    "c2": ("iq1s_encode_c2", KERNEL_NAMES["iq1_s"], _IQ1),
+    "c3": ("iq2xs_encode_c3", KERNEL_NAMES["iq2_xs"], _IQ2),
+    "c4": ("iq1s_encode_c4", KERNEL_NAMES["iq1_s"], _IQ1),
+    "c2_pinned": ("iq1s_encode_c2_pinned", KERNEL_NAMES["iq1_s"], _IQ1),
+    "c2_iq1m": ("iq1m_encode_c2_iq1m", KERNEL_NAMES["iq1_m"], _IQ1),
+    "c2_every": ("iq1s_every_c2", "iq1s_encode_kernel<0, 1, 0>", _IQ1),
+    "c2_fake": ("iq1s_fake_c2", "iq1s_payload_wide_kernel<0, 2, 0>", _IQ1),
+    "c5": ("iq2xs_candidates_c5", "iq2xs_wide_kernel<3, 0>", _IQ2),
+    "c5_iq1s": ("iq1s_candidates_c5_iq1s", "iq1s_encode_kernel<0, 3, 0>", _IQ1),
+    "c5_weight": ("iq2xs_candidates_c5_weight", "iq2xs_wide_kernel<3, 0>", _IQ2),
+    "c2_dequant": ("dequant_iq1s_c2", DEQUANT_KERNELS["iq1_s"], DEQUANT_SOURCES),
+    "c3_dequant": ("dequant_iq2xs_c3", DEQUANT_KERNELS["iq2_xs"], DEQUANT_SOURCES),
+}
+
+
+def profiled_kernel(config):
+    """(record name, kernel name, kernel sources) of the kernel a workload's
+    counters and traffic belong to."""
+    return PROFILED[config]
+
+
+def _pmc_csv(pmc_dir, config, what):
+    # pmc_<config>_<what>/ if present, else pmc_<what>/ (the c2 run)
+    for d in ("pmc_%s_%s" % (config, what), "pmc_%s" % what):
+        path = os.path.join(pmc_dir, d, "enc_counter_collection.csv")
+        if os.path.exists(path):
+            return path
+    raise SystemExit("no %s counter run under %s" % (what, pmc_dir))
+
+
+def record_traffic(config, pmc_dir):
+    """Turn the FETCH_SIZE / WRITE_SIZE counter runs of a workload's kernel and
+    of a plain 256 MiB copy into HBM bytes per launch, written to
+    profiles/traffic_<kernel>_<config>.json.
+
+    pmc_dir holds pmc_<config>_FETCH_SIZE/enc_counter_collection.csv and
+    pmc_<config>_WRITE_SIZE/... (or pmc_FETCH_SIZE/... for c2) and the copy runs
     pmc_copy_FETCH_SIZE/copy_counter_collection.csv, pmc_copy_WRITE_SIZE/...
     The copy reads and writes exactly 268435456 bytes; each counter is scaled by
     known bytes / (counted KiB * 1024) of that copy."""
-    kname = KERNEL_NAMES[fmt].split("<")[0]
+    name, kernel, sources = profiled_kernel(config)
+    kname = kernel.split("<")[0]
     known = 64 * 1024 * 1024 * 4
-    cfg = name.rsplit("_", 1)[-1]
-
-    def enc_csv(counter):
-        # pmc_<config>_<COUNTER>/ if present, else pmc_<COUNTER>/ (the c2 run)
-        for d in ("pmc_%s_%s" % (cfg, counter), "pmc_%s" % counter):
-            path = os.path.join(pmc_dir, d, "enc_counter_collection.csv")
-            if os.path.exists(path):
-                return path
-        raise SystemExit("no %s counter run under %s" % (counter, pmc_dir))
-
-    f_enc, nf = _counter_kib(enc_csv("FETCH_SIZE"), kname, "FETCH_SIZE")
-    w_enc, nw = _counter_kib(enc_csv("WRITE_SIZE"), kname, "WRITE_SIZE")
-    f_cp, _ = _counter_kib(os.path.join(pmc_dir, "pmc_copy_FETCH_SIZE", "copy_counter_collection.csv"),
-                           "copyBuffer", "FETCH_SIZE")
-    w_cp, _ = _counter_kib(os.path.join(pmc_dir, "pmc_copy_WRITE_SIZE", "copy_counter_collection.csv"),
-                           "copyBuffer", "WRITE_SIZE")
+    f_enc, nf = _counter_mean(_pmc_csv(pmc_dir, config, "FETCH_SIZE"), kname, "FETCH_SIZE")
+    w_enc, nw = _counter_mean(_pmc_csv(pmc_dir, config, "WRITE_SIZE"), kname, "WRITE_SIZE")
+    f_cp, _ = _counter_mean(os.path.join(pmc_dir, "pmc_copy_FETCH_SIZE", "copy_counter_collection.csv"),
+                            "copyBuffer", "FETCH_SIZE")
+    w_cp, _ = _counter_mean(os.path.join(pmc_dir, "pmc_copy_WRITE_SIZE", "copy_counter_collection.csv"),
+                            "copyBuffer", "WRITE_SIZE")
     ff, wf = known / (f_cp * 1024), known / (w_cp * 1024)
     rec = {
-        "kernel": KERNEL_NAMES[fmt],
-        "kernel_source_sha": source_sha(KERNEL_SOURCES[fmt]),
+        "kernel": kernel,
+        "kernel_source_sha": source_sha(sources),
         "fetch_kib_per_launch": f_enc, "fetch_dispatches": nf,
         "write_kib_per_launch": w_enc, "write_dispatches": nw,
         "copy_known_bytes": known, "copy_fetch_kib": f_cp, "copy_write_kib": w_cp,
@@ -152,37 +211,159 @@ def record_traffic(name, fmt, pmc_dir):
     print(json.dumps(rec))
 
 
-def traffic_for(name, sha):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on this kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+# The VALU / matrix-core counters of one rocprofv3 pass (8 SQ counters and one
+# GRBM counter at most per pass on this GPU).
+VALU_COUNTERS = ["SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU2", "SQ_INSTS_MFMA",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+N_XCD, N_SIMD = 8, 1024
+
+
+def record_counters(config, pmc_dir, units):
+    """Turn a VALU counter pass (pmc_<config>_valu/enc_counter_collection.csv)
+    into profiles/counters_<kernel>_<config>.json: the VALU issue-port busy
+    fraction (quad-cycles with at least one VALU issue per SIMD over the
+    kernel's quad-cycles; a dual issue puts two instructions in one), the
+    dual-issued share, the matrix-core busy fraction, and the VALU
+    lane-instructions per (group, entry)."""
+    name, kernel, sources = profiled_kernel(config)
+    kname = kernel.split("<")[0]
+    path = _pmc_csv(pmc_dir, config, "valu")
+    v = {c: _counter_mean(path, kname, c)[0] for c in VALU_COUNTERS}
+    cycles = v["GRBM_GUI_ACTIVE"] / N_XCD
+    issue_quads = (v["SQ_INSTS_VALU"] - v["SQ_ACTIVE_INST_VALU2"]) / N_SIMD
+    rec = {
+        "kernel": kernel,
+        "kernel_source_sha": source_sha(sources),
+        "counters_per_dispatch": v,
+        "kernel_cycles_per_xcd": cycles,
+        "valu_issue_busy": issue_quads / (cycles / 4.0),
+        "dual_issued_share": 2.0 * v["SQ_ACTIVE_INST_VALU2"] / v["SQ_INSTS_VALU"],
+        "mfma_busy": v["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cycles),
+        "valu_lane_instr_per_unit": (v["SQ_INSTS_VALU"] * 64 / units) if units else None,
+        "units_per_launch": units,
+    }
+    out = os.path.join(ROOT, "profiles", "counters_%s.json" % name)
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def _profile_record(kind, name, sha):
+    """A committed counter record (kind "traffic" or "counters"), if it was
+    taken on this kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s.json" % (kind, name))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_sha") != sha:
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
 
 
-def cpu_baseline(cfg, fmt, budget_s=15.0):
-    """The oracle on the first rows of the workload, on this host's cores."""
+def traffic_for(name, sha):
+    t = _profile_record("traffic", name, sha)
+    return None if t is None else t.get("hbm_bytes_per_launch")
+
+
+def counters_for(name, sha):
+    t = _profile_record("counters", name, sha)
+    if t is None:
+        return None
+    return {k: round(t[k], 4) if isinstance(t[k], float) else t[k]
+            for k in ("valu_issue_busy", "dual_issued_share", "mfma_busy",
+                      "valu_lane_instr_per_unit")}
+
+
+def host_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_usable": affinity}
+
+
+def cpu_baseline(cfg, fmt, full_budget_s=45.0, sample_s=20.0):
+    """The oracle on this host's cores: the whole workload when a short trial
+    predicts it finishes within full_budget_s, else its first rows, sized to
+    about sample_s."""
     import oracle
     w, grid, imp = cfg["w"], cfg["grid"], cfg["importance"]
     threads = oracle.num_threads()
-    rows = 2
-    while True:
-        sub = w[:1, :rows, :]
-        t0 = time.perf_counter()
-        oracle.encode(fmt, sub, grid, None if imp is None else imp[:1])
-        dt = time.perf_counter() - t0
-        if dt >= 0.6 * budget_s or rows >= w.shape[1]:
-            break
-        rows = min(w.shape[1], max(rows * 2, int(rows * budget_s / max(dt, 1e-3))))
-    nbytes = sub.size * 4
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d rows x %d cols of the workload (%d blocks), %.1f s"
-                      % (rows, w.shape[2], sub.size // 256, dt)}
+    B, R, C = w.shape
+    trial = min(R, 32)
+    t0 = time.perf_counter()
+    oracle.encode(fmt, w[:1, :trial], grid, None if imp is None else imp[:1])
+    rate = trial * C / max(time.perf_counter() - t0, 1e-6)          # values per second
+    if w.size / rate <= full_budget_s:
+        sub, ims, what = w, imp, "the whole workload"
+    else:
+        rows = max(1, min(R, int(sample_s * rate / C)))
+        sub, ims = w[:1, :rows], None if imp is None else imp[:1]
+        what = "the first %d rows x %d cols of the workload" % (rows, C)
+    t0 = time.perf_counter()
+    oracle.encode(fmt, sub, grid, ims)
+    dt = time.perf_counter() - t0
+    rec = {"value": sub.size * 4 / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": "%s (%d blocks), %.1f s" % (what, sub.size // 256, dt)}
+    rec.update(host_info())
+    return rec
+
+
+def search_flops_per_row(G, C, sweeps):
+    """Algorithmic fp32 flops of the choice search of one row of one 256-column
+    block: r = H e, step 2's e^T H_gg e for every candidate, and per sweep and
+    group the rest r_g - H_gg e_cur, one dot product per candidate and the
+    update r += H[:, g] (e_new - e_cur)."""
+    L = 256 // G
+    step2 = G * C * (2 * L * L + 2 * L)
+    sweep = G * (2 * L * L + C * 2 * L + 2 * 256 * L)
+    return 2 * 256 * 256 + step2 + sweeps * sweep
+
+
+def encode_roofline(fmt, weighted, units, kernel_ms, alg_bytes, config):
+    """The roofline record of an encode-type kernel: `units` (group, grid
+    entry) pairs per launch, `alg_bytes` algorithmic HBM bytes per launch."""
+    name, kernel, sources = profiled_kernel(config)
+    sha = source_sha(sources)
+    t = kernel_ms * 1e-3
+    con = CONTRACTION_FLOPS[(fmt, weighted)] * units
+    ele = ELEMENTWISE_FLOPS[(fmt, weighted)] * units
+    bound = {"fp32_vector_ms": round(ele / (PEAK_FP32_VECTOR_TFLOPS * 1e12) * 1e3, 5),
+             "bf16_mfma_ms": round(con / (PEAK_BF16_MFMA_TFLOPS * 1e12) * 1e3, 5),
+             "hbm_ms": round(alg_bytes / (PEAK_HBM_GBPS * 1e9) * 1e3, 5)}
+    achieved = ele / t / 1e12
+    return {
+        "bound": "alu",
+        "achieved": round(achieved, 3),
+        "peak": PEAK_FP32_VECTOR_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4),
+        "traffic": traffic_for(name, sha),
+        "kernel": kernel,
+        "kernel_ms": round(kernel_ms, 5),
+        "work": ("elementwise fp32 flops of the search (16 choice keys + shift terms): %d per "
+                 "(group, grid entry) x %d pairs" % (ELEMENTWISE_FLOPS[(fmt, weighted)], units)),
+        "mfma": {"achieved": round(con / t / 1e12, 3), "peak": PEAK_BF16_MFMA_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(con / t / 1e12 / PEAK_BF16_MFMA_TFLOPS, 4),
+                 "work": "contraction flops (weighted dot products): %d per pair"
+                         % CONTRACTION_FLOPS[(fmt, weighted)]},
+        "bound_ms": bound,
+        "frac_of_bound": round(max(bound.values()) / kernel_ms, 4),
+        "algorithmic_flops_per_launch": con + ele,
+        "algorithmic_bytes_per_launch": alg_bytes,
+        "counters": counters_for(name, sha),
+    }
 
 
 def main():
@@ -197,14 +378,24 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB device copy (for counter calibration) and exit")
     ap.add_argument("--record-traffic", metavar="PMC_DIR",
-                    help="convert rocprofv3 counter CSVs under PMC_DIR into "
-                         "profiles/traffic_<kernel>_<config>.json and exit (no GPU needed)")
+                    help="convert the FETCH_SIZE / WRITE_SIZE counter CSVs of --config under "
+                         "PMC_DIR into profiles/traffic_<kernel>_<config>.json and exit "
+                         "(no GPU needed)")
+    ap.add_argument("--record-counters", metavar="PMC_DIR",
+                    help="convert the VALU counter CSV of --config under PMC_DIR into "
+                         "profiles/counters_<kernel>_<config>.json and exit (no GPU needed)")
     args = ap.parse_args()
 
     if args.record_traffic:
-        fmt = "iq2_xs" if args.config == "c3" else "iq1_s"
-        record_traffic("%s_encode_%s" % (fmt.replace("_", ""), args.config), fmt,
-                       args.record_traffic)
+        record_traffic(args.config, args.record_traffic)
+        return
+    if args.record_counters:
+        import workloads
+        cfg = getattr(workloads, WORKLOADS[args.config][0])()
+        units = None
+        if not args.config.endswith("_dequant"):
+            units = cfg["w"].size // 8 * cfg["grid"].shape[0]
+        record_counters(args.config, args.record_counters, units)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -241,6 +432,7 @@ def main():
     imp = None if cfg["importance"] is None else torch.from_numpy(cfg["importance"]).to(dev)
     stream = torch.cuda.current_stream()
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    dequant = args.config.endswith("_dequant")
 
     if args.config.startswith("c5"):
         H = torch.from_numpy(cfg["H"]).to(dev)
@@ -260,6 +452,14 @@ def main():
             iq.choice_search(H, err.view(shape), sweeps=2)
             if ev:
                 ev[2].record(stream)
+    elif dequant:
+        B, R, C = w.shape
+        # the payload of the workload's encode, decoded once per step
+        packed = iq.encode(w, grid, imp, fmt=fmt)
+        xhat = torch.empty_like(w)
+
+        def step():
+            iq.dequant(packed, grid, fmt=fmt, out=xhat, status=status, check=False)
     elif args.config.endswith("_every"):
         B, R, C = w.shape
         out = torch.empty((16, B, R, C // 256, iq.BLOCK_BYTES[fmt]), dtype=torch.uint8, device=dev)
@@ -298,7 +498,7 @@ def main():
             step()
     torch.cuda.synchronize()
     if int(status.item()) != 0:
-        raise SystemExit("encode reported status %d" % int(status.item()))
+        raise SystemExit("the library reported status %d" % int(status.item()))
 
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -311,12 +511,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # Whole-step time from the host clock between the two synchronizations; the
-    # encode kernel's per-launch time from HIP events on its launch stream (one
-    # launch per step).
+    # kernel's per-launch time from HIP events on its launch stream (one launch
+    # per step outside the c5 workloads).
     ms_per_step = 1e3 * wall / args.steps
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
 
     nweights = w_np.size
+    nblk = nweights // 256
     value = nweights * 4 / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": "weights encoded/sec (GB/s fp32 in) + % FP32/MFMA roofline, IQ1_S 4096x4096",
@@ -335,49 +536,57 @@ def main():
                    "cols": int(w_np.shape[-1]), "batch": int(w_np.shape[0]),
                    "weights_per_sec": round(nweights / (ms_per_step * 1e-3), 1)},
     }
-    if args.config.startswith("c5"):
+    if dequant:
+        name, kernel, sources = profiled_kernel(args.config)
+        alg = nblk * (iq.BLOCK_BYTES[fmt] + 256 * 4)
+        achieved = alg / (kernel_ms * 1e-3) / 1e9
+        result["metric"] = "weights decoded/sec (GB/s fp32 out), %s 4096x4096" % fmt.upper()
+        result["value"] = round(nweights * 4 / (ms_per_step * 1e-3) / 1e9, 4)
+        result["roofline"] = {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic_for(name, source_sha(sources)),
+            "kernel": kernel, "kernel_ms": round(kernel_ms, 5),
+            "work": "payload read + fp32 values written: %d bytes per 256-value block x %d blocks"
+                    % (iq.BLOCK_BYTES[fmt] + 1024, nblk),
+            "algorithmic_bytes_per_launch": alg,
+        }
+    elif args.config.startswith("c5"):
         # Per-kernel times from HIP events around each launch of a second run
         # of the same steps (after the timed region, so that it is not
         # perturbed): the candidate encode, the dominant kernel, carries the
         # roofline (the same sweep as the encode, so the same algorithmic
-        # flops per group and entry); the choice search is reported beside it.
+        # flops per group and entry); the choice search is reported beside it
+        # against its own bounds.
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         for e in evs:
             step(e)
         torch.cuda.synchronize()
         cand_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
         search_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-        groups = w2.numel() // 8
-        flops = groups * cfg["grid"].shape[0] * FLOPS_PER_GROUP_ENTRY[(fmt, True)]
-        achieved = flops / (cand_ms * 1e-3) / 1e12
-        result["roofline"] = {
-            "bound": "alu",
-            "achieved": round(achieved, 3),
-            "peak": PEAK_FP32_VECTOR_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4),
-            "traffic": None,
-            "kernel": "candidate encode",
-            "kernel_ms": round(cand_ms, 5),
-            "algorithmic_flops_per_launch": flops,
-            "search_ms": round(search_ms, 5),
-        }
+        units = w2.numel() // 8 * cfg["grid"].shape[0]
+        # candidates written: [rows][blocks][G][8][256/G] fp32 + choices int32
+        cand_bytes = R * (C // 256) * (G * 8 * (256 // G) * 4 + G * 8 * 4)
+        roof = encode_roofline(fmt, True, units, cand_ms, w2.numel() * 4 + cand_bytes,
+                               args.config)
+        nsearch = R * (C // 256)
+        sflops = nsearch * search_flops_per_row(G, 8, 2)
+        sbytes = cand_bytes + H.numel() * 4 + nsearch * G * 4
+        sb = {"fp32_ms": round(sflops / (PEAK_FP32_VECTOR_TFLOPS * 1e12) * 1e3, 5),
+              "hbm_ms": round(sbytes / (PEAK_HBM_GBPS * 1e9) * 1e3, 5)}
+        roof["search"] = {"kernel_ms": round(search_ms, 5), "algorithmic_flops": sflops,
+                          "algorithmic_bytes": sbytes, "bound_ms": sb,
+                          "frac_of_bound": round(max(sb.values()) / search_ms, 4)}
+        result["roofline"] = roof
     else:
-        groups = nweights // 8
         weighted = imp is not None
-        flops = groups * cfg["grid"].shape[0] * FLOPS_PER_GROUP_ENTRY[(fmt, weighted)]
-        achieved = flops / (kernel_ms * 1e-3) / 1e12
-        name = "%s_encode_%s" % (fmt.replace("_", ""), args.config)
-        result["roofline"] = {
-            "bound": "alu",
-            "achieved": round(achieved, 3),
-            "peak": PEAK_FP32_VECTOR_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4),
-            "traffic": traffic_for(name, source_sha(KERNEL_SOURCES[fmt])),
-            "kernel_ms": round(kernel_ms, 5),
-            "algorithmic_flops_per_launch": flops,
-        }
+        units = nweights // 8 * cfg["grid"].shape[0]
+        mult = 16 if args.config.endswith("_every") else 1
+        out_bytes = nblk * (256 * 4 if args.config.endswith("_fake")
+                            else mult * iq.BLOCK_BYTES[fmt])
+        alg_bytes = nweights * 4 + out_bytes + (0 if imp is None else imp.numel() * 4)
+        result["roofline"] = encode_roofline(fmt, weighted, units, kernel_ms, alg_bytes,
+                                             args.config)
     if not args.no_cpu_baseline and args.config in ("c1", "c2", "c3", "c4"):
         result["cpu_baseline"] = cpu_baseline(cfg, fmt)
     print(json.dumps(result), flush=True)

@@ -129,14 +129,22 @@ def format_info(fmt: str) -> dict:
     return {n: getattr(info, n) for n, _ in _FormatInfo._fields_}
 
 
-def _status_tensor(status, device):
+def _status_arg(status, check, device):
+    """The status word to pass.  None with ``check``: NULL, so that the library
+    synchronizes the stream and returns the first data error as the call's
+    code.  None without ``check``: a fresh zeroed word nobody reads (the call
+    stays asynchronous).  Otherwise the caller's int32 tensor."""
     if status is None:
-        return torch.zeros(1, dtype=torch.int32, device=device), True
+        return None if check else torch.zeros(1, dtype=torch.int32, device=device)
     _dev_tensor(status, torch.int32, "status")
-    return status, False
+    return status
 
 
-def _raise_on_status(status, where):
+def _raise_on_status(status, check, where):
+    """With ``check`` and a caller's status word: synchronize and raise on a
+    data error (with a NULL word the call's own code has been checked)."""
+    if not check or status is None:
+        return
     code = int(status.item())
     if code:
         raise IQError(code, where)
@@ -212,12 +220,11 @@ def encode(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=None, 
     """
     f, dt, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, choices)
     out = _out_tensor(out, (B, R, C // 256, BLOCK_BYTES[fmt]), torch.uint8, w.device, "out")
-    status, own = _status_tensor(status, w.device)
+    status = _status_arg(status, check, w.device)
     code = load().iq_encode(f, dt, _ptr(w), B, R, C, _ptr(importance), _ptr(grid), grid.shape[0],
                             _ptr(scales), _ptr(choices), _ptr(out), _ptr(status), _stream())
     _check(code, "iq_encode")
-    if check:
-        _raise_on_status(status, "iq_encode")
+    _raise_on_status(status, check, "iq_encode")
     return out[0] if squeeze else out
 
 
@@ -231,13 +238,12 @@ def encode_every_choice(w, grid, importance=None, *, fmt="iq1_s", scales=None, o
     f, dt, B, R, C, squeeze, scales = _encode_args(w, grid, importance, fmt, scales, None)
     out = _out_tensor(out, (NUM_CHOICES[fmt], B, R, C // 256, BLOCK_BYTES[fmt]), torch.uint8,
                       w.device, "out")
-    status, own = _status_tensor(status, w.device)
+    status = _status_arg(status, check, w.device)
     code = load().iq_encode_every_choice(f, dt, _ptr(w), B, R, C, _ptr(importance), _ptr(grid),
                                          grid.shape[0], _ptr(scales), _ptr(out), _ptr(status),
                                          _stream())
     _check(code, "iq_encode_every_choice")
-    if check:
-        _raise_on_status(status, "iq_encode_every_choice")
+    _raise_on_status(status, check, "iq_encode_every_choice")
     return out[:, 0] if squeeze else out
 
 
@@ -253,13 +259,12 @@ def fake_quant(w, grid, importance=None, *, fmt="iq1_s", scales=None, choices=No
     xhat = _out_tensor(out, (B, R, C), torch.float32, w.device, "out")
     pk = (torch.empty((B, R, C // 256, BLOCK_BYTES[fmt]), dtype=torch.uint8, device=w.device)
           if packed else None)
-    status, own = _status_tensor(status, w.device)
+    status = _status_arg(status, check, w.device)
     code = load().iq_fake_quant(f, dt, _ptr(w), B, R, C, _ptr(importance), _ptr(grid),
                                 grid.shape[0], _ptr(scales), _ptr(choices), _ptr(xhat), _ptr(pk),
                                 _ptr(status), _stream())
     _check(code, "iq_fake_quant")
-    if check:
-        _raise_on_status(status, "iq_fake_quant")
+    _raise_on_status(status, check, "iq_fake_quant")
     if squeeze:
         xhat = xhat[0]
         pk = None if pk is None else pk[0]
@@ -282,12 +287,11 @@ def dequant(packed, grid, *, fmt="iq1_s", out=None, status=None, check=True):
         _dev_tensor(out, torch.float32, "out")
         if out.numel() != B * R * C:
             raise ValueError("out has the wrong size")
-    status, own = _status_tensor(status, packed.device)
+    status = _status_arg(status, check, packed.device)
     code = load().iq_dequant(f, _ptr(packed), B, R, C, _ptr(grid), grid.shape[0], _ptr(out),
                              _ptr(status), _stream())
     _check(code, "iq_dequant")
-    if check:
-        _raise_on_status(status, "iq_dequant")
+    _raise_on_status(status, check, "iq_dequant")
     return out[0] if squeeze else out
 
 
@@ -318,13 +322,12 @@ def encode_candidates(w, grid, importance=None, *, fmt="iq2_xs", top_c=8, codes=
     ncode = 4 if fmt == "iq1_s" else 2
     cc = (torch.empty((R, NB, G, tc, ncode), dtype=torch.int16, device=w.device)
           if codes else None)
-    status, own = _status_tensor(status, w.device)
+    status = _status_arg(status, check, w.device)
     code = load().iq_encode_candidates(f, dt, _ptr(w), R, C, _ptr(importance), _ptr(grid),
                                        grid.shape[0], int(top_c), _ptr(err), _ptr(ch), _ptr(cc),
                                        _ptr(status), _stream())
     _check(code, "iq_encode_candidates")
-    if check:
-        _raise_on_status(status, "iq_encode_candidates")
+    _raise_on_status(status, check, "iq_encode_candidates")
     return err, ch, cc
 
 

@@ -1,6 +1,8 @@
 // api.hip -- the extern "C" entry points of libiqcodec.so declared in
 // include/iq_codec.h: argument validation, the gfx950 device check, and the
-// stream-ordered launches.  No device memory is allocated here.
+// stream-ordered launches.  No device memory is allocated here: the one word
+// the library owns on a device (the status of calls made with status = NULL)
+// is a file-scope device variable.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -58,6 +60,52 @@ iq_status_t geometry(int64_t batch, int64_t rows, int64_t cols, iqk::BlockGeom* 
 }
 
 iq_status_t from_hip(hipError_t e) { return e == hipSuccess ? IQ_OK : IQ_ERR_HIP; }
+
+// ---------------------------------------------------------------------------
+// Calls made with status = NULL synchronize their stream and return the first
+// data error.  The kernels still need a device word to report into: each GPU
+// holds one in this file-scope variable (the library allocates nothing).  In
+// host code its name only stands in for the symbol; the device address is
+// taken once per device with hipGetSymbolAddress, with that device current,
+// and kept in g_sync_word.  A per-device lock, held from clearing the word to
+// reading it back after the stream has drained, serializes such calls, so two
+// host threads never share the word at once.
+// ---------------------------------------------------------------------------
+
+__device__ __align__(256) int32_t sync_status_word[1];
+
+__global__ void clear_sync_word_kernel(int32_t* word) { word[0] = 0; }
+
+std::mutex g_sync_mutex[kMaxDevices];
+int32_t* g_sync_word[kMaxDevices];    // guarded by g_sync_mutex[dev]
+
+// Runs launch(status) when the caller gave a status word.  Otherwise clears
+// the device's own word, runs launch(word), waits for the stream and returns
+// the word: IQ_OK, or the first data error code the kernels reported.
+template <class Launch>
+iq_status_t run_with_status(int32_t* status, hipStream_t stream, Launch&& launch)
+{
+    if (status) return from_hip(launch(status));
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return IQ_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return IQ_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_sync_mutex[dev]);
+    if (!g_sync_word[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(sync_status_word)) != hipSuccess || !p)
+            return IQ_ERR_HIP;
+        g_sync_word[dev] = static_cast<int32_t*>(p);
+    }
+    int32_t* word = g_sync_word[dev];
+    hipLaunchKernelGGL(clear_sync_word_kernel, dim3(1), dim3(1), 0, stream, word);
+    if (hipGetLastError() != hipSuccess) return IQ_ERR_HIP;
+    if (launch(word) != hipSuccess) return IQ_ERR_HIP;
+    int32_t host = 0;
+    if (hipMemcpyAsync(&host, word, sizeof(host), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return IQ_ERR_HIP;
+    return static_cast<iq_status_t>(host);
+}
 
 bool known_format(iq_format_t fmt)
 {
@@ -140,17 +188,19 @@ iq_status_t iq_encode(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
-    if (!w || !grid || !out || !status) return IQ_ERR_NULL;
+    if (!w || !grid || !out) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (dtype_bytes(wdtype) == 0) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(out, 2) || (scales && !aligned(scales, 2)) || (choices && !aligned(choices, 4)) ||
-        !aligned(status, 4))
+        (status && !aligned(status, 4)))
         return IQ_ERR_ARG;
     st = check_device(&g);
     if (st) return st;
-    return from_hip(launch_encode(fmt, wdtype, w, importance, grid, grid_size, scales, choices,
-                                  out, nullptr, iqk::kModePayload, status, g, stream));
+    return run_with_status(status, stream, [&](int32_t* s) {
+        return launch_encode(fmt, wdtype, w, importance, grid, grid_size, scales, choices, out,
+                             nullptr, iqk::kModePayload, s, g, stream);
+    });
 }
 
 iq_status_t iq_encode_every_choice(iq_format_t fmt, iq_dtype_t wdtype, const void* w,
@@ -163,16 +213,18 @@ iq_status_t iq_encode_every_choice(iq_format_t fmt, iq_dtype_t wdtype, const voi
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
-    if (!w || !grid || !out || !status) return IQ_ERR_NULL;
+    if (!w || !grid || !out) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (dtype_bytes(wdtype) == 0) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
-        !aligned(out, 2) || (scales && !aligned(scales, 2)) || !aligned(status, 4))
+        !aligned(out, 2) || (scales && !aligned(scales, 2)) || (status && !aligned(status, 4)))
         return IQ_ERR_ARG;
     st = check_device(&g);
     if (st) return st;
-    return from_hip(launch_encode(fmt, wdtype, w, importance, grid, grid_size, scales, nullptr,
-                                  out, nullptr, iqk::kModeEvery, status, g, stream));
+    return run_with_status(status, stream, [&](int32_t* s) {
+        return launch_encode(fmt, wdtype, w, importance, grid, grid_size, scales, nullptr, out,
+                             nullptr, iqk::kModeEvery, s, g, stream);
+    });
 }
 
 iq_status_t iq_fake_quant(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t batch,
@@ -184,12 +236,12 @@ iq_status_t iq_fake_quant(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
-    if (!w || !grid || !xhat || !status) return IQ_ERR_NULL;
+    if (!w || !grid || !xhat) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (dtype_bytes(wdtype) == 0) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(xhat, 16) || (out && !aligned(out, 2)) || (scales && !aligned(scales, 2)) ||
-        (choices && !aligned(choices, 4)) || !aligned(status, 4))
+        (choices && !aligned(choices, 4)) || (status && !aligned(status, 4)))
         return IQ_ERR_ARG;
     // The decoded values may not overlap the weights: a block's values are
     // written while the other half of the block may still be reading them.
@@ -199,8 +251,10 @@ iq_status_t iq_fake_quant(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int
     if (x0 < w0 + wbytes && w0 < x0 + xbytes) return IQ_ERR_ARG;
     st = check_device(&g);
     if (st) return st;
-    return from_hip(launch_encode(fmt, wdtype, w, importance, grid, grid_size, scales, choices,
-                                  out, xhat, iqk::kModeFake, status, g, stream));
+    return run_with_status(status, stream, [&](int32_t* s) {
+        return launch_encode(fmt, wdtype, w, importance, grid, grid_size, scales, choices, out,
+                             xhat, iqk::kModeFake, s, g, stream);
+    });
 }
 
 iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, int64_t rows,
@@ -211,12 +265,15 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
     iqk::BlockGeom g;
     iq_status_t st = geometry(batch, rows, cols, &g);
     if (st) return st;
-    if (!packed || !grid || !out || !status) return IQ_ERR_NULL;
+    if (!packed || !grid || !out) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
-    if (!aligned(grid, 16) || !aligned(out, 16) || !aligned(status, 4)) return IQ_ERR_ARG;
+    if (!aligned(grid, 16) || !aligned(out, 16) || (status && !aligned(status, 4)))
+        return IQ_ERR_ARG;
     st = check_device(&g);
     if (st) return st;
-    return from_hip(iqk::launch_dequant((int)fmt, packed, grid, grid_size, out, status, g, stream));
+    return run_with_status(status, stream, [&](int32_t* s) {
+        return iqk::launch_dequant((int)fmt, packed, grid, grid_size, out, s, g, stream);
+    });
 }
 
 iq_status_t iq_encode_candidates(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t rows,
@@ -229,23 +286,24 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, iq_dtype_t wdtype, const void*
     iqk::BlockGeom g;
     iq_status_t st = geometry(1, rows, cols, &g);
     if (st) return st;
-    if (!w || !grid || !cand_err || !cand_choice || !status) return IQ_ERR_NULL;
+    if (!w || !grid || !cand_err || !cand_choice) return IQ_ERR_NULL;
     if (grid_size < 1 || grid_size > grid_max(fmt)) return IQ_ERR_GRID;
     if (top_c < 1 || top_c > num_choices(fmt)) return IQ_ERR_ARG;
     if (dtype_bytes(wdtype) == 0) return IQ_ERR_ARG;
     if (!aligned(w, 16) || !aligned(grid, 16) || (importance && !aligned(importance, 16)) ||
         !aligned(cand_err, 16) || !aligned(cand_choice, 4) ||
-        (cand_codes && !aligned(cand_codes, 2)) || !aligned(status, 4))
+        (cand_codes && !aligned(cand_codes, 2)) || (status && !aligned(status, 4)))
         return IQ_ERR_ARG;
     st = check_device(&g);
     if (st) return st;
-    if (fmt != IQ_FMT_IQ2_XS)
-        return from_hip(iqk::launch_iq1_candidates((int)fmt, (int)wdtype, w, importance, grid,
-                                                   grid_size, top_c, cand_err, cand_choice,
-                                                   cand_codes, status, g, stream));
-    return from_hip(iqk::launch_iq2xs_candidates((int)wdtype, w, importance, grid, grid_size, top_c,
-                                                 cand_err, cand_choice, cand_codes, status, g,
-                                                 stream));
+    return run_with_status(status, stream, [&](int32_t* s) {
+        if (fmt != IQ_FMT_IQ2_XS)
+            return iqk::launch_iq1_candidates((int)fmt, (int)wdtype, w, importance, grid, grid_size,
+                                              top_c, cand_err, cand_choice, cand_codes, s, g,
+                                              stream);
+        return iqk::launch_iq2xs_candidates((int)wdtype, w, importance, grid, grid_size, top_c,
+                                            cand_err, cand_choice, cand_codes, s, g, stream);
+    });
 }
 
 iq_status_t iq_choice_search(const float* H, const float* cand_err, int64_t rows, int32_t G,

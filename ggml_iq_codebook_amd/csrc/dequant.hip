@@ -108,8 +108,10 @@ __global__ __launch_bounds__(kThreads) void dequant_iq1m_kernel(const uint8_t* _
     uint32_t sc[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) sc[w] = (uint32_t)b[48 + 2 * w] | ((uint32_t)b[49 + 2 * w] << 8);
-    const uint32_t dh = (sc[0] >> 12) | ((sc[1] >> 8) & 0x00f0u) | ((sc[2] >> 4) & 0x0f00u) |
-                        (sc[3] & 0xf000u);
+    // d's fp16 bits, nibble w (bits 4w..4w+3) in the top 4 bits of word w
+    uint32_t dh = 0u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dh |= (sc[w] >> 12) << (4 * w);
     const int k = (int)((sc[m >> 2] >> (3 * (m & 3))) & 7u);
     const uint32_t nib = ((uint32_t)b[32 + (g >> 1)] >> (4 * (g & 1))) & 0xfu;
     const int e = (int)b[g] | (int)((nib & 7u) << 8);

@@ -559,6 +559,62 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         const bool zero_scale = !rejected && dh == 0u;
         int used = 0;
 
+        // The entry of this group under its (k, shift) choice cs: the lane
+        // rescans its entries of the chunk that holds its minimum of cs, then
+        // the lane of the column whose matrix-core minimum is least is kept.
+        auto pick_entry = [&](int cs) -> int {
+            float lane_min = best[0];
+#pragma unroll
+            for (int c = 1; c < 16; ++c)
+                if (cs == c) lane_min = best[c];
+            const int tchunk = (int)((chunk_of[cs >> 3] >> (4 * (cs & 7))) & 0xfu);
+            // The lane of the column whose matrix-core minimum is least holds
+            // the entry.  Unless two lanes of some column hold equal minima,
+            // the four lanes split that lane's entries of its chunk between
+            // them (kChunkTiles/4 tiles each) and keep the least key, lowest
+            // entry on equal keys; with equal minima every lane rescans its own
+            // entries and the lane of least minimum, then lowest entry, wins.
+            float cm = fminf(lane_min, __shfl_xor(lane_min, 16));
+            cm = fminf(cm, __shfl_xor(cm, 32));
+            const uint64_t holders = (__ballot(lane_min == cm) >> col) & 0x0001000100010001ull;
+            const bool tie = __ballot(__popcll(holders) > 1) != 0;      // wave-uniform
+            int idx;
+            float key;
+            if (!tie) {
+                const int kbs = __builtin_ctzll(holders) >> 4;
+                const int tch = __shfl(tchunk, col + 16 * kbs);
+                idx = rescan<kChunkTiles>(sq, tch, kbs, kb * (kChunkTiles / 4), kChunkTiles / 4, cs,
+                                          src, zero_block, w64, b4, inv_d, &key);
+#pragma unroll
+                for (int o = 16; o <= 32; o <<= 1) {
+                    const float ok = __shfl_xor(key, o);
+                    const int oi = __shfl_xor(idx, o);
+                    if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
+                }
+            } else {
+                idx = rescan<kChunkTiles>(sq, tchunk, kb, 0, kChunkTiles, cs, src, zero_block, w64,
+                                          b4, inv_d, &key);
+#pragma unroll
+                for (int o = 16; o <= 32; o <<= 1) {
+                    const float om = __shfl_xor(lane_min, o);
+                    const int oi = __shfl_xor(idx, o);
+                    if (om < lane_min || (om == lane_min && oi < idx)) { lane_min = om; idx = oi; }
+                }
+            }
+            return idx < n ? idx : n - 1;
+        };
+        // The choice unit's fp64 error under cs with this lane's entry: its
+        // four groups (IQ1_S sub-block) or two (IQ1_M scale group), adjacent
+        // columns.
+        auto unit_err64 = [&](int cs, int idx) -> double {
+            double e = group_error64<kChunk>(src, zero_block, sq, idx, cs, d);
+            e += __shfl_xor(e, 1);
+            if (!kM) e += __shfl_xor(e, 2);
+            return e;
+        };
+        // Choice c as (k, shift): IQ1_M takes the group's own shift under k.
+        auto full = [&](int c) { return kM ? c + 8 * (int)((shbits >> c) & 1u) : c; };
+
         // For each choice to emit: this group's (k, shift) choice cs, its
         // entry (the lane rescans its entries of the chunk that holds its
         // minimum of cs, then the lane of the column whose matrix-core minimum
@@ -575,6 +631,28 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                 for (int c = 0; c < kChoices; ++c) {
                     const bool better = zero_scale ? (cr < 0) : (cr < 0 || cost[c] < vr);
                     if (!((used >> c) & 1) && better) { cr = c; vr = cost[c]; }
+                }
+                // Unused choices whose fp32 cost is within 2^-18 of the
+                // least's magnitude are ranked again by their fp64 errors
+                // (with their own entries), the lower choice on equal errors,
+                // as the payload's runner-up is.
+                uint32_t nearm = 0u;
+                if (!zero_block) {
+#pragma unroll
+                    for (int c = 0; c < kChoices; ++c)
+                        if (!((used >> c) & 1) && c != cr && cost[c] - vr <= 0x1p-18f * fabsf(vr))
+                            nearm |= 1u << c;
+                }
+                if (__ballot(nearm != 0u) != 0) {               // wave-uniform
+                    double b64 = unit_err64(full(cr), pick_entry(full(cr)));
+                    for (int c = 0; c < kChoices; ++c) {
+                        if (__ballot((nearm >> c) & 1u) == 0) continue;   // wave-uniform
+                        const double e = unit_err64(full(c), pick_entry(full(c)));
+                        if (((nearm >> c) & 1u) && (e < b64 || (e == b64 && c < cr))) {
+                            b64 = e;
+                            cr = c;
+                        }
+                    }
                 }
                 used |= 1 << cr;
                 ch = cr;
@@ -912,8 +990,6 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         __asm__ volatile("" : "+v"(ln));
         const int g = ln & 31;                  // group = matrix column
         const int hl = ln >> 5;                 // K half / row half
-        const int sub = g >> 2;
-        const int lq = g & 3;
         const int64_t bt = blk / a.g.blocks_per_batch;
         const int64_t cb = blk % a.g.blocks_per_row;
         const WeightBlock<kDT> xb(a.w, blk);

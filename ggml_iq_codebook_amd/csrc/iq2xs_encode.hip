@@ -219,18 +219,16 @@ __device__ __forceinline__ int rescan(const float* __restrict__ sg, int chunk, i
     return idx;
 }
 
-// kMode: EncodeMode; kDT: the weight's iq_dtype_t.
-template <int kMode, int kDT>
-__global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
+// The every-choice output (16 payloads per block); kDT: the weight's
+// iq_dtype_t.
+template <int kDT>
+__global__ __launch_bounds__(kThreads) void iq2xs_every_kernel(Iq2xsArgs a)
 {
-    constexpr bool kCandidates = kMode == kModeCandidates;
-    constexpr int kPayloads = kMode == kModeEvery ? 16 : 1;
+    constexpr int kPayloads = 16;
     // Tiles per tracking chunk.  Recording chunks costs the sweep about 4
-    // instructions per choice and chunk; each pick rescans one lane's
-    // entries of a chunk, 4 per tile.  One pick per group (payload, fake
-    // quant): 8 tiles (128 entries); top_c picks (candidates): 4; 16 picks
-    // (every choice): 2.
-    constexpr int kChunkTiles = kCandidates ? 4 : (kMode == kModeEvery ? 2 : 8);
+    // instructions per choice and chunk; each of the 16 picks rescans one
+    // lane's entries of a chunk, 4 per tile: 2 tiles (32 entries).
+    constexpr int kChunkTiles = 2;
     constexpr int kChunk = kTile * kChunkTiles;
 
     __shared__ float sgrid[kMaxGrid * kEntryStride + 2 * (kMaxGrid / 32)];  // q[0..7], q^2[0..7]
@@ -251,8 +249,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
     const int npad = nchunks * kChunk;
 
     if (tid == 0) { sgrid_bad = 0; sgrid_inexact = 0; }
-    if (!kCandidates)
-        for (int i = tid; i < kPayloads * kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
+    for (int i = tid; i < kPayloads * kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     {
         int bad = 0, inexact = 0;
@@ -327,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
 
         uint32_t dh;
-        if (!kCandidates && a.scales) {
+        if (a.scales) {
             dh = (uint32_t)a.scales[blk];
         } else {
             const float t = amax / 155.0f;
@@ -339,18 +336,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
         if (scale_bad && !block_bad && half == 0 && lane == 0) report(a.status, IQ_ERR_SCALE_RANGE);
         const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
 
-        int forced = -1;
-        bool choice_bad = false;
-        if ((kMode == kModePayload || kMode == kModeFake) && a.choices) {
-            int ln = lane;                  // opaque: the address is formed here, not hoisted
-            __asm__ volatile("" : "+v"(ln));
-            const int cv = ln < 16 ? a.choices[blk * 16 + ln] : 0;
-            const bool bad = cv < 0 || cv > 15;
-            if (bad && half == 0) report(a.status, IQ_ERR_ARG);
-            choice_bad = __ballot(bad) != 0;
-            forced = choice_bad ? -1 : a.choices[blk * 16 + m];
-        }
-        const bool bad_block = grid_bad || block_bad || scale_bad || choice_bad;
+        const bool bad_block = grid_bad || block_bad || scale_bad;
         const bool zero_scale = dh == 0u;
         const bool skip = bad_block || zero_scale;
 
@@ -432,17 +418,6 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             wxs[j] = ((neg >> j) & 1) ? -wx : wx;
         }
 
-        // Scale-group cost of every local scale: the least minimum of each
-        // group's four lanes, summed over the two groups, times 2k+1.
-        float cost[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            float v = best[k];
-            v = fminf(v, __shfl_xor(v, 16));
-            v = fminf(v, __shfl_xor(v, 32));
-            cost[k] = (float)(2 * k + 1) * (v + __shfl_xor(v, 1));
-        }
-
         // Entry of local scale k for this lane's group: rescan the lane's part
         // of its winning chunk, then keep the lane of least matrix-core minimum.
         auto pick = [&](int k) -> int {
@@ -487,155 +462,23 @@ __global__ __launch_bounds__(kThreads) void iq2xs_kernel(Iq2xsArgs a)
             return idx < n ? idx : n - 1;
         };
 
-        if (kMode == kModeEvery) {
-            // Every local scale k for every scale group: the payload forced to k.
-            for (int k = 0; k < 16; ++k) {
-                const int idx = pick(k);
-                if (!skip && kb == 0) {
-                    uint8_t* ob = sout + (k * kBlocksPerWG + slot) * kBlockBytes;
-                    const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
-                    ob[2 + 2 * g] = (uint8_t)(code & 0xff);
-                    ob[3 + 2 * g] = (uint8_t)(code >> 8);
-                    if ((g & 3) == 0) ob[66 + (m >> 1)] = (uint8_t)(k | (k << 4));
-                    if (g == 0) {
-                        ob[0] = (uint8_t)(dh & 0xff);
-                        ob[1] = (uint8_t)(dh >> 8);
-                    }
-                }
-            }
-        } else if (!kCandidates) {
-            int kstar = 0;
-            float cbv = cost[0];
-#pragma unroll
-            for (int k = 1; k < 16; ++k)
-                if (cost[k] < cbv) { cbv = cost[k]; kstar = k; }
-            int idx;
-            if (forced >= 0) {                      // wave-uniform
-                kstar = forced;
-                idx = pick(kstar);
-            } else {
-                // The runner-up local scale.  The fp32 costs carry rounding
-                // of the size of the sums they cancel, so when the runner-up
-                // is within 2^-18 of the best's magnitude (32 to 64 ulps) both
-                // are evaluated again in fp64 from the error's definition,
-                // with their own entries; the lower error wins, the lower k on
-                // equal errors.
-                int k2 = kstar == 0 ? 1 : 0;
-                float c2 = cost[k2];
-#pragma unroll
-                for (int k = 0; k < 16; ++k)
-                    if (k != kstar && cost[k] < c2) { c2 = cost[k]; k2 = k; }
-                const bool near = !skip && c2 - cbv <= 0x1p-18f * fabsf(cbv);
-                if (__ballot(near) == 0) {
-                    idx = pick(kstar);
-                } else {
-                    const int i1 = pick(kstar);
-                    const int i2 = pick(k2);
-                    __asm__ volatile("" ::: "memory");
-                    float xr[8], wr[8];
-                    load_group(xb, wblk, g, skip, xr, wr);
-                    const double dd = (double)d;
-                    double e1 = group_error64(xr, wr, neg, sgrid + entry_off<kChunk>(i1),
-                                              dd * (double)(2 * kstar + 1));
-                    double e2 = group_error64(xr, wr, neg, sgrid + entry_off<kChunk>(i2),
-                                              dd * (double)(2 * k2 + 1));
-                    e1 += __shfl_xor(e1, 1);        // the other group of the scale group
-                    e2 += __shfl_xor(e2, 1);
-                    const bool take2 = near && (e2 < e1 || (e2 == e1 && k2 < kstar));
-                    idx = take2 ? i2 : i1;
-                    if (take2) kstar = k2;
-                }
-            }
-            const int kodd = __shfl_xor(kstar, 2);
-            const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
+        // Every local scale k for every scale group: the payload forced to k.
+        for (int k = 0; k < 16; ++k) {
+            const int idx = pick(k);
             if (!skip && kb == 0) {
-                uint8_t* ob = sout + slot * kBlockBytes;
+                uint8_t* ob = sout + (k * kBlocksPerWG + slot) * kBlockBytes;
+                const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
                 ob[2 + 2 * g] = (uint8_t)(code & 0xff);
                 ob[3 + 2 * g] = (uint8_t)(code >> 8);
-                if ((g & 3) == 0) ob[66 + (m >> 1)] = (uint8_t)(kstar | (kodd << 4));
+                if ((g & 3) == 0) ob[66 + (m >> 1)] = (uint8_t)(k | (k << 4));
                 if (g == 0) {
                     ob[0] = (uint8_t)(dh & 0xff);
                     ob[1] = (uint8_t)(dh >> 8);
                 }
             }
-            if (kMode == kModeFake && kb == 0) {
-                // The decoded group, d*(2k+1)*sign*q with the payload's fields
-                // (the 8th sign from even parity of the 7-bit mask; a zero
-                // block decodes as the all-zero payload does; a rejected block
-                // is written as zeros).
-                const uint32_t cz = skip ? 0u : code;
-                const int kz = skip ? 0 : kstar;
-                const float sk = f16_bits_to_f32(skip ? 0u : dh) * (float)(2 * kz + 1);
-                const uint32_t mask = cz >> 9;
-                const uint32_t signs = mask | ((__popc(mask) & 1u) << 7);
-                const float* q = sgrid + entry_off<kChunk>((int)(cz & 0x1ffu));
-                float v[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    v[j] = bad_block ? 0.0f : (((signs >> j) & 1u) ? -sk : sk) * q[j];
-                float4* o = reinterpret_cast<float4*>(a.xhat + blk * kBlockElems + g * 8);
-                o[0] = make_float4(v[0], v[1], v[2], v[3]);
-                o[1] = make_float4(v[4], v[5], v[6], v[7]);
-            }
-        } else {
-            // Top-C local scales by (cost, k); a zero scale makes every choice
-            // decode to zero with entry 0 and no signs, so the order is k = 0, 1, ...
-            const int C = a.top_c;
-            float xo[8], wo[8];
-            load_group(xb, wblk, g, bad_block, xo, wo);   // the original values
-            int used = 0;
-            for (int r = 0; r < C; ++r) {
-                int kr = -1;
-                float cr = 0.0f;
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const bool free_k = !((used >> k) & 1);
-                    const bool better = zero_scale ? (kr < 0) : (kr < 0 || cost[k] < cr);
-                    if (free_k && better) { kr = k; cr = cost[k]; }
-                }
-                used |= 1 << kr;
-                int idx = pick(kr);
-                int msk = neg & 0x7f;
-                if (zero_scale) { idx = 0; msk = 0; }
-                if (kb == 0) {
-                    const int64_t base = (blk * 16 + m) * C + r;     // [block][m][r]
-                    float ev[8];
-                    if (bad_block) {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) ev[j] = 0.0f;
-                    } else if (grid_exact) {
-                        // xhat exact in fp32: d*(2k+1) has at most 16
-                        // significant bits and a bf16-exact q at most 8, so
-                        // the product has at most 24; one rounding of xhat - x.
-                        const float sk = d * (float)(2 * kr + 1);
-                        const float* q = sgrid + entry_off<kChunk>(idx);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float sg = (!zero_scale && ((neg >> j) & 1)) ? -sk : sk;
-                            ev[j] = sg * q[j] - xo[j];
-                        }
-                    } else {
-                        // xhat in fp64 (exact: d*(2k+1) has at most 16
-                        // significant bits), one rounding of xhat - x to fp32.
-                        const double sk = (double)d * (double)(2 * kr + 1);
-                        const float* q = sgrid + entry_off<kChunk>(idx);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const double sg = (!zero_scale && ((neg >> j) & 1)) ? -sk : sk;
-                            ev[j] = (float)(sg * (double)q[j] - (double)xo[j]);
-                        }
-                    }
-                    float4* ep = reinterpret_cast<float4*>(a.cand_err + base * 16 + h * 8);
-                    ep[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
-                    ep[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
-                    if (h == 0) a.cand_choice[base] = kr;
-                    if (a.cand_codes)
-                        a.cand_codes[base * 2 + h] = bad_block ? (uint16_t)0 : (uint16_t)(idx | (msk << 9));
-                }
-            }
         }
     }
-    if (!kCandidates && a.out) {
+    if (a.out) {
         // Copy the staged payloads out and clear what was copied (each word
         // by the thread that copied it) for the next set.
         __syncthreads();
@@ -721,8 +564,9 @@ __device__ __forceinline__ int wide_entry(int t, int hl, int v)
     return kWTile * t + 8 * (v >> 2) + 4 * hl + (v & 3);
 }
 
-// VALU rescan for local scale k over rows v0 .. v0+nv-1 of half hs in both
-// tiles of chunk `chunk`: the lowest entry with the least key.
+// VALU rescan for local scale k over rows v0 .. v0+nv-1 of half hs in the
+// kCT tiles of chunk `chunk`: the lowest entry with the least key.
+template <int kCT>
 __device__ __forceinline__ int rescan_wide(const float* __restrict__ sg, int chunk, int hs, int v0,
                                            int nv, int k, const float (&wxs)[8],
                                            const float (&w)[8], float inv_d, float* key_out)
@@ -730,10 +574,10 @@ __device__ __forceinline__ int rescan_wide(const float* __restrict__ sg, int chu
     const float mk = (float)(2 * k + 1);
     int idx = -1;
     float vbest = 0.0f;
-    for (int tt = 0; tt < kWChunkTiles; ++tt) {
+    for (int tt = 0; tt < kCT; ++tt) {
         for (int v = v0; v < v0 + nv; ++v) {
-            const int e = wide_entry(chunk * kWChunkTiles + tt, hs, v);
-            const float2* p = reinterpret_cast<const float2*>(sg + entry_off<kWChunk>(e));
+            const int e = wide_entry(chunk * kCT + tt, hs, v);
+            const float2* p = reinterpret_cast<const float2*>(sg + entry_off<kWTile * kCT>(e));
             float q[8], q2[8];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -755,25 +599,35 @@ __device__ __forceinline__ int rescan_wide(const float* __restrict__ sg, int chu
     return idx;
 }
 
-template <int kDT>
-__global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs a)
+// kMode: kModePayload, kModeFake or kModeCandidates; kDT: the weight's
+// iq_dtype_t.
+template <int kMode, int kDT>
+__global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
 {
+    constexpr bool kCand = kMode == kModeCandidates;
+    // Tiles per tracking chunk: 2 (64 entries) for one pick per group; the
+    // candidates pick top_c local scales per group, each rescanning one
+    // lane-half of a chunk, so their chunks are one tile (32 entries): twice
+    // the tracking in the sweep, half the rescan per pick.
+    constexpr int kCT = kCand ? 1 : kWChunkTiles;
+    constexpr int kCh = kWTile * kCT;
     __shared__ float sgrid[kMaxGrid * kEntryStride + 2 * (kMaxGrid / 32)];  // q[0..7], q^2[0..7]
     __shared__ uint4 sbq[kMaxGrid];                     // entry e: q[0..7] as bf16
     __shared__ uint4 sbq2[kMaxGrid];                    // entry e: q^2[0..7] as bf16
     __shared__ int sgrid_bad, sgrid_inexact;
     __shared__ float4 ssnap[4 * kThreads];              // per lane: the minima at the last chunk end
-    __shared__ uint16_t sout16[kWavesPerWG * kBlockBytes / 2];    // the set's payloads
+    __shared__ uint16_t sout16[kCand ? 1 : kWavesPerWG * kBlockBytes / 2];    // the set's payloads
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: block pointers in SGPRs
     const int n = a.grid_size;
-    const int nchunks = (n + kWChunk - 1) / kWChunk;
-    const int npad = nchunks * kWChunk;
+    const int nchunks = (n + kCh - 1) / kCh;
+    const int npad = nchunks * kCh;
 
     if (tid == 0) { sgrid_bad = 0; sgrid_inexact = 0; }
-    for (int i = tid; i < kWavesPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
+    if (!kCand)
+        for (int i = tid; i < kWavesPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     {
         int bad = 0, inexact = 0;
@@ -782,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
             const int src = e < n ? e : n - 1;
             const float a0 = a.grid[8 * src + 2 * t], a1 = a.grid[8 * src + 2 * t + 1];
             bad |= !(a0 >= 0.0f && finite_f32(a0) && a1 >= 0.0f && finite_f32(a1));
-            float2* ge = reinterpret_cast<float2*>(sgrid + entry_off<kWChunk>(e));
+            float2* ge = reinterpret_cast<float2*>(sgrid + entry_off<kCh>(e));
             ge[t] = make_float2(a0, a1);
             ge[4 + t] = make_float2(a0 * a0, a1 * a1);
             inexact |= !(bf16_exact_with_square(a0) && bf16_exact_with_square(a1));
@@ -800,6 +654,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
     // Persistent workgroups: the grid is staged once, then each workgroup
     // takes every gridDim.x-th set of 16 blocks, a block per wave; the set's
     // payloads are staged in LDS and stored together (whole cache lines).
+    // The candidates are written straight from the lanes.
     const int64_t nsets = (a.g.nblocks + kWavesPerWG - 1) / kWavesPerWG;
     for (int64_t set = blockIdx.x; set < nsets; set += gridDim.x) {
     if (set != blockIdx.x) __syncthreads();     // the previous set's payloads are out
@@ -842,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
         for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
 
         uint32_t dh;
-        if (a.scales) {
+        if (!kCand && a.scales) {
             dh = (uint32_t)a.scales[blk];
         } else {
             const float t = amax / 155.0f;
@@ -856,7 +711,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
         const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
 
         bool choice_bad = false;
-        if (a.choices) {
+        if (!kCand && a.choices) {
             int ln = lane;                  // opaque: the address is formed here, not hoisted
             __asm__ volatile("" : "+v"(ln));
             const int cv = ln < 16 ? a.choices[blk * 16 + ln] : 0;
@@ -906,8 +761,8 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
             const v8bf opw2 = as_v8bf(make_uint4(hw2[0] | (hw2[1] << 16), hw2[2] | (hw2[3] << 16),
                                                  hw2[4] | (hw2[5] << 16), hw2[6] | (hw2[7] << 16)));
             for (int ch = 0; ch < nchunks; ++ch) {
-                for (int tt = 0; tt < kWChunkTiles; ++tt) {
-                    const int e = (ch * kWChunkTiles + tt) * kWTile + g;
+                for (int tt = 0; tt < kCT; ++tt) {
+                    const int e = (ch * kCT + tt) * kWTile + g;
                     const v8bf aq = as_v8bf(sbq[e]), aq2 = as_v8bf(sbq2[e]);
                     const v16f pn = mfma32(aq, opp2, mfma32(aq, opp1, zero16));
                     const v16f nn = mfma32(aq2, opw2, mfma32(aq2, opw1, zero16));
@@ -928,9 +783,9 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
                 bw[s2] = w[j];
             }
             for (int ch = 0; ch < nchunks; ++ch) {
-                for (int tt = 0; tt < kWChunkTiles; ++tt) {
-                    const int e = (ch * kWChunkTiles + tt) * kWTile + g;
-                    const float* q = sgrid + entry_off<kWChunk>(e);
+                for (int tt = 0; tt < kCT; ++tt) {
+                    const int e = (ch * kCT + tt) * kWTile + g;
+                    const float* q = sgrid + entry_off<kCh>(e);
                     v16f pn = zero16, nn = zero16;
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2) {
@@ -948,7 +803,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
         __asm__ volatile("" ::: "memory");
         load_group(xb, wblk, g, skip, x, w);
         const int neg2 = group_signs(x, w);
-        const int forced = (a.choices && !choice_bad) ? a.choices[blk * 16 + m] : -1;
+        const int forced = (!kCand && a.choices && !choice_bad) ? a.choices[blk * 16 + m] : -1;
         float wxs[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -983,18 +838,19 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
             if (!tie) {
                 const int hs = (om < lm) ? (hl ^ 1) : hl;             // holder half
                 const int tch = __shfl(tchunk, g + 32 * hs);
-                idx = rescan_wide(sgrid, tch, hs, 8 * hl, 8, k, wxs, w, inv_d, &key);
+                idx = rescan_wide<kCT>(sgrid, tch, hs, 8 * hl, 8, k, wxs, w, inv_d, &key);
                 const float ok = __shfl_xor(key, 32);
                 const int oi = __shfl_xor(idx, 32);
                 if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
             } else {
-                idx = rescan_wide(sgrid, tchunk, hl, 0, 16, k, wxs, w, inv_d, &key);
+                idx = rescan_wide<kCT>(sgrid, tchunk, hl, 0, 16, k, wxs, w, inv_d, &key);
                 const int oi = __shfl_xor(idx, 32);
                 if (om < lm || (om == lm && oi < idx)) idx = oi;
             }
             return idx < n ? idx : n - 1;
         };
 
+        if constexpr (!kCand) {
         int kstar = 0;
         float cbv = cost[0];
 #pragma unroll
@@ -1020,9 +876,9 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
                 float xr[8], wr[8];
                 load_group(xb, wblk, g, skip, xr, wr);
                 const double dd = (double)d;
-                double e1 = group_error64(xr, wr, neg2, sgrid + entry_off<kWChunk>(i1),
+                double e1 = group_error64(xr, wr, neg2, sgrid + entry_off<kCh>(i1),
                                           dd * (double)(2 * kstar + 1));
-                double e2 = group_error64(xr, wr, neg2, sgrid + entry_off<kWChunk>(i2),
+                double e2 = group_error64(xr, wr, neg2, sgrid + entry_off<kCh>(i2),
                                           dd * (double)(2 * k2 + 1));
                 e1 += quad_xchg<kQuadXor1>(e1);  // the other group of the scale group
                 e2 += quad_xchg<kQuadXor1>(e2);
@@ -1045,8 +901,123 @@ __global__ __launch_bounds__(kThreads) void iq2xs_payload_wide_kernel(Iq2xsArgs 
                 ob[1] = (uint8_t)(dh >> 8);
             }
         }
+        if (kMode == kModeFake && hl == 0) {
+            // The decoded group, d*(2k+1)*sign*q with the payload's fields
+            // (the 8th sign from even parity of the 7-bit mask; a zero block
+            // decodes as the all-zero payload does; a rejected block is
+            // written as zeros), with the decode kernel's fp32 expression.
+            const uint32_t cz = skip ? 0u : code;
+            const int kz = skip ? 0 : kstar;
+            const float sk = f16_bits_to_f32(skip ? 0u : dh) * (float)(2 * kz + 1);
+            const uint32_t mask = cz >> 9;
+            const uint32_t signs = mask | ((__popc(mask) & 1u) << 7);
+            const float* q = sgrid + entry_off<kCh>((int)(cz & 0x1ffu));
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = bad_block ? 0.0f : (((signs >> j) & 1u) ? -sk : sk) * q[j];
+            float4* o = reinterpret_cast<float4*>(a.xhat + blk * kBlockElems + g * 8);
+            o[0] = make_float4(v[0], v[1], v[2], v[3]);
+            o[1] = make_float4(v[4], v[5], v[6], v[7]);
+        }
+        } else {
+            // Top-C local scales by (cost, k); a zero scale makes every choice
+            // decode to zero with entry 0 and no signs, so the order is k = 0,
+            // 1, ...  Each pick rescans one lane-half of a 32-entry chunk.
+            const int C = a.top_c;
+            const int h = g & 1;                // group in the scale group
+            // The scale group's fp64 error under local scale k with this
+            // lane's entry (and the other group's, one column away).
+            auto cost64 = [&](int k, int e) -> double {
+                __asm__ volatile("" ::: "memory");
+                float xr[8], wr[8];
+                load_group(xb, wblk, g, skip, xr, wr);
+                const double v = group_error64(xr, wr, neg2, sgrid + entry_off<kCh>(e),
+                                               (double)d * (double)(2 * k + 1));
+                return v + quad_xchg<kQuadXor1>(v);
+            };
+            float xo[8], wo[8];
+            load_group(xb, wblk, g, bad_block, xo, wo);   // the original values
+            int used = 0;
+            for (int r = 0; r < C; ++r) {
+                int kr = -1;
+                float cr = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const bool free_k = !((used >> k) & 1);
+                    const bool better = zero_scale ? (kr < 0) : (kr < 0 || cost[k] < cr);
+                    if (free_k && better) { kr = k; cr = cost[k]; }
+                }
+                // Unused local scales whose fp32 cost is within 2^-18 of the
+                // least's magnitude are ranked again by their fp64 errors
+                // (with their own entries), the lower k on equal errors, as
+                // the payload's runner-up is.
+                uint32_t nearm = 0u;
+                if (!skip) {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k)
+                        if (!((used >> k) & 1) && k != kr && cost[k] - cr <= 0x1p-18f * fabsf(cr))
+                            nearm |= 1u << k;
+                }
+                int idx;
+                if (__ballot(nearm != 0u) != 0) {               // wave-uniform
+                    idx = pick(kr);
+                    double b64 = cost64(kr, idx);
+                    for (int k = 0; k < 16; ++k) {
+                        if (__ballot((nearm >> k) & 1u) == 0) continue;   // wave-uniform
+                        const int ik = pick(k);
+                        const double e = cost64(k, ik);
+                        if (((nearm >> k) & 1u) && (e < b64 || (e == b64 && k < kr))) {
+                            b64 = e;
+                            kr = k;
+                            idx = ik;
+                        }
+                    }
+                } else {
+                    idx = pick(kr);
+                }
+                used |= 1 << kr;
+                int msk = neg2 & 0x7f;
+                if (zero_scale) { idx = 0; msk = 0; }
+                if (hl == 0) {
+                    const int64_t base = (blk * 16 + m) * C + r;     // [block][m][r]
+                    float ev[8];
+                    if (bad_block) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) ev[j] = 0.0f;
+                    } else if (grid_exact) {
+                        // xhat exact in fp32: d*(2k+1) has at most 16
+                        // significant bits and a bf16-exact q at most 8, so
+                        // the product has at most 24; one rounding of xhat - x.
+                        const float sk = d * (float)(2 * kr + 1);
+                        const float* q = sgrid + entry_off<kCh>(idx);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float sg = (!zero_scale && ((neg2 >> j) & 1)) ? -sk : sk;
+                            ev[j] = sg * q[j] - xo[j];
+                        }
+                    } else {
+                        // xhat in fp64 (exact: d*(2k+1) has at most 16
+                        // significant bits), one rounding of xhat - x to fp32.
+                        const double sk = (double)d * (double)(2 * kr + 1);
+                        const float* q = sgrid + entry_off<kCh>(idx);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const double sg = (!zero_scale && ((neg2 >> j) & 1)) ? -sk : sk;
+                            ev[j] = (float)(sg * (double)q[j] - (double)xo[j]);
+                        }
+                    }
+                    float4* ep = reinterpret_cast<float4*>(a.cand_err + base * 16 + h * 8);
+                    ep[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
+                    ep[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
+                    if (h == 0) a.cand_choice[base] = kr;
+                    if (a.cand_codes)
+                        a.cand_codes[base * 2 + h] = bad_block ? (uint16_t)0 : (uint16_t)(idx | (msk << 9));
+                }
+            }
+        }
     }
-    if (a.out) {
+    if (!kCand && a.out) {
         // Copy the set's payloads out and clear what was copied (each word
         // by the thread that copied it) for the next set.
         __syncthreads();
@@ -1077,14 +1048,16 @@ hipError_t launch_mode(const Iq2xsArgs& a, int mode, hipStream_t stream)
 {
     const unsigned wgs = persistent_wgs(a.g);
     if (mode == kModeEvery)
-        hipLaunchKernelGGL((iq2xs_kernel<kModeEvery, kDT>), dim3(wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((iq2xs_every_kernel<kDT>), dim3(wgs), dim3(kThreads), 0, stream, a);
     else if (mode == kModeFake)
-        hipLaunchKernelGGL((iq2xs_kernel<kModeFake, kDT>), dim3(wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((iq2xs_wide_kernel<kModeFake, kDT>), dim3(wgs), dim3(kThreads), 0,
+                           stream, a);
     else if (mode == kModeCandidates)
-        hipLaunchKernelGGL((iq2xs_kernel<kModeCandidates, kDT>), dim3(wgs), dim3(kThreads), 0,
+        hipLaunchKernelGGL((iq2xs_wide_kernel<kModeCandidates, kDT>), dim3(wgs), dim3(kThreads), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((iq2xs_payload_wide_kernel<kDT>), dim3(wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((iq2xs_wide_kernel<kModePayload, kDT>), dim3(wgs), dim3(kThreads), 0,
+                           stream, a);
     return hipGetLastError();
 }
 

@@ -29,6 +29,12 @@
  *     written to `*status` with an atomic compare-and-swap from 0, so the first
  *     code to land sticks; the library never clears `*status`: the caller
  *     zeroes it.  Blocks with a data error are written as zeros.
+ *   - `status` may be NULL in every call that takes it.  The call then
+ *     reports into a status word of the library's own (one per device, a
+ *     file-scope device variable: nothing is allocated), waits for `stream`
+ *     to drain, and returns the first data error code, or IQ_OK.  Such calls
+ *     block the host, cannot be captured in a graph, and are serialized per
+ *     device by a lock the library holds until the word has been read back.
  *   - Concurrent calls that share `status` or an output buffer race.
  *   - Layouts are row-major and contiguous.  Weights are [batch][rows][cols]
  *     with cols a positive multiple of 256, stored as fp32, bf16, fp16 or fp64
@@ -129,9 +135,10 @@ const char* iq_status_str(iq_status_t st);
  *              *status = IQ_ERR_ARG.
  * IQ1_M ties: the lower shift, then the lower entry (#2525 IQ1_M CUDA body).
  *   out        [batch][rows][cols/256][block_bytes] uint8.
- *   status     one int32 (see the conventions above); required.
+ *   status     NULL, or one int32 (see the conventions above).
  * Errors: IQ_ERR_NULL, IQ_ERR_FORMAT, IQ_ERR_SHAPE, IQ_ERR_GRID, IQ_ERR_DEVICE,
- * IQ_ERR_HIP synchronously; the device codes through *status.
+ * IQ_ERR_HIP synchronously; the device codes through *status, or as the
+ * return value when status is NULL.
  */
 iq_status_t iq_encode(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t batch,
                       int64_t rows, int64_t cols, const float* importance, const float* grid,
@@ -187,8 +194,8 @@ iq_status_t iq_fake_quant(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int
  *   packed  [batch][rows][cols/256][block_bytes] uint8.
  *   grid    [grid_size][8] fp32 (the grid the payload was encoded with).
  *   out     [batch][rows][cols] fp32.
- *   status  one int32, required; IQ_ERR_CODE if an index is >= grid_size (that
- *           group decodes to zeros).
+ *   status  NULL or one int32 (see the conventions above); IQ_ERR_CODE if an
+ *           index is >= grid_size (that group decodes to zeros).
  */
 iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, int64_t rows,
                        int64_t cols, const float* grid, int32_t grid_size, float* out,
@@ -215,7 +222,8 @@ iq_status_t iq_dequant(iq_format_t fmt, const uint8_t* packed, int64_t batch, in
  *   cand_codes  NULL, or IQ2_XS [..][top_c][2] uint16 (index | mask<<9 per group),
  *               IQ1_M [..][top_c][2] (index | shift<<11 per group),
  *               IQ1_S [..][top_c][4] uint16 (the grid index of each group).
- *   status      one int32, required; a block with a data error is all zeros.
+ *   status      NULL or one int32 (see the conventions above); a block with a
+ *               data error is all zeros.
  */
 iq_status_t iq_encode_candidates(iq_format_t fmt, iq_dtype_t wdtype, const void* w, int64_t rows,
                                  int64_t cols, const float* importance, const float* grid,

@@ -427,9 +427,10 @@ static int iq1m_decode_block(const uint8_t* blk, const float* grid, int n, doubl
     int st = ORC_OK;
     uint32_t sc[4];
     for (int wd = 0; wd < 4; ++wd) sc[wd] = (uint32_t)blk[48 + 2 * wd] | ((uint32_t)blk[49 + 2 * wd] << 8);
-    /* d from the top nibble of each scale word, as the IQ1_M page prints it */
-    uint16_t dh = (uint16_t)((sc[0] >> 12) | ((sc[1] >> 8) & 0x00f0u) | ((sc[2] >> 4) & 0x0f00u) |
-                             (sc[3] & 0xf000u));
+    /* d's fp16 bits: nibble wd (bits 4wd..4wd+3) is the top nibble of scale
+       word wd (IQ1_M codec body, the four scale words) */
+    uint16_t dh = 0;
+    for (int wd = 0; wd < 4; ++wd) dh = (uint16_t)(dh | ((sc[wd] >> 12) << (4 * wd)));
     double d = orc_f16_to_f64(dh);
     for (int g = 0; g < 32; ++g) {
         int m = g / 2;

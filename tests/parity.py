@@ -12,6 +12,17 @@ import oracle
 
 TIE_RTOL = 1e-6
 
+# Oracle results of the full-size workloads, computed once per test process
+# (several tests compare different outputs of the GPU with the same encode).
+_ORACLE_CACHE = {}
+
+
+def oracle_cached(key, fn):
+    """fn() the first time key is asked for, the stored result afterwards."""
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE[key] = fn()
+    return _ORACLE_CACHE[key]
+
 
 def scale_bits(fmt, packed):
     """fp16 bits of every block's d: bytes 0-1, or for IQ1_M the top nibbles of
@@ -19,8 +30,7 @@ def scale_bits(fmt, packed):
     p = np.ascontiguousarray(packed).reshape(-1, oracle.BLOCK_BYTES[fmt]).astype(np.int64)
     if fmt == "iq1_m":
         sc = p[:, 48:56:2] | (p[:, 49:56:2] << 8)
-        return ((sc[:, 0] >> 12) | ((sc[:, 1] >> 8) & 0x00F0) | ((sc[:, 2] >> 4) & 0x0F00)
-                | (sc[:, 3] & 0xF000))
+        return sum((sc[:, w] >> 12) << (4 * w) for w in range(4))
     return p[:, 0] | (p[:, 1] << 8)
 
 
@@ -143,3 +153,180 @@ def near_tie_blocks(fmt, nblk=32, seed=0, weighted=True, steps=40):
     e = np.sort(all_errors(w), axis=1)
     gap = (e[:, 1] - e[:, 0]) / e[:, 0]
     return w, grid, imp, d.astype(np.uint16), unit, np.where(ok, gap, np.inf)
+
+
+def unit_choices(fmt, packed):
+    """The choice of every choice group: [n, G] int (IQ1_S c = k + 8*deltabit,
+    IQ2_XS and IQ1_M the local scale k)."""
+    p = np.ascontiguousarray(packed).reshape(-1, oracle.BLOCK_BYTES[fmt]).astype(np.int64)
+    if fmt == "iq1_s":
+        return (p[:, 34:50:2] | (p[:, 35:50:2] << 8)) >> 12
+    if fmt == "iq2_xs":
+        nib = p[:, 66:74]
+        return np.stack([nib & 15, nib >> 4], axis=2).reshape(-1, 16)
+    sc = p[:, 48:56:2] | (p[:, 49:56:2] << 8)
+    return np.stack([(sc >> (3 * t)) & 7 for t in range(4)], axis=2).reshape(-1, 16)
+
+
+def set_entry(fmt, blk, g, e, shift=None):
+    """A copy of one packed block with group g (0..31) given grid entry e (and,
+    for IQ1_M, the shift bit); every other field is kept."""
+    b = np.array(blk, dtype=np.uint8).reshape(-1).copy()
+    if fmt == "iq1_s":
+        i, l = divmod(g, 4)
+        b[2 + 4 * i + l] = e & 0xFF
+        qh = int(b[34 + 2 * i]) | (int(b[35 + 2 * i]) << 8)
+        qh = (qh & ~(7 << (3 * l))) | (((e >> 8) & 7) << (3 * l))
+        b[34 + 2 * i], b[35 + 2 * i] = qh & 0xFF, qh >> 8
+    elif fmt == "iq2_xs":
+        code = int(b[2 + 2 * g]) | (int(b[3 + 2 * g]) << 8)
+        code = (code & ~0x1FF) | (e & 0x1FF)
+        b[2 + 2 * g], b[3 + 2 * g] = code & 0xFF, code >> 8
+    else:
+        b[g] = e & 0xFF
+        byte, sh = 32 + g // 2, 4 * (g & 1)
+        nib = ((e >> 8) & 7) | ((shift & 1) << 3)
+        b[byte] = (int(b[byte]) & ~(0xF << sh)) | (nib << sh)
+    return b
+
+
+def entry_tie_blocks(fmt, nblk=48, seed=0, weighted=True):
+    """Blocks in which, under a forced choice and a pinned scale, one group's
+    two best grid entries differ in weighted error by 1.1e-6 to 4e-6 of its
+    choice group's error: above the tie bar, so a search that orders the two
+    entries by fp32 rounding gets some of these wrong.  For IQ1_M the
+    candidates are (shift, entry) pairs, and every second block aims at a pair
+    with different shifts.
+
+    The group's values are scaled by a factor alpha (its signs, and so the
+    IQ2_XS sign pattern, do not change); groups that hold the block's largest
+    magnitude, or would after scaling, are left alone, so the pinned scale is
+    the one the block predicts (IQ1_S, IQ2_XS; IQ1_M's also follows the RMS).  Every candidate's decoded values come
+    from the oracle's decode of the block with that candidate set in, so the
+    errors are the oracle's definition; the error difference of two entries is
+    linear in alpha, so the entry that first overtakes the best one as alpha
+    moves is found from the crossing points, and alpha is bisected between
+    that crossing and 1 to the target gap.  The gap is finally measured on the
+    oracle's own encode of the result.
+
+    Returns (w [1, nblk, 256], grid, imp or None, scales [1, nblk] uint16,
+    choices [1, nblk, 1, G] int32, group per block, kind per block (0 same
+    shift, 1 different shifts), relative gap per block (inf where no usable
+    crossing was found))."""
+    import workloads
+    grid = grid_for(fmt, None, seed)
+    n = grid.shape[0]
+    G = oracle.NUM_CHOICE_GROUPS[fmt]
+    per_unit = 32 // G                      # groups of 8 per choice group
+    w0 = workloads.student_t_weight((1, nblk, 256), 300 + seed)
+    imp = workloads.lognormal_importance((1, 256), 400 + seed) if weighted else None
+    wt = np.ones(256) if imp is None else imp.astype(np.float64).reshape(256)
+    d = oracle.predict_scales(fmt, w0).reshape(1, nblk)
+    p0 = oracle.encode(fmt, w0, grid, imp, scales=d).reshape(nblk, -1)
+    ch = unit_choices(fmt, p0).astype(np.int32)
+    target = 1.1e-6 * (4.0 / 1.1) ** ((np.arange(nblk) % 8) / 7.0)
+    shifts = (0, 1) if fmt == "iq1_m" else (None,)
+    x = w0.reshape(nblk, 256).astype(np.float32).copy()
+    groups = (np.arange(nblk) * 7) % 32
+    kinds = np.zeros(nblk, np.int64)
+    found = np.zeros(nblk, bool)
+    for b in range(nblk):
+        g = int(groups[b])
+        u = g // per_unit
+        cols = slice(8 * g, 8 * g + 8)
+        xg = x[b, cols].astype(np.float64)
+        wg = wt[cols]
+        # decoded values of every candidate (shift, entry) of group g
+        cands = [(s, e) for s in shifts for e in range(n)]
+        blks = np.stack([set_entry(fmt, p0[b], g, e, s) for s, e in cands])
+        xh = oracle.decode(fmt, blks.reshape(-1, 1, blks.shape[1]), grid).reshape(-1, 256)[:, cols]
+        rest = (oracle.block_errors(fmt, p0[b:b + 1], x[b:b + 1], grid,
+                                    None if imp is None else wt[None].astype(np.float32))[0, u]
+                - float((wg * (xg - xh[[cands.index(_pick(fmt, p0[b], g))]][0]) ** 2).sum()))
+        err = lambda a: ((wg[None] * (a * xg[None] - xh) ** 2).sum(axis=1))   # noqa: E731
+        e1 = int(np.argmin(err(1.0)))
+        # D_e(alpha) = E_e - E_e1 = c0_e - alpha * c1_e
+        c0 = (wg[None] * (xh ** 2 - xh[e1][None] ** 2)).sum(axis=1)
+        c1 = 2.0 * (wg[None] * xg[None] * (xh - xh[e1][None])).sum(axis=1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            cross = np.where(np.abs(c1) > 0, c0 / c1, np.inf)
+        cross[e1] = np.inf
+        want_other = fmt == "iq1_m" and b % 2 == 1
+        best = None
+        for side in (1, -1):            # alpha growing past 1, or shrinking below it
+            ok = (np.sign(cross - 1.0) == side) & (np.abs(cross - 1.0) < 0.5)
+            if not ok.any():
+                continue
+            first = int(np.argmin(np.where(ok, np.abs(cross - 1.0), np.inf)))
+            if want_other:
+                other = ok & (np.array([s for s, _ in cands]) != cands[e1][0])
+                if not other.any():
+                    continue
+                cand2 = int(np.argmin(np.where(other, np.abs(cross - 1.0), np.inf)))
+                if cand2 != first and abs(cross[cand2] - 1.0) > abs(cross[first] - 1.0):
+                    continue            # another entry overtakes e1 before the other shift does
+                first = cand2
+            if best is None or abs(cross[first] - 1.0) < abs(cross[best] - 1.0):
+                best = first
+        if best is None:
+            continue
+        e2 = best
+        ac = float(cross[e2])
+
+        def ratio(t):
+            a = ac + t * (1.0 - ac)
+            E = err(a)
+            return (E[e2] - E[e1]) / (E[e1] + rest)
+
+        if not ratio(1.0) > target[b]:
+            continue
+        lo, hi = 0.0, 1.0
+        for _ in range(60):
+            mid = 0.5 * (lo + hi)
+            if ratio(mid) < target[b]:
+                lo = mid
+            else:
+                hi = mid
+        a = ac + hi * (1.0 - ac)
+        E = err(a)
+        if int(np.argmin(E)) != e1 or int(np.argsort(E, kind="stable")[1]) != e2:
+            continue
+        # keep the block's largest magnitude where it is, so the pinned scale is
+        # also the one the block predicts
+        amax = np.abs(x[b]).max()
+        others = np.abs(np.delete(x[b], np.arange(8 * g, 8 * g + 8))).max()
+        if not np.abs((a * xg).astype(np.float32)).max() < others or others != amax:
+            continue
+        x[b, cols] = (a * xg).astype(np.float32)
+        kinds[b] = int(cands[e1][0] != cands[e2][0]) if fmt == "iq1_m" else 0
+        found[b] = True
+    w = x.reshape(1, nblk, 256)
+    choices = ch.reshape(1, nblk, 1, G)
+    p = oracle.encode(fmt, w, grid, imp, scales=d, choices=choices).reshape(nblk, -1)
+    gap = np.full(nblk, np.inf)
+    ib = None if imp is None else np.broadcast_to(imp.reshape(1, 256), (nblk, 256))
+    e_all = oracle.block_errors(fmt, p, x, grid, ib)
+    for b in np.nonzero(found)[0]:
+        g = int(groups[b])
+        u = g // per_unit
+        # the runner-up: the best candidate of group g other than the oracle's pick
+        cands = [(s, e) for s in shifts for e in range(n)]
+        pick = _pick(fmt, p[b], g)
+        blks = np.stack([set_entry(fmt, p[b], g, e, s) for s, e in cands if (s, e) != pick])
+        eu = oracle.block_errors(fmt, blks, np.broadcast_to(x[b], (len(blks), 256)), grid,
+                                 None if ib is None else np.broadcast_to(ib[b], (len(blks), 256)))[:, u]
+        gap[b] = (eu.min() - e_all[b, u]) / e_all[b, u]
+    return (w, grid, imp, d.astype(np.uint16), choices, groups, kinds, gap)
+
+
+def _pick(fmt, blk, g):
+    """(shift or None, entry) of group g of one packed block."""
+    b = np.asarray(blk, dtype=np.int64).reshape(-1)
+    if fmt == "iq1_s":
+        i, l = divmod(g, 4)
+        qh = b[34 + 2 * i] | (b[35 + 2 * i] << 8)
+        return (None, int(b[2 + 4 * i + l] | (((qh >> (3 * l)) & 7) << 8)))
+    if fmt == "iq2_xs":
+        return (None, int((b[2 + 2 * g] | (b[3 + 2 * g] << 8)) & 0x1FF))
+    nib = (b[32 + g // 2] >> (4 * (g & 1))) & 0xF
+    return (int(nib >> 3), int(b[g] | ((nib & 7) << 8)))

@@ -63,7 +63,6 @@ def test_encode_argument_errors_need_no_gpu(lib):
     # stream
     assert enc(5, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 2
     assert enc(0, 0, None, 1, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 1
-    assert enc(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None, None) == 1
     assert enc(0, 0, FAKE, 1, 1, 200, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
     assert enc(0, 0, FAKE, 1, 0, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
     assert enc(0, 0, FAKE, 0, 1, 256, None, FAKE, 16, None, None, FAKE, FAKE, None) == 3
@@ -130,3 +129,33 @@ def test_batched_search_argument_errors_need_no_gpu(lib):
     assert cs(FAKE, FAKE, 0, 3, 16, 8, 2, FAKE, None, None) == 3
     assert cs(FAKE, FAKE, 4, 3, 4, 8, 2, FAKE, None, None) == 8
     assert cs(FAKE, None, 4, 3, 8, 8, 2, FAKE, None, None) == 1
+
+
+def _no_device_visible():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_device_visible(),
+                    reason="reaches the device check; with a GPU present it would launch on "
+                           "placeholder pointers")
+def test_null_status_is_an_argument_the_calls_accept(lib):
+    # A NULL status asks the call to synchronize and return the data error
+    # itself, so it is not IQ_ERR_NULL: argument errors still come first, and a
+    # call with valid arguments goes on to the device check, which fails here
+    # for want of a GPU (IQ_ERR_HIP or IQ_ERR_DEVICE), before any launch.
+    enc = lib.iq_encode
+    assert enc(0, 0, FAKE, 1, 1, 200, None, FAKE, 16, None, None, FAKE, None, None) == 3
+    assert enc(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, None, None, None) == 1
+    assert enc(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, None, None) in (10, 11)
+    ev = lib.iq_encode_every_choice
+    assert ev(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, FAKE, None, None) in (10, 11)
+    fq = lib.iq_fake_quant
+    assert fq(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, P(0x200000), None, None,
+              None) in (10, 11)
+    assert lib.iq_dequant(0, FAKE, 1, 1, 256, FAKE, 16, FAKE, None, None) in (10, 11)
+    assert lib.iq_dequant(0, FAKE, 1, 1, 256, FAKE, 16, P(0x200008), None, None) == 8
+    cand = lib.iq_encode_candidates
+    assert cand(1, 0, FAKE, 1, 256, None, FAKE, 16, 8, FAKE, FAKE, None, None, None) in (10, 11)
+    # a misaligned status word is still rejected
+    assert enc(0, 0, FAKE, 1, 1, 256, None, FAKE, 16, None, None, FAKE, P(0x300002), None) == 8

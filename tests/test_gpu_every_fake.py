@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads
-from tests.parity import compare_payloads, grid_for
+from tests.parity import compare_payloads, grid_for, oracle_cached
 
 pytestmark = pytest.mark.gpu
 
@@ -108,23 +108,19 @@ def test_every_choice_zeroes_rejected_blocks_in_every_payload(fmt):
     np.testing.assert_array_equal(ev.reshape(nc, 6, -1)[:, keep], ref.reshape(nc, 6, -1)[:, keep])
 
 
-def test_every_choice_c2_sampled():
-    # The full IQ1_S 4096x4096 weighted workload in one launch; sampled blocks
-    # against the oracle's forced encodes.
+def test_every_choice_c2_full():
+    # The full IQ1_S 4096x4096 weighted workload in one launch; all 16
+    # payloads, every block, against the oracle's forced encodes.
     cfg = workloads.c2_iq1s_4096()
     w, grid, imp = cfg["w"], cfg["grid"], cfg["importance"]
     B, R, C = w.shape
     every = iq.encode_every_choice(_dev(w), _dev(grid), _dev(imp), fmt="iq1_s")
     torch.cuda.synchronize()
     ev = every.cpu().numpy().reshape(16, -1, 50)
-    nblk = ev.shape[1]
-    idx = np.unique(np.concatenate([[0, nblk - 1], np.random.default_rng(31).integers(0, nblk, 40)]))
-    x = w.reshape(-1, 256)[idx]
-    ib = _block_imp(imp, B, R, C)[idx]
+    ref = oracle.encode_every_choice("iq1_s", w, grid, imp).reshape(16, -1, 50)
+    ib = _block_imp(imp, B, R, C)
     for c in range(16):
-        ref = oracle.encode("iq1_s", x.reshape(-1, 1, 256), grid, ib,
-                            choices=np.full((len(idx), 1, 1, 8), c, np.int32))
-        compare_payloads("iq1_s", ev[c, idx], ref, x, grid, ib)
+        compare_payloads("iq1_s", ev[c], ref[c], w.reshape(-1, 256), grid, ib)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -209,18 +205,16 @@ def test_fake_quant_rejects_output_overlapping_the_weight():
 
 def test_fake_quant_c2_full_size():
     # The fused path at the full IQ1_S 4096x4096 weighted workload: bitwise the
-    # decode of its own payload, the payload sampled against the oracle.
+    # decode of its own payload; the payload, every block, against the
+    # oracle's encode, and the values against the oracle's decode.
     cfg = workloads.c2_iq1s_4096()
     w, grid, imp = cfg["w"], cfg["grid"], cfg["importance"]
     xh, pk = iq.fake_quant(_dev(w), _dev(grid), _dev(imp), fmt="iq1_s", packed=True)
     xd = iq.dequant(pk, _dev(grid), fmt="iq1_s")
     torch.cuda.synchronize()
     np.testing.assert_array_equal(_bits(xh), _bits(xd))
-    p = pk.cpu().numpy().reshape(-1, 50)
-    np.testing.assert_array_equal(_scales_of(p), oracle.predict_scales("iq1_s", w))
-    idx = np.unique(np.random.default_rng(32).integers(0, p.shape[0], 256))
-    x = w.reshape(-1, 256)[idx]
-    ib = _block_imp(imp, *w.shape)[idx]
-    compare_payloads("iq1_s", p[idx], oracle.encode_blocks("iq1_s", x, grid, ib), x, grid, ib)
-    np.testing.assert_array_equal(xh.cpu().numpy().reshape(-1, 256)[idx].astype(np.float64),
-                                  oracle.decode("iq1_s", p[idx].reshape(-1, 1, 50), grid))
+    p = pk.cpu().numpy()
+    ref = oracle_cached(("c2", "iq1_s", "encode"), lambda: oracle.encode("iq1_s", w, grid, imp))
+    compare_payloads("iq1_s", p, ref, w.reshape(-1, 256), grid, _block_imp(imp, *w.shape))
+    np.testing.assert_array_equal(xh.cpu().numpy().astype(np.float64),
+                                  oracle.decode("iq1_s", p, grid))

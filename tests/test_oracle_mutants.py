@@ -37,6 +37,7 @@ MUTANTS = {
     "iq2xs_decode_nibbles_swapped": ("int k = (m & 1) ? (blk[66 + m / 2] >> 4) : (blk[66 + m / 2] & 15);", 0,
                                      "int k = (m & 1) ? (blk[66 + m / 2] & 15) : (blk[66 + m / 2] >> 4);"),
     "iq1m_anchor_offset_changed": ("volatile float a = 0.58f + t;", 0, "volatile float a = 0.6f + t;"),
+    "iq1m_d_nibbles_reversed": ("((sc[wd] >> 12) << (4 * wd))", 0, "((sc[wd] >> 12) << (4 * (3 - wd)))"),
     "iq2xs_candidates_reverse_order": ("if (kb < 0 || cost[k] < cost[kb]) kb = k;", 1,
                                        "if (kb < 0 || cost[k] > cost[kb]) kb = k;"),
     "search_score_drops_factor_two": ("score[c] = Q[g * C + c] + 2.0 * dot;", 0,

@@ -55,12 +55,12 @@ def iq2xs_fields(packed):
 
 
 def iq1m_fields(packed):
-    """IQ1_M fields: d reassembled from the top nibbles of the four scale words
-    as the IQ1_M page prints it; per group the entry and the shift bit; per
+    """IQ1_M fields: d's fp16 bits from the top nibbles of the four scale words
+    (word w carries bits 4w..4w+3); per group the entry and the shift bit; per
     scale group the 3-bit local scale."""
     b = packed.reshape(-1, 56).astype(np.int64)
     sc = b[:, 48:56:2] | (b[:, 49:56:2] << 8)
-    d = (sc[:, 0] >> 12) | ((sc[:, 1] >> 8) & 0x00F0) | ((sc[:, 2] >> 4) & 0x0F00) | (sc[:, 3] & 0xF000)
+    d = sum((sc[:, w] >> 12) << (4 * w) for w in range(4))
     nib = np.stack([b[:, 32:48] & 15, b[:, 32:48] >> 4], axis=2).reshape(-1, 32)
     ent = b[:, 0:32] | ((nib & 7) << 8)
     k = np.stack([(sc >> (3 * t)) & 7 for t in range(4)], axis=2).reshape(-1, 16)
