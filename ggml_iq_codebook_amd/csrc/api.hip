@@ -322,7 +322,7 @@ iq_status_t iq_choice_search_blocks(const float* H, const float* cand_err, int64
         return IQ_ERR_SHAPE;
     if (!H || !cand_err || !picks) return IQ_ERR_NULL;
     if ((G != 8 && G != 16) || C < 1 || C > 16 || sweeps < 0 || sweeps > 8) return IQ_ERR_ARG;
-    if (!aligned(H, 4) || !aligned(cand_err, 4) || !aligned(picks, 4) || (trace && !aligned(trace, 4)))
+    if (!aligned(H, 4) || !aligned(cand_err, 16) || !aligned(picks, 4) || (trace && !aligned(trace, 4)))
         return IQ_ERR_ARG;
     iq_status_t st = check_device();
     if (st) return st;

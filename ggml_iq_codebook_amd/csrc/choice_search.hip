@@ -11,22 +11,24 @@
 // change of the row's objective when group g takes candidate c is
 // score_c - score_cur, score_c = e_c^T H_gg e_c + 2 e_c^T (r_g - H_gg e_cur).
 //
-// Layout: a 256-thread workgroup runs 16 rows of one block in lockstep
-// (grid.y = the block).  The products with H run on the matrix cores
-// (v_mfma_f32_16x16x4_f32, fp32 operands): e_c^T H_gg e_c for every
-// candidate, and for each step the rest of the next group gn,
-// r_gn - H_gn,gn e_gn = sum over the other groups h of H_gn,h e_h, formed
-// afresh from the current errors (no running r = H e is kept): the four waves
-// sum their quarters of K, leaving out gn and the group being decided, while
-// that group is decided, and the wave of each of gn's 16-column tiles adds
-// the decided group's part after.
-// The decision runs in the scorer layout, lane (row, candidate) =
-// (t/16, t%16): each lane scores its candidate from its own error vector and
-// the row's rest; one DPP reduction across the row's 16 lanes gives the lowest
-// index of least score, the current pick winning the ties it is in (each lane
-// keeps a bit mask of the groups whose pick is its candidate).  Two barriers
-// per step; the next step's H operands and candidate vectors are requested a
-// step ahead.
+// Layout: a 512-thread workgroup runs 16 rows of one block in lockstep
+// (grid.y = the block), with two kinds of waves.  The products with H run on
+// the matrix cores (v_mfma_f32_16x16x4_f32, fp32 operands): first
+// e_c^T H_gg e_c for every candidate (all eight waves), then, for each step of
+// the sweeps, the rest of the next group gn, r_gn - H_gn,gn e_gn = sum over
+// the other groups h of H_gn,h e_h, formed afresh from the current errors (no
+// running r = H e is kept).  Waves 0-3 compute those products: while group g
+// is being decided, each sums its quarter of K, leaving out gn and g; after
+// the decision each adds its quarter of H_gn,g e_g with g's new errors and
+// leaves its partial rest in LDS.  Waves 4-7 decide, one lane per (row,
+// candidate): the rest of g is the sum of the four partials, each lane scores
+// its candidate from its own error vector and that rest, and one DPP
+// reduction across the row's 16 lanes gives the lowest index of least score,
+// the current pick winning the ties it is in (each lane keeps a bit mask of
+// the groups whose pick is its candidate).  The two kinds of waves share the
+// SIMDs, so the products of the next group run beside the decision of the
+// current one; two barriers per step.  The next step's H operands and
+// candidate vectors are requested a step ahead.
 
 #include <hip/hip_runtime.h>
 
@@ -36,7 +38,9 @@
 namespace iqk {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kProdWaves = 4;    // waves 0-3: products with H; waves 4-7: decisions
 constexpr int kRows = 16;        // rows per workgroup
 constexpr int kMaxC = 16;
 
@@ -83,17 +87,17 @@ template <int L>
 __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
 {
     constexpr int G = 256 / L;
-    constexpr int KS = L / 4;                   // matrix-core K steps per group
     constexpr int KH = L / 16;                  // 16-column tiles per group
     // LDS rows are padded (and stay 16-byte aligned) so that the lanes of a
     // wave reading rows, blocks or columns together fall in different banks.
-    constexpr int kHR = L + 4;                  // H_gg row stride
+    constexpr int kHR = L + 4;                  // H_gg row stride, rest row stride
     constexpr int kHB = L * kHR + 4;            // H_gg block stride
     constexpr int kQS = G * kMaxC + 16;         // qself row stride
+    constexpr int kPR = L + 4;                  // partial rest row stride
     __shared__ __align__(16) float hdiag[G * kHB];        // H_gg blocks [g][i][j]
-    __shared__ __align__(16) float ecurT[256 * kRows];      // current errors, [column][row]
-    __shared__ __align__(16) float part[4 * KH * 64 * 4]; // the waves' partial rest tiles
-    __shared__ __align__(16) float enew[L * kRows];       // the decided group's errors, [i][row]
+    __shared__ __align__(16) float ecurT[256 * kRows];    // current errors, [column][row]
+    __shared__ __align__(16) float part[kProdWaves * kRows * kPR];  // [wave][row][i]
+    __shared__ __align__(16) float enew[kRows * kPR];     // the decided group's errors, [row][i]
     __shared__ __align__(16) float rest[kRows * kHR];     // r_g - H_gg e_cur,g, [row][i]
     __shared__ __align__(16) float qself[kRows * kQS];    // e_gc^T H_gg e_gc, [row][g*C + c]
     __shared__ int pick0[kRows * G];                      // step-2 picks
@@ -123,15 +127,15 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     }
     __syncthreads();
 
-    // e_gc^T H_gg e_gc on the matrix cores: for group g and 16 (row, cand)
-    // columns n, Y = H_gg E^T (lane: rows 4lq..4lq+3 of each 16-row block of
-    // Y, column n = lc), then the column's dot with E, summed over the four
-    // lanes of the column.  The K order of the products is permuted (step s of
-    // a 16-wide K block takes k = 4lq + s) so that a lane's four operands of a
-    // block are the four values of E it also needs for the dot: one 16-byte
-    // load per block.  Jobs (group, 16 columns) are spread over the waves and
-    // taken kJB at a time, the next batch requested before the current one is
-    // used.
+    // e_gc^T H_gg e_gc on the matrix cores (all waves): for group g and 16
+    // (row, cand) columns n, Y = H_gg E^T (lane: rows 4lq..4lq+3 of each
+    // 16-row block of Y, column n = lc), then the column's dot with E, summed
+    // over the four lanes of the column.  The K order of the products is
+    // permuted (step s of a 16-wide K block takes k = 4lq + s) so that a
+    // lane's four operands of a block are the four values of E it also needs
+    // for the dot: one 16-byte load per block.  Jobs (group, 16 columns) are
+    // spread over the waves and taken kJB at a time, the next batch requested
+    // before the current one is used.
     {
         constexpr int kJB = 8;
         const int ntile = C;                      // 16*C (row, cand) columns in tiles of 16
@@ -144,29 +148,23 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         auto load_batch = [&](int j0, float4 (&E)[kJB][KH]) {
 #pragma unroll
             for (int b = 0; b < kJB; ++b) {
-                const int job = j0 + 4 * b;
+                const int job = j0 + kWaves * b;
                 const int g = divC(job), n = (job - g * C) * 16 + lc;
                 const int rr = divC(n), c = n - rr * C;
                 const bool live = job < njobs && rr < nrows;
-                const float* ep = live ? cand_ptr(rr, g, c) : nullptr;
+                const float4* ep = live ? reinterpret_cast<const float4*>(cand_ptr(rr, g, c)) : nullptr;
 #pragma unroll
-                for (int h = 0; h < KH; ++h) {
-                    if (live) {
-                        E[b][h] = make_float4(ep[16 * h + 4 * lq], ep[16 * h + 4 * lq + 1],
-                                              ep[16 * h + 4 * lq + 2], ep[16 * h + 4 * lq + 3]);
-                    } else {
-                        E[b][h] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    }
-                }
+                for (int h = 0; h < KH; ++h)
+                    E[b][h] = live ? ep[4 * h + lq] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         };
         load_batch(wave, Ec);
-        for (int j0 = wave; j0 < njobs; j0 += 4 * kJB) {           // wave-uniform
-            load_batch(j0 + 4 * kJB, En);
+        for (int j0 = wave; j0 < njobs; j0 += kWaves * kJB) {     // wave-uniform
+            load_batch(j0 + kWaves * kJB, En);
             float qv[kJB];
 #pragma unroll
             for (int b = 0; b < kJB; ++b) {
-                const int job = j0 + 4 * b;
+                const int job = j0 + kWaves * b;
                 const int g = divC(job < njobs ? job : 0);
                 float q = 0.0f;
 #pragma unroll
@@ -197,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             for (int b = 0; b < kJB; ++b) qv[b] += __shfl_xor(qv[b], 32);
 #pragma unroll
             for (int b = 0; b < kJB; ++b) {
-                const int job = j0 + 4 * b;
+                const int job = j0 + kWaves * b;
                 const int g = divC(job), n = (job - g * C) * 16 + lc;
                 const int rr = divC(n);
                 if (job < njobs && lq == 0) qself[rr * kQS + g * C + (n - rr * C)] = qv[b];
@@ -218,139 +216,182 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         for (int c = 1; c < C; ++c)
             if (qself[rr * kQS + g * C + c] < qself[rr * kQS + g * C + best]) best = c;
         pick0[rr * G + g] = best;
-        const float* ep = rr < nrows ? cand_ptr(rr, g, best) : nullptr;
+        const float4* ep = rr < nrows ? reinterpret_cast<const float4*>(cand_ptr(rr, g, best)) : nullptr;
 #pragma unroll
-        for (int i = 0; i < L; ++i) ecurT[(g * L + i) * kRows + rr] = rr < nrows ? ep[i] : 0.0f;
+        for (int i4 = 0; i4 < L / 4; ++i4) {
+            const float4 v = ep ? ep[i4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            ecurT[(g * L + 4 * i4) * kRows + rr] = v.x;
+            ecurT[(g * L + 4 * i4 + 1) * kRows + rr] = v.y;
+            ecurT[(g * L + 4 * i4 + 2) * kRows + rr] = v.z;
+            ecurT[(g * L + 4 * i4 + 3) * kRows + rr] = v.w;
+        }
     }
     __syncthreads();
     if (a.trace)
         for (int it = t; it < nrows * G; it += kThreads)
             a.trace[out_index(0, row0 + it / G, it % G)] = pick0[it];
 
-    // Scorer layout: lane (srow, scand); pmask bit g = group g's pick is scand.
-    const int srow = t >> 4;
-    const int scand = t & 15;
-    const bool scorer = scand < C && srow < nrows;
-    uint32_t pmask = 0u;
-    for (int g = 0; g < G; ++g) pmask |= (uint32_t)(pick0[srow * G + g] == scand) << g;
+    const bool prod = wave < kProdWaves;        // wave-uniform
 
-    // The rest of group gn for the 16 rows, r_gn - H_gn,gn e_gn: the sum over
-    // the other groups h of H_gn,h e_h, formed afresh for every step on the
-    // matrix cores (no running r = H e is kept).  Output tile ih holds the
-    // columns gn*L + 16ih .. + 15 (lane: columns 4lq..4lq+3 of the tile, row
-    // lc).  The part that does not depend on the group gx being decided runs
-    // before its decision: wave w takes the K range 64w .. 64w + 63 in steps
-    // of 4 (k = 64w + 4s + lq) with the columns of gn and gx left out, and puts
-    // its partial tiles in LDS.  After the decision, wave ih adds the four
-    // partials of tile ih in a fixed order, then H_gn,gx e_gx with the errors
-    // just decided, and writes the rest.  The H operands (H symmetric:
-    // H[k][column]) are requested a step ahead.
-    constexpr int kPS = 16;                     // K steps per wave
-    float hP[KH][kPS], hPn[KH][kPS];            // H[64w + 4s + lq][gn*L + 16ih + lc]
-    float hX[KS], hXn[KS];                      // H[gx*L + 4s + lq][gn*L + 16w + lc], w < KH
-    auto load_hP = [&](int gn, float (&h)[KH][kPS]) {
+    if (prod) {
+        // ---------------- product waves ----------------
+        // The wave's partial rest of group gn for the 16 rows: K range
+        // 64w .. 64w + 63 in steps of 4 (k = 64w + 4s + lq), the columns of gn
+        // and gx (gx < 0: none) left out.  Output tile ih holds the columns
+        // gn*L + 16ih .. + 15 (lane: columns 4lq..4lq+3 of the tile, row lc).
+        // Then its quarter of the late product H_gn,gx e_gx (k = gx*L +
+        // (L/4)w + 4s + lq, s < KH) with gx's new errors, and the tiles go to
+        // part[w] as [row][column].  The H operands (H symmetric: H[k][column])
+        // are requested a step ahead.
+        constexpr int kPS = 16;                 // K steps per wave
+        float hP[KH][kPS], hPn[KH][kPS];        // H[64w + 4s + lq][gn*L + 16ih + lc]
+        float hX[KH][KH], hXn[KH][KH];          // H[gx*L + (L/4)w + 4s + lq][gn*L + 16ih + lc]
+        auto load_hP = [&](int gn, float (&h)[KH][kPS]) {
 #pragma unroll
-        for (int ih = 0; ih < KH; ++ih)
+            for (int ih = 0; ih < KH; ++ih)
 #pragma unroll
-            for (int s = 0; s < kPS; ++s)
-                h[ih][s] = Hb[(64 * wave + 4 * s + lq) * 256 + gn * L + 16 * ih + lc];
-    };
-    auto load_hX = [&](int gn, int gx, float (&h)[KS]) {
-        if (wave >= KH) return;                                 // wave-uniform
+                for (int s = 0; s < kPS; ++s)
+                    h[ih][s] = Hb[(64 * wave + 4 * s + lq) * 256 + gn * L + 16 * ih + lc];
+        };
+        auto load_hX = [&](int gn, int gx, float (&h)[KH][KH]) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) h[s] = Hb[(gx * L + 4 * s + lq) * 256 + gn * L + 16 * wave + lc];
-    };
-    // The wave's partial tiles, columns of gn and gx (gx < 0: none) left out
-    // (wave-uniform conditions).  The errors in LDS do not change while this
-    // runs: a decision stages its group's new errors apart and they are copied
-    // in after the next barrier.  All B operands are read before the products
-    // start.
-    auto partial = [&](int gn, int gx, v4f (&p)[KH]) {
-        float bv[kPS];
+            for (int ih = 0; ih < KH; ++ih)
 #pragma unroll
-        for (int s = 0; s < kPS; ++s) bv[s] = ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
-        __builtin_amdgcn_sched_barrier(0);
+                for (int s = 0; s < KH; ++s)
+                    h[ih][s] = Hb[(gx * L + (L / 4) * wave + 4 * s + lq) * 256 + gn * L + 16 * ih + lc];
+        };
+        auto partial = [&](int gn, int gx, v4f (&p)[KH]) {
+            float bv[kPS];
 #pragma unroll
-        for (int ih = 0; ih < KH; ++ih) p[ih] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int s = 0; s < kPS; ++s) bv[s] = ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
 #pragma unroll
-        for (int s = 0; s < kPS; ++s) {
-            const int kg = (64 * wave + 4 * s) / L;             // wave-uniform
-            if (kg != gn && kg != gx) {
+            for (int ih = 0; ih < KH; ++ih) p[ih] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int ih = 0; ih < KH; ++ih) p[ih] = mfma4(hP[ih][s], bv[s], p[ih]);
+            for (int s = 0; s < kPS; ++s) {
+                const int kg = (64 * wave + 4 * s) / L;             // wave-uniform
+                if (kg != gn && kg != gx) {
+#pragma unroll
+                    for (int ih = 0; ih < KH; ++ih) p[ih] = mfma4(hP[ih][s], bv[s], p[ih]);
+                }
             }
-        }
-    };
-    auto store_partial = [&](const v4f (&p)[KH]) {
+        };
+        auto store_part = [&](const v4f (&p)[KH]) {
 #pragma unroll
-        for (int ih = 0; ih < KH; ++ih)
-            *reinterpret_cast<v4f*>(&part[((wave * KH + ih) * 64 + lane) * 4]) = p[ih];
-    };
-    auto finish_rest = [&](int gx) {
-        if (wave >= KH) return;                                 // wave-uniform
-        const int ih = wave;
-        v4f d = *reinterpret_cast<const v4f*>(&part[(ih * 64 + lane) * 4]);
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-            const v4f o = *reinterpret_cast<const v4f*>(&part[((w * KH + ih) * 64 + lane) * 4]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) d[i] += o[i];
-        }
-        if (gx >= 0) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) d = mfma4(hX[s], enew[(4 * s + lq) * kRows + lc], d);
-        }
-        *reinterpret_cast<float4*>(&rest[lc * kHR + 16 * ih + 4 * lq]) =
-            make_float4(d[0], d[1], d[2], d[3]);
-    };
+            for (int ih = 0; ih < KH; ++ih)
+                *reinterpret_cast<v4f*>(&part[(wave * kRows + lc) * kPR + 16 * ih + 4 * lq]) = p[ih];
+        };
 
-    // The first group's rest (no group being decided).
-    v4f pp[KH];
-    load_hP(0, hP);
-    partial(0, -1, pp);
-    store_partial(pp);
-    __syncthreads();
-    finish_rest(-1);
-
-    // The step operands, one step ahead: the scorer's candidate vector and the
-    // H operands of the next rest.
-    float cv[L], cvn[L];
-    auto load_cv = [&](int g, float (&v)[L]) {
-        if (scorer) {
-            const float* ep = cand_ptr(srow, g, scand);
-#pragma unroll
-            for (int i = 0; i < L; ++i) v[i] = ep[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < L; ++i) v[i] = 0.0f;
-        }
-    };
-    load_cv(0, cv);
-    load_hP(1, hP);
-    load_hX(1, 0, hX);
-    __syncthreads();
-
-    for (int sw = 0; sw < a.sweeps; ++sw) {
-        for (int g = 0; g < G; ++g) {
+        // The rest of group 0 (no group being decided).
+        v4f pp[KH];
+        load_hP(0, hP);
+        partial(0, -1, pp);
+        store_part(pp);
+        load_hP(1 % G, hP);
+        load_hX(1 % G, 0, hX);
+        __syncthreads();                        // part holds the rest of group 0
+        // One step: the products of gn beside the decision of g, with the
+        // operands requested the step before (cur); the next step's go into
+        // nxt once cur's are in use.  Steps alternate between the two register
+        // sets, so a load is first used about a step after it was issued.
+        auto pstep = [&](int g, float (&hPc)[KH][kPS], float (&hXc)[KH][KH],
+                         float (&hPx)[KH][kPS], float (&hXx)[KH][KH]) {
             const int gn = g + 1 < G ? g + 1 : 0;
             const int gnn = gn + 1 < G ? gn + 1 : 0;
-            load_cv(gn, cvn);
-            // The next group's rest without group g, while group g is decided.
-            partial(gn, g, pp);
-            load_hP(gnn, hPn);
-            load_hX(gnn, gn, hXn);
-            // Scores, the decision and the error update of group g.
+            float bv[kPS];
+#pragma unroll
+            for (int s = 0; s < kPS; ++s) bv[s] = ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
+#pragma unroll
+            for (int ih = 0; ih < KH; ++ih) pp[ih] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < kPS; ++s) {
+                const int kg = (64 * wave + 4 * s) / L;             // wave-uniform
+                if (kg != gn && kg != g) {
+#pragma unroll
+                    for (int ih = 0; ih < KH; ++ih) pp[ih] = mfma4(hPc[ih][s], bv[s], pp[ih]);
+                }
+            }
+            // The next step's H operands, requested once this step's are in
+            // use (a wait for these must not wait for those).
+            load_hP(gnn, hPx);
+            load_hX(gnn, gn, hXx);
+            __syncthreads();                    // A: g decided, its errors in enew
+#pragma unroll
+            for (int s = 0; s < KH; ++s) {
+                const float b = enew[lc * kPR + (L / 4) * wave + 4 * s + lq];
+#pragma unroll
+                for (int ih = 0; ih < KH; ++ih) pp[ih] = mfma4(hXc[ih][s], b, pp[ih]);
+            }
+            store_part(pp);
+            __syncthreads();                    // B: part holds the rest of gn
+        };
+        for (int sw = 0; sw < a.sweeps; ++sw) {
+#pragma unroll 1
+            for (int g = 0; g < G; g += 2) {    // G is even
+                pstep(g, hP, hX, hPn, hXn);
+                pstep(g + 1, hPn, hXn, hP, hX);
+            }
+        }
+    } else {
+        // ---------------- decision waves ----------------
+        // Lane (srow, scand); pmask bit g = group g's pick is scand.
+        const int dt = t - 64 * kProdWaves;
+        const int srow = dt >> 4;
+        const int scand = dt & 15;
+        const bool scorer = scand < C && srow < nrows;
+        uint32_t pmask = 0u;
+        for (int g = 0; g < G; ++g) pmask |= (uint32_t)(pick0[srow * G + g] == scand) << g;
+        float cv[L], cvn[L];
+        auto load_cv = [&](int g, float (&v)[L]) {
+            if (scorer) {
+                const float4* ep = reinterpret_cast<const float4*>(cand_ptr(srow, g, scand));
+#pragma unroll
+                for (int i4 = 0; i4 < L / 4; ++i4) {
+                    const float4 u = ep[i4];
+                    v[4 * i4] = u.x; v[4 * i4 + 1] = u.y; v[4 * i4 + 2] = u.z; v[4 * i4 + 3] = u.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < L; ++i) v[i] = 0.0f;
+            }
+        };
+        load_cv(0, cv);
+        __syncthreads();                        // part holds the rest of group 0
+        // One step: group g decided with its candidate vector requested the
+        // step before (cur); the next group's goes into nxt.
+        auto dstep = [&](int g, float (&cur)[L], float (&nxt)[L]) {
+            const int gn = g + 1 < G ? g + 1 : 0;
+            // The rest of g: the four partials summed in a fixed order, one
+            // column (two for L = 32) per lane, then the whole row read back by
+            // the row's 16 lanes (one wave: in order in LDS).
+#pragma unroll
+            for (int h = 0; h < KH; ++h) {
+                const int i = scand + 16 * h;
+                float v = part[(0 * kRows + srow) * kPR + i];
+#pragma unroll
+                for (int w = 1; w < kProdWaves; ++w) v += part[(w * kRows + srow) * kPR + i];
+                rest[srow * kHR + i] = v;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             float sc = __builtin_inff();
             if (scorer) {
-                float dot = 0.0f;
+                float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int i = 0; i < L; ++i) dot = __builtin_fmaf(cv[i], rest[srow * kHR + i], dot);
+                for (int i4 = 0; i4 < L / 4; ++i4) {
+                    const float4 r4 = *reinterpret_cast<const float4*>(&rest[srow * kHR + 4 * i4]);
+                    d4[0] = __builtin_fmaf(cur[4 * i4], r4.x, d4[0]);
+                    d4[1] = __builtin_fmaf(cur[4 * i4 + 1], r4.y, d4[1]);
+                    d4[2] = __builtin_fmaf(cur[4 * i4 + 2], r4.z, d4[2]);
+                    d4[3] = __builtin_fmaf(cur[4 * i4 + 3], r4.w, d4[3]);
+                }
+                const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
                 sc = __builtin_fmaf(2.0f, dot, qself[srow * kQS + g * C + scand]);
             }
-            // The least score of the row (DPP), then the row's lanes that hold
-            // it (a ballot, 16 bits per row): the group keeps its pick if the
-            // pick holds it (only a strictly lower score moves it), else moves
-            // to the lowest candidate that does.
+            // The least score of the row (DPP), then the row's lanes that
+            // hold it (a ballot, 16 bits per row): the group keeps its pick if
+            // the pick holds it (only a strictly lower score moves it), else
+            // moves to the lowest candidate that does.
             const bool mine = (pmask >> g) & 1u;
             const float m = row_min(sc);
             const int rsh = 16 * (lane >> 4);
@@ -359,39 +400,41 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             const bool move = req != 0u && (req & rcur) == 0u;
             const int bc = __builtin_ctz(req | 0x10000u);
             // The row's new errors of group g (the new pick's, or the current
-            // pick's when it stays), staged for the rest of gn.
+            // pick's when it stays).
             if (move ? scand == bc : mine) {
 #pragma unroll
-                for (int i = 0; i < L; ++i) enew[i * kRows + srow] = cv[i];
+                for (int i4 = 0; i4 < L / 4; ++i4)
+                    *reinterpret_cast<float4*>(&enew[srow * kPR + 4 * i4]) =
+                        make_float4(cur[4 * i4], cur[4 * i4 + 1], cur[4 * i4 + 2], cur[4 * i4 + 3]);
             }
             if (move) pmask = (pmask & ~(1u << g)) | ((uint32_t)(scand == bc) << g);
-            store_partial(pp);
-            __syncthreads();
-
-            // The rest of gn with the errors of g just decided; the rows that
-            // moved update their errors of g.
-            finish_rest(g);
-            if (move && scand == bc) {
+            // The next group's candidate vector, requested once this one's is
+            // used (a wait for this one must not wait for that).
+            load_cv(gn, nxt);
+            __syncthreads();                    // A: g decided, its errors in enew
+            // g's errors into the error columns (the product waves read them
+            // from the next step on)
 #pragma unroll
-                for (int i = 0; i < L; ++i) ecurT[(g * L + i) * kRows + srow] = cv[i];
+            for (int h = 0; h < KH; ++h) {
+                const int i = scand + 16 * h;
+                ecurT[(g * L + i) * kRows + srow] = enew[srow * kPR + i];
             }
-#pragma unroll
-            for (int i = 0; i < L; ++i) cv[i] = cvn[i];
-#pragma unroll
-            for (int ih = 0; ih < KH; ++ih)
-#pragma unroll
-                for (int s = 0; s < kPS; ++s) hP[ih][s] = hPn[ih][s];
-#pragma unroll
-            for (int s = 0; s < KS; ++s) hX[s] = hXn[s];
-            __syncthreads();
+            __syncthreads();                    // B: part holds the rest of gn
+        };
+        for (int sw = 0; sw < a.sweeps; ++sw) {
+#pragma unroll 1
+            for (int g = 0; g < G; g += 2) {    // G is even
+                dstep(g, cv, cvn);
+                dstep(g + 1, cvn, cv);
+            }
+            if (a.trace && srow < nrows)
+                for (int g = 0; g < G; ++g)
+                    if ((pmask >> g) & 1u) a.trace[out_index(sw + 1, row0 + srow, g)] = scand;
         }
-        if (a.trace && srow < nrows)
+        if (srow < nrows)
             for (int g = 0; g < G; ++g)
-                if ((pmask >> g) & 1u) a.trace[out_index(sw + 1, row0 + srow, g)] = scand;
+                if ((pmask >> g) & 1u) a.picks[((row0 + srow) * a.nblk + blk) * G + g] = scand;
     }
-    if (srow < nrows)
-        for (int g = 0; g < G; ++g)
-            if ((pmask >> g) & 1u) a.picks[((row0 + srow) * a.nblk + blk) * G + g] = scand;
 }
 
 }  // namespace

@@ -7,9 +7,12 @@
 // 8th sign implied by even parity of its 7-bit mask.  Every product is exact in
 // fp32 (d has 11 significant bits, 2k+1 at most 5, q + delta at most 4).
 //
-// HBM-bound streaming kernel: one lane per 8-value group, two float4 stores
-// per lane (coalesced 32-byte runs); the payload bytes of a block are read by
-// 32 consecutive lanes and the grid (<= 64 KiB) stays in L2/L1.
+// HBM-bound streaming kernel: a wave per 256-value block, a lane per 4
+// consecutive values (half a group), so every store instruction of a wave
+// writes one contiguous KiB.  The lane reads the few payload bytes its group
+// needs (the 64 lanes of a block share one 50 to 74-byte record, served by the
+// L1) and one float4 of its grid entry (the grid, at most 64 KiB, stays in
+// L2/L1).
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -20,15 +23,18 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Lane t of the launch covers values 4t..4t+3: block t/64, group (t%64)/2,
+// half t%2 of the group.
 __global__ __launch_bounds__(kThreads) void dequant_iq1s_kernel(const uint8_t* __restrict__ packed,
                                                                 const float* __restrict__ grid, int n,
                                                                 float* __restrict__ out,
-                                                                int32_t* status, int64_t ngroups)
+                                                                int32_t* status, int64_t nquads)
 {
-    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (gid >= ngroups) return;
-    const int64_t blk = gid >> 5;
-    const int g = (int)(gid & 31);
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= nquads) return;
+    const int64_t blk = t >> 6;
+    const int g = (int)(t >> 1) & 31;
+    const int h = (int)t & 1;
     const int sub = g >> 2, l = g & 3;
     const uint8_t* b = packed + blk * 50;
     const uint32_t dh = (uint32_t)b[0] | ((uint32_t)b[1] << 8);
@@ -37,33 +43,26 @@ __global__ __launch_bounds__(kThreads) void dequant_iq1s_kernel(const uint8_t* _
     const int k = (int)((qh >> 12) & 7u);
     const float delta = (qh >> 15) ? -0.125f : 0.125f;
     const float s = f16_bits_to_f32(dh) * (float)(2 * k + 1);
-    float v[8];
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (e < n) {
-        const float4* q4 = reinterpret_cast<const float4*>(grid + 8 * e);
-        const float4 q0 = q4[0], q1 = q4[1];
-        v[0] = s * (q0.x + delta); v[1] = s * (q0.y + delta);
-        v[2] = s * (q0.z + delta); v[3] = s * (q0.w + delta);
-        v[4] = s * (q1.x + delta); v[5] = s * (q1.y + delta);
-        v[6] = s * (q1.z + delta); v[7] = s * (q1.w + delta);
-    } else {
+        const float4 q = reinterpret_cast<const float4*>(grid + 8 * e)[h];
+        v = make_float4(s * (q.x + delta), s * (q.y + delta), s * (q.z + delta), s * (q.w + delta));
+    } else if (h == 0) {
         report(status, IQ_ERR_CODE);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
-    float4* o = reinterpret_cast<float4*>(out + gid * 8);
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    reinterpret_cast<float4*>(out)[t] = v;
 }
 
 __global__ __launch_bounds__(kThreads) void dequant_iq2xs_kernel(const uint8_t* __restrict__ packed,
                                                                  const float* __restrict__ grid, int n,
                                                                  float* __restrict__ out,
-                                                                 int32_t* status, int64_t ngroups)
+                                                                 int32_t* status, int64_t nquads)
 {
-    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (gid >= ngroups) return;
-    const int64_t blk = gid >> 5;
-    const int g = (int)(gid & 31);
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= nquads) return;
+    const int64_t blk = t >> 6;
+    const int g = (int)(t >> 1) & 31;
+    const int h = (int)t & 1;
     const int m = g >> 1;
     const uint8_t* b = packed + blk * 74;
     const uint32_t dh = (uint32_t)b[0] | ((uint32_t)b[1] << 8);
@@ -73,36 +72,32 @@ __global__ __launch_bounds__(kThreads) void dequant_iq2xs_kernel(const uint8_t* 
     const uint32_t sb = b[66 + (m >> 1)];
     const int k = (int)((m & 1) ? (sb >> 4) : (sb & 15u));
     const float s = f16_bits_to_f32(dh) * (float)(2 * k + 1);
-    const uint32_t signs = mask | ((__popc(mask) & 1u) << 7);
-    float v[8];
+    // the 8 signs (the 8th from even parity of the 7-bit mask), this half's 4
+    const uint32_t signs = (mask | ((__popc(mask) & 1u) << 7)) >> (4 * h);
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (e < n) {
-        const float4* q4 = reinterpret_cast<const float4*>(grid + 8 * e);
-        const float4 q0 = q4[0], q1 = q4[1];
-        const float q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (((signs >> j) & 1u) ? -s : s) * q[j];
-    } else {
+        const float4 q = reinterpret_cast<const float4*>(grid + 8 * e)[h];
+        v = make_float4(((signs & 1u) ? -s : s) * q.x, ((signs & 2u) ? -s : s) * q.y,
+                        ((signs & 4u) ? -s : s) * q.z, ((signs & 8u) ? -s : s) * q.w);
+    } else if (h == 0) {
         report(status, IQ_ERR_CODE);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
-    float4* o = reinterpret_cast<float4*>(out + gid * 8);
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    reinterpret_cast<float4*>(out)[t] = v;
 }
 
-// IQ1_M (#2525 IQ1_M codec body): d reassembled from the top nibbles of the
+// IQ1_M (#2525 IQ1_M codec body): d's fp16 bits from the top nibbles of the
 // four scale words; the 3-bit local scale of the group's scale group; the
 // group's nibble gives the 3 high index bits and the shift.
 __global__ __launch_bounds__(kThreads) void dequant_iq1m_kernel(const uint8_t* __restrict__ packed,
                                                                 const float* __restrict__ grid, int n,
                                                                 float* __restrict__ out,
-                                                                int32_t* status, int64_t ngroups)
+                                                                int32_t* status, int64_t nquads)
 {
-    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (gid >= ngroups) return;
-    const int64_t blk = gid >> 5;
-    const int g = (int)(gid & 31);
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t >= nquads) return;
+    const int64_t blk = t >> 6;
+    const int g = (int)(t >> 1) & 31;
+    const int h = (int)t & 1;
     const int m = g >> 1;
     const uint8_t* b = packed + blk * 56;
     uint32_t sc[4];
@@ -117,22 +112,14 @@ __global__ __launch_bounds__(kThreads) void dequant_iq1m_kernel(const uint8_t* _
     const int e = (int)b[g] | (int)((nib & 7u) << 8);
     const float delta = (nib & 8u) ? -0.125f : 0.125f;
     const float s = f16_bits_to_f32(dh) * (float)(2 * k + 1);
-    float v[8];
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (e < n) {
-        const float4* q4 = reinterpret_cast<const float4*>(grid + 8 * e);
-        const float4 q0 = q4[0], q1 = q4[1];
-        v[0] = s * (q0.x + delta); v[1] = s * (q0.y + delta);
-        v[2] = s * (q0.z + delta); v[3] = s * (q0.w + delta);
-        v[4] = s * (q1.x + delta); v[5] = s * (q1.y + delta);
-        v[6] = s * (q1.z + delta); v[7] = s * (q1.w + delta);
-    } else {
+        const float4 q = reinterpret_cast<const float4*>(grid + 8 * e)[h];
+        v = make_float4(s * (q.x + delta), s * (q.y + delta), s * (q.z + delta), s * (q.w + delta));
+    } else if (h == 0) {
         report(status, IQ_ERR_CODE);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
-    float4* o = reinterpret_cast<float4*>(out + gid * 8);
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    reinterpret_cast<float4*>(out)[t] = v;
 }
 
 }  // namespace
@@ -140,17 +127,17 @@ __global__ __launch_bounds__(kThreads) void dequant_iq1m_kernel(const uint8_t* _
 hipError_t launch_dequant(int fmt, const uint8_t* packed, const float* grid, int grid_size,
                           float* out, int32_t* status, const BlockGeom& g, hipStream_t stream)
 {
-    const int64_t ngroups = g.nblocks * 32;
-    const int64_t wgs = (ngroups + kThreads - 1) / kThreads;
+    const int64_t nquads = g.nblocks * 64;
+    const int64_t wgs = (nquads + kThreads - 1) / kThreads;
     if (fmt == IQ_FMT_IQ1_S)
         hipLaunchKernelGGL(dequant_iq1s_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream,
-                           packed, grid, grid_size, out, status, ngroups);
+                           packed, grid, grid_size, out, status, nquads);
     else if (fmt == IQ_FMT_IQ1_M)
         hipLaunchKernelGGL(dequant_iq1m_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream,
-                           packed, grid, grid_size, out, status, ngroups);
+                           packed, grid, grid_size, out, status, nquads);
     else
         hipLaunchKernelGGL(dequant_iq2xs_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream,
-                           packed, grid, grid_size, out, status, ngroups);
+                           packed, grid, grid_size, out, status, nquads);
     return hipGetLastError();
 }
 

@@ -868,38 +868,53 @@ __device__ __forceinline__ void fold_wide8(const v16f& u, const v16f& v, float (
     }
 }
 
-// VALU rescan for choice cs = k + 8*deltabit over rows v0 .. v0+nv-1 of half
-// hs in the tiles of chunk `chunk`: the lowest entry with the least key
-// (2k+1)*U - 2V/d, recomputed in fp32 from the group's values and weights.
-template <class GS>
+// VALU rescan for choice cs = k + 8*deltabit over rows v0 .. v0+kNV-1 (v0 a
+// multiple of 4) of half hs in the tiles of chunk `chunk`: the lowest entry
+// with the least key (2k+1)*U - 2V/d, recomputed in fp32 from the group's
+// values and weights.  The lane visits its entries in increasing order, so a
+// strict comparison keeps the lowest of equal keys; the entry offsets inside
+// a tile are constants of the unrolled row loop.
+template <int kNV, class GS>
 __device__ __forceinline__ int rescan_w1(const uint4* __restrict__ sq, int chunk, int hs, int v0,
-                                         int nv, int cs, const GS& src, bool zero_block, float w64,
+                                         int cs, const GS& src, bool zero_block, float w64,
                                          float b4, float inv_d, float* key_out)
 {
     float x[8], w[8];
     __asm__ volatile("" ::: "memory");
     src.load(zero_block, x, w);
+    float wx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wx[j] = w[j] * x[j];
     const float mk = (float)(2 * (cs & 7) + 1);
     const float dl = (cs >> 3) ? -0.25f : 0.25f;      // 2*delta
     const float bd = (cs >> 3) ? b4 : -b4;
-    int idx = -1;
-    float vbest = 0.0f;
+    // entry e0 + de, de = 32*tile + 8*(i/4) + i%4 for row v0 + i; the table
+    // holds entry e at e + e/128 (one spare slot per chunk)
+    const int e0 = kW1Tile * kW1ChunkTiles * chunk + 4 * hs + 8 * (v0 >> 2);
+    const uint4* base = sq + e0 + chunk;
+    int idx = e0;
+    float vbest = __builtin_inff();
+#pragma unroll 1
     for (int tt = 0; tt < kW1ChunkTiles; ++tt) {
-        for (int v = v0; v < v0 + nv; ++v) {
-            const int e = kW1Tile * (chunk * kW1ChunkTiles + tt) + 8 * (v >> 2) + 4 * hs + (v & 3);
-            const uint4 u = sq[e + chunk];
+#pragma unroll
+        for (int i = 0; i < kNV; ++i) {
+            const int de = 8 * (i >> 2) + (i & 3);
+            const uint4 u = base[kW1Tile * tt + de];
             const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
             float A = 0.0f, M = 0.0f, N = 0.0f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-                A = __builtin_fmaf(w[j] * x[j], q, A);
+                const float q = (j & 1) ? __uint_as_float(uu[j >> 1] & 0xffff0000u)
+                                        : __uint_as_float(uu[j >> 1] << 16);
+                A = __builtin_fmaf(wx[j], q, A);
                 M = __builtin_fmaf(w[j], q, M);
                 N = __builtin_fmaf(w[j], fabsf(q), N);
             }
             const float U = __builtin_fmaf(M, dl, N + w64);
             const float key = __builtin_fmaf(U, mk, __builtin_fmaf(A, -2.0f, bd) * inv_d);
-            if (idx < 0 || key < vbest) { vbest = key; idx = e; }
+            const bool better = key < vbest;
+            vbest = better ? key : vbest;
+            idx = better ? e0 + kW1Tile * tt + de : idx;
         }
     }
     *key_out = vbest;
@@ -1203,12 +1218,12 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
             if (!tie) {
                 const int hs = (om < lm) ? (hl2 ^ 1) : hl2;             // holder half
                 const int tch = __shfl(tchunk, g2 + 32 * hs);
-                idx = rescan_w1(wsq, tch, hs, 8 * hl2, 8, cs, src2, zero_block, w64, b4, inv_d, &key);
+                idx = rescan_w1<8>(wsq, tch, hs, 8 * hl2, cs, src2, zero_block, w64, b4, inv_d, &key);
                 const float ok = __shfl(key, ln2 ^ 32);
                 const int oi = __shfl(idx, ln2 ^ 32);
                 if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
             } else {
-                idx = rescan_w1(wsq, tchunk, hl2, 0, 16, cs, src2, zero_block, w64, b4, inv_d, &key);
+                idx = rescan_w1<16>(wsq, tchunk, hl2, 0, cs, src2, zero_block, w64, b4, inv_d, &key);
                 const int oi = __shfl(idx, ln2 ^ 32);
                 if (om < lm || (om == lm && oi < idx)) idx = oi;
             }

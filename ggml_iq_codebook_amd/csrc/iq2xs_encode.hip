@@ -564,20 +564,28 @@ __device__ __forceinline__ int wide_entry(int t, int hl, int v)
     return kWTile * t + 8 * (v >> 2) + 4 * hl + (v & 3);
 }
 
-// VALU rescan for local scale k over rows v0 .. v0+nv-1 of half hs in the
-// kCT tiles of chunk `chunk`: the lowest entry with the least key.
-template <int kCT>
+// VALU rescan for local scale k over rows v0 .. v0+kNV-1 (v0 a multiple of 4)
+// of half hs in the kCT tiles of chunk `chunk`: the lowest entry with the
+// least key.  The lane visits its entries in increasing order, so a strict
+// comparison keeps the lowest of equal keys; the entry offsets inside the
+// chunk are constants of the unrolled loop.
+template <int kCT, int kNV>
 __device__ __forceinline__ int rescan_wide(const float* __restrict__ sg, int chunk, int hs, int v0,
-                                           int nv, int k, const float (&wxs)[8],
-                                           const float (&w)[8], float inv_d, float* key_out)
+                                           int k, const float (&wxs)[8], const float (&w)[8],
+                                           float inv_d, float* key_out)
 {
     const float mk = (float)(2 * k + 1);
-    int idx = -1;
-    float vbest = 0.0f;
+    // entry e0 + de, de = 32*tile + 8*(i/4) + i%4 for row v0 + i
+    const int e0 = kWTile * kCT * chunk + 4 * hs + 8 * (v0 >> 2);
+    const float* base = sg + kEntryStride * e0 + 2 * chunk;      // entry_off<32*kCT>(e0)
+    int idx = e0;
+    float vbest = __builtin_inff();
+#pragma unroll
     for (int tt = 0; tt < kCT; ++tt) {
-        for (int v = v0; v < v0 + nv; ++v) {
-            const int e = wide_entry(chunk * kCT + tt, hs, v);
-            const float2* p = reinterpret_cast<const float2*>(sg + entry_off<kWTile * kCT>(e));
+#pragma unroll
+        for (int i = 0; i < kNV; ++i) {
+            const int de = kWTile * tt + 8 * (i >> 2) + (i & 3);
+            const float2* p = reinterpret_cast<const float2*>(base + kEntryStride * de);
             float q[8], q2[8];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -592,7 +600,9 @@ __device__ __forceinline__ int rescan_wide(const float* __restrict__ sg, int chu
                 N = __builtin_fmaf(w[j], q2[j], N);
             }
             const float key = __builtin_fmaf(N, mk, (-2.0f * P) * inv_d);
-            if (idx < 0 || key < vbest || (key == vbest && e < idx)) { vbest = key; idx = e; }
+            const bool better = key < vbest;
+            vbest = better ? key : vbest;
+            idx = better ? e0 + de : idx;
         }
     }
     *key_out = vbest;
@@ -838,12 +848,12 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
             if (!tie) {
                 const int hs = (om < lm) ? (hl ^ 1) : hl;             // holder half
                 const int tch = __shfl(tchunk, g + 32 * hs);
-                idx = rescan_wide<kCT>(sgrid, tch, hs, 8 * hl, 8, k, wxs, w, inv_d, &key);
+                idx = rescan_wide<kCT, 8>(sgrid, tch, hs, 8 * hl, k, wxs, w, inv_d, &key);
                 const float ok = __shfl_xor(key, 32);
                 const int oi = __shfl_xor(idx, 32);
                 if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
             } else {
-                idx = rescan_wide<kCT>(sgrid, tchunk, hl, 0, 16, k, wxs, w, inv_d, &key);
+                idx = rescan_wide<kCT, 16>(sgrid, tchunk, hl, 0, k, wxs, w, inv_d, &key);
                 const int oi = __shfl_xor(idx, 32);
                 if (om < lm || (om == lm && oi < idx)) idx = oi;
             }

@@ -240,7 +240,8 @@ iq_status_t iq_encode_candidates(iq_format_t fmt, iq_dtype_t wdtype, const void*
  * the lowest candidate index.
  *
  *   H        [256][256] fp32, symmetric (the caller damps it).
- *   cand_err [rows][G][C][256/G] fp32 candidate error vectors.
+ *   cand_err [rows][G][C][256/G] fp32 candidate error vectors, 16-byte aligned
+ *            (each vector is read as 16-byte words; IQ_ERR_ARG otherwise).
  *   G        8 or 16 groups; C in 1..16 candidates; sweeps in 0..8.
  *   picks    [rows][G] int32 output, candidate indices.
  *   trace    NULL or [sweeps+1][rows][G] int32: picks after step 2 and after

@@ -129,6 +129,8 @@ def test_batched_search_argument_errors_need_no_gpu(lib):
     assert cs(FAKE, FAKE, 0, 3, 16, 8, 2, FAKE, None, None) == 3
     assert cs(FAKE, FAKE, 4, 3, 4, 8, 2, FAKE, None, None) == 8
     assert cs(FAKE, None, 4, 3, 8, 8, 2, FAKE, None, None) == 1
+    # the candidate vectors are read as 16-byte words
+    assert cs(FAKE, P(0x100004), 4, 3, 16, 8, 2, FAKE, None, None) == 8
 
 
 def _no_device_visible():
