@@ -110,6 +110,8 @@ DEQUANT_KERNELS = {"iq1_s": "dequant_iq1s_kernel", "iq2_xs": "dequant_iq2xs_kern
                    "iq1_m": "dequant_iq1m_kernel"}
 DEQUANT_SOURCES = ["ggml_iq_codebook_amd/csrc/dequant.hip",
                    "ggml_iq_codebook_amd/csrc/device_common.hpp"]
+SEARCH_SOURCES = ["ggml_iq_codebook_amd/csrc/choice_search.hip",
+                  "ggml_iq_codebook_amd/csrc/device_common.hpp"]
 
 
 def log(*a):
@@ -157,6 +159,15 @@ PROFILED = {
     "c5_weight": ("iq2xs_candidates_c5_weight", "iq2xs_wide_kernel<3, 0>", _IQ2),
     "c2_dequant": ("dequant_iq1s_c2", DEQUANT_KERNELS["iq1_s"], DEQUANT_SOURCES),
     "c3_dequant": ("dequant_iq2xs_c3", DEQUANT_KERNELS["iq2_xs"], DEQUANT_SOURCES),
+}
+
+
+# The choice search of the candidate workloads, recorded beside the candidate
+# encode: (record name, kernel name, sources).
+PROFILED_SEARCH = {
+    "c5": ("choice_search_c5", "choice_search_kernel<16>", SEARCH_SOURCES),
+    "c5_iq1s": ("choice_search_c5_iq1s", "choice_search_kernel<32>", SEARCH_SOURCES),
+    "c5_weight": ("choice_search_c5_weight", "choice_search_kernel<16>", SEARCH_SOURCES),
 }
 
 
@@ -211,21 +222,23 @@ def record_traffic(config, pmc_dir):
     print(json.dumps(rec))
 
 
-# The VALU / matrix-core counters of one rocprofv3 pass (8 SQ counters and one
-# GRBM counter at most per pass on this GPU).
+# The VALU / matrix-core / LDS counters of one rocprofv3 pass (8 SQ counters
+# and 2 GRBM counters at most per pass on this GPU).
 VALU_COUNTERS = ["SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU2", "SQ_INSTS_MFMA",
-                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
-N_XCD, N_SIMD = 8, 1024
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "SQ_BUSY_CYCLES",
+                 "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
 
 
-def record_counters(config, pmc_dir, units):
+def record_counters(config, pmc_dir, units, which=None):
     """Turn a VALU counter pass (pmc_<config>_valu/enc_counter_collection.csv)
     into profiles/counters_<kernel>_<config>.json: the VALU issue-port busy
     fraction (quad-cycles with at least one VALU issue per SIMD over the
     kernel's quad-cycles; a dual issue puts two instructions in one), the
-    dual-issued share, the matrix-core busy fraction, and the VALU
-    lane-instructions per (group, entry)."""
-    name, kernel, sources = profiled_kernel(config)
+    dual-issued share, the matrix-core busy fraction, the share of the
+    kernel's cycles an LDS (one per CU) is stalled on bank conflicts, and the
+    VALU lane-instructions per (group, entry)."""
+    name, kernel, sources = which or profiled_kernel(config)
     kname = kernel.split("<")[0]
     path = _pmc_csv(pmc_dir, config, "valu")
     v = {c: _counter_mean(path, kname, c)[0] for c in VALU_COUNTERS}
@@ -239,6 +252,7 @@ def record_counters(config, pmc_dir, units):
         "valu_issue_busy": issue_quads / (cycles / 4.0),
         "dual_issued_share": 2.0 * v["SQ_ACTIVE_INST_VALU2"] / v["SQ_INSTS_VALU"],
         "mfma_busy": v["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cycles),
+        "lds_conflict_share": v["SQ_LDS_BANK_CONFLICT"] / (N_CU * cycles),
         "valu_lane_instr_per_unit": (v["SQ_INSTS_VALU"] * 64 / units) if units else None,
         "units_per_launch": units,
     }
@@ -273,7 +287,7 @@ def counters_for(name, sha):
         return None
     return {k: round(t[k], 4) if isinstance(t[k], float) else t[k]
             for k in ("valu_issue_busy", "dual_issued_share", "mfma_busy",
-                      "valu_lane_instr_per_unit")}
+                      "lds_conflict_share", "valu_lane_instr_per_unit") if k in t}
 
 
 def host_info():
@@ -369,7 +383,9 @@ def encode_roofline(fmt, weighted, units, kernel_ms, alg_bytes, config):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for the decode workloads, whose "
+                         "launches take about 15 us)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warm-up steps (default: at least 10 and at least 1 s of them, "
                          "so the clocks have settled; the count run is reported)")
@@ -386,6 +402,8 @@ def main():
                          "profiles/counters_<kernel>_<config>.json and exit (no GPU needed)")
     args = ap.parse_args()
 
+    if args.steps is None:
+        args.steps = 200 if args.config.endswith("_dequant") else 20
     if args.record_traffic:
         record_traffic(args.config, args.record_traffic)
         return
@@ -396,6 +414,9 @@ def main():
         if not args.config.endswith("_dequant"):
             units = cfg["w"].size // 8 * cfg["grid"].shape[0]
         record_counters(args.config, args.record_counters, units)
+        if args.config in PROFILED_SEARCH:
+            record_counters(args.config, args.record_counters, None,
+                            PROFILED_SEARCH[args.config])
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -574,9 +595,12 @@ def main():
         sbytes = cand_bytes + H.numel() * 4 + nsearch * G * 4
         sb = {"fp32_ms": round(sflops / (PEAK_FP32_VECTOR_TFLOPS * 1e12) * 1e3, 5),
               "hbm_ms": round(sbytes / (PEAK_HBM_GBPS * 1e9) * 1e3, 5)}
-        roof["search"] = {"kernel_ms": round(search_ms, 5), "algorithmic_flops": sflops,
+        sname, skernel, ssrc = PROFILED_SEARCH[args.config]
+        roof["search"] = {"kernel": skernel, "kernel_ms": round(search_ms, 5),
+                          "algorithmic_flops": sflops,
                           "algorithmic_bytes": sbytes, "bound_ms": sb,
-                          "frac_of_bound": round(max(sb.values()) / search_ms, 4)}
+                          "frac_of_bound": round(max(sb.values()) / search_ms, 4),
+                          "counters": counters_for(sname, source_sha(ssrc))}
         result["roofline"] = roof
     else:
         weighted = imp is not None

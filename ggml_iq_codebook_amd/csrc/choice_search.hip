@@ -121,12 +121,6 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         return cb + (row0 + rr) * cstride + ((int64_t)g * C + c) * L;
     };
 
-    for (int i = t; i < G * L * L; i += kThreads) {
-        const int g = i / (L * L), rem = i % (L * L), ii = rem / L, jj = rem % L;
-        hdiag[g * kHB + ii * kHR + jj] = Hb[(g * L + ii) * 256 + g * L + jj];
-    }
-    __syncthreads();
-
     // e_gc^T H_gg e_gc on the matrix cores (all waves): for group g and 16
     // (row, cand) columns n, Y = H_gg E^T (lane: rows 4lq..4lq+3 of each
     // 16-row block of Y, column n = lc), then the column's dot with E, summed
@@ -158,7 +152,14 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
                     E[b][h] = live ? ep[4 * h + lq] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         };
+        // The first batch is requested before the diagonal blocks of H are
+        // staged, so the two reads overlap.
         load_batch(wave, Ec);
+        for (int i = t; i < G * L * L; i += kThreads) {
+            const int g = i / (L * L), rem = i % (L * L), ii = rem / L, jj = rem % L;
+            hdiag[g * kHB + ii * kHR + jj] = Hb[(g * L + ii) * 256 + g * L + jj];
+        }
+        __syncthreads();
         for (int j0 = wave; j0 < njobs; j0 += kWaves * kJB) {     // wave-uniform
             load_batch(j0 + kWaves * kJB, En);
             float qv[kJB];
