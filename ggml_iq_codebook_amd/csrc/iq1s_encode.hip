@@ -275,6 +275,10 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     // Per wave, its half block's values and weights as fp32 (32 + 32 float4),
     // read back by the rescans instead of global memory (kStage modes).
     __shared__ float4 sxw_all[kStage ? kWavesPerWG * 64 : 1];
+    // Candidates: per wave and choice unit, the choices and their costs in
+    // (cost, choice) order (4 sub-blocks x 16 or 8 scale groups x 8 per wave).
+    __shared__ float srank_cost[kMode == kModeCandidates ? kWavesPerWG * 64 : 1];
+    __shared__ uint8_t srank_c[kMode == kModeCandidates ? kWavesPerWG * 64 : 1];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
 
@@ -621,38 +625,86 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         // is least is kept), and the payload, decoded values or candidate.
         const int nloop = kMode == kModeEvery ? kChoices
                         : (kMode == kModeCandidates ? a.top_c : (refine ? 2 : 1));
+        // Candidates: the order of the unit's choices by (cost, choice),
+        // formed once.  Every lane of a choice unit (IQ1_S: 4 groups x 4
+        // lanes; IQ1_M: 2 x 4) holds the same costs; the lane of slot u ranks
+        // choice u by counting the costs below it and files the choice and
+        // its cost under its rank in the LDS.  Equal costs (or a NaN) leave
+        // the ranks short of a permutation; a wave with such a unit takes the
+        // selection below in every round instead.  A zero scale keeps the
+        // order 0, 1, ...
+        bool ordered = false;
+        const float* rc = srank_cost;
+        const uint8_t* rk8 = srank_c;
+        if constexpr (kMode == kModeCandidates) {
+            const int uslot = kM ? ((col & 1) | (kb << 1)) : ((col & 3) | (kb << 2));
+            const int ubase = wave * 64 + (kM ? (col >> 1) : (col >> 2)) * kChoices;
+            float mine = cost[0];
+#pragma unroll
+            for (int c = 1; c < kChoices; ++c)
+                if (uslot == c) mine = cost[c];
+            int rank = 0;
+#pragma unroll
+            for (int c = 0; c < kChoices; ++c) rank += cost[c] < mine ? 1 : 0;
+            if (zero_scale) rank = uslot;
+            srank_cost[ubase + rank] = mine;
+            srank_c[ubase + rank] = (uint8_t)uslot;
+            int rmask = 1 << rank;
+            rmask |= __shfl_xor(rmask, 1);
+            if (!kM) rmask |= __shfl_xor(rmask, 2);
+            rmask |= __shfl_xor(rmask, 16);
+            rmask |= __shfl_xor(rmask, 32);
+            ordered = __ballot(rmask != (1 << kChoices) - 1) == 0;   // wave-uniform
+            rc = srank_cost + ubase;
+            rk8 = srank_c + ubase;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
         for (int it = 0; it < nloop; ++it) {
             int ch = kMode == kModeEvery ? it : cstar;
             if (refine && it == 0 && near) ch = c2;
             if (kMode == kModeCandidates) {
                 int cr = -1;
                 float vr = 0.0f;
-#pragma unroll
-                for (int c = 0; c < kChoices; ++c) {
-                    const bool better = zero_scale ? (cr < 0) : (cr < 0 || cost[c] < vr);
-                    if (!((used >> c) & 1) && better) { cr = c; vr = cost[c]; }
+                bool nr = false;
+                if (ordered) {                                  // wave-uniform
+                    cr = rk8[it];
+                    vr = rc[it];
+                    if (it + 1 < kChoices && !zero_block) nr = rc[it + 1] - vr <= 0x1p-18f * fabsf(vr);
                 }
-                // Unused choices whose fp32 cost is within 2^-18 of the
-                // least's magnitude are ranked again by their fp64 errors
-                // (with their own entries), the lower choice on equal errors,
-                // as the payload's runner-up is.
-                uint32_t nearm = 0u;
-                if (!zero_block) {
+                if (!ordered || __ballot(nr) != 0) {            // wave-uniform
+                    const int cord = cr;
+                    cr = -1;
 #pragma unroll
-                    for (int c = 0; c < kChoices; ++c)
-                        if (!((used >> c) & 1) && c != cr && cost[c] - vr <= 0x1p-18f * fabsf(vr))
-                            nearm |= 1u << c;
-                }
-                if (__ballot(nearm != 0u) != 0) {               // wave-uniform
-                    double b64 = unit_err64(full(cr), pick_entry(full(cr)));
                     for (int c = 0; c < kChoices; ++c) {
-                        if (__ballot((nearm >> c) & 1u) == 0) continue;   // wave-uniform
-                        const double e = unit_err64(full(c), pick_entry(full(c)));
-                        if (((nearm >> c) & 1u) && (e < b64 || (e == b64 && c < cr))) {
-                            b64 = e;
-                            cr = c;
+                        const bool better = zero_scale ? (cr < 0) : (cr < 0 || cost[c] < vr);
+                        if (!((used >> c) & 1) && better) { cr = c; vr = cost[c]; }
+                    }
+                    // Unused choices whose fp32 cost is within 2^-18 of the
+                    // least's magnitude are ranked again by their fp64 errors
+                    // (with their own entries), the lower choice on equal
+                    // errors, as the payload's runner-up is.
+                    uint32_t nearm = 0u;
+                    if (!zero_block) {
+#pragma unroll
+                        for (int c = 0; c < kChoices; ++c)
+                            if (!((used >> c) & 1) && c != cr && cost[c] - vr <= 0x1p-18f * fabsf(vr))
+                                nearm |= 1u << c;
+                    }
+                    if (__ballot(nearm != 0u) != 0) {           // wave-uniform
+                        double b64 = unit_err64(full(cr), pick_entry(full(cr)));
+                        for (int c = 0; c < kChoices; ++c) {
+                            if (__ballot((nearm >> c) & 1u) == 0) continue;   // wave-uniform
+                            const double e = unit_err64(full(c), pick_entry(full(c)));
+                            if (((nearm >> c) & 1u) && (e < b64 || (e == b64 && c < cr))) {
+                                b64 = e;
+                                cr = c;
+                            }
                         }
                     }
+                    // a pick out of the filed order ends its use
+                    if (ordered && __ballot(cr != cord) != 0) ordered = false;
                 }
                 used |= 1 << cr;
                 ch = cr;

@@ -17,28 +17,26 @@
 //
 // With the signs fixed, the error of a group and an entry is, up to a
 // constant, s^2*N - 2s*P with N = sum w*q^2 and P = sum (w*sign*x)*q.  P and
-// N for 16 entries x 16 groups are two [16 x 8] x [8 x 16] products on the
-// matrix cores.  When every grid value and its square are exact in bf16 (the
-// odd-integer grids {1,3,5} among them), each is one v_mfma_f32_16x16x32_bf16
-// with the group side split in three bf16 parts whose sum is the fp32 value,
-// so the products are exact; any other magnitude grid is used as given with
-// fp32 operands (two v_mfma_f32_16x16x4_f32 each, four times the matrix-core
-// time).  Dividing by d, the key of local scale k is (2k+1)*N - 2P/d: one FMA
-// with a literal multiplier; the choice cost of a scale group is (2k+1) times
-// the sum of its two groups' minima.
+// N for a tile of entries x groups are two [entries x 8] x [8 x groups]
+// products on the matrix cores.  When every grid value and its square are
+// exact in bf16 (the odd-integer grids {1,3,5} among them), the group side is
+// split in three bf16 parts whose sum is the fp32 value, so the bf16 products
+// are exact; any other magnitude grid is used as given with fp32 operands
+// (four times the matrix-core time).  Dividing by d, the key of local scale k
+// is (2k+1)*N - 2P/d: one FMA with a literal multiplier; the choice cost of a
+// scale group is (2k+1) times the sum of its two groups' minima.
 //
-// Two kernels.  The payload encode (iq2xs_payload_wide_kernel, below) runs
-// 32 x 32 matrix tiles with a wave per block.  The other outputs (every
-// choice, fake quant, candidates) run iq2xs_kernel with 16 x 16 tiles.
-//
-// Layout of iq2xs_kernel: a wave owns 16 groups (half a block); matrix
-// column j = lane%16 is group j, the lane's accumulator rows are entries
-// 4*(lane/16)+r of each 16-entry tile.  A 1024-thread workgroup runs 8 blocks per pass and 2 passes
-// per set of 16 blocks; the workgroups are persistent (one per CU) and stage
-// the grid once in LDS (q and q^2 as fp32 and as bf16, and a padded fp32 copy
-// for the rescans: 85 KiB).  Value-only minima (v_min3); each lane records
-// the chunk that last lowered each minimum; the lane of each column whose
-// matrix-core minimum is least is found, and the four lanes of the column
+// Two kernels.  iq2xs_wide_kernel (the payload, the fake quant and the
+// candidates) runs 32 x 32 matrix tiles, v_mfma_f32_32x32x16_bf16, with a
+// wave per block: matrix column = group, two lanes per column, each holding
+// 16 entries of every 32-entry tile.  iq2xs_every_kernel (the payload under
+// every choice) runs 16 x 16 tiles with a wave per half block: column j =
+// lane%16 is group j, the lane's accumulator rows are entries 4*(lane/16)+r
+// of each 16-entry tile.  Both run persistent 1024-thread workgroups (one per
+// CU) that stage the grid once in LDS (q and q^2 as bf16 operands, and a
+// padded fp32 copy for the rescans).  Value-only minima (v_min3); each lane
+// records the chunk that last lowered each minimum; the lane of each column
+// whose matrix-core minimum is least is found, and the lanes of the column
 // split its entries of that chunk and rescan them on the VALU (lowest entry
 // of least key).
 #include <hip/hip_runtime.h>
@@ -609,6 +607,56 @@ __device__ __forceinline__ int rescan_wide(const float* __restrict__ sg, int chu
     return idx;
 }
 
+// The same rescan with the same keys, for the candidates' many picks: it
+// reads only q from the LDS (q^2 formed in fp32 is the table's value
+// exactly), and it requests the four entries of a row quad before it forms
+// their keys, so a pick waits for the LDS kNV/4 times rather than kNV times.
+template <int kCT, int kNV>
+__device__ __forceinline__ int rescan_quads(const float* __restrict__ sg, int chunk, int hs, int v0,
+                                            int k, const float (&wxs)[8], const float (&w)[8],
+                                            float inv_d, float* key_out)
+{
+    const float mk = (float)(2 * k + 1);
+    const int e0 = kWTile * kCT * chunk + 4 * hs + 8 * (v0 >> 2);
+    const float* base = sg + kEntryStride * e0 + 2 * chunk;      // entry_off<32*kCT>(e0)
+    int idx = e0;
+    float vbest = __builtin_inff();
+#pragma unroll
+    for (int tt = 0; tt < kCT; ++tt) {
+#pragma unroll
+        for (int r4 = 0; r4 < kNV / 4; ++r4) {
+            float q[4][8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int de = kWTile * tt + 8 * r4 + i;
+                const float2* p = reinterpret_cast<const float2*>(base + kEntryStride * de);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float2 u = p[t];
+                    q[i][2 * t] = u.x;
+                    q[i][2 * t + 1] = u.y;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int de = kWTile * tt + 8 * r4 + i;
+                float P = 0.0f, N = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    P = __builtin_fmaf(wxs[j], q[i][j], P);
+                    N = __builtin_fmaf(w[j], q[i][j] * q[i][j], N);
+                }
+                const float key = __builtin_fmaf(N, mk, (-2.0f * P) * inv_d);
+                const bool better = key < vbest;
+                vbest = better ? key : vbest;
+                idx = better ? e0 + de : idx;
+            }
+        }
+    }
+    *key_out = vbest;
+    return idx;
+}
+
 // kMode: kModePayload, kModeFake or kModeCandidates; kDT: the weight's
 // iq_dtype_t.
 template <int kMode, int kDT>
@@ -627,6 +675,10 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
     __shared__ int sgrid_bad, sgrid_inexact;
     __shared__ float4 ssnap[4 * kThreads];              // per lane: the minima at the last chunk end
     __shared__ uint16_t sout16[kCand ? 1 : kWavesPerWG * kBlockBytes / 2];    // the set's payloads
+    // candidates: per wave and scale group, the 16 local scales and their
+    // costs in (cost, k) order
+    __shared__ float srank_cost[kCand ? kWavesPerWG * 16 * 16 : 1];
+    __shared__ uint8_t srank_k[kCand ? kWavesPerWG * 16 * 16 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -835,11 +887,10 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
         // its chunk's entries (lowest entry of least key).  With equal minima
         // in the two lanes of any column, every lane rescans its own entries
         // and the lane of least minimum, then lowest entry, wins.
+        // The snapshot in LDS holds the lane's final minima (the last chunk
+        // wrote it), so best[] need not stay live through the epilogue.
         auto pick = [&](int k) -> int {
-            float lm = best[0];
-#pragma unroll
-            for (int c = 1; c < 16; ++c)
-                if (k == c) lm = best[c];
+            const float lm = reinterpret_cast<const float*>(snap + (k >> 2) * kThreads)[k & 3];
             const int tchunk = (int)((chunk_of[k >> 3] >> (4 * (k & 7))) & 0xfu);
             const float om = __shfl_xor(lm, 32);
             const bool tie = __ballot(om == lm) != 0;                // wave-uniform
@@ -848,7 +899,10 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
             if (!tie) {
                 const int hs = (om < lm) ? (hl ^ 1) : hl;             // holder half
                 const int tch = __shfl(tchunk, g + 32 * hs);
-                idx = rescan_wide<kCT, 8>(sgrid, tch, hs, 8 * hl, k, wxs, w, inv_d, &key);
+                if constexpr (kCand)
+                    idx = rescan_quads<kCT, 8>(sgrid, tch, hs, 8 * hl, k, wxs, w, inv_d, &key);
+                else
+                    idx = rescan_wide<kCT, 8>(sgrid, tch, hs, 8 * hl, k, wxs, w, inv_d, &key);
                 const float ok = __shfl_xor(key, 32);
                 const int oi = __shfl_xor(idx, 32);
                 if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
@@ -948,43 +1002,88 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
             };
             float xo[8], wo[8];
             load_group(xb, wblk, g, bad_block, xo, wo);   // the original values
+
+            // The order of the 16 local scales by (cost, k), formed once: the
+            // four lanes of a scale group hold the same 16 costs, and the lane
+            // of slot s4 ranks k = 4*s4 .. 4*s4+3 by counting the costs below
+            // each, then files k and its cost under its rank in the LDS, where
+            // every lane of the group reads the order.  Equal costs (or a NaN)
+            // leave the ranks short of a permutation; a wave with such a scale
+            // group takes the selection below in every round instead.  A
+            // zero or rejected block keeps the order 0, 1, ...
+            const int s4 = h | (hl << 1);
+            float* rc = srank_cost + (wave * 16 + m) * 16;
+            uint8_t* rk8 = srank_k + (wave * 16 + m) * 16;
+            int rmask = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float mi = s4 == 0 ? cost[i] : s4 == 1 ? cost[4 + i] : s4 == 2 ? cost[8 + i] : cost[12 + i];
+                int rank = 0;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) rank += cost[k] < mi ? 1 : 0;
+                if (skip) rank = 4 * s4 + i;
+                rmask |= 1 << rank;
+                rc[rank] = mi;
+                rk8[rank] = (uint8_t)(4 * s4 + i);
+            }
+            rmask |= __shfl_xor(rmask, 1);
+            rmask |= __shfl_xor(rmask, 32);
+            bool ordered = __ballot(rmask != 0xffff) == 0;   // wave-uniform
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
             int used = 0;
             for (int r = 0; r < C; ++r) {
                 int kr = -1;
                 float cr = 0.0f;
-#pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const bool free_k = !((used >> k) & 1);
-                    const bool better = zero_scale ? (kr < 0) : (kr < 0 || cost[k] < cr);
-                    if (free_k && better) { kr = k; cr = cost[k]; }
-                }
-                // Unused local scales whose fp32 cost is within 2^-18 of the
-                // least's magnitude are ranked again by their fp64 errors
-                // (with their own entries), the lower k on equal errors, as
-                // the payload's runner-up is.
-                uint32_t nearm = 0u;
-                if (!skip) {
-#pragma unroll
-                    for (int k = 0; k < 16; ++k)
-                        if (!((used >> k) & 1) && k != kr && cost[k] - cr <= 0x1p-18f * fabsf(cr))
-                            nearm |= 1u << k;
+                bool near = false;
+                if (ordered) {                                  // wave-uniform
+                    kr = rk8[r];
+                    cr = rc[r];
+                    if (r + 1 < 16 && !skip) near = rc[r + 1] - cr <= 0x1p-18f * fabsf(cr);
                 }
                 int idx;
-                if (__ballot(nearm != 0u) != 0) {               // wave-uniform
+                if (ordered && __ballot(near) == 0) {           // wave-uniform
                     idx = pick(kr);
-                    double b64 = cost64(kr, idx);
-                    for (int k = 0; k < 16; ++k) {
-                        if (__ballot((nearm >> k) & 1u) == 0) continue;   // wave-uniform
-                        const int ik = pick(k);
-                        const double e = cost64(k, ik);
-                        if (((nearm >> k) & 1u) && (e < b64 || (e == b64 && k < kr))) {
-                            b64 = e;
-                            kr = k;
-                            idx = ik;
-                        }
-                    }
                 } else {
-                    idx = pick(kr);
+                    const int kord = kr;
+                    kr = -1;
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) {
+                        const bool free_k = !((used >> k) & 1);
+                        const bool better = zero_scale ? (kr < 0) : (kr < 0 || cost[k] < cr);
+                        if (free_k && better) { kr = k; cr = cost[k]; }
+                    }
+                    // Unused local scales whose fp32 cost is within 2^-18 of
+                    // the least's magnitude are ranked again by their fp64
+                    // errors (with their own entries), the lower k on equal
+                    // errors, as the payload's runner-up is.
+                    uint32_t nearm = 0u;
+                    if (!skip) {
+#pragma unroll
+                        for (int k = 0; k < 16; ++k)
+                            if (!((used >> k) & 1) && k != kr && cost[k] - cr <= 0x1p-18f * fabsf(cr))
+                                nearm |= 1u << k;
+                    }
+                    if (__ballot(nearm != 0u) != 0) {           // wave-uniform
+                        idx = pick(kr);
+                        double b64 = cost64(kr, idx);
+                        for (int k = 0; k < 16; ++k) {
+                            if (__ballot((nearm >> k) & 1u) == 0) continue;   // wave-uniform
+                            const int ik = pick(k);
+                            const double e = cost64(k, ik);
+                            if (((nearm >> k) & 1u) && (e < b64 || (e == b64 && k < kr))) {
+                                b64 = e;
+                                kr = k;
+                                idx = ik;
+                            }
+                        }
+                    } else {
+                        idx = pick(kr);
+                    }
+                    // a pick out of the filed order ends its use
+                    if (ordered && __ballot(kr != kord) != 0) ordered = false;
                 }
                 used |= 1 << kr;
                 int msk = neg2 & 0x7f;
