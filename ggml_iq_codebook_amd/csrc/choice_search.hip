@@ -12,23 +12,26 @@
 // score_c - score_cur, score_c = e_c^T H_gg e_c + 2 e_c^T (r_g - H_gg e_cur).
 //
 // Layout: a 512-thread workgroup runs 16 rows of one block in lockstep
-// (grid.y = the block), with two kinds of waves.  The products with H run on
-// the matrix cores (v_mfma_f32_16x16x4_f32, fp32 operands): first
-// e_c^T H_gg e_c for every candidate (all eight waves), then, for each step of
-// the sweeps, the rest of the next group gn, r_gn - H_gn,gn e_gn = sum over
-// the other groups h of H_gn,h e_h, formed afresh from the current errors (no
-// running r = H e is kept).  Waves 0-3 compute those products: while group g
-// is being decided, each sums its quarter of K, leaving out gn and g; after
-// the decision each adds its quarter of H_gn,g e_g with g's new errors and
-// leaves its partial rest in LDS.  Waves 4-7 decide, one lane per (row,
-// candidate): the rest of g is the sum of the four partials, each lane scores
-// its candidate from its own error vector and that rest, and one DPP
-// reduction across the row's 16 lanes gives the lowest index of least score,
-// the current pick winning the ties it is in (each lane keeps a bit mask of
-// the groups whose pick is its candidate).  The two kinds of waves share the
-// SIMDs, so the products of the next group run beside the decision of the
-// current one; two barriers per step.  The next step's H operands and
-// candidate vectors are requested a step ahead.
+// (grid.y = the block), with two kinds of waves.  First e_c^T H_gg e_c for
+// every candidate, on the matrix cores (v_mfma_f32_16x16x4_f32, fp32
+// operands, all eight waves).  Then the sweeps, one workgroup barrier per
+// step.  With the groups visited in order, the rest of group g,
+// r_g - H_gg e_cur,g = sum over h != g of H_g,h e_h, is the partial sum over
+// h outside {g-1, g}, which waves 0-3 form on the matrix cores during the
+// step before (each its quarter of K, from the current errors held
+// row-major in LDS), plus H_g,g-1 e_g-1 with the errors just decided for
+// g-1, which waves 4-7 add themselves.  Waves 4-7 decide, one lane per
+// (row, candidate), lane (row, i) also owning column i of the row's rest:
+// the lane adds the four partials and the late term for its column, the
+// row's rest reaches the lanes of the row by DPP broadcasts, each lane scores
+// its candidate from its own error vector, and one DPP reduction across the
+// row's 16 lanes gives the lowest index of least score, the current pick
+// winning the ties it is in (each lane keeps a bit mask of the groups whose
+// pick is its candidate).  A row whose pick moves writes its new errors into
+// the error rows.  The partial sums alternate between two buffers, so the
+// products of the next group run beside the decision of the current one.
+// H operands and candidate vectors are requested two steps ahead; the blocks
+// H_g,g-1 are staged in LDS.
 
 #include <hip/hip_runtime.h>
 
@@ -61,26 +64,46 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Lane exchange within a row of 16 lanes (DPP): rotate by 8 or 4, or swap with
-// the lane 2 or 1 away inside a quad.
+// Lane exchange within a row of 16 lanes (DPP): rotate by 8 or 4, swap with
+// the lane 2 or 1 away inside a quad, or take lane j of the row.  Every lane
+// has a source lane in these patterns.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xf, 0xf, true);
+}
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f(float v)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                 kCtrl, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, dpp_i<kCtrl>(__builtin_bit_cast(int, v)));
 }
 
 constexpr int kRor8 = 0x128, kRor4 = 0x124, kXor2 = 0x4e, kXor1 = 0xb1;
 
-// Least value over the 16 lanes of a row; every lane of the row ends with it
+// An integer whose signed order is the order of the float scores (-0 counted
+// as +0, so equal scores keep equal keys).
+__device__ __forceinline__ int score_key(float v)
+{
+    const int b = __builtin_bit_cast(int, v + 0.0f);
+    return b ^ (int)((uint32_t)(b >> 31) >> 1);
+}
+
+// Least key over the 16 lanes of a row; every lane of the row ends with it
 // (the four steps reach lanes +8, +4, ^2, ^1 away, which together cover the
 // row).
-__device__ __forceinline__ float row_min(float v)
+__device__ __forceinline__ int row_min(int v)
 {
-    v = fminf(v, dpp_f<kRor8>(v));
-    v = fminf(v, dpp_f<kRor4>(v));
-    v = fminf(v, dpp_f<kXor2>(v));
-    return fminf(v, dpp_f<kXor1>(v));
+    v = min(v, dpp_i<kRor8>(v));
+    v = min(v, dpp_i<kRor4>(v));
+    v = min(v, dpp_i<kXor2>(v));
+    return min(v, dpp_i<kXor1>(v));
+}
+
+// The value of lane j of the lane's row of 16 (DPP row broadcast).
+template <int j>
+__device__ __forceinline__ float bcast(float v)
+{
+    return dpp_f<0x150 + j>(v);
 }
 
 template <int L>
@@ -90,15 +113,16 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     constexpr int KH = L / 16;                  // 16-column tiles per group
     // LDS rows are padded (and stay 16-byte aligned) so that the lanes of a
     // wave reading rows, blocks or columns together fall in different banks.
-    constexpr int kHR = L + 4;                  // H_gg row stride, rest row stride
-    constexpr int kHB = L * kHR + 4;            // H_gg block stride
+    constexpr int kHR = L + 4;                  // H block row stride
+    constexpr int kHB = L * kHR + 4;            // H block stride
+    constexpr int kER = 256 + 4;                // error row stride
     constexpr int kQS = G * kMaxC + 16;         // qself row stride
     constexpr int kPR = L + 4;                  // partial rest row stride
-    __shared__ __align__(16) float hdiag[G * kHB];        // H_gg blocks [g][i][j]
-    __shared__ __align__(16) float ecurT[256 * kRows];    // current errors, [column][row]
-    __shared__ __align__(16) float part[kProdWaves * kRows * kPR];  // [wave][row][i]
-    __shared__ __align__(16) float enew[kRows * kPR];     // the decided group's errors, [row][i]
-    __shared__ __align__(16) float rest[kRows * kHR];     // r_g - H_gg e_cur,g, [row][i]
+    constexpr int kPB = kProdWaves * kRows * kPR;   // one partial buffer
+    // H_gg for step 2, then H_g,g-1 for the sweeps
+    __shared__ __align__(16) float hblk[G * kHB];
+    __shared__ __align__(16) float ecur[kRows * kER];     // current errors, [row][column]
+    __shared__ __align__(16) float part[2 * kPB];         // [buffer][wave][row][i]
     __shared__ __align__(16) float qself[kRows * kQS];    // e_gc^T H_gg e_gc, [row][g*C + c]
     __shared__ int pick0[kRows * G];                      // step-2 picks
 
@@ -119,6 +143,25 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     };
     auto cand_ptr = [&](int rr, int g, int c) -> const float* {
         return cb + (row0 + rr) * cstride + ((int64_t)g * C + c) * L;
+    };
+    // H block (g, gx) as [i][j] = H[g*L + i][gx*L + j] into hblk, 16 bytes
+    // a thread at a time, every load requested before the first store.
+    auto stage_blocks = [&](bool sub) {
+        constexpr int kU = G * L * L / 4 / kThreads;            // float4 per thread
+        float4 v[kU];
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+            const int u = t + kThreads * k;
+            const int g = u / (L * L / 4), rem = u % (L * L / 4), ii = rem / (L / 4), j4 = rem % (L / 4);
+            const int gx = sub ? (g + G - 1) % G : g;
+            v[k] = *reinterpret_cast<const float4*>(&Hb[(g * L + ii) * 256 + gx * L + 4 * j4]);
+        }
+#pragma unroll
+        for (int k = 0; k < kU; ++k) {
+            const int u = t + kThreads * k;
+            const int g = u / (L * L / 4), rem = u % (L * L / 4), ii = rem / (L / 4), j4 = rem % (L / 4);
+            *reinterpret_cast<float4*>(&hblk[g * kHB + ii * kHR + 4 * j4]) = v[k];
+        }
     };
 
     // e_gc^T H_gg e_gc on the matrix cores (all waves): for group g and 16
@@ -155,10 +198,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         // The first batch is requested before the diagonal blocks of H are
         // staged, so the two reads overlap.
         load_batch(wave, Ec);
-        for (int i = t; i < G * L * L; i += kThreads) {
-            const int g = i / (L * L), rem = i % (L * L), ii = rem / L, jj = rem % L;
-            hdiag[g * kHB + ii * kHR + jj] = Hb[(g * L + ii) * 256 + g * L + jj];
-        }
+        stage_blocks(false);
         __syncthreads();
         for (int j0 = wave; j0 < njobs; j0 += kWaves * kJB) {     // wave-uniform
             load_batch(j0 + kWaves * kJB, En);
@@ -173,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
                     v4f y = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int kh = 0; kh < KH; ++kh) {
-                        const float* hr = &hdiag[g * kHB + (16 * ih + lc) * kHR + 16 * kh + 4 * lq];
+                        const float* hr = &hblk[g * kHB + (16 * ih + lc) * kHR + 16 * kh + 4 * lq];
                         const float4 e4 = Ec[b][kh];
                         y = mfma4(hr[0], e4.x, y);
                         y = mfma4(hr[1], e4.y, y);
@@ -210,7 +250,8 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
     __syncthreads();
 
     // Step 2: each group's best candidate under its own block (lowest index on
-    // ties), and the current errors as columns.
+    // ties), and the current errors as rows; the blocks H_g,g-1 replace H_gg.
+    stage_blocks(true);
     for (int it = t; it < kRows * G; it += kThreads) {
         const int rr = it / G, g = it % G;
         int best = 0;
@@ -219,13 +260,9 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         pick0[rr * G + g] = best;
         const float4* ep = rr < nrows ? reinterpret_cast<const float4*>(cand_ptr(rr, g, best)) : nullptr;
 #pragma unroll
-        for (int i4 = 0; i4 < L / 4; ++i4) {
-            const float4 v = ep ? ep[i4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            ecurT[(g * L + 4 * i4) * kRows + rr] = v.x;
-            ecurT[(g * L + 4 * i4 + 1) * kRows + rr] = v.y;
-            ecurT[(g * L + 4 * i4 + 2) * kRows + rr] = v.z;
-            ecurT[(g * L + 4 * i4 + 3) * kRows + rr] = v.w;
-        }
+        for (int i4 = 0; i4 < L / 4; ++i4)
+            *reinterpret_cast<float4*>(&ecur[rr * kER + g * L + 4 * i4]) =
+                ep ? ep[i4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
     __syncthreads();
     if (a.trace)
@@ -236,17 +273,21 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
 
     if (prod) {
         // ---------------- product waves ----------------
-        // The wave's partial rest of group gn for the 16 rows: K range
-        // 64w .. 64w + 63 in steps of 4 (k = 64w + 4s + lq), the columns of gn
-        // and gx (gx < 0: none) left out.  Output tile ih holds the columns
-        // gn*L + 16ih .. + 15 (lane: columns 4lq..4lq+3 of the tile, row lc).
-        // Then its quarter of the late product H_gn,gx e_gx (k = gx*L +
-        // (L/4)w + 4s + lq, s < KH) with gx's new errors, and the tiles go to
-        // part[w] as [row][column].  The H operands (H symmetric: H[k][column])
-        // are requested a step ahead.
+        // During step g the wave forms its partial rest of group gn = g+1 for
+        // the 16 rows: K range 64w .. 64w + 63 in steps of 4 (k = 64w + 4s +
+        // lq), the columns of gn and g left out.  Output tile ih holds the
+        // columns gn*L + 16ih .. + 15 (lane: columns 4lq..4lq+3 of the tile,
+        // row lc); the tiles go to partial buffer (g+1)%2 as [row][column].
+        // The H operands (H symmetric: H[k][column]) are requested a step
+        // ahead.
         constexpr int kPS = 16;                 // K steps per wave
+        constexpr int kGW = 64 / L;             // groups in the wave's K range
         float hP[KH][kPS], hPn[KH][kPS];        // H[64w + 4s + lq][gn*L + 16ih + lc]
-        float hX[KH][KH], hXn[KH][KH];          // H[gx*L + (L/4)w + 4s + lq][gn*L + 16ih + lc]
+        // The wave's B operands, e[row lc][64w + 4s + lq], kept between steps:
+        // only the group decided last can have changed.
+        float bv[kPS];
+#pragma unroll
+        for (int s = 0; s < kPS; ++s) bv[s] = ecur[lc * kER + 64 * wave + 4 * s + lq];
         auto load_hP = [&](int gn, float (&h)[KH][kPS]) {
 #pragma unroll
             for (int ih = 0; ih < KH; ++ih)
@@ -254,87 +295,60 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
                 for (int s = 0; s < kPS; ++s)
                     h[ih][s] = Hb[(64 * wave + 4 * s + lq) * 256 + gn * L + 16 * ih + lc];
         };
-        auto load_hX = [&](int gn, int gx, float (&h)[KH][KH]) {
+        auto pstep = [&](int gn, int gx, const float (&h)[KH][kPS], int buf) {
+            // the group decided in the step before gx's, if in the wave's range
+            const int gp = gx > 0 ? gx - 1 : G - 1;
 #pragma unroll
-            for (int ih = 0; ih < KH; ++ih)
+            for (int q = 0; q < kGW; ++q) {
+                if (kGW * wave + q == gp) {                         // wave-uniform
 #pragma unroll
-                for (int s = 0; s < KH; ++s)
-                    h[ih][s] = Hb[(gx * L + (L / 4) * wave + 4 * s + lq) * 256 + gn * L + 16 * ih + lc];
-        };
-        auto partial = [&](int gn, int gx, v4f (&p)[KH]) {
-            float bv[kPS];
-#pragma unroll
-            for (int s = 0; s < kPS; ++s) bv[s] = ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
-#pragma unroll
-            for (int ih = 0; ih < KH; ++ih) p[ih] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < kPS; ++s) {
-                const int kg = (64 * wave + 4 * s) / L;             // wave-uniform
-                if (kg != gn && kg != gx) {
-#pragma unroll
-                    for (int ih = 0; ih < KH; ++ih) p[ih] = mfma4(hP[ih][s], bv[s], p[ih]);
+                    for (int s = q * (L / 4); s < (q + 1) * (L / 4); ++s)
+                        bv[s] = ecur[lc * kER + 64 * wave + 4 * s + lq];
                 }
             }
-        };
-        auto store_part = [&](const v4f (&p)[KH]) {
-#pragma unroll
-            for (int ih = 0; ih < KH; ++ih)
-                *reinterpret_cast<v4f*>(&part[(wave * kRows + lc) * kPR + 16 * ih + 4 * lq]) = p[ih];
-        };
-
-        // The rest of group 0 (no group being decided).
-        v4f pp[KH];
-        load_hP(0, hP);
-        partial(0, -1, pp);
-        store_part(pp);
-        load_hP(1 % G, hP);
-        load_hX(1 % G, 0, hX);
-        __syncthreads();                        // part holds the rest of group 0
-        // One step: the products of gn beside the decision of g, with the
-        // operands requested the step before (cur); the next step's go into
-        // nxt once cur's are in use.  Steps alternate between the two register
-        // sets, so a load is first used about a step after it was issued.
-        auto pstep = [&](int g, float (&hPc)[KH][kPS], float (&hXc)[KH][KH],
-                         float (&hPx)[KH][kPS], float (&hXx)[KH][KH]) {
-            const int gn = g + 1 < G ? g + 1 : 0;
-            const int gnn = gn + 1 < G ? gn + 1 : 0;
-            float bv[kPS];
-#pragma unroll
-            for (int s = 0; s < kPS; ++s) bv[s] = ecurT[(64 * wave + 4 * s + lq) * kRows + lc];
+            v4f pp[KH];
 #pragma unroll
             for (int ih = 0; ih < KH; ++ih) pp[ih] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            // the wave's K range holds 64/L groups; those of gn and gx are left out
 #pragma unroll
-            for (int s = 0; s < kPS; ++s) {
-                const int kg = (64 * wave + 4 * s) / L;             // wave-uniform
-                if (kg != gn && kg != g) {
+            for (int q = 0; q < kGW; ++q) {
+                const int kg = kGW * wave + q;                      // wave-uniform
+                if (kg != gn && kg != gx) {
 #pragma unroll
-                    for (int ih = 0; ih < KH; ++ih) pp[ih] = mfma4(hPc[ih][s], bv[s], pp[ih]);
+                    for (int s = q * (L / 4); s < (q + 1) * (L / 4); ++s)
+#pragma unroll
+                        for (int ih = 0; ih < KH; ++ih) pp[ih] = mfma4(h[ih][s], bv[s], pp[ih]);
                 }
             }
-            // The next step's H operands, requested once this step's are in
-            // use (a wait for these must not wait for those).
-            load_hP(gnn, hPx);
-            load_hX(gnn, gn, hXx);
-            __syncthreads();                    // A: g decided, its errors in enew
 #pragma unroll
-            for (int s = 0; s < KH; ++s) {
-                const float b = enew[lc * kPR + (L / 4) * wave + 4 * s + lq];
-#pragma unroll
-                for (int ih = 0; ih < KH; ++ih) pp[ih] = mfma4(hXc[ih][s], b, pp[ih]);
-            }
-            store_part(pp);
-            __syncthreads();                    // B: part holds the rest of gn
+            for (int ih = 0; ih < KH; ++ih)
+                *reinterpret_cast<v4f*>(&part[buf * kPB + (wave * kRows + lc) * kPR + 16 * ih + 4 * lq]) = pp[ih];
         };
+
+        // The partial of group 0 (group G-1, decided last, left out).
+        load_hP(0, hP);
+        load_hP(1 % G, hPn);
+        pstep(0, G - 1, hP, 0);
+        load_hP(2 % G, hP);
+        __syncthreads();                        // X: partial of group 0 in buffer 0
+        // Step g: the partial of gn = g+1 with the operands requested two
+        // steps before; the operands of the step after next go into the
+        // registers just used.  Steps alternate between the two register sets.
         for (int sw = 0; sw < a.sweeps; ++sw) {
 #pragma unroll 1
             for (int g = 0; g < G; g += 2) {    // G is even
-                pstep(g, hP, hX, hPn, hXn);
-                pstep(g + 1, hPn, hXn, hP, hX);
+                pstep(g + 1, g, hPn, 1);
+                load_hP((g + 3) % G, hPn);
+                __syncthreads();                // X_g
+                pstep((g + 2) % G, g + 1, hP, 0);
+                load_hP((g + 4) % G, hP);
+                __syncthreads();                // X_g+1
             }
         }
     } else {
         // ---------------- decision waves ----------------
-        // Lane (srow, scand); pmask bit g = group g's pick is scand.
+        // Lane (srow, scand); pmask bit g = group g's pick is scand.  The lane
+        // also owns columns scand + 16h of its row's rest.
         const int dt = t - 64 * kProdWaves;
         const int srow = dt >> 4;
         const int scand = dt & 15;
@@ -342,91 +356,126 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         uint32_t pmask = 0u;
         for (int g = 0; g < G; ++g) pmask |= (uint32_t)(pick0[srow * G + g] == scand) << g;
         float cv[L], cvn[L];
+        // Every lane loads a vector: a lane past the row's candidates or the
+        // block's rows reads a real one (its values are never scored).
+        const float* cbase = cand_ptr(srow < nrows ? srow : nrows - 1, 0, scand < C ? scand : C - 1);
         auto load_cv = [&](int g, float (&v)[L]) {
-            if (scorer) {
-                const float4* ep = reinterpret_cast<const float4*>(cand_ptr(srow, g, scand));
+            const float4* ep = reinterpret_cast<const float4*>(cbase + g * C * L);
 #pragma unroll
-                for (int i4 = 0; i4 < L / 4; ++i4) {
-                    const float4 u = ep[i4];
-                    v[4 * i4] = u.x; v[4 * i4 + 1] = u.y; v[4 * i4 + 2] = u.z; v[4 * i4 + 3] = u.w;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < L; ++i) v[i] = 0.0f;
+            for (int i4 = 0; i4 < L / 4; ++i4) {
+                const float4 u = ep[i4];
+                v[4 * i4] = u.x; v[4 * i4 + 1] = u.y; v[4 * i4 + 2] = u.z; v[4 * i4 + 3] = u.w;
             }
         };
+        // H_g,g-1 e_g-1 for the lane's columns of group g, from the errors
+        // of g-1 in the error rows (the lanes of a row read the same row).
+        auto late = [&](int g, float (&lr)[KH]) {
+            const int gp = g > 0 ? g - 1 : G - 1;
+            const float* er = &ecur[srow * kER + gp * L];
+#pragma unroll
+            for (int h = 0; h < KH; ++h) {
+                const float* hr = &hblk[g * kHB + (scand + 16 * h) * kHR];
+                float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j4 = 0; j4 < L / 4; ++j4) {
+                    const float4 h4 = *reinterpret_cast<const float4*>(hr + 4 * j4);
+                    const float4 e4 = *reinterpret_cast<const float4*>(er + 4 * j4);
+                    d4[0] = __builtin_fmaf(h4.x, e4.x, d4[0]);
+                    d4[1] = __builtin_fmaf(h4.y, e4.y, d4[1]);
+                    d4[2] = __builtin_fmaf(h4.z, e4.z, d4[2]);
+                    d4[3] = __builtin_fmaf(h4.w, e4.w, d4[3]);
+                }
+                lr[h] = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+            }
+        };
+        float lr[KH];
         load_cv(0, cv);
-        __syncthreads();                        // part holds the rest of group 0
-        // One step: group g decided with its candidate vector requested the
-        // step before (cur); the next group's goes into nxt.
-        auto dstep = [&](int g, float (&cur)[L], float (&nxt)[L]) {
+        load_cv(1 % G, cvn);
+        late(0, lr);
+        __syncthreads();                        // X: partial of group 0 in buffer 0
+        // Step g: group g decided with its candidate vector requested two
+        // steps before (cur); once it is used, the vector of the group after
+        // next goes into the same registers.  Its late term
+        // (lr, formed in the step before) and the four partials give the
+        // rest; after the decision the row's errors of g are current in the
+        // error rows, and the late term of the next group follows.
+        auto dstep = [&](int g, float (&cur)[L]) {
             const int gn = g + 1 < G ? g + 1 : 0;
-            // The rest of g: the four partials summed in a fixed order, one
-            // column (two for L = 32) per lane, then the whole row read back by
-            // the row's 16 lanes (one wave: in order in LDS).
+            const int g2 = gn + 1 < G ? gn + 1 : 0;
+            const float* pb = part + (g & 1) * kPB;
+            float r[KH];
 #pragma unroll
             for (int h = 0; h < KH; ++h) {
                 const int i = scand + 16 * h;
-                float v = part[(0 * kRows + srow) * kPR + i];
+                float v = pb[(0 * kRows + srow) * kPR + i];
 #pragma unroll
-                for (int w = 1; w < kProdWaves; ++w) v += part[(w * kRows + srow) * kPR + i];
-                rest[srow * kHR + i] = v;
+                for (int w = 1; w < kProdWaves; ++w) v += pb[(w * kRows + srow) * kPR + i];
+                r[h] = v + lr[h];
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            float sc = __builtin_inff();
-            if (scorer) {
+            // The candidate's dot with the row's rest: column j of tile h
+            // comes from lane j of the row (DPP row broadcast).  Lanes that
+            // score nothing keep the largest key, above any score's.
+            int key = 0x7fffffff;
+            {
                 float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int i4 = 0; i4 < L / 4; ++i4) {
-                    const float4 r4 = *reinterpret_cast<const float4*>(&rest[srow * kHR + 4 * i4]);
-                    d4[0] = __builtin_fmaf(cur[4 * i4], r4.x, d4[0]);
-                    d4[1] = __builtin_fmaf(cur[4 * i4 + 1], r4.y, d4[1]);
-                    d4[2] = __builtin_fmaf(cur[4 * i4 + 2], r4.z, d4[2]);
-                    d4[3] = __builtin_fmaf(cur[4 * i4 + 3], r4.w, d4[3]);
+                for (int h = 0; h < KH; ++h) {
+                    d4[0] = __builtin_fmaf(cur[16 * h + 0], bcast<0>(r[h]), d4[0]);
+                    d4[1] = __builtin_fmaf(cur[16 * h + 1], bcast<1>(r[h]), d4[1]);
+                    d4[2] = __builtin_fmaf(cur[16 * h + 2], bcast<2>(r[h]), d4[2]);
+                    d4[3] = __builtin_fmaf(cur[16 * h + 3], bcast<3>(r[h]), d4[3]);
+                    d4[0] = __builtin_fmaf(cur[16 * h + 4], bcast<4>(r[h]), d4[0]);
+                    d4[1] = __builtin_fmaf(cur[16 * h + 5], bcast<5>(r[h]), d4[1]);
+                    d4[2] = __builtin_fmaf(cur[16 * h + 6], bcast<6>(r[h]), d4[2]);
+                    d4[3] = __builtin_fmaf(cur[16 * h + 7], bcast<7>(r[h]), d4[3]);
+                    d4[0] = __builtin_fmaf(cur[16 * h + 8], bcast<8>(r[h]), d4[0]);
+                    d4[1] = __builtin_fmaf(cur[16 * h + 9], bcast<9>(r[h]), d4[1]);
+                    d4[2] = __builtin_fmaf(cur[16 * h + 10], bcast<10>(r[h]), d4[2]);
+                    d4[3] = __builtin_fmaf(cur[16 * h + 11], bcast<11>(r[h]), d4[3]);
+                    d4[0] = __builtin_fmaf(cur[16 * h + 12], bcast<12>(r[h]), d4[0]);
+                    d4[1] = __builtin_fmaf(cur[16 * h + 13], bcast<13>(r[h]), d4[1]);
+                    d4[2] = __builtin_fmaf(cur[16 * h + 14], bcast<14>(r[h]), d4[2]);
+                    d4[3] = __builtin_fmaf(cur[16 * h + 15], bcast<15>(r[h]), d4[3]);
                 }
                 const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-                sc = __builtin_fmaf(2.0f, dot, qself[srow * kQS + g * C + scand]);
+                const float sc = __builtin_fmaf(2.0f, dot, qself[srow * kQS + g * C + (scand < C ? scand : 0)]);
+                if (scorer) key = sc == sc ? score_key(sc) : 0x7ffffffe;   // a NaN after every number
             }
             // The least score of the row (DPP), then the row's lanes that
             // hold it (a ballot, 16 bits per row): the group keeps its pick if
             // the pick holds it (only a strictly lower score moves it), else
             // moves to the lowest candidate that does.
             const bool mine = (pmask >> g) & 1u;
-            const float m = row_min(sc);
+            const int m = row_min(key);
             const int rsh = 16 * (lane >> 4);
-            const uint32_t req = (uint32_t)(__ballot(sc == m) >> rsh) & 0xffffu;
+            const uint32_t req = (uint32_t)(__ballot(key == m) >> rsh) & 0xffffu;
             const uint32_t rcur = (uint32_t)(__ballot(mine) >> rsh) & 0xffffu;
             const bool move = req != 0u && (req & rcur) == 0u;
             const int bc = __builtin_ctz(req | 0x10000u);
-            // The row's new errors of group g (the new pick's, or the current
-            // pick's when it stays).
-            if (move ? scand == bc : mine) {
+            // A row whose pick moves writes its new errors of group g.
+            if (move && scand == bc) {
 #pragma unroll
                 for (int i4 = 0; i4 < L / 4; ++i4)
-                    *reinterpret_cast<float4*>(&enew[srow * kPR + 4 * i4]) =
+                    *reinterpret_cast<float4*>(&ecur[srow * kER + g * L + 4 * i4]) =
                         make_float4(cur[4 * i4], cur[4 * i4 + 1], cur[4 * i4 + 2], cur[4 * i4 + 3]);
             }
             if (move) pmask = (pmask & ~(1u << g)) | ((uint32_t)(scand == bc) << g);
-            // The next group's candidate vector, requested once this one's is
-            // used (a wait for this one must not wait for that).
-            load_cv(gn, nxt);
-            __syncthreads();                    // A: g decided, its errors in enew
-            // g's errors into the error columns (the product waves read them
-            // from the next step on)
-#pragma unroll
-            for (int h = 0; h < KH; ++h) {
-                const int i = scand + 16 * h;
-                ecurT[(g * L + i) * kRows + srow] = enew[srow * kPR + i];
-            }
-            __syncthreads();                    // B: part holds the rest of gn
+            // The vector of the group after next, into the registers just
+            // used (a wait for the next group's must not wait for it).
+            load_cv(g2, cur);
+            // the row's errors of g (written by this wave) before the late
+            // term of gn reads them
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            late(gn, lr);
+            __syncthreads();                    // X_g: g decided, the partial of gn ready
         };
         for (int sw = 0; sw < a.sweeps; ++sw) {
 #pragma unroll 1
             for (int g = 0; g < G; g += 2) {    // G is even
-                dstep(g, cv, cvn);
-                dstep(g + 1, cvn, cv);
+                dstep(g, cv);
+                dstep(g + 1, cvn);
             }
             if (a.trace && srow < nrows)
                 for (int g = 0; g < G; ++g)
