@@ -99,11 +99,32 @@ __device__ __forceinline__ int row_min(int v)
     return min(v, dpp_i<kXor1>(v));
 }
 
-// The value of lane j of the lane's row of 16 (DPP row broadcast).
-template <int j>
-__device__ __forceinline__ float bcast(float v)
+// d[j % 4] += (value of lane j of the row) * c[j], j = 0..15: sixteen FMAs
+// whose first operand comes by DPP row broadcast.  The leading s_nop covers
+// the wait states between a VALU write of v and its first DPP read.
+__device__ __forceinline__ void dot_row16(float v, const float* c, float (&d)[4])
 {
-    return dpp_f<0x150 + j>(v);
+    __asm__("s_nop 1\n\t"
+            "v_fmac_f32_dpp %0, %4, %5 row_newbcast:0 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %1, %4, %6 row_newbcast:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %2, %4, %7 row_newbcast:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %3, %4, %8 row_newbcast:3 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %0, %4, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %1, %4, %10 row_newbcast:5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %2, %4, %11 row_newbcast:6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %3, %4, %12 row_newbcast:7 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %0, %4, %13 row_newbcast:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %1, %4, %14 row_newbcast:9 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %2, %4, %15 row_newbcast:10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %3, %4, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %0, %4, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %1, %4, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %2, %4, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+            "v_fmac_f32_dpp %3, %4, %20 row_newbcast:15 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(d[0]), "+v"(d[1]), "+v"(d[2]), "+v"(d[3])
+            : "v"(v), "v"(c[0]), "v"(c[1]), "v"(c[2]), "v"(c[3]), "v"(c[4]), "v"(c[5]), "v"(c[6]),
+              "v"(c[7]), "v"(c[8]), "v"(c[9]), "v"(c[10]), "v"(c[11]), "v"(c[12]), "v"(c[13]),
+              "v"(c[14]), "v"(c[15]));
 }
 
 template <int L>
@@ -419,24 +440,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             {
                 float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int h = 0; h < KH; ++h) {
-                    d4[0] = __builtin_fmaf(cur[16 * h + 0], bcast<0>(r[h]), d4[0]);
-                    d4[1] = __builtin_fmaf(cur[16 * h + 1], bcast<1>(r[h]), d4[1]);
-                    d4[2] = __builtin_fmaf(cur[16 * h + 2], bcast<2>(r[h]), d4[2]);
-                    d4[3] = __builtin_fmaf(cur[16 * h + 3], bcast<3>(r[h]), d4[3]);
-                    d4[0] = __builtin_fmaf(cur[16 * h + 4], bcast<4>(r[h]), d4[0]);
-                    d4[1] = __builtin_fmaf(cur[16 * h + 5], bcast<5>(r[h]), d4[1]);
-                    d4[2] = __builtin_fmaf(cur[16 * h + 6], bcast<6>(r[h]), d4[2]);
-                    d4[3] = __builtin_fmaf(cur[16 * h + 7], bcast<7>(r[h]), d4[3]);
-                    d4[0] = __builtin_fmaf(cur[16 * h + 8], bcast<8>(r[h]), d4[0]);
-                    d4[1] = __builtin_fmaf(cur[16 * h + 9], bcast<9>(r[h]), d4[1]);
-                    d4[2] = __builtin_fmaf(cur[16 * h + 10], bcast<10>(r[h]), d4[2]);
-                    d4[3] = __builtin_fmaf(cur[16 * h + 11], bcast<11>(r[h]), d4[3]);
-                    d4[0] = __builtin_fmaf(cur[16 * h + 12], bcast<12>(r[h]), d4[0]);
-                    d4[1] = __builtin_fmaf(cur[16 * h + 13], bcast<13>(r[h]), d4[1]);
-                    d4[2] = __builtin_fmaf(cur[16 * h + 14], bcast<14>(r[h]), d4[2]);
-                    d4[3] = __builtin_fmaf(cur[16 * h + 15], bcast<15>(r[h]), d4[3]);
-                }
+                for (int h = 0; h < KH; ++h) dot_row16(r[h], &cur[16 * h], d4);
                 const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
                 const float sc = __builtin_fmaf(2.0f, dot, qself[srow * kQS + g * C + (scand < C ? scand : 0)]);
                 if (scorer) key = sc == sc ? score_key(sc) : 0x7ffffffe;   // a NaN after every number
