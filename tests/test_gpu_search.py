@@ -200,6 +200,22 @@ def test_iq1s_candidates_small_rows():
     _check_candidates(w[:4], workloads.iq1s_grid(333), imp, 1, fmt="iq1_s")
 
 
+@pytest.mark.parametrize("fmt,top_c", [("iq2_xs", 8), ("iq2_xs", 16), ("iq1_s", 8), ("iq1_s", 16),
+                                       ("iq1_m", 8)])
+def test_candidates_with_exactly_tied_choices(fmt, top_c):
+    # A choice group of zero importance in a live block: every choice costs
+    # exactly 0, so the (cost, choice) order is the choice order and the
+    # kernel leaves its once-formed ranking for the per-round selection.
+    grid = {"iq2_xs": workloads.iq2xs_grid, "iq1_s": workloads.iq1s_grid,
+            "iq1_m": workloads.iq1s_grid}[fmt]()
+    w = workloads.student_t_weight((12, 256), 41)
+    imp = workloads.lognormal_importance((256,), 42)
+    L = 256 // iq.CHOICE_GROUPS[fmt]
+    imp[L:2 * L] = 0.0
+    err, ch = _check_candidates(w, grid, imp, top_c, fmt=fmt)
+    assert np.all(ch[:, 1] == np.arange(top_c))
+
+
 def test_iq1s_candidates_zero_and_rejected_blocks():
     grid = workloads.iq1s_grid(256)
     w = workloads.normal_weight((3, 512), 36)
