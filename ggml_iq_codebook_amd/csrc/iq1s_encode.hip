@@ -192,6 +192,9 @@ __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, 
     float x[8], w[8];
     __asm__ volatile("" ::: "memory");
     src.load(zero_block, x, w);
+    float wx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wx[j] = w[j] * x[j];
     const float mk = (float)(2 * (cs & 7) + 1);
     const float dl = (cs >> 3) ? -0.25f : 0.25f;      // 2*delta
     const float bd = (cs >> 3) ? b4 : -b4;
@@ -207,7 +210,7 @@ __device__ __forceinline__ int rescan(const uint4* __restrict__ sq, int tchunk, 
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-                A = __builtin_fmaf(w[j] * x[j], q, A);
+                A = __builtin_fmaf(wx[j], q, A);
                 M = __builtin_fmaf(w[j], q, M);
                 N = __builtin_fmaf(w[j], fabsf(q), N);
             }

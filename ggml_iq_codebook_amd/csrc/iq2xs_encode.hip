@@ -607,8 +607,8 @@ __device__ __forceinline__ int rescan_wide(const float* __restrict__ sg, int chu
     return idx;
 }
 
-// The same rescan with the same keys, for the candidates' many picks: it
-// reads only q from the LDS (q^2 formed in fp32 is the table's value
+// The same rescan with the same keys, for a pick whose holder lane is known:
+// it reads only q from the LDS (q^2 formed in fp32 is the table's value
 // exactly), and it requests the four entries of a row quad before it forms
 // their keys, so a pick waits for the LDS kNV/4 times rather than kNV times.
 template <int kCT, int kNV>
@@ -899,10 +899,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
             if (!tie) {
                 const int hs = (om < lm) ? (hl ^ 1) : hl;             // holder half
                 const int tch = __shfl(tchunk, g + 32 * hs);
-                if constexpr (kCand)
-                    idx = rescan_quads<kCT, 8>(sgrid, tch, hs, 8 * hl, k, wxs, w, inv_d, &key);
-                else
-                    idx = rescan_wide<kCT, 8>(sgrid, tch, hs, 8 * hl, k, wxs, w, inv_d, &key);
+                idx = rescan_quads<kCT, 8>(sgrid, tch, hs, 8 * hl, k, wxs, w, inv_d, &key);
                 const float ok = __shfl_xor(key, 32);
                 const int oi = __shfl_xor(idx, 32);
                 if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }

@@ -131,7 +131,8 @@ def _search_parity(H, cand, sweeps=2):
     return trace, rtrace, len(differ)
 
 
-@pytest.mark.parametrize("G,C,rows", [(16, 8, 37), (8, 4, 20), (16, 16, 9), (8, 16, 11), (16, 1, 5)])
+@pytest.mark.parametrize("G,C,rows", [(16, 8, 37), (8, 4, 20), (16, 16, 9), (8, 16, 11), (16, 1, 5),
+                                      (16, 3, 23), (8, 5, 13), (16, 12, 18)])
 def test_choice_search_random_candidates(G, C, rows):
     H = workloads.block_hessian(256, 7)
     rng = np.random.default_rng(G * 100 + C)
