@@ -1085,39 +1085,44 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
                 used |= 1 << kr;
                 int msk = neg2 & 0x7f;
                 if (zero_scale) { idx = 0; msk = 0; }
-                if (hl == 0) {
+                {
+                    // The two lanes of the column write four errors each
+                    // (elements 4*hl .. 4*hl+3 of the group).
                     const int64_t base = (blk * 16 + m) * C + r;     // [block][m][r]
-                    float ev[8];
+                    const int j0 = 4 * hl;
+                    float xq[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) xq[jj] = hl ? xo[4 + jj] : xo[jj];
+                    float ev[4];
                     if (bad_block) {
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) ev[j] = 0.0f;
+                        for (int jj = 0; jj < 4; ++jj) ev[jj] = 0.0f;
                     } else if (grid_exact) {
                         // xhat exact in fp32: d*(2k+1) has at most 16
                         // significant bits and a bf16-exact q at most 8, so
                         // the product has at most 24; one rounding of xhat - x.
                         const float sk = d * (float)(2 * kr + 1);
-                        const float* q = sgrid + entry_off<kCh>(idx);
+                        const float* q = sgrid + entry_off<kCh>(idx) + j0;
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float sg = (!zero_scale && ((neg2 >> j) & 1)) ? -sk : sk;
-                            ev[j] = sg * q[j] - xo[j];
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const float sg = (!zero_scale && ((neg2 >> (j0 + jj)) & 1)) ? -sk : sk;
+                            ev[jj] = sg * q[jj] - xq[jj];
                         }
                     } else {
                         // xhat in fp64 (exact: d*(2k+1) has at most 16
                         // significant bits), one rounding of xhat - x to fp32.
                         const double sk = (double)d * (double)(2 * kr + 1);
-                        const float* q = sgrid + entry_off<kCh>(idx);
+                        const float* q = sgrid + entry_off<kCh>(idx) + j0;
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const double sg = (!zero_scale && ((neg2 >> j) & 1)) ? -sk : sk;
-                            ev[j] = (float)(sg * (double)q[j] - (double)xo[j]);
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const double sg = (!zero_scale && ((neg2 >> (j0 + jj)) & 1)) ? -sk : sk;
+                            ev[jj] = (float)(sg * (double)q[jj] - (double)xq[jj]);
                         }
                     }
-                    float4* ep = reinterpret_cast<float4*>(a.cand_err + base * 16 + h * 8);
-                    ep[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
-                    ep[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
-                    if (h == 0) a.cand_choice[base] = kr;
-                    if (a.cand_codes)
+                    reinterpret_cast<float4*>(a.cand_err + base * 16 + h * 8)[hl] =
+                        make_float4(ev[0], ev[1], ev[2], ev[3]);
+                    if (hl == 0 && h == 0) a.cand_choice[base] = kr;
+                    if (hl == 0 && a.cand_codes)
                         a.cand_codes[base * 2 + h] = bad_block ? (uint16_t)0 : (uint16_t)(idx | (msk << 9));
                 }
             }
