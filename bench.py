@@ -155,7 +155,7 @@ PROFILED = {
     "c2_every": ("iq1s_every_c2", "iq1s_encode_kernel<0, 1, 0>", _IQ1),
     "c2_fake": ("iq1s_fake_c2", "iq1s_payload_wide_kernel<0, 2, 0>", _IQ1),
     "c5": ("iq2xs_candidates_c5", "iq2xs_wide_kernel<3, 0>", _IQ2),
-    "c5_iq1s": ("iq1s_candidates_c5_iq1s", "iq1s_encode_kernel<0, 3, 0>", _IQ1),
+    "c5_iq1s": ("iq1s_candidates_c5_iq1s", "iq1s_payload_wide_kernel<0, 3, 0>", _IQ1),
     "c5_weight": ("iq2xs_candidates_c5_weight", "iq2xs_wide_kernel<3, 0>", _IQ2),
     "c2_dequant": ("dequant_iq1s_c2", DEQUANT_KERNELS["iq1_s"], DEQUANT_SOURCES),
     "c3_dequant": ("dequant_iq2xs_c3", DEQUANT_KERNELS["iq2_xs"], DEQUANT_SOURCES),

@@ -29,10 +29,10 @@
 // value-only minima (v_min3 over two entries).
 //
 // Two kernels run this search.  iq1s_payload_wide_kernel (32 x 32 tiles, a
-// wave per block, defined further down) gives the payload of both formats and
-// the IQ1_S fake quant; iq1s_encode_kernel (16 x 16 tiles, described here)
-// gives every choice, the candidates and the IQ1_M fake quant, whose many
-// picks per group rescan fewer entries per lane in this layout.
+// wave per block, defined further down) gives the payload and the top-C
+// candidates of both formats and the IQ1_S fake quant; iq1s_encode_kernel
+// (16 x 16 tiles, described here) gives every choice and the IQ1_M fake
+// quant.
 //
 // Layout: a wave owns 16 groups (half a block): matrix column j = lane%16 is
 // group j; the lane's four accumulator rows are 4*(lane/16)+r of every
@@ -261,11 +261,10 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     // Payloads staged in LDS: one per block, or one per block and choice.
     constexpr int kPayloads = kMode == kModeEvery ? kChoices : 1;
     constexpr int kChunkTiles = chunk_tiles<kFmt, kMode>();
-    // The modes that pick several choices per group keep each wave's half
-    // block in LDS for their rescans (measured: candidates 5 % faster); the
-    // payload and fake-quant modes read global memory again, which kept their
-    // sweep's code as it was (the staging variant cost the c2 payload 3 %).
-    constexpr bool kStage = kMode == kModeEvery || kMode == kModeCandidates;
+    // Every choice picks 8 or 16 choices per group and keeps each wave's
+    // half block in LDS for its rescans; fake quant reads global memory
+    // again (one pick per group).
+    constexpr bool kStage = kMode == kModeEvery;
     constexpr int kChunk = kTile * kChunkTiles;
     // Entry e sits at e + e/kChunk: one spare slot per chunk, so the lanes of
     // a rescan that read different chunks (a multiple of the 64 banks apart
@@ -278,10 +277,6 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     // Per wave, its half block's values and weights as fp32 (32 + 32 float4),
     // read back by the rescans instead of global memory (kStage modes).
     __shared__ float4 sxw_all[kStage ? kWavesPerWG * 64 : 1];
-    // Candidates: per wave and choice unit, the choices and their costs in
-    // (cost, choice) order (4 sub-blocks x 16 or 8 scale groups x 8 per wave).
-    __shared__ float srank_cost[kMode == kModeCandidates ? kWavesPerWG * 64 : 1];
-    __shared__ uint8_t srank_c[kMode == kModeCandidates ? kWavesPerWG * 64 : 1];
     __shared__ int sgrid_bad;
     uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
 
@@ -293,8 +288,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
     const int npad = nchunks * kChunk;
 
     if (tid == 0) sgrid_bad = 0;
-    if (kMode != kModeCandidates)
-        for (int i = tid; i < kPayloads * kBlocksPerWG * kBB / 2; i += kThreads) sout16[i] = 0;
+    for (int i = tid; i < kPayloads * kBlocksPerWG * kBB / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     // Stage the grid as bf16 (exact for ternary values); entries past the end
     // repeat the last one, which always comes first in index order.
@@ -560,158 +554,17 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
         const bool refine = kDecides && __ballot(near) != 0;      // wave-uniform
         int idx_alt = 0;
         double err_alt = 0.0;
-        // Candidates: the top_c choices by (cost, choice); with a zero scale
-        // every choice decodes to zero with entry 0, so the order is 0, 1, ...
         const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
-        const bool zero_scale = !rejected && dh == 0u;
-        int used = 0;
 
-        // The entry of this group under its (k, shift) choice cs: the lane
-        // rescans its entries of the chunk that holds its minimum of cs, then
-        // the lane of the column whose matrix-core minimum is least is kept.
-        auto pick_entry = [&](int cs) -> int {
-            float lane_min = best[0];
-#pragma unroll
-            for (int c = 1; c < 16; ++c)
-                if (cs == c) lane_min = best[c];
-            const int tchunk = (int)((chunk_of[cs >> 3] >> (4 * (cs & 7))) & 0xfu);
-            // The lane of the column whose matrix-core minimum is least holds
-            // the entry.  Unless two lanes of some column hold equal minima,
-            // the four lanes split that lane's entries of its chunk between
-            // them (kChunkTiles/4 tiles each) and keep the least key, lowest
-            // entry on equal keys; with equal minima every lane rescans its own
-            // entries and the lane of least minimum, then lowest entry, wins.
-            float cm = fminf(lane_min, __shfl_xor(lane_min, 16));
-            cm = fminf(cm, __shfl_xor(cm, 32));
-            const uint64_t holders = (__ballot(lane_min == cm) >> col) & 0x0001000100010001ull;
-            const bool tie = __ballot(__popcll(holders) > 1) != 0;      // wave-uniform
-            int idx;
-            float key;
-            if (!tie) {
-                const int kbs = __builtin_ctzll(holders) >> 4;
-                const int tch = __shfl(tchunk, col + 16 * kbs);
-                idx = rescan<kChunkTiles>(sq, tch, kbs, kb * (kChunkTiles / 4), kChunkTiles / 4, cs,
-                                          src, zero_block, w64, b4, inv_d, &key);
-#pragma unroll
-                for (int o = 16; o <= 32; o <<= 1) {
-                    const float ok = __shfl_xor(key, o);
-                    const int oi = __shfl_xor(idx, o);
-                    if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
-                }
-            } else {
-                idx = rescan<kChunkTiles>(sq, tchunk, kb, 0, kChunkTiles, cs, src, zero_block, w64,
-                                          b4, inv_d, &key);
-#pragma unroll
-                for (int o = 16; o <= 32; o <<= 1) {
-                    const float om = __shfl_xor(lane_min, o);
-                    const int oi = __shfl_xor(idx, o);
-                    if (om < lane_min || (om == lane_min && oi < idx)) { lane_min = om; idx = oi; }
-                }
-            }
-            return idx < n ? idx : n - 1;
-        };
-        // The choice unit's fp64 error under cs with this lane's entry: its
-        // four groups (IQ1_S sub-block) or two (IQ1_M scale group), adjacent
-        // columns.
-        auto unit_err64 = [&](int cs, int idx) -> double {
-            double e = group_error64<kChunk>(src, zero_block, sq, idx, cs, d);
-            e += __shfl_xor(e, 1);
-            if (!kM) e += __shfl_xor(e, 2);
-            return e;
-        };
-        // Choice c as (k, shift): IQ1_M takes the group's own shift under k.
-        auto full = [&](int c) { return kM ? c + 8 * (int)((shbits >> c) & 1u) : c; };
 
         // For each choice to emit: this group's (k, shift) choice cs, its
         // entry (the lane rescans its entries of the chunk that holds its
         // minimum of cs, then the lane of the column whose matrix-core minimum
         // is least is kept), and the payload, decoded values or candidate.
-        const int nloop = kMode == kModeEvery ? kChoices
-                        : (kMode == kModeCandidates ? a.top_c : (refine ? 2 : 1));
-        // Candidates: the order of the unit's choices by (cost, choice),
-        // formed once.  Every lane of a choice unit (IQ1_S: 4 groups x 4
-        // lanes; IQ1_M: 2 x 4) holds the same costs; the lane of slot u ranks
-        // choice u by counting the costs below it and files the choice and
-        // its cost under its rank in the LDS.  Equal costs (or a NaN) leave
-        // the ranks short of a permutation; a wave with such a unit takes the
-        // selection below in every round instead.  A zero scale keeps the
-        // order 0, 1, ...
-        bool ordered = false;
-        const float* rc = srank_cost;
-        const uint8_t* rk8 = srank_c;
-        if constexpr (kMode == kModeCandidates) {
-            const int uslot = kM ? ((col & 1) | (kb << 1)) : ((col & 3) | (kb << 2));
-            const int ubase = wave * 64 + (kM ? (col >> 1) : (col >> 2)) * kChoices;
-            float mine = cost[0];
-#pragma unroll
-            for (int c = 1; c < kChoices; ++c)
-                if (uslot == c) mine = cost[c];
-            int rank = 0;
-#pragma unroll
-            for (int c = 0; c < kChoices; ++c) rank += cost[c] < mine ? 1 : 0;
-            if (zero_scale) rank = uslot;
-            srank_cost[ubase + rank] = mine;
-            srank_c[ubase + rank] = (uint8_t)uslot;
-            int rmask = 1 << rank;
-            rmask |= __shfl_xor(rmask, 1);
-            if (!kM) rmask |= __shfl_xor(rmask, 2);
-            rmask |= __shfl_xor(rmask, 16);
-            rmask |= __shfl_xor(rmask, 32);
-            ordered = __ballot(rmask != (1 << kChoices) - 1) == 0;   // wave-uniform
-            rc = srank_cost + ubase;
-            rk8 = srank_c + ubase;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+        const int nloop = kMode == kModeEvery ? kChoices : (refine ? 2 : 1);
         for (int it = 0; it < nloop; ++it) {
             int ch = kMode == kModeEvery ? it : cstar;
             if (refine && it == 0 && near) ch = c2;
-            if (kMode == kModeCandidates) {
-                int cr = -1;
-                float vr = 0.0f;
-                bool nr = false;
-                if (ordered) {                                  // wave-uniform
-                    cr = rk8[it];
-                    vr = rc[it];
-                    if (it + 1 < kChoices && !zero_block) nr = rc[it + 1] - vr <= 0x1p-18f * fabsf(vr);
-                }
-                if (!ordered || __ballot(nr) != 0) {            // wave-uniform
-                    const int cord = cr;
-                    cr = -1;
-#pragma unroll
-                    for (int c = 0; c < kChoices; ++c) {
-                        const bool better = zero_scale ? (cr < 0) : (cr < 0 || cost[c] < vr);
-                        if (!((used >> c) & 1) && better) { cr = c; vr = cost[c]; }
-                    }
-                    // Unused choices whose fp32 cost is within 2^-18 of the
-                    // least's magnitude are ranked again by their fp64 errors
-                    // (with their own entries), the lower choice on equal
-                    // errors, as the payload's runner-up is.
-                    uint32_t nearm = 0u;
-                    if (!zero_block) {
-#pragma unroll
-                        for (int c = 0; c < kChoices; ++c)
-                            if (!((used >> c) & 1) && c != cr && cost[c] - vr <= 0x1p-18f * fabsf(vr))
-                                nearm |= 1u << c;
-                    }
-                    if (__ballot(nearm != 0u) != 0) {           // wave-uniform
-                        double b64 = unit_err64(full(cr), pick_entry(full(cr)));
-                        for (int c = 0; c < kChoices; ++c) {
-                            if (__ballot((nearm >> c) & 1u) == 0) continue;   // wave-uniform
-                            const double e = unit_err64(full(c), pick_entry(full(c)));
-                            if (((nearm >> c) & 1u) && (e < b64 || (e == b64 && c < cr))) {
-                                b64 = e;
-                                cr = c;
-                            }
-                        }
-                    }
-                    // a pick out of the filed order ends its use
-                    if (ordered && __ballot(cr != cord) != 0) ordered = false;
-                }
-                used |= 1 << cr;
-                ch = cr;
-            }
             int cs = kM ? ch + 8 * (int)((shbits >> ch) & 1u) : ch;
             float lane_min = best[0];
 #pragma unroll
@@ -764,39 +617,6 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
                     cs = kM ? ch + 8 * (int)((shbits >> ch) & 1u) : ch;
                     idx = idx_alt;
                 }
-            }
-            if (kMode == kModeCandidates) {
-                // One lane per group writes its 8 errors xhat - x (xhat exact
-                // in fp32, one rounding), its code and, once per choice group,
-                // the choice.
-                if (zero_scale) idx = 0;
-                if (kb == 0) {
-                    const int unit = kM ? (g >> 1) : sub;
-                    const int part = kM ? (g & 1) : lq;
-                    const int64_t base = (blk * kGroups + unit) * a.top_c + it;    // [block][unit][r]
-                    float xo[8], wo[8];
-                    src.load(rejected, xo, wo);
-                    const float sk = f16_bits_to_f32(dh) * (float)(2 * (cs & 7) + 1);
-                    const float delta = (cs >> 3) ? -0.125f : 0.125f;
-                    const uint4 u = sq[idx + idx / kChunk];
-                    const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-                    float ev[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-                        ev[j] = rejected ? 0.0f : sk * (q + delta) - xo[j];
-                    }
-                    float4* ep = reinterpret_cast<float4*>(a.cand_err + base * (256 / kGroups) + part * 8);
-                    ep[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
-                    ep[1] = make_float4(ev[4], ev[5], ev[6], ev[7]);
-                    if (part == 0) a.cand_choice[base] = ch;
-                    if (a.cand_codes) {
-                        const int shc = (kM && !zero_scale) ? (cs >> 3) : 0;
-                        const uint16_t code = kM ? (uint16_t)(idx | (shc << 11)) : (uint16_t)idx;
-                        a.cand_codes[base * (kM ? 2 : 4) + part] = rejected ? (uint16_t)0 : code;
-                    }
-                }
-                continue;
             }
             // every choice: payload it; otherwise the one payload
             uint8_t* ob = sout + ((kMode == kModeEvery ? it : 0) * kBlocksPerWG + slot) * kBB;
@@ -860,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
             }
         }
     }
-    if (kMode != kModeCandidates && a.out) {
+    if (a.out) {
         // Copy the staged payloads out and clear what was copied (each word
         // by the thread that copied it) for the next set.
         __syncthreads();
@@ -884,8 +704,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// IQ1_S payload encode and fake quant in 32 x 32 matrix tiles: a wave owns a
-// whole block.
+// IQ1_S / IQ1_M payload encode, top-C candidates and IQ1_S fake quant in
+// 32 x 32 matrix tiles: a wave owns a whole block.
 //
 // v_mfma_f32_32x32x16_bf16 takes the block's 32 groups as the columns and 32
 // grid entries as the rows (the lane holds 16 of them), so each group is
@@ -899,8 +719,6 @@ __global__ __launch_bounds__(kThreads) void iq1s_encode_kernel(Iq1sArgs a)
 // ---------------------------------------------------------------------------
 constexpr int kW1Tile = 32;
 constexpr int kW1ChunkTiles = 4;                       // 128-entry chunks (16 for 2048 entries)
-constexpr int kW1Chunk = kW1Tile * kW1ChunkTiles;
-constexpr int kW1Slots = kMaxGrid + kMaxGrid / kW1Chunk;
 
 // The 8 keys (2k+1)*U + V of the lane's 16 entries for k = 0..7 folded into
 // best[kBase + k] (a tree of three-input minima).
@@ -929,7 +747,7 @@ __device__ __forceinline__ void fold_wide8(const v16f& u, const v16f& v, float (
 // values and weights.  The lane visits its entries in increasing order, so a
 // strict comparison keeps the lowest of equal keys; the entry offsets inside
 // a tile are constants of the unrolled row loop.
-template <int kNV, class GS>
+template <int kNV, int kCT, class GS>
 __device__ __forceinline__ int rescan_w1(const uint4* __restrict__ sq, int chunk, int hs, int v0,
                                          int cs, const GS& src, bool zero_block, float w64,
                                          float b4, float inv_d, float* key_out)
@@ -944,13 +762,13 @@ __device__ __forceinline__ int rescan_w1(const uint4* __restrict__ sq, int chunk
     const float dl = (cs >> 3) ? -0.25f : 0.25f;      // 2*delta
     const float bd = (cs >> 3) ? b4 : -b4;
     // entry e0 + de, de = 32*tile + 8*(i/4) + i%4 for row v0 + i; the table
-    // holds entry e at e + e/128 (one spare slot per chunk)
-    const int e0 = kW1Tile * kW1ChunkTiles * chunk + 4 * hs + 8 * (v0 >> 2);
+    // holds entry e at e + e/(32*kCT) (one spare slot per chunk of kCT tiles)
+    const int e0 = kW1Tile * kCT * chunk + 4 * hs + 8 * (v0 >> 2);
     const uint4* base = sq + e0 + chunk;
     int idx = e0;
     float vbest = __builtin_inff();
 #pragma unroll 1
-    for (int tt = 0; tt < kW1ChunkTiles; ++tt) {
+    for (int tt = 0; tt < kCT; ++tt) {
 #pragma unroll
         for (int i = 0; i < kNV; ++i) {
             const int de = 8 * (i >> 2) + (i & 3);
@@ -978,13 +796,13 @@ __device__ __forceinline__ int rescan_w1(const uint4* __restrict__ sq, int chunk
 
 // fp64 error of group g against entry e under choice cs (as group_error64,
 // with the wide kernel's table skew).
-template <class GS>
+template <int kCh, class GS>
 __device__ __forceinline__ double group_error64_w1(const GS& src, bool zero, const uint4* sq, int e,
                                                    int cs, float d)
 {
     float x[8], w[8];
     src.load(zero, x, w);
-    const uint4 u = sq[e + e / kW1Chunk];
+    const uint4 u = sq[e + e / kCh];
     const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
     const double sc = (double)d * (double)(2 * (cs & 7) + 1);
     const double delta = (cs >> 3) ? -0.125 : 0.125;
@@ -998,8 +816,8 @@ __device__ __forceinline__ double group_error64_w1(const GS& src, bool zero, con
     return err;
 }
 
-// kFmt: IQ_FMT_IQ1_S (payload or fake quant) or IQ_FMT_IQ1_M (payload);
-// kMode: kModePayload or kModeFake; kDT: the weight's iq_dtype_t.
+// kFmt: IQ_FMT_IQ1_S or IQ_FMT_IQ1_M; kMode: kModePayload, kModeFake (IQ1_S)
+// or kModeCandidates; kDT: the weight's iq_dtype_t.
 template <int kFmt, int kMode, int kDT>
 __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
 {
@@ -1009,20 +827,38 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
     constexpr int kBB = kM ? kBlockBytesM : kBlockBytes;
     constexpr int kCG = kM ? 16 : 8;         // choice groups per block
     constexpr int kNC = kM ? 8 : 16;         // choices per choice group
-    __shared__ uint4 wsp[kW1Slots];                    // (q[0..7] + 1/8)^2 as bf16
-    __shared__ uint4 wsq[kW1Slots];                    // q[0..7] as bf16
-    __shared__ uint16_t sout16[kWavesPerWG * kBB / 2];   // the set's payloads
+    // Tracking chunks of kCT tiles; more than 16 chunks take 8-bit indices.
+    // The candidates pick top_c choices per group, each a rescan of its
+    // chunk, so their chunks are 2 tiles (32 of them for 2048 entries; 14 %
+    // faster at top_c 8 than 4 tiles).  One pick per group keeps 4 tiles
+    // (2 tiles cost the payload 2 %: the tracking runs twice as often).
+    constexpr bool kCand = kMode == kModeCandidates;
+    constexpr int kCT = kCand ? 2 : kW1ChunkTiles;   // tiles per chunk
+    constexpr int kCh = kW1Tile * kCT;                // entries per chunk
+    constexpr int kSlots = kMaxGrid + kMaxGrid / kCh;
+    constexpr int kCB = kMaxGrid / kCh > 16 ? 8 : 4;  // bits of a chunk index
+    constexpr int kFPW = 32 / kCB;                    // chunk indices per word
+    constexpr int kCW = 16 / kFPW;                    // words of chunk indices
+    __shared__ uint4 wsp[kSlots];                      // (q[0..7] + 1/8)^2 as bf16
+    __shared__ uint4 wsq[kSlots];                      // q[0..7] as bf16
+    __shared__ uint16_t sout16[kCand ? 1 : kWavesPerWG * kBB / 2];   // the set's payloads
+    // candidates: each lane's 16 minima after the sweep, and per wave and
+    // choice unit the choices and their costs in (cost, choice) order
+    __shared__ float4 sbest[kCand ? 4 * kThreads : 1];   // [c/4][thread]
+    __shared__ float srank_cost[kCand ? kWavesPerWG * 128 : 1];
+    __shared__ uint8_t srank_c[kCand ? kWavesPerWG * 128 : 1];
     __shared__ int sgrid_bad;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: block pointers in SGPRs
     const int n = a.grid_size;
-    const int nchunks = (n + kW1Chunk - 1) / kW1Chunk;
-    const int npad = nchunks * kW1Chunk;
+    const int nchunks = (n + kCh - 1) / kCh;
+    const int npad = nchunks * kCh;
 
     if (tid == 0) sgrid_bad = 0;
-    for (int i = tid; i < kWavesPerWG * kBB / 2; i += kThreads) sout16[i] = 0;
+    if (!kCand)
+        for (int i = tid; i < kWavesPerWG * kBB / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     {
         const float4* gsrc = reinterpret_cast<const float4*>(a.grid);
@@ -1039,7 +875,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
                 const float pp = v[t] + 0.125f;
                 hp[t] = bf16_bits(pp * pp);        // exact: 81/64, 1/64, 49/64
             }
-            const int at = e + e / kW1Chunk;
+            const int at = e + e / kCh;
             wsq[at] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
                                  h[4] | (h[5] << 16), h[6] | (h[7] << 16));
             wsp[at] = make_uint4(hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16),
@@ -1124,7 +960,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
 
         bool choice_bad = false;
-        if (a.choices) {
+        if (!kCand && a.choices) {
             int lc = lane;                      // opaque: the address is formed here, not hoisted
             __asm__ volatile("" : "+v"(lc));
             const int cv = lc < kCG ? a.choices[blk * kCG + lc] : 0;
@@ -1159,16 +995,19 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
         const v8bf on1 = pack(n1), on2 = pack(n2), ow1 = pack(w1), ow2 = pack(w2);
         const v8bf oh1 = pack(h1), oh2 = pack(h2);
 
-        // chunk_of: 4-bit chunk index of choice c in bits 4*(c%8) of word c/8.
+        // chunk_of: kCB-bit chunk index of choice c in bits kCB*(c%kFPW) of
+        // word c/kFPW.
         float best[16], snap[16];
-        uint32_t chunk_of[2] = {0u, 0u};
+        uint32_t chunk_of[kCW];
+#pragma unroll
+        for (int i = 0; i < kCW; ++i) chunk_of[i] = 0u;
 #pragma unroll
         for (int c = 0; c < 16; ++c) { best[c] = __builtin_inff(); snap[c] = best[c]; }
         const v16f zero16 = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f,
                              0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
         for (int ch = 0; ch < nchunks; ++ch) {
-            for (int tt = 0; tt < kW1ChunkTiles; ++tt) {
-                const int at = (ch * kW1ChunkTiles + tt) * kW1Tile + g + ch;
+            for (int tt = 0; tt < kCT; ++tt) {
+                const int at = (ch * kCT + tt) * kW1Tile + g + ch;
                 const v8bf ap = as_v8bf(wsp[at]), aq = as_v8bf(wsq[at]);
                 const v16f vq = mfma32(aq, on2, mfma32(aq, on1, zero16));
                 v16f uu = mfma32(ap, ow2, mfma32(ap, ow1, zero16));
@@ -1176,13 +1015,22 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
                 uu = mfma32(aq, oh2, mfma32(aq, oh1, uu));          // U(-1/8)
                 fold_wide8<8>(uu, vq, best);
             }
-            const uint32_t chrep = (uint32_t)ch * 0x11111111u;
+            const uint32_t chrep = (uint32_t)ch * (kCB == 4 ? 0x11111111u : 0x01010101u);
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
-                const uint32_t msk = best[c] < snap[c] ? (0xfu << (4 * (c & 7))) : 0u;
-                chunk_of[c >> 3] = (chunk_of[c >> 3] & ~msk) | (chrep & msk);
+                const uint32_t msk = best[c] < snap[c] ? (((1u << kCB) - 1u) << (kCB * (c % kFPW))) : 0u;
+                chunk_of[c / kFPW] = (chunk_of[c / kFPW] & ~msk) | (chrep & msk);
                 snap[c] = best[c];
             }
+        }
+
+        // Candidates: the lane's minima go to LDS, where the picks read them,
+        // so that they need not stay live through the epilogue.
+        if constexpr (kCand) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                sbest[q4 * kThreads + tid] = make_float4(best[4 * q4], best[4 * q4 + 1],
+                                                         best[4 * q4 + 2], best[4 * q4 + 3]);
         }
 
         // Lane-derived values for the rest of the block, formed here from an
@@ -1242,30 +1090,20 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
                 if (k == 0 || cost[k] < cbest) { cbest = cost[k]; cstar = k; }
             }
         }
-        const int forced = (a.choices && !choice_bad) ? a.choices[blk * kCG + (kM ? (g2 >> 1) : sub2)] : -1;
-        if (forced >= 0) cstar = forced;
-        int c2 = 0;
-        bool near = false;
-        if (forced < 0) {                           // wave-uniform
-            float v2 = 0.0f;
-            c2 = -1;
-#pragma unroll
-            for (int c = 0; c < kNC; ++c)
-                if (c != cstar && (c2 < 0 || cost[c] < v2)) { c2 = c; v2 = cost[c]; }
-            near = !zero_block && v2 - cbest <= 0x1p-18f * fabsf(cbest);
-        }
-        const bool refine = __ballot(near) != 0;  // wave-uniform
-
         // Entry for choice cs: the lane of the column whose minimum is least
         // holds it; the two lanes split its entries of the chunk.  With equal
         // minima in the two lanes of any column, every lane rescans its own
         // entries and the lane of least minimum, then lowest entry, wins.
         auto pick = [&](int cs) -> int {
             float lm = best[0];
+            if constexpr (kCand) {
+                lm = reinterpret_cast<const float*>(sbest + (cs >> 2) * kThreads + tid)[cs & 3];
+            } else {
 #pragma unroll
-            for (int c = 1; c < 16; ++c)
-                if (cs == c) lm = best[c];
-            const int tchunk = (int)((chunk_of[cs >> 3] >> (4 * (cs & 7))) & 0xfu);
+                for (int c = 1; c < 16; ++c)
+                    if (cs == c) lm = best[c];
+            }
+            const int tchunk = (int)((chunk_of[cs / kFPW] >> (kCB * (cs % kFPW))) & ((1u << kCB) - 1u));
             const float om = __shfl(lm, ln2 ^ 32);
             const bool tie = __ballot(om == lm) != 0;                // wave-uniform
             int idx;
@@ -1273,12 +1111,14 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
             if (!tie) {
                 const int hs = (om < lm) ? (hl2 ^ 1) : hl2;             // holder half
                 const int tch = __shfl(tchunk, g2 + 32 * hs);
-                idx = rescan_w1<8>(wsq, tch, hs, 8 * hl2, cs, src2, zero_block, w64, b4, inv_d, &key);
+                idx = rescan_w1<8, kCT>(wsq, tch, hs, 8 * hl2, cs, src2, zero_block, w64, b4, inv_d,
+                                        &key);
                 const float ok = __shfl(key, ln2 ^ 32);
                 const int oi = __shfl(idx, ln2 ^ 32);
                 if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
             } else {
-                idx = rescan_w1<16>(wsq, tchunk, hl2, 0, cs, src2, zero_block, w64, b4, inv_d, &key);
+                idx = rescan_w1<16, kCT>(wsq, tchunk, hl2, 0, cs, src2, zero_block, w64, b4, inv_d,
+                                         &key);
                 const int oi = __shfl(idx, ln2 ^ 32);
                 if (om < lm || (om == lm && oi < idx)) idx = oi;
             }
@@ -1287,93 +1127,234 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
 
         // IQ1_M: the (k, shift) choice of this group under its scale group's k
         auto full = [&](int k) { return kM ? k + 8 * (int)((shbits >> k) & 1u) : k; };
-        int ch = cstar;
-        int cs = full(cstar);
-        int idx;
-        if (!refine) {
-            idx = pick(cs);
-        } else {
-            // The runner-up within 2^-18 of the best: both in fp64 from the
-            // error's definition, summed over the sub-block; the lower error
-            // wins, the lower choice on equal errors.
-            const int cs2 = full(near ? c2 : cstar);
-            const int i2 = pick(cs2);
-            const int i1 = pick(cs);
-            double e2 = group_error64_w1(src2, zero_block, wsq, i2, cs2, d);
-            double e1 = group_error64_w1(src2, zero_block, wsq, i1, cs, d);
-            e2 += quad_xchg<kQuadXor1>(e2);
-            e1 += quad_xchg<kQuadXor1>(e1);
-            if (!kM) {
-                e2 += quad_xchg<kQuadXor2>(e2);
-                e1 += quad_xchg<kQuadXor2>(e1);
+        if constexpr (kCand) {
+            // Candidates: the unit's top_c choices by (cost, choice), formed
+            // once.  Every lane of a choice unit (IQ1_S: 4 groups x 2 halves;
+            // IQ1_M: 2 x 2) holds the same costs; the lane of slot u ranks
+            // choices 2u and 2u+1 by counting the costs below each and files
+            // each choice and its cost under its rank in the LDS.  Equal costs
+            // (or a NaN) leave the ranks short of a permutation; a wave with
+            // such a unit takes the selection below in every round instead.
+            // With a zero scale every choice decodes to zero with entry 0, so
+            // the order is 0, 1, ...
+            const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
+            const bool zero_scale = !rejected && dh == 0u;
+            const int unit = kM ? (g2 >> 1) : sub2;
+            const int part = kM ? (g2 & 1) : lq2;
+            const int uslot = kM ? ((g2 & 1) | (hl2 << 1)) : (lq2 | (hl2 << 2));
+            const int ubase = wave * 128 + unit * kNC;
+            int rmask = 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int uc = 2 * uslot + i;
+                float mine = cost[0];
+#pragma unroll
+                for (int c = 1; c < kNC; ++c)
+                    if (uc == c) mine = cost[c];
+                int rank = 0;
+#pragma unroll
+                for (int c = 0; c < kNC; ++c) rank += cost[c] < mine ? 1 : 0;
+                if (zero_scale) rank = uc;
+                srank_cost[ubase + rank] = mine;
+                srank_c[ubase + rank] = (uint8_t)uc;
+                rmask |= 1 << rank;
             }
-            idx = i1;
-            if (near && (e2 < e1 || (e2 == e1 && c2 < cstar))) { ch = c2; cs = cs2; idx = i2; }
-        }
+            rmask |= quad_xchg<kQuadXor1>(rmask);
+            if (!kM) rmask |= quad_xchg<kQuadXor2>(rmask);
+            rmask |= __shfl(rmask, ln2 ^ 32);
+            bool ordered = __ballot(rmask != (1 << kNC) - 1) == 0;     // wave-uniform
+            const float* rc = srank_cost + ubase;
+            const uint8_t* rk8 = srank_c + ubase;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        if (kM) {
-            // IQ1_M: low byte per group; one nibble per group (3 high bits,
-            // shift bit); four scale words with the 3-bit local scales of four
-            // scale groups and one nibble of d each.
-            const int nib = ((idx >> 8) & 7) | ((cs >> 3) << 3);
-            const int nib_odd = quad_xchg<kQuadXor1>(nib);
-            int kk = (ch & 7) << (3 * ((g2 >> 1) & 3));
-            kk |= quad_xchg<kQuadXor2>(kk);
-            kk |= __shfl(kk, ln2 ^ 4);
-            if (!zero_block && hl2 == 0) {
-                uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBB;
-                ob[g2] = (uint8_t)(idx & 0xff);
-                if ((g2 & 1) == 0) ob[32 + (g2 >> 1)] = (uint8_t)(nib | (nib_odd << 4));
-                if ((g2 & 7) == 0) {
-                    const int wd = g2 >> 3;
-                    const uint32_t v = (uint32_t)kk | (((dh >> (4 * wd)) & 0xfu) << 12);
-                    ob[48 + 2 * wd] = (uint8_t)(v & 0xff);
-                    ob[49 + 2 * wd] = (uint8_t)(v >> 8);
+            // The unit's fp64 error under cs with this lane's entry: its four
+            // groups (IQ1_S sub-block) or two (IQ1_M scale group).
+            auto unit_err64 = [&](int cs, int idx) -> double {
+                double e = group_error64_w1<kCh>(src2, zero_block, wsq, idx, cs, d);
+                e += quad_xchg<kQuadXor1>(e);
+                if (!kM) e += quad_xchg<kQuadXor2>(e);
+                return e;
+            };
+            uint32_t used = 0u;
+            for (int it = 0; it < a.top_c; ++it) {
+                int cr = -1;
+                float vr = 0.0f;
+                bool nr = false;
+                if (ordered) {                                  // wave-uniform
+                    cr = rk8[it];
+                    vr = rc[it];
+                    if (it + 1 < kNC && !zero_block) nr = rc[it + 1] - vr <= 0x1p-18f * fabsf(vr);
+                }
+                if (!ordered || __ballot(nr) != 0) {            // wave-uniform
+                    const int cord = cr;
+                    cr = -1;
+#pragma unroll
+                    for (int c = 0; c < kNC; ++c) {
+                        const bool better = zero_scale ? (cr < 0) : (cr < 0 || cost[c] < vr);
+                        if (!((used >> c) & 1u) && better) { cr = c; vr = cost[c]; }
+                    }
+                    // Unused choices whose fp32 cost is within 2^-18 of the
+                    // least's magnitude are ranked again by their fp64 errors
+                    // (with their own entries), the lower choice on equal
+                    // errors, as the payload's runner-up is.
+                    uint32_t nearm = 0u;
+                    if (!zero_block) {
+#pragma unroll
+                        for (int c = 0; c < kNC; ++c)
+                            if (!((used >> c) & 1u) && c != cr && cost[c] - vr <= 0x1p-18f * fabsf(vr))
+                                nearm |= 1u << c;
+                    }
+                    if (__ballot(nearm != 0u) != 0) {           // wave-uniform
+                        double b64 = unit_err64(full(cr), pick(full(cr)));
+                        for (int c = 0; c < kNC; ++c) {
+                            if (__ballot((nearm >> c) & 1u) == 0) continue;   // wave-uniform
+                            const double e = unit_err64(full(c), pick(full(c)));
+                            if (((nearm >> c) & 1u) && (e < b64 || (e == b64 && c < cr))) {
+                                b64 = e;
+                                cr = c;
+                            }
+                        }
+                    }
+                    // a pick out of the filed order ends its use
+                    if (ordered && __ballot(cr != cord) != 0) ordered = false;
+                }
+                used |= 1u << cr;
+                const int cs = full(cr);
+                int idx = pick(cs);
+                if (zero_scale) idx = 0;
+                // Each lane of a group writes 4 of its 8 errors xhat - x
+                // (xhat exact in fp32, one rounding); the first half also its
+                // code and, once per unit, the choice.
+                const int64_t base = (blk * kCG + unit) * a.top_c + it;    // [block][unit][r]
+                float xo[8], wo[8];
+                src2.load(rejected, xo, wo);
+                const float sk = f16_bits_to_f32(dh) * (float)(2 * (cs & 7) + 1);
+                const float delta = (cs >> 3) ? -0.125f : 0.125f;
+                const uint4 u = wsq[idx + idx / kCh];
+                const uint32_t u0 = hl2 ? u.z : u.x, u1 = hl2 ? u.w : u.y;
+                const uint32_t uu[4] = {u0 & 0xffffu, u0 >> 16, u1 & 0xffffu, u1 >> 16};
+                float ev[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float xj = hl2 ? xo[4 + j] : xo[j];
+                    ev[j] = rejected ? 0.0f : sk * (bf16_to_f32(uu[j]) + delta) - xj;
+                }
+                float4* ep = reinterpret_cast<float4*>(a.cand_err + base * (256 / kCG) + part * 8 + 4 * hl2);
+                ep[0] = make_float4(ev[0], ev[1], ev[2], ev[3]);
+                if (hl2 == 0) {
+                    if (part == 0) a.cand_choice[base] = cr;
+                    if (a.cand_codes) {
+                        const int shc = (kM && !zero_scale) ? (cs >> 3) : 0;
+                        const uint16_t code = kM ? (uint16_t)(idx | (shc << 11)) : (uint16_t)idx;
+                        a.cand_codes[base * (kM ? 2 : 4) + part] = rejected ? (uint16_t)0 : code;
+                    }
                 }
             }
-        }
-        // IQ1_S: low byte per group, qh word per sub-block, d per block.
-        int hi = ((idx >> 8) & 7) << (3 * lq2);
-        hi |= quad_xchg<kQuadXor1>(hi);
-        hi |= quad_xchg<kQuadXor2>(hi);
-        if (!kM && !zero_block && hl2 == 0) {
-            uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBB;
-            ob[2 + g2] = (uint8_t)(idx & 0xff);
-            if (lq2 == 0) {
-                const uint32_t qh = (uint32_t)hi | ((uint32_t)cs << 12);
-                ob[34 + 2 * sub2] = (uint8_t)(qh & 0xff);
-                ob[35 + 2 * sub2] = (uint8_t)(qh >> 8);
+        } else {
+            const int forced = (a.choices && !choice_bad) ? a.choices[blk * kCG + (kM ? (g2 >> 1) : sub2)] : -1;
+            if (forced >= 0) cstar = forced;
+            int c2 = 0;
+            bool near = false;
+            if (forced < 0) {                           // wave-uniform
+                float v2 = 0.0f;
+                c2 = -1;
+    #pragma unroll
+                for (int c = 0; c < kNC; ++c)
+                    if (c != cstar && (c2 < 0 || cost[c] < v2)) { c2 = c; v2 = cost[c]; }
+                near = !zero_block && v2 - cbest <= 0x1p-18f * fabsf(cbest);
             }
-            if (g2 == 0) {
-                ob[0] = (uint8_t)(dh & 0xff);
-                ob[1] = (uint8_t)(dh >> 8);
+            const bool refine = __ballot(near) != 0;  // wave-uniform
+
+            int ch = cstar;
+            int cs = full(cstar);
+            int idx;
+            if (!refine) {
+                idx = pick(cs);
+            } else {
+                // The runner-up within 2^-18 of the best: both in fp64 from the
+                // error's definition, summed over the sub-block; the lower error
+                // wins, the lower choice on equal errors.
+                const int cs2 = full(near ? c2 : cstar);
+                const int i2 = pick(cs2);
+                const int i1 = pick(cs);
+                double e2 = group_error64_w1<kCh>(src2, zero_block, wsq, i2, cs2, d);
+                double e1 = group_error64_w1<kCh>(src2, zero_block, wsq, i1, cs, d);
+                e2 += quad_xchg<kQuadXor1>(e2);
+                e1 += quad_xchg<kQuadXor1>(e1);
+                if (!kM) {
+                    e2 += quad_xchg<kQuadXor2>(e2);
+                    e1 += quad_xchg<kQuadXor2>(e1);
+                }
+                idx = i1;
+                if (near && (e2 < e1 || (e2 == e1 && c2 < cstar))) { ch = c2; cs = cs2; idx = i2; }
             }
-        }
-        if (kMode == kModeFake && hl2 == 0) {
-            // The decoded group, d*(2k+1)*(q + delta) with the payload's
-            // fields, the expression the decode kernel uses (a zero block
-            // decodes as the all-zero payload does; a rejected block is
-            // written as zeros).
-            const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
-            const uint32_t dz = zero_block ? 0u : dh;
-            const int ez = zero_block ? 0 : idx;
-            const int cz = zero_block ? 0 : cs;
-            const float sk = f16_bits_to_f32(dz) * (float)(2 * (cz & 7) + 1);
-            const float delta = (cz >> 3) ? -0.125f : 0.125f;
-            const uint4 u = wsq[ez + ez / kW1Chunk];
-            const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-            float v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
-                v[j] = rejected ? 0.0f : sk * (q + delta);
+
+            if (kM) {
+                // IQ1_M: low byte per group; one nibble per group (3 high bits,
+                // shift bit); four scale words with the 3-bit local scales of four
+                // scale groups and one nibble of d each.
+                const int nib = ((idx >> 8) & 7) | ((cs >> 3) << 3);
+                const int nib_odd = quad_xchg<kQuadXor1>(nib);
+                int kk = (ch & 7) << (3 * ((g2 >> 1) & 3));
+                kk |= quad_xchg<kQuadXor2>(kk);
+                kk |= __shfl(kk, ln2 ^ 4);
+                if (!zero_block && hl2 == 0) {
+                    uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBB;
+                    ob[g2] = (uint8_t)(idx & 0xff);
+                    if ((g2 & 1) == 0) ob[32 + (g2 >> 1)] = (uint8_t)(nib | (nib_odd << 4));
+                    if ((g2 & 7) == 0) {
+                        const int wd = g2 >> 3;
+                        const uint32_t v = (uint32_t)kk | (((dh >> (4 * wd)) & 0xfu) << 12);
+                        ob[48 + 2 * wd] = (uint8_t)(v & 0xff);
+                        ob[49 + 2 * wd] = (uint8_t)(v >> 8);
+                    }
+                }
             }
-            float4* o = reinterpret_cast<float4*>(a.xhat + blk * kBlockElems + g2 * 8);
-            o[0] = make_float4(v[0], v[1], v[2], v[3]);
-            o[1] = make_float4(v[4], v[5], v[6], v[7]);
+            // IQ1_S: low byte per group, qh word per sub-block, d per block.
+            int hi = ((idx >> 8) & 7) << (3 * lq2);
+            hi |= quad_xchg<kQuadXor1>(hi);
+            hi |= quad_xchg<kQuadXor2>(hi);
+            if (!kM && !zero_block && hl2 == 0) {
+                uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + wave * kBB;
+                ob[2 + g2] = (uint8_t)(idx & 0xff);
+                if (lq2 == 0) {
+                    const uint32_t qh = (uint32_t)hi | ((uint32_t)cs << 12);
+                    ob[34 + 2 * sub2] = (uint8_t)(qh & 0xff);
+                    ob[35 + 2 * sub2] = (uint8_t)(qh >> 8);
+                }
+                if (g2 == 0) {
+                    ob[0] = (uint8_t)(dh & 0xff);
+                    ob[1] = (uint8_t)(dh >> 8);
+                }
+            }
+            if (kMode == kModeFake && hl2 == 0) {
+                // The decoded group, d*(2k+1)*(q + delta) with the payload's
+                // fields, the expression the decode kernel uses (a zero block
+                // decodes as the all-zero payload does; a rejected block is
+                // written as zeros).
+                const bool rejected = grid_bad || block_bad || scale_bad || choice_bad;
+                const uint32_t dz = zero_block ? 0u : dh;
+                const int ez = zero_block ? 0 : idx;
+                const int cz = zero_block ? 0 : cs;
+                const float sk = f16_bits_to_f32(dz) * (float)(2 * (cz & 7) + 1);
+                const float delta = (cz >> 3) ? -0.125f : 0.125f;
+                const uint4 u = wsq[ez + ez / kCh];
+                const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+                float v[8];
+    #pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                    v[j] = rejected ? 0.0f : sk * (q + delta);
+                }
+                float4* o = reinterpret_cast<float4*>(a.xhat + blk * kBlockElems + g2 * 8);
+                o[0] = make_float4(v[0], v[1], v[2], v[3]);
+                o[1] = make_float4(v[4], v[5], v[6], v[7]);
+            }
         }
     }
-    if (a.out) {
+    if (!kCand && a.out) {
         // Copy the set's payloads out and clear what was copied (each word by
         // the thread that copied it) for the next set.
         __syncthreads();
@@ -1398,8 +1379,8 @@ hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
     // 16 blocks when there are fewer sets.
     const int64_t sets = (a.g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
     const dim3 grid((unsigned)(sets < a.g.cus ? sets : a.g.cus));
-    // The payload (both formats) and IQ1_S fake quant run the 32 x 32 kernel;
-    // every choice, candidates and IQ1_M fake quant the 16 x 16 one.
+    // The payload and candidates (both formats) and IQ1_S fake quant run the
+    // 32 x 32 kernel; every choice and IQ1_M fake quant the 16 x 16 one.
     if (mode == kModeEvery) {
         hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeEvery, kDT>), grid, dim3(kThreads), 0,
                            stream, a);
@@ -1411,8 +1392,8 @@ hipError_t launch_fmt(const Iq1sArgs& a, int mode, hipStream_t stream)
             hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeFake, kDT>), grid, dim3(kThreads), 0,
                                stream, a);
     } else if (mode == kModeCandidates) {
-        hipLaunchKernelGGL((iq1s_encode_kernel<kFmt, kModeCandidates, kDT>), grid, dim3(kThreads),
-                           0, stream, a);
+        hipLaunchKernelGGL((iq1s_payload_wide_kernel<kFmt, kModeCandidates, kDT>), grid,
+                           dim3(kThreads), 0, stream, a);
     } else {
         hipLaunchKernelGGL((iq1s_payload_wide_kernel<kFmt, kModePayload, kDT>), grid,
                            dim3(kThreads), 0, stream, a);
