@@ -1260,7 +1260,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
             if (forced < 0) {                           // wave-uniform
                 float v2 = 0.0f;
                 c2 = -1;
-    #pragma unroll
+#pragma unroll
                 for (int c = 0; c < kNC; ++c)
                     if (c != cstar && (c2 < 0 || cost[c] < v2)) { c2 = c; v2 = cost[c]; }
                 near = !zero_block && v2 - cbest <= 0x1p-18f * fabsf(cbest);
@@ -1343,7 +1343,7 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
                 const uint4 u = wsq[ez + ez / kCh];
                 const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
                 float v[8];
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float q = bf16_to_f32((uu[j >> 1] >> (16 * (j & 1))) & 0xffffu);
                     v[j] = rejected ? 0.0f : sk * (q + delta);
