@@ -152,7 +152,7 @@ PROFILED = {
     "c4": ("iq1s_encode_c4", KERNEL_NAMES["iq1_s"], _IQ1),
     "c2_pinned": ("iq1s_encode_c2_pinned", KERNEL_NAMES["iq1_s"], _IQ1),
     "c2_iq1m": ("iq1m_encode_c2_iq1m", KERNEL_NAMES["iq1_m"], _IQ1),
-    "c2_every": ("iq1s_every_c2", "iq1s_encode_kernel<0, 1, 0>", _IQ1),
+    "c2_every": ("iq1s_every_c2", "iq1s_payload_wide_kernel<0, 1, 0>", _IQ1),
     "c2_fake": ("iq1s_fake_c2", "iq1s_payload_wide_kernel<0, 2, 0>", _IQ1),
     "c5": ("iq2xs_candidates_c5", "iq2xs_wide_kernel<3, 0>", _IQ2),
     "c5_iq1s": ("iq1s_candidates_c5_iq1s", "iq1s_payload_wide_kernel<0, 3, 0>", _IQ1),
