@@ -1,6 +1,7 @@
 // iq2xs_encode.hip -- importance-weighted codebook search for IQ2_XS on
-// gfx950, with two epilogues: the packed payload, and the top-C candidates
-// that feed the local-Hessian choice search.
+// gfx950, with the epilogues of every output: the packed payload, the payload
+// under every choice, the fake quant, and the top-C candidates that feed the
+// local-Hessian choice search.
 //
 // The format (NVIDIA Model-Optimizer, "Add IQ tests and release notes" #2450,
 // code review; "Register each GGML IQ format once" #2525, IQ2_S commit body,
@@ -26,19 +27,15 @@
 // is (2k+1)*N - 2P/d: one FMA with a literal multiplier; the choice cost of a
 // scale group is (2k+1) times the sum of its two groups' minima.
 //
-// Two kernels.  iq2xs_wide_kernel (the payload, the fake quant and the
-// candidates) runs 32 x 32 matrix tiles, v_mfma_f32_32x32x16_bf16, with a
-// wave per block: matrix column = group, two lanes per column, each holding
-// 16 entries of every 32-entry tile.  iq2xs_every_kernel (the payload under
-// every choice) runs 16 x 16 tiles with a wave per half block: column j =
-// lane%16 is group j, the lane's accumulator rows are entries 4*(lane/16)+r
-// of each 16-entry tile.  Both run persistent 1024-thread workgroups (one per
-// CU) that stage the grid once in LDS (q and q^2 as bf16 operands, and a
-// padded fp32 copy for the rescans).  Value-only minima (v_min3); each lane
-// records the chunk that last lowered each minimum; the lane of each column
-// whose matrix-core minimum is least is found, and the lanes of the column
-// split its entries of that chunk and rescan them on the VALU (lowest entry
-// of least key).
+// One kernel, iq2xs_wide_kernel, runs every output in 32 x 32 matrix tiles,
+// v_mfma_f32_32x32x16_bf16, with a wave per block: matrix column = group, two
+// lanes per column, each holding 16 entries of every 32-entry tile.
+// Persistent 1024-thread workgroups (one per CU) stage the grid once in LDS
+// (q and q^2 as bf16 operands, and a padded fp32 copy for the rescans).
+// Value-only minima (v_min3); each lane records the chunk that last lowered
+// each minimum; the lane of each column whose matrix-core minimum is least is
+// found, and the two lanes of the column split its entries of that chunk and
+// rescan them on the VALU (lowest entry of least key).
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -47,14 +44,9 @@
 namespace iqk {
 namespace {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerWG = 16;
 constexpr int kThreads = kWave * kWavesPerWG;        // 1024
-constexpr int kBlocksPerPass = kWavesPerWG / 2;
-constexpr int kPasses = 2;
-constexpr int kBlocksPerWG = kBlocksPerPass * kPasses;   // 16
-constexpr int kTile = 16;
 constexpr int kMaxGrid = 512;
 constexpr int kBlockBytes = 74;
 
@@ -127,35 +119,6 @@ __device__ __forceinline__ bool bf16_exact_with_square(float v)
     return range && bf16_to_f32(bf16_bits(v)) == v && bf16_to_f32(bf16_bits(v2)) == v2;
 }
 
-// One matrix tile of P' = -2P/d and N: the 16 keys (2k+1)*N + P' of the
-// lane's 4 entries folded into the running minima.
-__device__ __forceinline__ void fold_tile(const v4f& pn, const v4f& nn, float (&best)[16])
-{
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const float mk = (float)(2 * k + 1);
-        const float k0 = __builtin_fmaf(nn[0], mk, pn[0]);
-        const float k1 = __builtin_fmaf(nn[1], mk, pn[1]);
-        const float k2 = __builtin_fmaf(nn[2], mk, pn[2]);
-        const float k3 = __builtin_fmaf(nn[3], mk, pn[3]);
-        best[k] = fminf(best[k], fminf(fminf(fminf(k0, k1), k2), k3));
-    }
-}
-
-// After chunk ch: record ch (4 bits at bits 4*(k%8) of word k/8) for every
-// minimum that it lowered.
-__device__ __forceinline__ void track_chunk(int ch, const float (&best)[16], float (&snap)[16],
-                                            uint32_t (&chunk_of)[2])
-{
-    const uint32_t chrep = (uint32_t)ch * 0x11111111u;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const uint32_t msk = best[k] < snap[k] ? (0xfu << (4 * (k & 7))) : 0u;
-        chunk_of[k >> 3] = (chunk_of[k >> 3] & ~msk) | (chrep & msk);
-        snap[k] = best[k];
-    }
-}
-
 // Weighted squared error of a group against s*sign*q in fp64, from its
 // definition: sum of w*(x - s*sign*q)^2.
 __device__ __forceinline__ double group_error64(const float (&x)[8], const float (&w)[8], int neg,
@@ -172,8 +135,7 @@ __device__ __forceinline__ double group_error64(const float (&x)[8], const float
 }
 
 // Per-entry fp32 copy of the grid for the VALU rescans: q[0..7], q^2[0..7],
-// padded to 18 floats so the four entries the four lanes of a column read
-// together (4 apart) fall in different LDS banks.
+// padded to 18 floats (at 16, entries 4 apart would share their LDS banks).
 constexpr int kEntryStride = 18;
 // Tracking chunks are 32 or 64 entries, a multiple of the 64 LDS banks apart
 // at that stride, so lanes rescanning different chunks would all hit the same
@@ -182,339 +144,21 @@ constexpr int kEntryStride = 18;
 template <int kChunk>
 __device__ __forceinline__ int entry_off(int e) { return kEntryStride * e + 2 * (e / kChunk); }
 
-// VALU rescan for local scale k: positions p0 .. p0+np-1 of the entries one
-// lane of a column covers in chunk `chunk` (position p = tile p/4 of the
-// chunk, row 4*kbs + p%4): the lowest entry with the least key
-// (2k+1)*N - 2P/d.  Returns the entry, writes its key.
-template <int kChunkTiles>
-__device__ __forceinline__ int rescan(const float* __restrict__ sg, int chunk, int kbs, int p0,
-                                      int np, int k, const float (&wxs)[8], const float (&w)[8],
-                                      float inv_d, float* key_out)
-{
-    const float mk = (float)(2 * k + 1);
-    int idx = -1;
-    float vbest = 0.0f;
-    for (int pp = p0; pp < p0 + np; ++pp) {
-        const int e = (chunk * kChunkTiles + (pp >> 2)) * kTile + 4 * kbs + (pp & 3);
-        const float2* p = reinterpret_cast<const float2*>(sg + entry_off<kChunkTiles * kTile>(e));
-        float q[8], q2[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const float2 u = p[t], v = p[4 + t];
-            q[2 * t] = u.x; q[2 * t + 1] = u.y;
-            q2[2 * t] = v.x; q2[2 * t + 1] = v.y;
-        }
-        float P = 0.0f, N = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            P = __builtin_fmaf(wxs[j], q[j], P);
-            N = __builtin_fmaf(w[j], q2[j], N);
-        }
-        const float key = __builtin_fmaf(N, mk, (-2.0f * P) * inv_d);
-        if (idx < 0 || key < vbest) { vbest = key; idx = e; }
-    }
-    *key_out = vbest;
-    return idx;
-}
-
-// The every-choice output (16 payloads per block); kDT: the weight's
-// iq_dtype_t.
-template <int kDT>
-__global__ __launch_bounds__(kThreads) void iq2xs_every_kernel(Iq2xsArgs a)
-{
-    constexpr int kPayloads = 16;
-    // Tiles per tracking chunk.  Recording chunks costs the sweep about 4
-    // instructions per choice and chunk; each of the 16 picks rescans one
-    // lane's entries of a chunk, 4 per tile: 2 tiles (32 entries).
-    constexpr int kChunkTiles = 2;
-    constexpr int kChunk = kTile * kChunkTiles;
-
-    __shared__ float sgrid[kMaxGrid * kEntryStride + 2 * (kMaxGrid / 32)];  // q[0..7], q^2[0..7]
-    __shared__ float2 sq[kMaxGrid * 4];                 // entry e, slice kb: (q[kb], q[kb+4])
-    __shared__ float2 sq2[kMaxGrid * 4];                // same for q^2
-    __shared__ uint4 sbq[kMaxGrid];                     // entry e: q[0..7] as bf16
-    __shared__ uint4 sbq2[kMaxGrid];                    // entry e: q^2[0..7] as bf16
-    __shared__ int sgrid_inexact;
-    __shared__ uint16_t sout16[kPayloads * kBlocksPerWG * kBlockBytes / 2];
-    __shared__ int sgrid_bad;
-    uint8_t* sout = reinterpret_cast<uint8_t*>(sout16);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
-    const int n = a.grid_size;
-    const int nchunks = (n + kChunk - 1) / kChunk;
-    const int npad = nchunks * kChunk;
-
-    if (tid == 0) { sgrid_bad = 0; sgrid_inexact = 0; }
-    for (int i = tid; i < kPayloads * kBlocksPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
-    __syncthreads();
-    {
-        int bad = 0, inexact = 0;
-        // One (entry, slice) pair per thread: consecutive threads write
-        // consecutive LDS words.
-        for (int i = tid; i < npad * 4; i += kThreads) {
-            const int e = i >> 2, t = i & 3;
-            const int src = e < n ? e : n - 1;
-            const float a0 = a.grid[8 * src + 2 * t], a1 = a.grid[8 * src + 2 * t + 1];
-            const float b0 = a.grid[8 * src + t], b1 = a.grid[8 * src + t + 4];
-            bad |= !(a0 >= 0.0f && finite_f32(a0) && a1 >= 0.0f && finite_f32(a1));
-            float2* ge = reinterpret_cast<float2*>(sgrid + entry_off<kChunk>(e));
-            ge[t] = make_float2(a0, a1);
-            ge[4 + t] = make_float2(a0 * a0, a1 * a1);
-            sq[i] = make_float2(b0, b1);
-            sq2[i] = make_float2(b0 * b0, b1 * b1);
-            // Word t of the bf16 rows: elements 2t and 2t+1.
-            inexact |= !(bf16_exact_with_square(a0) && bf16_exact_with_square(a1));
-            reinterpret_cast<uint32_t*>(sbq)[i] = bf16_bits(a0) | (bf16_bits(a1) << 16);
-            reinterpret_cast<uint32_t*>(sbq2)[i] = bf16_bits(a0 * a0) | (bf16_bits(a1 * a1) << 16);
-        }
-        if (bad) sgrid_bad = 1;
-        if (inexact) sgrid_inexact = 1;
-    }
-    __syncthreads();
-    const bool grid_bad = sgrid_bad != 0;
-    const bool grid_exact = sgrid_inexact == 0;     // workgroup-uniform
-    if (grid_bad && tid == 0) report(a.status, IQ_ERR_GRID);
-
-    const int col = lane & 15;
-    const int kb = lane >> 4;
-    const int half = wave & 1;
-    const int g = half * 16 + col;          // group in block
-    const int m = g >> 1;                   // scale group
-    const int h = g & 1;                    // group in scale group
-
-    // Persistent workgroups: the grid is staged once, then each workgroup
-    // takes every gridDim.x-th set of 16 blocks.
-    const int64_t nsets = (a.g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
-    for (int64_t set = blockIdx.x; set < nsets; set += gridDim.x) {
-    if (set != blockIdx.x) __syncthreads();     // the previous set's payloads are out
-    for (int pass = 0; pass < kPasses; ++pass) {
-        const int slot = pass * kBlocksPerPass + (wave >> 1);
-        const int64_t blk = set * kBlocksPerWG + slot;
-        if (blk >= a.g.nblocks) continue;                      // wave-uniform
-        const int64_t bt = blk / a.g.blocks_per_batch;
-        const int64_t cb = blk % a.g.blocks_per_row;
-        const WeightBlock<kDT> xb(a.w, blk);
-        const float* wblk = a.imp ? a.imp + bt * a.g.cols + cb * kBlockElems : nullptr;
-
-        int err = 0;
-        float amax = 0.0f;
-        {
-            const float4 xv = xb.quad(lane);
-            const float xs[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                if (!finite_f32(xs[t])) err = IQ_ERR_NONFINITE;
-                amax = fmaxf(amax, fabsf(xs[t]));
-            }
-            if (wblk && !err) {
-                const float4 wv = reinterpret_cast<const float4*>(wblk)[lane];
-                const float ws[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    if (!(ws[t] >= 0.0f) || !finite_f32(ws[t])) err = IQ_ERR_IMPORTANCE;
-            }
-        }
-        if (err && half == 0) report(a.status, err);
-        const bool block_bad = __ballot(err != 0) != 0;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-
-        uint32_t dh;
-        if (a.scales) {
-            dh = (uint32_t)a.scales[blk];
-        } else {
-            const float t = amax / 155.0f;
-            const float u = t * 0.61f;
-            dh = f32_to_f16_bits(u);
-        }
-        const bool scale_bad = ((dh & 0x7c00u) == 0x7c00u) || ((dh & 0x8000u) && (dh & 0x7fffu));
-        dh &= 0x7fffu;
-        if (scale_bad && !block_bad && half == 0 && lane == 0) report(a.status, IQ_ERR_SCALE_RANGE);
-        const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
-
-        const bool bad_block = grid_bad || block_bad || scale_bad;
-        const bool zero_scale = dh == 0u;
-        const bool skip = bad_block || zero_scale;
-
-        // The lane's group: values, weights and signs.
-        float x[8], w[8];
-        load_group(xb, wblk, g, skip, x, w);
-        const int neg = group_signs(x, w);
-        const float inv_d = skip ? 1.0f : 1.0f / d;
-
-        // Sweep.
-        float best[16], snap[16];
-        uint32_t chunk_of[2] = {0u, 0u};
-#pragma unroll
-        for (int k = 0; k < 16; ++k) { best[k] = __builtin_inff(); snap[k] = best[k]; }
-        const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (grid_exact) {
-            // The lane's K slice kb of the group side: part kb of the exact
-            // three-way bf16 split of -2*(w*sign*x)/d and of w, for all 8
-            // elements (slice 3 is zero padding).
-            uint32_t hp[8], hw[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float v = w[j] * x[j];
-                if ((neg >> j) & 1) v = -v;
-                v = -2.0f * (v * inv_d);
-                hp[j] = kb < 3 ? split_part(v, kb) : 0u;
-                hw[j] = kb < 3 ? split_part(w[j], kb) : 0u;
-            }
-            const v8bf opp = as_v8bf(make_uint4(hp[0] | (hp[1] << 16), hp[2] | (hp[3] << 16),
-                                                hp[4] | (hp[5] << 16), hp[6] | (hp[7] << 16)));
-            const v8bf opw = as_v8bf(make_uint4(hw[0] | (hw[1] << 16), hw[2] | (hw[3] << 16),
-                                                hw[4] | (hw[5] << 16), hw[6] | (hw[7] << 16)));
-            for (int ch = 0; ch < nchunks; ++ch) {
-                for (int tt = 0; tt < kChunkTiles; ++tt) {
-                    const int e = (ch * kChunkTiles + tt) * kTile + col;
-                    const v4f pn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(sbq[e]), opp, zero4, 0, 0, 0);
-                    const v4f nn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(sbq2[e]), opw, zero4, 0, 0, 0);
-                    fold_tile(pn, nn, best);
-                }
-                track_chunk(ch, best, snap, chunk_of);
-            }
-        } else {
-            // fp32 operands: elements kb and kb+4 of the group side, read
-            // again rather than selected from registers.
-            float bw0 = 1.0f, bw1 = 1.0f, bx0 = 0.0f, bx1 = 0.0f;
-            if (!skip) {
-                bx0 = xb.one(g * 8 + kb);
-                bx1 = xb.one(g * 8 + kb + 4);
-                if (wblk) { bw0 = wblk[g * 8 + kb]; bw1 = wblk[g * 8 + kb + 4]; }
-            }
-            float bp0 = bw0 * bx0, bp1 = bw1 * bx1;
-            if ((neg >> kb) & 1) bp0 = -bp0;
-            if ((neg >> (kb + 4)) & 1) bp1 = -bp1;
-            bp0 = -2.0f * (bp0 * inv_d);
-            bp1 = -2.0f * (bp1 * inv_d);
-            for (int ch = 0; ch < nchunks; ++ch) {
-                for (int tt = 0; tt < kChunkTiles; ++tt) {
-                    const int e = (ch * kChunkTiles + tt) * kTile + col;
-                    const float2 aq = sq[4 * e + kb];
-                    const float2 aq2 = sq2[4 * e + kb];
-                    v4f pn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.x, bp0, zero4, 0, 0, 0);
-                    pn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq.y, bp1, pn, 0, 0, 0);
-                    v4f nn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq2.x, bw0, zero4, 0, 0, 0);
-                    nn = __builtin_amdgcn_mfma_f32_16x16x4f32(aq2.y, bw1, nn, 0, 0, 0);
-                    fold_tile(pn, nn, best);
-                }
-                track_chunk(ch, best, snap, chunk_of);
-            }
-        }
-
-        // The rescans need the signed weighted values again; they are
-        // rebuilt from memory rather than held through the sweep.
-        __asm__ volatile("" ::: "memory");
-        load_group(xb, wblk, g, skip, x, w);
-        float wxs[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float wx = w[j] * x[j];
-            wxs[j] = ((neg >> j) & 1) ? -wx : wx;
-        }
-
-        // Entry of local scale k for this lane's group: rescan the lane's part
-        // of its winning chunk, then keep the lane of least matrix-core minimum.
-        auto pick = [&](int k) -> int {
-            float lm = best[0];
-#pragma unroll
-            for (int c = 1; c < 16; ++c)
-                if (k == c) lm = best[c];
-            const int tchunk = (int)((chunk_of[k >> 3] >> (4 * (k & 7))) & 0xfu);
-            // The lane of the column whose matrix-core minimum is least holds
-            // the entry.  Unless two lanes of some column hold equal minima,
-            // the four lanes split that lane's entries of its chunk and keep
-            // the least key, lowest entry on equal keys; with equal minima
-            // every lane rescans its own entries and the lane of least
-            // minimum, then lowest entry, wins.
-            constexpr int kPer = kChunkTiles;          // 4*kChunkTiles entries over 4 lanes
-            float cm = fminf(lm, __shfl_xor(lm, 16));
-            cm = fminf(cm, __shfl_xor(cm, 32));
-            const uint64_t holders = (__ballot(lm == cm) >> col) & 0x0001000100010001ull;
-            const bool tie = __ballot(__popcll(holders) > 1) != 0;      // wave-uniform
-            int idx;
-            float key;
-            if (!tie) {
-                const int kbs = __builtin_ctzll(holders) >> 4;
-                const int tch = __shfl(tchunk, col + 16 * kbs);
-                idx = rescan<kChunkTiles>(sgrid, tch, kbs, kb * kPer, kPer, k, wxs, w, inv_d, &key);
-#pragma unroll
-                for (int o = 16; o <= 32; o <<= 1) {
-                    const float ok = __shfl_xor(key, o);
-                    const int oi = __shfl_xor(idx, o);
-                    if (ok < key || (ok == key && oi < idx)) { key = ok; idx = oi; }
-                }
-            } else {
-                idx = rescan<kChunkTiles>(sgrid, tchunk, kb, 0, 4 * kChunkTiles, k, wxs, w, inv_d,
-                                          &key);
-#pragma unroll
-                for (int o = 16; o <= 32; o <<= 1) {
-                    const float om = __shfl_xor(lm, o);
-                    const int oi = __shfl_xor(idx, o);
-                    if (om < lm || (om == lm && oi < idx)) { lm = om; idx = oi; }
-                }
-            }
-            return idx < n ? idx : n - 1;
-        };
-
-        // Every local scale k for every scale group: the payload forced to k.
-        for (int k = 0; k < 16; ++k) {
-            const int idx = pick(k);
-            if (!skip && kb == 0) {
-                uint8_t* ob = sout + (k * kBlocksPerWG + slot) * kBlockBytes;
-                const uint32_t code = (uint32_t)idx | ((uint32_t)(neg & 0x7f) << 9);
-                ob[2 + 2 * g] = (uint8_t)(code & 0xff);
-                ob[3 + 2 * g] = (uint8_t)(code >> 8);
-                if ((g & 3) == 0) ob[66 + (m >> 1)] = (uint8_t)(k | (k << 4));
-                if (g == 0) {
-                    ob[0] = (uint8_t)(dh & 0xff);
-                    ob[1] = (uint8_t)(dh >> 8);
-                }
-            }
-        }
-    }
-    if (a.out) {
-        // Copy the staged payloads out and clear what was copied (each word
-        // by the thread that copied it) for the next set.
-        __syncthreads();
-        const int64_t first = set * kBlocksPerWG;
-        const int64_t left = a.g.nblocks - first;
-        const int nb = left < kBlocksPerWG ? (int)left : kBlocksPerWG;
-        for (int k = 0; k < kPayloads; ++k) {
-            uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (k * a.g.nblocks + first) * kBlockBytes);
-            uint16_t* s16 = sout16 + k * kBlocksPerWG * (kBlockBytes / 2);
-            // An opaque copy of the thread index: the offsets derived from it are
-            // recomputed here rather than held (and spilled) across the sets.
-            int t0 = tid;
-            __asm__ volatile("" : "+v"(t0));
-            for (int i = t0; i < nb * (kBlockBytes / 2); i += kThreads) {
-                o16[i] = s16[i];
-                s16[i] = 0;
-            }
-        }
-    }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Payload encode in 32 x 32 matrix tiles: a wave owns a whole block.
+// The search in 32 x 32 matrix tiles: a wave owns a whole block.
 //
 // v_mfma_f32_32x32x16_bf16 takes the 32 groups of the block as the 32 columns
 // (lane l: column l%32) and 32 grid entries as the rows; the lane holds 16 of
 // the rows (8*(v/4) + 4*(l/32) + v%4, v = 0..15), so each group is covered by
-// two lanes instead of four, and the per-group work outside the sweep (signs,
-// split, costs, choice, packing) is repeated twice instead of four times.  K
-// is 16 per product: the three bf16 parts of the group side go in two
-// products per output (parts 0 and 1 in the lanes' two K halves, then part 2
-// and zeros).  The payload is written straight from the lanes (coalesced
-// 16-bit codes), so waves never wait for each other after the grid staging.
+// the two lanes of its column, which share the per-group work outside the
+// sweep (signs, split, costs, choice, packing).  K is 16 per product: the
+// three bf16 parts of the group side go in two products per output (parts 0
+// and 1 in the lanes' two K halves, then part 2 and zeros).  A set's payloads
+// are staged in LDS and stored together after a workgroup barrier (whole
+// cache lines); the candidates are written straight from the lanes.
 // ---------------------------------------------------------------------------
 constexpr int kWTile = 32;                 // entries per wide tile
 constexpr int kWChunkTiles = 2;            // wide tiles per tracking chunk
-constexpr int kWChunk = kWTile * kWChunkTiles;
 
 // The 16 keys (2k+1)*N + P' of the lane's 16 entries folded into the minima
 // (a tree of three-input minima: 8 per local scale).
@@ -657,8 +301,8 @@ __device__ __forceinline__ int rescan_quads(const float* __restrict__ sg, int ch
     return idx;
 }
 
-// kMode: kModePayload, kModeFake or kModeCandidates; kDT: the weight's
-// iq_dtype_t.
+// kMode: kModePayload, kModeEvery, kModeFake or kModeCandidates; kDT: the
+// weight's iq_dtype_t.
 template <int kMode, int kDT>
 __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
 {
@@ -667,14 +311,16 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
     // candidates pick top_c local scales per group, each rescanning one
     // lane-half of a chunk, so their chunks are one tile (32 entries): twice
     // the tracking in the sweep, half the rescan per pick.
-    constexpr int kCT = kCand ? 1 : kWChunkTiles;
+    constexpr bool kEvery = kMode == kModeEvery;
+    constexpr int kNP = kEvery ? 16 : 1;           // payloads per block
+    constexpr int kCT = (kCand || kEvery) ? 1 : kWChunkTiles;
     constexpr int kCh = kWTile * kCT;
     __shared__ float sgrid[kMaxGrid * kEntryStride + 2 * (kMaxGrid / 32)];  // q[0..7], q^2[0..7]
     __shared__ uint4 sbq[kMaxGrid];                     // entry e: q[0..7] as bf16
     __shared__ uint4 sbq2[kMaxGrid];                    // entry e: q^2[0..7] as bf16
     __shared__ int sgrid_bad, sgrid_inexact;
     __shared__ float4 ssnap[4 * kThreads];              // per lane: the minima at the last chunk end
-    __shared__ uint16_t sout16[kCand ? 1 : kWavesPerWG * kBlockBytes / 2];    // the set's payloads
+    __shared__ uint16_t sout16[kCand ? 1 : kNP * kWavesPerWG * kBlockBytes / 2];    // the set's payloads
     // candidates: per wave and scale group, the 16 local scales and their
     // costs in (cost, k) order
     __shared__ float srank_cost[kCand ? kWavesPerWG * 16 * 16 : 1];
@@ -689,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
 
     if (tid == 0) { sgrid_bad = 0; sgrid_inexact = 0; }
     if (!kCand)
-        for (int i = tid; i < kWavesPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
+        for (int i = tid; i < kNP * kWavesPerWG * kBlockBytes / 2; i += kThreads) sout16[i] = 0;
     __syncthreads();
     {
         int bad = 0, inexact = 0;
@@ -773,7 +419,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
         const float d = scale_bad ? 0.0f : f16_bits_to_f32(dh);
 
         bool choice_bad = false;
-        if (!kCand && a.choices) {
+        if (!kCand && !kEvery && a.choices) {
             int ln = lane;                  // opaque: the address is formed here, not hoisted
             __asm__ volatile("" : "+v"(ln));
             const int cv = ln < 16 ? a.choices[blk * 16 + ln] : 0;
@@ -865,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
         __asm__ volatile("" ::: "memory");
         load_group(xb, wblk, g, skip, x, w);
         const int neg2 = group_signs(x, w);
-        const int forced = (!kCand && a.choices && !choice_bad) ? a.choices[blk * 16 + m] : -1;
+        const int forced = (!kCand && !kEvery && a.choices && !choice_bad) ? a.choices[blk * 16 + m] : -1;
         float wxs[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -911,7 +557,26 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
             return idx < n ? idx : n - 1;
         };
 
-        if constexpr (!kCand) {
+        if constexpr (kEvery) {
+            // Every choice: payload k has every scale group at local scale k,
+            // a pick per group and k (a rejected or zero-scale block stays all
+            // zeros in every payload).
+#pragma unroll 1
+            for (int k = 0; k < 16; ++k) {
+                const int idx = pick(k);
+                const uint32_t code = (uint32_t)idx | ((uint32_t)(neg2 & 0x7f) << 9);
+                if (hl == 0 && !skip) {
+                    uint8_t* ob = reinterpret_cast<uint8_t*>(sout16) + (k * kWavesPerWG + wave) * kBlockBytes;
+                    ob[2 + 2 * g] = (uint8_t)(code & 0xff);
+                    ob[3 + 2 * g] = (uint8_t)(code >> 8);
+                    if ((g & 3) == 0) ob[66 + (g >> 2)] = (uint8_t)(k | (k << 4));
+                    if (g == 0) {
+                        ob[0] = (uint8_t)(dh & 0xff);
+                        ob[1] = (uint8_t)(dh >> 8);
+                    }
+                }
+            }
+        } else if constexpr (!kCand) {
         int kstar = 0;
         float cbv = cost[0];
 #pragma unroll
@@ -1129,18 +794,22 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
         }
     }
     if (!kCand && a.out) {
-        // Copy the set's payloads out and clear what was copied (each word
-        // by the thread that copied it) for the next set.
+        // Copy the set's payloads out (every choice: payload k of the set to
+        // out[k]) and clear what was copied (each word by the thread that
+        // copied it) for the next set.
         __syncthreads();
         const int64_t first = set * kWavesPerWG;
         const int64_t left = a.g.nblocks - first;
         const int nb = left < kWavesPerWG ? (int)left : kWavesPerWG;
-        uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + first * kBlockBytes);
-        int t0 = tid;
-        __asm__ volatile("" : "+v"(t0));
-        for (int i = t0; i < nb * (kBlockBytes / 2); i += kThreads) {
-            o16[i] = sout16[i];
-            sout16[i] = 0;
+        for (int k = 0; k < kNP; ++k) {
+            uint16_t* o16 = reinterpret_cast<uint16_t*>(a.out + (k * a.g.nblocks + first) * kBlockBytes);
+            uint16_t* s16 = sout16 + k * kWavesPerWG * (kBlockBytes / 2);
+            int t0 = tid;
+            __asm__ volatile("" : "+v"(t0));
+            for (int i = t0; i < nb * (kBlockBytes / 2); i += kThreads) {
+                o16[i] = s16[i];
+                s16[i] = 0;
+            }
         }
     }
     }
@@ -1150,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
 // blocks when there are fewer sets.
 unsigned persistent_wgs(const BlockGeom& g)
 {
-    const int64_t sets = (g.nblocks + kBlocksPerWG - 1) / kBlocksPerWG;
+    const int64_t sets = (g.nblocks + kWavesPerWG - 1) / kWavesPerWG;
     return (unsigned)(sets < g.cus ? sets : g.cus);
 }
 
@@ -1159,7 +828,8 @@ hipError_t launch_mode(const Iq2xsArgs& a, int mode, hipStream_t stream)
 {
     const unsigned wgs = persistent_wgs(a.g);
     if (mode == kModeEvery)
-        hipLaunchKernelGGL((iq2xs_every_kernel<kDT>), dim3(wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((iq2xs_wide_kernel<kModeEvery, kDT>), dim3(wgs), dim3(kThreads), 0,
+                           stream, a);
     else if (mode == kModeFake)
         hipLaunchKernelGGL((iq2xs_wide_kernel<kModeFake, kDT>), dim3(wgs), dim3(kThreads), 0,
                            stream, a);
