@@ -627,24 +627,25 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
                 ob[1] = (uint8_t)(dh >> 8);
             }
         }
-        if (kMode == kModeFake && hl == 0) {
+        if (kMode == kModeFake) {
             // The decoded group, d*(2k+1)*sign*q with the payload's fields
             // (the 8th sign from even parity of the 7-bit mask; a zero block
             // decodes as the all-zero payload does; a rejected block is
             // written as zeros), with the decode kernel's fp32 expression.
+            // The two lanes of the column write four values each: one
+            // 1 KiB store per wave.
             const uint32_t cz = skip ? 0u : code;
             const int kz = skip ? 0 : kstar;
             const float sk = f16_bits_to_f32(skip ? 0u : dh) * (float)(2 * kz + 1);
             const uint32_t mask = cz >> 9;
-            const uint32_t signs = mask | ((__popc(mask) & 1u) << 7);
-            const float* q = sgrid + entry_off<kCh>((int)(cz & 0x1ffu));
-            float v[8];
+            const uint32_t signs = (mask | ((__popc(mask) & 1u) << 7)) >> (4 * hl);
+            const float* q = sgrid + entry_off<kCh>((int)(cz & 0x1ffu)) + 4 * hl;
+            float v[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j)
                 v[j] = bad_block ? 0.0f : (((signs >> j) & 1u) ? -sk : sk) * q[j];
-            float4* o = reinterpret_cast<float4*>(a.xhat + blk * kBlockElems + g * 8);
-            o[0] = make_float4(v[0], v[1], v[2], v[3]);
-            o[1] = make_float4(v[4], v[5], v[6], v[7]);
+            reinterpret_cast<float4*>(a.xhat + blk * kBlockElems + g * 8)[hl] =
+                make_float4(v[0], v[1], v[2], v[3]);
         }
         } else {
             // Top-C local scales by (cost, k); a zero scale makes every choice
