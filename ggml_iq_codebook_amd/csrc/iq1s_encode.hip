@@ -118,23 +118,32 @@ constexpr int kW1Tile = 32;
 constexpr int kW1ChunkTiles = 4;                       // 128-entry chunks (16 for 2048 entries)
 
 // The 8 keys (2k+1)*U + V of the lane's 16 entries for k = 0..7 folded into
-// best[kBase + k] (a tree of three-input minima).
+// best[kBase + k].  Each minimum is a chain of three-input minima over pairs
+// of keys, and the chains of two local scales alternate, so each wave's
+// instruction stream is two key FMAs and one minimum throughout: the dual
+// issue pairs an FMA of one wave with a minimum of another, never two minima,
+// and a stream with the minima spread evenly leaves two waves waiting on
+// minima at the same time less often than one with them in runs.
 template <int kBase>
 __device__ __forceinline__ void fold_wide8(const v16f& u, const v16f& v, float (&best)[16])
 {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float mk = (float)(2 * k + 1);
-        float key[16];
+    for (int k = 0; k < 8; k += 2) {
+        const float ma = (float)(2 * k + 1), mb = (float)(2 * k + 3);
+        float ba = best[kBase + k], bb = best[kBase + k + 1];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) key[r] = __builtin_fmaf(u[r], mk, v[r]);
-        const float a0 = fminf(fminf(key[0], key[1]), key[2]);
-        const float a1 = fminf(fminf(key[3], key[4]), key[5]);
-        const float a2 = fminf(fminf(key[6], key[7]), key[8]);
-        const float a3 = fminf(fminf(key[9], key[10]), key[11]);
-        const float a4 = fminf(fminf(key[12], key[13]), key[14]);
-        const float a5 = fminf(fminf(key[15], best[kBase + k]), a0);
-        best[kBase + k] = fminf(fminf(fminf(fminf(a1, a2), a3), a4), a5);
+        for (int r = 0; r < 16; r += 2) {
+            const float a0 = __builtin_fmaf(u[r], ma, v[r]);
+            const float a1 = __builtin_fmaf(u[r + 1], ma, v[r + 1]);
+            ba = fminf(fminf(ba, a0), a1);
+            __builtin_amdgcn_sched_barrier(0);
+            const float b0 = __builtin_fmaf(u[r], mb, v[r]);
+            const float b1 = __builtin_fmaf(u[r + 1], mb, v[r + 1]);
+            bb = fminf(fminf(bb, b0), b1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        best[kBase + k] = ba;
+        best[kBase + k + 1] = bb;
     }
 }
 

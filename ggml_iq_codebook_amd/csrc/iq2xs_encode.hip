@@ -160,23 +160,51 @@ __device__ __forceinline__ int entry_off(int e) { return kEntryStride * e + 2 * 
 constexpr int kWTile = 32;                 // entries per wide tile
 constexpr int kWChunkTiles = 2;            // wide tiles per tracking chunk
 
-// The 16 keys (2k+1)*N + P' of the lane's 16 entries folded into the minima
-// (a tree of three-input minima: 8 per local scale).
+// The 16 keys (2k+1)*N + P' of the lane's 16 entries folded into the minima.
+// kChain false: a tree of three-input minima, 8 per local scale.  kChain
+// true: each minimum a chain of three-input minima over pairs of keys, the
+// chains of two local scales alternating, so that each wave's instruction
+// stream is two key FMAs and one minimum throughout (the dual issue pairs an
+// FMA of one wave with a minimum of another, never two minima).  Which is
+// faster depends on the epilogue the compiler schedules around the sweep:
+// measured, the chains help the fake quant (5 %) and not the other modes.
+template <bool kChain>
 __device__ __forceinline__ void fold_wide(const v16f& pn, const v16f& nn, float (&best)[16])
 {
+    if constexpr (kChain) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const float mk = (float)(2 * k + 1);
-        float key[16];
+        for (int k = 0; k < 16; k += 2) {
+            const float ma = (float)(2 * k + 1), mb = (float)(2 * k + 3);
+            float ba = best[k], bb = best[k + 1];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) key[v] = __builtin_fmaf(nn[v], mk, pn[v]);
-        const float a0 = fminf(fminf(key[0], key[1]), key[2]);
-        const float a1 = fminf(fminf(key[3], key[4]), key[5]);
-        const float a2 = fminf(fminf(key[6], key[7]), key[8]);
-        const float a3 = fminf(fminf(key[9], key[10]), key[11]);
-        const float a4 = fminf(fminf(key[12], key[13]), key[14]);
-        const float a5 = fminf(fminf(key[15], best[k]), a0);
-        best[k] = fminf(fminf(fminf(fminf(a1, a2), a3), a4), a5);
+            for (int r = 0; r < 16; r += 2) {
+                const float a0 = __builtin_fmaf(nn[r], ma, pn[r]);
+                const float a1 = __builtin_fmaf(nn[r + 1], ma, pn[r + 1]);
+                ba = fminf(fminf(ba, a0), a1);
+                __builtin_amdgcn_sched_barrier(0);
+                const float b0 = __builtin_fmaf(nn[r], mb, pn[r]);
+                const float b1 = __builtin_fmaf(nn[r + 1], mb, pn[r + 1]);
+                bb = fminf(fminf(bb, b0), b1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            best[k] = ba;
+            best[k + 1] = bb;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const float mk = (float)(2 * k + 1);
+            float key[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) key[v] = __builtin_fmaf(nn[v], mk, pn[v]);
+            const float a0 = fminf(fminf(key[0], key[1]), key[2]);
+            const float a1 = fminf(fminf(key[3], key[4]), key[5]);
+            const float a2 = fminf(fminf(key[6], key[7]), key[8]);
+            const float a3 = fminf(fminf(key[9], key[10]), key[11]);
+            const float a4 = fminf(fminf(key[12], key[13]), key[14]);
+            const float a5 = fminf(fminf(key[15], best[k]), a0);
+            best[k] = fminf(fminf(fminf(fminf(a1, a2), a3), a4), a5);
+        }
     }
 }
 
@@ -474,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
                     const v8bf aq = as_v8bf(sbq[e]), aq2 = as_v8bf(sbq2[e]);
                     const v16f pn = mfma32(aq, opp2, mfma32(aq, opp1, zero16));
                     const v16f nn = mfma32(aq2, opw2, mfma32(aq2, opw1, zero16));
-                    fold_wide(pn, nn, best);
+                    fold_wide<kMode == kModeFake>(pn, nn, best);
                 }
                 track_chunk_lds(ch, best, snap, chunk_of);
             }
@@ -500,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
                         pn = __builtin_amdgcn_mfma_f32_32x32x2f32(q[2 * s2 + hl], bp[s2], pn, 0, 0, 0);
                         nn = __builtin_amdgcn_mfma_f32_32x32x2f32(q[8 + 2 * s2 + hl], bw[s2], nn, 0, 0, 0);
                     }
-                    fold_wide(pn, nn, best);
+                    fold_wide<kMode == kModeFake>(pn, nn, best);
                 }
                 track_chunk_lds(ch, best, snap, chunk_of);
             }
