@@ -303,6 +303,8 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
     const int64_t nsets = (a.g.nblocks + kWavesPerWG - 1) / kWavesPerWG;
     for (int64_t set = blockIdx.x; set < nsets; set += gridDim.x) {
     if (set != blockIdx.x) __syncthreads();     // the previous set's payloads are out
+    // every wave of the workgroup has a block of this set (workgroup-uniform)
+    const bool set_full = (set + 1) * kWavesPerWG <= a.g.nblocks;
     const int64_t blk = set * kWavesPerWG + wave;
     if (blk < a.g.nblocks) {                    // wave-uniform
         int ln = lane;                          // opaque: lane offsets are formed per block
@@ -435,6 +437,9 @@ __global__ __launch_bounds__(kThreads) void iq1s_payload_wide_kernel(Iq1sArgs a)
                 chunk_of[c / kFPW] = (chunk_of[c / kFPW] & ~msk) | (chrep & msk);
                 snap[c] = best[c];
             }
+            // The waves of a full set sweep in step, a chunk at a time, so
+            // that no wave is left to finish its block alone.
+            if (set_full) __syncthreads();
         }
 
         // Candidates and every choice: the lane's minima go to LDS, where the

@@ -394,6 +394,8 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
     const int64_t nsets = (a.g.nblocks + kWavesPerWG - 1) / kWavesPerWG;
     for (int64_t set = blockIdx.x; set < nsets; set += gridDim.x) {
     if (set != blockIdx.x) __syncthreads();     // the previous set's payloads are out
+    // every wave of the workgroup has a block of this set (workgroup-uniform)
+    const bool set_full = (set + 1) * kWavesPerWG <= a.g.nblocks;
     const int64_t blk = set * kWavesPerWG + wave;
     if (blk < a.g.nblocks) {                    // wave-uniform
         // The lane's indices, formed in every block from an opaque copy of
@@ -505,6 +507,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
                     fold_wide<kMode == kModeFake>(pn, nn, best);
                 }
                 track_chunk_lds(ch, best, snap, chunk_of);
+                if (!kEvery && set_full) __syncthreads();   // the waves of a full set sweep in step
             }
         } else {
             // fp32 operands (v_mfma_f32_32x32x2_f32, K = 2): product s takes
@@ -531,6 +534,7 @@ __global__ __launch_bounds__(kThreads) void iq2xs_wide_kernel(Iq2xsArgs a)
                     fold_wide<kMode == kModeFake>(pn, nn, best);
                 }
                 track_chunk_lds(ch, best, snap, chunk_of);
+                if (!kEvery && set_full) __syncthreads();   // the waves of a full set sweep in step
             }
         }
 
