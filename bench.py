@@ -463,16 +463,10 @@ def main():
         R, C = w2.shape
         shape = (R, G, 8, 256 // G) if H.dim() == 2 else (R, C // 256, G, 8, 256 // G)
 
-        def step(ev=None):
-            if ev:
-                ev[0].record(stream)
+        def step():
             err, ch, _ = iq.encode_candidates(w2, grid, imp2, fmt=fmt, top_c=8, status=status,
                                               check=False)
-            if ev:
-                ev[1].record(stream)
             iq.choice_search(H, err.view(shape), sweeps=2)
-            if ev:
-                ev[2].record(stream)
     elif dequant:
         B, R, C = w.shape
         # the payload of the workload's encode, decoded once per step
@@ -573,18 +567,32 @@ def main():
             "algorithmic_bytes_per_launch": alg,
         }
     elif args.config.startswith("c5"):
-        # Per-kernel times from HIP events around each launch of a second run
-        # of the same steps (after the timed region, so that it is not
-        # perturbed): the candidate encode, the dominant kernel, carries the
-        # roofline (the same sweep as the encode, so the same algorithmic
-        # flops per group and entry); the choice search is reported beside it
-        # against its own bounds.
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        for e in evs:
-            step(e)
-        torch.cuda.synchronize()
-        cand_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-        search_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+        # Per-kernel times, after the timed region (so that it is not
+        # perturbed): HIP events on the launch stream around `steps`
+        # back-to-back launches of each kernel alone (an event pair around
+        # every launch adds several microseconds to kernels this short).  The
+        # candidate encode, the dominant kernel, carries the roofline (the
+        # same sweep as the encode, so the same algorithmic flops per group
+        # and entry); the choice search is reported beside it against its own
+        # bounds.
+        err0, _, _ = iq.encode_candidates(w2, grid, imp2, fmt=fmt, top_c=8, status=status,
+                                          check=False)
+        cand_in = err0.view(shape)
+
+        def per_launch(fn):
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.steps
+
+        cand_ms = per_launch(lambda: iq.encode_candidates(w2, grid, imp2, fmt=fmt, top_c=8,
+                                                          status=status, check=False))
+        search_ms = per_launch(lambda: iq.choice_search(H, cand_in, sweeps=2))
         units = w2.numel() // 8 * cfg["grid"].shape[0]
         # candidates written: [rows][blocks][G][8][256/G] fp32 + choices int32
         cand_bytes = R * (C // 256) * (G * 8 * (256 // G) * 4 + G * 8 * 4)
