@@ -91,6 +91,17 @@ def _iq2xs_grid_kind(kind, n, seed):
     return grid
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_full_sets_then_a_short_set(fmt):
+    # 4101 blocks: 257 sets of 16 blocks for 256 persistent workgroups, so one
+    # workgroup takes a full set and then a set of 5.  The waves of a full set
+    # meet at workgroup barriers during the sweep; a short set takes none
+    # (its idle waves never reach them).
+    w = workloads.normal_weight((1, 4101, 256), 61)
+    imp = workloads.lognormal_importance((1, 256), 62)
+    _check_full(fmt, w, grid_for(fmt), imp)
+
+
 @pytest.mark.parametrize("kind", ["wide", "real", "one_off"])
 @pytest.mark.parametrize("shape,n", [((2, 5, 768), 512), ((1, 3, 512), 37), ((1, 4, 256), 100)])
 def test_iq2xs_grids_not_exact_in_bf16(kind, shape, n):
