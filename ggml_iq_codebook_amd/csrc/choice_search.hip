@@ -410,6 +410,8 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             }
         };
         float lr[KH];
+        const int qc = scand < C ? scand : 0;
+        float qnext = qself[srow * kQS + qc];     // group 0
         load_cv(0, cv);
         load_cv(1 % G, cvn);
         late(0, lr);
@@ -423,6 +425,10 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         auto dstep = [&](int g, float (&cur)[L]) {
             const int gn = g + 1 < G ? g + 1 : 0;
             const int g2 = gn + 1 < G ? gn + 1 : 0;
+            // e_c^T H_gg e_c of this step's group, read during the step
+            // before; the next group's is requested now.
+            const float qs = qnext;
+            qnext = qself[srow * kQS + gn * C + qc];
             const float* pb = part + (g & 1) * kPB;
             float r[KH];
 #pragma unroll
@@ -436,14 +442,15 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             // The candidate's dot with the row's rest: column j of tile h
             // comes from lane j of the row (DPP row broadcast).  Lanes that
             // score nothing keep the largest key, above any score's.
-            int key = 0x7fffffff;
+            int key;
             {
                 float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int h = 0; h < KH; ++h) dot_row16(r[h], &cur[16 * h], d4);
                 const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-                const float sc = __builtin_fmaf(2.0f, dot, qself[srow * kQS + g * C + (scand < C ? scand : 0)]);
-                if (scorer) key = sc == sc ? score_key(sc) : 0x7ffffffe;   // a NaN after every number
+                const float sc = __builtin_fmaf(2.0f, dot, qs);
+                const int sk = sc == sc ? score_key(sc) : 0x7ffffffe;   // a NaN after every number
+                key = scorer ? sk : 0x7fffffff;
             }
             // The least score of the row (DPP), then the row's lanes that
             // hold it (a ballot, 16 bits per row): the group keeps its pick if
