@@ -390,16 +390,25 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         };
         // H_g,g-1 e_g-1 for the lane's columns of group g, from the errors
         // of g-1 in the error rows (the lanes of a row read the same row).
-        auto late = [&](int g, float (&lr)[KH]) {
+        // The lane's row of H_g,g-1 (row scand + 16h), read at the start of
+        // the step whose late term it serves, beside the partials.
+        auto load_hrow = [&](int g, float4 (&hv)[KH][L / 4]) {
+#pragma unroll
+            for (int h = 0; h < KH; ++h) {
+                const float* hr = &hblk[g * kHB + (scand + 16 * h) * kHR];
+#pragma unroll
+                for (int j4 = 0; j4 < L / 4; ++j4) hv[h][j4] = *reinterpret_cast<const float4*>(hr + 4 * j4);
+            }
+        };
+        auto late = [&](int g, float (&lr)[KH], const float4 (&hv)[KH][L / 4]) {
             const int gp = g > 0 ? g - 1 : G - 1;
             const float* er = &ecur[srow * kER + gp * L];
 #pragma unroll
             for (int h = 0; h < KH; ++h) {
-                const float* hr = &hblk[g * kHB + (scand + 16 * h) * kHR];
                 float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int j4 = 0; j4 < L / 4; ++j4) {
-                    const float4 h4 = *reinterpret_cast<const float4*>(hr + 4 * j4);
+                    const float4 h4 = hv[h][j4];
                     const float4 e4 = *reinterpret_cast<const float4*>(er + 4 * j4);
                     d4[0] = __builtin_fmaf(h4.x, e4.x, d4[0]);
                     d4[1] = __builtin_fmaf(h4.y, e4.y, d4[1]);
@@ -412,9 +421,11 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
         float lr[KH];
         const int qc = scand < C ? scand : 0;
         float qnext = qself[srow * kQS + qc];     // group 0
+        float4 hv[KH][L / 4];
         load_cv(0, cv);
         load_cv(1 % G, cvn);
-        late(0, lr);
+        load_hrow(0, hv);
+        late(0, lr, hv);
         __syncthreads();                        // X: partial of group 0 in buffer 0
         // Step g: group g decided with its candidate vector requested two
         // steps before (cur); once it is used, the vector of the group after
@@ -429,6 +440,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             // before; the next group's is requested now.
             const float qs = qnext;
             qnext = qself[srow * kQS + gn * C + qc];
+            load_hrow(gn, hv);
             const float* pb = part + (g & 1) * kPB;
             float r[KH];
 #pragma unroll
@@ -479,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void choice_search_kernel(SearchArgs a)
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            late(gn, lr);
+            late(gn, lr, hv);
             __syncthreads();                    // X_g: g decided, the partial of gn ready
         };
         for (int sw = 0; sw < a.sweeps; ++sw) {
