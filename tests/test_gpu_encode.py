@@ -102,6 +102,20 @@ def test_full_sets_then_a_short_set(fmt):
     _check_full(fmt, w, grid_for(fmt), imp)
 
 
+@pytest.mark.parametrize("fmt,mode", [("iq1_s", "encode"), ("iq1_s", "fake"), ("iq1_m", "encode"),
+                                      ("iq2_xs", "encode"), ("iq2_xs", "fake")])
+def test_repeated_full_size_launches_are_identical(fmt, mode):
+    # The 4096x4096 workload launched again and again: every output byte the
+    # same each time (the sweeps' workgroup barriers and LDS staging leave no
+    # room for a race to show as a changed code or value).
+    cfg = workloads.c3_iq2xs_4096() if fmt == "iq2_xs" else workloads.c2_iq1s_4096()
+    w, grid, imp = _dev(cfg["w"]), _dev(cfg["grid"]), _dev(cfg["importance"])
+    fn = iq.encode if mode == "encode" else iq.fake_quant
+    ref = fn(w, grid, imp, fmt=fmt)
+    for _ in range(6):
+        assert torch.equal(fn(w, grid, imp, fmt=fmt), ref)
+
+
 @pytest.mark.parametrize("kind", ["wide", "real", "one_off"])
 @pytest.mark.parametrize("shape,n", [((2, 5, 768), 512), ((1, 3, 512), 37), ((1, 4, 256), 100)])
 def test_iq2xs_grids_not_exact_in_bf16(kind, shape, n):
