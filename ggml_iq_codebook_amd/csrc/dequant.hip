@@ -9,7 +9,7 @@
 //
 // HBM-bound streaming kernel: a wave per 256-value block, a lane per 4
 // consecutive values (half a group), so every store instruction of a wave
-// writes one contiguous KiB.  The lane reads the few payload bytes its group
+// writes one contiguous KiB, with non-temporal stores.  The lane reads the few payload bytes its group
 // needs (the 64 lanes of a block share one 50 to 74-byte record, served by the
 // L1) and one float4 of its grid entry (the grid, at most 64 KiB, stays in
 // L2/L1).
@@ -22,6 +22,15 @@ namespace iqk {
 namespace {
 
 constexpr int kThreads = 256;
+
+// The values are written once and not read again by this kernel: a
+// non-temporal store (measured 9 % faster than a plain one on the 4096 x 4096
+// decodes).
+typedef float f4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_streaming(float* out, int64_t quad, float4 v)
+{
+    __builtin_nontemporal_store(f4v{v.x, v.y, v.z, v.w}, reinterpret_cast<f4v*>(out) + quad);
+}
 
 // Lane t of the launch covers values 4t..4t+3: block t/64, group (t%64)/2,
 // half t%2 of the group.
@@ -50,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void dequant_iq1s_kernel(const uint8_t* _
     } else if (h == 0) {
         report(status, IQ_ERR_CODE);
     }
-    reinterpret_cast<float4*>(out)[t] = v;
+    store_streaming(out, t, v);
 }
 
 __global__ __launch_bounds__(kThreads) void dequant_iq2xs_kernel(const uint8_t* __restrict__ packed,
@@ -82,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void dequant_iq2xs_kernel(const uint8_t* 
     } else if (h == 0) {
         report(status, IQ_ERR_CODE);
     }
-    reinterpret_cast<float4*>(out)[t] = v;
+    store_streaming(out, t, v);
 }
 
 // IQ1_M (#2525 IQ1_M codec body): d's fp16 bits from the top nibbles of the
@@ -119,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void dequant_iq1m_kernel(const uint8_t* _
     } else if (h == 0) {
         report(status, IQ_ERR_CODE);
     }
-    reinterpret_cast<float4*>(out)[t] = v;
+    store_streaming(out, t, v);
 }
 
 }  // namespace
