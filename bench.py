@@ -186,7 +186,7 @@ def _pmc_csv(pmc_dir, config, what):
     raise SystemExit("no %s counter run under %s" % (what, pmc_dir))
 
 
-def record_traffic(config, pmc_dir):
+def record_traffic(config, pmc_dir, which=None):
     """Turn the FETCH_SIZE / WRITE_SIZE counter runs of a workload's kernel and
     of a plain 256 MiB copy into HBM bytes per launch, written to
     profiles/traffic_<kernel>_<config>.json.
@@ -196,7 +196,7 @@ def record_traffic(config, pmc_dir):
     pmc_copy_FETCH_SIZE/copy_counter_collection.csv, pmc_copy_WRITE_SIZE/...
     The copy reads and writes exactly 268435456 bytes; each counter is scaled by
     known bytes / (counted KiB * 1024) of that copy."""
-    name, kernel, sources = profiled_kernel(config)
+    name, kernel, sources = which or profiled_kernel(config)
     kname = kernel.split("<")[0]
     known = 64 * 1024 * 1024 * 4
     f_enc, nf = _counter_mean(_pmc_csv(pmc_dir, config, "FETCH_SIZE"), kname, "FETCH_SIZE")
@@ -406,6 +406,8 @@ def main():
         args.steps = 200 if args.config.endswith("_dequant") else 20
     if args.record_traffic:
         record_traffic(args.config, args.record_traffic)
+        if args.config in PROFILED_SEARCH:
+            record_traffic(args.config, args.record_traffic, PROFILED_SEARCH[args.config])
         return
     if args.record_counters:
         import workloads
@@ -608,6 +610,7 @@ def main():
                           "algorithmic_flops": sflops,
                           "algorithmic_bytes": sbytes, "bound_ms": sb,
                           "frac_of_bound": round(max(sb.values()) / search_ms, 4),
+                          "traffic": traffic_for(sname, source_sha(ssrc)),
                           "counters": counters_for(sname, source_sha(ssrc))}
         result["roofline"] = roof
     else:
