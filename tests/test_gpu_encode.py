@@ -92,14 +92,16 @@ def _iq2xs_grid_kind(kind, n, seed):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_full_sets_then_a_short_set(fmt):
+@pytest.mark.parametrize("n", [None, 37, 300])
+def test_full_sets_then_a_short_set(fmt, n):
     # 4101 blocks: 257 sets of 16 blocks for 256 persistent workgroups, so one
     # workgroup takes a full set and then a set of 5.  The waves of a full set
-    # meet at workgroup barriers during the sweep; a short set takes none
-    # (its idle waves never reach them).
+    # meet at workgroup barriers during the sweep (one per tracking chunk: a
+    # truncated grid has one or a few chunks); a short set takes none (its
+    # idle waves never reach them).
     w = workloads.normal_weight((1, 4101, 256), 61)
     imp = workloads.lognormal_importance((1, 256), 62)
-    _check_full(fmt, w, grid_for(fmt), imp)
+    _check_full(fmt, w, grid_for(fmt, n), imp)
 
 
 @pytest.mark.parametrize("fmt,mode", [("iq1_s", "encode"), ("iq1_s", "fake"), ("iq1_m", "encode"),
